@@ -1,0 +1,53 @@
+"""Plant mistakes in copies of the oracle (CPU only) and check the pins catch each.
+
+Every mutant is a textual patch of oracle/path_oracle.c compiled into a
+temporary library; the real oracle is never modified.  A mutant survives if
+every pin in oracle_pins passes on it, which fails this test.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "path_oracle.c")
+
+# (id, text to replace, replacement, expected occurrences)
+MUTANTS = [
+    ("off_by_one_H", "apply_h(u, w + (size_t)(j + 1) * d, beta[j + 1], d);", "apply_h(u, w + (size_t)j * d, beta[j], d);", 2),
+    ("apply_h_no_beta", "u[c] -= beta * wu * w[c];", "u[c] -= wu * w[c];", 1),
+    ("apply_h_sign", "u[c] -= beta * wu * w[c];", "u[c] += beta * wu * w[c];", 1),
+    ("apply_h_drop_dot_term", "wu += w[c] * u[c];", "wu += w[c];", 1),
+    ("fox_bias_index", "if (logf) bias += logf[j + 1];", "if (logf) bias += logf[j];", 2),
+    ("scale_dropped", "sbuf[j] = scale * kt + bias;", "sbuf[j] = kt + bias;", 1),
+    ("scale_on_bias", "sbuf[j] = scale * kt + bias;", "sbuf[j] = scale * (kt + bias);", 1),
+    ("scores_scale_on_bias", "S[(size_t)i * L + j] = scale * kt + bias;", "S[(size_t)i * L + j] = scale * (kt + bias);", 1),
+    ("key_operand_swapped", "for (int c = 0; c < d; ++c) kt += k[(size_t)j * d + c] * u[c];\n        sbuf",
+     "for (int c = 0; c < d; ++c) kt += v[(size_t)j * d + c] * u[c];\n        sbuf", 1),
+    ("no_normalise", "for (int c = 0; c < d; ++c) o[c] /= z;", "", 1),
+    ("lse_no_max", "*lse = m + log(z);\n}\n\ntypedef struct {\n    const double *q", "*lse = log(z);\n}\n\ntypedef struct {\n    const double *q", 1),
+    ("transport_reversed", "for (int s = hi; s >= lo; --s) apply_h", "for (int s = lo; s <= hi; ++s) apply_h", 1),
+    ("causal_diag_excluded", "for (int j = 0; j <= i; ++j) {\n        double p", "for (int j = 0; j < i; ++j) {\n        double p", 1),
+    ("decode_no_update", "for (int64_t j = 0; j < n; ++j) apply_h(kc + (size_t)j * d, w, beta, d);", "", 1),
+    ("decode_new_key_transformed",
+     "for (int64_t j = 0; j < n; ++j) apply_h(kc + (size_t)j * d, w, beta, d);\n    int64_t nt = n;\n    if (knew && vnew) {\n        memcpy(kc + (size_t)n * d, knew, sizeof(double) * (size_t)d);\n        memcpy(vc + (size_t)n * d, vnew, sizeof(double) * (size_t)d);\n        nt = n + 1;\n    }",
+     "int64_t nt = n;\n    if (knew && vnew) {\n        memcpy(kc + (size_t)n * d, knew, sizeof(double) * (size_t)d);\n        memcpy(vc + (size_t)n * d, vnew, sizeof(double) * (size_t)d);\n        nt = n + 1;\n    }\n    for (int64_t j = 0; j < nt; ++j) apply_h(kc + (size_t)j * d, w, beta, d);", 1),
+    ("decode_scale_dropped", "double p = exp(scale * s - m);", "double p = exp(s - m);", 1),
+]
+
+
+@pytest.mark.parametrize("mid,old,new,count", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(mid, old, new, count, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == count, "patch for %s no longer matches the oracle source" % mid
+    mutant = tmp_path / ("oracle_%s.c" % mid)
+    mutant.write_text(src.replace(old, new))
+    lib = oracle.compile_source(str(mutant), str(tmp_path / ("liboracle_%s.so" % mid)))
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, FloatingPointError) as e:
+            caught.append((pin.__name__, str(e)[:80]))
+    assert caught, "mutant %s survived every pin" % mid
