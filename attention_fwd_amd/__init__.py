@@ -1,0 +1,214 @@
+"""PaTH attention for AMD MI355X: a thin ctypes binding of libpath_attn.so.
+
+Every step of the computation runs in the library's HIP kernels; this module
+only marshals torch tensors (device memory) and the current HIP stream into
+the C ABI declared in include/path_attn.h.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["fwd", "fwd_prep", "fwd_scan", "decode_step", "fwd_workspace_size", "decode_workspace_size", "lib", "PathError",
+           "PATH_OK", "PATH_EINVAL", "PATH_EUNSUPPORTED", "PATH_EHIP", "PATH_DTYPE_F32", "PATH_DTYPE_BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpath_attn.so")
+
+PATH_OK, PATH_EINVAL, PATH_EUNSUPPORTED, PATH_EHIP = 0, 1, 2, 3
+PATH_DTYPE_F32, PATH_DTYPE_BF16 = 0, 1
+_DTYPES = {torch.float32: PATH_DTYPE_F32, torch.bfloat16: PATH_DTYPE_BF16}
+
+_lib = None
+
+
+class PathError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        msg = _lib.path_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__("%s: %s (status %d)" % (what, msg, status))
+
+
+def lib():
+    """The loaded C library (ctypes), with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libpath_attn.so is not built (run __graft_entry__.build() or "
+                               "python attention_fwd_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, fp, i, i64, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.path_abi_version.restype = ctypes.c_int
+        L.path_abi_version.argtypes = []
+        L.path_status_string.restype = ctypes.c_char_p
+        L.path_status_string.argtypes = [ctypes.c_int]
+        L.path_attn_fwd_workspace_size.restype = sz
+        L.path_attn_fwd_workspace_size.argtypes = [i, i, i, i, ctypes.c_int]
+        L.path_attn_fwd.restype = ctypes.c_int
+        L.path_attn_fwd.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, i, i, i, i, ctypes.c_int, ctypes.c_float,
+                                    vp, sz, vp]
+        L.path_attn_fwd_prep.restype = ctypes.c_int
+        L.path_attn_fwd_prep.argtypes = list(L.path_attn_fwd.argtypes)
+        L.path_attn_fwd_scan.restype = ctypes.c_int
+        L.path_attn_fwd_scan.argtypes = [vp, fp, i, i, i, i, i, ctypes.c_int, ctypes.c_float, vp, sz, vp]
+        L.path_decode_workspace_size.restype = sz
+        L.path_decode_workspace_size.argtypes = [i, i, i64, i, ctypes.c_int]
+        L.path_decode_step.restype = ctypes.c_int
+        L.path_decode_step.argtypes = [vp, vp, i64, i64, vp, vp, fp, vp, vp, vp, fp, i, i, i, ctypes.c_int,
+                                       ctypes.c_float, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device (cuda/hip) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fwd_workspace_size(B, H, L, d, dtype=torch.bfloat16):
+    return int(lib().path_attn_fwd_workspace_size(B, H, L, d, _DTYPES[dtype]))
+
+
+def decode_workspace_size(B, H, rows, d, dtype=torch.bfloat16):
+    return int(lib().path_decode_workspace_size(B, H, rows, d, _DTYPES[dtype]))
+
+
+def fwd(q, k, v, w, beta, logf=None, scale=None, out=None, lse=None, return_lse=False, workspace=None,
+        stream=None):
+    """Causal PaTH attention forward (path_attn_fwd).
+
+    q, k, v, w: [B, H, L, d] bf16 or fp32 device tensors; beta, logf: [B, H, L]
+    fp32 (logf optional, enables the PaTH-FoX bias).  Returns out (and lse
+    when return_lse or an lse tensor is given).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d]")
+    B, H, L, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError("dtype must be bfloat16 or float32")
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (w, "w")):
+        _check(t, n, dt, (B, H, L, d), dev)
+    _check(beta, "beta", torch.float32, (B, H, L), dev)
+    if logf is not None:
+        _check(logf, "logf", torch.float32, (B, H, L), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", dt, (B, H, L, d), dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, L), device=dev, dtype=torch.float32)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H, L), dev)
+    need = fwd_workspace_size(B, H, L, d, dt)
+    if need == 0:
+        raise PathError(PATH_EUNSUPPORTED if d != 64 else PATH_EINVAL, "path_attn_fwd_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    _check(workspace, "workspace", None, None, dev)
+    with torch.cuda.device(dev):
+        st = lib().path_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf), _ptr(out), _ptr(lse),
+                                 B, H, L, d, _DTYPES[dt], float(scale or 0.0), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != PATH_OK:
+        raise PathError(st, "path_attn_fwd")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def fwd_prep(q, k, v, w, beta, logf, out, lse, workspace, scale=None, stream=None):
+    """First stage of the forward (path_attn_fwd_prep); tensors preallocated by the caller."""
+    B, H, L, d = q.shape
+    dev, dt = q.device, q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (w, "w"), (out, "out")):
+        _check(t, n, dt, (B, H, L, d), dev)
+    _check(beta, "beta", torch.float32, (B, H, L), dev)
+    for t, n in ((logf, "logf"), (lse, "lse")):
+        if t is not None:
+            _check(t, n, torch.float32, (B, H, L), dev)
+    _check(workspace, "workspace", None, None, dev)
+    st = lib().path_attn_fwd_prep(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf), _ptr(out), _ptr(lse),
+                                  B, H, L, d, _DTYPES[q.dtype], float(scale or 0.0), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != PATH_OK:
+        raise PathError(st, "path_attn_fwd_prep")
+
+
+def fwd_scan(out, lse, has_logf, workspace, scale=None, stream=None):
+    """Second stage of the forward (path_attn_fwd_scan) on a workspace filled by fwd_prep."""
+    B, H, L, d = out.shape
+    _check(out, "out", None, None, None)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H, L), out.device)
+    _check(workspace, "workspace", None, None, out.device)
+    st = lib().path_attn_fwd_scan(_ptr(out), _ptr(lse), int(bool(has_logf)), B, H, L, d, _DTYPES[out.dtype],
+                                  float(scale or 0.0), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
+    if st != PATH_OK:
+        raise PathError(st, "path_attn_fwd_scan")
+
+
+def decode_step(kcache, vcache, n, q, w, beta, k_new=None, v_new=None, scale=None, out=None, lse=None,
+                return_lse=False, workspace=None, stream=None):
+    """One PaTH decode step (path_decode_step): updates kcache rows [0, n) in place.
+
+    kcache, vcache: [B, H, ncap, d]; q, w, k_new, v_new: [B, H, d]; beta: [B, H] fp32.
+    Returns out [B, H, d] (and lse [B, H] when requested).
+    """
+    if kcache.dim() != 4:
+        raise ValueError("kcache must be [B, H, ncap, d]")
+    B, H, ncap, d = kcache.shape
+    dt = kcache.dtype
+    if dt not in _DTYPES:
+        raise ValueError("dtype must be bfloat16 or float32")
+    dev = kcache.device
+    _check(kcache, "kcache", dt, (B, H, ncap, d), dev)
+    _check(vcache, "vcache", dt, (B, H, ncap, d), dev)
+    for t, nm in ((q, "q"), (w, "w")):
+        _check(t, nm, dt, (B, H, d), dev)
+    _check(beta, "beta", torch.float32, (B, H), dev)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        _check(k_new, "k_new", dt, (B, H, d), dev)
+        _check(v_new, "v_new", dt, (B, H, d), dev)
+    if out is None:
+        out = torch.empty((B, H, d), device=dev, dtype=dt)
+    _check(out, "out", dt, (B, H, d), dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H), device=dev, dtype=torch.float32)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H), dev)
+    rows = int(n) + (1 if k_new is not None else 0)
+    need = decode_workspace_size(B, H, max(rows, 1), d, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=dev, dtype=torch.uint8)
+    _check(workspace, "workspace", None, None, dev)
+    with torch.cuda.device(dev):
+        st = lib().path_decode_step(_ptr(kcache), _ptr(vcache), int(n), ncap, _ptr(q), _ptr(w), _ptr(beta),
+                                    _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), B, H, d, _DTYPES[dt],
+                                    float(scale or 0.0), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != PATH_OK:
+        raise PathError(st, "path_decode_step")
+    return (out, lse) if (return_lse or lse is not None) else out

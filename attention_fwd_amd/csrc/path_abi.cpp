@@ -1,0 +1,227 @@
+// path_abi.cpp -- the C ABI declared in include/path_attn.h: argument
+// validation (before anything is enqueued), workspace sizing and launches.
+#include "path_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "path_kernels.h"
+#include "path_layout.h"
+
+namespace {
+
+constexpr int64_t kMaxGrid = 2147483647;  // blockIdx.x range
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int64_t elem_size(path_dtype_t t) { return t == PATH_DTYPE_BF16 ? 2 : (t == PATH_DTYPE_F32 ? 4 : 0); }
+
+// [p, p+n) and [q, q+m) overlap?
+bool overlap(const void *p, int64_t n, const void *q, int64_t m) {
+    if (!p || !q || n <= 0 || m <= 0) return false;
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + (uintptr_t)m && b < a + (uintptr_t)n;
+}
+
+// Checked product of positive sizes; -1 on overflow past 2^62.
+int64_t mul_chk(std::initializer_list<int64_t> xs) {
+    int64_t r = 1;
+    for (int64_t x : xs) {
+        if (x < 0) return -1;
+        if (x != 0 && r > (int64_t(1) << 62) / x) return -1;
+        r *= x;
+    }
+    return r;
+}
+
+path_status_t fwd_sizes_ok(int B, int H, int L, int d, path_dtype_t dtype) {
+    if (B < 1 || H < 1 || L < 1 || d < 1 || elem_size(dtype) == 0) return PATH_EINVAL;
+    if (d != 64) return PATH_EUNSUPPORTED;
+    const int64_t nb = ((int64_t)L + path::kBlk - 1) / path::kBlk;
+    if (mul_chk({B, H, nb * path::kBlk, d, 8}) < 0) return PATH_EINVAL;
+    if (mul_chk({B, H, nb}) > kMaxGrid) return PATH_EINVAL;
+    return PATH_OK;
+}
+
+path_status_t dec_sizes_ok(int B, int H, int64_t rows, int d, path_dtype_t dtype) {
+    if (B < 1 || H < 1 || rows < 1 || d < 1 || elem_size(dtype) == 0) return PATH_EINVAL;
+    if (d != 64) return PATH_EUNSUPPORTED;
+    if (mul_chk({B, H, rows, d, 8}) < 0) return PATH_EINVAL;
+    return PATH_OK;
+}
+
+size_t dec_ws_bytes(int B, int H, int64_t rows, int d) {
+    int nsplit;
+    int64_t chunk;
+    path::decode_plan((int64_t)B * H, rows, &nsplit, &chunk);
+    return (size_t)B * H * nsplit * (d + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int path_abi_version(void) { return PATH_ABI_VERSION; }
+
+const char *path_status_string(path_status_t s) {
+    switch (s) {
+        case PATH_OK: return "ok";
+        case PATH_EINVAL: return "invalid argument";
+        case PATH_EUNSUPPORTED: return "unsupported configuration";
+        case PATH_EHIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+size_t path_attn_fwd_workspace_size(int B, int H, int L, int d, path_dtype_t dtype) {
+    if (fwd_sizes_ok(B, H, L, d, dtype) != PATH_OK) return 0;
+    return path::fwd_layout(B, H, L, d, elem_size(dtype)).total;
+}
+
+namespace {
+
+path_status_t fwd_check(const void *q, const void *k, const void *v, const void *w, const float *beta,
+                        const float *logf, void *out, float *lse, int B, int H, int L, int d, path_dtype_t dtype,
+                        float scale, void *workspace, size_t workspace_bytes) {
+    path_status_t st = fwd_sizes_ok(B, H, L, d, dtype);
+    if (st != PATH_OK) return st;
+    if (!q || !k || !v || !w || !beta || !out || !workspace) return PATH_EINVAL;
+    for (const void *p : {q, k, v, w, (const void *)out, (const void *)workspace})
+        if (!aligned(p, 16)) return PATH_EINVAL;
+    for (const void *p : {(const void *)beta, (const void *)logf, (const void *)lse})
+        if (p && !aligned(p, 4)) return PATH_EINVAL;
+    const size_t need = path::fwd_layout(B, H, L, d, elem_size(dtype)).total;
+    if (workspace_bytes < need) return PATH_EINVAL;
+    if (!(std::isfinite(scale))) return PATH_EINVAL;
+    const int64_t tens = (int64_t)B * H * L * d * elem_size(dtype), tok = (int64_t)B * H * L * 4;
+    for (const void *p : {q, k, v, w})
+        if (overlap(out, tens, p, tens) || overlap(workspace, (int64_t)need, p, tens)) return PATH_EINVAL;
+    for (const void *p : {(const void *)beta, (const void *)logf})
+        if (overlap(out, tens, p, tok) || overlap(workspace, (int64_t)need, p, tok) || overlap(lse, tok, p, tok))
+            return PATH_EINVAL;
+    if (overlap(out, tens, workspace, (int64_t)need) || overlap(lse, tok, workspace, (int64_t)need) ||
+        overlap(lse, tok, out, tens))
+        return PATH_EINVAL;
+    for (const void *p : {q, k, v, w})
+        if (overlap(lse, tok, p, tens)) return PATH_EINVAL;
+    return PATH_OK;
+}
+
+path_status_t scan_check(void *out, float *lse, int B, int H, int L, int d, path_dtype_t dtype, float scale,
+                         void *workspace, size_t workspace_bytes) {
+    path_status_t st = fwd_sizes_ok(B, H, L, d, dtype);
+    if (st != PATH_OK) return st;
+    if (!out || !workspace || !aligned(out, 16) || !aligned(workspace, 16)) return PATH_EINVAL;
+    if (lse && !aligned(lse, 4)) return PATH_EINVAL;
+    const size_t need = path::fwd_layout(B, H, L, d, elem_size(dtype)).total;
+    if (workspace_bytes < need || !std::isfinite(scale)) return PATH_EINVAL;
+    const int64_t tens = (int64_t)B * H * L * d * elem_size(dtype), tok = (int64_t)B * H * L * 4;
+    if (overlap(out, tens, workspace, (int64_t)need) || overlap(lse, tok, workspace, (int64_t)need) ||
+        overlap(lse, tok, out, tens))
+        return PATH_EINVAL;
+    return PATH_OK;
+}
+
+path_status_t launch_prep_stage(const void *q, const void *k, const void *v, const void *w, const float *beta,
+                                const float *logf, void *out, float *lse, int B, int H, int L, int d,
+                                path_dtype_t dtype, float scale, void *workspace, hipStream_t s) {
+    path::PrepArgs pa{q, k, v, w, beta, logf, out, lse, workspace, B, H, L, d, scale};
+    return path::launch_prep(pa, dtype == PATH_DTYPE_BF16, s) == hipSuccess ? PATH_OK : PATH_EHIP;
+}
+
+path_status_t launch_scan_stage(void *out, float *lse, bool fox, int B, int H, int L, int d, path_dtype_t dtype,
+                                float scale, void *workspace, hipStream_t s) {
+    path::FwdArgs fa{out, lse, workspace, B, H, L, d, scale, fox ? 1 : 0};
+    return path::launch_fwd(fa, dtype == PATH_DTYPE_BF16, s) == hipSuccess ? PATH_OK : PATH_EHIP;
+}
+
+float eff_scale(float scale, int d) { return scale <= 0.f ? 1.0f / std::sqrt((float)d) : scale; }
+
+}  // namespace
+
+path_status_t path_attn_fwd(const void *q, const void *k, const void *v, const void *w, const float *beta,
+                            const float *logf, void *out, float *lse, int B, int H, int L, int d,
+                            path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    path_status_t st = fwd_check(q, k, v, w, beta, logf, out, lse, B, H, L, d, dtype, scale, workspace,
+                                 workspace_bytes);
+    if (st != PATH_OK) return st;
+    scale = eff_scale(scale, d);
+    hipStream_t s = (hipStream_t)stream;
+    st = launch_prep_stage(q, k, v, w, beta, logf, out, lse, B, H, L, d, dtype, scale, workspace, s);
+    if (st != PATH_OK) return st;
+    return launch_scan_stage(out, lse, logf != nullptr, B, H, L, d, dtype, scale, workspace, s);
+}
+
+path_status_t path_attn_fwd_prep(const void *q, const void *k, const void *v, const void *w, const float *beta,
+                                 const float *logf, void *out, float *lse, int B, int H, int L, int d,
+                                 path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    path_status_t st = fwd_check(q, k, v, w, beta, logf, out, lse, B, H, L, d, dtype, scale, workspace,
+                                 workspace_bytes);
+    if (st != PATH_OK) return st;
+    return launch_prep_stage(q, k, v, w, beta, logf, out, lse, B, H, L, d, dtype, eff_scale(scale, d), workspace,
+                             (hipStream_t)stream);
+}
+
+path_status_t path_attn_fwd_scan(void *out, float *lse, int has_logf, int B, int H, int L, int d,
+                                 path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    path_status_t st = scan_check(out, lse, B, H, L, d, dtype, scale, workspace, workspace_bytes);
+    if (st != PATH_OK) return st;
+    return launch_scan_stage(out, lse, has_logf != 0, B, H, L, d, dtype, eff_scale(scale, d), workspace,
+                             (hipStream_t)stream);
+}
+
+size_t path_decode_workspace_size(int B, int H, int64_t n, int d, path_dtype_t dtype) {
+    if (dec_sizes_ok(B, H, n, d, dtype) != PATH_OK) return 0;
+    return dec_ws_bytes(B, H, n, d);
+}
+
+path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,
+                               const float *beta, const void *k_new, const void *v_new, void *out, float *lse,
+                               int B, int H, int d, path_dtype_t dtype, float scale, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    if (n < 0 || ncap < 1 || n > ncap) return PATH_EINVAL;
+    if ((k_new == nullptr) != (v_new == nullptr)) return PATH_EINVAL;
+    const int64_t natt = n + (k_new ? 1 : 0);
+    if (natt > ncap) return PATH_EINVAL;
+    path_status_t st = dec_sizes_ok(B, H, natt, d, dtype);
+    if (st != PATH_OK) return st;
+    if (mul_chk({B, H, ncap, d, 8}) < 0) return PATH_EINVAL;
+    if (!kcache || !vcache || !q || !w || !beta || !out || !workspace) return PATH_EINVAL;
+    for (const void *p : {(const void *)kcache, (const void *)vcache, q, w, k_new, v_new, (const void *)out,
+                          (const void *)workspace})
+        if (p && !aligned(p, 16)) return PATH_EINVAL;
+    if (!aligned(beta, 4) || (lse && !aligned(lse, 4))) return PATH_EINVAL;
+    const size_t need = dec_ws_bytes(B, H, natt, d);
+    if (workspace_bytes < need) return PATH_EINVAL;
+    if (!(std::isfinite(scale))) return PATH_EINVAL;
+    const int64_t es = elem_size(dtype);
+    const int64_t cache = (int64_t)B * H * ncap * d * es, vec = (int64_t)B * H * d * es, sc = (int64_t)B * H * 4;
+    if (overlap(kcache, cache, vcache, cache)) return PATH_EINVAL;
+    for (const void *p : {q, w, k_new, v_new, (const void *)out, (const void *)workspace}) {
+        const int64_t sz = p == workspace ? (int64_t)need : vec;
+        if (overlap(kcache, cache, p, sz) || overlap(vcache, cache, p, sz)) return PATH_EINVAL;
+    }
+    for (const void *p : {q, w, k_new, v_new, (const void *)workspace})
+        if (overlap(out, vec, p, p == workspace ? (int64_t)need : vec)) return PATH_EINVAL;
+    if (lse && (overlap(lse, sc, beta, sc) || overlap(lse, sc, out, vec) || overlap(lse, sc, workspace, (int64_t)need) ||
+                overlap(lse, sc, kcache, cache) || overlap(lse, sc, vcache, cache)))
+        return PATH_EINVAL;
+    if (scale <= 0.f) scale = 1.0f / std::sqrt((float)d);
+
+    path::DecodeArgs da{};
+    da.kc = kcache; da.vc = vcache; da.n = n; da.ncap = ncap;
+    da.q = q; da.w = w; da.beta = beta; da.knew = k_new; da.vnew = v_new;
+    da.out = out; da.lse = lse; da.ws = workspace;
+    da.B = B; da.H = H; da.d = d; da.scale = scale;
+    path::decode_plan((int64_t)B * H, natt, &da.nsplit, &da.chunk);
+    if ((int64_t)da.nsplit * B * H > kMaxGrid) return PATH_EINVAL;
+    if (path::launch_decode(da, dtype == PATH_DTYPE_BF16, (hipStream_t)stream) != hipSuccess) return PATH_EHIP;
+    return PATH_OK;
+}
+
+}  // extern "C"

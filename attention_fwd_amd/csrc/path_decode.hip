@@ -1,0 +1,224 @@
+// path_decode.hip -- PaTH decode step: in-place rank-1 key-cache update fused
+// with single-query attention.
+//
+// Source: "技術要約: PaTH Attention" (gist.science), section 3 (inference):
+// the historical keys are updated in place with the newest transition matrix
+// H_t = I - beta_t w_t w_t^T, so no cache of w / beta is kept, and decoding
+// then proceeds like ordinary softmax decoding over the (updated) cache.
+//
+// Per cached row j (one pass over HBM: read k_j, write k_j', read v_j):
+//   a_j   = w . k_j,  b_j = q . k_j            (one 8-lane reduction for both)
+//   k_j'  = k_j - beta a_j w                   (stored back, rounded to the cache type)
+//   s_j   = scale * q . k_j' = scale * (b_j - beta a_j (q . w))
+// followed by an online softmax over the rows of a split.  Eight lanes share
+// a row (8 elements = 16 bytes of bf16 each), a wave covers 8 rows per load
+// and every lane keeps 4 rows in flight.  Splits of the cache write partial
+// (max, sum, accumulator) records that a second small kernel merges in a fixed
+// order, so results are bitwise reproducible.
+#include "path_common.h"
+#include "path_kernels.h"
+
+namespace path {
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kRowsPerIter = 4;  // rows per lane group per iteration
+
+template <typename S>
+__device__ __forceinline__ void load8(const S *p, float *x) {
+    if constexpr (sizeof(S) == 2) {
+        u32x4 u = *(const u32x4 *)p;
+        x[0] = bf16_to_f32(u.x & 0xffff); x[1] = bf16_to_f32(u.x >> 16);
+        x[2] = bf16_to_f32(u.y & 0xffff); x[3] = bf16_to_f32(u.y >> 16);
+        x[4] = bf16_to_f32(u.z & 0xffff); x[5] = bf16_to_f32(u.z >> 16);
+        x[6] = bf16_to_f32(u.w & 0xffff); x[7] = bf16_to_f32(u.w >> 16);
+    } else {
+        f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+}
+
+template <typename S>
+__device__ __forceinline__ void store8(S *p, const float *x) {
+    if constexpr (sizeof(S) == 2) {
+        u32x4 u = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+        *(u32x4 *)p = u;
+    } else {
+        f32x4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
+        *(f32x4 *)p = a;
+        *(f32x4 *)(p + 4) = b;
+    }
+}
+
+template <typename S, int D>
+__global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) {
+    static_assert(D == 64, "decode kernel is laid out for head dimension 64 (8 lanes x 8 elements per row)");
+    constexpr int NG = kDecThreads / 8;  // lane groups (rows in flight per load) per workgroup
+    __shared__ float sred[NG][D + 2];
+
+    const int split = (int)(blockIdx.x % a.nsplit);
+    const int64_t bh = blockIdx.x / a.nsplit;
+    const int tid = threadIdx.x, grp = tid >> 3, sub = tid & 7;
+    const int64_t natt = a.n + (a.knew ? 1 : 0);
+    const int64_t r0 = (int64_t)split * a.chunk;
+    const int64_t r1 = min(natt, r0 + a.chunk);
+
+    S *kc = (S *)a.kc + bh * a.ncap * D;
+    S *vc = (S *)a.vc + bh * a.ncap * D;
+    float q[8], w[8];
+    load8<S>((const S *)a.q + bh * D + 8 * sub, q);
+    load8<S>((const S *)a.w + bh * D + 8 * sub, w);
+    const float beta = a.beta[bh];
+    float qw = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qw += q[e] * w[e];
+    qw = sum8(qw);
+    const float c2 = a.scale * kLog2e;
+
+    float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+
+    for (int64_t base = r0 + grp; base < r1; base += (int64_t)NG * kRowsPerIter) {
+        float kx[kRowsPerIter][8], vx[kRowsPerIter][8], x[kRowsPerIter];
+        bool ok[kRowsPerIter], fresh[kRowsPerIter];
+#pragma unroll
+        for (int u = 0; u < kRowsPerIter; ++u) {
+            const int64_t j = base + (int64_t)u * NG;
+            ok[u] = j < r1;
+            fresh[u] = ok[u] && j == a.n;  // the appended token (only when knew != NULL)
+            if (ok[u] && !fresh[u]) {
+                load8<S>(kc + j * D + 8 * sub, kx[u]);
+                load8<S>(vc + j * D + 8 * sub, vx[u]);
+            } else if (fresh[u]) {
+                load8<S>((const S *)a.knew + bh * D + 8 * sub, kx[u]);
+                load8<S>((const S *)a.vnew + bh * D + 8 * sub, vx[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kx[u][e] = vx[u][e] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRowsPerIter; ++u) {
+            const int64_t j = base + (int64_t)u * NG;
+            float pa = 0.f, pb = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pa += w[e] * kx[u][e];
+                pb += q[e] * kx[u][e];
+            }
+            const float ta = sum8(pa), tb = sum8(pb);
+            if (fresh[u]) {
+                // new key enters untransformed; store k_new, v_new at row n
+                store8<S>(kc + j * D + 8 * sub, kx[u]);
+                store8<S>(vc + j * D + 8 * sub, vx[u]);
+                x[u] = tb * c2;
+            } else if (ok[u]) {
+                const float cb = beta * ta;
+                float kn[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kn[e] = kx[u][e] - cb * w[e];
+                store8<S>(kc + j * D + 8 * sub, kn);
+                x[u] = (tb - cb * qw) * c2;
+            } else {
+                x[u] = -INFINITY;
+            }
+        }
+        float mx = m;
+#pragma unroll
+        for (int u = 0; u < kRowsPerIter; ++u) mx = fmaxf(mx, x[u]);
+        if (mx != -INFINITY) {
+            const float alpha = fast_exp2(m - mx);
+            l *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll
+            for (int u = 0; u < kRowsPerIter; ++u) {
+                const float p = fast_exp2(x[u] - mx);
+                l += p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += p * vx[u][e];
+            }
+            m = mx;
+        }
+    }
+
+    // merge the lane groups of the workgroup in a fixed order
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sred[grp][8 * sub + e] = acc[e];
+    if (sub == 0) {
+        sred[grp][D] = m;
+        sred[grp][D + 1] = l;
+    }
+    __syncthreads();
+    if (tid < D) {
+        float mm = -INFINITY;
+        for (int g = 0; g < NG; ++g) mm = fmaxf(mm, sred[g][D]);
+        float ls = 0.f, as = 0.f;
+        for (int g = 0; g < NG; ++g) {
+            const float mg = sred[g][D];
+            const float wgt = mg == -INFINITY ? 0.f : fast_exp2(mg - mm);
+            ls += wgt * sred[g][D + 1];
+            as += wgt * sred[g][tid];
+        }
+        float *part = (float *)a.ws + ((int64_t)bh * a.nsplit + split) * (D + 2);
+        part[tid] = as;
+        if (tid == 0) {
+            part[D] = mm;
+            part[D + 1] = ls;
+        }
+    }
+}
+
+template <typename S, int D>
+__global__ __launch_bounds__(64) void path_decode_combine_kernel(DecodeArgs a) {
+    const int64_t bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float *part = (const float *)a.ws + (int64_t)bh * a.nsplit * (D + 2);
+    float mm = -INFINITY;
+    for (int s = 0; s < a.nsplit; ++s) mm = fmaxf(mm, part[(int64_t)s * (D + 2) + D]);
+    float ls = 0.f, as = 0.f;
+    for (int s = 0; s < a.nsplit; ++s) {
+        const float *p = part + (int64_t)s * (D + 2);
+        const float wgt = p[D] == -INFINITY ? 0.f : fast_exp2(p[D] - mm);
+        ls += wgt * p[D + 1];
+        as += wgt * p[tid];
+    }
+    if (tid < D) ((S *)a.out)[bh * D + tid] = Elem<S>::from_float(as / ls);
+    if (tid == 0 && a.lse) a.lse[bh] = (mm + __log2f(ls)) * kLn2;
+}
+
+}  // namespace
+
+void decode_plan(int64_t BH, int64_t rows, int *nsplit, int64_t *chunk) {
+    const int64_t target_wg = 4096;
+    const int64_t step = (int64_t)(kDecThreads / 8) * kRowsPerIter;  // rows per workgroup iteration
+    int64_t per_head = (target_wg + BH - 1) / BH;
+    const int64_t max_split = (rows + step - 1) / step;
+    if (per_head > max_split) per_head = max_split;
+    if (per_head < 1) per_head = 1;
+    int64_t c = (rows + per_head - 1) / per_head;
+    c = (c + step - 1) / step * step;
+    if (c < step) c = step;
+    *chunk = c;
+    *nsplit = (int)((rows + c - 1) / c);
+    if (*nsplit < 1) *nsplit = 1;
+}
+
+template <typename S>
+static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
+    dim3 grid((unsigned)(a.nsplit * a.B * a.H));
+    hipLaunchKernelGGL((path_decode_kernel<S, 64>), grid, dim3(kDecThreads), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((path_decode_combine_kernel<S, 64>), dim3((unsigned)(a.B * a.H)), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t st) {
+    if (a.d != 64) return hipErrorInvalidValue;
+    return bf16 ? launch_decode_t<uint16_t>(a, st) : launch_decode_t<float>(a, st);
+}
+
+}  // namespace path

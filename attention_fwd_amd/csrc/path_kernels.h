@@ -1,0 +1,50 @@
+// path_kernels.h -- launch interface between the C ABI and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace path {
+
+struct PrepArgs {
+    const void *q, *k, *v, *w;
+    const float *beta, *logf;
+    void *out;
+    float *lse;
+    void *ws;
+    int B, H, L, d;
+    float scale;
+};
+
+struct FwdArgs {
+    void *out;
+    float *lse;
+    const void *ws;
+    int B, H, L, d;
+    float scale;
+    int fox;
+};
+
+struct DecodeArgs {
+    void *kc, *vc;
+    int64_t n, ncap;
+    const void *q, *w;
+    const float *beta;
+    const void *knew, *vnew;
+    void *out;
+    float *lse;
+    void *ws;
+    int B, H, d;
+    float scale;
+    int nsplit;
+    int64_t chunk;
+};
+
+hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st);
+hipError_t launch_fwd(const FwdArgs &a, bool bf16, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t st);
+
+// Decode split plan: rows per split and number of splits for n attending rows.
+void decode_plan(int64_t BH, int64_t rows, int *nsplit, int64_t *chunk);
+
+}  // namespace path

@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the PaTH attention hot path on one MI355X.
+
+A step is one causal PaTH forward pass (prep + scan kernels) over the
+B32 H32 L4096 d64 bf16 workload; K steps are timed after W warm-up steps.
+Alongside it the decode step (B16 H32 d64, 32768 cached rows, bf16, 64 steps
+with fresh q, w, beta each) is timed, and the fp64 CPU oracle is timed on a
+bounded sample of the forward workload.  Prints one JSON line.
+
+Work units (fixed, declared):
+  forward  F = 4 B H L^2 d flop: per causal pair of 64-token blocks the query-
+           key logits, the probability-value product and the rank-64 query
+           transform (2 + 2 + 4) * 64^2 d; the in-block (diagonal) work is not
+           counted.
+  decode   bytes = 3 B H n d * 2: read every cached key, write it back
+           updated, read every cached value.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
+METRIC = "PaTH fwd TFLOP/s + % MFMA peak (B32 H32 d64 L4096); decode-step HBM GB/s"
+FWD_WORKLOAD = "sweep_L4096_d64_bf16"
+DEC_WORKLOAD = "decode_N32768_bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_path_fwd_kernel_B32H32L4096.txt")
+KERNEL_SOURCES = ["attention_fwd_amd/csrc/path_fwd.hip", "attention_fwd_amd/csrc/path_common.h",
+                  "attention_fwd_amd/csrc/path_layout.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the scan kernel from committed counter runs, if
+    they were taken on the current kernel source (else None)."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256_16") != kernel_hash():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def bench_forward(steps, warmup):
+    import torch
+
+    import attention_fwd_amd as pa
+    import pathgen
+
+    c = pathgen.WORKLOADS[FWD_WORKLOAD]
+    B, H, L, d = c["B"], c["H"], c["L"], c["d"]
+    x = pathgen.fwd_inputs(B, H, L, d, c["dtype"], seed=0, fox=c["fox"], clip=c["clip"], device="cuda")
+    out = torch.empty_like(x["q"])
+    lse = torch.empty((B, H, L), device="cuda", dtype=torch.float32)
+    ws = torch.empty(pa.fwd_workspace_size(B, H, L, d, x["q"].dtype), device="cuda", dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        pa.fwd_prep(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out, lse, ws)
+        if ev:
+            ev[1].record(stream)
+        pa.fwd_scan(out, lse, x["logf"] is not None, ws)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    flops = 4.0 * B * H * L * L * d
+    return dict(B=B, H=H, L=L, d=d, flops=flops, wall_s=wall, ms_per_step=wall * 1e3 / steps,
+                prep_ms=prep_ms, scan_ms=scan_ms, x=x)
+
+
+def bench_decode(steps):
+    import torch
+
+    import attention_fwd_amd as pa
+    import pathgen
+
+    c = pathgen.WORKLOADS[DEC_WORKLOAD]
+    B, H, n, d = c["B"], c["H"], c["n"], c["d"]
+    x = pathgen.decode_inputs(B, H, n, d, steps=steps, dtype=c["dtype"], seed=0, clip=c["clip"], device="cuda")
+    out = torch.empty((B, H, d), device="cuda", dtype=x["kcache"].dtype)
+    ws = torch.empty(max(pa.decode_workspace_size(B, H, n, d, x["kcache"].dtype), 16), device="cuda",
+                     dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    kc, vc = x["kcache"], x["vcache"]
+    for t in range(3):  # warm-up on the same cache (the update is an ordinary step)
+        pa.decode_step(kc, vc, n, x["q"][t], x["w"][t], x["beta"][t], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for t in range(steps):
+        evs[t][0].record(stream)
+        pa.decode_step(kc, vc, n, x["q"][t], x["w"][t], x["beta"][t], out=out, workspace=ws)
+        evs[t][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    nbytes = 3.0 * B * H * n * d * kc.element_size()
+    return dict(B=B, H=H, n=n, d=d, steps=steps, step_ms=step_ms, wall_s=wall, bytes=nbytes)
+
+
+def cpu_baseline(x, target_s):
+    """The fp64 oracle, as it stands, on whole heads of the forward workload."""
+    import oracle
+
+    B, H, L, d = x["q"].shape
+    G = B * H
+    flat = {k: (v.reshape(G, L, -1) if v.dim() == 4 else v.reshape(G, L)) for k, v in x.items() if v is not None}
+    threads = oracle.default_threads()
+
+    def run(nh):
+        sel = {k: v[:nh].cpu() for k, v in flat.items()}
+        t0 = time.perf_counter()
+        oracle.fwd(sel["q"], sel["k"], sel["v"], sel["w"], sel["beta"], nthreads=threads)
+        return time.perf_counter() - t0
+
+    nh = 1
+    t = run(nh)
+    if t < target_s:
+        nh = int(min(G, max(1, round(nh * target_s / max(t, 1e-3)))))
+        t = run(nh)
+    tflops = 4.0 * nh * L * L * d / t / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d heads of the B%d H%d L%d d%d workload, every row, %.1f s" % (nh, G, B, H, L, d, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline budget; 0 skips it")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the PaTH hot path here has no multi-GPU mode "
+              "(heads would shard with no communication); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_fwd_amd as pa
+
+    pa.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    log("forward: %s, %d warm-up + %d timed steps" % (FWD_WORKLOAD, args.warmup, args.steps))
+    f = bench_forward(args.steps, args.warmup)
+    log("forward: %.3f ms/step (prep %.3f ms, scan %.3f ms)" % (f["ms_per_step"], f["prep_ms"], f["scan_ms"]))
+    log("decode: %s, %d steps" % (DEC_WORKLOAD, args.decode_steps))
+    dres = bench_decode(args.decode_steps)
+    log("decode: %.3f ms/step" % dres["step_ms"])
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("cpu baseline: oracle, ~%.0f s" % args.cpu_seconds)
+        cpu = cpu_baseline(f["x"], args.cpu_seconds)
+        log("cpu baseline: %s" % cpu["sample"])
+
+    value = f["flops"] / (f["ms_per_step"] * 1e-3) / 1e12
+    scan_tflops = f["flops"] / (f["scan_ms"] * 1e-3) / 1e12
+    traffic = read_traffic()
+    dec_gbs = dres["bytes"] / (dres["step_ms"] * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(f["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": FWD_WORKLOAD, "B": f["B"], "H": f["H"], "L": f["L"], "d": f["d"], "causal": True,
+                   "decode_workload": DEC_WORKLOAD},
+        "roofline": {"bound": "mfma", "kernel": "path_fwd_kernel (scan)", "achieved": round(scan_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(scan_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "forward": {"ms_per_step": round(f["ms_per_step"], 4), "prep_ms": round(f["prep_ms"], 4),
+                    "scan_ms": round(f["scan_ms"], 4), "frac_of_peak_whole_pass": round(value / PEAK_BF16_TFLOPS, 4),
+                    "tokens_per_s": round(f["B"] * f["L"] / (f["ms_per_step"] * 1e-3)),
+                    "flop_per_step": f["flops"]},
+        "decode": {"ms_per_step": round(dres["step_ms"], 4), "GB_per_s": round(dec_gbs, 1),
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                   "tokens_per_s": round(dres["B"] / (dres["step_ms"] * 1e-3)), "bytes_per_step": dres["bytes"],
+                   "steps": dres["steps"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

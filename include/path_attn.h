@@ -1,0 +1,158 @@
+/*
+ * path_attn.h -- C ABI of the PaTH attention library for AMD MI355X (gfx950).
+ *
+ * PaTH attention (sources, by page title and section):
+ *   [TS]  "技術要約: PaTH Attention" (gist.science, Japanese technical summary of
+ *         arXiv 2505.16381), section 2 "手法": attention logit
+ *         k_j^T (prod_{s=j+1..i} H_s) q_i with H_s = I - beta_s w_s w_s^T and
+ *         beta_s = 2 sigmoid(.) in (0, 2); section 3 "効率的な学習と推論": UT-
+ *         transform form of a product of H's, a blockwise FlashAttention-style
+ *         algorithm (boundary-adjusted queries/keys, right-to-left scan over
+ *         key blocks), and decoding by updating cached keys in place with the
+ *         newest H_t; section 6 "限界": beta is clipped near 2 for bf16.
+ *   [IPX] "거리에서 경로로, PaTH Attention" (iplexlaw.co.kr), section 3
+ *         (softmax over the transformed scores, weighted sum of values) and
+ *         section 4 (PaTH-FoX: an additive, data-dependent forget gate).
+ *
+ * All functions are synchronous on the host: argument errors are reported
+ * before anything is enqueued.  Kernels run asynchronously on `stream`
+ * (a hipStream_t; NULL = the default stream) and results are valid once
+ * that stream's work has completed.  The library keeps no pointer after a
+ * call returns, allocates no device memory and holds no mutable global
+ * state; calls from several host threads are safe (calls that share output
+ * or workspace memory must be ordered by the caller).
+ *
+ * Layout: every tensor is contiguous and row-major.  Per-token tensors are
+ * [B, H, L, d] (B batches, H heads, L tokens, head dimension d); per-token
+ * scalars are [B, H, L].  Pointers are DEVICE pointers owned by the caller
+ * and must be 16-byte aligned.  d must be 64 (other head sizes return
+ * PATH_EUNSUPPORTED).  Any L >= 1 is accepted.
+ *
+ * Numerics: dtype selects the element type of q, k, v, w, the output and the
+ * caches.  beta, the log-forget gate, lse and all accumulation are fp32.
+ * PATH_DTYPE_F32 runs fp32 end to end (fp32 matrix-core instructions);
+ * PATH_DTYPE_BF16 feeds bf16 operands to the matrix cores and accumulates in
+ * fp32.  w is used as given (not re-normalised) and beta is not clipped; NaN
+ * or Inf inputs propagate and are not checked.
+ */
+#ifndef PATH_ATTN_H
+#define PATH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PATH_ABI_VERSION 1
+
+typedef enum {
+    PATH_OK = 0,
+    PATH_EINVAL = 1,        /* NULL pointer, bad size, misaligned, workspace too small, n > ncap */
+    PATH_EUNSUPPORTED = 2,  /* valid but not implemented (head dimension other than 64) */
+    PATH_EHIP = 3           /* the HIP runtime rejected a launch */
+} path_status_t;
+
+typedef enum {
+    PATH_DTYPE_F32 = 0,
+    PATH_DTYPE_BF16 = 1
+} path_dtype_t;
+
+/* Version of this ABI (PATH_ABI_VERSION). */
+int path_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *path_status_string(path_status_t status);
+
+/*
+ * Workspace bytes that path_attn_fwd needs for these sizes (0 if the sizes
+ * are invalid).  The caller allocates it on the device; its contents on
+ * entry do not matter and are garbage afterwards.
+ */
+size_t path_attn_fwd_workspace_size(int B, int H, int L, int d, path_dtype_t dtype);
+
+/*
+ * Causal PaTH attention forward ([TS] s.2 logit, [IPX] s.3 softmax and value
+ * sum, [TS] s.3 blockwise algorithm), with the optional PaTH-FoX bias
+ * ([IPX] s.4):
+ *
+ *   s_ij = scale * k_j^T (H_{j+1} H_{j+2} ... H_i) q_i  +  sum_{s=j+1..i} logf_s,
+ *          j <= i,  H_s = I - beta_s w_s w_s^T
+ *   out_i = sum_{j<=i} softmax_j(s_ij) v_j,   lse_i = log sum_{j<=i} exp(s_ij)
+ *
+ * q, k, v, w : [B, H, L, d], element type `dtype`           (read only)
+ * beta       : [B, H, L] fp32                                (read only)
+ * logf       : [B, H, L] fp32 log forget gate, or NULL for plain PaTH.
+ *              The bias is added after `scale`, and is 0 on the diagonal.
+ * out        : [B, H, L, d], element type `dtype`            (written; must not alias an input)
+ * lse        : [B, H, L] fp32 natural-log normaliser, or NULL
+ * scale      : multiplies the transformed dot product; <= 0 selects 1/sqrt(d)
+ * workspace  : device scratch of at least path_attn_fwd_workspace_size() bytes
+ *
+ * Returns PATH_OK, PATH_EINVAL, PATH_EUNSUPPORTED or PATH_EHIP.
+ */
+path_status_t path_attn_fwd(const void *q, const void *k, const void *v, const void *w, const float *beta,
+                            const float *logf, void *out, float *lse, int B, int H, int L, int d,
+                            path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
+ * The two stages of path_attn_fwd, for callers that schedule or time them
+ * separately (path_attn_fwd is exactly prep followed by scan on one stream).
+ *
+ * path_attn_fwd_prep: per 64-token block, the UT transform of the block's
+ *   transitions ([TS] s.3), the boundary-adjusted queries and keys, the
+ *   block's transition product and the causal attention inside the block.
+ *   Same arguments and errors as path_attn_fwd.  After it, rows of the first
+ *   block are final; other rows of out/lse hold intermediate values.
+ * path_attn_fwd_scan: the right-to-left scan over earlier key blocks with
+ *   online softmax ([TS] s.3), finishing out and lse.  `workspace` must hold
+ *   the results of a path_attn_fwd_prep call with the same sizes, dtype,
+ *   scale, out and lse, enqueued before it on the same stream (or otherwise
+ *   completed); has_logf must be non-zero iff that call had a logf.
+ */
+path_status_t path_attn_fwd_prep(const void *q, const void *k, const void *v, const void *w, const float *beta,
+                                 const float *logf, void *out, float *lse, int B, int H, int L, int d,
+                                 path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+path_status_t path_attn_fwd_scan(void *out, float *lse, int has_logf, int B, int H, int L, int d,
+                                 path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* Workspace bytes that path_decode_step needs (0 if the sizes are invalid). */
+size_t path_decode_workspace_size(int B, int H, int64_t n, int d, path_dtype_t dtype);
+
+/*
+ * One PaTH decode step ([TS] s.3, inference): the newest transition
+ * H_t = I - beta_t w_t w_t^T is applied IN PLACE to every cached key,
+ *
+ *   kcache[b,h,j,:] <- H_t kcache[b,h,j,:]      for j in [0, n)
+ *
+ * (rounded to `dtype`), so that no w/beta history is kept; then the single
+ * query q_t attends to the cache with softmax.  If k_new and v_new are both
+ * non-NULL they are stored at row n AFTER the update (the newest key has the
+ * empty product) and the query attends to n+1 rows; otherwise to n rows.
+ *
+ * kcache, vcache : [B, H, ncap, d] element type `dtype`; rows >= n (+1) untouched
+ * n              : rows in use, 0 <= n <= ncap (n + 1 <= ncap with k_new; at least one row must attend)
+ * q, w           : [B, H, d] element type `dtype`; beta: [B, H] fp32
+ * k_new, v_new   : [B, H, d] or both NULL
+ * out            : [B, H, d] element type `dtype`; lse: [B, H] fp32 or NULL
+ * scale          : <= 0 selects 1/sqrt(d)
+ * workspace      : at least path_decode_workspace_size(B, H, n (+1), d, dtype) bytes
+ *
+ * A cache row that went through steps j+1..t holds H_t ... H_{j+1} k_j; as
+ * every H is symmetric its dot product with q_t equals the forward logit
+ * k_j^T (H_{j+1} ... H_t) q_t.
+ */
+path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,
+                               const float *beta, const void *k_new, const void *v_new, void *out, float *lse,
+                               int B, int H, int d, path_dtype_t dtype, float scale, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PATH_ATTN_H */

@@ -1,0 +1,117 @@
+"""The C-ABI library without a GPU: it loads, exports what the header declares,
+sizes workspaces, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_fwd_amd as pa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "path_attn.h")
+BF, F32 = pa.PATH_DTYPE_BF16, pa.PATH_DTYPE_F32
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(path_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pa.lib()
+    names = declared_functions()
+    assert {"path_attn_fwd", "path_decode_step", "path_attn_fwd_workspace_size", "path_decode_workspace_size",
+            "path_status_string", "path_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), "missing export " + n
+
+
+def test_version_and_status_strings():
+    lib = pa.lib()
+    assert lib.path_abi_version() == 1
+    for s in range(4):
+        assert lib.path_status_string(s)
+    assert lib.path_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes():
+    lib = pa.lib()
+    assert lib.path_attn_fwd_workspace_size(1, 1, 64, 64, BF) > 0
+    assert lib.path_attn_fwd_workspace_size(0, 1, 64, 64, BF) == 0
+    assert lib.path_attn_fwd_workspace_size(1, 1, 0, 64, BF) == 0
+    assert lib.path_attn_fwd_workspace_size(1, 1, 64, 128, BF) == 0   # unsupported head size
+    assert lib.path_attn_fwd_workspace_size(1, 1, 64, 64, 7) == 0     # bad dtype
+    a = lib.path_attn_fwd_workspace_size(2, 3, 65, 64, BF)
+    b = lib.path_attn_fwd_workspace_size(2, 3, 128, 64, BF)
+    assert a == b  # both round up to two 64-token blocks
+    assert lib.path_attn_fwd_workspace_size(2, 3, 128, 64, F32) > b
+    assert lib.path_decode_workspace_size(16, 32, 32768, 64, BF) > 0
+    assert lib.path_decode_workspace_size(16, 32, 0, 64, BF) == 0
+
+
+# Fake device addresses: the library must reject these calls before any HIP call.
+A = 1 << 20
+
+
+def P(i):
+    return ctypes.c_void_p(A * (i + 1))
+
+
+def fwd_call(**over):
+    args = dict(q=P(0), k=P(1), v=P(2), w=P(3), beta=P(4), logf=None, out=P(5), lse=None, B=1, H=1, L=64, d=64,
+                dtype=BF, scale=0.0, ws=P(6), wsb=1 << 40, stream=None)
+    args.update(over)
+    return pa.lib().path_attn_fwd(args["q"], args["k"], args["v"], args["w"], args["beta"], args["logf"],
+                                  args["out"], args["lse"], args["B"], args["H"], args["L"], args["d"],
+                                  args["dtype"], args["scale"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), pa.PATH_EINVAL),
+    (dict(out=None), pa.PATH_EINVAL),
+    (dict(ws=None), pa.PATH_EINVAL),
+    (dict(beta=None), pa.PATH_EINVAL),
+    (dict(B=0), pa.PATH_EINVAL),
+    (dict(H=-1), pa.PATH_EINVAL),
+    (dict(L=0), pa.PATH_EINVAL),
+    (dict(d=128), pa.PATH_EUNSUPPORTED),
+    (dict(d=0), pa.PATH_EINVAL),
+    (dict(dtype=5), pa.PATH_EINVAL),
+    (dict(wsb=16), pa.PATH_EINVAL),
+    (dict(q=ctypes.c_void_p(A + 8)), pa.PATH_EINVAL),          # misaligned
+    (dict(lse=ctypes.c_void_p(A * 9 + 2)), pa.PATH_EINVAL),    # misaligned fp32 array
+    (dict(out=P(0)), pa.PATH_EINVAL),                          # out aliases q
+    (dict(ws=P(2)), pa.PATH_EINVAL),                           # workspace overlaps v
+    (dict(scale=float("nan")), pa.PATH_EINVAL),
+])
+def test_fwd_rejects_bad_arguments(over, status):
+    assert fwd_call(**over) == status
+
+
+def dec_call(**over):
+    args = dict(kc=P(0), vc=ctypes.c_void_p(A * 40), n=100, ncap=100, q=P(80), w=P(81), beta=P(82), kn=None, vn=None,
+                out=P(83), lse=None, B=1, H=1, d=64, dtype=BF, scale=0.0, ws=P(84), wsb=1 << 30, stream=None)
+    args.update(over)
+    return pa.lib().path_decode_step(args["kc"], args["vc"], args["n"], args["ncap"], args["q"], args["w"],
+                                     args["beta"], args["kn"], args["vn"], args["out"], args["lse"], args["B"],
+                                     args["H"], args["d"], args["dtype"], args["scale"], args["ws"], args["wsb"],
+                                     args["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(n=101), pa.PATH_EINVAL),                             # n > ncap
+    (dict(n=-1), pa.PATH_EINVAL),
+    (dict(n=0), pa.PATH_EINVAL),                               # nothing to attend to
+    (dict(kn=P(90)), pa.PATH_EINVAL),                          # k_new without v_new
+    (dict(kn=P(90), vn=P(91)), pa.PATH_EINVAL),                # no room for the new row
+    (dict(kc=None), pa.PATH_EINVAL),
+    (dict(d=32), pa.PATH_EUNSUPPORTED),
+    (dict(wsb=8), pa.PATH_EINVAL),
+    (dict(q=ctypes.c_void_p(A * 81 + 4)), pa.PATH_EINVAL),
+    (dict(vc=P(0)), pa.PATH_EINVAL),                           # caches alias
+    (dict(out=P(0)), pa.PATH_EINVAL),                          # out inside the key cache
+    (dict(dtype=3), pa.PATH_EINVAL),
+])
+def test_decode_rejects_bad_arguments(over, status):
+    assert dec_call(**over) == status

@@ -1,0 +1,158 @@
+"""GPU parity of path_decode_step against the fp64 oracle (through the C ABI).
+
+Checks: the in-place cache update (fp32: 1e-5; bf16: within one bf16 ulp plus
+the fp32 forward-error bound of evaluating k - beta (w.k) w, against the
+oracle's fp64 update of the same pre-step cache), the output
+(1e-4 fp32 / 2e-2 bf16 max-abs, and 2e-2 relative to max |o| for bf16), the
+log-sum-exp (1e-4 fp32 / 1e-2 bf16), and decode reproducing the forward pass.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_fwd_amd as pa
+import oracle
+import pathgen
+from parity_util import bf16_ulp_distance, cache_update_bound, max_abs, say, to_np
+
+gpu = pytest.mark.gpu
+
+
+def step_and_check(kc, vc, n, q, w, beta, kn=None, vn=None, heads=None, dtype="bf16", scale=None):
+    B, H, ncap, d = kc.shape
+    G = B * H
+    heads = list(range(G)) if heads is None else heads
+    kc_before = kc.reshape(G, ncap, d)[heads].cpu()
+    vc_before = vc.reshape(G, ncap, d)[heads].cpu()
+    out, lse = pa.decode_step(kc, vc, n, q, w, beta, k_new=kn, v_new=vn, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    qs, ws = q.reshape(G, d)[heads].cpu(), w.reshape(G, d)[heads].cpu()
+    bs = beta.reshape(G)[heads].cpu()
+    kns = kn.reshape(G, d)[heads].cpu() if kn is not None else None
+    vns = vn.reshape(G, d)[heads].cpu() if vn is not None else None
+    rk, rv, ro, rl = oracle.decode(kc_before, vc_before, n, qs, ws, bs, k_new=kns, v_new=vns, scale=scale)
+    rows = n + (1 if kn is not None else 0)
+    kc_after = kc.reshape(G, ncap, d)[heads].cpu()
+    og = to_np(out.reshape(G, d)[heads])
+    lg = to_np(lse.reshape(G)[heads])
+    eo, el = max_abs(og, ro), max_abs(lg, rl)
+    if dtype == "f32":
+        ek = max_abs(to_np(kc_after[:, :rows]), rk[:, :rows])
+        say("  fp32 cache %.2e out %.2e lse %.2e" % (ek, eo, el))
+        assert ek <= 1e-5 and eo <= 1e-4 and el <= 1e-4
+    else:
+        kb = to_np(kc_before[:, :n])
+        bound = cache_update_bound(kb, to_np(ws), to_np(bs), rk[:, :n])
+        err = np.abs(to_np(kc_after[:, :n]) - rk[:, :n])
+        ratio = float((err / bound).max()) if n else 0.0
+        ulp = bf16_ulp_distance(kc_after[:, :n], torch.from_numpy(rk[:, :n]).float().to(torch.bfloat16))
+        rel = eo / max(float(np.abs(ro).max()), 1e-30)
+        say("  bf16 cache err/bound %.3f (max ulp distance %d) out %.2e (rel %.2e) lse %.2e" % (ratio, ulp, eo, rel, el))
+        assert ratio <= 1.0, "cache update outside the fp32-evaluation + 1 ulp bound (ratio %.3f)" % ratio
+        if kn is not None:
+            assert torch.equal(kc_after[:, n], kns.to(kc_after.dtype)), "appended key must be stored as given"
+        assert eo <= 2e-2 and rel <= 2e-2 and el <= 1e-2
+    # rows past the attended range are untouched
+    assert torch.equal(kc_after[:, rows:], kc_before[:, rows:])
+    assert torch.equal(vc.reshape(G, ncap, d)[heads].cpu()[:, rows:], vc_before[:, rows:])
+    return out, lse
+
+
+@gpu
+@pytest.mark.parametrize("n", [1, 7, 128, 1000, 4097])
+@pytest.mark.parametrize("append", [False, True], ids=["cache", "append"])
+def test_decode_fp32(n, append):
+    B, H, d = 2, 3, 64
+    say("case decode fp32 n=%d append=%s" % (n, append))
+    x = pathgen.decode_inputs(B, H, n, d, steps=1, dtype="f32", seed=n, device="cuda", rowcap=n + 1)
+    kn = vn = None
+    if append:
+        kn = torch.randn(B, H, d, device="cuda")
+        vn = torch.randn(B, H, d, device="cuda")
+    step_and_check(x["kcache"], x["vcache"], n, x["q"][0], x["w"][0], x["beta"][0], kn, vn, dtype="f32")
+
+
+@gpu
+@pytest.mark.parametrize("n,append", [(4096, False), (333, True), (70000, False)])
+def test_decode_bf16(n, append):
+    B, H, d = 2, 4, 64
+    say("case decode bf16 n=%d append=%s" % (n, append))
+    x = pathgen.decode_inputs(B, H, n, d, steps=3, dtype="bf16", seed=11, clip=1.98, device="cuda",
+                              rowcap=n + 3)
+    for t in range(3):
+        kn = vn = None
+        rows = n + (t if append else 0)
+        if append:
+            kn = torch.randn(B, H, d, device="cuda").to(torch.bfloat16)
+            vn = torch.randn(B, H, d, device="cuda").to(torch.bfloat16)
+        step_and_check(x["kcache"], x["vcache"], rows, x["q"][t], x["w"][t], x["beta"][t], kn, vn)
+
+
+@gpu
+def test_decode_bf16_peaky():
+    """q scaled x8 so attention concentrates and |o| = O(1): a skipped or wrong update shows clearly."""
+    B, H, n, d = 2, 2, 4096, 64
+    say("case decode bf16 peaky")
+    x = pathgen.decode_inputs(B, H, n, d, steps=1, dtype="bf16", seed=12, clip=1.98, device="cuda")
+    q = (x["q"][0].float() * 8).to(torch.bfloat16)
+    out, _ = step_and_check(x["kcache"], x["vcache"], n, q, x["w"][0], x["beta"][0])
+    assert float(out.float().abs().max()) > 0.3
+
+
+@gpu
+def test_decode_workload_full_size():
+    """Full decode workload (B16 H32 n=32768 bf16), two steps, four heads checked."""
+    c = pathgen.WORKLOADS["decode_N32768_bf16"]
+    say("case decode full size")
+    x = pathgen.decode_inputs(c["B"], c["H"], c["n"], c["d"], steps=2, dtype="bf16", seed=0, clip=1.98, device="cuda")
+    G = c["B"] * c["H"]
+    for t in range(2):
+        step_and_check(x["kcache"], x["vcache"], c["n"], x["q"][t], x["w"][t], x["beta"][t], heads=[0, 5, 300, G - 1])
+
+
+@gpu
+def test_decode_reproduces_forward_fp32():
+    """Decoding token by token from an empty cache gives the forward pass's rows."""
+    B, H, T, d = 1, 2, 70, 64
+    say("case decode vs forward")
+    x = pathgen.fwd_inputs(B, H, T, d, "f32", seed=21, device="cuda")
+    fo, fl = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], return_lse=True)
+    ro, rl = oracle.fwd(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["w"].cpu(), x["beta"].cpu())
+    kc = torch.zeros(B, H, T, d, device="cuda")
+    vc = torch.zeros(B, H, T, d, device="cuda")
+    for t in range(T):
+        o, l = pa.decode_step(kc, vc, t, x["q"][:, :, t].contiguous(), x["w"][:, :, t].contiguous(),
+                              x["beta"][:, :, t].contiguous(), k_new=x["k"][:, :, t].contiguous(),
+                              v_new=x["v"][:, :, t].contiguous(), return_lse=True)
+        torch.cuda.synchronize()
+        assert max_abs(to_np(o), ro[:, :, t]) <= 1e-4, "step %d vs oracle" % t
+        assert max_abs(to_np(l), rl[:, :, t]) <= 1e-4
+        assert max_abs(to_np(o), to_np(fo[:, :, t])) <= 1e-4, "step %d vs forward kernel" % t
+
+
+@gpu
+def test_decode_deterministic():
+    B, H, n, d = 2, 3, 5000, 64
+    x = pathgen.decode_inputs(B, H, n, d, steps=1, dtype="bf16", seed=13, clip=1.98, device="cuda")
+    res = []
+    for _ in range(2):
+        kc, vc = x["kcache"].clone(), x["vcache"].clone()
+        o, l = pa.decode_step(kc, vc, n, x["q"][0], x["w"][0], x["beta"][0], return_lse=True)
+        torch.cuda.synchronize()
+        res.append((o, l, kc))
+    assert all(torch.equal(a, b) for a, b in zip(res[0], res[1]))
+
+
+@gpu
+def test_decode_checkpoint_resume():
+    """Eight steps in one go equal four steps, a host round-trip of the cache, then four more."""
+    B, H, n, d = 1, 2, 3000, 64
+    x = pathgen.decode_inputs(B, H, n, d, steps=8, dtype="bf16", seed=14, clip=1.98, device="cuda")
+    kc1, vc1 = x["kcache"].clone(), x["vcache"].clone()
+    outs1 = [pa.decode_step(kc1, vc1, n, x["q"][t], x["w"][t], x["beta"][t]) for t in range(8)]
+    kc2, vc2 = x["kcache"].clone(), x["vcache"].clone()
+    outs2 = [pa.decode_step(kc2, vc2, n, x["q"][t], x["w"][t], x["beta"][t]) for t in range(4)]
+    kc2, vc2 = kc2.cpu().cuda(), vc2.cpu().cuda()
+    outs2 += [pa.decode_step(kc2, vc2, n, x["q"][t], x["w"][t], x["beta"][t]) for t in range(4, 8)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(outs1, outs2)) and torch.equal(kc1, kc2)

@@ -1,0 +1,136 @@
+"""GPU parity of path_attn_fwd against the fp64 oracle (through the C ABI).
+
+Tolerances (max-abs, fp32 accumulation in both paths): 1e-4 for fp32 inputs,
+2e-2 for bf16 inputs, on the output and on the log-sum-exp.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_fwd_amd as pa
+import oracle
+import pathgen
+from parity_util import max_abs, say, to_np
+
+gpu = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def run_and_compare(B, H, L, d, dtype, fox, seed, rows=None, heads=None, clip=None, scale=None):
+    say("case B%d H%d L%d d%d %s fox=%s seed=%d" % (B, H, L, d, dtype, fox, seed))
+    if clip is None and dtype == "bf16":
+        clip = 1.98
+    x = pathgen.fwd_inputs(B, H, L, d, dtype, seed=seed, fox=fox, clip=clip, device="cuda")
+    out, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    G = B * H
+    flat = {k: (v.reshape(G, L, -1) if v is not None and v.dim() == 4 else (v.reshape(G, L) if v is not None else None))
+            for k, v in x.items()}
+    heads = list(range(G)) if heads is None else list(heads)
+    sel = {k: (v[heads].cpu() if v is not None else None) for k, v in flat.items()}
+    o_gpu = out.reshape(G, L, d)[heads].cpu()
+    l_gpu = lse.reshape(G, L)[heads].cpu()
+    tol = TOL[dtype]
+    if rows is None:
+        ro, rl = oracle.fwd(sel["q"], sel["k"], sel["v"], sel["w"], sel["beta"], sel["logf"], scale=scale)
+        eo, el = max_abs(to_np(o_gpu), ro), max_abs(to_np(l_gpu), rl)
+    else:
+        r = np.asarray(rows, dtype=np.int64)
+        ro, rl = oracle.fwd(sel["q"], sel["k"], sel["v"], sel["w"], sel["beta"], sel["logf"], scale=scale, rows=r)
+        og, lg = to_np(o_gpu), to_np(l_gpu)
+        eo = max_abs(og[r[:, 0], r[:, 1]], ro)
+        el = max_abs(lg[r[:, 0], r[:, 1]], rl)
+    say("  max-abs out %.3e  lse %.3e  (tol %.0e)" % (eo, el, tol))
+    assert eo <= tol, "output error %.3e > %.0e" % (eo, tol)
+    assert el <= tol, "lse error %.3e > %.0e" % (el, tol)
+    return out, lse
+
+
+FP32_CASES = [(1, 2, 64), (1, 1, 1), (1, 1, 2), (1, 2, 63), (1, 1, 65), (2, 1, 128), (1, 2, 200), (1, 1, 257),
+              (1, 2, 512), (1, 1, 700)]
+
+
+@gpu
+@pytest.mark.parametrize("B,H,L", FP32_CASES, ids=lambda v: str(v))
+@pytest.mark.parametrize("fox", [False, True], ids=["path", "fox"])
+def test_fwd_fp32(B, H, L, fox):
+    run_and_compare(B, H, L, 64, "f32", fox, seed=1000 + L)
+
+
+@gpu
+def test_fwd_fp32_tiny_workload():
+    """The tiny fp32 workload exactly as specified: B1 H2 L64 d64, scale 1/sqrt(d), seed 0, no clip."""
+    cfg = pathgen.WORKLOADS["tiny_fp32"]
+    run_and_compare(cfg["B"], cfg["H"], cfg["L"], cfg["d"], "f32", False, seed=0, clip=None, scale=0.125)
+
+
+@gpu
+@pytest.mark.parametrize("B,H,L", [(1, 2, 64), (2, 2, 200), (1, 2, 1000), (1, 1, 1), (1, 1, 333), (1, 1, 2048)],
+                         ids=lambda v: str(v))
+@pytest.mark.parametrize("fox", [False, True], ids=["path", "fox"])
+def test_fwd_bf16_small(B, H, L, fox):
+    run_and_compare(B, H, L, 64, "bf16", fox, seed=2000 + L)
+
+
+@gpu
+def test_fwd_bf16_beta_extremes():
+    """beta at the ends of its range: near 0 (plain attention) and exactly 2 (reflections) in fp32."""
+    B, H, L, d = 1, 2, 300, 64
+    for bval in (0.0, 2.0, 1.0):
+        x = pathgen.fwd_inputs(B, H, L, d, "f32", seed=7, device="cuda")
+        beta = torch.full((B, H, L), bval, device="cuda")
+        say("case beta=%g" % bval)
+        out, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], beta, return_lse=True)
+        ro, rl = oracle.fwd(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["w"].cpu(), beta.cpu())
+        assert max_abs(to_np(out), ro) <= 1e-4
+        assert max_abs(to_np(lse), rl) <= 1e-4
+
+
+@gpu
+@pytest.mark.parametrize("name", ["lm760m_L4096_bf16", "sweep_L1024_d64_bf16", "sweep_L2048_d64_bf16",
+                                  "sweep_L4096_d64_bf16"])
+def test_fwd_workload_full_heads(name):
+    """Full-size workload; two whole heads (first and last) compared row by row."""
+    c = pathgen.WORKLOADS[name]
+    G = c["B"] * c["H"]
+    run_and_compare(c["B"], c["H"], c["L"], c["d"], c["dtype"], c["fox"], seed=0, heads=[0, G - 1])
+
+
+@gpu
+@pytest.mark.parametrize("name", ["sweep_L8192_d64_bf16", "fox_L16384_bf16"])
+def test_fwd_workload_sampled_rows(name):
+    """Long workloads: 256 random rows of two heads plus the last 64 rows of each."""
+    c = pathgen.WORKLOADS[name]
+    G, L = c["B"] * c["H"], c["L"]
+    rng = np.random.default_rng(5)
+    heads = [int(rng.integers(G)), G - 1]
+    rows = [(int(rng.integers(2)), int(rng.integers(L))) for _ in range(256)]
+    rows += [(g, L - 1 - t) for g in (0, 1) for t in range(64)]
+    run_and_compare(c["B"], c["H"], L, c["d"], c["dtype"], c["fox"], seed=0, heads=heads, rows=rows)
+
+
+@gpu
+def test_fwd_deterministic_and_guarded():
+    """Two runs are bitwise equal; nothing is written outside out / lse."""
+    B, H, L, d = 2, 3, 777, 64
+    x = pathgen.fwd_inputs(B, H, L, d, "bf16", seed=3, fox=True, clip=1.98, device="cuda")
+    n = B * H * L * d
+    big = torch.full((n + 4096,), 7.0, device="cuda", dtype=torch.bfloat16)
+    bigl = torch.full((B * H * L + 1024,), 7.0, device="cuda")
+    outs = []
+    for _ in range(2):
+        out = big[:n].view(B, H, L, d)
+        lse = bigl[:B * H * L].view(B, H, L)
+        pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out=out, lse=lse)
+        torch.cuda.synchronize()
+        outs.append((out.clone(), lse.clone()))
+        assert torch.all(big[n:] == 7.0) and torch.all(bigl[B * H * L:] == 7.0), "write past the end"
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@gpu
+def test_fwd_rejects_bad_arguments_on_device():
+    x = pathgen.fwd_inputs(1, 1, 64, 64, "bf16", device="cuda")
+    with pytest.raises(pa.PathError):
+        pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], workspace=torch.empty(16, device="cuda",
+                                                                                  dtype=torch.uint8))
