@@ -35,14 +35,16 @@ template <typename S>
 struct PrepCfg {
     static constexpr bool kBf = sizeof(S) == 2;
     static constexpr int SP = 64 + 16 / (int)sizeof(S);  // padded LDS row stride, elements
-    static constexpr int MAT = 64 * SP;
-    // matrix slots; bf16 keeps transposed copies of W and A (fp32 has no room
-    // for them in 160 KiB of LDS and reads them with a stride instead).  During
-    // the triangular solve G (fp32) lives in the UT/RT slots and the solver's
-    // columns in the A/Z slots, which are only written after the solve.
-    enum { W = 0, Q, K, X, Y, UT, RT, A, Z, AUP, WT };
-    static constexpr int NMAT = kBf ? 11 : 9;
-    static constexpr int GSTRIDE = 68;  // fp32 row stride of G in the solve layout
+    static constexpr int MAT = 64 * SP;                  // elements of one 64 x 64 matrix
+    static constexpr int MATB = MAT * (int)sizeof(S);
+    static constexpr int GS = 68;                        // fp32 row stride of G and E in the solve
+    // W, X, Y live for the whole kernel (bf16 adds W^T; fp32 has no room for
+    // transposed copies and reads them with a stride instead).  A second
+    // region is reused: Q, K while the products with them run, then G and E
+    // for the triangular solve, then A, A^T (bf16) and V^T.
+    static constexpr int NFIX = kBf ? 4 : 3;
+    static constexpr int RB = 2 * 64 * GS * 4;
+    static_assert(RB >= (kBf ? 3 : 2) * MATB, "reuse region too small");
 };
 
 // Fragment of the matrix view `m` (element (row, k) at row*SP + k when KC, at
@@ -167,22 +169,48 @@ __device__ __forceinline__ void store_rows_t(S *dst, const f32x16 &c, int d0, in
     }
 }
 
+// c += A(m0.., k) * B where B's fragments come from two accumulator tiles
+// (rows = contraction index): k chunk kc is register half kc%2 of tile kc/2.
+template <typename S, bool AKC>
+__device__ __forceinline__ void tile_mma_breg(f32x16 &c, const S *A, int m0, const f32x16 *bt, int lane) {
+    const int h = lane >> 5, l = lane & 31;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+        auto a = lds_frag<S, AKC>(A, m0 + l, 16 * kc, h);
+        Elem<S>::mma(c, a, acc_frag<S>(bt[kc >> 1], kc & 1));
+    }
+}
+
+// c += A * B(n0.., k) where A's fragments come from two accumulator tiles.
+template <typename S, bool BKC>
+__device__ __forceinline__ void tile_mma_areg(f32x16 &c, const f32x16 *at, const S *B, int n0, int lane) {
+    const int h = lane >> 5, l = lane & 31;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+        auto b = lds_frag<S, BKC>(B, n0 + l, 16 * kc, h);
+        Elem<S>::mma(c, acc_frag<S>(at[kc >> 1], kc & 1), b);
+    }
+}
+
 template <typename S, int D, bool FOX>
-__global__ __launch_bounds__(256) void path_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
     static_assert(D == 64, "prep kernel is laid out for head dimension 64");
     typedef PrepCfg<S> C;
-    constexpr int SP = C::SP, MAT = C::MAT;
+    constexpr int SP = C::SP, MAT = C::MAT, GS = C::GS;
+    constexpr bool kBf = C::kBf;
     constexpr int CH = 16 / (int)sizeof(S);  // elements per 16-byte chunk
-    __shared__ __attribute__((aligned(16))) S lds[C::NMAT * MAT];
-    __shared__ float sBeta[64], sCl[64];
+    constexpr int RCH = D / CH;              // chunks per row
+    constexpr int VPT = 64 * RCH / 256;      // chunks per thread per matrix
+    __shared__ __attribute__((aligned(16))) S fixed[C::NFIX * MAT];
+    __shared__ __attribute__((aligned(16))) char region[C::RB];
+    __shared__ float sBeta[64], sCl[64], sT[3][16][17];
 
-    S *sW = lds + C::W * MAT, *sQ = lds + C::Q * MAT, *sK = lds + C::K * MAT, *sA = lds + C::A * MAT;
-    S *sX = lds + C::X * MAT, *sY = lds + C::Y * MAT, *sUt = lds + C::UT * MAT, *sRt = lds + C::RT * MAT;
-    S *sZ = lds + C::Z * MAT;
-    S *sWt = C::kBf ? lds + C::WT * MAT : nullptr;
-    S *sAup = C::kBf ? lds + C::AUP * MAT : nullptr;
-    float *sG = (float *)sUt;  // alive only until the solve; UT/RT are written after it
-    float *sE = (float *)sA;   // solver columns, alive only during the solve
+    S *sW = fixed, *sX = fixed + MAT, *sY = fixed + 2 * MAT;
+    S *sWt = kBf ? fixed + 3 * MAT : nullptr;
+    S *sQ = (S *)region, *sK = (S *)region + MAT;                    // phases 1-2
+    float *sG = (float *)region, *sE = (float *)region + 64 * GS;     // phase 3
+    S *sA = (S *)region, *sAup = kBf ? (S *)region + MAT : nullptr;  // phase 4
+    S *sVt = (S *)region + (kBf ? 2 : 1) * MAT;
 
     const int L = a.L;
     const FwdLayout lay = fwd_layout(a.B, a.H, L, D, sizeof(S));
@@ -193,21 +221,26 @@ __global__ __launch_bounds__(256) void path_prep_kernel(PrepArgs a) {
     const int nvalid = min(kBlk, L - (int)row0);
     const int64_t tok0 = bh * L + row0;  // first token of the block in [B*H, L]
 
-    // ---- 1. stage W, Q, K (zero rows past L), beta, and the forget-gate prefix
+    // ---- 1. stage W, Q, K in LDS and V in registers (zero rows past L), beta, forget-gate prefix
+    u32x4 vreg[VPT];
     {
-        const S *gq = (const S *)a.q + tok0 * D, *gk = (const S *)a.k + tok0 * D, *gw = (const S *)a.w + tok0 * D;
-        for (int idx = tid; idx < 64 * (D / CH); idx += 256) {
-            const int r = idx / (D / CH), cc = idx % (D / CH);
-            u32x4 vq = {0, 0, 0, 0}, vk = vq, vw = vq;
+        const S *gq = (const S *)a.q + tok0 * D, *gk = (const S *)a.k + tok0 * D;
+        const S *gw = (const S *)a.w + tok0 * D, *gv = (const S *)a.v + tok0 * D;
+#pragma unroll
+        for (int s = 0; s < VPT; ++s) {
+            const int idx = tid + 256 * s, r = idx / RCH, cc = idx % RCH;
+            u32x4 vq = {0, 0, 0, 0}, vk = vq, vw = vq, vv = vq;
             if (r < nvalid) {
                 vq = *(const u32x4 *)(gq + r * D + cc * CH);
                 vk = *(const u32x4 *)(gk + r * D + cc * CH);
                 vw = *(const u32x4 *)(gw + r * D + cc * CH);
+                vv = *(const u32x4 *)(gv + r * D + cc * CH);
             }
+            vreg[s] = vv;
             *(u32x4 *)(sQ + r * SP + cc * CH) = vq;
             *(u32x4 *)(sK + r * SP + cc * CH) = vk;
             *(u32x4 *)(sW + r * SP + cc * CH) = vw;
-            if constexpr (C::kBf) {
+            if constexpr (kBf) {
                 const S *we = (const S *)&vw;
 #pragma unroll
                 for (int e = 0; e < CH; ++e) sWt[(cc * CH + e) * SP + r] = we[e];
@@ -234,88 +267,100 @@ __global__ __launch_bounds__(256) void path_prep_kernel(PrepArgs a) {
     __syncthreads();
 
     const int mt = (wv >> 1) * 32, nt = (wv & 1) * 32;  // this wave's tile of a 64x64 product
+    const int dt = wv & 1;                             // waves 2, 3: head-dimension tile
 
-    // ---- 2. G = W W^T (fp32, solve layout), X = tril(Q W^T), Y = strictly-upper(K W^T)
+    // ---- 2. G = W W^T, X = tril(Q W^T), Y = strictly_upper(K W^T); products with Q and K
+    f32x16 g = {};
+    f32x16 s[2], qi[2], ki[2];  // waves 0,1: diagonal logits K Q^T; waves 2,3: Q^T, K^T tiles
+    tile_mma<S, true, true>(g, sW, sW, mt, nt, D, lane);
     {
         f32x16 c = {};
-        tile_mma<S, true, true>(c, sW, sW, mt, nt, D, lane);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = mt + acc_row(r, h), col = nt + l32;
-            sG[row * C::GSTRIDE + (col & 3) * 16 + (col >> 2)] = c[r];
-        }
-        c = f32x16{};
         tile_mma<S, true, true>(c, sQ, sW, mt, nt, D, lane);
         store_tile<S, false>(sX, c, mt, nt, lane, [](int i, int cc, float v) { return cc <= i ? v : 0.f; });
         c = f32x16{};
         tile_mma<S, true, true>(c, sK, sW, mt, nt, D, lane);
         store_tile<S, false>(sY, c, mt, nt, lane, [](int j, int r, float v) { return r > j ? v : 0.f; });
     }
-    __syncthreads();
-
-    // ---- 3. A = (I + strictly_lower(D_b G))^-1 D_b by forward substitution.
-    // Column t of E = (I + strictly_lower(D_b G))^-1 solves
-    //   x_r = [r == t] - beta_r sum_{c<r} G_rc x_c,
-    // and A = E D_b.  Thread (t, p) owns column t and the rows c = p (mod 4) of
-    // it (its private slice of sE); a row's sum is 16 products per thread plus
-    // a 4-lane reduction.  Entries not yet computed are zero, so every row runs
-    // the same fixed-length loop.
-    {
-        const int p = lane & 3, t = 4 * (lane >> 2) + wv;
-        float *myE = sE + t * C::GSTRIDE + p * 16;
+    if (wv < 2) {
 #pragma unroll
-        for (int cc = 0; cc < 16; cc += 4) *(f32x4 *)(myE + cc) = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-        for (int r = 0; r < 64; ++r) {
-            const float *g = sG + r * C::GSTRIDE + p * 16;
-            float part = 0.f;
-#pragma unroll
-            for (int cc = 0; cc < 16; cc += 4) {
-                const f32x4 gv = *(const f32x4 *)(g + cc), ev = *(const f32x4 *)(myE + cc);
-                part += gv.x * ev.x + gv.y * ev.y + gv.z * ev.z + gv.w * ev.w;
-            }
-            part = sum4(part);
-            const float x = (r == t) ? 1.f : (r > t ? -sBeta[r] * part : 0.f);
-            if (p == (r & 3)) myE[r >> 2] = x;
+        for (int rt = 0; rt < 2; ++rt) {
+            s[rt] = f32x16{};
+            tile_mma<S, true, true>(s[rt], sK, sQ, 32 * rt, 32 * wv, D, lane);
         }
-        float xs[16];
+    } else {
 #pragma unroll
-        for (int cc = 0; cc < 16; cc += 4) {
-            const f32x4 ev = *(const f32x4 *)(myE + cc);
-            xs[cc] = ev.x; xs[cc + 1] = ev.y; xs[cc + 2] = ev.z; xs[cc + 3] = ev.w;
-        }
-        const float bt = sBeta[t];
-        __syncthreads();  // sE aliases sA
-#pragma unroll
-        for (int cc = 0; cc < 16; ++cc) {
-            const int c = 4 * cc + p;
-            const S v = Elem<S>::from_float(bt * xs[cc]);
-            sA[c * SP + t] = v;
-            if constexpr (C::kBf) sAup[t * SP + c] = v;
+        for (int t = 0; t < 2; ++t) {
+            load_tile_t<S>(qi[t], sQ, 32 * dt, 32 * t, lane);
+            load_tile_t<S>(ki[t], sK, 32 * dt, 32 * t, lane);
         }
     }
+    __syncthreads();  // Q, K dead: their space becomes G and E
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sG[(mt + acc_row(r, h)) * GS + nt + l32] = g[r];
     __syncthreads();
 
-    // ---- 4. UT = -(A W)^T, RT = -(A^T W)^T, Z = -tril(Q W^T) A
+    // ---- 3. E = (I + strictly_lower(D_b G))^-1 in 16 x 16 tiles, A = E D_b.
+    // (a) diagonal tiles, one per wave: column t, rows c = p (mod 4) per lane;
+    //     x_r = [r == t] - beta_r sum_{c<r} G_rc x_c (entries not yet known are 0)
     {
-        f32x16 c = {};
-        if constexpr (C::kBf)
-            tile_mma<S, true, true>(c, sA, sWt, mt, nt, 64, lane);
-        else
-            tile_mma<S, true, false>(c, sA, sW, mt, nt, 64, lane);
-        store_tile<S, true>(sUt, c, mt, nt, lane, [](int, int, float v) { return -v; });
-        c = f32x16{};
-        if constexpr (C::kBf)
-            tile_mma<S, true, true>(c, sAup, sWt, mt, nt, 64, lane);
-        else
-            tile_mma<S, false, false>(c, sA, sW, mt, nt, 64, lane);
-        store_tile<S, true>(sRt, c, mt, nt, lane, [](int, int, float v) { return -v; });
-        c = f32x16{};
-        if constexpr (C::kBf)
-            tile_mma<S, true, true>(c, sX, sAup, mt, nt, 64, lane);
-        else
-            tile_mma<S, true, false>(c, sX, sA, mt, nt, 64, lane);
-        store_tile<S, false>(sZ, c, mt, nt, lane, [](int, int, float v) { return -v; });
+        const int I16 = 16 * wv, t = lane >> 2, p = lane & 3;
+        float xs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float *gr = sG + (I16 + r) * GS + I16 + p;
+            float part = gr[0] * xs[0] + gr[4] * xs[1] + gr[8] * xs[2] + gr[12] * xs[3];
+            part = sum4(part);
+            const float x = (r == t) ? 1.f : (r > t ? -sBeta[I16 + r] * part : 0.f);
+            if (p == (r & 3)) xs[r >> 2] = x;
+        }
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) sE[(I16 + 4 * cc + p) * GS + I16 + t] = xs[cc];
+    }
+    __syncthreads();
+    // (b) off-diagonal tiles by distance from the diagonal:
+    //     E_IJ = -E_II T_IJ,  T_IJ = D_I sum_{K=J}^{I-1} G_IK E_KJ
+    for (int lev = 1; lev < 4; ++lev) {
+        const int nblk = 4 - lev;
+        for (int idx = tid; idx < nblk * 256; idx += 256) {
+            const int b = idx >> 8, r = (idx >> 4) & 15, t = idx & 15, I = lev + b;
+            const float *gr = sG + (16 * I + r) * GS;
+            float acc = 0.f;
+            for (int c = 16 * b; c < 16 * I; ++c) acc += gr[c] * sE[c * GS + 16 * b + t];
+            sT[b][r][t] = sBeta[16 * I + r] * acc;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < nblk * 256; idx += 256) {
+            const int b = idx >> 8, r = (idx >> 4) & 15, t = idx & 15, I = lev + b;
+            const float *er = sE + (16 * I + r) * GS + 16 * I;
+            float acc = 0.f;
+            for (int c = 0; c <= r; ++c) acc += er[c] * sT[b][c][t];
+            sE[(16 * I + r) * GS + 16 * b + t] = -acc;
+        }
+        __syncthreads();
+    }
+    {
+        // A = E D_b (lower triangle only; E's upper tiles were never written)
+        const int r = tid >> 2, c0 = (tid & 3) * 16;
+        float av[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int c = c0 + e;
+            av[e] = c <= r ? sE[r * GS + c] * sBeta[c] : 0.f;
+        }
+        __syncthreads();  // E and G are dead: their space becomes A, A^T, V^T
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const S v = Elem<S>::from_float(av[e]);
+            sA[r * SP + c0 + e] = v;
+            if constexpr (kBf) sAup[(c0 + e) * SP + r] = v;
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < VPT; ++s2) {
+            const int idx = tid + 256 * s2, vr = idx / RCH, cc = idx % RCH;
+            const S *ve = (const S *)&vreg[s2];
+#pragma unroll
+            for (int e = 0; e < CH; ++e) sVt[(cc * CH + e) * SP + vr] = ve[e];
+        }
     }
     __syncthreads();
 
@@ -324,16 +369,23 @@ __global__ __launch_bounds__(256) void path_prep_kernel(PrepArgs a) {
     constexpr int KCH = D / 16;  // k chunks over the head dimension
 
     if (wv < 2) {
-        // ---- 5a. diagonal block: S^T = K Q^T + Y Z^T (Z already negated), causal softmax, O^T = V^T P^T
-        const int ct = wv;                 // query column tile
-        const int i = 32 * ct + l32;       // query row in the block
-        f32x16 s[2];
+        // ---- 4a. diagonal block, query column tile ct: Z^T = A^T X^T (Z = tril(Q W^T) A),
+        //      S^T = K Q^T - Y Z^T, causal softmax down columns, O^T = V^T P^T
+        const int ct = wv;
+        const int i = 32 * ct + l32;  // query row in the block
+        f32x16 zt[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            s[rt] = f32x16{};
-            tile_mma<S, true, true>(s[rt], sK, sQ, 32 * rt, 32 * ct, D, lane);
-            tile_mma<S, true, true>(s[rt], sY, sZ, 32 * rt, 32 * ct, 64, lane);
+            zt[rt] = f32x16{};
+            if constexpr (kBf)
+                tile_mma<S, true, true>(zt[rt], sAup, sX, 32 * rt, 32 * ct, 64, lane);
+            else
+                tile_mma<S, false, true>(zt[rt], sA, sX, 32 * rt, 32 * ct, 64, lane);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) zt[rt][r] = -zt[rt][r];
         }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) tile_mma_breg<S, true>(s[rt], sY, 32 * rt, zt, lane);
         const float c2 = a.scale * kLog2e;
         const float cli = FOX ? sCl[i] : 0.f;
         float mx = -INFINITY;
@@ -359,26 +411,18 @@ __global__ __launch_bounds__(256) void path_prep_kernel(PrepArgs a) {
                 sum += p;
             }
         sum = other_half_sum(sum);
-        // V^T fragments: row d = 32 dt + l32, k = key
-        const S *gv = (const S *)a.v + tok0 * D;
         f32x16 o[D / 32];
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+        for (int d2 = 0; d2 < D / 32; ++d2) o[d2] = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             auto pf = acc_frag<S>(s[kc >> 1], kc & 1);
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int key = 16 * kc + frag_k(e, h);
-                    x[e] = key < nvalid ? Elem<S>::to_f32(gv[(int64_t)key * D + 32 * dt + l32]) : 0.f;
-                }
-                auto vf = Elem<S>::from_f32(x);
-                Elem<S>::mma(o[dt], vf, pf);
-                if (dt == wv) {  // each of the two waves stores half of the V^T record
-                    S *dst = recV + ((int64_t)(dt * 4 + kc) * 64 + lane) * 8;
+            for (int d2 = 0; d2 < D / 32; ++d2) {
+                auto vf = lds_frag<S, true>(sVt, 32 * d2 + l32, 16 * kc, h);
+                Elem<S>::mma(o[d2], vf, pf);
+                if (d2 == wv) {  // each of the two waves stores half of the V^T record
+                    S *dst = recV + ((int64_t)(d2 * 4 + kc) * 64 + lane) * 8;
                     *(typename Elem<S>::Frag *)dst = vf;
                 }
             }
@@ -392,38 +436,47 @@ __global__ __launch_bounds__(256) void path_prep_kernel(PrepArgs a) {
             const float inv = 1.f / sum;
             S *go = (S *)a.out + tok0 * D;
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) store_rows_t<S, D>(go, o[dt], 32 * dt, i, inv, lane);
+            for (int d2 = 0; d2 < D / 32; ++d2) store_rows_t<S, D>(go, o[d2], 32 * d2, i, inv, lane);
             if (h == 0 && a.lse) a.lse[tok0 + i] = (mx + __log2f(sum)) * kLn2;
         }
     } else {
-        // ---- 5b. key-block record (khat, -M) and qhat
-        const int half = wv - 2;
-        // khat^T = K^T + RT Y^T  (RT holds -(A^T W)^T): tiles (dt, jt = half)
+        // ---- 4b. head-dimension tile dt: -U = -A W and -R = -A^T W (rows = block
+        //      token, cols = d), then qhat^T = Q^T - U^T X^T, khat^T = K^T - R^T Y^T
+        //      and (-M)^T = -W^T U, each using those accumulators as operands.
+        f32x16 nu[2], nr[2];
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            f32x16 c;
-            load_tile_t<S>(c, sK, 32 * dt, 32 * half, lane);
-            tile_mma<S, true, true>(c, sRt, sY, 32 * dt, 32 * half, 64, lane);
-            store_frags<S>(recK, c, half * KCH + 2 * dt, lane);
-        }
-        // (-M)^T = W^T UT^T: tiles (rt over d2, ct = half over d1); fragments of -M with row d1
+        for (int rt = 0; rt < 2; ++rt) {
+            nu[rt] = f32x16{};
+            nr[rt] = f32x16{};
+            if constexpr (kBf) {
+                tile_mma<S, true, true>(nu[rt], sA, sWt, 32 * rt, 32 * dt, 64, lane);
+                tile_mma<S, true, true>(nr[rt], sAup, sWt, 32 * rt, 32 * dt, 64, lane);
+            } else {
+                tile_mma<S, true, false>(nu[rt], sA, sW, 32 * rt, 32 * dt, 64, lane);
+                tile_mma<S, false, false>(nr[rt], sA, sW, 32 * rt, 32 * dt, 64, lane);
+            }
 #pragma unroll
-        for (int rt = 0; rt < D / 32; ++rt) {
-            f32x16 c = {};
-            if constexpr (C::kBf)
-                tile_mma<S, true, true>(c, sWt, sUt, 32 * rt, 32 * half, 64, lane);
-            else
-                tile_mma<S, false, true>(c, sW, sUt, 32 * rt, 32 * half, 64, lane);
-            store_frags<S>(recM, c, half * KCH + 2 * rt, lane);
+            for (int r = 0; r < 16; ++r) {
+                nu[rt][r] = -nu[rt][r];
+                nr[rt][r] = -nr[rt][r];
+            }
         }
-        // qhat^T = Q^T + UT X^T: tiles (dt, it = half)
         S *gqh = (S *)((char *)a.ws + lay.off_qhat) + (bh * lay.lp + row0) * D;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            f32x16 c;
-            load_tile_t<S>(c, sQ, 32 * dt, 32 * half, lane);
-            tile_mma<S, true, true>(c, sUt, sX, 32 * dt, 32 * half, 64, lane);
-            store_rows_t<S, D>(gqh, c, 32 * dt, 32 * half + l32, 1.f, lane);
+        for (int t = 0; t < 2; ++t) {
+            tile_mma_areg<S, true>(qi[t], nu, sX, 32 * t, lane);
+            store_rows_t<S, D>(gqh, qi[t], 32 * dt, 32 * t + l32, 1.f, lane);
+            tile_mma_areg<S, true>(ki[t], nr, sY, 32 * t, lane);
+            store_frags<S>(recK, ki[t], t * KCH + 2 * dt, lane);
+        }
+#pragma unroll
+        for (int rt2 = 0; rt2 < 2; ++rt2) {
+            f32x16 c = {};
+            if constexpr (kBf)
+                tile_mma_breg<S, true>(c, sWt, 32 * rt2, nu, lane);
+            else
+                tile_mma_breg<S, false>(c, sW, 32 * rt2, nu, lane);
+            store_frags<S>(recM, c, dt * KCH + 2 * rt2, lane);
         }
     }
 }
