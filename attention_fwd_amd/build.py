@@ -11,25 +11,42 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpath_attn.so")
 SOURCES = ["path_abi.cpp", "path_prep.hip", "path_fwd.hip", "path_decode.hip"]
 
-FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+COMPILE_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU instructions are kept out of all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the softmax and the query
+    # update read them every step, and AGPR copies would double that traffic
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp] + srcs
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=900)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l and "not a recognized feature" not in l)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the shared library."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    cmds, objs = [], []
+    for s in SOURCES:
+        obj = os.path.join(objdir, s + ".o")
+        objs.append(obj)
+        cmds.append([hipcc] + COMPILE_FLAGS + inc + ["-c", os.path.join(CSRC, s), "-o", obj])
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
     return LIB
 

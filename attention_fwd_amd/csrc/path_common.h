@@ -40,12 +40,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// Round-to-nearest-even fp32 -> two packed bf16 (v_cvt_pk_bf16_f32 on gfx950).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> two packed bf16 (one v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    bf16x2 r;
-    r.x = (__bf16)lo;
-    r.y = (__bf16)hi;
-    return __builtin_bit_cast(uint32_t, r);
+    const f32x2 x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
 __device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)(pack_bf16(x, 0.f) & 0xffffu); }

@@ -30,8 +30,41 @@
 namespace path {
 namespace {
 
+// Four consecutive elements (8 bytes of bf16 / 16 bytes of fp32) as fp32.
+template <typename S>
+__device__ __forceinline__ void load4(const S *p, float *x) {
+    if constexpr (sizeof(S) == 2) {
+        const u32x2 u = *(const u32x2 *)p;
+        x[0] = bf16_to_f32(u.x & 0xffff);
+        x[1] = bf16_to_f32(u.x >> 16);
+        x[2] = bf16_to_f32(u.y & 0xffff);
+        x[3] = bf16_to_f32(u.y >> 16);
+    } else {
+        const f32x4 v = *(const f32x4 *)p;
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    }
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy one key-block record (REC elements, 16-byte chunks spread over the
+// workgroup) and, with the forget gate, its 64 tail sums from global memory
+// straight into LDS (global_load_lds: lane l of a wave lands at the wave's
+// LDS base + 16 l).  Completion is tracked by vmcnt.
+template <typename S, int REC, int NLD, bool FOX>
+__device__ __forceinline__ void issue_record(const S *src, const float *tail, S *dst, float *dtail, int wv, int lane) {
+    constexpr int VEC = 16 / (int)sizeof(S);
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+        const int chunk = 256 * t + 64 * wv;  // first 16-byte chunk of this wave
+        __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)(chunk + lane) * VEC),
+                                         (lds_void *)(dst + chunk * VEC), 16, 0, 0);
+    }
+    if (FOX && wv == 0) __builtin_amdgcn_global_load_lds((const void *)(tail + lane), (lds_void *)dtail, 4, 0, 0);
+}
+
 template <typename S, int D, bool FOX>
-__global__ __launch_bounds__(256, 1) void path_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void path_fwd_kernel(FwdArgs a) {
     static_assert(D == 64, "forward kernel is laid out for head dimension 64");
     typedef Elem<S> E;
     typedef typename E::Frag Frag;
@@ -79,17 +112,25 @@ __global__ __launch_bounds__(256, 1) void path_fwd_kernel(FwdArgs a) {
         for (int ct = 0; ct < 2; ++ct) {
             const int i = 32 * ct + l32;
             const bool valid = (int64_t)I * kBlk + i < a.L;
+            const int io = valid ? i : 0;  // rows past L read row 0 of the block, then drop it
             m[ct] = md[i];
             const float ls = ld[i];
             lp[ct] = h == 0 ? ls : 0.f;
             off[ct] = FOX ? fq[i] : 0.f;
+            const float os = valid ? ls : 0.f;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int d = 32 * dt + acc_row(r, h);
-                    qt[dt][ct][r] = E::to_f32(qh[(int64_t)i * D + d]);
-                    o[dt][ct][r] = valid ? E::to_f32(od[(int64_t)i * D + d]) * ls : 0.f;
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d = 32 * dt + 8 * g4 + 4 * h;  // 4 contiguous rows of the tile
+                    float qv[4], ov[4];
+                    load4<S>(qh + (int64_t)i * D + d, qv);
+                    load4<S>(od + (int64_t)io * D + d, ov);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        qt[dt][ct][4 * g4 + e] = qv[e];
+                        o[dt][ct][4 * g4 + e] = ov[e] * os;
+                    }
                 }
         }
 #pragma unroll
@@ -98,108 +139,99 @@ __global__ __launch_bounds__(256, 1) void path_fwd_kernel(FwdArgs a) {
             for (int kc = 0; kc < KCH; ++kc) qb[ct][kc] = acc_frag<S>(qt[kc >> 1][ct], kc & 1);
     }
 
-    // ---- stage the first record
-    u32x4 pre[NLD];
-    float pre_tail = 0.f;
-    {
-        const u32x4 *src = (const u32x4 *)(recs + (int64_t)Jtop * REC);
-#pragma unroll
-        for (int t = 0; t < NLD; ++t) pre[t] = src[tid + 256 * t];
-        if (FOX && tid < kBlk) pre_tail = fk[(int64_t)Jtop * kBlk + tid];
-        u32x4 *dst = (u32x4 *)srec[0];
-#pragma unroll
-        for (int t = 0; t < NLD; ++t) dst[tid + 256 * t] = pre[t];
-        if (FOX && tid < kBlk) stail[0][tid] = pre_tail;
-    }
+    // ---- key-block records are copied global -> LDS by the DMA path
+    issue_record<S, REC, NLD, FOX>(recs + (int64_t)Jtop * REC, fk + (int64_t)Jtop * kBlk, srec[0], stail[0], wv, lane);
 
     const float c2 = a.scale * kLog2e;
+    constexpr float kTau = 8.f;  // running max is refreshed only when it grows by more than 2^8
     for (int J = Jtop; J >= 0; --J) {
         const int buf = (Jtop - J) & 1;
-        __syncthreads();
-        if (J > 0) {  // prefetch the next record into registers
-            const u32x4 *src = (const u32x4 *)(recs + (int64_t)(J - 1) * REC);
-#pragma unroll
-            for (int t = 0; t < NLD; ++t) pre[t] = src[tid + 256 * t];
-            if (FOX && tid < kBlk) pre_tail = fk[(int64_t)(J - 1) * kBlk + tid];
-        }
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of record J have landed
+        __syncthreads();                // ... and every other wave's
+        if (J > 0)
+            issue_record<S, REC, NLD, FOX>(recs + (int64_t)(J - 1) * REC, fk + (int64_t)(J - 1) * kBlk, srec[buf ^ 1],
+                                           stail[buf ^ 1], wv, lane);
         if (active && J < I) {
             const S *sk = srec[buf];
             const S *sv = srec[buf] + kBlk * D;
             const S *sm = srec[buf] + 2 * kBlk * D;
-            // S^T = khat_J qt^T
-            f32x16 s[2][2];
+            const float fbJ = FOX ? fb[J] : 0.f;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int hf = 0; hf < 2; ++hf) {  // keys 32 hf .. 32 hf + 31 of the block
+                // S^T = khat qt^T for this half
+                f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) s[rt][ct] = f32x16{};
+                for (int kc = 0; kc < KCH; ++kc) {
+                    const Frag af = *(const Frag *)(sk + ((hf * KCH + kc) * 64 + lane) * 8);
 #pragma unroll
-            for (int kc = 0; kc < KCH; ++kc)
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const Frag af = *(const Frag *)(sk + ((rt * KCH + kc) * 64 + lane) * 8);
-#pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) E::mma(s[rt][ct], af, qb[ct][kc]);
+                    for (int ct = 0; ct < 2; ++ct) E::mma(s[ct], af, qb[ct][kc]);
                 }
-            // qt <- P_J qt for the next (older) block
-            if (J > 0) {
+                if (hf == 0 && J > 0) {
+                    // qt <- P_J qt (uses the old qt fragments; independent of the softmax)
 #pragma unroll
-                for (int kc = 0; kc < KCH; ++kc)
+                    for (int kc = 0; kc < KCH; ++kc)
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt) {
+                            const Frag af = *(const Frag *)(sm + ((dt * KCH + kc) * 64 + lane) * 8);
+#pragma unroll
+                            for (int ct = 0; ct < 2; ++ct) E::mma(qt[dt][ct], af, qb[ct][kc]);
+                        }
+                }
+                // online softmax down each column (log2 units)
+                Frag pf[2][2];
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    float mx = -INFINITY;
+                    if (FOX) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            s[ct][r] = fmaf(s[ct][r], c2, stail[buf][32 * hf + acc_row(r, h)]);
+                            mx = fmaxf(mx, s[ct][r]);
+                        }
+                        mx = other_half_max(mx) + off[ct];
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ct][r]);
+                        mx = other_half_max(mx) * c2;
+                    }
+                    if (__any(mx > m[ct] + kTau)) {
+                        const float mnew = fmaxf(m[ct], mx);
+                        const float alpha = fast_exp2(m[ct] - mnew);
+                        m[ct] = mnew;
+                        lp[ct] *= alpha;
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) o[dt][ct][r] *= alpha;
+                    }
+                    float ps0 = 0.f, ps1 = 0.f;
+                    if (FOX) {
+                        const float sh = m[ct] - off[ct];
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) s[ct][r] = fast_exp2(s[ct][r] - sh);
+                    } else {
+                        const float nm = -m[ct];
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) s[ct][r] = fast_exp2(fmaf(s[ct][r], c2, nm));
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        ps0 += s[ct][r];
+                        ps1 += s[ct][r + 1];
+                    }
+                    lp[ct] += ps0 + ps1;
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) pf[ct][cc] = acc_frag<S>(s[ct], cc);
+                }
+                // O^T += V^T P^T over the half's two key chunks
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
-                        const Frag af = *(const Frag *)(sm + ((dt * KCH + kc) * 64 + lane) * 8);
+                        const Frag af = *(const Frag *)(sv + ((dt * 4 + 2 * hf + cc) * 64 + lane) * 8);
 #pragma unroll
-                        for (int ct = 0; ct < 2; ++ct) E::mma(qt[dt][ct], af, qb[ct][kc]);
+                        for (int ct = 0; ct < 2; ++ct) E::mma(o[dt][ct], af, pf[ct][cc]);
                     }
-            }
-            // online softmax down each column (log2 domain)
-            float fbJ = 0.f;
-            if (FOX) fbJ = fb[J];
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float x = s[rt][ct][r] * c2;
-                        if (FOX) x += stail[buf][32 * rt + acc_row(r, h)] + off[ct];
-                        s[rt][ct][r] = x;
-                        mx = fmaxf(mx, x);
-                    }
-                mx = other_half_max(mx);
-                const float mnew = fmaxf(m[ct], mx);
-                const float alpha = fast_exp2(m[ct] - mnew);
-                m[ct] = mnew;
-                float sum = 0.f;
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float p = fast_exp2(s[rt][ct][r] - mnew);
-                        s[rt][ct][r] = p;
-                        sum += p;
-                    }
-                lp[ct] = lp[ct] * alpha + sum;
-                if (__any(alpha != 1.f)) {
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) o[dt][ct][r] *= alpha;
-                }
-                if (FOX) off[ct] += fbJ;
-            }
-            // O^T += V_J^T P^T
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                Frag pf[2];
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) pf[ct] = acc_frag<S>(s[kc >> 1][ct], kc & 1);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const Frag af = *(const Frag *)(sv + ((dt * 4 + kc) * 64 + lane) * 8);
-#pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) E::mma(o[dt][ct], af, pf[ct]);
-                }
             }
             if (J > 0) {
 #pragma unroll
@@ -207,12 +239,10 @@ __global__ __launch_bounds__(256, 1) void path_fwd_kernel(FwdArgs a) {
 #pragma unroll
                     for (int kc = 0; kc < KCH; ++kc) qb[ct][kc] = acc_frag<S>(qt[kc >> 1][ct], kc & 1);
             }
-        }
-        if (J > 0) {
-            u32x4 *dst = (u32x4 *)srec[buf ^ 1];
-#pragma unroll
-            for (int t = 0; t < NLD; ++t) dst[tid + 256 * t] = pre[t];
-            if (FOX && tid < kBlk) stail[buf ^ 1][tid] = pre_tail;
+            if (FOX) {
+                off[0] += fbJ;
+                off[1] += fbJ;
+            }
         }
     }
 

@@ -124,7 +124,19 @@ __device__ __forceinline__ void load_tile_t(f32x16 &c, const S *mat, int m0, int
     constexpr int SP = PrepCfg<S>::SP;
     const int h = lane >> 5, col = n0 + (lane & 31);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) c[r] = Elem<S>::to_f32(mat[col * SP + m0 + acc_row(r, h)]);
+    for (int g = 0; g < 4; ++g) {
+        const S *p = mat + col * SP + m0 + 8 * g + 4 * h;
+        if constexpr (sizeof(S) == 2) {
+            const u32x2 u = *(const u32x2 *)p;
+            c[4 * g + 0] = bf16_to_f32(u.x & 0xffff);
+            c[4 * g + 1] = bf16_to_f32(u.x >> 16);
+            c[4 * g + 2] = bf16_to_f32(u.y & 0xffff);
+            c[4 * g + 3] = bf16_to_f32(u.y >> 16);
+        } else {
+            const f32x4 v = *(const f32x4 *)p;
+            c[4 * g + 0] = v.x; c[4 * g + 1] = v.y; c[4 * g + 2] = v.z; c[4 * g + 3] = v.w;
+        }
+    }
 }
 
 // Write the two fragments held in accumulator tile c (as the A operand whose
@@ -319,22 +331,38 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
     __syncthreads();
     // (b) off-diagonal tiles by distance from the diagonal:
     //     E_IJ = -E_II T_IJ,  T_IJ = D_I sum_{K=J}^{I-1} G_IK E_KJ
+#pragma unroll
     for (int lev = 1; lev < 4; ++lev) {
         const int nblk = 4 - lev;
-        for (int idx = tid; idx < nblk * 256; idx += 256) {
+#pragma unroll
+        for (int q = 0; q < nblk; ++q) {
+            const int idx = tid + 256 * q;
             const int b = idx >> 8, r = (idx >> 4) & 15, t = idx & 15, I = lev + b;
-            const float *gr = sG + (16 * I + r) * GS;
-            float acc = 0.f;
-            for (int c = 16 * b; c < 16 * I; ++c) acc += gr[c] * sE[c * GS + 16 * b + t];
-            sT[b][r][t] = sBeta[16 * I + r] * acc;
+            const float *gr = sG + (16 * I + r) * GS + 16 * b;
+            const float *ec = sE + 16 * b * GS + 16 * b + t;
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16 * lev; c += 4) {
+                const f32x4 gv = *(const f32x4 *)(gr + c);
+                acc0 += gv.x * ec[c * GS] + gv.y * ec[(c + 1) * GS];
+                acc1 += gv.z * ec[(c + 2) * GS] + gv.w * ec[(c + 3) * GS];
+            }
+            sT[b][r][t] = sBeta[16 * I + r] * (acc0 + acc1);
         }
         __syncthreads();
-        for (int idx = tid; idx < nblk * 256; idx += 256) {
+#pragma unroll
+        for (int q = 0; q < nblk; ++q) {
+            const int idx = tid + 256 * q;
             const int b = idx >> 8, r = (idx >> 4) & 15, t = idx & 15, I = lev + b;
-            const float *er = sE + (16 * I + r) * GS + 16 * I;
-            float acc = 0.f;
-            for (int c = 0; c <= r; ++c) acc += er[c] * sT[b][c][t];
-            sE[(16 * I + r) * GS + 16 * b + t] = -acc;
+            const float *er = sE + (16 * I + r) * GS + 16 * I;  // E_II row r: zero above the diagonal
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; c += 4) {
+                const f32x4 ev = *(const f32x4 *)(er + c);
+                acc0 += ev.x * sT[b][c][t] + ev.y * sT[b][c + 1][t];
+                acc1 += ev.z * sT[b][c + 2][t] + ev.w * sT[b][c + 3][t];
+            }
+            sE[(16 * I + r) * GS + 16 * b + t] = -(acc0 + acc1);
         }
         __syncthreads();
     }
