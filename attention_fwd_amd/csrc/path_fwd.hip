@@ -51,35 +51,58 @@ typedef __attribute__((address_space(3))) void lds_void;
 // workgroup) and, with the forget gate, its 64 tail sums from global memory
 // straight into LDS (global_load_lds: lane l of a wave lands at the wave's
 // LDS base + 16 l).  Completion is tracked by vmcnt.
-template <typename S, int REC, int NLD, bool FOX>
+template <typename S, int REC, int NLD, int NW, bool FOX>
 __device__ __forceinline__ void issue_record(const S *src, const float *tail, S *dst, float *dtail, int wv, int lane) {
     constexpr int VEC = 16 / (int)sizeof(S);
 #pragma unroll
     for (int t = 0; t < NLD; ++t) {
-        const int chunk = 256 * t + 64 * wv;  // first 16-byte chunk of this wave
+        const int chunk = 64 * NW * t + 64 * wv;  // first 16-byte chunk of this wave
         __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)(chunk + lane) * VEC),
                                          (lds_void *)(dst + chunk * VEC), 16, 0, 0);
     }
     if (FOX && wv == 0) __builtin_amdgcn_global_load_lds((const void *)(tail + lane), (lds_void *)dtail, 4, 0, 0);
 }
 
+// Waves per workgroup (= 64-query blocks sharing each key-block record) and
+// key-block records in flight (LDS buffers).
+#ifndef PATH_FWD_NW
+#define PATH_FWD_NW 4
+#endif
+#ifndef PATH_FWD_NBUF
+#define PATH_FWD_NBUF 2
+#endif
+// 32-query column tiles per wave (1 or 2); a workgroup covers NW * CT / 2 query blocks
+#ifndef PATH_FWD_CT
+#define PATH_FWD_CT 2
+#endif
+constexpr int kFwdWaves = PATH_FWD_NW;
+constexpr int kFwdBufs = PATH_FWD_NBUF;
+constexpr int kFwdCt = PATH_FWD_CT;
+constexpr int kFwdBlocksPerWg = kFwdWaves * kFwdCt / 2;
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and
+// lgkmcnt left at their maxima so they are not waited for).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
 template <typename S, int D, bool FOX>
-__global__ __launch_bounds__(256, 2) void path_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * kFwdWaves, 4 / kFwdCt) void path_fwd_kernel(FwdArgs a) {
     static_assert(D == 64, "forward kernel is laid out for head dimension 64");
     typedef Elem<S> E;
     typedef typename E::Frag Frag;
+    constexpr int NW = kFwdWaves, NB = kFwdBufs, NT = 64 * NW, CT = kFwdCt, QB = kFwdBlocksPerWg;
     constexpr int REC = 2 * kBlk * D + D * D;  // elements per key-block record
     constexpr int KCH = D / 16, DT = D / 32;
     constexpr int VEC = 16 / (int)sizeof(S);   // elements per 16-byte load
-    constexpr int NLD = REC / VEC / 256;       // 16-byte loads per thread per record
-    static_assert(REC % (VEC * 256) == 0, "record must split evenly over the workgroup");
-    __shared__ __attribute__((aligned(32))) S srec[2][REC];
-    __shared__ float stail[2][kBlk];
+    constexpr int NLD = REC / VEC / NT;        // 16-byte loads per thread per record
+    static_assert(REC % (VEC * NT) == 0, "record must split evenly over the workgroup");
+    __shared__ __attribute__((aligned(32))) S srec[NB][REC];
+    __shared__ float stail[NB][kBlk];
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const FwdLayout lay = fwd_layout(a.B, a.H, a.L, D, sizeof(S));
     const int nb = (int)lay.nb;
-    const int ntile = (nb + 3) / 4;
+    const int ntile = (nb + QB - 1) / QB;
 
     // Work item: heads are kept together on one XCD (workgroups are dealt
     // round-robin over the 8 XCDs, each with its own L2), longest tiles first.
@@ -89,9 +112,10 @@ __global__ __launch_bounds__(256, 2) void path_fwd_kernel(FwdArgs a) {
     const int64_t bh = item / ntile;
     const int tile = ntile - 1 - (int)(item % ntile);
 
-    const int I = 4 * tile + wv;                 // this wave's query block
+    const int I = QB * tile + (wv * CT) / 2;     // this wave's query block
+    const int c0 = 32 * ((wv * CT) % 2);         // first query column of this wave inside the block
     const bool active = I >= 1 && I < nb;        // block 0 is complete after prep
-    const int Jtop = min(4 * tile + 3, nb - 1) - 1;
+    const int Jtop = min(QB * tile + QB - 1, nb - 1) - 1;
     if (Jtop < 0) return;
 
     const S *recs = (const S *)((const char *)a.ws + lay.off_rec) + bh * lay.nb * REC;
@@ -99,9 +123,9 @@ __global__ __launch_bounds__(256, 2) void path_fwd_kernel(FwdArgs a) {
     const float *fb = (const float *)((const char *)a.ws + lay.off_fb) + bh * lay.nb;
 
     // ---- per-wave state
-    f32x16 qt[DT][2], o[DT][2];
-    Frag qb[2][KCH];
-    float m[2], lp[2], off[2];
+    f32x16 qt[DT][CT], o[DT][CT];
+    Frag qb[CT][KCH];
+    float m[CT], lp[CT], off[CT];
     if (active) {
         const S *qh = (const S *)((const char *)a.ws + lay.off_qhat) + (bh * lay.lp + (int64_t)I * kBlk) * D;
         const S *od = (const S *)a.out + (bh * a.L + (int64_t)I * kBlk) * D;
@@ -109,8 +133,8 @@ __global__ __launch_bounds__(256, 2) void path_fwd_kernel(FwdArgs a) {
         const float *ld = (const float *)((const char *)a.ws + lay.off_ldiag) + bh * lay.lp + (int64_t)I * kBlk;
         const float *fq = (const float *)((const char *)a.ws + lay.off_fq) + bh * lay.lp + (int64_t)I * kBlk;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int i = 32 * ct + l32;
+        for (int ct = 0; ct < CT; ++ct) {
+            const int i = c0 + 32 * ct + l32;
             const bool valid = (int64_t)I * kBlk + i < a.L;
             const int io = valid ? i : 0;  // rows past L read row 0 of the block, then drop it
             m[ct] = md[i];
@@ -134,23 +158,39 @@ __global__ __launch_bounds__(256, 2) void path_fwd_kernel(FwdArgs a) {
                 }
         }
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int kc = 0; kc < KCH; ++kc) qb[ct][kc] = acc_frag<S>(qt[kc >> 1][ct], kc & 1);
     }
 
-    // ---- key-block records are copied global -> LDS by the DMA path
-    issue_record<S, REC, NLD, FOX>(recs + (int64_t)Jtop * REC, fk + (int64_t)Jtop * kBlk, srec[0], stail[0], wv, lane);
+    // ---- key-block records are copied global -> LDS by the DMA path, NB - 1 records ahead
+    constexpr int kLoadsPerRecord = NLD;  // per wave (wave 0 adds one for the forget-gate tail)
+#pragma unroll
+    for (int k = 0; k < NB - 1; ++k)
+        if (Jtop - k >= 0)
+            issue_record<S, REC, NLD, NW, FOX>(recs + (int64_t)(Jtop - k) * REC, fk + (int64_t)(Jtop - k) * kBlk,
+                                               srec[k], stail[k], wv, lane);
 
     const float c2 = a.scale * kLog2e;
     constexpr float kTau = 8.f;  // running max is refreshed only when it grows by more than 2^8
     for (int J = Jtop; J >= 0; --J) {
-        const int buf = (Jtop - J) & 1;
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of record J have landed
-        __syncthreads();                // ... and every other wave's
-        if (J > 0)
-            issue_record<S, REC, NLD, FOX>(recs + (int64_t)(J - 1) * REC, fk + (int64_t)(J - 1) * kBlk, srec[buf ^ 1],
-                                           stail[buf ^ 1], wv, lane);
+        const int it = Jtop - J, buf = it % NB;
+        // wait for this wave's copies of record J; the copies of the NB - 2 newer
+        // records issued after it may stay in flight
+        if (NB > 2 && J >= 1) {
+            if (FOX && wv == 0)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerRecord + 1));
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerRecord));
+        } else {
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        __syncthreads();  // every wave's copies have landed; buffer (it + NB - 1) % NB is free
+        if (J - (NB - 1) >= 0) {
+            const int jn = J - (NB - 1);
+            issue_record<S, REC, NLD, NW, FOX>(recs + (int64_t)jn * REC, fk + (int64_t)jn * kBlk,
+                                               srec[(it + NB - 1) % NB], stail[(it + NB - 1) % NB], wv, lane);
+        }
         if (active && J < I) {
             const S *sk = srec[buf];
             const S *sv = srec[buf] + kBlk * D;
@@ -159,12 +199,14 @@ __global__ __launch_bounds__(256, 2) void path_fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {  // keys 32 hf .. 32 hf + 31 of the block
                 // S^T = khat qt^T for this half
-                f32x16 s[2] = {f32x16{}, f32x16{}};
+                f32x16 s[CT];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) s[ct] = f32x16{};
 #pragma unroll
                 for (int kc = 0; kc < KCH; ++kc) {
                     const Frag af = *(const Frag *)(sk + ((hf * KCH + kc) * 64 + lane) * 8);
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) E::mma(s[ct], af, qb[ct][kc]);
+                    for (int ct = 0; ct < CT; ++ct) E::mma(s[ct], af, qb[ct][kc]);
                 }
                 if (hf == 0 && J > 0) {
                     // qt <- P_J qt (uses the old qt fragments; independent of the softmax)
@@ -174,13 +216,13 @@ __global__ __launch_bounds__(256, 2) void path_fwd_kernel(FwdArgs a) {
                         for (int dt = 0; dt < DT; ++dt) {
                             const Frag af = *(const Frag *)(sm + ((dt * KCH + kc) * 64 + lane) * 8);
 #pragma unroll
-                            for (int ct = 0; ct < 2; ++ct) E::mma(qt[dt][ct], af, qb[ct][kc]);
+                            for (int ct = 0; ct < CT; ++ct) E::mma(qt[dt][ct], af, qb[ct][kc]);
                         }
                 }
                 // online softmax down each column (log2 units)
-                Frag pf[2][2];
+                Frag pf[CT][2];
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
+                for (int ct = 0; ct < CT; ++ct) {
                     float mx = -INFINITY;
                     if (FOX) {
 #pragma unroll
@@ -230,18 +272,18 @@ __global__ __launch_bounds__(256, 2) void path_fwd_kernel(FwdArgs a) {
                     for (int dt = 0; dt < DT; ++dt) {
                         const Frag af = *(const Frag *)(sv + ((dt * 4 + 2 * hf + cc) * 64 + lane) * 8);
 #pragma unroll
-                        for (int ct = 0; ct < 2; ++ct) E::mma(o[dt][ct], af, pf[ct][cc]);
+                        for (int ct = 0; ct < CT; ++ct) E::mma(o[dt][ct], af, pf[ct][cc]);
                     }
             }
             if (J > 0) {
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                     for (int kc = 0; kc < KCH; ++kc) qb[ct][kc] = acc_frag<S>(qt[kc >> 1][ct], kc & 1);
             }
             if (FOX) {
-                off[0] += fbJ;
-                off[1] += fbJ;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) off[ct] += fbJ;
             }
         }
     }
@@ -250,8 +292,8 @@ __global__ __launch_bounds__(256, 2) void path_fwd_kernel(FwdArgs a) {
     if (active) {
         S *go = (S *)a.out + (bh * a.L + (int64_t)I * kBlk) * D;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int i = 32 * ct + l32;
+        for (int ct = 0; ct < CT; ++ct) {
+            const int i = c0 + 32 * ct + l32;
             const float lsum = other_half_sum(lp[ct]);
             if ((int64_t)I * kBlk + i >= a.L) continue;
             const float inv = 1.f / lsum;
@@ -281,9 +323,9 @@ __global__ __launch_bounds__(256, 2) void path_fwd_kernel(FwdArgs a) {
 template <typename S, int D, bool FOX>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t st) {
     const FwdLayout lay = fwd_layout(a.B, a.H, a.L, D, sizeof(S));
-    const int64_t ntile = (lay.nb + 3) / 4;
+    const int64_t ntile = (lay.nb + kFwdBlocksPerWg - 1) / kFwdBlocksPerWg;
     dim3 grid((unsigned)(ntile * lay.bh));
-    hipLaunchKernelGGL((path_fwd_kernel<S, D, FOX>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((path_fwd_kernel<S, D, FOX>), grid, dim3(64 * kFwdWaves), 0, st, a);
     return hipGetLastError();
 }
 

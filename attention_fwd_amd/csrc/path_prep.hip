@@ -100,20 +100,24 @@ __device__ __forceinline__ void tile_mma(f32x16 &c, const S *A, const S *B, int 
     }
 }
 
-// Store a 32x32 accumulator tile (rows m0.., cols n0..) into an LDS matrix,
-// optionally transposed, after `f(row, col, value)`.
-template <typename S, bool TRANS, typename F>
-__device__ __forceinline__ void store_tile(S *mat, const f32x16 &c, int m0, int n0, int lane, F f) {
+// Store the transpose of a 32x32 accumulator tile: element (row, col) goes to
+// mat[col][row] (zero where keep(row, col) is false); 4 contiguous rows per store.
+template <typename S, typename F>
+__device__ __forceinline__ void store_tile_t(S *mat, const f32x16 &c, int m0, int n0, int lane, F keep) {
     constexpr int SP = PrepCfg<S>::SP;
     const int h = lane >> 5, col = n0 + (lane & 31);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = m0 + acc_row(r, h);
-        const float v = f(row, col, c[r]);
-        if (TRANS)
-            mat[col * SP + row] = Elem<S>::from_float(v);
-        else
-            mat[row * SP + col] = Elem<S>::from_float(v);
+    for (int g = 0; g < 4; ++g) {
+        const int row = m0 + 8 * g + 4 * h;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = keep(row + e, col) ? c[4 * g + e] : 0.f;
+        S *p = mat + col * SP + row;
+        if constexpr (sizeof(S) == 2) {
+            *(u32x2 *)p = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        } else {
+            *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
+        }
     }
 }
 
@@ -215,7 +219,8 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
     constexpr int VPT = 64 * RCH / 256;      // chunks per thread per matrix
     __shared__ __attribute__((aligned(16))) S fixed[C::NFIX * MAT];
     __shared__ __attribute__((aligned(16))) char region[C::RB];
-    __shared__ float sBeta[64], sCl[64], sT[3][16][17];
+    __shared__ float sBeta[64], sCl[64];
+    __shared__ __attribute__((aligned(16))) float sT[3][16][20];
 
     S *sW = fixed, *sX = fixed + MAT, *sY = fixed + 2 * MAT;
     S *sWt = kBf ? fixed + 3 * MAT : nullptr;
@@ -240,22 +245,29 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
         const S *gw = (const S *)a.w + tok0 * D, *gv = (const S *)a.v + tok0 * D;
 #pragma unroll
         for (int s = 0; s < VPT; ++s) {
-            const int idx = tid + 256 * s, r = idx / RCH, cc = idx % RCH;
+            const int idx = tid + 256 * s;
+            // Q, K: consecutive lanes take consecutive chunks of a row (coalesced)
+            const int r = idx / RCH, cc = idx % RCH;
             u32x4 vq = {0, 0, 0, 0}, vk = vq, vw = vq, vv = vq;
             if (r < nvalid) {
                 vq = *(const u32x4 *)(gq + r * D + cc * CH);
                 vk = *(const u32x4 *)(gk + r * D + cc * CH);
-                vw = *(const u32x4 *)(gw + r * D + cc * CH);
-                vv = *(const u32x4 *)(gv + r * D + cc * CH);
             }
-            vreg[s] = vv;
             *(u32x4 *)(sQ + r * SP + cc * CH) = vq;
             *(u32x4 *)(sK + r * SP + cc * CH) = vk;
-            *(u32x4 *)(sW + r * SP + cc * CH) = vw;
+            // W, V: consecutive lanes take consecutive rows, so that the transposed
+            // LDS copies (W^T now, V^T after the solve) are written without bank conflicts
+            const int rw = idx % 64, cw = idx / 64;
+            if (rw < nvalid) {
+                vw = *(const u32x4 *)(gw + rw * D + cw * CH);
+                vv = *(const u32x4 *)(gv + rw * D + cw * CH);
+            }
+            vreg[s] = vv;
+            *(u32x4 *)(sW + rw * SP + cw * CH) = vw;
             if constexpr (kBf) {
                 const S *we = (const S *)&vw;
 #pragma unroll
-                for (int e = 0; e < CH; ++e) sWt[(cc * CH + e) * SP + r] = we[e];
+                for (int e = 0; e < CH; ++e) sWt[(cw * CH + e) * SP + rw] = we[e];
             }
         }
         if (tid < 64) sBeta[tid] = tid < nvalid ? a.beta[tok0 + tid] : 0.f;
@@ -286,12 +298,13 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
     f32x16 s[2], qi[2], ki[2];  // waves 0,1: diagonal logits K Q^T; waves 2,3: Q^T, K^T tiles
     tile_mma<S, true, true>(g, sW, sW, mt, nt, D, lane);
     {
+        // X^T = W Q^T and Y^T = W K^T, stored back transposed (4 contiguous elements per store)
         f32x16 c = {};
-        tile_mma<S, true, true>(c, sQ, sW, mt, nt, D, lane);
-        store_tile<S, false>(sX, c, mt, nt, lane, [](int i, int cc, float v) { return cc <= i ? v : 0.f; });
+        tile_mma<S, true, true>(c, sW, sQ, mt, nt, D, lane);
+        store_tile_t<S>(sX, c, mt, nt, lane, [](int cc, int i) { return cc <= i; });
         c = f32x16{};
-        tile_mma<S, true, true>(c, sK, sW, mt, nt, D, lane);
-        store_tile<S, false>(sY, c, mt, nt, lane, [](int j, int r, float v) { return r > j ? v : 0.f; });
+        tile_mma<S, true, true>(c, sW, sK, mt, nt, D, lane);
+        store_tile_t<S>(sY, c, mt, nt, lane, [](int r, int j) { return r > j; });
     }
     if (wv < 2) {
 #pragma unroll
@@ -320,7 +333,7 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float *gr = sG + (I16 + r) * GS + I16 + p;
-            float part = gr[0] * xs[0] + gr[4] * xs[1] + gr[8] * xs[2] + gr[12] * xs[3];
+            float part = (gr[0] * xs[0] + gr[4] * xs[1]) + (gr[8] * xs[2] + gr[12] * xs[3]);
             part = sum4(part);
             const float x = (r == t) ? 1.f : (r > t ? -sBeta[I16 + r] * part : 0.f);
             if (p == (r & 3)) xs[r >> 2] = x;
@@ -333,61 +346,65 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
     //     E_IJ = -E_II T_IJ,  T_IJ = D_I sum_{K=J}^{I-1} G_IK E_KJ
 #pragma unroll
     for (int lev = 1; lev < 4; ++lev) {
-        const int nblk = 4 - lev;
-#pragma unroll
-        for (int q = 0; q < nblk; ++q) {
-            const int idx = tid + 256 * q;
-            const int b = idx >> 8, r = (idx >> 4) & 15, t = idx & 15, I = lev + b;
+        // one work item = 4 adjacent columns of one row of one tile
+        const int b = tid >> 6, r = (tid >> 2) & 15, t4 = 4 * (tid & 3), I = lev + b;
+        const bool act = b < 4 - lev;
+        if (act) {
             const float *gr = sG + (16 * I + r) * GS + 16 * b;
-            const float *ec = sE + 16 * b * GS + 16 * b + t;
-            float acc0 = 0.f, acc1 = 0.f;
+            const float *ec = sE + 16 * b * GS + 16 * b + t4;
+            // four independent accumulators keep the dependent FMA chains short
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, a3 = a0;
 #pragma unroll
             for (int c = 0; c < 16 * lev; c += 4) {
                 const f32x4 gv = *(const f32x4 *)(gr + c);
-                acc0 += gv.x * ec[c * GS] + gv.y * ec[(c + 1) * GS];
-                acc1 += gv.z * ec[(c + 2) * GS] + gv.w * ec[(c + 3) * GS];
+                a0 += gv.x * *(const f32x4 *)(ec + c * GS);
+                a1 += gv.y * *(const f32x4 *)(ec + (c + 1) * GS);
+                a2 += gv.z * *(const f32x4 *)(ec + (c + 2) * GS);
+                a3 += gv.w * *(const f32x4 *)(ec + (c + 3) * GS);
             }
-            sT[b][r][t] = sBeta[16 * I + r] * (acc0 + acc1);
+            *(f32x4 *)&sT[b][r][t4] = sBeta[16 * I + r] * ((a0 + a1) + (a2 + a3));
         }
         __syncthreads();
-#pragma unroll
-        for (int q = 0; q < nblk; ++q) {
-            const int idx = tid + 256 * q;
-            const int b = idx >> 8, r = (idx >> 4) & 15, t = idx & 15, I = lev + b;
+        if (act) {
             const float *er = sE + (16 * I + r) * GS + 16 * I;  // E_II row r: zero above the diagonal
-            float acc0 = 0.f, acc1 = 0.f;
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, a3 = a0;
 #pragma unroll
             for (int c = 0; c < 16; c += 4) {
                 const f32x4 ev = *(const f32x4 *)(er + c);
-                acc0 += ev.x * sT[b][c][t] + ev.y * sT[b][c + 1][t];
-                acc1 += ev.z * sT[b][c + 2][t] + ev.w * sT[b][c + 3][t];
+                a0 += ev.x * *(const f32x4 *)&sT[b][c][t4];
+                a1 += ev.y * *(const f32x4 *)&sT[b][c + 1][t4];
+                a2 += ev.z * *(const f32x4 *)&sT[b][c + 2][t4];
+                a3 += ev.w * *(const f32x4 *)&sT[b][c + 3][t4];
             }
-            sE[(16 * I + r) * GS + 16 * b + t] = -(acc0 + acc1);
+            *(f32x4 *)(sE + (16 * I + r) * GS + 16 * b + t4) = -((a0 + a1) + (a2 + a3));
         }
         __syncthreads();
     }
     {
-        // A = E D_b (lower triangle only; E's upper tiles were never written)
-        const int r = tid >> 2, c0 = (tid & 3) * 16;
+        // A = E D_b (lower triangle only; E's upper tiles were never written).
+        // Thread (column c, 16 rows from rg): conflict-free column reads of E.
+        const int c = tid & 63, rg = 16 * (tid >> 6);
+        const float bc = sBeta[c];
         float av[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int c = c0 + e;
-            av[e] = c <= r ? sE[r * GS + c] * sBeta[c] : 0.f;
-        }
+        for (int e = 0; e < 16; ++e) av[e] = c <= rg + e ? sE[(rg + e) * GS + c] * bc : 0.f;
         __syncthreads();  // E and G are dead: their space becomes A, A^T, V^T
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const S v = Elem<S>::from_float(av[e]);
-            sA[r * SP + c0 + e] = v;
-            if constexpr (kBf) sAup[(c0 + e) * SP + r] = v;
+        for (int e = 0; e < 16; ++e) sA[(rg + e) * SP + c] = Elem<S>::from_float(av[e]);
+        if constexpr (kBf) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 8) {
+                const u32x4 u = {pack_bf16(av[e], av[e + 1]), pack_bf16(av[e + 2], av[e + 3]),
+                                 pack_bf16(av[e + 4], av[e + 5]), pack_bf16(av[e + 6], av[e + 7])};
+                *(u32x4 *)(sAup + c * SP + rg + e) = u;
+            }
         }
 #pragma unroll
         for (int s2 = 0; s2 < VPT; ++s2) {
-            const int idx = tid + 256 * s2, vr = idx / RCH, cc = idx % RCH;
+            const int idx = tid + 256 * s2, vr = idx % 64, cw = idx / 64;
             const S *ve = (const S *)&vreg[s2];
 #pragma unroll
-            for (int e = 0; e < CH; ++e) sVt[(cc * CH + e) * SP + vr] = ve[e];
+            for (int e = 0; e < CH; ++e) sVt[(cw * CH + e) * SP + vr] = ve[e];
         }
     }
     __syncthreads();
