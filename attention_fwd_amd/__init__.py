@@ -123,7 +123,7 @@ def fwd(q, k, v, w, beta, logf=None, scale=None, out=None, lse=None, return_lse=
         _check(lse, "lse", torch.float32, (B, H, L), dev)
     need = fwd_workspace_size(B, H, L, d, dt)
     if need == 0:
-        raise PathError(PATH_EUNSUPPORTED if d != 64 else PATH_EINVAL, "path_attn_fwd_workspace_size")
+        raise PathError(PATH_EUNSUPPORTED if d not in (64, 128) else PATH_EINVAL, "path_attn_fwd_workspace_size")
     if workspace is None:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     _check(workspace, "workspace", None, None, dev)

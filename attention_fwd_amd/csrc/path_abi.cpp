@@ -38,7 +38,7 @@ int64_t mul_chk(std::initializer_list<int64_t> xs) {
 
 path_status_t fwd_sizes_ok(int B, int H, int L, int d, path_dtype_t dtype) {
     if (B < 1 || H < 1 || L < 1 || d < 1 || elem_size(dtype) == 0) return PATH_EINVAL;
-    if (d != 64) return PATH_EUNSUPPORTED;
+    if (d != 64 && d != 128) return PATH_EUNSUPPORTED;
     const int64_t nb = ((int64_t)L + path::kBlk - 1) / path::kBlk;
     if (mul_chk({B, H, nb * path::kBlk, d, 8}) < 0) return PATH_EINVAL;
     if (mul_chk({B, H, nb}) > kMaxGrid) return PATH_EINVAL;
@@ -47,7 +47,7 @@ path_status_t fwd_sizes_ok(int B, int H, int L, int d, path_dtype_t dtype) {
 
 path_status_t dec_sizes_ok(int B, int H, int64_t rows, int d, path_dtype_t dtype) {
     if (B < 1 || H < 1 || rows < 1 || d < 1 || elem_size(dtype) == 0) return PATH_EINVAL;
-    if (d != 64) return PATH_EUNSUPPORTED;
+    if (d != 64 && d != 128) return PATH_EUNSUPPORTED;
     if (mul_chk({B, H, rows, d, 8}) < 0) return PATH_EINVAL;
     return PATH_OK;
 }

@@ -22,10 +22,12 @@ namespace path {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kRowsPerIter = 4;  // rows per lane group per iteration
+// rows each lane group keeps in flight per iteration (fewer for the wider head)
+template <int D>
+constexpr int rows_per_iter() { return D == 64 ? 4 : 2; }
 
 template <typename S>
-__device__ __forceinline__ void load8(const S *p, float *x) {
+__device__ __forceinline__ void load8(const S *p, float *x) {  // 8 consecutive elements as fp32
     if constexpr (sizeof(S) == 2) {
         u32x4 u = *(const u32x4 *)p;
         x[0] = bf16_to_f32(u.x & 0xffff); x[1] = bf16_to_f32(u.x >> 16);
@@ -51,9 +53,22 @@ __device__ __forceinline__ void store8(S *p, const float *x) {
     }
 }
 
+template <typename S, int N>
+__device__ __forceinline__ void loadn(const S *p, float *x) {  // N (multiple of 8) consecutive elements
+#pragma unroll
+    for (int c = 0; c < N; c += 8) load8<S>(p + c, x + c);
+}
+template <typename S, int N>
+__device__ __forceinline__ void storen(S *p, const float *x) {
+#pragma unroll
+    for (int c = 0; c < N; c += 8) store8<S>(p + c, x + c);
+}
+
 template <typename S, int D>
 __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) {
-    static_assert(D == 64, "decode kernel is laid out for head dimension 64 (8 lanes x 8 elements per row)");
+    static_assert(D == 64 || D == 128, "decode kernel: head dimension 64 or 128");
+    constexpr int EPL = D / 8;           // elements per lane: 8 lanes share a row
+    constexpr int kRowsPerIter = rows_per_iter<D>();
     constexpr int NG = kDecThreads / 8;  // lane groups (rows in flight per load) per workgroup
     __shared__ float sred[NG][D + 2];
 
@@ -66,22 +81,22 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
 
     S *kc = (S *)a.kc + bh * a.ncap * D;
     S *vc = (S *)a.vc + bh * a.ncap * D;
-    float q[8], w[8];
-    load8<S>((const S *)a.q + bh * D + 8 * sub, q);
-    load8<S>((const S *)a.w + bh * D + 8 * sub, w);
+    float q[EPL], w[EPL];
+    loadn<S, EPL>((const S *)a.q + bh * D + EPL * sub, q);
+    loadn<S, EPL>((const S *)a.w + bh * D + EPL * sub, w);
     const float beta = a.beta[bh];
     float qw = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qw += q[e] * w[e];
+    for (int e = 0; e < EPL; ++e) qw += q[e] * w[e];
     qw = sum8(qw);
     const float c2 = a.scale * kLog2e;
 
-    float m = -INFINITY, l = 0.f, acc[8];
+    float m = -INFINITY, l = 0.f, acc[EPL];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 
     for (int64_t base = r0 + grp; base < r1; base += (int64_t)NG * kRowsPerIter) {
-        float kx[kRowsPerIter][8], vx[kRowsPerIter][8], x[kRowsPerIter];
+        float kx[kRowsPerIter][EPL], vx[kRowsPerIter][EPL], x[kRowsPerIter];
         bool ok[kRowsPerIter], fresh[kRowsPerIter];
 #pragma unroll
         for (int u = 0; u < kRowsPerIter; ++u) {
@@ -89,14 +104,14 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
             ok[u] = j < r1;
             fresh[u] = ok[u] && j == a.n;  // the appended token (only when knew != NULL)
             if (ok[u] && !fresh[u]) {
-                load8<S>(kc + j * D + 8 * sub, kx[u]);
-                load8<S>(vc + j * D + 8 * sub, vx[u]);
+                loadn<S, EPL>(kc + j * D + EPL * sub, kx[u]);
+                loadn<S, EPL>(vc + j * D + EPL * sub, vx[u]);
             } else if (fresh[u]) {
-                load8<S>((const S *)a.knew + bh * D + 8 * sub, kx[u]);
-                load8<S>((const S *)a.vnew + bh * D + 8 * sub, vx[u]);
+                loadn<S, EPL>((const S *)a.knew + bh * D + EPL * sub, kx[u]);
+                loadn<S, EPL>((const S *)a.vnew + bh * D + EPL * sub, vx[u]);
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kx[u][e] = vx[u][e] = 0.f;
+                for (int e = 0; e < EPL; ++e) kx[u][e] = vx[u][e] = 0.f;
             }
         }
 #pragma unroll
@@ -104,22 +119,22 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
             const int64_t j = base + (int64_t)u * NG;
             float pa = 0.f, pb = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < EPL; ++e) {
                 pa += w[e] * kx[u][e];
                 pb += q[e] * kx[u][e];
             }
             const float ta = sum8(pa), tb = sum8(pb);
             if (fresh[u]) {
                 // new key enters untransformed; store k_new, v_new at row n
-                store8<S>(kc + j * D + 8 * sub, kx[u]);
-                store8<S>(vc + j * D + 8 * sub, vx[u]);
+                storen<S, EPL>(kc + j * D + EPL * sub, kx[u]);
+                storen<S, EPL>(vc + j * D + EPL * sub, vx[u]);
                 x[u] = tb * c2;
             } else if (ok[u]) {
                 const float cb = beta * ta;
-                float kn[8];
+                float kn[EPL];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kn[e] = kx[u][e] - cb * w[e];
-                store8<S>(kc + j * D + 8 * sub, kn);
+                for (int e = 0; e < EPL; ++e) kn[e] = kx[u][e] - cb * w[e];
+                storen<S, EPL>(kc + j * D + EPL * sub, kn);
                 x[u] = (tb - cb * qw) * c2;
             } else {
                 x[u] = -INFINITY;
@@ -132,13 +147,13 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
             const float alpha = fast_exp2(m - mx);
             l *= alpha;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+            for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
 #pragma unroll
             for (int u = 0; u < kRowsPerIter; ++u) {
                 const float p = fast_exp2(x[u] - mx);
                 l += p;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += p * vx[u][e];
+                for (int e = 0; e < EPL; ++e) acc[e] += p * vx[u][e];
             }
             m = mx;
         }
@@ -146,7 +161,7 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
 
     // merge the lane groups of the workgroup in a fixed order
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sred[grp][8 * sub + e] = acc[e];
+    for (int e = 0; e < EPL; ++e) sred[grp][EPL * sub + e] = acc[e];
     if (sub == 0) {
         sred[grp][D] = m;
         sred[grp][D + 1] = l;
@@ -172,7 +187,7 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
 }
 
 template <typename S, int D>
-__global__ __launch_bounds__(64) void path_decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(D) void path_decode_combine_kernel(DecodeArgs a) {
     const int64_t bh = blockIdx.x;
     const int tid = threadIdx.x;
     const float *part = (const float *)a.ws + (int64_t)bh * a.nsplit * (D + 2);
@@ -193,7 +208,7 @@ __global__ __launch_bounds__(64) void path_decode_combine_kernel(DecodeArgs a) {
 
 void decode_plan(int64_t BH, int64_t rows, int *nsplit, int64_t *chunk) {
     const int64_t target_wg = 4096;
-    const int64_t step = (int64_t)(kDecThreads / 8) * kRowsPerIter;  // rows per workgroup iteration
+    const int64_t step = (int64_t)(kDecThreads / 8) * 4;  // rows per workgroup iteration (multiple of both)
     int64_t per_head = (target_wg + BH - 1) / BH;
     const int64_t max_split = (rows + step - 1) / step;
     if (per_head > max_split) per_head = max_split;
@@ -206,19 +221,20 @@ void decode_plan(int64_t BH, int64_t rows, int *nsplit, int64_t *chunk) {
     if (*nsplit < 1) *nsplit = 1;
 }
 
-template <typename S>
+template <typename S, int D>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
     dim3 grid((unsigned)(a.nsplit * a.B * a.H));
-    hipLaunchKernelGGL((path_decode_kernel<S, 64>), grid, dim3(kDecThreads), 0, st, a);
+    hipLaunchKernelGGL((path_decode_kernel<S, D>), grid, dim3(kDecThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((path_decode_combine_kernel<S, 64>), dim3((unsigned)(a.B * a.H)), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((path_decode_combine_kernel<S, D>), dim3((unsigned)(a.B * a.H)), dim3(D), 0, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t st) {
-    if (a.d != 64) return hipErrorInvalidValue;
-    return bf16 ? launch_decode_t<uint16_t>(a, st) : launch_decode_t<float>(a, st);
+    if (a.d == 64) return bf16 ? launch_decode_t<uint16_t, 64>(a, st) : launch_decode_t<float, 64>(a, st);
+    if (a.d == 128) return bf16 ? launch_decode_t<uint16_t, 128>(a, st) : launch_decode_t<float, 128>(a, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace path

@@ -63,22 +63,22 @@ __device__ __forceinline__ void issue_record(const S *src, const float *tail, S 
     if (FOX && wv == 0) __builtin_amdgcn_global_load_lds((const void *)(tail + lane), (lds_void *)dtail, 4, 0, 0);
 }
 
-// Waves per workgroup (= 64-query blocks sharing each key-block record) and
-// key-block records in flight (LDS buffers).
-#ifndef PATH_FWD_NW
-#define PATH_FWD_NW 4
-#endif
-#ifndef PATH_FWD_NBUF
-#define PATH_FWD_NBUF 2
-#endif
-// 32-query column tiles per wave (1 or 2); a workgroup covers NW * CT / 2 query blocks
-#ifndef PATH_FWD_CT
-#define PATH_FWD_CT 2
-#endif
-constexpr int kFwdWaves = PATH_FWD_NW;
-constexpr int kFwdBufs = PATH_FWD_NBUF;
-constexpr int kFwdCt = PATH_FWD_CT;
-constexpr int kFwdBlocksPerWg = kFwdWaves * kFwdCt / 2;
+// Launch shape per element type and head dimension: NW waves per workgroup,
+// CT 32-query column tiles per wave (a workgroup covers NW * CT / 2 query
+// blocks that share every key-block record), NB key-block records in flight
+// (LDS buffers).  d = 64: 4 waves x 64 queries, two 24 KiB (bf16) records,
+// two workgroups per CU.  d = 128: a record is 64 KiB (bf16), and the query
+// state of 64 columns (q-tilde, O: 256 fp32 accumulators) no longer fits a
+// wave's registers, so waves take 32 queries and 8 of them share the records;
+// fp32 records (128 KiB) are single-buffered.
+template <typename S, int D>
+struct FwdCfg {
+    static constexpr int NW = D == 64 ? 4 : (sizeof(S) == 2 ? 8 : 4);
+    static constexpr int CT = D == 64 ? 2 : 1;
+    static constexpr int NB = (D == 128 && sizeof(S) == 4) ? 1 : 2;
+    static constexpr int QB = NW * CT / 2;  // query blocks per workgroup
+    static constexpr int WG_PER_CU = D == 64 ? 2 : 1;
+};
 
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"
 // (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and
@@ -86,11 +86,12 @@ constexpr int kFwdBlocksPerWg = kFwdWaves * kFwdCt / 2;
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 template <typename S, int D, bool FOX>
-__global__ __launch_bounds__(64 * kFwdWaves, 4 / kFwdCt) void path_fwd_kernel(FwdArgs a) {
-    static_assert(D == 64, "forward kernel is laid out for head dimension 64");
+__global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU)) void path_fwd_kernel(FwdArgs a) {
+    static_assert(D == 64 || D == 128, "forward kernel: head dimension 64 or 128");
     typedef Elem<S> E;
     typedef typename E::Frag Frag;
-    constexpr int NW = kFwdWaves, NB = kFwdBufs, NT = 64 * NW, CT = kFwdCt, QB = kFwdBlocksPerWg;
+    typedef FwdCfg<S, D> F;
+    constexpr int NW = F::NW, NB = F::NB, NT = 64 * NW, CT = F::CT, QB = F::QB;
     constexpr int REC = 2 * kBlk * D + D * D;  // elements per key-block record
     constexpr int KCH = D / 16, DT = D / 32;
     constexpr int VEC = 16 / (int)sizeof(S);   // elements per 16-byte load
@@ -164,9 +165,10 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4 / kFwdCt) void path_fwd_kernel(Fw
     }
 
     // ---- key-block records are copied global -> LDS by the DMA path, NB - 1 records ahead
+    // (a single buffer is refilled after every wave is done with it)
     constexpr int kLoadsPerRecord = NLD;  // per wave (wave 0 adds one for the forget-gate tail)
 #pragma unroll
-    for (int k = 0; k < NB - 1; ++k)
+    for (int k = 0; k < (NB > 1 ? NB - 1 : 1); ++k)
         if (Jtop - k >= 0)
             issue_record<S, REC, NLD, NW, FOX>(recs + (int64_t)(Jtop - k) * REC, fk + (int64_t)(Jtop - k) * kBlk,
                                                srec[k], stail[k], wv, lane);
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4 / kFwdCt) void path_fwd_kernel(Fw
             __builtin_amdgcn_s_waitcnt(0);
         }
         __syncthreads();  // every wave's copies have landed; buffer (it + NB - 1) % NB is free
-        if (J - (NB - 1) >= 0) {
+        if (NB > 1 && J - (NB - 1) >= 0) {
             const int jn = J - (NB - 1);
             issue_record<S, REC, NLD, NW, FOX>(recs + (int64_t)jn * REC, fk + (int64_t)jn * kBlk,
                                                srec[(it + NB - 1) % NB], stail[(it + NB - 1) % NB], wv, lane);
@@ -286,6 +288,11 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4 / kFwdCt) void path_fwd_kernel(Fw
                 for (int ct = 0; ct < CT; ++ct) off[ct] += fbJ;
             }
         }
+        if (NB == 1 && J >= 1) {
+            __syncthreads();  // every wave is done with the buffer
+            issue_record<S, REC, NLD, NW, FOX>(recs + (int64_t)(J - 1) * REC, fk + (int64_t)(J - 1) * kBlk, srec[0],
+                                               stail[0], wv, lane);
+        }
     }
 
     // ---- epilogue
@@ -322,17 +329,24 @@ __global__ __launch_bounds__(64 * kFwdWaves, 4 / kFwdCt) void path_fwd_kernel(Fw
 
 template <typename S, int D, bool FOX>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t st) {
+    typedef FwdCfg<S, D> F;
     const FwdLayout lay = fwd_layout(a.B, a.H, a.L, D, sizeof(S));
-    const int64_t ntile = (lay.nb + kFwdBlocksPerWg - 1) / kFwdBlocksPerWg;
+    const int64_t ntile = (lay.nb + F::QB - 1) / F::QB;
     dim3 grid((unsigned)(ntile * lay.bh));
-    hipLaunchKernelGGL((path_fwd_kernel<S, D, FOX>), grid, dim3(64 * kFwdWaves), 0, st, a);
+    hipLaunchKernelGGL((path_fwd_kernel<S, D, FOX>), grid, dim3(64 * F::NW), 0, st, a);
     return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_fwd_d(const FwdArgs &a, bool bf16, hipStream_t st) {
+    if (bf16) return a.fox ? launch_fwd_t<uint16_t, D, true>(a, st) : launch_fwd_t<uint16_t, D, false>(a, st);
+    return a.fox ? launch_fwd_t<float, D, true>(a, st) : launch_fwd_t<float, D, false>(a, st);
+}
+
 hipError_t launch_fwd(const FwdArgs &a, bool bf16, hipStream_t st) {
-    if (a.d != 64) return hipErrorInvalidValue;
-    if (bf16) return a.fox ? launch_fwd_t<uint16_t, 64, true>(a, st) : launch_fwd_t<uint16_t, 64, false>(a, st);
-    return a.fox ? launch_fwd_t<float, 64, true>(a, st) : launch_fwd_t<float, 64, false>(a, st);
+    if (a.d == 64) return launch_fwd_d<64>(a, bf16, st);
+    if (a.d == 128) return launch_fwd_d<128>(a, bf16, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace path

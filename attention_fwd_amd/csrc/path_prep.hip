@@ -31,27 +31,36 @@
 namespace path {
 namespace {
 
-template <typename S>
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <typename S, int D>
 struct PrepCfg {
     static constexpr bool kBf = sizeof(S) == 2;
-    static constexpr int SP = 64 + 16 / (int)sizeof(S);  // padded LDS row stride, elements
-    static constexpr int MAT = 64 * SP;                  // elements of one 64 x 64 matrix
-    static constexpr int MATB = MAT * (int)sizeof(S);
-    static constexpr int GS = 68;                        // fp32 row stride of G and E in the solve
-    // W, X, Y live for the whole kernel (bf16 adds W^T; fp32 has no room for
-    // transposed copies and reads them with a stride instead).  A second
-    // region is reused: Q, K while the products with them run, then G and E
-    // for the triangular solve, then A, A^T (bf16) and V^T.
-    static constexpr int NFIX = kBf ? 4 : 3;
-    static constexpr int RB = 2 * 64 * GS * 4;
-    static_assert(RB >= (kBf ? 3 : 2) * MATB, "reuse region too small");
+    static constexpr int PAD = 16 / (int)sizeof(S);
+    static constexpr int SP = 64 + PAD;    // padded row stride of [.][64] matrices (X, Y, A, W^T, V^T)
+    static constexpr int SPD = D + PAD;    // padded row stride of [64][D] matrices (W, Q, K)
+    static constexpr int MAT = 64 * SP;    // one 64 x 64 matrix
+    static constexpr int MATD = 64 * SPD;  // one 64 x D matrix, token rows
+    static constexpr int MATT = D * SP;    // one D x 64 matrix, head-dimension rows
+    static constexpr int GS = 68;          // fp32 row stride of G and E in the solve
+    // W, X, Y live for the whole kernel.  bf16 also keeps W^T (fp32 has no
+    // room for transposed copies and reads them with a stride instead): at
+    // D = 64 in a slot of its own, written while W is staged; at D = 128 in
+    // W's slot once the products with W are done, written from registers, so
+    // that two workgroups still fit in one CU.  A second region is reused: Q,
+    // K while the products with them run, then G and E for the triangular
+    // solve, then A, A^T (bf16) and V^T.
+    static constexpr bool kWtLate = kBf && D > 64;
+    static constexpr int WSLOT = kWtLate ? cmax(MATD, MATT) : MATD;
+    static constexpr int FIX = WSLOT + 2 * MAT + ((kBf && !kWtLate) ? MATT : 0);  // elements
+    static constexpr int RB = cmax(cmax(2 * MATD * (int)sizeof(S), 2 * 64 * GS * 4),
+                                   ((kBf ? 2 : 1) * MAT + MATT) * (int)sizeof(S));
 };
 
 // Fragment of the matrix view `m` (element (row, k) at row*SP + k when KC, at
-// k*SP + row otherwise) for rows `row`, k in [k0, k0+16).
-template <typename S, bool KC>
+// k*SP + row otherwise; SP = row stride in elements) for rows `row`, k in [k0, k0+16).
+template <typename S, bool KC, int SP>
 __device__ __forceinline__ typename Elem<S>::Frag lds_frag(const S *mat, int row, int k0, int h) {
-    constexpr int SP = PrepCfg<S>::SP;
     typedef typename Elem<S>::Frag Frag;
     if constexpr (KC) {
         const S *p = mat + row * SP + k0 + 4 * h;
@@ -88,23 +97,22 @@ __device__ __forceinline__ typename Elem<S>::Frag lds_frag(const S *mat, int row
     }
 }
 
-// c += A(m0.., k) * B(n0.., k) over k in [0, K): one 32x32 tile.
-template <typename S, bool AKC, bool BKC>
+// c += A(m0.., k) * B(n0.., k) over k in [0, K): one 32x32 tile (SA, SB: row strides).
+template <typename S, bool AKC, bool BKC, int SA, int SB>
 __device__ __forceinline__ void tile_mma(f32x16 &c, const S *A, const S *B, int m0, int n0, int K, int lane) {
     const int h = lane >> 5, l = lane & 31;
 #pragma unroll
     for (int k0 = 0; k0 < K; k0 += 16) {
-        auto a = lds_frag<S, AKC>(A, m0 + l, k0, h);
-        auto b = lds_frag<S, BKC>(B, n0 + l, k0, h);
+        auto a = lds_frag<S, AKC, SA>(A, m0 + l, k0, h);
+        auto b = lds_frag<S, BKC, SB>(B, n0 + l, k0, h);
         Elem<S>::mma(c, a, b);
     }
 }
 
 // Store the transpose of a 32x32 accumulator tile: element (row, col) goes to
 // mat[col][row] (zero where keep(row, col) is false); 4 contiguous rows per store.
-template <typename S, typename F>
+template <typename S, int SP, typename F>
 __device__ __forceinline__ void store_tile_t(S *mat, const f32x16 &c, int m0, int n0, int lane, F keep) {
-    constexpr int SP = PrepCfg<S>::SP;
     const int h = lane >> 5, col = n0 + (lane & 31);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -123,9 +131,8 @@ __device__ __forceinline__ void store_tile_t(S *mat, const f32x16 &c, int m0, in
 
 // Accumulator tile initialised from the transpose of an LDS matrix:
 // c(row, col) = mat[col][row] (rows = k index of mat, 4 contiguous per group).
-template <typename S>
+template <typename S, int SP>
 __device__ __forceinline__ void load_tile_t(f32x16 &c, const S *mat, int m0, int n0, int lane) {
-    constexpr int SP = PrepCfg<S>::SP;
     const int h = lane >> 5, col = n0 + (lane & 31);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -187,44 +194,68 @@ __device__ __forceinline__ void store_rows_t(S *dst, const f32x16 &c, int d0, in
 
 // c += A(m0.., k) * B where B's fragments come from two accumulator tiles
 // (rows = contraction index): k chunk kc is register half kc%2 of tile kc/2.
-template <typename S, bool AKC>
+template <typename S, bool AKC, int SA>
 __device__ __forceinline__ void tile_mma_breg(f32x16 &c, const S *A, int m0, const f32x16 *bt, int lane) {
     const int h = lane >> 5, l = lane & 31;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-        auto a = lds_frag<S, AKC>(A, m0 + l, 16 * kc, h);
+        auto a = lds_frag<S, AKC, SA>(A, m0 + l, 16 * kc, h);
         Elem<S>::mma(c, a, acc_frag<S>(bt[kc >> 1], kc & 1));
     }
 }
 
 // c += A * B(n0.., k) where A's fragments come from two accumulator tiles.
-template <typename S, bool BKC>
+template <typename S, bool BKC, int SB>
 __device__ __forceinline__ void tile_mma_areg(f32x16 &c, const f32x16 *at, const S *B, int n0, int lane) {
     const int h = lane >> 5, l = lane & 31;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-        auto b = lds_frag<S, BKC>(B, n0 + l, 16 * kc, h);
+        auto b = lds_frag<S, BKC, SB>(B, n0 + l, 16 * kc, h);
         Elem<S>::mma(c, acc_frag<S>(at[kc >> 1], kc & 1), b);
+    }
+}
+
+// Accumulator tile of the transpose of a token-major global matrix:
+// c(row, col) = src[col][row] for head-dimension rows d0.. and token columns
+// t0.. (4 contiguous rows per load); tokens at or past nvalid read as zero.
+template <typename S, int D>
+__device__ __forceinline__ void load_tile_t_global(f32x16 &c, const S *src, int d0, int t0, int nvalid, int lane) {
+    const int h = lane >> 5, col = t0 + (lane & 31);
+    const bool ok = col < nvalid;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const S *p = src + (int64_t)col * D + d0 + 8 * g + 4 * h;
+        if constexpr (sizeof(S) == 2) {
+            const u32x2 u = ok ? *(const u32x2 *)p : u32x2{0, 0};
+            c[4 * g + 0] = bf16_to_f32(u.x & 0xffff);
+            c[4 * g + 1] = bf16_to_f32(u.x >> 16);
+            c[4 * g + 2] = bf16_to_f32(u.y & 0xffff);
+            c[4 * g + 3] = bf16_to_f32(u.y >> 16);
+        } else {
+            const f32x4 v = ok ? *(const f32x4 *)p : f32x4{0.f, 0.f, 0.f, 0.f};
+            c[4 * g + 0] = v.x; c[4 * g + 1] = v.y; c[4 * g + 2] = v.z; c[4 * g + 3] = v.w;
+        }
     }
 }
 
 template <typename S, int D, bool FOX>
 __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
-    static_assert(D == 64, "prep kernel is laid out for head dimension 64");
-    typedef PrepCfg<S> C;
-    constexpr int SP = C::SP, MAT = C::MAT, GS = C::GS;
-    constexpr bool kBf = C::kBf;
+    static_assert(D == 64 || D == 128, "prep kernel: head dimension 64 or 128");
+    typedef PrepCfg<S, D> C;
+    constexpr int SP = C::SP, SPD = C::SPD, MAT = C::MAT, GS = C::GS;
+    constexpr bool kBf = C::kBf, kWtLate = C::kWtLate;
     constexpr int CH = 16 / (int)sizeof(S);  // elements per 16-byte chunk
     constexpr int RCH = D / CH;              // chunks per row
     constexpr int VPT = 64 * RCH / 256;      // chunks per thread per matrix
-    __shared__ __attribute__((aligned(16))) S fixed[C::NFIX * MAT];
+    constexpr int DT = D / 32;               // 32-row head-dimension tiles
+    __shared__ __attribute__((aligned(16))) S fixed[C::FIX];
     __shared__ __attribute__((aligned(16))) char region[C::RB];
     __shared__ float sBeta[64], sCl[64];
     __shared__ __attribute__((aligned(16))) float sT[3][16][20];
 
-    S *sW = fixed, *sX = fixed + MAT, *sY = fixed + 2 * MAT;
-    S *sWt = kBf ? fixed + 3 * MAT : nullptr;
-    S *sQ = (S *)region, *sK = (S *)region + MAT;                    // phases 1-2
+    S *sW = fixed, *sX = fixed + C::WSLOT, *sY = fixed + C::WSLOT + MAT;
+    S *sWt = kBf ? (kWtLate ? fixed : fixed + C::WSLOT + 2 * MAT) : nullptr;
+    S *sQ = (S *)region, *sK = (S *)region + C::MATD;                 // phases 1-2
     float *sG = (float *)region, *sE = (float *)region + 64 * GS;     // phase 3
     S *sA = (S *)region, *sAup = kBf ? (S *)region + MAT : nullptr;  // phase 4
     S *sVt = (S *)region + (kBf ? 2 : 1) * MAT;
@@ -240,6 +271,7 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
 
     // ---- 1. stage W, Q, K in LDS and V in registers (zero rows past L), beta, forget-gate prefix
     u32x4 vreg[VPT];
+    u32x4 wreg[kWtLate ? VPT : 1];
     {
         const S *gq = (const S *)a.q + tok0 * D, *gk = (const S *)a.k + tok0 * D;
         const S *gw = (const S *)a.w + tok0 * D, *gv = (const S *)a.v + tok0 * D;
@@ -253,18 +285,20 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
                 vq = *(const u32x4 *)(gq + r * D + cc * CH);
                 vk = *(const u32x4 *)(gk + r * D + cc * CH);
             }
-            *(u32x4 *)(sQ + r * SP + cc * CH) = vq;
-            *(u32x4 *)(sK + r * SP + cc * CH) = vk;
+            *(u32x4 *)(sQ + r * SPD + cc * CH) = vq;
+            *(u32x4 *)(sK + r * SPD + cc * CH) = vk;
             // W, V: consecutive lanes take consecutive rows, so that the transposed
-            // LDS copies (W^T now, V^T after the solve) are written without bank conflicts
+            // LDS copies (W^T, V^T) are written without bank conflicts
             const int rw = idx % 64, cw = idx / 64;
             if (rw < nvalid) {
                 vw = *(const u32x4 *)(gw + rw * D + cw * CH);
                 vv = *(const u32x4 *)(gv + rw * D + cw * CH);
             }
             vreg[s] = vv;
-            *(u32x4 *)(sW + rw * SP + cw * CH) = vw;
-            if constexpr (kBf) {
+            *(u32x4 *)(sW + rw * SPD + cw * CH) = vw;
+            if constexpr (kWtLate) {
+                wreg[s] = vw;
+            } else if constexpr (kBf) {
                 const S *we = (const S *)&vw;
 #pragma unroll
                 for (int e = 0; e < CH; ++e) sWt[(cw * CH + e) * SP + rw] = we[e];
@@ -291,32 +325,32 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
     __syncthreads();
 
     const int mt = (wv >> 1) * 32, nt = (wv & 1) * 32;  // this wave's tile of a 64x64 product
-    const int dt = wv & 1;                             // waves 2, 3: head-dimension tile
 
     // ---- 2. G = W W^T, X = tril(Q W^T), Y = strictly_upper(K W^T); products with Q and K
     f32x16 g = {};
-    f32x16 s[2], qi[2], ki[2];  // waves 0,1: diagonal logits K Q^T; waves 2,3: Q^T, K^T tiles
-    tile_mma<S, true, true>(g, sW, sW, mt, nt, D, lane);
+    f32x16 s[2];                     // waves 0,1: diagonal logits K Q^T
+    f32x16 qi[2], ki[2];             // D = 64, waves 2,3: Q^T, K^T tiles of head-dimension tile wv & 1
+    tile_mma<S, true, true, SPD, SPD>(g, sW, sW, mt, nt, D, lane);
     {
         // X^T = W Q^T and Y^T = W K^T, stored back transposed (4 contiguous elements per store)
         f32x16 c = {};
-        tile_mma<S, true, true>(c, sW, sQ, mt, nt, D, lane);
-        store_tile_t<S>(sX, c, mt, nt, lane, [](int cc, int i) { return cc <= i; });
+        tile_mma<S, true, true, SPD, SPD>(c, sW, sQ, mt, nt, D, lane);
+        store_tile_t<S, SP>(sX, c, mt, nt, lane, [](int cc, int i) { return cc <= i; });
         c = f32x16{};
-        tile_mma<S, true, true>(c, sW, sK, mt, nt, D, lane);
-        store_tile_t<S>(sY, c, mt, nt, lane, [](int r, int j) { return r > j; });
+        tile_mma<S, true, true, SPD, SPD>(c, sW, sK, mt, nt, D, lane);
+        store_tile_t<S, SP>(sY, c, mt, nt, lane, [](int r, int j) { return r > j; });
     }
     if (wv < 2) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             s[rt] = f32x16{};
-            tile_mma<S, true, true>(s[rt], sK, sQ, 32 * rt, 32 * wv, D, lane);
+            tile_mma<S, true, true, SPD, SPD>(s[rt], sK, sQ, 32 * rt, 32 * wv, D, lane);
         }
-    } else {
+    } else if constexpr (D == 64) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            load_tile_t<S>(qi[t], sQ, 32 * dt, 32 * t, lane);
-            load_tile_t<S>(ki[t], sK, 32 * dt, 32 * t, lane);
+            load_tile_t<S, SPD>(qi[t], sQ, 32 * (wv & 1), 32 * t, lane);
+            load_tile_t<S, SPD>(ki[t], sK, 32 * (wv & 1), 32 * t, lane);
         }
     }
     __syncthreads();  // Q, K dead: their space becomes G and E
@@ -405,6 +439,11 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
             const S *ve = (const S *)&vreg[s2];
 #pragma unroll
             for (int e = 0; e < CH; ++e) sVt[(cw * CH + e) * SP + vr] = ve[e];
+            if constexpr (kWtLate) {  // W is dead since phase 2: its slot becomes W^T
+                const S *we = (const S *)&wreg[s2];
+#pragma unroll
+                for (int e = 0; e < CH; ++e) sWt[(cw * CH + e) * SP + vr] = we[e];
+            }
         }
     }
     __syncthreads();
@@ -423,14 +462,14 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
         for (int rt = 0; rt < 2; ++rt) {
             zt[rt] = f32x16{};
             if constexpr (kBf)
-                tile_mma<S, true, true>(zt[rt], sAup, sX, 32 * rt, 32 * ct, 64, lane);
+                tile_mma<S, true, true, SP, SP>(zt[rt], sAup, sX, 32 * rt, 32 * ct, 64, lane);
             else
-                tile_mma<S, false, true>(zt[rt], sA, sX, 32 * rt, 32 * ct, 64, lane);
+                tile_mma<S, false, true, SP, SP>(zt[rt], sA, sX, 32 * rt, 32 * ct, 64, lane);
 #pragma unroll
             for (int r = 0; r < 16; ++r) zt[rt][r] = -zt[rt][r];
         }
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) tile_mma_breg<S, true>(s[rt], sY, 32 * rt, zt, lane);
+        for (int rt = 0; rt < 2; ++rt) tile_mma_breg<S, true, SP>(s[rt], sY, 32 * rt, zt, lane);
         const float c2 = a.scale * kLog2e;
         const float cli = FOX ? sCl[i] : 0.f;
         float mx = -INFINITY;
@@ -456,17 +495,17 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
                 sum += p;
             }
         sum = other_half_sum(sum);
-        f32x16 o[D / 32];
+        f32x16 o[DT];
 #pragma unroll
-        for (int d2 = 0; d2 < D / 32; ++d2) o[d2] = f32x16{};
+        for (int d2 = 0; d2 < DT; ++d2) o[d2] = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             auto pf = acc_frag<S>(s[kc >> 1], kc & 1);
 #pragma unroll
-            for (int d2 = 0; d2 < D / 32; ++d2) {
-                auto vf = lds_frag<S, true>(sVt, 32 * d2 + l32, 16 * kc, h);
+            for (int d2 = 0; d2 < DT; ++d2) {
+                auto vf = lds_frag<S, true, SP>(sVt, 32 * d2 + l32, 16 * kc, h);
                 Elem<S>::mma(o[d2], vf, pf);
-                if (d2 == wv) {  // each of the two waves stores half of the V^T record
+                if ((d2 & 1) == wv) {  // each of the two waves stores half of the V^T record
                     S *dst = recV + ((int64_t)(d2 * 4 + kc) * 64 + lane) * 8;
                     *(typename Elem<S>::Frag *)dst = vf;
                 }
@@ -481,24 +520,28 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
             const float inv = 1.f / sum;
             S *go = (S *)a.out + tok0 * D;
 #pragma unroll
-            for (int d2 = 0; d2 < D / 32; ++d2) store_rows_t<S, D>(go, o[d2], 32 * d2, i, inv, lane);
+            for (int d2 = 0; d2 < DT; ++d2) store_rows_t<S, D>(go, o[d2], 32 * d2, i, inv, lane);
             if (h == 0 && a.lse) a.lse[tok0 + i] = (mx + __log2f(sum)) * kLn2;
         }
-    } else {
+    }
+    if (wv >= 2 || D > 64) {
         // ---- 4b. head-dimension tile dt: -U = -A W and -R = -A^T W (rows = block
         //      token, cols = d), then qhat^T = Q^T - U^T X^T, khat^T = K^T - R^T Y^T
         //      and (-M)^T = -W^T U, each using those accumulators as operands.
+        //      D = 64: waves 2, 3 take one tile each; D = 128: every wave takes
+        //      one (waves 0, 1 after the diagonal block).
+        const int dt = D == 64 ? (wv & 1) : (wv ^ 2);
         f32x16 nu[2], nr[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             nu[rt] = f32x16{};
             nr[rt] = f32x16{};
             if constexpr (kBf) {
-                tile_mma<S, true, true>(nu[rt], sA, sWt, 32 * rt, 32 * dt, 64, lane);
-                tile_mma<S, true, true>(nr[rt], sAup, sWt, 32 * rt, 32 * dt, 64, lane);
+                tile_mma<S, true, true, SP, SP>(nu[rt], sA, sWt, 32 * rt, 32 * dt, 64, lane);
+                tile_mma<S, true, true, SP, SP>(nr[rt], sAup, sWt, 32 * rt, 32 * dt, 64, lane);
             } else {
-                tile_mma<S, true, false>(nu[rt], sA, sW, 32 * rt, 32 * dt, 64, lane);
-                tile_mma<S, false, false>(nr[rt], sA, sW, 32 * rt, 32 * dt, 64, lane);
+                tile_mma<S, true, false, SP, SPD>(nu[rt], sA, sW, 32 * rt, 32 * dt, 64, lane);
+                tile_mma<S, false, false, SP, SPD>(nr[rt], sA, sW, 32 * rt, 32 * dt, 64, lane);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -509,18 +552,22 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
         S *gqh = (S *)((char *)a.ws + lay.off_qhat) + (bh * lay.lp + row0) * D;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            tile_mma_areg<S, true>(qi[t], nu, sX, 32 * t, lane);
+            if constexpr (D > 64) {
+                load_tile_t_global<S, D>(qi[t], (const S *)a.q + tok0 * D, 32 * dt, 32 * t, nvalid, lane);
+                load_tile_t_global<S, D>(ki[t], (const S *)a.k + tok0 * D, 32 * dt, 32 * t, nvalid, lane);
+            }
+            tile_mma_areg<S, true, SP>(qi[t], nu, sX, 32 * t, lane);
             store_rows_t<S, D>(gqh, qi[t], 32 * dt, 32 * t + l32, 1.f, lane);
-            tile_mma_areg<S, true>(ki[t], nr, sY, 32 * t, lane);
+            tile_mma_areg<S, true, SP>(ki[t], nr, sY, 32 * t, lane);
             store_frags<S>(recK, ki[t], t * KCH + 2 * dt, lane);
         }
 #pragma unroll
-        for (int rt2 = 0; rt2 < 2; ++rt2) {
+        for (int rt2 = 0; rt2 < DT; ++rt2) {
             f32x16 c = {};
             if constexpr (kBf)
-                tile_mma_breg<S, true>(c, sWt, 32 * rt2, nu, lane);
+                tile_mma_breg<S, true, SP>(c, sWt, 32 * rt2, nu, lane);
             else
-                tile_mma_breg<S, false>(c, sW, 32 * rt2, nu, lane);
+                tile_mma_breg<S, false, SPD>(c, sW, 32 * rt2, nu, lane);
             store_frags<S>(recM, c, dt * KCH + 2 * rt2, lane);
         }
     }
@@ -536,11 +583,17 @@ static hipError_t launch_prep_t(const PrepArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st) {
-    if (a.d != 64) return hipErrorInvalidValue;
+template <int D>
+static hipError_t launch_prep_d(const PrepArgs &a, bool bf16, hipStream_t st) {
     const bool fox = a.logf != nullptr;
-    if (bf16) return fox ? launch_prep_t<uint16_t, 64, true>(a, st) : launch_prep_t<uint16_t, 64, false>(a, st);
-    return fox ? launch_prep_t<float, 64, true>(a, st) : launch_prep_t<float, 64, false>(a, st);
+    if (bf16) return fox ? launch_prep_t<uint16_t, D, true>(a, st) : launch_prep_t<uint16_t, D, false>(a, st);
+    return fox ? launch_prep_t<float, D, true>(a, st) : launch_prep_t<float, D, false>(a, st);
+}
+
+hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st) {
+    if (a.d == 64) return launch_prep_d<64>(a, bf16, st);
+    if (a.d == 128) return launch_prep_d<128>(a, bf16, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace path

@@ -40,7 +40,8 @@ def test_workspace_sizes():
     assert lib.path_attn_fwd_workspace_size(1, 1, 64, 64, BF) > 0
     assert lib.path_attn_fwd_workspace_size(0, 1, 64, 64, BF) == 0
     assert lib.path_attn_fwd_workspace_size(1, 1, 0, 64, BF) == 0
-    assert lib.path_attn_fwd_workspace_size(1, 1, 64, 128, BF) == 0   # unsupported head size
+    assert lib.path_attn_fwd_workspace_size(1, 1, 64, 96, BF) == 0    # unsupported head size
+    assert lib.path_attn_fwd_workspace_size(1, 1, 64, 128, BF) > lib.path_attn_fwd_workspace_size(1, 1, 64, 64, BF)
     assert lib.path_attn_fwd_workspace_size(1, 1, 64, 64, 7) == 0     # bad dtype
     a = lib.path_attn_fwd_workspace_size(2, 3, 65, 64, BF)
     b = lib.path_attn_fwd_workspace_size(2, 3, 128, 64, BF)
@@ -75,7 +76,8 @@ def fwd_call(**over):
     (dict(B=0), pa.PATH_EINVAL),
     (dict(H=-1), pa.PATH_EINVAL),
     (dict(L=0), pa.PATH_EINVAL),
-    (dict(d=128), pa.PATH_EUNSUPPORTED),
+    (dict(d=96), pa.PATH_EUNSUPPORTED),
+    (dict(d=32), pa.PATH_EUNSUPPORTED),
     (dict(d=0), pa.PATH_EINVAL),
     (dict(dtype=5), pa.PATH_EINVAL),
     (dict(wsb=16), pa.PATH_EINVAL),
@@ -107,6 +109,7 @@ def dec_call(**over):
     (dict(kn=P(90), vn=P(91)), pa.PATH_EINVAL),                # no room for the new row
     (dict(kc=None), pa.PATH_EINVAL),
     (dict(d=32), pa.PATH_EUNSUPPORTED),
+    (dict(d=256), pa.PATH_EUNSUPPORTED),
     (dict(wsb=8), pa.PATH_EINVAL),
     (dict(q=ctypes.c_void_p(A * 81 + 4)), pa.PATH_EINVAL),
     (dict(vc=P(0)), pa.PATH_EINVAL),                           # caches alias

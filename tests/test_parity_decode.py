@@ -89,6 +89,34 @@ def test_decode_bf16(n, append):
 
 
 @gpu
+@pytest.mark.parametrize("n,append", [(1, False), (7, True), (1000, False), (4097, True)])
+def test_decode_fp32_d128(n, append):
+    B, H, d = 2, 3, 128
+    say("case decode fp32 d128 n=%d append=%s" % (n, append))
+    x = pathgen.decode_inputs(B, H, n, d, steps=1, dtype="f32", seed=50 + n, device="cuda", rowcap=n + 1)
+    kn = vn = None
+    if append:
+        kn = torch.randn(B, H, d, device="cuda")
+        vn = torch.randn(B, H, d, device="cuda")
+    step_and_check(x["kcache"], x["vcache"], n, x["q"][0], x["w"][0], x["beta"][0], kn, vn, dtype="f32")
+
+
+@gpu
+@pytest.mark.parametrize("n,append", [(4096, False), (333, True)])
+def test_decode_bf16_d128(n, append):
+    B, H, d = 2, 4, 128
+    say("case decode bf16 d128 n=%d append=%s" % (n, append))
+    x = pathgen.decode_inputs(B, H, n, d, steps=2, dtype="bf16", seed=17, clip=1.98, device="cuda", rowcap=n + 2)
+    for t in range(2):
+        kn = vn = None
+        rows = n + (t if append else 0)
+        if append:
+            kn = torch.randn(B, H, d, device="cuda").to(torch.bfloat16)
+            vn = torch.randn(B, H, d, device="cuda").to(torch.bfloat16)
+        step_and_check(x["kcache"], x["vcache"], rows, x["q"][t], x["w"][t], x["beta"][t], kn, vn)
+
+
+@gpu
 def test_decode_bf16_peaky():
     """q scaled x8 so attention concentrates and |o| = O(1): a skipped or wrong update shows clearly."""
     B, H, n, d = 2, 2, 4096, 64
@@ -111,10 +139,11 @@ def test_decode_workload_full_size():
 
 
 @gpu
-def test_decode_reproduces_forward_fp32():
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_reproduces_forward_fp32(d):
     """Decoding token by token from an empty cache gives the forward pass's rows."""
-    B, H, T, d = 1, 2, 70, 64
-    say("case decode vs forward")
+    B, H, T = 1, 2, 70
+    say("case decode vs forward d%d" % d)
     x = pathgen.fwd_inputs(B, H, T, d, "f32", seed=21, device="cuda")
     fo, fl = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], return_lse=True)
     ro, rl = oracle.fwd(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["w"].cpu(), x["beta"].cpu())

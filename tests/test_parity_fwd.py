@@ -72,6 +72,24 @@ def test_fwd_bf16_small(B, H, L, fox):
     run_and_compare(B, H, L, 64, "bf16", fox, seed=2000 + L)
 
 
+D128_FP32_CASES = [(1, 2, 64), (1, 1, 1), (1, 1, 65), (1, 2, 200), (2, 1, 257), (1, 1, 700)]
+
+
+@gpu
+@pytest.mark.parametrize("B,H,L", D128_FP32_CASES, ids=lambda v: str(v))
+@pytest.mark.parametrize("fox", [False, True], ids=["path", "fox"])
+def test_fwd_fp32_d128(B, H, L, fox):
+    run_and_compare(B, H, L, 128, "f32", fox, seed=3000 + L)
+
+
+@gpu
+@pytest.mark.parametrize("B,H,L", [(1, 2, 64), (2, 2, 200), (1, 2, 1000), (1, 1, 1), (1, 1, 333), (1, 1, 2048)],
+                         ids=lambda v: str(v))
+@pytest.mark.parametrize("fox", [False, True], ids=["path", "fox"])
+def test_fwd_bf16_d128_small(B, H, L, fox):
+    run_and_compare(B, H, L, 128, "bf16", fox, seed=4000 + L)
+
+
 @gpu
 def test_fwd_bf16_beta_extremes():
     """beta at the ends of its range: near 0 (plain attention) and exactly 2 (reflections) in fp32."""
@@ -88,7 +106,7 @@ def test_fwd_bf16_beta_extremes():
 
 @gpu
 @pytest.mark.parametrize("name", ["lm760m_L4096_bf16", "sweep_L1024_d64_bf16", "sweep_L2048_d64_bf16",
-                                  "sweep_L4096_d64_bf16"])
+                                  "sweep_L4096_d64_bf16", "sweep_L4096_d128_bf16"])
 def test_fwd_workload_full_heads(name):
     """Full-size workload; two whole heads (first and last) compared row by row."""
     c = pathgen.WORKLOADS[name]
