@@ -251,7 +251,6 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
     __shared__ __attribute__((aligned(16))) S fixed[C::FIX];
     __shared__ __attribute__((aligned(16))) char region[C::RB];
     __shared__ float sBeta[64], sCl[64];
-    __shared__ __attribute__((aligned(16))) float sT[3][16][20];
 
     S *sW = fixed, *sX = fixed + C::WSLOT, *sY = fixed + C::WSLOT + MAT;
     S *sWt = kBf ? (kWtLate ? fixed : fixed + C::WSLOT + 2 * MAT) : nullptr;
@@ -376,41 +375,33 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
         for (int cc = 0; cc < 4; ++cc) sE[(I16 + 4 * cc + p) * GS + I16 + t] = xs[cc];
     }
     __syncthreads();
-    // (b) off-diagonal tiles by distance from the diagonal:
-    //     E_IJ = -E_II T_IJ,  T_IJ = D_I sum_{K=J}^{I-1} G_IK E_KJ
+    // (b) off-diagonal tiles by distance from the diagonal, one tile per wave:
+    //     E_IJ = -E_II T_IJ,  T_IJ = D_I sum_{K=J}^{I-1} G_IK E_KJ,
+    //     as 16x16x4 fp32 matrix-core products.  With the k order k(s, g) = 4g + s
+    //     (lane group g = lane / 16 supplies k = 4g + s at step s), register s of
+    //     a 16x16 accumulator (rows 4g .. 4g+3, column lane % 16) is exactly the B
+    //     operand of step s, so T feeds the second product from registers.
 #pragma unroll
     for (int lev = 1; lev < 4; ++lev) {
-        // one work item = 4 adjacent columns of one row of one tile
-        const int b = tid >> 6, r = (tid >> 2) & 15, t4 = 4 * (tid & 3), I = lev + b;
-        const bool act = b < 4 - lev;
-        if (act) {
-            const float *gr = sG + (16 * I + r) * GS + 16 * b;
-            const float *ec = sE + 16 * b * GS + 16 * b + t4;
-            // four independent accumulators keep the dependent FMA chains short
-            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, a3 = a0;
+        if (wv < 4 - lev) {
+            const int Jt = wv, It = wv + lev, i16 = lane & 15, g4 = 4 * (lane >> 4);
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < 16 * lev; c += 4) {
-                const f32x4 gv = *(const f32x4 *)(gr + c);
-                a0 += gv.x * *(const f32x4 *)(ec + c * GS);
-                a1 += gv.y * *(const f32x4 *)(ec + (c + 1) * GS);
-                a2 += gv.z * *(const f32x4 *)(ec + (c + 2) * GS);
-                a3 += gv.w * *(const f32x4 *)(ec + (c + 3) * GS);
-            }
-            *(f32x4 *)&sT[b][r][t4] = sBeta[16 * I + r] * ((a0 + a1) + (a2 + a3));
-        }
-        __syncthreads();
-        if (act) {
-            const float *er = sE + (16 * I + r) * GS + 16 * I;  // E_II row r: zero above the diagonal
-            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, a3 = a0;
+            for (int K = Jt; K < It; ++K) {
+                const f32x4 ga = *(const f32x4 *)(sG + (16 * It + i16) * GS + 16 * K + g4);
 #pragma unroll
-            for (int c = 0; c < 16; c += 4) {
-                const f32x4 ev = *(const f32x4 *)(er + c);
-                a0 += ev.x * *(const f32x4 *)&sT[b][c][t4];
-                a1 += ev.y * *(const f32x4 *)&sT[b][c + 1][t4];
-                a2 += ev.z * *(const f32x4 *)&sT[b][c + 2][t4];
-                a3 += ev.w * *(const f32x4 *)&sT[b][c + 3][t4];
+                for (int st = 0; st < 4; ++st)
+                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[st], sE[(16 * K + g4 + st) * GS + 16 * Jt + i16], t,
+                                                             0, 0, 0);
             }
-            *(f32x4 *)(sE + (16 * I + r) * GS + 16 * b + t4) = -((a0 + a1) + (a2 + a3));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) t[r] *= sBeta[16 * It + g4 + r];
+            const f32x4 ea = *(const f32x4 *)(sE + (16 * It + i16) * GS + 16 * It + g4);
+            f32x4 e = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) e = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[st], t[st], e, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sE[(16 * It + g4 + r) * GS + 16 * Jt + i16] = -e[r];
         }
         __syncthreads();
     }

@@ -4,8 +4,10 @@
 A step is one causal PaTH forward pass (prep + scan kernels) over the
 B32 H32 L4096 d64 bf16 workload; K steps are timed after W warm-up steps.
 Alongside it the decode step (B16 H32 d64, 32768 cached rows, bf16, 64 steps
-with fresh q, w, beta each) is timed, and the fp64 CPU oracle is timed on a
-bounded sample of the forward workload.  Prints one JSON line.
+with fresh q, w, beta each) and the other forward workloads (L 1024 - 8192 at
+d64, L4096 at d128, B8 H16 L4096, PaTH-FoX B4 H16 L16384) are timed, and the
+fp64 CPU oracle is timed on a bounded sample of the forward workload.  Prints
+one JSON line.
 
 Work units (fixed, declared):
   forward  F = 4 B H L^2 d flop: per causal pair of 64-token blocks the query-
@@ -33,6 +35,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
 METRIC = "PaTH fwd TFLOP/s + % MFMA peak (B32 H32 d64 L4096); decode-step HBM GB/s"
 FWD_WORKLOAD = "sweep_L4096_d64_bf16"
 DEC_WORKLOAD = "decode_N32768_bf16"
+SWEEP_WORKLOADS = ["sweep_L1024_d64_bf16", "sweep_L2048_d64_bf16", "sweep_L8192_d64_bf16", "sweep_L4096_d128_bf16",
+                   "lm760m_L4096_bf16", "fox_L16384_bf16"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_path_fwd_kernel_B32H32L4096.txt")
 KERNEL_SOURCES = ["attention_fwd_amd/csrc/path_fwd.hip", "attention_fwd_amd/csrc/path_common.h",
                   "attention_fwd_amd/csrc/path_layout.h"]
@@ -67,13 +71,13 @@ def read_traffic():
         return None
 
 
-def bench_forward(steps, warmup):
+def bench_forward(steps, warmup, name=FWD_WORKLOAD):
     import torch
 
     import attention_fwd_amd as pa
     import pathgen
 
-    c = pathgen.WORKLOADS[FWD_WORKLOAD]
+    c = pathgen.WORKLOADS[name]
     B, H, L, d = c["B"], c["H"], c["L"], c["d"]
     x = pathgen.fwd_inputs(B, H, L, d, c["dtype"], seed=0, fox=c["fox"], clip=c["clip"], device="cuda")
     out = torch.empty_like(x["q"])
@@ -106,6 +110,25 @@ def bench_forward(steps, warmup):
     flops = 4.0 * B * H * L * L * d
     return dict(B=B, H=H, L=L, d=d, flops=flops, wall_s=wall, ms_per_step=wall * 1e3 / steps,
                 prep_ms=prep_ms, scan_ms=scan_ms, x=x)
+
+
+def bench_sweep(steps, warmup):
+    """The other forward workloads, timed the same way (not the headline line)."""
+    import torch
+
+    res = {}
+    for name in SWEEP_WORKLOADS:
+        f = bench_forward(steps, warmup, name)
+        del f["x"]
+        torch.cuda.empty_cache()
+        tf = f["flops"] / (f["ms_per_step"] * 1e-3) / 1e12
+        res[name] = {"ms_per_step": round(f["ms_per_step"], 4), "prep_ms": round(f["prep_ms"], 4),
+                     "scan_ms": round(f["scan_ms"], 4), "TFLOP_per_s": round(tf, 1),
+                     "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "tokens_per_s": round(f["B"] * f["L"] / (f["ms_per_step"] * 1e-3))}
+        log("sweep %s: %.3f ms/step (prep %.3f, scan %.3f) %.1f TFLOP/s" %
+            (name, f["ms_per_step"], f["prep_ms"], f["scan_ms"], tf))
+    return res
 
 
 def bench_decode(steps):
@@ -170,6 +193,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline budget; 0 skips it")
+    ap.add_argument("--sweep-steps", type=int, default=5, help="timed steps per other forward workload; 0 skips them")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the PaTH hot path here has no multi-GPU mode "
@@ -188,6 +212,9 @@ def main():
     log("decode: %s, %d steps" % (DEC_WORKLOAD, args.decode_steps))
     dres = bench_decode(args.decode_steps)
     log("decode: %.3f ms/step" % dres["step_ms"])
+    sweep = None
+    if args.sweep_steps > 0:
+        sweep = bench_sweep(args.sweep_steps, 2)
     cpu = None
     if args.cpu_seconds > 0:
         log("cpu baseline: oracle, ~%.0f s" % args.cpu_seconds)
@@ -225,6 +252,7 @@ def main():
                                 "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None},
                    "tokens_per_s": round(dres["B"] / (dres["step_ms"] * 1e-3)), "bytes_per_step": dres["bytes"],
                    "steps": dres["steps"]},
+        "other_workloads": sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
