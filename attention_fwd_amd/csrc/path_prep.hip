@@ -42,20 +42,25 @@ struct PrepCfg {
     static constexpr int MAT = 64 * SP;    // one 64 x 64 matrix
     static constexpr int MATD = 64 * SPD;  // one 64 x D matrix, token rows
     static constexpr int MATT = D * SP;    // one D x 64 matrix, head-dimension rows
-    static constexpr int GS = 68;          // fp32 row stride of G and E in the solve
+    // G and E of the triangular solve: fp32, only the ten 16 x 16 tiles on or
+    // below the diagonal, tile (I, K) at TS * (I (I + 1) / 2 + K), row pitch TP.
+    static constexpr int TP = 20, TS = 16 * TP;
     // W, X, Y live for the whole kernel.  bf16 also keeps W^T (fp32 has no
-    // room for transposed copies and reads them with a stride instead): at
-    // D = 64 in a slot of its own, written while W is staged; at D = 128 in
-    // W's slot once the products with W are done, written from registers, so
-    // that two workgroups still fit in one CU.  A second region is reused: Q,
-    // K while the products with them run, then G and E for the triangular
-    // solve, then A, A^T (bf16) and V^T.
-    static constexpr bool kWtLate = kBf && D > 64;
+    // room for transposed copies and reads them with a stride instead) in W's
+    // slot once the products with W are done, written from registers.  A
+    // second region is reused: Q, K while the products with them run, then G
+    // and E for the triangular solve, then A (fp32) or A^T (bf16; A is read
+    // from it with a stride) and V^T.  At D = 64, bf16, this is 53.8 KB, so
+    // three workgroups share a CU.
+    static constexpr bool kWtLate = kBf;
     static constexpr int WSLOT = kWtLate ? cmax(MATD, MATT) : MATD;
-    static constexpr int FIX = WSLOT + 2 * MAT + ((kBf && !kWtLate) ? MATT : 0);  // elements
-    static constexpr int RB = cmax(cmax(2 * MATD * (int)sizeof(S), 2 * 64 * GS * 4),
-                                   ((kBf ? 2 : 1) * MAT + MATT) * (int)sizeof(S));
+    static constexpr int FIX = WSLOT + 2 * MAT;  // elements
+    static constexpr int RB = cmax(cmax(2 * MATD * (int)sizeof(S), 2 * 10 * TS * 4), (MAT + MATT) * (int)sizeof(S));
+    static constexpr int WG_PER_CU = kBf ? (D == 64 ? 3 : 2) : 1;
 };
+
+// Offset (floats) of tile (I, K), K <= I, in the packed lower-triangular tile store.
+__device__ __forceinline__ int tri_tile(int I, int K) { return (I * (I + 1) / 2 + K) * (16 * 20); }
 
 // Fragment of the matrix view `m` (element (row, k) at row*SP + k when KC, at
 // k*SP + row otherwise; SP = row stride in elements) for rows `row`, k in [k0, k0+16).
@@ -239,10 +244,11 @@ __device__ __forceinline__ void load_tile_t_global(f32x16 &c, const S *src, int 
 }
 
 template <typename S, int D, bool FOX>
-__global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_kernel(PrepArgs a) {
     static_assert(D == 64 || D == 128, "prep kernel: head dimension 64 or 128");
     typedef PrepCfg<S, D> C;
-    constexpr int SP = C::SP, SPD = C::SPD, MAT = C::MAT, GS = C::GS;
+    constexpr int SP = C::SP, SPD = C::SPD, MAT = C::MAT, TP = C::TP;
+    static_assert(C::TS == 16 * 20, "tri_tile assumes 16 x 20 tiles");
     constexpr bool kBf = C::kBf, kWtLate = C::kWtLate;
     constexpr int CH = 16 / (int)sizeof(S);  // elements per 16-byte chunk
     constexpr int RCH = D / CH;              // chunks per row
@@ -253,11 +259,11 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
     __shared__ float sBeta[64], sCl[64];
 
     S *sW = fixed, *sX = fixed + C::WSLOT, *sY = fixed + C::WSLOT + MAT;
-    S *sWt = kBf ? (kWtLate ? fixed : fixed + C::WSLOT + 2 * MAT) : nullptr;
-    S *sQ = (S *)region, *sK = (S *)region + C::MATD;                 // phases 1-2
-    float *sG = (float *)region, *sE = (float *)region + 64 * GS;     // phase 3
-    S *sA = (S *)region, *sAup = kBf ? (S *)region + MAT : nullptr;  // phase 4
-    S *sVt = (S *)region + (kBf ? 2 : 1) * MAT;
+    S *sWt = kBf ? fixed : nullptr;
+    S *sQ = (S *)region, *sK = (S *)region + C::MATD;               // phases 1-2
+    float *sG = (float *)region, *sE = (float *)region + 10 * C::TS;  // phase 3
+    S *sA = kBf ? nullptr : (S *)region, *sAup = kBf ? (S *)region : nullptr;  // phase 4
+    S *sVt = (S *)region + MAT;
 
     const int L = a.L;
     const FwdLayout lay = fwd_layout(a.B, a.H, L, D, sizeof(S));
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
 
     // ---- 1. stage W, Q, K in LDS and V in registers (zero rows past L), beta, forget-gate prefix
     u32x4 vreg[VPT];
-    u32x4 wreg[kWtLate ? VPT : 1];
+    u32x4 wreg[VPT];
     {
         const S *gq = (const S *)a.q + tok0 * D, *gk = (const S *)a.k + tok0 * D;
         const S *gw = (const S *)a.w + tok0 * D, *gv = (const S *)a.v + tok0 * D;
@@ -295,13 +301,7 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
             }
             vreg[s] = vv;
             *(u32x4 *)(sW + rw * SPD + cw * CH) = vw;
-            if constexpr (kWtLate) {
-                wreg[s] = vw;
-            } else if constexpr (kBf) {
-                const S *we = (const S *)&vw;
-#pragma unroll
-                for (int e = 0; e < CH; ++e) sWt[(cw * CH + e) * SP + rw] = we[e];
-            }
+            wreg[s] = vw;
         }
         if (tid < 64) sBeta[tid] = tid < nvalid ? a.beta[tok0 + tid] : 0.f;
         if (FOX && wv == 0) {
@@ -352,9 +352,14 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
             load_tile_t<S, SPD>(ki[t], sK, 32 * (wv & 1), 32 * t, lane);
         }
     }
-    __syncthreads();  // Q, K dead: their space becomes G and E
+    __syncthreads();  // Q, K dead: their space becomes G and E (tiles on or below the diagonal)
+    if (mt >= nt) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sG[(mt + acc_row(r, h)) * GS + nt + l32] = g[r];
+        for (int r = 0; r < 16; ++r) {
+            const int row = mt + acc_row(r, h), col = nt + l32;
+            if ((row >> 4) >= (col >> 4)) sG[tri_tile(row >> 4, col >> 4) + (row & 15) * TP + (col & 15)] = g[r];
+        }
+    }
     __syncthreads();
 
     // ---- 3. E = (I + strictly_lower(D_b G))^-1 in 16 x 16 tiles, A = E D_b.
@@ -363,16 +368,17 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
     {
         const int I16 = 16 * wv, t = lane >> 2, p = lane & 3;
         float xs[4] = {0.f, 0.f, 0.f, 0.f};
+        const float *gt = sG + tri_tile(wv, wv);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float *gr = sG + (I16 + r) * GS + I16 + p;
+            const float *gr = gt + r * TP + p;
             float part = (gr[0] * xs[0] + gr[4] * xs[1]) + (gr[8] * xs[2] + gr[12] * xs[3]);
             part = sum4(part);
             const float x = (r == t) ? 1.f : (r > t ? -sBeta[I16 + r] * part : 0.f);
             if (p == (r & 3)) xs[r >> 2] = x;
         }
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) sE[(I16 + 4 * cc + p) * GS + I16 + t] = xs[cc];
+        for (int cc = 0; cc < 4; ++cc) sE[tri_tile(wv, wv) + (4 * cc + p) * TP + t] = xs[cc];
     }
     __syncthreads();
     // (b) off-diagonal tiles by distance from the diagonal, one tile per wave:
@@ -388,35 +394,38 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
             f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int K = Jt; K < It; ++K) {
-                const f32x4 ga = *(const f32x4 *)(sG + (16 * It + i16) * GS + 16 * K + g4);
+                const f32x4 ga = *(const f32x4 *)(sG + tri_tile(It, K) + i16 * TP + g4);
 #pragma unroll
                 for (int st = 0; st < 4; ++st)
-                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[st], sE[(16 * K + g4 + st) * GS + 16 * Jt + i16], t,
+                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[st], sE[tri_tile(K, Jt) + (g4 + st) * TP + i16], t,
                                                              0, 0, 0);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) t[r] *= sBeta[16 * It + g4 + r];
-            const f32x4 ea = *(const f32x4 *)(sE + (16 * It + i16) * GS + 16 * It + g4);
+            const f32x4 ea = *(const f32x4 *)(sE + tri_tile(It, It) + i16 * TP + g4);
             f32x4 e = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < 4; ++st) e = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[st], t[st], e, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sE[(16 * It + g4 + r) * GS + 16 * Jt + i16] = -e[r];
+            for (int r = 0; r < 4; ++r) sE[tri_tile(It, Jt) + (g4 + r) * TP + i16] = -e[r];
         }
         __syncthreads();
     }
     {
-        // A = E D_b (lower triangle only; E's upper tiles were never written).
-        // Thread (column c, 16 rows from rg): conflict-free column reads of E.
-        const int c = tid & 63, rg = 16 * (tid >> 6);
+        // A = E D_b (lower triangle only: tiles above the diagonal are not stored).
+        // Thread (column c, 16 rows of row tile wv).
+        const int c = tid & 63, rg = 16 * wv;
         const float bc = sBeta[c];
+        const bool tile_ok = (c >> 4) <= wv;
+        const float *et = sE + tri_tile(wv, tile_ok ? (c >> 4) : 0) + (c & 15);
         float av[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) av[e] = c <= rg + e ? sE[(rg + e) * GS + c] * bc : 0.f;
-        __syncthreads();  // E and G are dead: their space becomes A, A^T, V^T
+        for (int e = 0; e < 16; ++e) av[e] = (tile_ok && c <= rg + e) ? et[e * TP] * bc : 0.f;
+        __syncthreads();  // E and G are dead: their space becomes A (fp32) or A^T (bf16) and V^T
+        if constexpr (!kBf) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sA[(rg + e) * SP + c] = Elem<S>::from_float(av[e]);
-        if constexpr (kBf) {
+            for (int e = 0; e < 16; ++e) sA[(rg + e) * SP + c] = Elem<S>::from_float(av[e]);
+        } else {
 #pragma unroll
             for (int e = 0; e < 16; e += 8) {
                 const u32x4 u = {pack_bf16(av[e], av[e + 1]), pack_bf16(av[e + 2], av[e + 3]),
@@ -528,7 +537,7 @@ __global__ __launch_bounds__(256, 2) void path_prep_kernel(PrepArgs a) {
             nu[rt] = f32x16{};
             nr[rt] = f32x16{};
             if constexpr (kBf) {
-                tile_mma<S, true, true, SP, SP>(nu[rt], sA, sWt, 32 * rt, 32 * dt, 64, lane);
+                tile_mma<S, false, true, SP, SP>(nu[rt], sAup, sWt, 32 * rt, 32 * dt, 64, lane);
                 tile_mma<S, true, true, SP, SP>(nr[rt], sAup, sWt, 32 * rt, 32 * dt, 64, lane);
             } else {
                 tile_mma<S, true, false, SP, SPD>(nu[rt], sA, sW, 32 * rt, 32 * dt, 64, lane);
