@@ -80,6 +80,25 @@ struct FwdCfg {
     static constexpr int WG_PER_CU = D == 64 ? 2 : 1;
 };
 
+// The running max m of the online softmax is folded into the logit product
+// (bf16, no forget gate): the product gets one more 16-wide k-chunk whose A
+// rows are (1, 1, 0, ..., 0) and whose B column is (-m_hi, -m_lo, 0, ..., 0),
+// with m_hi, m_lo bf16 and m = m_hi + m_lo exactly, so the accumulator holds
+// s - m and each probability is a single exp2.  Only k = 0, 1 (fragment
+// elements 0, 1 of lane half 0) are non-zero.
+__device__ __forceinline__ float bf16_round(float x) { return bf16_to_f32(to_bf16(x)); }
+__device__ __forceinline__ i16x8 fold_ones(int h) {
+    const u32x4 u = {h == 0 ? 0x3F803F80u : 0u, 0u, 0u, 0u};
+    return __builtin_bit_cast(i16x8, u);
+}
+// Split m0 into two bf16 pieces; m becomes their (exact) sum, frag the B column.
+__device__ __forceinline__ void fold_split(float m0, int h, float &m, i16x8 &frag) {
+    const float hi = bf16_round(m0), lo = bf16_round(m0 - hi);
+    m = hi + lo;
+    const u32x4 u = {h == 0 ? pack_bf16(-hi, -lo) : 0u, 0u, 0u, 0u};
+    frag = __builtin_bit_cast(i16x8, u);
+}
+
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"
 // (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and
 // lgkmcnt left at their maxima so they are not waited for).
@@ -96,6 +115,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
     constexpr int KCH = D / 16, DT = D / 32;
     constexpr int VEC = 16 / (int)sizeof(S);   // elements per 16-byte load
     constexpr int NLD = REC / VEC / NT;        // 16-byte loads per thread per record
+    constexpr bool kFold = sizeof(S) == 2 && !FOX;  // running max folded into the logit product
     static_assert(REC % (VEC * NT) == 0, "record must split evenly over the workgroup");
     __shared__ __attribute__((aligned(32))) S srec[NB][REC];
     __shared__ float stail[NB][kBlk];
@@ -127,6 +147,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
     f32x16 qt[DT][CT], o[DT][CT];
     Frag qb[CT][KCH];
     float m[CT], lp[CT], off[CT];
+    i16x8 mb[CT];  // kFold: B column (-m_hi, -m_lo) of the extra k-chunk
     if (active) {
         const S *qh = (const S *)((const char *)a.ws + lay.off_qhat) + (bh * lay.lp + (int64_t)I * kBlk) * D;
         const S *od = (const S *)a.out + (bh * a.L + (int64_t)I * kBlk) * D;
@@ -138,8 +159,14 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
             const int i = c0 + 32 * ct + l32;
             const bool valid = (int64_t)I * kBlk + i < a.L;
             const int io = valid ? i : 0;  // rows past L read row 0 of the block, then drop it
+            float ls = ld[i];
             m[ct] = md[i];
-            const float ls = ld[i];
+            if constexpr (kFold) {
+                // switch the reference to the nearest two-piece bf16 value
+                const float m0 = m[ct];
+                fold_split(m0, h, m[ct], mb[ct]);
+                ls *= fast_exp2(m0 - m[ct]);
+            }
             lp[ct] = h == 0 ? ls : 0.f;
             off[ct] = FOX ? fq[i] : 0.f;
             const float os = valid ? ls : 0.f;
@@ -173,8 +200,9 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
             issue_record<S, REC, NLD, NW, FOX>(recs + (int64_t)(Jtop - k) * REC, fk + (int64_t)(Jtop - k) * kBlk,
                                                srec[k], stail[k], wv, lane);
 
-    const float c2 = a.scale * kLog2e;
+    // qhat comes pre-scaled by scale * log2(e): logits are in log2 units
     constexpr float kTau = 8.f;  // running max is refreshed only when it grows by more than 2^8
+    const i16x8 ones = fold_ones(h);
     for (int J = Jtop; J >= 0; --J) {
         const int it = Jtop - J, buf = it % NB;
         // wait for this wave's copies of record J; the copies of the NB - 2 newer
@@ -203,7 +231,10 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
                 // S^T = khat qt^T for this half
                 f32x16 s[CT];
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) s[ct] = f32x16{};
+                for (int ct = 0; ct < CT; ++ct) {
+                    s[ct] = f32x16{};
+                    if constexpr (kFold) s[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, mb[ct], s[ct], 0, 0, 0);
+                }
 #pragma unroll
                 for (int kc = 0; kc < KCH; ++kc) {
                     const Frag af = *(const Frag *)(sk + ((hf * KCH + kc) * 64 + lane) * 8);
@@ -229,37 +260,48 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
                     if (FOX) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            s[ct][r] = fmaf(s[ct][r], c2, stail[buf][32 * hf + acc_row(r, h)]);
+                            s[ct][r] += stail[buf][32 * hf + acc_row(r, h)];
                             mx = fmaxf(mx, s[ct][r]);
                         }
                         mx = other_half_max(mx) + off[ct];
                     } else {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ct][r]);
-                        mx = other_half_max(mx) * c2;
+                        mx = other_half_max(mx);  // kFold: relative to m
                     }
-                    if (__any(mx > m[ct] + kTau)) {
-                        const float mnew = fmaxf(m[ct], mx);
-                        const float alpha = fast_exp2(m[ct] - mnew);
+                    if (__any(mx > (kFold ? kTau : m[ct] + kTau))) {
+                        float mnew;
+                        if constexpr (kFold)
+                            fold_split(m[ct] + fmaxf(mx, 0.f), h, mnew, mb[ct]);
+                        else
+                            mnew = fmaxf(m[ct], mx);
+                        const float dlt = mnew - m[ct];
+                        const float alpha = fast_exp2(-dlt);
                         m[ct] = mnew;
                         lp[ct] *= alpha;
 #pragma unroll
                         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                             for (int r = 0; r < 16; ++r) o[dt][ct][r] *= alpha;
+                        if constexpr (kFold) {
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) s[ct][r] -= dlt;
+                        }
                     }
-                    float ps0 = 0.f, ps1 = 0.f;
                     if (FOX) {
                         const float sh = m[ct] - off[ct];
 #pragma unroll
                         for (int r = 0; r < 16; ++r) s[ct][r] = fast_exp2(s[ct][r] - sh);
+                    } else if constexpr (kFold) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) s[ct][r] = fast_exp2(s[ct][r]);
                     } else {
-                        const float nm = -m[ct];
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) s[ct][r] = fast_exp2(fmaf(s[ct][r], c2, nm));
+                        for (int r = 0; r < 16; ++r) s[ct][r] = fast_exp2(s[ct][r] - m[ct]);
                     }
+                    float ps0 = s[ct][0], ps1 = s[ct][1];
 #pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
+                    for (int r = 2; r < 16; r += 2) {
                         ps0 += s[ct][r];
                         ps1 += s[ct][r + 1];
                     }

@@ -6,7 +6,8 @@
 //   record J   : K-hat (64 x d), V^T (d x 64) and -M_J (d x d), each stored as
 //                matrix-core fragments (see path_common.h), contiguous, so the
 //                forward kernel streams one record per key block;
-//   qhat       : boundary-adjusted queries, [Lp, d] natural row order;
+//   qhat       : boundary-adjusted queries times scale * log2(e) (logits in
+//                log2 units), [Lp, d] natural row order;
 //   mdiag/ldiag: running max (log2 units) and sum of the diagonal block;
 //   fq/fk/fb   : forget-gate prefix terms (log2 units), used with logf only.
 #pragma once

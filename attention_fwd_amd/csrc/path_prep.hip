@@ -557,7 +557,7 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
                 load_tile_t_global<S, D>(ki[t], (const S *)a.k + tok0 * D, 32 * dt, 32 * t, nvalid, lane);
             }
             tile_mma_areg<S, true, SP>(qi[t], nu, sX, 32 * t, lane);
-            store_rows_t<S, D>(gqh, qi[t], 32 * dt, 32 * t + l32, 1.f, lane);
+            store_rows_t<S, D>(gqh, qi[t], 32 * dt, 32 * t + l32, a.scale * kLog2e, lane);  // log2 units
             tile_mma_areg<S, true, SP>(ki[t], nr, sY, 32 * t, lane);
             store_frags<S>(recK, ki[t], t * KCH + 2 * dt, lane);
         }
