@@ -56,7 +56,7 @@ struct PrepCfg {
     static constexpr int WSLOT = kWtLate ? cmax(MATD, MATT) : MATD;
     static constexpr int FIX = WSLOT + 2 * MAT;  // elements
     static constexpr int RB = cmax(cmax(2 * MATD * (int)sizeof(S), 2 * 10 * TS * 4), (MAT + MATT) * (int)sizeof(S));
-    static constexpr int WG_PER_CU = kBf ? (D == 64 ? 3 : 2) : 1;
+    static constexpr int WG_PER_CU = kBf ? (D == 64 ? 3 : 2) : 1;  // = waves per SIMD (4-wave workgroups)
 };
 
 // Offset (floats) of tile (I, K), K <= I, in the packed lower-triangular tile store.

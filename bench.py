@@ -37,26 +37,30 @@ FWD_WORKLOAD = "sweep_L4096_d64_bf16"
 DEC_WORKLOAD = "decode_N32768_bf16"
 SWEEP_WORKLOADS = ["sweep_L1024_d64_bf16", "sweep_L2048_d64_bf16", "sweep_L8192_d64_bf16", "sweep_L4096_d128_bf16",
                    "lm760m_L4096_bf16", "fox_L16384_bf16"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_path_fwd_kernel_B32H32L4096.txt")
-KERNEL_SOURCES = ["attention_fwd_amd/csrc/path_fwd.hip", "attention_fwd_amd/csrc/path_common.h",
-                  "attention_fwd_amd/csrc/path_layout.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_B32H32L4096_decode_N32768.txt")
+COPY_BYTES = 1 << 30        # calibration copy of the counter run
+KERNEL_SOURCES = {
+    "path_fwd_kernel": ["attention_fwd_amd/csrc/path_fwd.hip", "attention_fwd_amd/csrc/path_common.h",
+                        "attention_fwd_amd/csrc/path_layout.h"],
+    "path_decode_kernel": ["attention_fwd_amd/csrc/path_decode.hip", "attention_fwd_amd/csrc/path_common.h"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash():
+def kernel_hash(kernel):
     h = hashlib.sha256()
-    for s in KERNEL_SOURCES:
+    for s in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, s), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch of the scan kernel from committed counter runs, if
-    they were taken on the current kernel source (else None)."""
+def read_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if
+    the counters were taken on the current kernel source (else None)."""
     try:
         kv = {}
         with open(TRAFFIC_FILE) as f:
@@ -64,9 +68,9 @@ def read_traffic():
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     kv[k.strip()] = v.strip()
-        if kv.get("kernel_source_sha256_16") != kernel_hash():
+        if kv.get(kernel + ".source_sha256_16") != kernel_hash(kernel):
             return None
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[kernel + ".hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -161,6 +165,46 @@ def bench_decode(steps):
     return dict(B=B, H=H, n=n, d=d, steps=steps, step_ms=step_ms, wall_s=wall, bytes=nbytes)
 
 
+def counter_run(fwd_steps=2, dec_steps=2):
+    """No timing: the kernels a hardware-counter pass reads.  First a plain
+    device copy of COPY_BYTES (read and written once each, the calibration of
+    FETCH_SIZE / WRITE_SIZE), then forward steps of the headline workload and
+    decode steps of the decode workload."""
+    import torch
+
+    import attention_fwd_amd as pa
+    import pathgen
+
+    src = torch.ones(COPY_BYTES // 2, device="cuda", dtype=torch.bfloat16)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    c = pathgen.WORKLOADS[FWD_WORKLOAD]
+    x = pathgen.fwd_inputs(c["B"], c["H"], c["L"], c["d"], c["dtype"], seed=0, fox=c["fox"], clip=c["clip"],
+                           device="cuda")
+    out = torch.empty_like(x["q"])
+    lse = torch.empty(x["beta"].shape, device="cuda", dtype=torch.float32)
+    ws = torch.empty(pa.fwd_workspace_size(c["B"], c["H"], c["L"], c["d"], x["q"].dtype), device="cuda",
+                     dtype=torch.uint8)
+    for _ in range(fwd_steps):
+        pa.fwd_prep(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out, lse, ws)
+        pa.fwd_scan(out, lse, x["logf"] is not None, ws)
+    torch.cuda.synchronize()
+    del x, out, lse, ws
+    torch.cuda.empty_cache()
+    c = pathgen.WORKLOADS[DEC_WORKLOAD]
+    x = pathgen.decode_inputs(c["B"], c["H"], c["n"], c["d"], steps=dec_steps, dtype=c["dtype"], seed=0,
+                              clip=c["clip"], device="cuda")
+    ws = torch.empty(max(pa.decode_workspace_size(c["B"], c["H"], c["n"], c["d"], x["kcache"].dtype), 16),
+                     device="cuda", dtype=torch.uint8)
+    for t in range(dec_steps):
+        pa.decode_step(x["kcache"], x["vcache"], c["n"], x["q"][t], x["w"][t], x["beta"][t], workspace=ws)
+    torch.cuda.synchronize()
+    log("counter run done: copy %d bytes, %d forward steps, %d decode steps" % (COPY_BYTES, fwd_steps, dec_steps))
+
+
 def cpu_baseline(x, target_s):
     """The fp64 oracle, as it stands, on whole heads of the forward workload."""
     import oracle
@@ -194,6 +238,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline budget; 0 skips it")
     ap.add_argument("--sweep-steps", type=int, default=5, help="timed steps per other forward workload; 0 skips them")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="no timing: a calibration copy plus a few forward and decode steps, for rocprofv3 --pmc")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the PaTH hot path here has no multi-GPU mode "
@@ -206,6 +252,9 @@ def main():
 
     pa.lib()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
+    if args.counter_run:
+        counter_run()
+        return
     log("forward: %s, %d warm-up + %d timed steps" % (FWD_WORKLOAD, args.warmup, args.steps))
     f = bench_forward(args.steps, args.warmup)
     log("forward: %.3f ms/step (prep %.3f ms, scan %.3f ms)" % (f["ms_per_step"], f["prep_ms"], f["scan_ms"]))
@@ -223,7 +272,7 @@ def main():
 
     value = f["flops"] / (f["ms_per_step"] * 1e-3) / 1e12
     scan_tflops = f["flops"] / (f["scan_ms"] * 1e-3) / 1e12
-    traffic = read_traffic()
+    traffic = read_traffic("path_fwd_kernel")
     dec_gbs = dres["bytes"] / (dres["step_ms"] * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
@@ -249,7 +298,8 @@ def main():
                     "flop_per_step": f["flops"]},
         "decode": {"ms_per_step": round(dres["step_ms"], 4), "GB_per_s": round(dec_gbs, 1),
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                                "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                                "traffic": read_traffic("path_decode_kernel")},
                    "tokens_per_s": round(dres["B"] / (dres["step_ms"] * 1e-3)), "bytes_per_step": dres["bytes"],
                    "steps": dres["steps"]},
         "other_workloads": sweep,
