@@ -20,9 +20,18 @@
 // Softmax runs down accumulator columns: 32 values in-lane plus one swap
 // between lane halves.  The diagonal block was already folded into `out` and
 // the (max, sum) workspace by the prep kernel, so every block here is a full,
-// unmasked 64 x 64 tile.  A workgroup is 4 waves = 4 consecutive query blocks
+// unmasked 64 x 64 tile.
+//
+// A step J first issues its 36 matrix-core products (the 64-key logits and
+// the query transform, which is independent of the softmax), then takes the
+// column maxima of all 64 keys with a single check for the rare rescale, and
+// only then runs the vector work (exp2, column sums, bf16 probabilities)
+// interleaved with the 16 products of P V, so one branch-free region holds
+// the whole softmax.  A workgroup is 4 waves = 4 consecutive query blocks
 // sharing each key-block record (khat, V^T, -M: 24 KiB bf16 at d = 64),
-// double-buffered in LDS.
+// double-buffered in LDS; two workgroups share a CU.
+#include <type_traits>
+
 #include "path_common.h"
 #include "path_kernels.h"
 #include "path_layout.h"
@@ -53,31 +62,34 @@ typedef __attribute__((address_space(3))) void lds_void;
 // LDS base + 16 l).  Completion is tracked by vmcnt.
 template <typename S, int REC, int NLD, int NW, bool FOX>
 __device__ __forceinline__ void issue_record(const S *src, const float *tail, S *dst, float *dtail, int wv, int lane) {
-    constexpr int VEC = 16 / (int)sizeof(S);
+    // chunk t of thread tid is 16-byte chunk t * NT + tid: a uniform base plus
+    // the same per-lane offset for every t, so the addressing needs one VGPR
+    constexpr int NT = 64 * NW;
+    const int tid = 64 * wv + lane;
 #pragma unroll
     for (int t = 0; t < NLD; ++t) {
-        const int chunk = 64 * NW * t + 64 * wv;  // first 16-byte chunk of this wave
-        __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)(chunk + lane) * VEC),
-                                         (lds_void *)(dst + chunk * VEC), 16, 0, 0);
+        const char *g = (const char *)src + (size_t)t * NT * 16;
+        char *l = (char *)dst + (size_t)t * NT * 16 + 1024 * wv;  // the wave's LDS base (uniform)
+        __builtin_amdgcn_global_load_lds((const void *)(g + 16 * tid), (lds_void *)l, 16, 0, 0);
     }
     if (FOX && wv == 0) __builtin_amdgcn_global_load_lds((const void *)(tail + lane), (lds_void *)dtail, 4, 0, 0);
 }
 
 // Launch shape per element type and head dimension: NW waves per workgroup,
 // CT 32-query column tiles per wave (a workgroup covers NW * CT / 2 query
-// blocks that share every key-block record), NB key-block records in flight
-// (LDS buffers).  d = 64: 4 waves x 64 queries, two 24 KiB (bf16) records,
-// two workgroups per CU.  d = 128: a record is 64 KiB (bf16), and the query
-// state of 64 columns (q-tilde, O: 256 fp32 accumulators) no longer fits a
-// wave's registers, so waves take 32 queries and 8 of them share the records;
-// fp32 records (128 KiB) are single-buffered.
+// blocks that share every key-block record), NB key-block records in LDS.
+// d = 64: 4 waves x 64 queries, two records, two workgroups per CU.  d = 128:
+// a record is 64 KiB (bf16), and the query state of 64 columns (q-tilde, O:
+// 256 fp32 accumulators) no longer fits a wave's registers, so waves take 32
+// queries and 8 of them share the records; fp32 records (128 KiB) are
+// single-buffered.
 template <typename S, int D>
 struct FwdCfg {
     static constexpr int NW = D == 64 ? 4 : (sizeof(S) == 2 ? 8 : 4);
     static constexpr int CT = D == 64 ? 2 : 1;
     static constexpr int NB = (D == 128 && sizeof(S) == 4) ? 1 : 2;
     static constexpr int QB = NW * CT / 2;  // query blocks per workgroup
-    static constexpr int WG_PER_CU = D == 64 ? 2 : 1;
+    static constexpr int WG_PER_CU = D == 128 ? 1 : 2;
 };
 
 // The running max m of the online softmax is folded into the logit product
@@ -103,22 +115,185 @@ __device__ __forceinline__ void fold_split(float m0, int h, float &m, i16x8 &fra
 // (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and
 // lgkmcnt left at their maxima so they are not waited for).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// Same with lgkmcnt(0): this wave's LDS reads have returned as well.
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also wait for every outstanding global load, including the record copies
+// meant to stay in flight); the caller waits for what it needs first.  The
+// memory clobber keeps the compiler from moving loads or stores across it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// Per-wave state of the scan: query-side accumulators (transposed), output,
+// logit buffers (NS of them), and the online-softmax statistics (log2 units).
+template <int D, int CT, int NS>
+struct WaveState {
+    static constexpr int DT = D / 32;
+    f32x16 qt[DT][CT], o[DT][CT], s[NS][2][CT];
+    float m[CT], lp[CT], off[CT];
+    i16x8 mb[CT];  // folded max: B column (-m_hi, -m_lo) of the extra k-chunk
+};
+
+constexpr float kTau = 8.f;  // the running max is refreshed only when it grows by more than 2^kTau
+
+// Matrix-core part of step J into logit buffer SB: bf16 copy of qt as the B
+// operand, S^T = khat qt^T for all 64 keys, and qt <- P_J qt.
+template <typename S, int D, int CT, int NS, bool FOLD, int SB>
+__device__ __forceinline__ void step_mma(WaveState<D, CT, NS> &w, const S *rec, int lane, int h) {
+    typedef Elem<S> E;
+    typedef typename E::Frag Frag;
+    constexpr int KCH = D / 16, DT = D / 32;
+    const S *sk = rec;
+    const S *sm = rec + 2 * kBlk * D;
+    Frag qb[CT][KCH];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int kc = 0; kc < KCH; ++kc) qb[ct][kc] = acc_frag<S>(w.qt[kc >> 1][ct], kc & 1);
+    const i16x8 ones = fold_ones(h);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            w.s[SB][hf][ct] = f32x16{};
+            if constexpr (FOLD)
+                w.s[SB][hf][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, w.mb[ct], w.s[SB][hf][ct], 0, 0, 0);
+        }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int kc = 0; kc < KCH; ++kc) {
+            const Frag af = *(const Frag *)(sk + ((hf * KCH + kc) * 64 + lane) * 8);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) E::mma(w.s[SB][hf][ct], af, qb[ct][kc]);
+        }
+    // qt <- P_J qt (after block 0 the result is not used)
+#pragma unroll
+    for (int kc = 0; kc < KCH; ++kc)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const Frag af = *(const Frag *)(sm + ((dt * KCH + kc) * 64 + lane) * 8);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) E::mma(w.qt[dt][ct], af, qb[ct][kc]);
+        }
+}
+
+// Column maxima of logit buffer SB (with the forget-gate tail bias added) and,
+// rarely, the rescale when the running max grew by more than 2^kTau.
+template <typename S, int D, int CT, int NS, bool FOX, bool FOLD, int SB>
+__device__ __forceinline__ void step_check(WaveState<D, CT, NS> &w, const float *tail, int h) {
+    constexpr int DT = D / 32;
+    float mx[CT];
+    bool grow = false;
+    f32x4 tl[2][4];  // forget-gate tail of the key rows this lane holds: rows 32 hf + 8 g + 4 h + e
+    if (FOX) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) tl[hf][g] = *(const f32x4 *)(tail + 32 * hf + 8 * g + 4 * h);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        float x = -INFINITY;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (FOX) w.s[SB][hf][ct][r] += tl[hf][r >> 2][r & 3];
+                x = fmaxf(x, w.s[SB][hf][ct][r]);
+            }
+        mx[ct] = FOX ? other_half_max(x) + w.off[ct] : other_half_max(x);
+        grow = grow || (mx[ct] > (FOLD ? kTau : w.m[ct] + kTau));
+    }
+    if (__any(grow)) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            float mnew;
+            if constexpr (FOLD)
+                fold_split(w.m[ct] + fmaxf(mx[ct], 0.f), h, mnew, w.mb[ct]);
+            else
+                mnew = fmaxf(w.m[ct], mx[ct]);
+            const float dlt = mnew - w.m[ct];
+            const float alpha = fast_exp2(-dlt);
+            w.m[ct] = mnew;
+            w.lp[ct] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) w.o[dt][ct][r] *= alpha;
+            if constexpr (FOLD) {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) w.s[SB][hf][ct][r] -= dlt;
+            }
+        }
+    }
+}
+
+// Vector part of step J from logit buffer SB: probabilities, their column
+// sums, and O^T += V^T P^T.
+template <typename S, int D, int CT, int NS, bool FOX, bool FOLD, int SB>
+__device__ __forceinline__ void step_softmax_pv(WaveState<D, CT, NS> &w, const S *rec, float fbJ, int lane) {
+    typedef Elem<S> E;
+    typedef typename E::Frag Frag;
+    constexpr int DT = D / 32;
+    const S *sv = rec + kBlk * D;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        Frag pf[CT][2];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            f32x16 &x = w.s[SB][hf][ct];
+            if (FOX) {
+                const float sh = w.m[ct] - w.off[ct];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r] - sh);
+            } else if constexpr (FOLD) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r] - w.m[ct]);
+            }
+            float ps0 = x[0], ps1 = x[1];
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) {
+                ps0 += x[r];
+                ps1 += x[r + 1];
+            }
+            w.lp[ct] += ps0 + ps1;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) pf[ct][cc] = acc_frag<S>(x, cc);
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const Frag af = *(const Frag *)(sv + ((dt * 4 + 2 * hf + cc) * 64 + lane) * 8);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) E::mma(w.o[dt][ct], af, pf[ct][cc]);
+            }
+    }
+    if (FOX) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) w.off[ct] += fbJ;
+    }
+}
 
 template <typename S, int D, bool FOX>
 __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU)) void path_fwd_kernel(FwdArgs a) {
     static_assert(D == 64 || D == 128, "forward kernel: head dimension 64 or 128");
-    typedef Elem<S> E;
-    typedef typename E::Frag Frag;
     typedef FwdCfg<S, D> F;
     constexpr int NW = F::NW, NB = F::NB, NT = 64 * NW, CT = F::CT, QB = F::QB;
     constexpr int REC = 2 * kBlk * D + D * D;  // elements per key-block record
-    constexpr int KCH = D / 16, DT = D / 32;
+    constexpr int DT = D / 32;
     constexpr int VEC = 16 / (int)sizeof(S);   // elements per 16-byte load
     constexpr int NLD = REC / VEC / NT;        // 16-byte loads per thread per record
     constexpr bool kFold = sizeof(S) == 2 && !FOX;  // running max folded into the logit product
     static_assert(REC % (VEC * NT) == 0, "record must split evenly over the workgroup");
     __shared__ __attribute__((aligned(32))) S srec[NB][REC];
-    __shared__ float stail[NB][kBlk];
+    __shared__ __attribute__((aligned(16))) float stail[NB][kBlk];
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const FwdLayout lay = fwd_layout(a.B, a.H, a.L, D, sizeof(S));
@@ -143,11 +318,9 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
     const float *fk = (const float *)((const char *)a.ws + lay.off_fk) + bh * lay.lp;
     const float *fb = (const float *)((const char *)a.ws + lay.off_fb) + bh * lay.nb;
 
-    // ---- per-wave state
-    f32x16 qt[DT][CT], o[DT][CT];
-    Frag qb[CT][KCH];
-    float m[CT], lp[CT], off[CT];
-    i16x8 mb[CT];  // kFold: B column (-m_hi, -m_lo) of the extra k-chunk
+    // ---- per-wave state: qhat (pre-scaled by scale * log2(e): logits are in
+    // log2 units), the diagonal block's output, max and sum
+    WaveState<D, CT, 1> w;
     if (active) {
         const S *qh = (const S *)((const char *)a.ws + lay.off_qhat) + (bh * lay.lp + (int64_t)I * kBlk) * D;
         const S *od = (const S *)a.out + (bh * a.L + (int64_t)I * kBlk) * D;
@@ -160,15 +333,15 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
             const bool valid = (int64_t)I * kBlk + i < a.L;
             const int io = valid ? i : 0;  // rows past L read row 0 of the block, then drop it
             float ls = ld[i];
-            m[ct] = md[i];
+            w.m[ct] = md[i];
             if constexpr (kFold) {
                 // switch the reference to the nearest two-piece bf16 value
-                const float m0 = m[ct];
-                fold_split(m0, h, m[ct], mb[ct]);
-                ls *= fast_exp2(m0 - m[ct]);
+                const float m0 = w.m[ct];
+                fold_split(m0, h, w.m[ct], w.mb[ct]);
+                ls *= fast_exp2(m0 - w.m[ct]);
             }
-            lp[ct] = h == 0 ? ls : 0.f;
-            off[ct] = FOX ? fq[i] : 0.f;
+            w.lp[ct] = h == 0 ? ls : 0.f;
+            w.off[ct] = FOX ? fq[i] : 0.f;
             const float os = valid ? ls : 0.f;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
@@ -180,160 +353,51 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
                     load4<S>(od + (int64_t)io * D + d, ov);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        qt[dt][ct][4 * g4 + e] = qv[e];
-                        o[dt][ct][4 * g4 + e] = ov[e] * os;
+                        w.qt[dt][ct][4 * g4 + e] = qv[e];
+                        w.o[dt][ct][4 * g4 + e] = ov[e] * os;
                     }
                 }
         }
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int kc = 0; kc < KCH; ++kc) qb[ct][kc] = acc_frag<S>(qt[kc >> 1][ct], kc & 1);
     }
 
-    // ---- key-block records are copied global -> LDS by the DMA path, NB - 1 records ahead
-    // (a single buffer is refilled after every wave is done with it)
-    constexpr int kLoadsPerRecord = NLD;  // per wave (wave 0 adds one for the forget-gate tail)
+    // ---- key-block records are copied global -> LDS by the DMA path (completion
+    // tracked by vmcnt; wave 0 has one more copy per record with the forget gate)
+    // wait until at most n records' copies of this wave are in flight (lgkmcnt(0) too)
+    auto wait_records = [&](auto n) {
+        if (FOX && wv == 0)
+            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((NLD + 1) * decltype(n)::value));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(NLD * decltype(n)::value));
+    };
+    auto rec_ptr = [&](int J) { return recs + (int64_t)J * REC; };
+    auto tail_ptr = [&](int J) { return fk + (int64_t)J * kBlk; };
+    // All waves in step; NB - 1 records ahead (a single buffer is refilled
+    // after every wave is done with it).
 #pragma unroll
     for (int k = 0; k < (NB > 1 ? NB - 1 : 1); ++k)
-        if (Jtop - k >= 0)
-            issue_record<S, REC, NLD, NW, FOX>(recs + (int64_t)(Jtop - k) * REC, fk + (int64_t)(Jtop - k) * kBlk,
-                                               srec[k], stail[k], wv, lane);
-
-    // qhat comes pre-scaled by scale * log2(e): logits are in log2 units
-    constexpr float kTau = 8.f;  // running max is refreshed only when it grows by more than 2^8
-    const i16x8 ones = fold_ones(h);
+        if (Jtop - k >= 0) issue_record<S, REC, NLD, NW, FOX>(rec_ptr(Jtop - k), tail_ptr(Jtop - k), srec[k], stail[k], wv, lane);
     for (int J = Jtop; J >= 0; --J) {
         const int it = Jtop - J, buf = it % NB;
         // wait for this wave's copies of record J; the copies of the NB - 2 newer
         // records issued after it may stay in flight
-        if (NB > 2 && J >= 1) {
-            if (FOX && wv == 0)
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerRecord + 1));
-            else
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerRecord));
-        } else {
-            __builtin_amdgcn_s_waitcnt(0);
-        }
-        __syncthreads();  // every wave's copies have landed; buffer (it + NB - 1) % NB is free
+        if (NB > 2 && J >= 1)
+            wait_records(std::integral_constant<int, (NB > 2 ? NB - 2 : 0)>{});
+        else
+            wait_records(std::integral_constant<int, 0>{});
+        barrier_only();  // every wave's copies have landed; buffer (it + NB - 1) % NB is free
         if (NB > 1 && J - (NB - 1) >= 0) {
             const int jn = J - (NB - 1);
-            issue_record<S, REC, NLD, NW, FOX>(recs + (int64_t)jn * REC, fk + (int64_t)jn * kBlk,
-                                               srec[(it + NB - 1) % NB], stail[(it + NB - 1) % NB], wv, lane);
+            issue_record<S, REC, NLD, NW, FOX>(rec_ptr(jn), tail_ptr(jn), srec[(it + NB - 1) % NB],
+                                               stail[(it + NB - 1) % NB], wv, lane);
         }
         if (active && J < I) {
-            const S *sk = srec[buf];
-            const S *sv = srec[buf] + kBlk * D;
-            const S *sm = srec[buf] + 2 * kBlk * D;
-            const float fbJ = FOX ? fb[J] : 0.f;
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {  // keys 32 hf .. 32 hf + 31 of the block
-                // S^T = khat qt^T for this half
-                f32x16 s[CT];
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    s[ct] = f32x16{};
-                    if constexpr (kFold) s[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, mb[ct], s[ct], 0, 0, 0);
-                }
-#pragma unroll
-                for (int kc = 0; kc < KCH; ++kc) {
-                    const Frag af = *(const Frag *)(sk + ((hf * KCH + kc) * 64 + lane) * 8);
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) E::mma(s[ct], af, qb[ct][kc]);
-                }
-                if (hf == 0 && J > 0) {
-                    // qt <- P_J qt (uses the old qt fragments; independent of the softmax)
-#pragma unroll
-                    for (int kc = 0; kc < KCH; ++kc)
-#pragma unroll
-                        for (int dt = 0; dt < DT; ++dt) {
-                            const Frag af = *(const Frag *)(sm + ((dt * KCH + kc) * 64 + lane) * 8);
-#pragma unroll
-                            for (int ct = 0; ct < CT; ++ct) E::mma(qt[dt][ct], af, qb[ct][kc]);
-                        }
-                }
-                // online softmax down each column (log2 units)
-                Frag pf[CT][2];
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    float mx = -INFINITY;
-                    if (FOX) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            s[ct][r] += stail[buf][32 * hf + acc_row(r, h)];
-                            mx = fmaxf(mx, s[ct][r]);
-                        }
-                        mx = other_half_max(mx) + off[ct];
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ct][r]);
-                        mx = other_half_max(mx);  // kFold: relative to m
-                    }
-                    if (__any(mx > (kFold ? kTau : m[ct] + kTau))) {
-                        float mnew;
-                        if constexpr (kFold)
-                            fold_split(m[ct] + fmaxf(mx, 0.f), h, mnew, mb[ct]);
-                        else
-                            mnew = fmaxf(m[ct], mx);
-                        const float dlt = mnew - m[ct];
-                        const float alpha = fast_exp2(-dlt);
-                        m[ct] = mnew;
-                        lp[ct] *= alpha;
-#pragma unroll
-                        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) o[dt][ct][r] *= alpha;
-                        if constexpr (kFold) {
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) s[ct][r] -= dlt;
-                        }
-                    }
-                    if (FOX) {
-                        const float sh = m[ct] - off[ct];
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) s[ct][r] = fast_exp2(s[ct][r] - sh);
-                    } else if constexpr (kFold) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) s[ct][r] = fast_exp2(s[ct][r]);
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) s[ct][r] = fast_exp2(s[ct][r] - m[ct]);
-                    }
-                    float ps0 = s[ct][0], ps1 = s[ct][1];
-#pragma unroll
-                    for (int r = 2; r < 16; r += 2) {
-                        ps0 += s[ct][r];
-                        ps1 += s[ct][r + 1];
-                    }
-                    lp[ct] += ps0 + ps1;
-#pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) pf[ct][cc] = acc_frag<S>(s[ct], cc);
-                }
-                // O^T += V^T P^T over the half's two key chunks
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        const Frag af = *(const Frag *)(sv + ((dt * 4 + 2 * hf + cc) * 64 + lane) * 8);
-#pragma unroll
-                        for (int ct = 0; ct < CT; ++ct) E::mma(o[dt][ct], af, pf[ct][cc]);
-                    }
-            }
-            if (J > 0) {
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                    for (int kc = 0; kc < KCH; ++kc) qb[ct][kc] = acc_frag<S>(qt[kc >> 1][ct], kc & 1);
-            }
-            if (FOX) {
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) off[ct] += fbJ;
-            }
+            step_mma<S, D, CT, 1, kFold, 0>(w, srec[buf], lane, h);
+            step_check<S, D, CT, 1, FOX, kFold, 0>(w, stail[buf], h);
+            step_softmax_pv<S, D, CT, 1, FOX, kFold, 0>(w, srec[buf], FOX ? fb[J] : 0.f, lane);
         }
         if (NB == 1 && J >= 1) {
             __syncthreads();  // every wave is done with the buffer
-            issue_record<S, REC, NLD, NW, FOX>(recs + (int64_t)(J - 1) * REC, fk + (int64_t)(J - 1) * kBlk, srec[0],
-                                               stail[0], wv, lane);
+            issue_record<S, REC, NLD, NW, FOX>(rec_ptr(J - 1), tail_ptr(J - 1), srec[0], stail[0], wv, lane);
         }
     }
 
@@ -343,7 +407,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             const int i = c0 + 32 * ct + l32;
-            const float lsum = other_half_sum(lp[ct]);
+            const float lsum = other_half_sum(w.lp[ct]);
             if ((int64_t)I * kBlk + i >= a.L) continue;
             const float inv = 1.f / lsum;
 #pragma unroll
@@ -352,7 +416,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int d = 32 * dt + 8 * g4 + 4 * h;
                     S *p = go + (int64_t)i * D + d;
-                    const f32x16 &c = o[dt][ct];
+                    const f32x16 &c = w.o[dt][ct];
                     if constexpr (sizeof(S) == 2) {
                         u32x2 u = {pack_bf16(c[4 * g4] * inv, c[4 * g4 + 1] * inv),
                                    pack_bf16(c[4 * g4 + 2] * inv, c[4 * g4 + 3] * inv)};
@@ -362,7 +426,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
                         *(f32x4 *)p = v;
                     }
                 }
-            if (a.lse && h == 0) a.lse[bh * a.L + (int64_t)I * kBlk + i] = (m[ct] + __log2f(lsum)) * kLn2;
+            if (a.lse && h == 0) a.lse[bh * a.L + (int64_t)I * kBlk + i] = (w.m[ct] + __log2f(lsum)) * kLn2;
         }
     }
 }
