@@ -11,7 +11,8 @@ follows is the attention logit of the Japanese technical summary
 H_i) q_i with H_s = I - beta_s w_s w_s^T, followed by the causal softmax and
 the weighted sum of values described in section 3-4 of the iplexlaw blog
 "거리에서 경로로, PaTH Attention".  Decode follows section 3 of the same
-summary: the newest H_t is applied in place to every cached key.
+summary: the newest H_t is applied in place to every cached key; the decode
+cache after a prefix is what those in-place updates would have produced.
 """
 from __future__ import annotations
 
@@ -59,6 +60,8 @@ def _load(path=None):
         lib.oracle_scores_head.restype = None
         lib.oracle_scores_head.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_double, dp]
+        lib.oracle_decode_cache.restype = ctypes.c_int
+        lib.oracle_decode_cache.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp]
         lib.oracle_transport.restype = None
         lib.oracle_transport.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp]
         _libs[path] = lib
@@ -168,3 +171,20 @@ def decode(kc, vc, n, q, w, beta, k_new=None, v_new=None, scale=None, nthreads=N
     if rc != 0:
         raise ValueError("oracle_decode: bad arguments")
     return kc, vc, out.reshape(lead + (d,)), lse.reshape(lead)
+
+
+def decode_cache(k, w, beta, lib=None):
+    """Decode cache after a prefix of L tokens, fp64: row j = H_{L-1} ... H_{j+1} k_j.
+
+    k, w: [..., L, d]; beta: [..., L].  Returns [..., L, d].
+    """
+    k, w, beta = _f64(k), _f64(w), _f64(beta)
+    lead = k.shape[:-2]
+    L, d = k.shape[-2], k.shape[-1]
+    G = int(np.prod(lead)) if lead else 1
+    assert w.shape == k.shape and beta.shape == k.shape[:-1]
+    out = np.zeros((G, L, d))
+    rc = _load(lib).oracle_decode_cache(_ptr(k), _ptr(w), _ptr(beta), G, L, d, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_decode_cache: bad arguments")
+    return out.reshape(lead + (L, d))

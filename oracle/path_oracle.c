@@ -37,6 +37,11 @@
  * (H_t ... H_{j+1} k_j)^T q_t = k_j^T (H_{j+1} ... H_t) q_t, the forward logit.
  * A new key/value (if given) enters after the update, untransformed, because
  * the logit of j = t has the empty product.
+ *
+ * Decode cache after a prefix of L tokens [TS s.3]: if tokens 0 .. L-1 had
+ * been fed one decode step at a time, cache row j would have been updated by
+ * steps j+1, ..., L-1 in that order, so it holds H_{L-1} ... H_{j+1} k_j
+ * (H_{j+1} acts first; row L-1 is k_{L-1} itself).
  */
 #include <math.h>
 #include <pthread.h>
@@ -276,5 +281,25 @@ int oracle_decode(double *kc, double *vc, int64_t n, int64_t rowcap, const doubl
     for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
     free(th);
     pthread_mutex_destroy(&jb.mu);
+    return 0;
+}
+
+/*
+ * Decode cache of G heads after a prefix of L tokens: out[g][j] =
+ * H_{L-1} ... H_{j+1} k_j, applying H_{j+1} first and H_{L-1} last (the order
+ * of the in-place decode updates).  k, w: [G, L, d]; beta: [G, L];
+ * out: [G, L, d].  Returns 0 or -1.
+ */
+int oracle_decode_cache(const double *k, const double *w, const double *beta, int G, int L, int d, double *out) {
+    if (G < 0 || L < 0 || d < 1) return -1;
+    for (int g = 0; g < G; ++g) {
+        const double *kg = k + (size_t)g * L * d, *wg = w + (size_t)g * L * d, *bg = beta + (size_t)g * L;
+        double *og = out + (size_t)g * L * d;
+        for (int j = 0; j < L; ++j) {
+            double *u = og + (size_t)j * d;
+            memcpy(u, kg + (size_t)j * d, sizeof(double) * (size_t)d);
+            for (int s = j + 1; s < L; ++s) apply_h(u, wg + (size_t)s * d, bg[s], d);
+        }
+    }
     return 0;
 }

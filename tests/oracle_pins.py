@@ -14,7 +14,9 @@ AssertionError when that build disagrees with an independent fact:
   * beta = 2 making every H an orthogonal reflection (norms, det = (-1)^n),
   * beta = 1 making every H a projector,
   * all w equal with beta = 2 (H^2 = I: closed form by parity),
-  * decode reproducing forward rows (the in-place key update of section 3).
+  * decode reproducing forward rows (the in-place key update of section 3),
+  * the decode cache after a prefix equal to explicit products and to feeding
+    the prefix through decode steps one token at a time.
 They are used by test_oracle_pins.py on the real oracle and by
 test_oracle_mutants.py on deliberately broken copies of it.
 """
@@ -264,5 +266,30 @@ def pin_decode(lib):
     _close(kc2, ku, 1e-13, "decode cache without new token")
 
 
+def pin_decode_cache(lib):
+    """Decode cache after a prefix: explicit products H_{L-1} ... H_{j+1} k_j (brute force),
+    equality with feeding the prefix through decode steps one token at a time, and the
+    special cases beta = 0 (cache = keys) and beta = 1 (every older row orthogonal to
+    the last w, since H = I - w w^T annihilates w)."""
+    L, d = 11, 5
+    q, k, v, w, b, _ = _rand_inputs(L, d, 21)
+    got = oracle.decode_cache(k, w, b, lib=lib)
+    for j in range(L):
+        M = np.eye(d)
+        for s in range(j + 1, L):
+            M = _H(w[s], b[s]) @ M  # H_{j+1} acts first
+        _close(got[j], M @ k[j], 1e-13, "decode cache row %d vs explicit product" % j)
+    kc = np.zeros((L, d))
+    vc = np.zeros((L, d))
+    for t in range(L):
+        kc, vc, _, _ = oracle.decode(kc, vc, t, q[t], w[t], b[t], k_new=k[t], v_new=v[t], lib=lib)
+    _close(got, kc, 1e-13, "decode cache vs token-by-token decode")
+    _, _, _, w0, _, _ = _rand_inputs(L, d, 22)
+    _close(oracle.decode_cache(k, w0, np.zeros(L), lib=lib), k, 0.0, "beta = 0 leaves the keys")
+    c1 = oracle.decode_cache(k, w0, np.ones(L), lib=lib)
+    _close(c1[:-1] @ w0[-1], np.zeros(L - 1), 1e-13, "beta = 1: older rows orthogonal to the last w")
+    _close(c1[-1], k[-1], 0.0, "last row untransformed")
+
+
 ALL_PINS = [pin_golden, pin_bruteforce, pin_ut_closed_form, pin_beta_zero, pin_beta_two, pin_beta_one,
-            pin_equal_w, pin_small_L, pin_fox_zero, pin_rows_subset, pin_decode]
+            pin_equal_w, pin_small_L, pin_fox_zero, pin_rows_subset, pin_decode, pin_decode_cache]

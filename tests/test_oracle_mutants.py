@@ -34,6 +34,10 @@ MUTANTS = [
      "for (int64_t j = 0; j < n; ++j) apply_h(kc + (size_t)j * d, w, beta, d);\n    int64_t nt = n;\n    if (knew && vnew) {\n        memcpy(kc + (size_t)n * d, knew, sizeof(double) * (size_t)d);\n        memcpy(vc + (size_t)n * d, vnew, sizeof(double) * (size_t)d);\n        nt = n + 1;\n    }",
      "int64_t nt = n;\n    if (knew && vnew) {\n        memcpy(kc + (size_t)n * d, knew, sizeof(double) * (size_t)d);\n        memcpy(vc + (size_t)n * d, vnew, sizeof(double) * (size_t)d);\n        nt = n + 1;\n    }\n    for (int64_t j = 0; j < nt; ++j) apply_h(kc + (size_t)j * d, w, beta, d);", 1),
     ("decode_scale_dropped", "double p = exp(scale * s - m);", "double p = exp(s - m);", 1),
+    ("cache_order_reversed", "for (int s = j + 1; s < L; ++s) apply_h(u, wg + (size_t)s * d, bg[s], d);",
+     "for (int s = L - 1; s > j; --s) apply_h(u, wg + (size_t)s * d, bg[s], d);", 1),
+    ("cache_includes_own_H", "for (int s = j + 1; s < L; ++s) apply_h(u, wg", "for (int s = j; s < L; ++s) apply_h(u, wg", 1),
+    ("cache_drops_last_H", "for (int s = j + 1; s < L; ++s) apply_h(u, wg", "for (int s = j + 1; s < L - 1; ++s) apply_h(u, wg", 1),
 ]
 
 
