@@ -12,7 +12,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_prep", "fwd_scan", "decode_step", "fwd_workspace_size", "decode_workspace_size", "lib", "PathError",
+__all__ = ["fwd", "fwd_prep", "fwd_scan", "decode_step", "decode_cache_from_fwd", "fwd_workspace_size", "decode_workspace_size", "lib", "PathError",
            "PATH_OK", "PATH_EINVAL", "PATH_EUNSUPPORTED", "PATH_EHIP", "PATH_DTYPE_F32", "PATH_DTYPE_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpath_attn.so")
@@ -58,6 +58,8 @@ def lib():
         L.path_decode_step.restype = ctypes.c_int
         L.path_decode_step.argtypes = [vp, vp, i64, i64, vp, vp, fp, vp, vp, vp, fp, i, i, i, ctypes.c_int,
                                        ctypes.c_float, vp, sz, vp]
+        L.path_decode_cache_from_fwd.restype = ctypes.c_int
+        L.path_decode_cache_from_fwd.argtypes = [vp, sz, vp, vp, vp, i64, i, i, i, i, ctypes.c_int, vp]
         _lib = L
     return _lib
 
@@ -212,3 +214,31 @@ def decode_step(kcache, vcache, n, q, w, beta, k_new=None, v_new=None, scale=Non
     if st != PATH_OK:
         raise PathError(st, "path_decode_step")
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_cache_from_fwd(workspace, v, kcache, vcache, stream=None):
+    """Fill decode caches from a forward pass's workspace (path_decode_cache_from_fwd).
+
+    workspace: the workspace a fwd / fwd_prep call over this prefix used (same
+    B, H, L, d, dtype); v: [B, H, L, d] prefix values; kcache, vcache:
+    [B, H, ncap, d] with ncap >= L, rows [0, L) written: kcache row j =
+    H_{L-1} ... H_{j+1} k_j, vcache row j = v_j.
+    """
+    if v.dim() != 4 or kcache.dim() != 4:
+        raise ValueError("v must be [B, H, L, d] and kcache [B, H, ncap, d]")
+    B, H, L, d = v.shape
+    ncap = kcache.shape[2]
+    dt, dev = v.dtype, v.device
+    if dt not in _DTYPES:
+        raise ValueError("dtype must be bfloat16 or float32")
+    _check(v, "v", dt, (B, H, L, d), dev)
+    _check(kcache, "kcache", dt, (B, H, ncap, d), dev)
+    _check(vcache, "vcache", dt, (B, H, ncap, d), dev)
+    _check(workspace, "workspace", None, None, dev)
+    with torch.cuda.device(dev):
+        st = lib().path_decode_cache_from_fwd(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(v),
+                                              _ptr(kcache), _ptr(vcache), int(ncap), B, H, L, d, _DTYPES[dt],
+                                              _stream(stream))
+    if st != PATH_OK:
+        raise PathError(st, "path_decode_cache_from_fwd")
+    return kcache, vcache

@@ -224,4 +224,25 @@ path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t nc
     return PATH_OK;
 }
 
+path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace_bytes, const void *v,
+                                         void *kcache, void *vcache, int64_t ncap, int B, int H, int L, int d,
+                                         path_dtype_t dtype, void *stream) {
+    path_status_t st = fwd_sizes_ok(B, H, L, d, dtype);
+    if (st != PATH_OK) return st;
+    if (ncap < L || mul_chk({B, H, ncap, d, 8}) < 0) return PATH_EINVAL;
+    if (!workspace || !v || !kcache || !vcache) return PATH_EINVAL;
+    for (const void *p : {workspace, v, (const void *)kcache, (const void *)vcache})
+        if (!aligned(p, 16)) return PATH_EINVAL;
+    const size_t need = path::fwd_layout(B, H, L, d, elem_size(dtype)).total;
+    if (workspace_bytes < need) return PATH_EINVAL;
+    const int64_t es = elem_size(dtype);
+    const int64_t cache = (int64_t)B * H * ncap * d * es, tens = (int64_t)B * H * L * d * es;
+    if (overlap(kcache, cache, vcache, cache)) return PATH_EINVAL;
+    for (const void *p : {(const void *)kcache, (const void *)vcache})
+        if (overlap(p, cache, workspace, (int64_t)need) || overlap(p, cache, v, tens)) return PATH_EINVAL;
+    path::CacheArgs ca{workspace, v, kcache, vcache, ncap, B, H, L, d};
+    if ((int64_t)B * H > kMaxGrid) return PATH_EINVAL;
+    return path::launch_cache(ca, dtype == PATH_DTYPE_BF16, (hipStream_t)stream) == hipSuccess ? PATH_OK : PATH_EHIP;
+}
+
 }  // extern "C"

@@ -40,9 +40,17 @@ struct DecodeArgs {
     int64_t chunk;
 };
 
+struct CacheArgs {
+    const void *ws, *v;
+    void *kc, *vc;
+    int64_t ncap;
+    int B, H, L, d;
+};
+
 hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t st);
+hipError_t launch_cache(const CacheArgs &a, bool bf16, hipStream_t st);
 
 // Decode split plan: rows per split and number of splits for n attending rows.
 void decode_plan(int64_t BH, int64_t rows, int *nsplit, int64_t *chunk);

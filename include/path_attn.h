@@ -25,8 +25,8 @@
  * Layout: every tensor is contiguous and row-major.  Per-token tensors are
  * [B, H, L, d] (B batches, H heads, L tokens, head dimension d); per-token
  * scalars are [B, H, L].  Pointers are DEVICE pointers owned by the caller
- * and must be 16-byte aligned.  d must be 64 (other head sizes return
- * PATH_EUNSUPPORTED).  Any L >= 1 is accepted.
+ * and must be 16-byte aligned.  d must be 64 or 128 (other head sizes
+ * return PATH_EUNSUPPORTED).  Any L >= 1 is accepted.
  *
  * Numerics: dtype selects the element type of q, k, v, w, the output and the
  * caches.  beta, the log-forget gate, lse and all accumulation are fp32.
@@ -50,7 +50,7 @@ extern "C" {
 typedef enum {
     PATH_OK = 0,
     PATH_EINVAL = 1,        /* NULL pointer, bad size, misaligned, workspace too small, n > ncap */
-    PATH_EUNSUPPORTED = 2,  /* valid but not implemented (head dimension other than 64) */
+    PATH_EUNSUPPORTED = 2,  /* valid but not implemented (head dimension other than 64, 128) */
     PATH_EHIP = 3           /* the HIP runtime rejected a launch */
 } path_status_t;
 
@@ -150,6 +150,32 @@ path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t nc
                                const float *beta, const void *k_new, const void *v_new, void *out, float *lse,
                                int B, int H, int d, path_dtype_t dtype, float scale, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/*
+ * Decode cache of a prefix from its forward pass ([TS] s.3: prefill, then
+ * decode with in-place key updates).  After path_attn_fwd (or
+ * path_attn_fwd_prep) has processed tokens 0 .. L-1, this fills the caches
+ * that L decode steps would have produced:
+ *
+ *   kcache[b,h,j,:] = H_{L-1} ... H_{j+1} k_j     (H_{j+1} applied first; row L-1 = k_{L-1})
+ *   vcache[b,h,j,:] = v_j                          for j in [0, L)
+ *
+ * rounded to `dtype`, so that path_decode_step with n = L continues the
+ * sequence.  The keys come from the boundary-adjusted key blocks and block
+ * transition products that the forward pass left in its workspace.
+ *
+ * workspace      : the workspace of a path_attn_fwd / path_attn_fwd_prep call with
+ *                  the same B, H, L, d and dtype, enqueued before this call on the
+ *                  same stream (or completed); results are undefined otherwise
+ * v              : [B, H, L, d] element type `dtype`, the prefix values (read only)
+ * kcache, vcache : [B, H, ncap, d] element type `dtype`, ncap >= L; rows >= L untouched
+ *
+ * Returns PATH_OK, PATH_EINVAL (NULL, sizes, misaligned, workspace too small,
+ * ncap < L, overlapping buffers), PATH_EUNSUPPORTED or PATH_EHIP.
+ */
+path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace_bytes, const void *v,
+                                         void *kcache, void *vcache, int64_t ncap, int B, int H, int L, int d,
+                                         path_dtype_t dtype, void *stream);
 
 #ifdef __cplusplus
 }

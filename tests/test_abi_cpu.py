@@ -118,3 +118,31 @@ def dec_call(**over):
 ])
 def test_decode_rejects_bad_arguments(over, status):
     assert dec_call(**over) == status
+
+
+def cache_call(**over):
+    # the workspace sits above every other buffer, so the baseline call has no overlap
+    args = dict(ws=ctypes.c_void_p(A * 1024), wsb=1 << 40, v=ctypes.c_void_p(A * 64), kc=ctypes.c_void_p(A * 128),
+                vc=ctypes.c_void_p(A * 192),
+                ncap=256, B=1, H=1, L=200, d=64, dtype=BF, stream=None)
+    args.update(over)
+    return pa.lib().path_decode_cache_from_fwd(args["ws"], args["wsb"], args["v"], args["kc"], args["vc"], args["ncap"],
+                                               args["B"], args["H"], args["L"], args["d"], args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ws=None), pa.PATH_EINVAL),
+    (dict(v=None), pa.PATH_EINVAL),
+    (dict(kc=None), pa.PATH_EINVAL),
+    (dict(ncap=199), pa.PATH_EINVAL),                          # cache shorter than the prefix
+    (dict(L=0), pa.PATH_EINVAL),
+    (dict(d=96), pa.PATH_EUNSUPPORTED),
+    (dict(dtype=4), pa.PATH_EINVAL),
+    (dict(wsb=1024), pa.PATH_EINVAL),                          # workspace smaller than the forward's
+    (dict(v=ctypes.c_void_p(A * 64 + 8)), pa.PATH_EINVAL),     # misaligned
+    (dict(vc=ctypes.c_void_p(A * 128)), pa.PATH_EINVAL),       # caches alias
+    (dict(kc=ctypes.c_void_p(A * 1024 + 4096)), pa.PATH_EINVAL),  # key cache inside the used workspace
+    (dict(vc=ctypes.c_void_p(A * 64)), pa.PATH_EINVAL),        # value cache over the values
+])
+def test_cache_from_fwd_rejects_bad_arguments(over, status):
+    assert cache_call(**over) == status
