@@ -4,7 +4,8 @@
 A step is one causal PaTH forward pass (prep + scan kernels) over the
 B32 H32 L4096 d64 bf16 workload; K steps are timed after W warm-up steps.
 Alongside it the decode step (B16 H32 d64, 32768 cached rows, bf16, 64 steps
-with fresh q, w, beta each) and the other forward workloads (L 1024 - 8192 at
+with fresh q, w, beta each), the prefill -> decode cache build on the
+forward's workspace, and the other forward workloads (L 1024 - 8192 at
 d64, L4096 at d128, B8 H16 L4096, PaTH-FoX B4 H16 L16384) are timed, and the
 fp64 CPU oracle is timed on a bounded sample of the forward workload.  Prints
 one JSON line.
@@ -43,6 +44,8 @@ KERNEL_SOURCES = {
     "path_fwd_kernel": ["attention_fwd_amd/csrc/path_fwd.hip", "attention_fwd_amd/csrc/path_common.h",
                         "attention_fwd_amd/csrc/path_layout.h"],
     "path_decode_kernel": ["attention_fwd_amd/csrc/path_decode.hip", "attention_fwd_amd/csrc/path_common.h"],
+    "path_cache_kernel": ["attention_fwd_amd/csrc/path_cache.hip", "attention_fwd_amd/csrc/path_common.h",
+                          "attention_fwd_amd/csrc/path_layout.h"],
 }
 
 
@@ -165,6 +168,44 @@ def bench_decode(steps):
     return dict(B=B, H=H, n=n, d=d, steps=steps, step_ms=step_ms, wall_s=wall, bytes=nbytes)
 
 
+def bench_cache(steps, f):
+    """Prefill -> decode cache (path_decode_cache_from_fwd) on the forward workload's workspace.
+
+    Algorithmic bytes per launch: read the key blocks khat (B H Lp d) and the
+    block transitions (B H nb d^2) from the forward's records, write the key
+    cache (B H L d), read and write the values (2 B H L d), all in bf16."""
+    import torch
+
+    import attention_fwd_amd as pa
+
+    x = f["x"]
+    B, H, L, d = f["B"], f["H"], f["L"], f["d"]
+    ws = torch.empty(pa.fwd_workspace_size(B, H, L, d, x["q"].dtype), device="cuda", dtype=torch.uint8)
+    pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], workspace=ws)
+    kc = torch.empty((B, H, L, d), device="cuda", dtype=x["q"].dtype)
+    vc = torch.empty_like(kc)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        pa.decode_cache_from_fwd(ws, x["v"], kc, vc)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        pa.decode_cache_from_fwd(ws, x["v"], kc, vc)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    nb = (L + 63) // 64
+    es = kc.element_size()
+    nbytes = float(B * H * (nb * 64 * d + nb * d * d + L * d + 2 * L * d) * es)
+    del ws, kc, vc
+    torch.cuda.empty_cache()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GB_per_s": round(gbs, 1), "bytes": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": read_traffic("path_cache_kernel")}}
+
+
 def counter_run(fwd_steps=2, dec_steps=2):
     """No timing: the kernels a hardware-counter pass reads.  First a plain
     device copy of COPY_BYTES (read and written once each, the calibration of
@@ -191,8 +232,12 @@ def counter_run(fwd_steps=2, dec_steps=2):
     for _ in range(fwd_steps):
         pa.fwd_prep(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out, lse, ws)
         pa.fwd_scan(out, lse, x["logf"] is not None, ws)
+    kc = torch.empty_like(x["k"])
+    vc = torch.empty_like(x["v"])
+    for _ in range(fwd_steps):
+        pa.decode_cache_from_fwd(ws, x["v"], kc, vc)
     torch.cuda.synchronize()
-    del x, out, lse, ws
+    del x, out, lse, ws, kc, vc
     torch.cuda.empty_cache()
     c = pathgen.WORKLOADS[DEC_WORKLOAD]
     x = pathgen.decode_inputs(c["B"], c["H"], c["n"], c["d"], steps=dec_steps, dtype=c["dtype"], seed=0,
@@ -202,7 +247,8 @@ def counter_run(fwd_steps=2, dec_steps=2):
     for t in range(dec_steps):
         pa.decode_step(x["kcache"], x["vcache"], c["n"], x["q"][t], x["w"][t], x["beta"][t], workspace=ws)
     torch.cuda.synchronize()
-    log("counter run done: copy %d bytes, %d forward steps, %d decode steps" % (COPY_BYTES, fwd_steps, dec_steps))
+    log("counter run done: copy %d bytes, %d forward steps + cache builds, %d decode steps" %
+        (COPY_BYTES, fwd_steps, dec_steps))
 
 
 def cpu_baseline(x, target_s):
@@ -258,6 +304,8 @@ def main():
     log("forward: %s, %d warm-up + %d timed steps" % (FWD_WORKLOAD, args.warmup, args.steps))
     f = bench_forward(args.steps, args.warmup)
     log("forward: %.3f ms/step (prep %.3f ms, scan %.3f ms)" % (f["ms_per_step"], f["prep_ms"], f["scan_ms"]))
+    cache = bench_cache(10, f)
+    log("prefill -> decode cache: %.3f ms, %.1f GB/s" % (cache["ms"], cache["GB_per_s"]))
     log("decode: %s, %d steps" % (DEC_WORKLOAD, args.decode_steps))
     dres = bench_decode(args.decode_steps)
     log("decode: %.3f ms/step" % dres["step_ms"])
@@ -302,6 +350,7 @@ def main():
                                 "traffic": read_traffic("path_decode_kernel")},
                    "tokens_per_s": round(dres["B"] / (dres["step_ms"] * 1e-3)), "bytes_per_step": dres["bytes"],
                    "steps": dres["steps"]},
+        "decode_cache_from_fwd": cache,
         "other_workloads": sweep,
         "cpu_baseline": cpu,
     }
