@@ -13,7 +13,8 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_prep", "fwd_scan", "decode_step", "decode_cache_from_fwd", "fwd_workspace_size", "decode_workspace_size", "lib", "PathError",
-           "PATH_OK", "PATH_EINVAL", "PATH_EUNSUPPORTED", "PATH_EHIP", "PATH_DTYPE_F32", "PATH_DTYPE_BF16"]
+           "PATH_OK", "PATH_EINVAL", "PATH_EUNSUPPORTED", "PATH_EHIP", "PATH_DTYPE_F32", "PATH_DTYPE_BF16",
+           "PATH_FWD_SKIP_NEGLIGIBLE"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpath_attn.so")
 
@@ -49,6 +50,8 @@ def lib():
         L.path_attn_fwd.restype = ctypes.c_int
         L.path_attn_fwd.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, i, i, i, i, ctypes.c_int, ctypes.c_float,
                                     vp, sz, vp]
+        L.path_attn_fwd_ex.restype = ctypes.c_int
+        L.path_attn_fwd_ex.argtypes = list(L.path_attn_fwd.argtypes[:-1]) + [ctypes.c_uint, vp]
         L.path_attn_fwd_prep.restype = ctypes.c_int
         L.path_attn_fwd_prep.argtypes = list(L.path_attn_fwd.argtypes)
         L.path_attn_fwd_scan.restype = ctypes.c_int
@@ -96,13 +99,18 @@ def decode_workspace_size(B, H, rows, d, dtype=torch.bfloat16):
     return int(lib().path_decode_workspace_size(B, H, rows, d, _DTYPES[dtype]))
 
 
+PATH_FWD_SKIP_NEGLIGIBLE = 1
+
+
 def fwd(q, k, v, w, beta, logf=None, scale=None, out=None, lse=None, return_lse=False, workspace=None,
-        stream=None):
-    """Causal PaTH attention forward (path_attn_fwd).
+        stream=None, skip_negligible=False):
+    """Causal PaTH attention forward (path_attn_fwd / path_attn_fwd_ex).
 
     q, k, v, w: [B, H, L, d] bf16 or fp32 device tensors; beta, logf: [B, H, L]
-    fp32 (logf optional, enables the PaTH-FoX bias).  Returns out (and lse
-    when return_lse or an lse tensor is given).
+    fp32 (logf optional, enables the PaTH-FoX bias).  skip_negligible (with
+    logf) stops the walk over key blocks once the rest provably contributes
+    below 2^-64 of the running maximum per key.  Returns out (and lse when
+    return_lse or an lse tensor is given).
     """
     if q.dim() != 4:
         raise ValueError("q must be [B, H, L, d]")
@@ -130,11 +138,12 @@ def fwd(q, k, v, w, beta, logf=None, scale=None, out=None, lse=None, return_lse=
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     _check(workspace, "workspace", None, None, dev)
     with torch.cuda.device(dev):
-        st = lib().path_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf), _ptr(out), _ptr(lse),
-                                 B, H, L, d, _DTYPES[dt], float(scale or 0.0), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(stream))
+        st = lib().path_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf), _ptr(out),
+                                    _ptr(lse), B, H, L, d, _DTYPES[dt], float(scale or 0.0), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    PATH_FWD_SKIP_NEGLIGIBLE if skip_negligible else 0, _stream(stream))
     if st != PATH_OK:
-        raise PathError(st, "path_attn_fwd")
+        raise PathError(st, "path_attn_fwd_ex")
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -132,8 +132,8 @@ path_status_t launch_prep_stage(const void *q, const void *k, const void *v, con
 }
 
 path_status_t launch_scan_stage(void *out, float *lse, bool fox, int B, int H, int L, int d, path_dtype_t dtype,
-                                float scale, void *workspace, hipStream_t s) {
-    path::FwdArgs fa{out, lse, workspace, B, H, L, d, scale, fox ? 1 : 0};
+                                float scale, void *workspace, hipStream_t s, bool skip = false) {
+    path::FwdArgs fa{out, lse, workspace, B, H, L, d, scale, fox ? 1 : 0, (fox && skip) ? 1 : 0};
     return path::launch_fwd(fa, dtype == PATH_DTYPE_BF16, s) == hipSuccess ? PATH_OK : PATH_EHIP;
 }
 
@@ -141,10 +141,11 @@ float eff_scale(float scale, int d) { return scale <= 0.f ? 1.0f / std::sqrt((fl
 
 }  // namespace
 
-path_status_t path_attn_fwd(const void *q, const void *k, const void *v, const void *w, const float *beta,
-                            const float *logf, void *out, float *lse, int B, int H, int L, int d,
-                            path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
-                            void *stream) {
+path_status_t path_attn_fwd_ex(const void *q, const void *k, const void *v, const void *w, const float *beta,
+                               const float *logf, void *out, float *lse, int B, int H, int L, int d,
+                               path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
+                               unsigned flags, void *stream) {
+    if (flags & ~PATH_FWD_SKIP_NEGLIGIBLE) return PATH_EINVAL;
     path_status_t st = fwd_check(q, k, v, w, beta, logf, out, lse, B, H, L, d, dtype, scale, workspace,
                                  workspace_bytes);
     if (st != PATH_OK) return st;
@@ -152,7 +153,16 @@ path_status_t path_attn_fwd(const void *q, const void *k, const void *v, const v
     hipStream_t s = (hipStream_t)stream;
     st = launch_prep_stage(q, k, v, w, beta, logf, out, lse, B, H, L, d, dtype, scale, workspace, s);
     if (st != PATH_OK) return st;
-    return launch_scan_stage(out, lse, logf != nullptr, B, H, L, d, dtype, scale, workspace, s);
+    return launch_scan_stage(out, lse, logf != nullptr, B, H, L, d, dtype, scale, workspace, s,
+                             (flags & PATH_FWD_SKIP_NEGLIGIBLE) != 0);
+}
+
+path_status_t path_attn_fwd(const void *q, const void *k, const void *v, const void *w, const float *beta,
+                            const float *logf, void *out, float *lse, int B, int H, int L, int d,
+                            path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    return path_attn_fwd_ex(q, k, v, w, beta, logf, out, lse, B, H, L, d, dtype, scale, workspace, workspace_bytes,
+                            0u, stream);
 }
 
 path_status_t path_attn_fwd_prep(const void *q, const void *k, const void *v, const void *w, const float *beta,

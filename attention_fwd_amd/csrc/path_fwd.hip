@@ -135,6 +135,7 @@ struct WaveState {
 };
 
 constexpr float kTau = 8.f;  // the running max is refreshed only when it grows by more than 2^kTau
+constexpr float kSkipLog2 = 64.f;  // skipped key blocks contribute below 2^-64 of the running max each
 
 // Matrix-core part of step J into logit buffer SB: bf16 copy of qt as the B
 // operand, S^T = khat qt^T for all 64 keys, and qt <- P_J qt.
@@ -294,6 +295,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
     static_assert(REC % (VEC * NT) == 0, "record must split evenly over the workgroup");
     __shared__ __attribute__((aligned(32))) S srec[NB][REC];
     __shared__ __attribute__((aligned(16))) float stail[NB][kBlk];
+    __shared__ int sdone[NW];  // skipping: this wave needs no more key blocks
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const FwdLayout lay = fwd_layout(a.B, a.H, a.L, D, sizeof(S));
@@ -360,6 +362,42 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
         }
     }
 
+    // ---- skipping negligible key blocks (forget gate only, on request).  With
+    // every transition a contraction (0 <= beta ||w||^2 <= 2, checked per block
+    // by prep), a logit of query i against any key of block J or earlier is at
+    // most ||qhat_i|| * max_j ||k_j|| plus the forget-gate bias of the block
+    // boundary (off_i, log2 units; the bias only falls further back).  Once
+    // that bound is more than kSkipLog2 below the running max for every query
+    // of a wave, the remaining blocks add less than L 2^-kSkipLog2 of the
+    // normaliser, far below fp32 resolution, and the wave stops; the workgroup
+    // leaves the walk when all its waves have.
+    const bool skip = FOX && a.skip;
+    bool wdone = !active;
+    float qbound[CT];
+    if (skip) {
+        const float *kn = (const float *)((const char *)a.ws + lay.off_kn) + bh * lay.nb;
+        float km = 0.f;
+        for (int j = lane; j <= Jtop; j += 64) km = fmaxf(km, kn[j]);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) km = fmaxf(km, __shfl_xor(km, o));
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            float ss = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ss += w.qt[dt][ct][r] * w.qt[dt][ct][r];
+            qbound[ct] = sqrtf(other_half_sum(ss)) * (1.f + 0x1p-10f) * km;  // rounded up; inf if not contractive
+        }
+        if (lane == 0) sdone[wv] = wdone;
+    }
+    auto negligible = [&]() {
+        bool ok = true;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) ok = ok && (qbound[ct] + w.off[ct] - w.m[ct] < -kSkipLog2);
+        return __all(ok);
+    };
+
     // ---- key-block records are copied global -> LDS by the DMA path (completion
     // tracked by vmcnt; wave 0 has one more copy per record with the forget gate)
     // wait until at most n records' copies of this wave are in flight (lgkmcnt(0) too)
@@ -385,21 +423,34 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
         else
             wait_records(std::integral_constant<int, 0>{});
         barrier_only();  // every wave's copies have landed; buffer (it + NB - 1) % NB is free
+        if (skip) {
+            bool all = true;
+#pragma unroll
+            for (int v2 = 0; v2 < NW; ++v2) all = all && sdone[v2];
+            if (all) break;  // uniform: every wave read the same flags after the barrier
+        }
         if (NB > 1 && J - (NB - 1) >= 0) {
             const int jn = J - (NB - 1);
             issue_record<S, REC, NLD, NW, FOX>(rec_ptr(jn), tail_ptr(jn), srec[(it + NB - 1) % NB],
                                                stail[(it + NB - 1) % NB], wv, lane);
         }
-        if (active && J < I) {
+        if (active && J < I && !wdone) {
             step_mma<S, D, CT, 1, kFold, 0>(w, srec[buf], lane, h);
             step_check<S, D, CT, 1, FOX, kFold, 0>(w, stail[buf], h);
             step_softmax_pv<S, D, CT, 1, FOX, kFold, 0>(w, srec[buf], FOX ? fb[J] : 0.f, lane);
+        }
+        if (skip) {  // bound for blocks J - 1 and earlier (off now sits at the J-1 / J boundary)
+            wdone = wdone || negligible();
+            if (lane == 0) sdone[wv] = wdone;
         }
         if (NB == 1 && J >= 1) {
             __syncthreads();  // every wave is done with the buffer
             issue_record<S, REC, NLD, NW, FOX>(rec_ptr(J - 1), tail_ptr(J - 1), srec[0], stail[0], wv, lane);
         }
     }
+
+    // no record copy may still be landing in LDS when the workgroup leaves early
+    if (skip) __builtin_amdgcn_s_waitcnt(0);
 
     // ---- epilogue
     if (active) {

@@ -23,6 +23,7 @@ struct FwdArgs {
     int B, H, L, d;
     float scale;
     int fox;
+    int skip;  // with fox: skip key blocks whose contribution is provably below 2^-kSkipLog2
 };
 
 struct DecodeArgs {

@@ -322,6 +322,29 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
         }
     }
     __syncthreads();
+    if (FOX && wv == 1) {
+        // bound for skipping negligible key blocks in the scan: row s = lane;
+        // the block's transitions are contractions when 0 <= beta_s ||w_s||^2 <= 2
+        float kk = 0.f, ww = 0.f;
+#pragma unroll
+        for (int c0 = 0; c0 < D; c0 += CH) {
+            const u32x4 uk = *(const u32x4 *)(sK + lane * SPD + c0);
+            const u32x4 uw = *(const u32x4 *)(sW + lane * SPD + c0);
+            const S *ek = (const S *)&uk, *ew = (const S *)&uw;
+#pragma unroll
+            for (int e = 0; e < CH; ++e) {
+                const float xk = Elem<S>::to_f32(ek[e]), xw = Elem<S>::to_f32(ew[e]);
+                kk += xk * xk;
+                ww += xw * xw;
+            }
+        }
+        const float bw = sBeta[lane] * ww;
+        const bool contr = bw >= 0.f && bw <= 2.f;
+        float kn = contr ? sqrtf(kk) * (1.f + 0x1p-10f) : INFINITY;  // rounded up
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) kn = fmaxf(kn, __shfl_xor(kn, o));
+        if (lane == 0) ((float *)((char *)a.ws + lay.off_kn))[bh * lay.nb + J] = kn;
+    }
 
     const int mt = (wv >> 1) * 32, nt = (wv & 1) * 32;  // this wave's tile of a 64x64 product
 

@@ -138,6 +138,39 @@ def bench_sweep(steps, warmup):
     return res
 
 
+def bench_fox_skip(steps, warmup, name="fox_L16384_bf16"):
+    """The forget-gate workload with PATH_FWD_SKIP_NEGLIGIBLE (whole forward,
+    prep + scan): time and tokens/s only -- the skipped blocks are not work
+    done, so no FLOP rate is claimed for it."""
+    import torch
+
+    import attention_fwd_amd as pa
+    import pathgen
+
+    c = pathgen.WORKLOADS[name]
+    B, H, L, d = c["B"], c["H"], c["L"], c["d"]
+    x = pathgen.fwd_inputs(B, H, L, d, c["dtype"], seed=0, fox=True, clip=c["clip"], device="cuda")
+    out = torch.empty_like(x["q"])
+    ws = torch.empty(pa.fwd_workspace_size(B, H, L, d, x["q"].dtype), device="cuda", dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for skip in (False, True):
+        for _ in range(warmup):
+            pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out=out, workspace=ws, skip_negligible=skip)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out=out, workspace=ws, skip_negligible=skip)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[skip] = e0.elapsed_time(e1) / steps
+    del x, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": name, "ms_per_step": round(res[True], 4), "full_walk_ms_per_step": round(res[False], 4),
+            "tokens_per_s": round(B * L / (res[True] * 1e-3)), "speedup_vs_full_walk": round(res[False] / res[True], 2)}
+
+
 def bench_decode(steps):
     import torch
 
@@ -309,9 +342,12 @@ def main():
     log("decode: %s, %d steps" % (DEC_WORKLOAD, args.decode_steps))
     dres = bench_decode(args.decode_steps)
     log("decode: %.3f ms/step" % dres["step_ms"])
-    sweep = None
+    sweep = fox_skip = None
     if args.sweep_steps > 0:
         sweep = bench_sweep(args.sweep_steps, 2)
+        fox_skip = bench_fox_skip(args.sweep_steps, 2)
+        log("fox workload, skipping negligible blocks: %.3f ms/step (full walk %.3f ms)" %
+            (fox_skip["ms_per_step"], fox_skip["full_walk_ms_per_step"]))
     cpu = None
     if args.cpu_seconds > 0:
         log("cpu baseline: oracle, ~%.0f s" % args.cpu_seconds)
@@ -352,6 +388,7 @@ def main():
                    "steps": dres["steps"]},
         "decode_cache_from_fwd": cache,
         "other_workloads": sweep,
+        "fox_skip_negligible": fox_skip,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

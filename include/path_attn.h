@@ -98,6 +98,28 @@ path_status_t path_attn_fwd(const void *q, const void *k, const void *v, const v
                             void *stream);
 
 /*
+ * path_attn_fwd with options.  flags is a bitwise OR of:
+ *
+ *   PATH_FWD_SKIP_NEGLIGIBLE  with logf: stop the right-to-left walk over key
+ *       blocks for a query block once every remaining block provably adds
+ *       less than 2^-64 of the running softmax maximum per key, i.e. far
+ *       below fp32 resolution of the output.  The bound is
+ *       ||qhat_i|| * max_j ||k_j|| + (forget-gate bias of the block boundary),
+ *       valid because every transition is a contraction when
+ *       0 <= beta_s ||w_s||^2 <= 2 (blocks violating that are never skipped).
+ *       The forget gate makes old keys decay, so long sequences need only a
+ *       window of recent blocks ([IPX] s.4).  Ignored without logf.
+ *
+ * Other bits must be zero (PATH_EINVAL).  Arguments and errors otherwise as
+ * path_attn_fwd, which is path_attn_fwd_ex with flags = 0.
+ */
+#define PATH_FWD_SKIP_NEGLIGIBLE 1u
+path_status_t path_attn_fwd_ex(const void *q, const void *k, const void *v, const void *w, const float *beta,
+                               const float *logf, void *out, float *lse, int B, int H, int L, int d,
+                               path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
+                               unsigned flags, void *stream);
+
+/*
  * The two stages of path_attn_fwd, for callers that schedule or time them
  * separately (path_attn_fwd is exactly prep followed by scan on one stream).
  *

@@ -47,8 +47,10 @@ def _unit_rows(z):
     return z / torch.linalg.vector_norm(z, dim=-1, keepdim=True)
 
 
-def fwd_inputs(B, H, L, d, dtype="bf16", seed=0, fox=False, clip=None, device="cpu"):
-    """Inputs of one forward pass: dict(q, k, v, w [B,H,L,d] dtype; beta, logf [B,H,L] fp32)."""
+def fwd_inputs(B, H, L, d, dtype="bf16", seed=0, fox=False, clip=None, device="cpu", fox_mean=3.0):
+    """Inputs of one forward pass: dict(q, k, v, w [B,H,L,d] dtype; beta, logf [B,H,L] fp32).
+
+    With fox, logf = logsigmoid(fox_mean + N(0, 1)) (the workloads use fox_mean 3)."""
     tdt = TORCH_DTYPES[dtype]
     g = _gen(device, seed)
     shape = (B, H, L, d)
@@ -63,7 +65,7 @@ def fwd_inputs(B, H, L, d, dtype="bf16", seed=0, fox=False, clip=None, device="c
     logf = None
     if fox:
         logf = torch.nn.functional.logsigmoid(
-            3.0 + torch.randn((B, H, L), generator=g, device=device, dtype=f32))
+            float(fox_mean) + torch.randn((B, H, L), generator=g, device=device, dtype=f32))
     out = dict(q=q.to(tdt), k=k.to(tdt), v=v.to(tdt), w=w.to(tdt), beta=beta.contiguous(), logf=logf)
     return out
 

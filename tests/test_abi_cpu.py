@@ -146,3 +146,10 @@ def cache_call(**over):
 ])
 def test_cache_from_fwd_rejects_bad_arguments(over, status):
     assert cache_call(**over) == status
+
+
+def test_fwd_ex_rejects_unknown_flags():
+    lib = pa.lib()
+    args = [P(0), P(1), P(2), P(3), P(4), None, P(5), None, 1, 1, 64, 64, BF, 0.0, P(6), 1 << 40]
+    assert lib.path_attn_fwd_ex(*args, 2, None) == pa.PATH_EINVAL
+    assert lib.path_attn_fwd_ex(*args[:1], None, *args[2:], 1, None) == pa.PATH_EINVAL  # k NULL, valid flag
