@@ -55,13 +55,13 @@ def _load(path=None):
         lib.oracle_fwd.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_double, i64p, ctypes.c_int64, dp, dp, ctypes.c_int]
         lib.oracle_decode.restype = ctypes.c_int
-        lib.oracle_decode.argtypes = [dp, dp, ctypes.c_int64, ctypes.c_int64, dp, dp, dp, dp, dp,
+        lib.oracle_decode.argtypes = [dp, dp, dp, ctypes.c_int64, ctypes.c_int64, dp, dp, dp, dp, dp, dp,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_double, dp, dp, ctypes.c_int]
         lib.oracle_scores_head.restype = None
         lib.oracle_scores_head.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_double, dp]
         lib.oracle_decode_cache.restype = ctypes.c_int
-        lib.oracle_decode_cache.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp]
+        lib.oracle_decode_cache.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp]
         lib.oracle_transport.restype = None
         lib.oracle_transport.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp]
         _libs[path] = lib
@@ -146,17 +146,22 @@ def transport(x, w, beta, lo, hi, lib=None):
     return out
 
 
-def decode(kc, vc, n, q, w, beta, k_new=None, v_new=None, scale=None, nthreads=None, lib=None):
+def decode(kc, vc, n, q, w, beta, k_new=None, v_new=None, scale=None, nthreads=None, lib=None, logf=None,
+           fcache=None):
     """One decode step in fp64.
 
     kc, vc: [..., rowcap, d] cache (copied; the updated copy is returned).
     q, w: [..., d]; beta: [...].  Rows [0, n) get k <- H_t k; with k_new/v_new
     ([..., d]) the pair is written at row n afterwards and n+1 rows attend.
-    Returns (kc_new, vc_new, out [..., d], lse [...]).
+    Forget gate: logf [...] = log f_t and fcache [..., rowcap] = c_j (cumulative
+    log f up to row j); row j's logit gets c_t - c_j with c_t = c_{n-1} + log f_t.
+    Returns (kc_new, vc_new, out [..., d], lse [...]), plus the updated fcache
+    when logf is given.
     """
     kc = _f64(kc).copy()
     vc = _f64(vc).copy()
-    q, w, beta, k_new, v_new = (_f64(x) for x in (q, w, beta, k_new, v_new))
+    q, w, beta, k_new, v_new, logf = (_f64(x) for x in (q, w, beta, k_new, v_new, logf))
+    fc = _f64(fcache).copy() if fcache is not None else None
     lead = q.shape[:-1]
     d = q.shape[-1]
     G = int(np.prod(lead)) if lead else 1
@@ -165,26 +170,30 @@ def decode(kc, vc, n, q, w, beta, k_new=None, v_new=None, scale=None, nthreads=N
         scale = 1.0 / np.sqrt(d)
     out = np.zeros((G, d))
     lse = np.zeros((G,))
-    rc = _load(lib).oracle_decode(_ptr(kc), _ptr(vc), int(n), int(rowcap), _ptr(q), _ptr(w), _ptr(beta),
-                               _ptr(k_new), _ptr(v_new), G, d, float(scale), _ptr(out), _ptr(lse),
+    rc = _load(lib).oracle_decode(_ptr(kc), _ptr(vc), _ptr(fc), int(n), int(rowcap), _ptr(q), _ptr(w), _ptr(beta),
+                               _ptr(logf), _ptr(k_new), _ptr(v_new), G, d, float(scale), _ptr(out), _ptr(lse),
                                int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_decode: bad arguments")
-    return kc, vc, out.reshape(lead + (d,)), lse.reshape(lead)
+    res = (kc, vc, out.reshape(lead + (d,)), lse.reshape(lead))
+    return res + (fc,) if logf is not None else res
 
 
-def decode_cache(k, w, beta, lib=None):
+def decode_cache(k, w, beta, lib=None, logf=None):
     """Decode cache after a prefix of L tokens, fp64: row j = H_{L-1} ... H_{j+1} k_j.
 
-    k, w: [..., L, d]; beta: [..., L].  Returns [..., L, d].
+    k, w: [..., L, d]; beta: [..., L].  Returns [..., L, d]; with logf
+    ([..., L]) also the gate cache [..., L] of inclusive prefix sums of log f.
     """
-    k, w, beta = _f64(k), _f64(w), _f64(beta)
+    k, w, beta, logf = _f64(k), _f64(w), _f64(beta), _f64(logf)
     lead = k.shape[:-2]
     L, d = k.shape[-2], k.shape[-1]
     G = int(np.prod(lead)) if lead else 1
     assert w.shape == k.shape and beta.shape == k.shape[:-1]
     out = np.zeros((G, L, d))
-    rc = _load(lib).oracle_decode_cache(_ptr(k), _ptr(w), _ptr(beta), G, L, d, _ptr(out))
+    fc = np.zeros((G, L)) if logf is not None else None
+    rc = _load(lib).oracle_decode_cache(_ptr(k), _ptr(w), _ptr(beta), _ptr(logf), G, L, d, _ptr(out), _ptr(fc))
     if rc != 0:
         raise ValueError("oracle_decode_cache: bad arguments")
-    return out.reshape(lead + (L, d))
+    out = out.reshape(lead + (L, d))
+    return (out, fc.reshape(lead + (L,))) if logf is not None else out

@@ -38,6 +38,10 @@
  * A new key/value (if given) enters after the update, untransformed, because
  * the logit of j = t has the empty product.
  *
+ * Decode with the forget gate: the bias of row j at step t is the path sum
+ * sum_{s=j+1..t} log f_s = c_t - c_j with c_j = sum_{s<=j} log f_s, so a
+ * cache of c_j per row (and the newest c_t = c_{t-1} + log f_t) is enough.
+ *
  * Decode cache after a prefix of L tokens [TS s.3]: if tokens 0 .. L-1 had
  * been fed one decode step at a time, cache row j would have been updated by
  * steps j+1, ..., L-1 in that order, so it holds H_{L-1} ... H_{j+1} k_j
@@ -201,14 +205,17 @@ int oracle_fwd(const double *q, const double *k, const double *v, const double *
  *   the update and the query attends to n+1 rows; otherwise to n rows.
  *   q, w: [d]; beta: scalar.  out: [d]; lse: scalar.
  */
-static void decode_head(double *kc, double *vc, int64_t n, const double *q, const double *w, double beta,
-                        const double *knew, const double *vnew, int d, double scale, double *out,
-                        double *lse) {
+static void decode_head(double *kc, double *vc, double *fc, int64_t n, const double *q, const double *w,
+                        double beta, const double *logf, const double *knew, const double *vnew, int d,
+                        double scale, double *out, double *lse) {
     for (int64_t j = 0; j < n; ++j) apply_h(kc + (size_t)j * d, w, beta, d);
+    /* forget gate: c_t of the current token; row j gets c_t - c_j */
+    const double ct = logf ? (n > 0 ? fc[n - 1] : 0.0) + *logf : 0.0;
     int64_t nt = n;
     if (knew && vnew) {
         memcpy(kc + (size_t)n * d, knew, sizeof(double) * (size_t)d);
         memcpy(vc + (size_t)n * d, vnew, sizeof(double) * (size_t)d);
+        if (logf) fc[n] = ct;
         nt = n + 1;
     }
     double m = -INFINITY;
@@ -216,6 +223,7 @@ static void decode_head(double *kc, double *vc, int64_t n, const double *q, cons
         double s = 0.0;
         for (int c = 0; c < d; ++c) s += kc[(size_t)j * d + c] * q[c];
         s *= scale;
+        if (logf) s += ct - fc[j];
         if (s > m) m = s;
     }
     double z = 0.0;
@@ -223,7 +231,7 @@ static void decode_head(double *kc, double *vc, int64_t n, const double *q, cons
     for (int64_t j = 0; j < nt; ++j) {
         double s = 0.0;
         for (int c = 0; c < d; ++c) s += kc[(size_t)j * d + c] * q[c];
-        double p = exp(scale * s - m);
+        double p = exp(scale * s + (logf ? ct - fc[j] : 0.0) - m);
         z += p;
         for (int c = 0; c < d; ++c) out[c] += p * vc[(size_t)j * d + c];
     }
@@ -232,9 +240,9 @@ static void decode_head(double *kc, double *vc, int64_t n, const double *q, cons
 }
 
 typedef struct {
-    double *kc, *vc;
+    double *kc, *vc, *fc;
     int64_t n, rowcap;
-    const double *q, *w, *beta, *knew, *vnew;
+    const double *q, *w, *beta, *logf, *knew, *vnew;
     int G, d;
     double scale;
     double *out, *lse;
@@ -251,8 +259,9 @@ static void *dec_worker(void *arg) {
         pthread_mutex_unlock(&jb->mu);
         if (g >= jb->G) break;
         size_t base = (size_t)g * (size_t)jb->rowcap * jb->d;
-        decode_head(jb->kc + base, jb->vc + base, jb->n, jb->q + (size_t)g * jb->d, jb->w + (size_t)g * jb->d,
-                    jb->beta[g], jb->knew ? jb->knew + (size_t)g * jb->d : NULL,
+        decode_head(jb->kc + base, jb->vc + base, jb->fc ? jb->fc + (size_t)g * (size_t)jb->rowcap : NULL, jb->n,
+                    jb->q + (size_t)g * jb->d, jb->w + (size_t)g * jb->d, jb->beta[g], jb->logf ? jb->logf + g : NULL,
+                    jb->knew ? jb->knew + (size_t)g * jb->d : NULL,
                     jb->vnew ? jb->vnew + (size_t)g * jb->d : NULL, jb->d, jb->scale,
                     jb->out + (size_t)g * jb->d, jb->lse + g);
     }
@@ -262,18 +271,21 @@ static void *dec_worker(void *arg) {
 /*
  * Decode step over G heads.  kc, vc: [G, rowcap, d]; rows [0, n) are the cache
  * (kc updated in place); with knew/vnew ([G, d]) rowcap must be >= n+1.
- * q, w: [G, d]; beta: [G]; out: [G, d]; lse: [G].  Returns 0 or -1.
+ * q, w: [G, d]; beta: [G]; out: [G, d]; lse: [G].
+ * Forget gate (both or neither): logf [G] = log f_t, fc [G, rowcap] = c_j per
+ * cached row (c_n is written when knew/vnew are given).  Returns 0 or -1.
  */
-int oracle_decode(double *kc, double *vc, int64_t n, int64_t rowcap, const double *q, const double *w,
-                  const double *beta, const double *knew, const double *vnew, int G, int d, double scale,
-                  double *out, double *lse, int nthreads) {
+int oracle_decode(double *kc, double *vc, double *fc, int64_t n, int64_t rowcap, const double *q, const double *w,
+                  const double *beta, const double *logf, const double *knew, const double *vnew, int G, int d,
+                  double scale, double *out, double *lse, int nthreads) {
     if (G < 0 || d < 1 || n < 0 || nthreads < 1) return -1;
     if ((knew == NULL) != (vnew == NULL)) return -1;
+    if ((logf == NULL) != (fc == NULL)) return -1;
     if (rowcap < n + (knew ? 1 : 0)) return -1;
     if (n + (knew ? 1 : 0) < 1) return -1;
     dec_job_t jb;
-    jb.kc = kc; jb.vc = vc; jb.n = n; jb.rowcap = rowcap;
-    jb.q = q; jb.w = w; jb.beta = beta; jb.knew = knew; jb.vnew = vnew;
+    jb.kc = kc; jb.vc = vc; jb.fc = fc; jb.n = n; jb.rowcap = rowcap;
+    jb.q = q; jb.w = w; jb.beta = beta; jb.logf = logf; jb.knew = knew; jb.vnew = vnew;
     jb.G = G; jb.d = d; jb.scale = scale; jb.out = out; jb.lse = lse; jb.next = 0;
     pthread_mutex_init(&jb.mu, NULL);
     pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
@@ -288,10 +300,21 @@ int oracle_decode(double *kc, double *vc, int64_t n, int64_t rowcap, const doubl
  * Decode cache of G heads after a prefix of L tokens: out[g][j] =
  * H_{L-1} ... H_{j+1} k_j, applying H_{j+1} first and H_{L-1} last (the order
  * of the in-place decode updates).  k, w: [G, L, d]; beta: [G, L];
- * out: [G, L, d].  Returns 0 or -1.
+ * out: [G, L, d].  With the forget gate, logf [G, L] gives the gate cache
+ * fc[g][j] = sum_{s<=j} log f_s (fc: [G, L]).  Returns 0 or -1.
  */
-int oracle_decode_cache(const double *k, const double *w, const double *beta, int G, int L, int d, double *out) {
-    if (G < 0 || L < 0 || d < 1) return -1;
+int oracle_decode_cache(const double *k, const double *w, const double *beta, const double *logf, int G, int L,
+                        int d, double *out, double *fc) {
+    if (G < 0 || L < 0 || d < 1 || ((logf == NULL) != (fc == NULL))) return -1;
+    if (logf) {
+        for (int g = 0; g < G; ++g) {
+            double c = 0.0;
+            for (int j = 0; j < L; ++j) {
+                c += logf[(size_t)g * L + j];
+                fc[(size_t)g * L + j] = c;
+            }
+        }
+    }
     for (int g = 0; g < G; ++g) {
         const double *kg = k + (size_t)g * L * d, *wg = w + (size_t)g * L * d, *bg = beta + (size_t)g * L;
         double *og = out + (size_t)g * L * d;

@@ -266,6 +266,30 @@ def pin_decode(lib):
     _close(kc2, ku, 1e-13, "decode cache without new token")
 
 
+def pin_decode_fox(lib):
+    """Decode with the forget gate from an empty cache reproduces the PaTH-FoX forward row by row,
+    and the gate cache holds the inclusive prefix sums of log f."""
+    T, d = 13, 5
+    q, k, v, w, b, lf = _rand_inputs(T, d, 31, fox=True)
+    ref_o, ref_l = oracle.fwd(q, k, v, w, b, lf, lib=lib)
+    kc, vc, fc = np.zeros((T, d)), np.zeros((T, d)), np.zeros(T)
+    for t in range(T):
+        kc, vc, o, l, fc = oracle.decode(kc, vc, t, q[t], w[t], b[t], k_new=k[t], v_new=v[t], lib=lib,
+                                         logf=np.array(lf[t]), fcache=fc)
+        _close(o, ref_o[t], 1e-12, "gated decode step %d vs forward row" % t)
+        _close(l, ref_l[t], 1e-12, "gated decode lse %d" % t)
+    _close(fc, np.cumsum(lf), 1e-13, "gate cache = prefix sums of log f")
+    _, fc2 = oracle.decode_cache(k, w, b, lib=lib, logf=lf)
+    _close(fc2, fc, 1e-13, "decode-cache gate column = the gated decode's")
+    # without a new token the query at position n attends to the n updated rows with bias c_n - c_j
+    n = T
+    kc2, _, o, _, _ = oracle.decode(kc, vc, n, q[0], w[0], b[0], lib=lib, logf=np.array(-0.7), fcache=fc)
+    ct = fc[n - 1] - 0.7
+    s_ = kc2 @ q[0] / math.sqrt(d) + (ct - fc)
+    p = np.exp(s_ - s_.max())
+    _close(o, p @ vc / p.sum(), 1e-13, "gated decode without new token")
+
+
 def pin_decode_cache(lib):
     """Decode cache after a prefix: explicit products H_{L-1} ... H_{j+1} k_j (brute force),
     equality with feeding the prefix through decode steps one token at a time, and the
@@ -292,4 +316,4 @@ def pin_decode_cache(lib):
 
 
 ALL_PINS = [pin_golden, pin_bruteforce, pin_ut_closed_form, pin_beta_zero, pin_beta_two, pin_beta_one,
-            pin_equal_w, pin_small_L, pin_fox_zero, pin_rows_subset, pin_decode, pin_decode_cache]
+            pin_equal_w, pin_small_L, pin_fox_zero, pin_rows_subset, pin_decode, pin_decode_fox, pin_decode_cache]

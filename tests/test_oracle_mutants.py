@@ -31,9 +31,16 @@ MUTANTS = [
     ("causal_diag_excluded", "for (int j = 0; j <= i; ++j) {\n        double p", "for (int j = 0; j < i; ++j) {\n        double p", 1),
     ("decode_no_update", "for (int64_t j = 0; j < n; ++j) apply_h(kc + (size_t)j * d, w, beta, d);", "", 1),
     ("decode_new_key_transformed",
-     "for (int64_t j = 0; j < n; ++j) apply_h(kc + (size_t)j * d, w, beta, d);\n    int64_t nt = n;\n    if (knew && vnew) {\n        memcpy(kc + (size_t)n * d, knew, sizeof(double) * (size_t)d);\n        memcpy(vc + (size_t)n * d, vnew, sizeof(double) * (size_t)d);\n        nt = n + 1;\n    }",
-     "int64_t nt = n;\n    if (knew && vnew) {\n        memcpy(kc + (size_t)n * d, knew, sizeof(double) * (size_t)d);\n        memcpy(vc + (size_t)n * d, vnew, sizeof(double) * (size_t)d);\n        nt = n + 1;\n    }\n    for (int64_t j = 0; j < nt; ++j) apply_h(kc + (size_t)j * d, w, beta, d);", 1),
-    ("decode_scale_dropped", "double p = exp(scale * s - m);", "double p = exp(s - m);", 1),
+     "        if (logf) fc[n] = ct;\n        nt = n + 1;\n    }",
+     "        if (logf) fc[n] = ct;\n        nt = n + 1;\n        apply_h(kc + (size_t)n * d, w, beta, d);\n    }", 1),
+    ("decode_scale_dropped", "double p = exp(scale * s + (logf ? ct - fc[j] : 0.0) - m);",
+     "double p = exp(s + (logf ? ct - fc[j] : 0.0) - m);", 1),
+    ("decode_gate_sign", "double p = exp(scale * s + (logf ? ct - fc[j] : 0.0) - m);",
+     "double p = exp(scale * s + (logf ? fc[j] - ct : 0.0) - m);", 1),
+    ("decode_gate_no_newest", "const double ct = logf ? (n > 0 ? fc[n - 1] : 0.0) + *logf : 0.0;",
+     "const double ct = logf ? (n > 0 ? fc[n - 1] : 0.0) : 0.0;", 1),
+    ("decode_gate_row_index", "double p = exp(scale * s + (logf ? ct - fc[j] : 0.0) - m);",
+     "double p = exp(scale * s + (logf ? ct - (j > 0 ? fc[j - 1] : 0.0) : 0.0) - m);", 1),
     ("cache_order_reversed", "for (int s = j + 1; s < L; ++s) apply_h(u, wg + (size_t)s * d, bg[s], d);",
      "for (int s = L - 1; s > j; --s) apply_h(u, wg + (size_t)s * d, bg[s], d);", 1),
     ("cache_includes_own_H", "for (int s = j + 1; s < L; ++s) apply_h(u, wg", "for (int s = j; s < L; ++s) apply_h(u, wg", 1),
