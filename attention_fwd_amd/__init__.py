@@ -12,8 +12,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_prep", "fwd_scan", "decode_step", "decode_cache_from_fwd", "fwd_workspace_size", "decode_workspace_size", "lib", "PathError",
-           "PATH_OK", "PATH_EINVAL", "PATH_EUNSUPPORTED", "PATH_EHIP", "PATH_DTYPE_F32", "PATH_DTYPE_BF16",
+__all__ = ["fwd", "fwd_prep", "fwd_scan", "decode_step", "decode_cache_from_fwd", "fwd_workspace_size",
+           "decode_workspace_size", "lib", "PathError", "PATH_OK", "PATH_EINVAL", "PATH_EUNSUPPORTED", "PATH_EHIP", "PATH_DTYPE_F32", "PATH_DTYPE_BF16",
            "PATH_FWD_SKIP_NEGLIGIBLE"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpath_attn.so")
@@ -59,10 +59,10 @@ def lib():
         L.path_decode_workspace_size.restype = sz
         L.path_decode_workspace_size.argtypes = [i, i, i64, i, ctypes.c_int]
         L.path_decode_step.restype = ctypes.c_int
-        L.path_decode_step.argtypes = [vp, vp, i64, i64, vp, vp, fp, vp, vp, vp, fp, i, i, i, ctypes.c_int,
+        L.path_decode_step.argtypes = [vp, vp, i64, i64, vp, vp, fp, fp, fp, vp, vp, vp, fp, i, i, i, ctypes.c_int,
                                        ctypes.c_float, vp, sz, vp]
         L.path_decode_cache_from_fwd.restype = ctypes.c_int
-        L.path_decode_cache_from_fwd.argtypes = [vp, sz, vp, vp, vp, i64, i, i, i, i, ctypes.c_int, vp]
+        L.path_decode_cache_from_fwd.argtypes = [vp, sz, vp, fp, vp, vp, fp, i64, i, i, i, i, ctypes.c_int, vp]
         _lib = L
     return _lib
 
@@ -180,11 +180,13 @@ def fwd_scan(out, lse, has_logf, workspace, scale=None, stream=None):
 
 
 def decode_step(kcache, vcache, n, q, w, beta, k_new=None, v_new=None, scale=None, out=None, lse=None,
-                return_lse=False, workspace=None, stream=None):
+                return_lse=False, workspace=None, stream=None, logf=None, fcache=None):
     """One PaTH decode step (path_decode_step): updates kcache rows [0, n) in place.
 
     kcache, vcache: [B, H, ncap, d]; q, w, k_new, v_new: [B, H, d]; beta: [B, H] fp32.
-    Returns out [B, H, d] (and lse [B, H] when requested).
+    PaTH-FoX: logf [B, H] fp32 (log f of the current token) with fcache
+    [B, H, ncap] fp32 (cumulative log f per cached row; row n is written when
+    k_new is given).  Returns out [B, H, d] (and lse [B, H] when requested).
     """
     if kcache.dim() != 4:
         raise ValueError("kcache must be [B, H, ncap, d]")
@@ -200,6 +202,11 @@ def decode_step(kcache, vcache, n, q, w, beta, k_new=None, v_new=None, scale=Non
     _check(beta, "beta", torch.float32, (B, H), dev)
     if (k_new is None) != (v_new is None):
         raise ValueError("k_new and v_new go together")
+    if (logf is None) != (fcache is None):
+        raise ValueError("logf and fcache go together")
+    if logf is not None:
+        _check(logf, "logf", torch.float32, (B, H), dev)
+        _check(fcache, "fcache", torch.float32, (B, H, ncap), dev)
     if k_new is not None:
         _check(k_new, "k_new", dt, (B, H, d), dev)
         _check(v_new, "v_new", dt, (B, H, d), dev)
@@ -217,7 +224,8 @@ def decode_step(kcache, vcache, n, q, w, beta, k_new=None, v_new=None, scale=Non
     _check(workspace, "workspace", None, None, dev)
     with torch.cuda.device(dev):
         st = lib().path_decode_step(_ptr(kcache), _ptr(vcache), int(n), ncap, _ptr(q), _ptr(w), _ptr(beta),
-                                    _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), B, H, d, _DTYPES[dt],
+                                    _ptr(logf), _ptr(fcache), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), B, H,
+                                    d, _DTYPES[dt],
                                     float(scale or 0.0), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream))
     if st != PATH_OK:
@@ -225,13 +233,14 @@ def decode_step(kcache, vcache, n, q, w, beta, k_new=None, v_new=None, scale=Non
     return (out, lse) if (return_lse or lse is not None) else out
 
 
-def decode_cache_from_fwd(workspace, v, kcache, vcache, stream=None):
+def decode_cache_from_fwd(workspace, v, kcache, vcache, stream=None, logf=None, fcache=None):
     """Fill decode caches from a forward pass's workspace (path_decode_cache_from_fwd).
 
     workspace: the workspace a fwd / fwd_prep call over this prefix used (same
     B, H, L, d, dtype); v: [B, H, L, d] prefix values; kcache, vcache:
     [B, H, ncap, d] with ncap >= L, rows [0, L) written: kcache row j =
-    H_{L-1} ... H_{j+1} k_j, vcache row j = v_j.
+    H_{L-1} ... H_{j+1} k_j, vcache row j = v_j.  With logf [B, H, L] and
+    fcache [B, H, ncap] (fp32) the gate cache gets the prefix sums of log f.
     """
     if v.dim() != 4 or kcache.dim() != 4:
         raise ValueError("v must be [B, H, L, d] and kcache [B, H, ncap, d]")
@@ -244,10 +253,15 @@ def decode_cache_from_fwd(workspace, v, kcache, vcache, stream=None):
     _check(kcache, "kcache", dt, (B, H, ncap, d), dev)
     _check(vcache, "vcache", dt, (B, H, ncap, d), dev)
     _check(workspace, "workspace", None, None, dev)
+    if (logf is None) != (fcache is None):
+        raise ValueError("logf and fcache go together")
+    if logf is not None:
+        _check(logf, "logf", torch.float32, (B, H, L), dev)
+        _check(fcache, "fcache", torch.float32, (B, H, ncap), dev)
     with torch.cuda.device(dev):
         st = lib().path_decode_cache_from_fwd(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(v),
-                                              _ptr(kcache), _ptr(vcache), int(ncap), B, H, L, d, _DTYPES[dt],
-                                              _stream(stream))
+                                              _ptr(logf), _ptr(kcache), _ptr(vcache), _ptr(fcache), int(ncap), B, H,
+                                              L, d, _DTYPES[dt], _stream(stream))
     if st != PATH_OK:
         raise PathError(st, "path_decode_cache_from_fwd")
     return kcache, vcache

@@ -191,11 +191,12 @@ size_t path_decode_workspace_size(int B, int H, int64_t n, int d, path_dtype_t d
 }
 
 path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,
-                               const float *beta, const void *k_new, const void *v_new, void *out, float *lse,
-                               int B, int H, int d, path_dtype_t dtype, float scale, void *workspace,
-                               size_t workspace_bytes, void *stream) {
+                               const float *beta, const float *logf, float *fcache, const void *k_new,
+                               const void *v_new, void *out, float *lse, int B, int H, int d, path_dtype_t dtype,
+                               float scale, void *workspace, size_t workspace_bytes, void *stream) {
     if (n < 0 || ncap < 1 || n > ncap) return PATH_EINVAL;
     if ((k_new == nullptr) != (v_new == nullptr)) return PATH_EINVAL;
+    if ((logf == nullptr) != (fcache == nullptr)) return PATH_EINVAL;
     const int64_t natt = n + (k_new ? 1 : 0);
     if (natt > ncap) return PATH_EINVAL;
     path_status_t st = dec_sizes_ok(B, H, natt, d, dtype);
@@ -206,6 +207,7 @@ path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t nc
                           (const void *)workspace})
         if (p && !aligned(p, 16)) return PATH_EINVAL;
     if (!aligned(beta, 4) || (lse && !aligned(lse, 4))) return PATH_EINVAL;
+    if (logf && (!aligned(logf, 4) || !aligned(fcache, 4))) return PATH_EINVAL;
     const size_t need = dec_ws_bytes(B, H, natt, d);
     if (workspace_bytes < need) return PATH_EINVAL;
     if (!(std::isfinite(scale))) return PATH_EINVAL;
@@ -221,11 +223,20 @@ path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t nc
     if (lse && (overlap(lse, sc, beta, sc) || overlap(lse, sc, out, vec) || overlap(lse, sc, workspace, (int64_t)need) ||
                 overlap(lse, sc, kcache, cache) || overlap(lse, sc, vcache, cache)))
         return PATH_EINVAL;
+    if (fcache) {
+        const int64_t fcs = (int64_t)B * H * ncap * 4;
+        for (const void *p : {(const void *)kcache, (const void *)vcache})
+            if (overlap(fcache, fcs, p, cache)) return PATH_EINVAL;
+        for (const void *p : {q, w, k_new, v_new, (const void *)out, (const void *)workspace})
+            if (overlap(fcache, fcs, p, p == workspace ? (int64_t)need : vec)) return PATH_EINVAL;
+        for (const void *p : {(const void *)beta, (const void *)logf, (const void *)lse})
+            if (overlap(fcache, fcs, p, sc)) return PATH_EINVAL;
+    }
     if (scale <= 0.f) scale = 1.0f / std::sqrt((float)d);
 
     path::DecodeArgs da{};
     da.kc = kcache; da.vc = vcache; da.n = n; da.ncap = ncap;
-    da.q = q; da.w = w; da.beta = beta; da.knew = k_new; da.vnew = v_new;
+    da.q = q; da.w = w; da.beta = beta; da.logf = logf; da.fcache = fcache; da.knew = k_new; da.vnew = v_new;
     da.out = out; da.lse = lse; da.ws = workspace;
     da.B = B; da.H = H; da.d = d; da.scale = scale;
     path::decode_plan((int64_t)B * H, natt, &da.nsplit, &da.chunk);
@@ -235,12 +246,15 @@ path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t nc
 }
 
 path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace_bytes, const void *v,
-                                         void *kcache, void *vcache, int64_t ncap, int B, int H, int L, int d,
-                                         path_dtype_t dtype, void *stream) {
+                                         const float *logf, void *kcache, void *vcache, float *fcache,
+                                         int64_t ncap, int B, int H, int L, int d, path_dtype_t dtype,
+                                         void *stream) {
     path_status_t st = fwd_sizes_ok(B, H, L, d, dtype);
     if (st != PATH_OK) return st;
     if (ncap < L || mul_chk({B, H, ncap, d, 8}) < 0) return PATH_EINVAL;
     if (!workspace || !v || !kcache || !vcache) return PATH_EINVAL;
+    if ((logf == nullptr) != (fcache == nullptr)) return PATH_EINVAL;
+    if (logf && (!aligned(logf, 4) || !aligned(fcache, 4))) return PATH_EINVAL;
     for (const void *p : {workspace, v, (const void *)kcache, (const void *)vcache})
         if (!aligned(p, 16)) return PATH_EINVAL;
     const size_t need = path::fwd_layout(B, H, L, d, elem_size(dtype)).total;
@@ -250,7 +264,15 @@ path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace
     if (overlap(kcache, cache, vcache, cache)) return PATH_EINVAL;
     for (const void *p : {(const void *)kcache, (const void *)vcache})
         if (overlap(p, cache, workspace, (int64_t)need) || overlap(p, cache, v, tens)) return PATH_EINVAL;
-    path::CacheArgs ca{workspace, v, kcache, vcache, ncap, B, H, L, d};
+    if (fcache) {
+        const int64_t fcs = (int64_t)B * H * ncap * 4, lfs = (int64_t)B * H * L * 4;
+        for (const void *p : {(const void *)kcache, (const void *)vcache})
+            if (overlap(fcache, fcs, p, cache)) return PATH_EINVAL;
+        if (overlap(fcache, fcs, workspace, (int64_t)need) || overlap(fcache, fcs, v, tens) ||
+            overlap(fcache, fcs, logf, lfs))
+            return PATH_EINVAL;
+    }
+    path::CacheArgs ca{workspace, v, logf, fcache, kcache, vcache, ncap, B, H, L, d};
     if ((int64_t)B * H > kMaxGrid) return PATH_EINVAL;
     return path::launch_cache(ca, dtype == PATH_DTYPE_BF16, (hipStream_t)stream) == hipSuccess ? PATH_OK : PATH_EHIP;
 }

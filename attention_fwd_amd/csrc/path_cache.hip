@@ -65,6 +65,24 @@ __global__ __launch_bounds__(64 * (D / 32)) void path_cache_kernel(CacheArgs a) 
         for (int64_t i = tid; i < nch; i += 64 * DT) *(u32x4 *)(vd + i * CH) = *(const u32x4 *)(vs + i * CH);
     }
 
+    // forget gate: inclusive prefix sums of log f (wave 0, 64 tokens per pass)
+    if (a.logf && ct == 0) {
+        const float *lf = a.logf + bh * (int64_t)a.L;
+        float *fc = a.fcache + bh * a.ncap;
+        float carry = 0.f;
+        for (int c0 = 0; c0 < a.L; c0 += 64) {
+            float v = c0 + lane < a.L ? lf[c0 + lane] : 0.f;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const float u = __shfl_up(v, o);
+                if (lane >= o) v += u;
+            }
+            v += carry;
+            if (c0 + lane < a.L) fc[c0 + lane] = v;
+            carry = __shfl(v, 63);
+        }
+    }
+
     // Sigma[:, 32 ct .. 32 ct + 31] = identity columns
     f32x16 sg[DT];
 #pragma unroll

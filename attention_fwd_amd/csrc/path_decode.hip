@@ -10,6 +10,9 @@
 //   a_j   = w . k_j,  b_j = q . k_j            (one 8-lane reduction for both)
 //   k_j'  = k_j - beta a_j w                   (stored back, rounded to the cache type)
 //   s_j   = scale * q . k_j' = scale * (b_j - beta a_j (q . w))
+//           (+ c_t - c_j with the forget gate: c_j = sum_{s<=j} log f_s is kept
+//            per cached row, c_t = c_{n-1} + log f_t; "거리에서 경로로, PaTH
+//            Attention", section 4, PaTH-FoX)
 // followed by an online softmax over the rows of a split.  Eight lanes share
 // a row (8 elements = 16 bytes of bf16 each), a wave covers 8 rows per load
 // and every lane keeps 4 rows in flight.  Splits of the cache write partial
@@ -90,22 +93,27 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
     for (int e = 0; e < EPL; ++e) qw += q[e] * w[e];
     qw = sum8(qw);
     const float c2 = a.scale * kLog2e;
+    const bool gate = a.logf != nullptr;
+    float *fcr = gate ? a.fcache + bh * a.ncap : nullptr;
+    const float ct = gate ? (a.n > 0 ? fcr[a.n - 1] : 0.f) + a.logf[bh] : 0.f;
 
     float m = -INFINITY, l = 0.f, acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 
     for (int64_t base = r0 + grp; base < r1; base += (int64_t)NG * kRowsPerIter) {
-        float kx[kRowsPerIter][EPL], vx[kRowsPerIter][EPL], x[kRowsPerIter];
+        float kx[kRowsPerIter][EPL], vx[kRowsPerIter][EPL], x[kRowsPerIter], gb[kRowsPerIter];
         bool ok[kRowsPerIter], fresh[kRowsPerIter];
 #pragma unroll
         for (int u = 0; u < kRowsPerIter; ++u) {
             const int64_t j = base + (int64_t)u * NG;
             ok[u] = j < r1;
             fresh[u] = ok[u] && j == a.n;  // the appended token (only when knew != NULL)
+            gb[u] = 0.f;                   // forget-gate bias, log2 units
             if (ok[u] && !fresh[u]) {
                 loadn<S, EPL>(kc + j * D + EPL * sub, kx[u]);
                 loadn<S, EPL>(vc + j * D + EPL * sub, vx[u]);
+                if (gate) gb[u] = (ct - fcr[j]) * kLog2e;
             } else if (fresh[u]) {
                 loadn<S, EPL>((const S *)a.knew + bh * D + EPL * sub, kx[u]);
                 loadn<S, EPL>((const S *)a.vnew + bh * D + EPL * sub, vx[u]);
@@ -128,6 +136,7 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
                 // new key enters untransformed; store k_new, v_new at row n
                 storen<S, EPL>(kc + j * D + EPL * sub, kx[u]);
                 storen<S, EPL>(vc + j * D + EPL * sub, vx[u]);
+                if (gate && sub == 0) fcr[j] = ct;
                 x[u] = tb * c2;
             } else if (ok[u]) {
                 const float cb = beta * ta;
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) kn[e] = kx[u][e] - cb * w[e];
                 storen<S, EPL>(kc + j * D + EPL * sub, kn);
-                x[u] = (tb - cb * qw) * c2;
+                x[u] = (tb - cb * qw) * c2 + gb[u];
             } else {
                 x[u] = -INFINITY;
             }

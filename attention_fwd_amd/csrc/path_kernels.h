@@ -31,6 +31,8 @@ struct DecodeArgs {
     int64_t n, ncap;
     const void *q, *w;
     const float *beta;
+    const float *logf;  // forget gate: log f_t [B, H], or NULL
+    float *fcache;      // forget gate: c_j = sum_{s<=j} log f_s per cached row [B, H, ncap], or NULL
     const void *knew, *vnew;
     void *out;
     float *lse;
@@ -43,6 +45,8 @@ struct DecodeArgs {
 
 struct CacheArgs {
     const void *ws, *v;
+    const float *logf;  // prefix log-forget gate [B, H, L] or NULL
+    float *fcache;      // its inclusive prefix sums [B, H, ncap] or NULL
     void *kc, *vc;
     int64_t ncap;
     int B, H, L, d;

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PATH_ABI_VERSION 1
+#define PATH_ABI_VERSION 2
 
 typedef enum {
     PATH_OK = 0,
@@ -156,9 +156,16 @@ size_t path_decode_workspace_size(int B, int H, int64_t n, int d, path_dtype_t d
  * non-NULL they are stored at row n AFTER the update (the newest key has the
  * empty product) and the query attends to n+1 rows; otherwise to n rows.
  *
+ * PaTH-FoX ([IPX] s.4): with logf and fcache (both or neither) row j's logit
+ * gets sum_{s=j+1..t} log f_s = c_t - c_j, where fcache holds
+ * c_j = sum_{s<=j} log f_s for the cached rows and c_t = c_{n-1} + logf_t
+ * (c_{-1} = 0); with k_new, c_t is stored at fcache row n.
+ *
  * kcache, vcache : [B, H, ncap, d] element type `dtype`; rows >= n (+1) untouched
  * n              : rows in use, 0 <= n <= ncap (n + 1 <= ncap with k_new; at least one row must attend)
  * q, w           : [B, H, d] element type `dtype`; beta: [B, H] fp32
+ * logf           : [B, H] fp32 log f_t of the current token, or NULL
+ * fcache         : [B, H, ncap] fp32 gate cache (read rows [0, n), row n written with k_new), or NULL
  * k_new, v_new   : [B, H, d] or both NULL
  * out            : [B, H, d] element type `dtype`; lse: [B, H] fp32 or NULL
  * scale          : <= 0 selects 1/sqrt(d)
@@ -169,7 +176,8 @@ size_t path_decode_workspace_size(int B, int H, int64_t n, int d, path_dtype_t d
  * k_j^T (H_{j+1} ... H_t) q_t.
  */
 path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,
-                               const float *beta, const void *k_new, const void *v_new, void *out, float *lse,
+                               const float *beta, const float *logf, float *fcache, const void *k_new,
+                               const void *v_new, void *out, float *lse,
                                int B, int H, int d, path_dtype_t dtype, float scale, void *workspace,
                                size_t workspace_bytes, void *stream);
 
@@ -181,6 +189,7 @@ path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t nc
  *
  *   kcache[b,h,j,:] = H_{L-1} ... H_{j+1} k_j     (H_{j+1} applied first; row L-1 = k_{L-1})
  *   vcache[b,h,j,:] = v_j                          for j in [0, L)
+ *   fcache[b,h,j]   = sum_{s<=j} logf[b,h,s]        (when logf and fcache are given)
  *
  * rounded to `dtype`, so that path_decode_step with n = L continues the
  * sequence.  The keys come from the boundary-adjusted key blocks and block
@@ -190,14 +199,17 @@ path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t nc
  *                  the same B, H, L, d and dtype, enqueued before this call on the
  *                  same stream (or completed); results are undefined otherwise
  * v              : [B, H, L, d] element type `dtype`, the prefix values (read only)
+ * logf, fcache   : [B, H, L] fp32 prefix log-forget gate and [B, H, ncap] fp32 gate cache
+ *                  for a PaTH-FoX decode, or both NULL
  * kcache, vcache : [B, H, ncap, d] element type `dtype`, ncap >= L; rows >= L untouched
  *
  * Returns PATH_OK, PATH_EINVAL (NULL, sizes, misaligned, workspace too small,
  * ncap < L, overlapping buffers), PATH_EUNSUPPORTED or PATH_EHIP.
  */
 path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace_bytes, const void *v,
-                                         void *kcache, void *vcache, int64_t ncap, int B, int H, int L, int d,
-                                         path_dtype_t dtype, void *stream);
+                                         const float *logf, void *kcache, void *vcache, float *fcache,
+                                         int64_t ncap, int B, int H, int L, int d, path_dtype_t dtype,
+                                         void *stream);
 
 #ifdef __cplusplus
 }

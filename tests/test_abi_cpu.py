@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = pa.lib()
-    assert lib.path_abi_version() == 1
+    assert lib.path_abi_version() == 2
     for s in range(4):
         assert lib.path_status_string(s)
     assert lib.path_status_string(99) == b"unknown status"
@@ -92,11 +92,13 @@ def test_fwd_rejects_bad_arguments(over, status):
 
 
 def dec_call(**over):
-    args = dict(kc=P(0), vc=ctypes.c_void_p(A * 40), n=100, ncap=100, q=P(80), w=P(81), beta=P(82), kn=None, vn=None,
+    args = dict(kc=P(0), vc=ctypes.c_void_p(A * 40), n=100, ncap=100, q=P(80), w=P(81), beta=P(82), lf=None, fc=None,
+                kn=None, vn=None,
                 out=P(83), lse=None, B=1, H=1, d=64, dtype=BF, scale=0.0, ws=P(84), wsb=1 << 30, stream=None)
     args.update(over)
     return pa.lib().path_decode_step(args["kc"], args["vc"], args["n"], args["ncap"], args["q"], args["w"],
-                                     args["beta"], args["kn"], args["vn"], args["out"], args["lse"], args["B"],
+                                     args["beta"], args["lf"], args["fc"], args["kn"], args["vn"], args["out"],
+                                     args["lse"], args["B"],
                                      args["H"], args["d"], args["dtype"], args["scale"], args["ws"], args["wsb"],
                                      args["stream"])
 
@@ -115,6 +117,9 @@ def dec_call(**over):
     (dict(vc=P(0)), pa.PATH_EINVAL),                           # caches alias
     (dict(out=P(0)), pa.PATH_EINVAL),                          # out inside the key cache
     (dict(dtype=3), pa.PATH_EINVAL),
+    (dict(lf=P(86)), pa.PATH_EINVAL),                          # gate without its cache
+    (dict(lf=P(86), fc=P(0)), pa.PATH_EINVAL),                 # gate cache over the key cache
+    (dict(lf=P(86), fc=ctypes.c_void_p(A * 87 + 2)), pa.PATH_EINVAL),  # misaligned gate cache
 ])
 def test_decode_rejects_bad_arguments(over, status):
     assert dec_call(**over) == status
@@ -123,11 +128,12 @@ def test_decode_rejects_bad_arguments(over, status):
 def cache_call(**over):
     # the workspace sits above every other buffer, so the baseline call has no overlap
     args = dict(ws=ctypes.c_void_p(A * 1024), wsb=1 << 40, v=ctypes.c_void_p(A * 64), kc=ctypes.c_void_p(A * 128),
-                vc=ctypes.c_void_p(A * 192),
+                vc=ctypes.c_void_p(A * 192), lf=None, fc=None,
                 ncap=256, B=1, H=1, L=200, d=64, dtype=BF, stream=None)
     args.update(over)
-    return pa.lib().path_decode_cache_from_fwd(args["ws"], args["wsb"], args["v"], args["kc"], args["vc"], args["ncap"],
-                                               args["B"], args["H"], args["L"], args["d"], args["dtype"], args["stream"])
+    return pa.lib().path_decode_cache_from_fwd(args["ws"], args["wsb"], args["v"], args["lf"], args["kc"], args["vc"],
+                                               args["fc"], args["ncap"], args["B"], args["H"], args["L"], args["d"],
+                                               args["dtype"], args["stream"])
 
 
 @pytest.mark.parametrize("over,status", [
@@ -143,6 +149,8 @@ def cache_call(**over):
     (dict(vc=ctypes.c_void_p(A * 128)), pa.PATH_EINVAL),       # caches alias
     (dict(kc=ctypes.c_void_p(A * 1024 + 4096)), pa.PATH_EINVAL),  # key cache inside the used workspace
     (dict(vc=ctypes.c_void_p(A * 64)), pa.PATH_EINVAL),        # value cache over the values
+    (dict(lf=ctypes.c_void_p(A * 256)), pa.PATH_EINVAL),       # gate without its cache
+    (dict(lf=ctypes.c_void_p(A * 256), fc=ctypes.c_void_p(A * 128)), pa.PATH_EINVAL),  # gate cache over keys
 ])
 def test_cache_from_fwd_rejects_bad_arguments(over, status):
     assert cache_call(**over) == status

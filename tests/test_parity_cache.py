@@ -113,6 +113,41 @@ def test_cache_bf16(L, d):
 
 
 @gpu
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("L", [64, 333])
+def test_cache_fox_prefill_then_decode(L, dtype):
+    """PaTH-FoX prefix: the gate cache holds the prefix sums of log f, and gated decode steps on
+    top of the caches reproduce the oracle's PaTH-FoX forward rows."""
+    say("case cache fox %s L%d" % (dtype, L))
+    T = L + 3
+    x = pathgen.fwd_inputs(1, 2, T, 64, dtype, seed=400 + L, fox=True, clip=1.98 if dtype == "bf16" else None,
+                           device="cuda")
+    xp = {k: v[:, :, :L].contiguous() for k, v in x.items()}
+    B, H, _, d = xp["q"].shape
+    ws = torch.empty(pa.fwd_workspace_size(B, H, L, d, xp["q"].dtype), device="cuda", dtype=torch.uint8)
+    pa.fwd(xp["q"], xp["k"], xp["v"], xp["w"], xp["beta"], xp["logf"], workspace=ws)
+    kc = torch.zeros((B, H, T, d), device="cuda", dtype=xp["q"].dtype)
+    vc = torch.zeros_like(kc)
+    fc = torch.zeros((B, H, T), device="cuda")
+    pa.decode_cache_from_fwd(ws, xp["v"], kc, vc, logf=xp["logf"], fcache=fc)
+    torch.cuda.synchronize()
+    _, rfc = oracle.decode_cache(xp["k"].cpu(), xp["w"].cpu(), xp["beta"].cpu(), logf=xp["logf"].cpu())
+    ef = max_abs(to_np(fc[:, :, :L]), rfc)
+    assert ef <= 1e-5 * max(1.0, float(np.abs(rfc).max())), "gate cache %.2e" % ef
+    ro, rl = oracle.fwd(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["w"].cpu(), x["beta"].cpu(), x["logf"].cpu())
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    for t in range(L, T):
+        sl = (slice(None), slice(None), t)
+        o, l = pa.decode_step(kc, vc, t, x["q"][sl].contiguous(), x["w"][sl].contiguous(), x["beta"][sl].contiguous(),
+                              k_new=x["k"][sl].contiguous(), v_new=x["v"][sl].contiguous(), return_lse=True,
+                              logf=x["logf"][sl].contiguous(), fcache=fc)
+        torch.cuda.synchronize()
+        eo, el = max_abs(to_np(o), ro[:, :, t]), max_abs(to_np(l), rl[:, :, t])
+        assert eo <= tol and el <= tol, "gated decode step %d after the cache: %.2e %.2e" % (t, eo, el)
+    say("  gate cache %.2e; gated decode after cache ok" % ef)
+
+
+@gpu
 def test_cache_after_fox_forward():
     """The forget gate changes only the logits, not the key blocks: the cache is the same."""
     say("case cache after a PaTH-FoX forward")

@@ -185,3 +185,66 @@ def test_decode_checkpoint_resume():
     outs2 += [pa.decode_step(kc2, vc2, n, x["q"][t], x["w"][t], x["beta"][t]) for t in range(4, 8)]
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(outs1, outs2)) and torch.equal(kc1, kc2)
+
+
+def gate_state(B, H, ncap, n, seed):
+    """Random gate cache (prefix sums of log f = logsigmoid(3 + N(0,1))) and the current log f."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    lf = torch.nn.functional.logsigmoid(3.0 + torch.randn((B, H, ncap + 1), generator=g, device="cuda"))
+    fc = torch.zeros((B, H, ncap), device="cuda")
+    fc[:, :, :n] = torch.cumsum(lf[:, :, :n].double(), dim=-1).float()
+    return fc, lf[:, :, n].contiguous()
+
+
+@gpu
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [1, 130, 2000])
+@pytest.mark.parametrize("append", [False, True], ids=["cache", "append"])
+def test_decode_fox(dtype, n, append):
+    """PaTH-FoX decode against the oracle: out, lse, the in-place key update, the gate cache row n."""
+    B, H, d = 2, 2, 64
+    say("case decode fox %s n%d append=%s" % (dtype, n, append))
+    ncap = n + 1
+    x = pathgen.decode_inputs(B, H, n, d, steps=2, dtype=dtype, seed=40 + n, clip=1.98 if dtype == "bf16" else None,
+                              device="cuda", rowcap=ncap)
+    fc, lf = gate_state(B, H, ncap, n, 50 + n)
+    kn = x["q"][1].clone() if append else None  # any [B, H, d] tensor serves as the new key/value
+    vn = x["w"][1].clone() if append else None
+    kc0, vc0, fc0 = x["kcache"].cpu(), x["vcache"].cpu(), fc.cpu()
+    out, lse = pa.decode_step(x["kcache"], x["vcache"], n, x["q"][0], x["w"][0], x["beta"][0], k_new=kn, v_new=vn,
+                              return_lse=True, logf=lf, fcache=fc)
+    torch.cuda.synchronize()
+    rk, _, ro, rl, rfc = oracle.decode(kc0, vc0, n, x["q"][0].cpu(), x["w"][0].cpu(), x["beta"][0].cpu(),
+                                        k_new=kn.cpu() if append else None, v_new=vn.cpu() if append else None,
+                                        logf=lf.cpu(), fcache=fc0)
+    eo, el = max_abs(to_np(out), ro), max_abs(to_np(lse), rl)
+    ek = max_abs(to_np(x["kcache"][:, :, :n]), rk[:, :, :n])
+    ef = max_abs(to_np(fc), rfc)
+    say("  out %.2e lse %.2e cache %.2e gate cache %.2e" % (eo, el, ek, ef))
+    tol_o, tol_l = (1e-4, 1e-4) if dtype == "f32" else (2e-2, 1e-2)
+    assert eo <= tol_o and el <= tol_l
+    assert ek <= (1e-5 if dtype == "f32" else 3e-2)
+    assert ef <= 1e-5 * max(1.0, float(np.abs(rfc).max())), "gate cache row n"
+
+
+@gpu
+def test_decode_fox_reproduces_forward_fp32():
+    """PaTH-FoX: decoding token by token from an empty cache gives the forward pass's rows."""
+    B, H, T, d = 1, 2, 70, 64
+    say("case decode fox vs forward")
+    x = pathgen.fwd_inputs(B, H, T, d, "f32", seed=22, fox=True, device="cuda")
+    fo = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"])
+    ro, rl = oracle.fwd(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["w"].cpu(), x["beta"].cpu(), x["logf"].cpu())
+    kc = torch.zeros(B, H, T, d, device="cuda")
+    vc = torch.zeros(B, H, T, d, device="cuda")
+    fc = torch.zeros(B, H, T, device="cuda")
+    for t in range(T):
+        sl = (slice(None), slice(None), t)
+        o, l = pa.decode_step(kc, vc, t, x["q"][sl].contiguous(), x["w"][sl].contiguous(), x["beta"][sl].contiguous(),
+                              k_new=x["k"][sl].contiguous(), v_new=x["v"][sl].contiguous(), return_lse=True,
+                              logf=x["logf"][sl].contiguous(), fcache=fc)
+        torch.cuda.synchronize()
+        assert max_abs(to_np(o), ro[:, :, t]) <= 1e-4, "step %d vs oracle" % t
+        assert max_abs(to_np(l), rl[:, :, t]) <= 1e-4
+        assert max_abs(to_np(o), to_np(fo[:, :, t])) <= 1e-4, "step %d vs forward kernel" % t
