@@ -22,13 +22,19 @@
 // the (max, sum) workspace by the prep kernel, so every block here is a full,
 // unmasked 64 x 64 tile.
 //
-// A step J first issues its 36 matrix-core products (the 64-key logits and
-// the query transform, which is independent of the softmax), then takes the
-// column maxima of all 64 keys with a single check for the rare rescale, and
-// only then runs the vector work (exp2, column sums, bf16 probabilities)
-// interleaved with the 16 products of P V, so one branch-free region holds
-// the whole softmax.  A workgroup is 4 waves = 4 consecutive query blocks
-// sharing each key-block record (khat, V^T, -M: 24 KiB bf16 at d = 64),
+// Without the forget gate the walk is first made with the softmax reference
+// max fixed at 0 ("bounded walk"): a step is then its 32 products of logits
+// and query transform, exp2 of the logits, column sums, bf16 probabilities
+// and the 16 products of P V, with no max, no check and no branch.  Floating
+// point makes that exact unless a probability overflows or every relevant one
+// underflows, which an end-of-walk test per query detects; such waves are
+// walked again by a second launch with the running max ("checked walk", also
+// the only walk under the forget gate).  A checked step issues its matrix-core
+// products first (the running max folded into the logit product as one more
+// k-chunk in bf16), then takes the column maxima of all 64 keys with a single
+// check for the rare rescale, and only then runs the vector work interleaved
+// with the products of P V.  A workgroup is 4 waves = 4 consecutive query
+// blocks sharing each key-block record (khat, V^T, -M: 24 KiB bf16 at d = 64),
 // double-buffered in LDS; two workgroups share a CU.
 #include <type_traits>
 
@@ -233,8 +239,8 @@ __device__ __forceinline__ void step_check(WaveState<D, CT, NS> &w, const float 
 }
 
 // Vector part of step J from logit buffer SB: probabilities, their column
-// sums, and O^T += V^T P^T.
-template <typename S, int D, int CT, int NS, bool FOX, bool FOLD, int SB>
+// sums, and O^T += V^T P^T.  BND: bounded walk, the reference max is 0.
+template <typename S, int D, int CT, int NS, bool FOX, bool FOLD, int SB, bool BND = false>
 __device__ __forceinline__ void step_softmax_pv(WaveState<D, CT, NS> &w, const S *rec, float fbJ, int lane) {
     typedef Elem<S> E;
     typedef typename E::Frag Frag;
@@ -250,7 +256,7 @@ __device__ __forceinline__ void step_softmax_pv(WaveState<D, CT, NS> &w, const S
                 const float sh = w.m[ct] - w.off[ct];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r] - sh);
-            } else if constexpr (FOLD) {
+            } else if constexpr (FOLD || BND) {  // the accumulator already holds s - m (BND: m = 0)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r]);
             } else {
@@ -282,7 +288,12 @@ __device__ __forceinline__ void step_softmax_pv(WaveState<D, CT, NS> &w, const S
     }
 }
 
-template <typename S, int D, bool FOX>
+// MODE: kChecked walks with the running max; kBounded walks with the
+// reference max fixed at 0 and flags the workgroups whose result it cannot
+// keep; kRedo repeats the checked walk for the flagged workgroups only.
+enum { kChecked = 0, kBounded = 1, kRedo = 2 };
+
+template <typename S, int D, bool FOX, int MODE>
 __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU)) void path_fwd_kernel(FwdArgs a) {
     static_assert(D == 64 || D == 128, "forward kernel: head dimension 64 or 128");
     typedef FwdCfg<S, D> F;
@@ -292,6 +303,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
     constexpr int VEC = 16 / (int)sizeof(S);   // elements per 16-byte load
     constexpr int NLD = REC / VEC / NT;        // 16-byte loads per thread per record
     constexpr bool kFold = sizeof(S) == 2 && !FOX;  // running max folded into the logit product
+    static_assert(MODE == kChecked || !FOX, "the bounded walk is for attention without the forget gate");
     static_assert(REC % (VEC * NT) == 0, "record must split evenly over the workgroup");
     __shared__ __attribute__((aligned(32))) S srec[NB][REC];
     __shared__ __attribute__((aligned(16))) float stail[NB][kBlk];
@@ -301,6 +313,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
     const FwdLayout lay = fwd_layout(a.B, a.H, a.L, D, sizeof(S));
     const int nb = (int)lay.nb;
     const int ntile = (nb + QB - 1) / QB;
+    int *redo = (int *)((char *)a.ws + lay.off_redo);
 
     // Work item: heads are kept together on one XCD (workgroups are dealt
     // round-robin over the 8 XCDs, each with its own L2), longest tiles first.
@@ -312,18 +325,33 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
 
     const int I = QB * tile + (wv * CT) / 2;     // this wave's query block
     const int c0 = 32 * ((wv * CT) % 2);         // first query column of this wave inside the block
-    const bool active = I >= 1 && I < nb;        // block 0 is complete after prep
     const int Jtop = min(QB * tile + QB - 1, nb - 1) - 1;
     if (Jtop < 0) return;
+    // redo flags: one per wave of the bounded walk (workgroup g, wave wv)
+    int *wflag = redo + g * NW;
+    bool redo_me = true;
+    if constexpr (MODE == kRedo) {
+        int any = 0;
+#pragma unroll
+        for (int v2 = 0; v2 < NW; ++v2) any |= wflag[v2];
+        if (!any) return;  // uniform: the bounded walk's results stand
+        redo_me = wflag[wv] != 0;
+    }
+    const bool active = I >= 1 && I < nb && redo_me;  // block 0 is complete after prep
 
     const S *recs = (const S *)((const char *)a.ws + lay.off_rec) + bh * lay.nb * REC;
     const float *fk = (const float *)((const char *)a.ws + lay.off_fk) + bh * lay.lp;
     const float *fb = (const float *)((const char *)a.ws + lay.off_fb) + bh * lay.nb;
 
     // ---- per-wave state: qhat (pre-scaled by scale * log2(e): logits are in
-    // log2 units), the diagonal block's output, max and sum
+    // log2 units), the diagonal block's output, max and sum.  In the bounded
+    // walk the reference max is 0, so the diagonal block's sum and output are
+    // taken at scale 2^m (0 or inf when that under- or overflows, which the
+    // end-of-walk test catches).
     WaveState<D, CT, 1> w;
-    if (active) {
+    auto init_state = [&](auto bounded) {
+        constexpr bool BND = decltype(bounded)::value;
+        if (!active) return;
         const S *qh = (const S *)((const char *)a.ws + lay.off_qhat) + (bh * lay.lp + (int64_t)I * kBlk) * D;
         const S *od = (const S *)a.out + (bh * a.L + (int64_t)I * kBlk) * D;
         const float *md = (const float *)((const char *)a.ws + lay.off_mdiag) + bh * lay.lp + (int64_t)I * kBlk;
@@ -336,7 +364,10 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
             const int io = valid ? i : 0;  // rows past L read row 0 of the block, then drop it
             float ls = ld[i];
             w.m[ct] = md[i];
-            if constexpr (kFold) {
+            if constexpr (BND) {
+                ls *= fast_exp2(w.m[ct]);
+                w.m[ct] = 0.f;
+            } else if constexpr (kFold) {
                 // switch the reference to the nearest two-piece bf16 value
                 const float m0 = w.m[ct];
                 fold_split(m0, h, w.m[ct], w.mb[ct]);
@@ -360,7 +391,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
                     }
                 }
         }
-    }
+    };
 
     // ---- skipping negligible key blocks (forget gate only, on request).  With
     // every transition a contraction (0 <= beta ||w||^2 <= 2, checked per block
@@ -374,7 +405,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
     const bool skip = FOX && a.skip;
     bool wdone = !active;
     float qbound[CT];
-    if (skip) {
+    auto setup_skip = [&]() {
         const float *kn = (const float *)((const char *)a.ws + lay.off_kn) + bh * lay.nb;
         float km = 0.f;
         for (int j = lane; j <= Jtop; j += 64) km = fmaxf(km, kn[j]);
@@ -390,7 +421,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
             qbound[ct] = sqrtf(other_half_sum(ss)) * (1.f + 0x1p-10f) * km;  // rounded up; inf if not contractive
         }
         if (lane == 0) sdone[wv] = wdone;
-    }
+    };
     auto negligible = [&]() {
         bool ok = true;
 #pragma unroll
@@ -409,51 +440,64 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
     };
     auto rec_ptr = [&](int J) { return recs + (int64_t)J * REC; };
     auto tail_ptr = [&](int J) { return fk + (int64_t)J * kBlk; };
-    // All waves in step; NB - 1 records ahead (a single buffer is refilled
-    // after every wave is done with it).
+    // One walk over the key blocks J = Jtop .. 0.  All waves in step; NB - 1
+    // records ahead (a single buffer is refilled after every wave is done with
+    // it).  The last step waits for every copy, so no copy is in flight after
+    // a full walk.
+    auto walk = [&](auto bounded) {
+        constexpr bool BND = decltype(bounded)::value;
 #pragma unroll
-    for (int k = 0; k < (NB > 1 ? NB - 1 : 1); ++k)
-        if (Jtop - k >= 0) issue_record<S, REC, NLD, NW, FOX>(rec_ptr(Jtop - k), tail_ptr(Jtop - k), srec[k], stail[k], wv, lane);
-    for (int J = Jtop; J >= 0; --J) {
-        const int it = Jtop - J, buf = it % NB;
-        // wait for this wave's copies of record J; the copies of the NB - 2 newer
-        // records issued after it may stay in flight
-        if (NB > 2 && J >= 1)
-            wait_records(std::integral_constant<int, (NB > 2 ? NB - 2 : 0)>{});
-        else
-            wait_records(std::integral_constant<int, 0>{});
-        barrier_only();  // every wave's copies have landed; buffer (it + NB - 1) % NB is free
-        if (skip) {
-            bool all = true;
+        for (int k = 0; k < (NB > 1 ? NB - 1 : 1); ++k)
+            if (Jtop - k >= 0)
+                issue_record<S, REC, NLD, NW, FOX>(rec_ptr(Jtop - k), tail_ptr(Jtop - k), srec[k], stail[k], wv, lane);
+        for (int J = Jtop; J >= 0; --J) {
+            // unsigned: the read buffer it % NB and the refilled one (it + NB - 1) % NB
+            // are then provably different, so the compiler does not make the
+            // reads of this record wait for the copies of the next one
+            const unsigned it = (unsigned)(Jtop - J);
+            const int buf = (int)(it % NB);
+            // wait for this wave's copies of record J; the copies of the NB - 2 newer
+            // records issued after it may stay in flight
+            if (NB > 2 && J >= 1)
+                wait_records(std::integral_constant<int, (NB > 2 ? NB - 2 : 0)>{});
+            else
+                wait_records(std::integral_constant<int, 0>{});
+            barrier_only();  // every wave's copies have landed; buffer (it + NB - 1) % NB is free
+            if (skip) {
+                bool all = true;
 #pragma unroll
-            for (int v2 = 0; v2 < NW; ++v2) all = all && sdone[v2];
-            if (all) break;  // uniform: every wave read the same flags after the barrier
+                for (int v2 = 0; v2 < NW; ++v2) all = all && sdone[v2];
+                if (all) break;  // uniform: every wave read the same flags after the barrier
+            }
+            if (NB > 1 && J - (NB - 1) >= 0) {
+                const int jn = J - (NB - 1);
+                issue_record<S, REC, NLD, NW, FOX>(rec_ptr(jn), tail_ptr(jn), srec[(it + NB - 1) % NB],
+                                                   stail[(it + NB - 1) % NB], wv, lane);
+            }
+            if (active && J < I && !wdone) {
+                if constexpr (BND) {
+                    step_mma<S, D, CT, 1, false, 0>(w, srec[buf], lane, h);
+                    step_softmax_pv<S, D, CT, 1, FOX, false, 0, true>(w, srec[buf], 0.f, lane);
+                } else {
+                    step_mma<S, D, CT, 1, kFold, 0>(w, srec[buf], lane, h);
+                    step_check<S, D, CT, 1, FOX, kFold, 0>(w, stail[buf], h);
+                    step_softmax_pv<S, D, CT, 1, FOX, kFold, 0>(w, srec[buf], FOX ? fb[J] : 0.f, lane);
+                }
+            }
+            if (skip) {  // bound for blocks J - 1 and earlier (off now sits at the J-1 / J boundary)
+                wdone = wdone || negligible();
+                if (lane == 0) sdone[wv] = wdone;
+            }
+            if (NB == 1 && J >= 1) {
+                __syncthreads();  // every wave is done with the buffer
+                issue_record<S, REC, NLD, NW, FOX>(rec_ptr(J - 1), tail_ptr(J - 1), srec[0], stail[0], wv, lane);
+            }
         }
-        if (NB > 1 && J - (NB - 1) >= 0) {
-            const int jn = J - (NB - 1);
-            issue_record<S, REC, NLD, NW, FOX>(rec_ptr(jn), tail_ptr(jn), srec[(it + NB - 1) % NB],
-                                               stail[(it + NB - 1) % NB], wv, lane);
-        }
-        if (active && J < I && !wdone) {
-            step_mma<S, D, CT, 1, kFold, 0>(w, srec[buf], lane, h);
-            step_check<S, D, CT, 1, FOX, kFold, 0>(w, stail[buf], h);
-            step_softmax_pv<S, D, CT, 1, FOX, kFold, 0>(w, srec[buf], FOX ? fb[J] : 0.f, lane);
-        }
-        if (skip) {  // bound for blocks J - 1 and earlier (off now sits at the J-1 / J boundary)
-            wdone = wdone || negligible();
-            if (lane == 0) sdone[wv] = wdone;
-        }
-        if (NB == 1 && J >= 1) {
-            __syncthreads();  // every wave is done with the buffer
-            issue_record<S, REC, NLD, NW, FOX>(rec_ptr(J - 1), tail_ptr(J - 1), srec[0], stail[0], wv, lane);
-        }
-    }
-
-    // no record copy may still be landing in LDS when the workgroup leaves early
-    if (skip) __builtin_amdgcn_s_waitcnt(0);
+    };
 
     // ---- epilogue
-    if (active) {
+    auto finish = [&]() {
+        if (!active) return;
         S *go = (S *)a.out + (bh * a.L + (int64_t)I * kBlk) * D;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
@@ -479,18 +523,69 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
                 }
             if (a.lse && h == 0) a.lse[bh * a.L + (int64_t)I * kBlk + i] = (w.m[ct] + __log2f(lsum)) * kLn2;
         }
+    };
+
+    if constexpr (MODE == kBounded) {
+        // ---- bounded walk.  Without the forget gate, each query first walks
+        // with the reference max fixed at 0: no folded max, no per-block max
+        // check, no rescale.  The result is exact to fp32 unless a probability
+        // overflowed or every relevant one underflowed, so it is kept when, for
+        // every valid query, the sum lies in [2^-60, 2^120] (each probability is
+        // at most the sum, so all are finite, also in bf16; terms lost below
+        // 2^-126 add at most L 2^-126 <= 2^-66 of the sum) and the output
+        // accumulators are finite.  Otherwise the wave leaves `out` as the prep
+        // kernel wrote it and flags itself, and a second launch repeats the walk
+        // with the running max for the flagged waves.  The bounded walk needs no
+        // more than the logits being within about +-100 (log2 units) of 0, which
+        // holds for any inputs of moderate norm.
+        init_state(std::true_type{});
+        walk(std::true_type{});
+        bool ok = true;
+        if (active) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const float lsum = other_half_sum(w.lp[ct]);
+                bool r = lsum >= 0x1p-60f && lsum <= 0x1p120f;  // false for NaN
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) r = r && __builtin_isfinite(w.o[dt][ct][e]);
+                const bool valid = (int64_t)I * kBlk + c0 + 32 * ct + l32 < a.L;
+                ok = ok && (r || !valid);
+            }
+        }
+        const bool keep = __all(ok);
+        if (lane == 0) wflag[wv] = keep ? 0 : 1;
+        if (keep) finish();
+        return;
     }
+    // ---- checked walk: the running max is tracked block by block (refreshed
+    // when it grows by more than 2^kTau)
+    init_state(std::false_type{});
+    if (skip) setup_skip();
+    walk(std::false_type{});
+
+    // no record copy may still be landing in LDS when the workgroup leaves early
+    if (skip) __builtin_amdgcn_s_waitcnt(0);
+    finish();
 }
 
 }  // namespace
 
+// Without the forget gate: the bounded walk, then the checked walk of the
+// workgroups it flagged (the others leave at once).
 template <typename S, int D, bool FOX>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t st) {
     typedef FwdCfg<S, D> F;
     const FwdLayout lay = fwd_layout(a.B, a.H, a.L, D, sizeof(S));
     const int64_t ntile = (lay.nb + F::QB - 1) / F::QB;
     dim3 grid((unsigned)(ntile * lay.bh));
-    hipLaunchKernelGGL((path_fwd_kernel<S, D, FOX>), grid, dim3(64 * F::NW), 0, st, a);
+    if constexpr (FOX) {
+        hipLaunchKernelGGL((path_fwd_kernel<S, D, true, kChecked>), grid, dim3(64 * F::NW), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((path_fwd_kernel<S, D, false, kBounded>), grid, dim3(64 * F::NW), 0, st, a);
+        hipLaunchKernelGGL((path_fwd_kernel<S, D, false, kRedo>), grid, dim3(64 * F::NW), 0, st, a);
+    }
     return hipGetLastError();
 }
 

@@ -11,7 +11,11 @@
 //   mdiag/ldiag: running max (log2 units) and sum of the diagonal block;
 //   fq/fk/fb   : forget-gate prefix terms (log2 units), used with logf only;
 //   kn         : per block, max_j ||k_j|| if every transition of the block is a
-//                contraction (0 <= beta ||w||^2 <= 2), else +inf (logf only).
+//                contraction (0 <= beta ||w||^2 <= 2), else +inf (logf only);
+//   redo       : per wave of the forward kernel (at most bh * (2 nb + 8) of
+//                them), 1 when the bounded walk of its queries must be
+//                repeated with the running max (written by the forward
+//                kernel, no logf only).
 #pragma once
 
 #include <stddef.h>
@@ -24,7 +28,7 @@ constexpr int kBlk = 64;
 struct FwdLayout {
     int64_t bh, nb, lp, d, es;
     int64_t rec_elems;  // elements per key-block record
-    size_t off_rec, off_qhat, off_mdiag, off_ldiag, off_fq, off_fk, off_fb, off_kn, total;
+    size_t off_rec, off_qhat, off_mdiag, off_ldiag, off_fq, off_fk, off_fb, off_kn, off_redo, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -54,6 +58,8 @@ __host__ __device__ inline FwdLayout fwd_layout(int64_t B, int64_t H, int64_t L,
     o = align256(o + (size_t)(f.bh * f.nb * 4));
     f.off_kn = o;
     o = align256(o + (size_t)(f.bh * f.nb * 4));
+    f.off_redo = o;
+    o = align256(o + (size_t)(f.bh * (2 * f.nb + 8) * 4));
     f.total = o;
     return f;
 }

@@ -3,6 +3,8 @@
 Tolerances (max-abs, fp32 accumulation in both paths): 1e-4 for fp32 inputs,
 2e-2 for bf16 inputs, on the output and on the log-sum-exp.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -125,6 +127,57 @@ def test_fwd_workload_sampled_rows(name):
     rows = [(int(rng.integers(2)), int(rng.integers(L))) for _ in range(256)]
     rows += [(g, L - 1 - t) for g in (0, 1) for t in range(64)]
     run_and_compare(c["B"], c["H"], L, c["d"], c["dtype"], c["fox"], seed=0, heads=heads, rows=rows)
+
+
+def offset_inputs(L, d, dtype, seed):
+    """Four heads; in heads 1-3 every logit carries a large common offset while
+    the softmax stays well conditioned: the last coordinate of each key is 8
+    and of each query is alpha, and every w is orthogonal to that axis, so the
+    transitions leave it alone and s_ij = scale (8 alpha + the usual term).
+    (The last coordinate is summed last by the matrix cores: the offset then
+    costs one rounding of the logit, where earlier it would cost one per added
+    term, about sqrt(d) 2^-24 |s| in fp32.)
+    With scale = ln(2) / 8 the logits in log2 units are s_ij / 8, and the offset
+    8 alpha / 8 = alpha is exact in bf16 after that scaling too (the bf16
+    pipeline keeps the scaled queries in bf16; an offset it had to round would
+    move the off-diagonal logits against the diagonal block's by 2^-9 of it).
+    Head 1: alpha = +150 (2^150 overflows fp32), head 2: alpha = -150 (every
+    probability underflows), head 3: alpha = +150 for the queries of the last
+    block only.  Head 0 is the plain workload."""
+    x = pathgen.fwd_inputs(1, 4, L, d, dtype, seed=seed, clip=1.98 if dtype == "bf16" else None, device="cuda")
+    q, k, w = x["q"].float(), x["k"].float(), x["w"].float()
+    for hh, alpha, first in ((1, 150.0, 0), (2, -150.0, 0), (3, 150.0, 64 * ((L - 1) // 64))):
+        w[0, hh, :, -1] = 0.0
+        w[0, hh] = w[0, hh] / w[0, hh].norm(dim=-1, keepdim=True)
+        k[0, hh, :, -1] = 8.0
+        q[0, hh, :, -1] = 0.0
+        q[0, hh, first:, -1] = alpha
+    dt = x["q"].dtype
+    x["q"], x["k"], x["w"] = q.to(dt).contiguous(), k.to(dt).contiguous(), w.to(dt).contiguous()
+    return x
+
+
+@gpu
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_large_common_offset(dtype, d):
+    """Logits far above or below 0 (overflow / underflow of a walk referenced to
+    0) and a head where only one query tile is affected: same bars as any input."""
+    L = 300
+    say("case large common logit offset %s d%d L%d" % (dtype, d, L))
+    x = offset_inputs(L, d, dtype, seed=77 + d)
+    scale = math.log(2.0) / 8
+    out, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], None, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    G = 4
+    ro, rl = oracle.fwd(*(x[n].cpu() for n in ("q", "k", "v", "w", "beta")), scale=scale)
+    eo = max_abs(to_np(out), ro)
+    el = max_abs(to_np(lse), rl)
+    say("  max-abs out %.3e  lse %.3e  (lse range %.1f .. %.1f)" % (eo, el, float(rl.min()), float(rl.max())))
+    assert np.isfinite(to_np(out)).all() and np.isfinite(to_np(lse)).all()
+    assert eo <= TOL[dtype], "output error %.3e" % eo
+    assert el <= TOL[dtype], "lse error %.3e" % el
+    assert G == out.shape[1]
 
 
 @gpu
