@@ -373,7 +373,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": FWD_WORKLOAD, "B": f["B"], "H": f["H"], "L": f["L"], "d": f["d"], "causal": True,
                    "decode_workload": DEC_WORKLOAD},
-        "roofline": {"bound": "mfma", "kernel": "path_fwd_kernel (scan)", "achieved": round(scan_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "path_fwd_kernel (scan stage: bounded walk + redo launch)", "achieved": round(scan_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(scan_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
         "forward": {"ms_per_step": round(f["ms_per_step"], 4), "prep_ms": round(f["prep_ms"], 4),
