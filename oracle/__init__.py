@@ -62,6 +62,9 @@ def _load(path=None):
                                            ctypes.c_double, dp]
         lib.oracle_decode_cache.restype = ctypes.c_int
         lib.oracle_decode_cache.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp]
+        lib.oracle_produce.restype = ctypes.c_int
+        lib.oracle_produce.argtypes = [dp, dp, dp, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, dp, dp]
         lib.oracle_transport.restype = None
         lib.oracle_transport.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp]
         _libs[path] = lib
@@ -197,3 +200,30 @@ def decode_cache(k, w, beta, lib=None, logf=None):
         raise ValueError("oracle_decode_cache: bad arguments")
     out = out.reshape(lead + (L, d))
     return (out, fc.reshape(lead + (L,))) if logf is not None else out
+
+
+def produce(wraw, conv_w, zbeta, beta_clip=0.0, lib=None):
+    """Producer of w and beta in fp64 (short causal convolution of width 3,
+    L2 normalisation, beta = 2 sigmoid(z), capped at beta_clip when > 0).
+
+    wraw: [B, H, L, d]; conv_w: [H, d, 3]; zbeta: [B, H, L].
+    Returns (w [B, H, L, d], beta [B, H, L]).
+    """
+    wraw, conv_w, zbeta = _f64(wraw), _f64(conv_w), _f64(zbeta)
+    B, H, L, d = wraw.shape
+    assert conv_w.shape == (H, d, 3) and zbeta.shape == (B, H, L)
+    G = B * H
+    w = np.zeros((G, L, d))
+    beta = np.zeros((G, L))
+    rc = _load(lib).oracle_produce(_ptr(wraw), _ptr(conv_w), _ptr(zbeta), float(beta_clip), G, H, L, d, _ptr(w),
+                                   _ptr(beta))
+    if rc != 0:
+        raise ValueError("oracle_produce: bad arguments")
+    return w.reshape(B, H, L, d), beta.reshape(B, H, L)
+
+
+def fwd_fused(q, k, v, wraw, conv_w, zbeta, beta_clip=0.0, logf=None, scale=None, rows=None, nthreads=None,
+              lib=None):
+    """PaTH forward with w and beta made by the producer (see produce), fp64."""
+    w, beta = produce(wraw, conv_w, zbeta, beta_clip, lib=lib)
+    return fwd(q, k, v, w, beta, logf, scale=scale, rows=rows, nthreads=nthreads, lib=lib)

@@ -46,6 +46,17 @@
  * been fed one decode step at a time, cache row j would have been updated by
  * steps j+1, ..., L-1 in that order, so it holds H_{L-1} ... H_{j+1} k_j
  * (H_{j+1} acts first; row L-1 is k_{L-1} itself).
+ *
+ * Producer of w and beta [IPX s.3; TS s.2; "PaTH Attention" Chinese summary,
+ * method paragraph]: w comes out of a low-dimensional linear projection, a
+ * short convolution of width 3 and an L2 normalisation; beta = 2 sigmoid(u^T
+ * x + b), so it lies in (0, 2).  The projections are ordinary matrix products
+ * outside this function, which takes their outputs: the pre-convolution rows
+ * x_t (wraw) and the pre-sigmoid values z_t.  Readings: the convolution is
+ * causal and per channel (depthwise), tap tau = 0, 1, 2 multiplying x_{t-2+tau}
+ * (zero before the first token), no bias, no activation; the normalisation is
+ * y / max(||y||, 1e-12); a positive beta_clip caps beta (the pages ask for
+ * clipping near 2 in bf16 without a value).
  */
 #include <math.h>
 #include <pthread.h>
@@ -322,6 +333,42 @@ int oracle_decode_cache(const double *k, const double *w, const double *beta, co
             double *u = og + (size_t)j * d;
             memcpy(u, kg + (size_t)j * d, sizeof(double) * (size_t)d);
             for (int s = j + 1; s < L; ++s) apply_h(u, wg + (size_t)s * d, bg[s], d);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Producer of w and beta (see the header): for every head g (conv weights of
+ * head g % H), token t and channel c
+ *   y_t[c] = sum_{tau=0..2} cw[(g % H)][c][tau] * x_{t-2+tau}[c]   (x_{<0} = 0)
+ *   w_t = y_t / max(||y_t||, 1e-12),  beta_t = 2 / (1 + exp(-z_t)), capped at
+ *   beta_clip when beta_clip > 0.
+ * wraw: [G, L, d], cw: [H, d, 3], z: [G, L]; out w: [G, L, d], beta: [G, L].
+ * Returns 0 or -1.
+ */
+int oracle_produce(const double *wraw, const double *cw, const double *z, double beta_clip, int G, int H, int L,
+                   int d, double *w, double *beta) {
+    if (G < 0 || H < 1 || L < 0 || d < 1 || G % H != 0) return -1;
+    for (int g = 0; g < G; ++g) {
+        const double *x = wraw + (size_t)g * L * d, *cwh = cw + (size_t)(g % H) * d * 3;
+        for (int t = 0; t < L; ++t) {
+            double *y = w + ((size_t)g * L + t) * d;
+            double nn = 0.0;
+            for (int c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int tau = 0; tau < 3; ++tau) {
+                    const int src = t - 2 + tau;
+                    if (src >= 0) acc += cwh[(size_t)c * 3 + tau] * x[(size_t)src * d + c];
+                }
+                y[c] = acc;
+                nn += acc * acc;
+            }
+            const double nrm = fmax(sqrt(nn), 1e-12);
+            for (int c = 0; c < d; ++c) y[c] /= nrm;
+            double b = 2.0 / (1.0 + exp(-z[(size_t)g * L + t]));
+            if (beta_clip > 0.0 && b > beta_clip) b = beta_clip;
+            beta[(size_t)g * L + t] = b;
         }
     }
     return 0;

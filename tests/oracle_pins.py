@@ -315,5 +315,42 @@ def pin_decode_cache(lib):
     _close(c1[-1], k[-1], 0.0, "last row untransformed")
 
 
+def pin_produce(lib):
+    """Producer of w and beta: the causal width-3 depthwise convolution and the L2
+    normalisation against torch's conv1d (fp64, padding 2, first L outputs: output t
+    is sum_tau cw[tau] x_{t-2+tau}) and F.normalize (eps 1e-12), per head with the
+    head's own weights; beta against 2 sigmoid(z) capped by torch.clamp; a token
+    whose window is all zero gives w = 0; the fused forward ignores the scale of
+    wraw and equals the forward on the produced (w, beta)."""
+    B, H, L, d = 2, 3, 9, 5
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((B, H, L, d))
+    x[1, 2, 3:6] = 0.0  # token 5 of that head sees only zeros
+    cw = rng.standard_normal((H, d, 3))
+    z = 2.0 * rng.standard_normal((B, H, L))
+    z[0, 0, :3] = 8.0  # 2 sigmoid(8) > 1.98: the cap applies
+    clip = 1.98
+    w, b = oracle.produce(x, cw, z, clip, lib=lib)
+    xt = torch.from_numpy(x)
+    for h in range(H):
+        inp = xt[:, h].transpose(1, 2)  # [B, d, L]
+        y = torch.nn.functional.conv1d(inp, torch.from_numpy(cw[h]).unsqueeze(1), padding=2, groups=d)[..., :L]
+        ref = torch.nn.functional.normalize(y.transpose(1, 2), dim=-1, eps=1e-12).numpy()
+        _close(w[:, h], ref, 1e-14, "w of head %d vs conv1d + normalize" % h)
+    _close(w[1, 2, 5], np.zeros(d), 0.0, "all-zero window gives w = 0")
+    bref = torch.clamp(2.0 * torch.sigmoid(torch.from_numpy(z)), max=clip).numpy()
+    _close(b, bref, 1e-15, "beta vs 2 sigmoid(z) capped")
+    assert float(b.max()) == clip, "cap reached"
+    _, b_free = oracle.produce(x, cw, z, 0.0, lib=lib)
+    assert float(b_free.max()) > clip, "no cap without beta_clip"
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    o1, l1 = oracle.fwd_fused(q, k, v, x, cw, z, clip, lib=lib)
+    o2, l2 = oracle.fwd_fused(q, k, v, 3.5 * x, cw, z, clip, lib=lib)
+    _close(o1, o2, 1e-12, "fused forward independent of the scale of wraw")
+    o3, l3 = oracle.fwd(q, k, v, w, b, lib=lib)
+    _close(o1, o3, 0.0, "fused forward = forward on the produced (w, beta)")
+
+
 ALL_PINS = [pin_golden, pin_bruteforce, pin_ut_closed_form, pin_beta_zero, pin_beta_two, pin_beta_one,
-            pin_equal_w, pin_small_L, pin_fox_zero, pin_rows_subset, pin_decode, pin_decode_fox, pin_decode_cache]
+            pin_equal_w, pin_small_L, pin_fox_zero, pin_rows_subset, pin_decode, pin_decode_fox, pin_decode_cache,
+            pin_produce]

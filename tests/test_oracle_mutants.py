@@ -45,6 +45,13 @@ MUTANTS = [
      "for (int s = L - 1; s > j; --s) apply_h(u, wg + (size_t)s * d, bg[s], d);", 1),
     ("cache_includes_own_H", "for (int s = j + 1; s < L; ++s) apply_h(u, wg", "for (int s = j; s < L; ++s) apply_h(u, wg", 1),
     ("cache_drops_last_H", "for (int s = j + 1; s < L; ++s) apply_h(u, wg", "for (int s = j + 1; s < L - 1; ++s) apply_h(u, wg", 1),
+    ("produce_taps_reversed", "acc += cwh[(size_t)c * 3 + tau] * x", "acc += cwh[(size_t)c * 3 + (2 - tau)] * x", 1),
+    ("produce_centred_window", "const int src = t - 2 + tau;\n                    if (src >= 0)",
+     "const int src = t - 1 + tau;\n                    if (src >= 0 && src < L)", 1),
+    ("produce_no_normalise", "for (int c = 0; c < d; ++c) y[c] /= nrm;", "", 1),
+    ("produce_beta_no_two", "double b = 2.0 / (1.0 + exp(-z", "double b = 1.0 / (1.0 + exp(-z", 1),
+    ("produce_clip_ignored", "if (beta_clip > 0.0 && b > beta_clip) b = beta_clip;", "", 1),
+    ("produce_head_index", "cwh = cw + (size_t)(g % H) * d * 3;", "cwh = cw + (size_t)(g / (G / H)) * d * 3;", 1),
 ]
 
 
