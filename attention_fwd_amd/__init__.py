@@ -12,7 +12,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_prep", "fwd_scan", "decode_step", "decode_cache_from_fwd", "fwd_workspace_size",
+__all__ = ["fwd", "fwd_fused", "fwd_prep", "fwd_scan", "decode_step", "decode_cache_from_fwd", "fwd_workspace_size",
            "decode_workspace_size", "lib", "PathError", "PATH_OK", "PATH_EINVAL", "PATH_EUNSUPPORTED", "PATH_EHIP", "PATH_DTYPE_F32", "PATH_DTYPE_BF16",
            "PATH_FWD_SKIP_NEGLIGIBLE"]
 
@@ -52,6 +52,9 @@ def lib():
                                     vp, sz, vp]
         L.path_attn_fwd_ex.restype = ctypes.c_int
         L.path_attn_fwd_ex.argtypes = list(L.path_attn_fwd.argtypes[:-1]) + [ctypes.c_uint, vp]
+        L.path_attn_fwd_fused.restype = ctypes.c_int
+        L.path_attn_fwd_fused.argtypes = [vp, vp, vp, vp, fp, fp, ctypes.c_float, fp, vp, fp, i, i, i, i, ctypes.c_int,
+                                          ctypes.c_float, vp, sz, vp]
         L.path_attn_fwd_prep.restype = ctypes.c_int
         L.path_attn_fwd_prep.argtypes = list(L.path_attn_fwd.argtypes)
         L.path_attn_fwd_scan.restype = ctypes.c_int
@@ -144,6 +147,50 @@ def fwd(q, k, v, w, beta, logf=None, scale=None, out=None, lse=None, return_lse=
                                     PATH_FWD_SKIP_NEGLIGIBLE if skip_negligible else 0, _stream(stream))
     if st != PATH_OK:
         raise PathError(st, "path_attn_fwd_ex")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def fwd_fused(q, k, v, wraw, conv_w, zbeta, beta_clip=0.0, logf=None, scale=None, out=None, lse=None,
+              return_lse=False, workspace=None, stream=None):
+    """PaTH forward with the producer of w and beta fused in (path_attn_fwd_fused).
+
+    wraw: [B, H, L, d] (dtype of q) pre-convolution rows; conv_w: [H, d, 3] fp32
+    causal width-3 depthwise weights; zbeta: [B, H, L] fp32 pre-sigmoid values;
+    beta_clip: cap on beta = 2 sigmoid(z) (0: none).  Otherwise as fwd.
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d]")
+    B, H, L, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError("dtype must be bfloat16 or float32")
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (wraw, "wraw")):
+        _check(t, n, dt, (B, H, L, d), dev)
+    _check(conv_w, "conv_w", torch.float32, (H, d, 3), dev)
+    _check(zbeta, "zbeta", torch.float32, (B, H, L), dev)
+    if logf is not None:
+        _check(logf, "logf", torch.float32, (B, H, L), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", dt, (B, H, L, d), dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, L), device=dev, dtype=torch.float32)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H, L), dev)
+    need = fwd_workspace_size(B, H, L, d, dt)
+    if need == 0:
+        raise PathError(PATH_EUNSUPPORTED if d not in (64, 128) else PATH_EINVAL, "path_attn_fwd_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    _check(workspace, "workspace", None, None, dev)
+    with torch.cuda.device(dev):
+        st = lib().path_attn_fwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(wraw), _ptr(conv_w), _ptr(zbeta),
+                                       float(beta_clip), _ptr(logf), _ptr(out), _ptr(lse), B, H, L, d, _DTYPES[dt],
+                                       float(scale or 0.0), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != PATH_OK:
+        raise PathError(st, "path_attn_fwd_fused")
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -126,8 +126,10 @@ path_status_t scan_check(void *out, float *lse, int B, int H, int L, int d, path
 
 path_status_t launch_prep_stage(const void *q, const void *k, const void *v, const void *w, const float *beta,
                                 const float *logf, void *out, float *lse, int B, int H, int L, int d,
-                                path_dtype_t dtype, float scale, void *workspace, hipStream_t s) {
-    path::PrepArgs pa{q, k, v, w, beta, logf, out, lse, workspace, B, H, L, d, scale};
+                                path_dtype_t dtype, float scale, void *workspace, hipStream_t s,
+                                const float *conv_w = nullptr, const float *zbeta = nullptr,
+                                float beta_clip = 0.f) {
+    path::PrepArgs pa{q, k, v, w, beta, logf, out, lse, workspace, B, H, L, d, scale, conv_w, zbeta, beta_clip};
     return path::launch_prep(pa, dtype == PATH_DTYPE_BF16, s) == hipSuccess ? PATH_OK : PATH_EHIP;
 }
 
@@ -155,6 +157,28 @@ path_status_t path_attn_fwd_ex(const void *q, const void *k, const void *v, cons
     if (st != PATH_OK) return st;
     return launch_scan_stage(out, lse, logf != nullptr, B, H, L, d, dtype, scale, workspace, s,
                              (flags & PATH_FWD_SKIP_NEGLIGIBLE) != 0);
+}
+
+path_status_t path_attn_fwd_fused(const void *q, const void *k, const void *v, const void *wraw,
+                                  const float *conv_w, const float *zbeta, float beta_clip, const float *logf,
+                                  void *out, float *lse, int B, int H, int L, int d, path_dtype_t dtype, float scale,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    path_status_t st = fwd_check(q, k, v, wraw, zbeta, logf, out, lse, B, H, L, d, dtype, scale, workspace,
+                                 workspace_bytes);
+    if (st != PATH_OK) return st;
+    if (!conv_w || !aligned(conv_w, 16) || !std::isfinite(beta_clip) || beta_clip < 0.f) return PATH_EINVAL;
+    const int64_t cwb = (int64_t)H * d * 3 * 4, tens = (int64_t)B * H * L * d * elem_size(dtype);
+    const int64_t tok = (int64_t)B * H * L * 4;
+    const size_t need = path::fwd_layout(B, H, L, d, elem_size(dtype)).total;
+    if (overlap(out, tens, conv_w, cwb) || overlap(workspace, (int64_t)need, conv_w, cwb) ||
+        overlap(lse, tok, conv_w, cwb))
+        return PATH_EINVAL;
+    scale = eff_scale(scale, d);
+    hipStream_t s = (hipStream_t)stream;
+    st = launch_prep_stage(q, k, v, wraw, nullptr, logf, out, lse, B, H, L, d, dtype, scale, workspace, s, conv_w,
+                           zbeta, beta_clip);
+    if (st != PATH_OK) return st;
+    return launch_scan_stage(out, lse, logf != nullptr, B, H, L, d, dtype, scale, workspace, s);
 }
 
 path_status_t path_attn_fwd(const void *q, const void *k, const void *v, const void *w, const float *beta,

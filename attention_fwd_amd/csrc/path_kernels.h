@@ -14,6 +14,12 @@ struct PrepArgs {
     void *ws;
     int B, H, L, d;
     float scale;
+    // Producer of w and beta fused into the prep (when conv_w is set): w then
+    // points at the pre-convolution rows [B, H, L, d], conv_w at the causal
+    // width-3 depthwise weights [H, d, 3] and zbeta at the pre-sigmoid values
+    // [B, H, L] (beta is unused); beta = 2 sigmoid(z), capped at beta_clip > 0.
+    const float *conv_w, *zbeta;
+    float beta_clip;
 };
 
 struct FwdArgs {

@@ -55,7 +55,8 @@ struct PrepCfg {
     static constexpr bool kWtLate = kBf;
     static constexpr int WSLOT = kWtLate ? cmax(MATD, MATT) : MATD;
     static constexpr int FIX = WSLOT + 2 * MAT;  // elements
-    static constexpr int RB = cmax(cmax(2 * MATD * (int)sizeof(S), 2 * 10 * TS * 4), (MAT + MATT) * (int)sizeof(S));
+    // (+ 1 KiB after Q, K in phases 1-2: per-thread partial norms of the fused producer)
+    static constexpr int RB = cmax(cmax(2 * MATD * (int)sizeof(S) + 1024, 2 * 10 * TS * 4), (MAT + MATT) * (int)sizeof(S));
     static constexpr int WG_PER_CU = kBf ? (D == 64 ? 3 : 2) : 1;  // = waves per SIMD (4-wave workgroups)
 };
 
@@ -261,6 +262,7 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
     S *sW = fixed, *sX = fixed + C::WSLOT, *sY = fixed + C::WSLOT + MAT;
     S *sWt = kBf ? fixed : nullptr;
     S *sQ = (S *)region, *sK = (S *)region + C::MATD;               // phases 1-2
+    float *sPart = (float *)((char *)region + 2 * C::MATD * sizeof(S));  // phases 1-2, fused producer: [4][64]
     float *sG = (float *)region, *sE = (float *)region + 10 * C::TS;  // phase 3
     S *sA = kBf ? nullptr : (S *)region, *sAup = kBf ? (S *)region : nullptr;  // phase 4
     S *sVt = (S *)region + MAT;
@@ -274,36 +276,106 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
     const int nvalid = min(kBlk, L - (int)row0);
     const int64_t tok0 = bh * L + row0;  // first token of the block in [B*H, L]
 
-    // ---- 1. stage W, Q, K in LDS and V in registers (zero rows past L), beta, forget-gate prefix
+    // ---- 1. stage W, Q, K in LDS and V in registers (zero rows past L), beta, forget-gate prefix.
+    // With the fused producer the staged W rows are the convolution outputs y_t (rounded to the
+    // element type) and sBeta holds 2 sigmoid(z_t) (capped); it becomes beta_t / ||y_t||^2 below,
+    // since I - beta w w^T with w = y / ||y|| equals I - (beta / ||y||^2) y y^T.
+    const bool fused = a.conv_w != nullptr;
     u32x4 vreg[VPT];
     u32x4 wreg[VPT];
+    float ynorm = 0.f;  // fused producer: this thread's part of ||y_row||^2 (row = lane)
     {
         const S *gq = (const S *)a.q + tok0 * D, *gk = (const S *)a.k + tok0 * D;
         const S *gw = (const S *)a.w + tok0 * D, *gv = (const S *)a.v + tok0 * D;
+        // Every global load of this phase is issued first, without branches (rows past L
+        // read row nvalid - 1 and are zeroed when consumed), so they are all in flight at once.
+        // Q, K: consecutive lanes take consecutive chunks of a row (coalesced).  W, V:
+        // consecutive lanes take consecutive rows (row = lane), so that the transposed LDS
+        // copies (W^T, V^T) are written without bank conflicts.
+        const u32x4 z4 = {0, 0, 0, 0};
+        u32x4 lq[VPT], lk[VPT], lw[VPT], lv[VPT];
+        u32x4 p1[VPT], p2[VPT];     // fused producer: rows t-1, t-2 from the previous block (lanes 0, 1)
+        f32x4 cw4[VPT][3 * CH / 4];  // fused producer: this chunk's convolution weights
 #pragma unroll
         for (int s = 0; s < VPT; ++s) {
             const int idx = tid + 256 * s;
-            // Q, K: consecutive lanes take consecutive chunks of a row (coalesced)
-            const int r = idx / RCH, cc = idx % RCH;
-            u32x4 vq = {0, 0, 0, 0}, vk = vq, vw = vq, vv = vq;
-            if (r < nvalid) {
-                vq = *(const u32x4 *)(gq + r * D + cc * CH);
-                vk = *(const u32x4 *)(gk + r * D + cc * CH);
+            const int r = min(idx / RCH, nvalid - 1), cc = idx % RCH;
+            lq[s] = *(const u32x4 *)(gq + r * D + cc * CH);
+            lk[s] = *(const u32x4 *)(gk + r * D + cc * CH);
+            const int rw = min(lane, nvalid - 1), cw = idx / 64;
+            lw[s] = *(const u32x4 *)(gw + rw * D + cw * CH);
+            lv[s] = *(const u32x4 *)(gv + rw * D + cw * CH);
+            if (fused) {
+                // previous-block rows exist for row0 >= 1 (t - 1) and row0 + lane >= 2 (t - 2)
+                const int64_t o1 = (lane == 0 && row0 >= 1) ? -D : 0;
+                const int64_t o2 = (lane < 2 && row0 + lane >= 2) ? (int64_t)(lane - 2) * D : 0;
+                p1[s] = *(const u32x4 *)(gw + o1 + cw * CH);
+                p2[s] = *(const u32x4 *)(gw + o2 + cw * CH);
+                // the chunk (cw = wave + 4 s) is the same for the whole wave: one scalar read of its taps
+                const int cwu = __builtin_amdgcn_readfirstlane(cw);
+                const f32x4 *cwp = (const f32x4 *)(a.conv_w + ((int64_t)((int)bh % a.H) * D + cwu * CH) * 3);
+#pragma unroll
+                for (int u = 0; u < 3 * CH / 4; ++u) cw4[s][u] = cwp[u];
             }
-            *(u32x4 *)(sQ + r * SPD + cc * CH) = vq;
-            *(u32x4 *)(sK + r * SPD + cc * CH) = vk;
-            // W, V: consecutive lanes take consecutive rows, so that the transposed
-            // LDS copies (W^T, V^T) are written without bank conflicts
-            const int rw = idx % 64, cw = idx / 64;
-            if (rw < nvalid) {
-                vw = *(const u32x4 *)(gw + rw * D + cw * CH);
-                vv = *(const u32x4 *)(gv + rw * D + cw * CH);
+        }
+#pragma unroll
+        for (int s = 0; s < VPT; ++s) {
+            const int idx = tid + 256 * s;
+            const int r = idx / RCH, cc = idx % RCH;
+            const bool qok = r < nvalid, wok = lane < nvalid;
+            *(u32x4 *)(sQ + r * SPD + cc * CH) = qok ? lq[s] : z4;
+            *(u32x4 *)(sK + r * SPD + cc * CH) = qok ? lk[s] : z4;
+            const int rw = lane, cw = idx / 64;
+            u32x4 vw = wok ? lw[s] : z4;
+            const u32x4 vv = wok ? lv[s] : z4;
+            if (fused) {
+                // y_t[c] = sum_tau cw[c][tau] x_{t-2+tau}[c] (causal, zero before token 0); rows
+                // t-1 and t-2 of this block are the neighbouring lanes' x
+                u32x4 x1, x2;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x1[e] = (uint32_t)__shfl_up((int)vw[e], 1);
+                    x2[e] = (uint32_t)__shfl_up((int)vw[e], 2);
+                }
+                if (rw == 0) x1 = row0 >= 1 ? p1[s] : z4;
+                if (rw < 2) x2 = row0 + rw >= 2 ? p2[s] : z4;
+                const float *tap = (const float *)cw4[s];
+                const S *e0 = (const S *)&vw, *e1 = (const S *)&x1, *e2 = (const S *)&x2;
+                float y[CH];
+#pragma unroll
+                for (int e = 0; e < CH; ++e)
+                    y[e] = tap[3 * e] * Elem<S>::to_f32(e2[e]) + tap[3 * e + 1] * Elem<S>::to_f32(e1[e]) +
+                           tap[3 * e + 2] * Elem<S>::to_f32(e0[e]);
+                if constexpr (sizeof(S) == 2) {
+                    vw = u32x4{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
+                               pack_bf16(y[6], y[7])};
+                } else {
+                    vw = __builtin_bit_cast(u32x4, f32x4{y[0], y[1], y[2], y[3]});
+                }
+                if (!wok) vw = z4;
+                const S *ey = (const S *)&vw;  // the norm of the rounded row, as the products see it
+#pragma unroll
+                for (int e = 0; e < CH; ++e) {
+                    const float t2 = Elem<S>::to_f32(ey[e]);
+                    ynorm += t2 * t2;
+                }
             }
             vreg[s] = vv;
             *(u32x4 *)(sW + rw * SPD + cw * CH) = vw;
             wreg[s] = vw;
         }
-        if (tid < 64) sBeta[tid] = tid < nvalid ? a.beta[tok0 + tid] : 0.f;
+        if (tid < 64) {
+            float bt = 0.f;
+            if (tid < nvalid) {
+                if (fused) {
+                    bt = 2.f / (1.f + expf(-a.zbeta[tok0 + tid]));
+                    if (a.beta_clip > 0.f) bt = fminf(bt, a.beta_clip);
+                } else {
+                    bt = a.beta[tok0 + tid];
+                }
+            }
+            sBeta[tid] = bt;
+        }
         if (FOX && wv == 0) {
             // inclusive prefix of log f inside the block (zero past L)
             float v = lane < nvalid ? a.logf[tok0 + lane] : 0.f;
@@ -321,29 +393,49 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
             if (lane == 0) fb[bh * lay.nb + J] = total * kLog2e;
         }
     }
+    if (fused) sPart[wv * 64 + lane] = ynorm;
     __syncthreads();
-    if (FOX && wv == 1) {
-        // bound for skipping negligible key blocks in the scan: row s = lane;
-        // the block's transitions are contractions when 0 <= beta_s ||w_s||^2 <= 2
+    if ((FOX || fused) && wv == 3) {
+        // row s = lane.  Fused producer: beta_s <- beta_s / max(||y_s||^2, 1e-24) (the
+        // normalisation y / max(||y||, 1e-12)).  Forget gate: bound for skipping negligible
+        // key blocks in the scan; the block's transitions are contractions when
+        // 0 <= beta_s ||w_s||^2 <= 2.
         float kk = 0.f, ww = 0.f;
+        if (fused) ww = (sPart[lane] + sPart[64 + lane]) + (sPart[128 + lane] + sPart[192 + lane]);
 #pragma unroll
         for (int c0 = 0; c0 < D; c0 += CH) {
-            const u32x4 uk = *(const u32x4 *)(sK + lane * SPD + c0);
-            const u32x4 uw = *(const u32x4 *)(sW + lane * SPD + c0);
-            const S *ek = (const S *)&uk, *ew = (const S *)&uw;
+            if (!fused) {
+                const u32x4 uw = *(const u32x4 *)(sW + lane * SPD + c0);
+                const S *ew = (const S *)&uw;
 #pragma unroll
-            for (int e = 0; e < CH; ++e) {
-                const float xk = Elem<S>::to_f32(ek[e]), xw = Elem<S>::to_f32(ew[e]);
-                kk += xk * xk;
-                ww += xw * xw;
+                for (int e = 0; e < CH; ++e) {
+                    const float xw = Elem<S>::to_f32(ew[e]);
+                    ww += xw * xw;
+                }
+            }
+            if (FOX) {
+                const u32x4 uk = *(const u32x4 *)(sK + lane * SPD + c0);
+                const S *ek = (const S *)&uk;
+#pragma unroll
+                for (int e = 0; e < CH; ++e) {
+                    const float xk = Elem<S>::to_f32(ek[e]);
+                    kk += xk * xk;
+                }
             }
         }
-        const float bw = sBeta[lane] * ww;
-        const bool contr = bw >= 0.f && bw <= 2.f;
-        float kn = contr ? sqrtf(kk) * (1.f + 0x1p-10f) : INFINITY;  // rounded up
+        float bt = sBeta[lane];
+        if (fused) {
+            bt = bt / fmaxf(ww, 1e-24f);
+            sBeta[lane] = bt;  // read again only after the next barrier
+        }
+        if (FOX) {
+            const float bw = bt * ww;
+            const bool contr = bw >= 0.f && bw <= 2.f;
+            float kn = contr ? sqrtf(kk) * (1.f + 0x1p-10f) : INFINITY;  // rounded up
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) kn = fmaxf(kn, __shfl_xor(kn, o));
-        if (lane == 0) ((float *)((char *)a.ws + lay.off_kn))[bh * lay.nb + J] = kn;
+            for (int o = 1; o < 64; o <<= 1) kn = fmaxf(kn, __shfl_xor(kn, o));
+            if (lane == 0) ((float *)((char *)a.ws + lay.off_kn))[bh * lay.nb + J] = kn;
+        }
     }
 
     const int mt = (wv >> 1) * 32, nt = (wv & 1) * 32;  // this wave's tile of a 64x64 product

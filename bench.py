@@ -171,6 +171,49 @@ def bench_fox_skip(steps, warmup, name="fox_L16384_bf16"):
             "tokens_per_s": round(B * L / (res[True] * 1e-3)), "speedup_vs_full_walk": round(res[False] / res[True], 2)}
 
 
+def bench_fused(steps, warmup, name=FWD_WORKLOAD):
+    """The headline forward shape with the producer of w and beta fused in
+    (path_attn_fwd_fused: width-3 causal convolution + L2 normalisation of w,
+    beta = 2 sigmoid(z) capped at 1.98), timed as a whole call next to the plain
+    forward on ready-made (w, beta) of the same shape."""
+    import torch
+
+    import attention_fwd_amd as pa
+    import pathgen
+
+    c = pathgen.WORKLOADS[name]
+    B, H, L, d = c["B"], c["H"], c["L"], c["d"]
+    x = pathgen.fused_inputs(B, H, L, d, c["dtype"], seed=0, device="cuda")
+    y = pathgen.fwd_inputs(B, H, L, d, c["dtype"], seed=0, clip=c["clip"], device="cuda")
+    out = torch.empty_like(x["q"])
+    ws = torch.empty(pa.fwd_workspace_size(B, H, L, d, x["q"].dtype), device="cuda", dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    calls = {
+        "fused": lambda: pa.fwd_fused(x["q"], x["k"], x["v"], x["wraw"], x["conv_w"], x["zbeta"], c["clip"],
+                                      out=out, workspace=ws),
+        "plain": lambda: pa.fwd(y["q"], y["k"], y["v"], y["w"], y["beta"], out=out, workspace=ws),
+    }
+    res = {}
+    for key, call in calls.items():
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[key] = e0.elapsed_time(e1) / steps
+    del x, y, out, ws
+    torch.cuda.empty_cache()
+    flops = 4.0 * B * H * L * L * d
+    return {"workload": name + "+producer", "ms_per_step": round(res["fused"], 4),
+            "TFLOP_per_s": round(flops / (res["fused"] * 1e-3) / 1e12, 1),
+            "plain_forward_ms_per_step": round(res["plain"], 4),
+            "tokens_per_s": round(B * L / (res["fused"] * 1e-3))}
+
+
 def bench_decode(steps):
     import torch
 
@@ -342,10 +385,13 @@ def main():
     log("decode: %s, %d steps" % (DEC_WORKLOAD, args.decode_steps))
     dres = bench_decode(args.decode_steps)
     log("decode: %.3f ms/step" % dres["step_ms"])
-    sweep = fox_skip = None
+    sweep = fox_skip = fused = None
     if args.sweep_steps > 0:
         sweep = bench_sweep(args.sweep_steps, 2)
         fox_skip = bench_fox_skip(args.sweep_steps, 2)
+        fused = bench_fused(args.sweep_steps, 2)
+        log("fused producer, %s: %.3f ms/step (plain forward %.3f ms)" %
+            (fused["workload"], fused["ms_per_step"], fused["plain_forward_ms_per_step"]))
         log("fox workload, skipping negligible blocks: %.3f ms/step (full walk %.3f ms)" %
             (fox_skip["ms_per_step"], fox_skip["full_walk_ms_per_step"]))
     cpu = None
@@ -389,6 +435,7 @@ def main():
         "decode_cache_from_fwd": cache,
         "other_workloads": sweep,
         "fox_skip_negligible": fox_skip,
+        "fused_producer": fused,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PATH_ABI_VERSION 2
+#define PATH_ABI_VERSION 3
 
 typedef enum {
     PATH_OK = 0,
@@ -118,6 +118,38 @@ path_status_t path_attn_fwd_ex(const void *q, const void *k, const void *v, cons
                                const float *logf, void *out, float *lse, int B, int H, int L, int d,
                                path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
                                unsigned flags, void *stream);
+
+/*
+ * PaTH forward with the producer of w and beta fused into it.
+ *
+ * Source: "거리에서 경로로, PaTH Attention" (iplexlaw.co.kr), section 3, and the
+ * Chinese summary's method paragraph: w comes from a low-dimensional linear
+ * projection, a short convolution of width 3 and an L2 normalisation, and
+ * beta = 2 sigmoid(.) ("技術要約: PaTH Attention", section 2: beta_s =
+ * 2 sigmoid(u^T x_s + b)).  The projections are plain matrix products done by
+ * the caller; this call takes their outputs and does the rest inside the
+ * prep kernel, so w and beta never go through device memory:
+ *   y_t[c]  = sum_{tau=0..2} conv_w[h][c][tau] * wraw[b][h][t-2+tau][c]
+ *             (causal, per channel, zero before the first token)
+ *   w_t     = y_t / max(||y_t||, 1e-12)
+ *   beta_t  = 2 sigmoid(zbeta[b][h][t]), capped at beta_clip when beta_clip > 0
+ * and then exactly path_attn_fwd on (q, k, v, w, beta, logf).  (The kernel
+ * keeps y_t, rounded to the element type, and uses beta_t / max(||y_t||^2,
+ * 1e-24) instead, which gives the same transition matrices.)
+ *
+ *   wraw    [B, H, L, d] element type, 16-byte aligned (the role of w above)
+ *   conv_w  [H, d, 3] fp32, 16-byte aligned
+ *   zbeta   [B, H, L] fp32 (the role of beta above)
+ *   beta_clip  0 for no cap, else a cap in (0, 2]; negative or non-finite
+ *              values are rejected
+ * Every other argument, the workspace and the errors are those of
+ * path_attn_fwd (wraw and zbeta are checked like w and beta; conv_w must not
+ * overlap out, lse or the workspace).  Device pointers, owned by the caller.
+ */
+path_status_t path_attn_fwd_fused(const void *q, const void *k, const void *v, const void *wraw,
+                                  const float *conv_w, const float *zbeta, float beta_clip, const float *logf,
+                                  void *out, float *lse, int B, int H, int L, int d, path_dtype_t dtype, float scale,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The two stages of path_attn_fwd, for callers that schedule or time them

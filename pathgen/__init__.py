@@ -70,6 +70,29 @@ def fwd_inputs(B, H, L, d, dtype="bf16", seed=0, fox=False, clip=None, device="c
     return out
 
 
+def fused_inputs(B, H, L, d, dtype="bf16", seed=0, fox=False, device="cpu", fox_mean=3.0):
+    """Inputs of a forward pass with the producer of w and beta fused in: dict(q, k, v,
+    wraw [B,H,L,d] dtype (all N(0, 1)); zbeta [B,H,L] fp32 N(0, 1) (so beta = 2 sigmoid(z)
+    has the workloads' distribution); logf as in fwd_inputs; conv_w [H,d,3] fp32
+    N(0, 1/3), a random initialisation of a width-3 depthwise convolution)."""
+    tdt = TORCH_DTYPES[dtype]
+    g = _gen(device, seed)
+    shape = (B, H, L, d)
+    f32 = torch.float32
+    q = torch.randn(shape, generator=g, device=device, dtype=f32)
+    k = torch.randn(shape, generator=g, device=device, dtype=f32)
+    v = torch.randn(shape, generator=g, device=device, dtype=f32)
+    wraw = torch.randn(shape, generator=g, device=device, dtype=f32)
+    zbeta = torch.randn((B, H, L), generator=g, device=device, dtype=f32)
+    logf = None
+    if fox:
+        logf = torch.nn.functional.logsigmoid(
+            float(fox_mean) + torch.randn((B, H, L), generator=g, device=device, dtype=f32))
+    conv_w = torch.randn((H, d, 3), generator=g, device=device, dtype=f32) / 3.0 ** 0.5
+    return dict(q=q.to(tdt), k=k.to(tdt), v=v.to(tdt), wraw=wraw.to(tdt), zbeta=zbeta, logf=logf,
+                conv_w=conv_w.contiguous())
+
+
 def decode_inputs(B, H, n, d, steps, dtype="bf16", seed=0, clip=None, device="cpu", rowcap=None):
     """Inputs of a decode run: cache K, V [B,H,rowcap,d] (rows >= n are zero),
     and per step q, w [steps,B,H,d] dtype, beta [steps,B,H] fp32."""

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = pa.lib()
-    assert lib.path_abi_version() == 2
+    assert lib.path_abi_version() == 3
     for s in range(4):
         assert lib.path_status_string(s)
     assert lib.path_status_string(99) == b"unknown status"
@@ -154,6 +154,34 @@ def cache_call(**over):
 ])
 def test_cache_from_fwd_rejects_bad_arguments(over, status):
     assert cache_call(**over) == status
+
+
+def fused_call(**over):
+    args = dict(q=P(0), k=P(1), v=P(2), wraw=P(3), cw=P(7), zb=P(4), clip=1.98, logf=None, out=P(5), lse=None, B=1,
+                H=1, L=64, d=64, dtype=BF, scale=0.0, ws=P(6), wsb=1 << 40, stream=None)
+    args.update(over)
+    a = args
+    return pa.lib().path_attn_fwd_fused(a["q"], a["k"], a["v"], a["wraw"], a["cw"], a["zb"], a["clip"], a["logf"],
+                                        a["out"], a["lse"], a["B"], a["H"], a["L"], a["d"], a["dtype"], a["scale"],
+                                        a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cw=None), pa.PATH_EINVAL),                           # no convolution weights
+    (dict(cw=ctypes.c_void_p(A * 8 + 4)), pa.PATH_EINVAL),     # misaligned weights
+    (dict(zb=None), pa.PATH_EINVAL),                           # no pre-sigmoid values
+    (dict(wraw=None), pa.PATH_EINVAL),                         # no pre-convolution rows
+    (dict(clip=-1.0), pa.PATH_EINVAL),                         # negative cap
+    (dict(clip=float("nan")), pa.PATH_EINVAL),                 # non-finite cap
+    (dict(clip=float("inf")), pa.PATH_EINVAL),
+    (dict(cw=P(5)), pa.PATH_EINVAL),                           # weights overlap out
+    (dict(cw=P(6)), pa.PATH_EINVAL),                           # weights inside the workspace
+    (dict(out=P(3)), pa.PATH_EINVAL),                          # out aliases wraw
+    (dict(d=96), pa.PATH_EUNSUPPORTED),
+    (dict(wsb=16), pa.PATH_EINVAL),                            # workspace too small
+])
+def test_fwd_fused_rejects_bad_arguments(over, status):
+    assert fused_call(**over) == status
 
 
 def test_fwd_ex_rejects_unknown_flags():
