@@ -145,7 +145,7 @@ constexpr float kSkipLog2 = 64.f;  // skipped key blocks contribute below 2^-64 
 
 // Matrix-core part of step J into logit buffer SB: bf16 copy of qt as the B
 // operand, S^T = khat qt^T for all 64 keys, and qt <- P_J qt.
-template <typename S, int D, int CT, int NS, bool FOLD, int SB>
+template <typename S, int D, int CT, int NS, bool FOLD, int SB, bool XF = true>
 __device__ __forceinline__ void step_mma(WaveState<D, CT, NS> &w, const S *rec, int lane, int h) {
     typedef Elem<S> E;
     typedef typename E::Frag Frag;
@@ -174,7 +174,8 @@ __device__ __forceinline__ void step_mma(WaveState<D, CT, NS> &w, const S *rec, 
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) E::mma(w.s[SB][hf][ct], af, qb[ct][kc]);
         }
-    // qt <- P_J qt (after block 0 the result is not used)
+    // qt <- P_J qt (XF false: block 0, whose transform no later block uses)
+    if constexpr (XF)
 #pragma unroll
     for (int kc = 0; kc < KCH; ++kc)
 #pragma unroll
@@ -450,7 +451,9 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
         for (int k = 0; k < (NB > 1 ? NB - 1 : 1); ++k)
             if (Jtop - k >= 0)
                 issue_record<S, REC, NLD, NW, FOX>(rec_ptr(Jtop - k), tail_ptr(Jtop - k), srec[k], stail[k], wv, lane);
-        for (int J = Jtop; J >= 0; --J) {
+        // one step; false when the walk stops early (skipping)
+        auto body = [&](int J, auto xform) -> bool {
+            constexpr bool XF = decltype(xform)::value;
             // unsigned: the read buffer it % NB and the refilled one (it + NB - 1) % NB
             // are then provably different, so the compiler does not make the
             // reads of this record wait for the copies of the next one
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
                 bool all = true;
 #pragma unroll
                 for (int v2 = 0; v2 < NW; ++v2) all = all && sdone[v2];
-                if (all) break;  // uniform: every wave read the same flags after the barrier
+                if (all) return false;  // uniform: every wave read the same flags after the barrier
             }
             if (NB > 1 && J - (NB - 1) >= 0) {
                 const int jn = J - (NB - 1);
@@ -476,10 +479,10 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
             }
             if (active && J < I && !wdone) {
                 if constexpr (BND) {
-                    step_mma<S, D, CT, 1, false, 0>(w, srec[buf], lane, h);
+                    step_mma<S, D, CT, 1, false, 0, XF>(w, srec[buf], lane, h);
                     step_softmax_pv<S, D, CT, 1, FOX, false, 0, true>(w, srec[buf], 0.f, lane);
                 } else {
-                    step_mma<S, D, CT, 1, kFold, 0>(w, srec[buf], lane, h);
+                    step_mma<S, D, CT, 1, kFold, 0, XF>(w, srec[buf], lane, h);
                     step_check<S, D, CT, 1, FOX, kFold, 0>(w, stail[buf], h);
                     step_softmax_pv<S, D, CT, 1, FOX, kFold, 0>(w, srec[buf], FOX ? fb[J] : 0.f, lane);
                 }
@@ -492,7 +495,11 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
                 __syncthreads();  // every wave is done with the buffer
                 issue_record<S, REC, NLD, NW, FOX>(rec_ptr(J - 1), tail_ptr(J - 1), srec[0], stail[0], wv, lane);
             }
-        }
+            return true;
+        };
+        bool go = true;
+        for (int J = Jtop; J >= 1 && go; --J) go = body(J, std::true_type{});
+        if (go) body(0, std::false_type{});  // block 0 without the query transform
     };
 
     // ---- epilogue
