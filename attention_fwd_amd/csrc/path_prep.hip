@@ -484,13 +484,28 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
         const int I16 = 16 * wv, t = lane >> 2, p = lane & 3;
         float xs[4] = {0.f, 0.f, 0.f, 0.f};
         const float *gt = sG + tri_tile(wv, wv);
+        // the tile's entries this lane uses and the betas do not depend on the serial
+        // loop: they are read PF steps ahead, so a step does not wait for its LDS reads
+        constexpr int PF = 3;
+        float gv[PF][4], bv[PF];
+        auto fetch = [&](int r, int slot) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) gv[slot][q4] = gt[r * TP + p + 4 * q4];
+            bv[slot] = sBeta[I16 + r];
+        };
+#pragma unroll
+        for (int r = 0; r < PF; ++r) fetch(r, r);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float *gr = gt + r * TP + p;
-            float part = (gr[0] * xs[0] + gr[4] * xs[1]) + (gr[8] * xs[2] + gr[12] * xs[3]);
+            const int sl = r % PF;
+            float part = (gv[sl][0] * xs[0] + gv[sl][1] * xs[1]) + (gv[sl][2] * xs[2] + gv[sl][3] * xs[3]);
+            const float br = bv[sl];
+            if (r + PF < 16) fetch(r + PF, sl);
             part = sum4(part);
-            const float x = (r == t) ? 1.f : (r > t ? -sBeta[I16 + r] * part : 0.f);
-            if (p == (r & 3)) xs[r >> 2] = x;
+            // branch-free (selects): lanes differ in t and p
+            const float xv = -br * part;
+            const float x = (r == t) ? 1.f : (r > t ? xv : 0.f);
+            xs[r >> 2] = (p == (r & 3)) ? x : xs[r >> 2];
         }
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) sE[tri_tile(wv, wv) + (4 * cc + p) * TP + t] = xs[cc];
