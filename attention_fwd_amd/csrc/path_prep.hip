@@ -550,7 +550,10 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
         const float *et = sE + tri_tile(wv, tile_ok ? (c >> 4) : 0) + (c & 15);
         float av[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) av[e] = (tile_ok && c <= rg + e) ? et[e * TP] * bc : 0.f;
+        for (int e = 0; e < 16; ++e) {
+            const float ev = et[e * TP];  // always in bounds; read unconditionally, then selected
+            av[e] = (tile_ok && c <= rg + e) ? ev * bc : 0.f;
+        }
         __syncthreads();  // E and G are dead: their space becomes A (fp32) or A^T (bf16) and V^T
         if constexpr (!kBf) {
 #pragma unroll
@@ -628,6 +631,9 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
         f32x16 o[DT];
 #pragma unroll
         for (int d2 = 0; d2 < DT; ++d2) o[d2] = f32x16{};
+        // each of the two waves stores half of the V^T record: fragments d2 = wv, wv + 2, ...,
+        // kept by selects during the products and stored after them (no branch among the products)
+        typename Elem<S>::Frag vkeep[DT / 2][4];
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             auto pf = acc_frag<S>(s[kc >> 1], kc & 1);
@@ -635,12 +641,17 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
             for (int d2 = 0; d2 < DT; ++d2) {
                 auto vf = lds_frag<S, true, SP>(sVt, 32 * d2 + l32, 16 * kc, h);
                 Elem<S>::mma(o[d2], vf, pf);
-                if ((d2 & 1) == wv) {  // each of the two waves stores half of the V^T record
-                    S *dst = recV + ((int64_t)(d2 * 4 + kc) * 64 + lane) * 8;
-                    *(typename Elem<S>::Frag *)dst = vf;
-                }
+                if ((d2 & 1) == 0) vkeep[d2 >> 1][kc] = vf;
+                else vkeep[d2 >> 1][kc] = wv == 1 ? vf : vkeep[d2 >> 1][kc];
             }
         }
+#pragma unroll
+        for (int k2 = 0; k2 < DT / 2; ++k2)
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+                S *dst = recV + ((int64_t)((2 * k2 + wv) * 4 + kc) * 64 + lane) * 8;
+                *(typename Elem<S>::Frag *)dst = vkeep[k2][kc];
+            }
         if (h == 0) {
             float *md = (float *)((char *)a.ws + lay.off_mdiag), *ld = (float *)((char *)a.ws + lay.off_ldiag);
             md[bh * lay.lp + row0 + i] = mx;
