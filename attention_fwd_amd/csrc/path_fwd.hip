@@ -109,6 +109,22 @@ __device__ __forceinline__ i16x8 fold_ones(int h) {
     const u32x4 u = {h == 0 ? 0x3F803F80u : 0u, 0u, 0u, 0u};
     return __builtin_bit_cast(i16x8, u);
 }
+// With the forget gate the extra k-chunk also carries the gate bias: on the key
+// side elements 2, 3 (lane half 0) hold the row's tail t_j = c_end(J) - c_j as
+// (t_hi, t_lo), on the query side elements 0, 1 hold the query's offset o =
+// off_i - m_i (the gate sum from the end of block J to the query, less the
+// reference max) as (o_hi, o_lo) and elements 2, 3 hold (1, 1), so the product
+// holds s + off_i + t_j - m_i; each pair represents its value to ~2^-17 of it.
+__device__ __forceinline__ i16x8 fold_keys(int h, float t) {
+    const float th = bf16_round(t);
+    const u32x4 u = {h == 0 ? 0x3F803F80u : 0u, h == 0 ? pack_bf16(th, t - th) : 0u, 0u, 0u};
+    return __builtin_bit_cast(i16x8, u);
+}
+__device__ __forceinline__ i16x8 fold_query(int h, float o) {
+    const float oh = bf16_round(o);
+    const u32x4 u = {h == 0 ? pack_bf16(oh, o - oh) : 0u, h == 0 ? 0x3F803F80u : 0u, 0u, 0u};
+    return __builtin_bit_cast(i16x8, u);
+}
 // Split m0 into two bf16 pieces; m becomes their (exact) sum, frag the B column.
 __device__ __forceinline__ void fold_split(float m0, int h, float &m, i16x8 &frag) {
     const float hi = bf16_round(m0), lo = bf16_round(m0 - hi);
@@ -137,7 +153,8 @@ struct WaveState {
     static constexpr int DT = D / 32;
     f32x16 qt[DT][CT], o[DT][CT], s[NS][2][CT];
     float m[CT], lp[CT], off[CT];
-    i16x8 mb[CT];  // folded max: B column (-m_hi, -m_lo) of the extra k-chunk
+    float mref[CT];  // the diagonal block's max: a lower bound of the final max (skipping)
+    i16x8 mb[CT];  // folded max (and gate offset): B column of the extra k-chunk
 };
 
 constexpr float kTau = 8.f;  // the running max is refreshed only when it grows by more than 2^kTau
@@ -145,8 +162,10 @@ constexpr float kSkipLog2 = 64.f;  // skipped key blocks contribute below 2^-64 
 
 // Matrix-core part of step J into logit buffer SB: bf16 copy of qt as the B
 // operand, S^T = khat qt^T for all 64 keys, and qt <- P_J qt.
-template <typename S, int D, int CT, int NS, bool FOLD, int SB, bool XF = true>
-__device__ __forceinline__ void step_mma(WaveState<D, CT, NS> &w, const S *rec, int lane, int h) {
+// TAIL (with FOLD): the forget-gate bias goes into the extra k-chunk too (tail:
+// the block's 64 tail sums in LDS).
+template <typename S, int D, int CT, int NS, bool FOLD, int SB, bool XF = true, bool TAIL = false>
+__device__ __forceinline__ void step_mma(WaveState<D, CT, NS> &w, const S *rec, const float *tail, int lane, int h) {
     typedef Elem<S> E;
     typedef typename E::Frag Frag;
     constexpr int KCH = D / 16, DT = D / 32;
@@ -157,15 +176,20 @@ __device__ __forceinline__ void step_mma(WaveState<D, CT, NS> &w, const S *rec, 
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int kc = 0; kc < KCH; ++kc) qb[ct][kc] = acc_frag<S>(w.qt[kc >> 1][ct], kc & 1);
-    const i16x8 ones = fold_ones(h);
+    if constexpr (TAIL) {
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+        for (int ct = 0; ct < CT; ++ct) w.mb[ct] = fold_query(h, w.off[ct] - w.m[ct]);
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const i16x8 ka = TAIL ? fold_keys(h, tail[32 * hf + (lane & 31)]) : fold_ones(h);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             w.s[SB][hf][ct] = f32x16{};
             if constexpr (FOLD)
-                w.s[SB][hf][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, w.mb[ct], w.s[SB][hf][ct], 0, 0, 0);
+                w.s[SB][hf][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, w.mb[ct], w.s[SB][hf][ct], 0, 0, 0);
         }
+    }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -193,8 +217,9 @@ __device__ __forceinline__ void step_check(WaveState<D, CT, NS> &w, const float 
     constexpr int DT = D / 32;
     float mx[CT];
     bool grow = false;
+    constexpr bool ADD = FOX && !FOLD;  // gate tail added here (folded into the product otherwise)
     f32x4 tl[2][4];  // forget-gate tail of the key rows this lane holds: rows 32 hf + 8 g + 4 h + e
-    if (FOX) {
+    if (ADD) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -207,10 +232,10 @@ __device__ __forceinline__ void step_check(WaveState<D, CT, NS> &w, const float 
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                if (FOX) w.s[SB][hf][ct][r] += tl[hf][r >> 2][r & 3];
+                if (ADD) w.s[SB][hf][ct][r] += tl[hf][r >> 2][r & 3];
                 x = fmaxf(x, w.s[SB][hf][ct][r]);
             }
-        mx[ct] = FOX ? other_half_max(x) + w.off[ct] : other_half_max(x);
+        mx[ct] = ADD ? other_half_max(x) + w.off[ct] : other_half_max(x);
         grow = grow || (mx[ct] > (FOLD ? kTau : w.m[ct] + kTau));
     }
     if (__any(grow)) {
@@ -253,13 +278,13 @@ __device__ __forceinline__ void step_softmax_pv(WaveState<D, CT, NS> &w, const S
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             f32x16 &x = w.s[SB][hf][ct];
-            if (FOX) {
+            if constexpr (FOLD || (BND && !FOX)) {  // the accumulator already holds the logit - m (BND: m = 0)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r]);
+            } else if constexpr (FOX) {
                 const float sh = w.m[ct] - w.off[ct];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r] - sh);
-            } else if constexpr (FOLD || BND) {  // the accumulator already holds s - m (BND: m = 0)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r]);
             } else {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) x[r] = fast_exp2(x[r] - w.m[ct]);
@@ -303,8 +328,10 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
     constexpr int DT = D / 32;
     constexpr int VEC = 16 / (int)sizeof(S);   // elements per 16-byte load
     constexpr int NLD = REC / VEC / NT;        // 16-byte loads per thread per record
-    constexpr bool kFold = sizeof(S) == 2 && !FOX;  // running max folded into the logit product
-    static_assert(MODE == kChecked || !FOX, "the bounded walk is for attention without the forget gate");
+    constexpr bool kFold = sizeof(S) == 2;  // running max (and gate bias) folded into the logit product
+    // bounded walk: without the gate nothing is folded; with it (bf16) the gate bias is
+    constexpr bool kFoldB = FOX && sizeof(S) == 2;
+    static_assert(MODE == kChecked || !FOX || sizeof(S) == 2, "the bounded walk with the forget gate is bf16 only");
     static_assert(REC % (VEC * NT) == 0, "record must split evenly over the workgroup");
     __shared__ __attribute__((aligned(32))) S srec[NB][REC];
     __shared__ __attribute__((aligned(16))) float stail[NB][kBlk];
@@ -365,6 +392,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
             const int io = valid ? i : 0;  // rows past L read row 0 of the block, then drop it
             float ls = ld[i];
             w.m[ct] = md[i];
+            w.mref[ct] = md[i];
             if constexpr (BND) {
                 ls *= fast_exp2(w.m[ct]);
                 w.m[ct] = 0.f;
@@ -423,10 +451,13 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
         }
         if (lane == 0) sdone[wv] = wdone;
     };
-    auto negligible = [&]() {
+    // reference: the running max (checked walk) or the diagonal block's max, a lower bound of the
+    // final max (bounded walk, whose m stays 0)
+    auto negligible = [&](auto bounded) {
         bool ok = true;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) ok = ok && (qbound[ct] + w.off[ct] - w.m[ct] < -kSkipLog2);
+        for (int ct = 0; ct < CT; ++ct)
+            ok = ok && (qbound[ct] + w.off[ct] - (decltype(bounded)::value ? w.mref[ct] : w.m[ct]) < -kSkipLog2);
         return __all(ok);
     };
 
@@ -479,16 +510,16 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
             }
             if (active && J < I && !wdone) {
                 if constexpr (BND) {
-                    step_mma<S, D, CT, 1, false, 0, XF>(w, srec[buf], lane, h);
-                    step_softmax_pv<S, D, CT, 1, FOX, false, 0, true>(w, srec[buf], 0.f, lane);
+                    step_mma<S, D, CT, 1, kFoldB, 0, XF, kFoldB>(w, srec[buf], stail[buf], lane, h);
+                    step_softmax_pv<S, D, CT, 1, FOX, kFoldB, 0, true>(w, srec[buf], FOX ? fb[J] : 0.f, lane);
                 } else {
-                    step_mma<S, D, CT, 1, kFold, 0, XF>(w, srec[buf], lane, h);
+                    step_mma<S, D, CT, 1, kFold, 0, XF, FOX && kFold>(w, srec[buf], stail[buf], lane, h);
                     step_check<S, D, CT, 1, FOX, kFold, 0>(w, stail[buf], h);
                     step_softmax_pv<S, D, CT, 1, FOX, kFold, 0>(w, srec[buf], FOX ? fb[J] : 0.f, lane);
                 }
             }
             if (skip) {  // bound for blocks J - 1 and earlier (off now sits at the J-1 / J boundary)
-                wdone = wdone || negligible();
+                wdone = wdone || negligible(std::integral_constant<bool, BND>{});
                 if (lane == 0) sdone[wv] = wdone;
             }
             if (NB == 1 && J >= 1) {
@@ -546,7 +577,10 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
         // more than the logits being within about +-100 (log2 units) of 0, which
         // holds for any inputs of moderate norm.
         init_state(std::true_type{});
+        if (skip) setup_skip();
         walk(std::true_type{});
+        // no record copy may still be landing in LDS when the workgroup leaves early
+        if (skip) __builtin_amdgcn_s_waitcnt(0);
         bool ok = true;
         if (active) {
 #pragma unroll
@@ -579,19 +613,20 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
 
 }  // namespace
 
-// Without the forget gate: the bounded walk, then the checked walk of the
-// workgroups it flagged (the others leave at once).
+// The bounded walk, then the checked walk of the waves it flagged (workgroups
+// without a flagged wave leave at once); fp32 with the forget gate: the checked
+// walk only.
 template <typename S, int D, bool FOX>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t st) {
     typedef FwdCfg<S, D> F;
     const FwdLayout lay = fwd_layout(a.B, a.H, a.L, D, sizeof(S));
     const int64_t ntile = (lay.nb + F::QB - 1) / F::QB;
     dim3 grid((unsigned)(ntile * lay.bh));
-    if constexpr (FOX) {
+    if constexpr (FOX && sizeof(S) == 4) {
         hipLaunchKernelGGL((path_fwd_kernel<S, D, true, kChecked>), grid, dim3(64 * F::NW), 0, st, a);
     } else {
-        hipLaunchKernelGGL((path_fwd_kernel<S, D, false, kBounded>), grid, dim3(64 * F::NW), 0, st, a);
-        hipLaunchKernelGGL((path_fwd_kernel<S, D, false, kRedo>), grid, dim3(64 * F::NW), 0, st, a);
+        hipLaunchKernelGGL((path_fwd_kernel<S, D, FOX, kBounded>), grid, dim3(64 * F::NW), 0, st, a);
+        hipLaunchKernelGGL((path_fwd_kernel<S, D, FOX, kRedo>), grid, dim3(64 * F::NW), 0, st, a);
     }
     return hipGetLastError();
 }
