@@ -129,7 +129,7 @@ def test_fwd_workload_sampled_rows(name):
     run_and_compare(c["B"], c["H"], L, c["d"], c["dtype"], c["fox"], seed=0, heads=heads, rows=rows)
 
 
-def offset_inputs(L, d, dtype, seed):
+def offset_inputs(L, d, dtype, seed, fox=False):
     """Four heads; in heads 1-3 every logit carries a large common offset while
     the softmax stays well conditioned: the last coordinate of each key is 8
     and of each query is alpha, and every w is orthogonal to that axis, so the
@@ -144,7 +144,8 @@ def offset_inputs(L, d, dtype, seed):
     Head 1: alpha = +150 (2^150 overflows fp32), head 2: alpha = -150 (every
     probability underflows), head 3: alpha = +150 for the queries of the last
     block only.  Head 0 is the plain workload."""
-    x = pathgen.fwd_inputs(1, 4, L, d, dtype, seed=seed, clip=1.98 if dtype == "bf16" else None, device="cuda")
+    x = pathgen.fwd_inputs(1, 4, L, d, dtype, seed=seed, fox=fox, clip=1.98 if dtype == "bf16" else None,
+                           device="cuda")
     q, k, w = x["q"].float(), x["k"].float(), x["w"].float()
     for hh, alpha, first in ((1, 150.0, 0), (2, -150.0, 0), (3, 150.0, 64 * ((L - 1) // 64))):
         w[0, hh, :, -1] = 0.0
@@ -160,17 +161,22 @@ def offset_inputs(L, d, dtype, seed):
 @gpu
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_fwd_large_common_offset(dtype, d):
+@pytest.mark.parametrize("gate", ["none", "fox", "fox_skip"])
+def test_fwd_large_common_offset(dtype, d, gate):
     """Logits far above or below 0 (overflow / underflow of a walk referenced to
-    0) and a head where only one query tile is affected: same bars as any input."""
+    0) and a head where only one query tile is affected: same bars as any input,
+    also under the forget gate, with and without skipping negligible blocks."""
     L = 300
-    say("case large common logit offset %s d%d L%d" % (dtype, d, L))
-    x = offset_inputs(L, d, dtype, seed=77 + d)
+    fox = gate != "none"
+    say("case large common logit offset %s d%d L%d gate=%s" % (dtype, d, L, gate))
+    x = offset_inputs(L, d, dtype, seed=77 + d, fox=fox)
     scale = math.log(2.0) / 8
-    out, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], None, scale=scale, return_lse=True)
+    out, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], scale=scale, return_lse=True,
+                      skip_negligible=gate == "fox_skip")
     torch.cuda.synchronize()
     G = 4
-    ro, rl = oracle.fwd(*(x[n].cpu() for n in ("q", "k", "v", "w", "beta")), scale=scale)
+    ro, rl = oracle.fwd(*(x[n].cpu() for n in ("q", "k", "v", "w", "beta")), x["logf"].cpu() if fox else None,
+                        scale=scale)
     eo = max_abs(to_np(out), ro)
     el = max_abs(to_np(lse), rl)
     say("  max-abs out %.3e  lse %.3e  (lse range %.1f .. %.1f)" % (eo, el, float(rl.min()), float(rl.max())))
