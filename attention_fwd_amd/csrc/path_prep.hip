@@ -221,29 +221,6 @@ __device__ __forceinline__ void tile_mma_areg(f32x16 &c, const f32x16 *at, const
     }
 }
 
-// Accumulator tile of the transpose of a token-major global matrix:
-// c(row, col) = src[col][row] for head-dimension rows d0.. and token columns
-// t0.. (4 contiguous rows per load); tokens at or past nvalid read as zero.
-template <typename S, int D>
-__device__ __forceinline__ void load_tile_t_global(f32x16 &c, const S *src, int d0, int t0, int nvalid, int lane) {
-    const int h = lane >> 5, col = t0 + (lane & 31);
-    const bool ok = col < nvalid;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const S *p = src + (int64_t)col * D + d0 + 8 * g + 4 * h;
-        if constexpr (sizeof(S) == 2) {
-            const u32x2 u = ok ? *(const u32x2 *)p : u32x2{0, 0};
-            c[4 * g + 0] = bf16_to_f32(u.x & 0xffff);
-            c[4 * g + 1] = bf16_to_f32(u.x >> 16);
-            c[4 * g + 2] = bf16_to_f32(u.y & 0xffff);
-            c[4 * g + 3] = bf16_to_f32(u.y >> 16);
-        } else {
-            const f32x4 v = ok ? *(const f32x4 *)p : f32x4{0.f, 0.f, 0.f, 0.f};
-            c[4 * g + 0] = v.x; c[4 * g + 1] = v.y; c[4 * g + 2] = v.z; c[4 * g + 3] = v.w;
-        }
-    }
-}
-
 template <typename S, int D, bool FOX>
 __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_kernel(PrepArgs a) {
     static_assert(D == 64 || D == 128, "prep kernel: head dimension 64 or 128");
@@ -443,7 +420,7 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
     // ---- 2. G = W W^T, X = tril(Q W^T), Y = strictly_upper(K W^T); products with Q and K
     f32x16 g = {};
     f32x16 s[2];                     // waves 0,1: diagonal logits K Q^T
-    f32x16 qi[2], ki[2];             // D = 64, waves 2,3: Q^T, K^T tiles of head-dimension tile wv & 1
+    f32x16 qi[2], ki[2];             // Q^T, K^T tiles of the head-dimension tile this wave takes in phase 4b
     tile_mma<S, true, true, SPD, SPD>(g, sW, sW, mt, nt, D, lane);
     {
         // X^T = W Q^T and Y^T = W K^T, stored back transposed (4 contiguous elements per store)
@@ -460,11 +437,13 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
             s[rt] = f32x16{};
             tile_mma<S, true, true, SPD, SPD>(s[rt], sK, sQ, 32 * rt, 32 * wv, D, lane);
         }
-    } else if constexpr (D == 64) {
+    }
+    if (wv >= 2 || D > 64) {
+        const int dt = D == 64 ? (wv & 1) : (wv ^ 2);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            load_tile_t<S, SPD>(qi[t], sQ, 32 * (wv & 1), 32 * t, lane);
-            load_tile_t<S, SPD>(ki[t], sK, 32 * (wv & 1), 32 * t, lane);
+            load_tile_t<S, SPD>(qi[t], sQ, 32 * dt, 32 * t, lane);
+            load_tile_t<S, SPD>(ki[t], sK, 32 * dt, 32 * t, lane);
         }
     }
     __syncthreads();  // Q, K dead: their space becomes G and E (tiles on or below the diagonal)
@@ -693,10 +672,6 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
         S *gqh = (S *)((char *)a.ws + lay.off_qhat) + (bh * lay.lp + row0) * D;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            if constexpr (D > 64) {
-                load_tile_t_global<S, D>(qi[t], (const S *)a.q + tok0 * D, 32 * dt, 32 * t, nvalid, lane);
-                load_tile_t_global<S, D>(ki[t], (const S *)a.k + tok0 * D, 32 * dt, 32 * t, nvalid, lane);
-            }
             tile_mma_areg<S, true, SP>(qi[t], nu, sX, 32 * t, lane);
             store_rows_t<S, D>(gqh, qi[t], 32 * dt, 32 * t + l32, a.scale * kLog2e, lane);  // log2 units
             tile_mma_areg<S, true, SP>(ki[t], nr, sY, 32 * t, lane);
