@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
     constexpr int RW = EPL * (int)sizeof(S) / 16;  // 16-byte words per lane per row
     typedef u32x4 Raw[RW];
     const int64_t stride = (int64_t)NG * kRowsPerIter;
-    auto fetch = [&](int64_t base, Raw *kr, Raw *vr) {
+    auto fetch = [&](int64_t base, Raw *kr, Raw *vr, float *fr) {
 #pragma unroll
         for (int u = 0; u < kRowsPerIter; ++u) {
             const int64_t j = base + (int64_t)u * NG;
@@ -122,6 +122,7 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
                 kr[u][c] = __builtin_nontemporal_load((const u32x4 *)(ks + EPL * sub + c * (16 / (int)sizeof(S))));
                 vr[u][c] = __builtin_nontemporal_load((const u32x4 *)(vs + EPL * sub + c * (16 / (int)sizeof(S))));
             }
+            if (gate) fr[u] = fcr[ok && !fresh ? j : 0];  // the row's gate prefix sum c_j
         }
     };
     auto widen = [&](const Raw &r, float *x) {
@@ -140,8 +141,8 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
         }
     };
     // one iteration: prefetch the rows at base + stride into (kn, vn), process (kc_, vc_)
-    auto step = [&](int64_t base, Raw *kcur, Raw *vcur, Raw *knext, Raw *vnext) {
-        if (base + stride < r1) fetch(base + stride, knext, vnext);
+    auto step = [&](int64_t base, Raw *kcur, Raw *vcur, float *fcur, Raw *knext, Raw *vnext, float *fnext) {
+        if (base + stride < r1) fetch(base + stride, knext, vnext, fnext);
         float x[kRowsPerIter];
 #pragma unroll
         for (int u = 0; u < kRowsPerIter; ++u) {
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) kn[e] = kx[e] - cb * w[e];
                 storen<S, EPL>(kc + j * D + EPL * sub, kn);
-                x[u] = (tb - cb * qw) * c2 + (gate ? (ct - fcr[j]) * kLog2e : 0.f);
+                x[u] = (tb - cb * qw) * c2 + (gate ? (ct - fcur[u]) * kLog2e : 0.f);
             } else {
                 x[u] = -INFINITY;
             }
@@ -196,11 +197,12 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
         }
     };
     Raw ka[kRowsPerIter], va[kRowsPerIter], kb[kRowsPerIter], vb[kRowsPerIter];
-    if (r0 + grp < r1) fetch(r0 + grp, ka, va);
+    float fa[kRowsPerIter], fb[kRowsPerIter];
+    if (r0 + grp < r1) fetch(r0 + grp, ka, va, fa);
     for (int64_t base = r0 + grp; base < r1; base += 2 * stride) {
-        step(base, ka, va, kb, vb);
+        step(base, ka, va, fa, kb, vb, fb);
         if (base + stride >= r1) break;
-        step(base + stride, kb, vb, ka, va);
+        step(base + stride, kb, vb, fb, ka, va, fa);
     }
 
     // merge the lane groups of the workgroup in a fixed order

@@ -214,7 +214,10 @@ def bench_fused(steps, warmup, name=FWD_WORKLOAD):
             "tokens_per_s": round(B * L / (res["fused"] * 1e-3))}
 
 
-def bench_decode(steps):
+def bench_decode(steps, gate=False):
+    """Decode steps of the decode workload; with gate, PaTH-FoX decode: a gate cache of
+    prefix sums c_j (fp32, read once per step like the keys) and log f_t per step
+    (logsigmoid(N(3, 1)), the forget-gate workload's distribution)."""
     import torch
 
     import attention_fwd_amd as pa
@@ -223,24 +226,34 @@ def bench_decode(steps):
     c = pathgen.WORKLOADS[DEC_WORKLOAD]
     B, H, n, d = c["B"], c["H"], c["n"], c["d"]
     x = pathgen.decode_inputs(B, H, n, d, steps=steps, dtype=c["dtype"], seed=0, clip=c["clip"], device="cuda")
+    fc = lf = None
+    if gate:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(1)
+        lf = torch.nn.functional.logsigmoid(3.0 + torch.randn((steps + 3, B, H), generator=g, device="cuda"))
+        fc = torch.cumsum(torch.nn.functional.logsigmoid(
+            3.0 + torch.randn((B, H, n), generator=g, device="cuda")), dim=-1).contiguous()
     out = torch.empty((B, H, d), device="cuda", dtype=x["kcache"].dtype)
     ws = torch.empty(max(pa.decode_workspace_size(B, H, n, d, x["kcache"].dtype), 16), device="cuda",
                      dtype=torch.uint8)
     stream = torch.cuda.current_stream()
     kc, vc = x["kcache"], x["vcache"]
+    gk = (lambda t: dict(logf=lf[t].contiguous(), fcache=fc)) if gate else (lambda t: {})
     for t in range(3):  # warm-up on the same cache (the update is an ordinary step)
-        pa.decode_step(kc, vc, n, x["q"][t], x["w"][t], x["beta"][t], out=out, workspace=ws)
+        pa.decode_step(kc, vc, n, x["q"][t], x["w"][t], x["beta"][t], out=out, workspace=ws, **gk(t))
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for t in range(steps):
         evs[t][0].record(stream)
-        pa.decode_step(kc, vc, n, x["q"][t], x["w"][t], x["beta"][t], out=out, workspace=ws)
+        pa.decode_step(kc, vc, n, x["q"][t], x["w"][t], x["beta"][t], out=out, workspace=ws, **gk(t))
         evs[t][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
-    nbytes = 3.0 * B * H * n * d * kc.element_size()
+    nbytes = 3.0 * B * H * n * d * kc.element_size() + (4.0 * B * H * n if gate else 0.0)
+    del x, kc, vc, fc, lf, ws
+    torch.cuda.empty_cache()
     return dict(B=B, H=H, n=n, d=d, steps=steps, step_ms=step_ms, wall_s=wall, bytes=nbytes)
 
 
@@ -385,6 +398,8 @@ def main():
     log("decode: %s, %d steps" % (DEC_WORKLOAD, args.decode_steps))
     dres = bench_decode(args.decode_steps)
     log("decode: %.3f ms/step" % dres["step_ms"])
+    gres = bench_decode(args.decode_steps, gate=True)
+    log("decode with the forget gate: %.3f ms/step" % gres["step_ms"])
     sweep = fox_skip = fused = None
     if args.sweep_steps > 0:
         sweep = bench_sweep(args.sweep_steps, 2)
@@ -432,6 +447,9 @@ def main():
                                 "traffic": read_traffic("path_decode_kernel")},
                    "tokens_per_s": round(dres["B"] / (dres["step_ms"] * 1e-3)), "bytes_per_step": dres["bytes"],
                    "steps": dres["steps"]},
+        "decode_forget_gate": {"ms_per_step": round(gres["step_ms"], 4), "bytes_per_step": gres["bytes"],
+                               "GB_per_s": round(gres["bytes"] / (gres["step_ms"] * 1e-3) / 1e9, 1),
+                               "frac_of_hbm_peak": round(gres["bytes"] / (gres["step_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "decode_cache_from_fwd": cache,
         "other_workloads": sweep,
         "fox_skip_negligible": fox_skip,
