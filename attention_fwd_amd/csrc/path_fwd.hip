@@ -22,18 +22,20 @@
 // the (max, sum) workspace by the prep kernel, so every block here is a full,
 // unmasked 64 x 64 tile.
 //
-// Without the forget gate the walk is first made with the softmax reference
-// max fixed at 0 ("bounded walk"): a step is then its 32 products of logits
-// and query transform, exp2 of the logits, column sums, bf16 probabilities
-// and the 16 products of P V, with no max, no check and no branch.  Floating
-// point makes that exact unless a probability overflows or every relevant one
+// The walk is first made with the softmax reference max fixed at 0 ("bounded
+// walk"; all bf16 inputs, fp32 without the forget gate): a step is then its
+// 32 products of logits and query transform (plus, with the gate, 4 that add
+// the gate bias), exp2 of the logits, column sums, bf16 probabilities and the
+// 16 products of P V, with no max, no check and no branch.  Floating point
+// makes that exact unless a probability overflows or every relevant one
 // underflows, which an end-of-walk test per query detects; such waves are
-// walked again by a second launch with the running max ("checked walk", also
-// the only walk under the forget gate).  A checked step issues its matrix-core
-// products first (the running max folded into the logit product as one more
-// k-chunk in bf16), then takes the column maxima of all 64 keys with a single
-// check for the rare rescale, and only then runs the vector work interleaved
-// with the products of P V.  A workgroup is 4 waves = 4 consecutive query
+// walked again by a second launch with the running max ("checked walk", the
+// only walk for fp32 with the gate).  A checked step issues its matrix-core
+// products first (in bf16 the running max and the gate bias folded into the
+// logit product as one more k-chunk), then takes the column maxima of all 64
+// keys with a single check for the rare rescale, and only then runs the vector
+// work interleaved with the products of P V.  The last step of a walk (key
+// block 0) skips the query transform.  A workgroup is 4 waves = 4 consecutive query
 // blocks sharing each key-block record (khat, V^T, -M: 24 KiB bf16 at d = 64),
 // double-buffered in LDS; two workgroups share a CU.
 #include <type_traits>
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
         }
     };
 
-    // ---- skipping negligible key blocks (forget gate only, on request).  With
+    // ---- skipping negligible key blocks (with the forget gate, on request).  With
     // every transition a contraction (0 <= beta ||w||^2 <= 2, checked per block
     // by prep), a logit of query i against any key of block J or earlier is at
     // most ||qhat_i|| * max_j ||k_j|| plus the forget-gate bias of the block

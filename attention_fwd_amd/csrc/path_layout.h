@@ -11,11 +11,11 @@
 //   mdiag/ldiag: running max (log2 units) and sum of the diagonal block;
 //   fq/fk/fb   : forget-gate prefix terms (log2 units), used with logf only;
 //   kn         : per block, max_j ||k_j|| if every transition of the block is a
-//                contraction (0 <= beta ||w||^2 <= 2), else +inf (logf only);
+//                contraction (0 <= beta ||w||^2 <= 2), else +inf (with logf);
 //   redo       : per wave of the forward kernel (at most bh * (2 nb + 8) of
 //                them), 1 when the bounded walk of its queries must be
 //                repeated with the running max (written by the forward
-//                kernel, no logf only).
+//                kernel's bounded walk).
 #pragma once
 
 #include <stddef.h>
