@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for PaTH attention (forward, PaTH-FoX bias, decode step).
+"""fp64 CPU oracle for PaTH attention (forward, PaTH-FoX bias, decode step, backward).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The
@@ -13,6 +13,9 @@ the weighted sum of values described in section 3-4 of the iplexlaw blog
 "거리에서 경로로, PaTH Attention".  Decode follows section 3 of the same
 summary: the newest H_t is applied in place to every cached key; the decode
 cache after a prefix is what those in-place updates would have produced.
+The backward is the chain rule applied to the same definition (the pages
+give the blockwise algorithm as what makes training possible but print no
+gradient formulas).
 """
 from __future__ import annotations
 
@@ -65,6 +68,9 @@ def _load(path=None):
         lib.oracle_produce.restype = ctypes.c_int
         lib.oracle_produce.argtypes = [dp, dp, dp, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, dp, dp]
+        lib.oracle_bwd.restype = ctypes.c_int
+        lib.oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_double, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
         lib.oracle_transport.restype = None
         lib.oracle_transport.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp]
         _libs[path] = lib
@@ -227,3 +233,36 @@ def fwd_fused(q, k, v, wraw, conv_w, zbeta, beta_clip=0.0, logf=None, scale=None
     """PaTH forward with w and beta made by the producer (see produce), fp64."""
     w, beta = produce(wraw, conv_w, zbeta, beta_clip, lib=lib)
     return fwd(q, k, v, w, beta, logf, scale=scale, rows=rows, nthreads=nthreads, lib=lib)
+
+
+def bwd(q, k, v, w, beta, logf, dout, dlse=None, scale=None, nthreads=None, lib=None):
+    """Gradient of sum(dout * o) + sum(dlse * lse) for the forward above, fp64.
+
+    q, k, v, w, dout: [..., L, d]; beta, logf, dlse: [..., L] (logf, dlse may
+    be None).  Returns a dict with dq, dk, dv, dw [..., L, d], dbeta [..., L],
+    dlogf [..., L] (None without logf), and the forward's o and lse.
+    """
+    q, k, v, w, beta, logf, dout, dlse = (_f64(x) for x in (q, k, v, w, beta, logf, dout, dlse))
+    lead = q.shape[:-2]
+    L, d = q.shape[-2], q.shape[-1]
+    G = int(np.prod(lead)) if lead else 1
+    for t in (k, v, w, dout):
+        assert t.shape == q.shape, (t.shape, q.shape)
+    for t in (beta, logf, dlse):
+        assert t is None or t.shape == q.shape[:-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    res = {n: np.zeros((G, L, d)) for n in ("dq", "dk", "dv", "dw", "o")}
+    res["dbeta"] = np.zeros((G, L))
+    res["lse"] = np.zeros((G, L))
+    res["dlogf"] = np.zeros((G, L)) if logf is not None else None
+    rc = _load(lib).oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf), _ptr(dout), _ptr(dlse),
+                               G, L, d, float(scale), _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]),
+                               _ptr(res["dw"]), _ptr(res["dbeta"]), _ptr(res["dlogf"]), _ptr(res["o"]),
+                               _ptr(res["lse"]), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_bwd: bad arguments")
+    for n, a in list(res.items()):
+        if a is not None:
+            res[n] = a.reshape(lead + a.shape[1:])
+    return res

@@ -57,6 +57,9 @@
  * (zero before the first token), no bias, no activation; the normalisation is
  * y / max(||y||, 1e-12); a positive beta_clip caps beta (the pages ask for
  * clipping near 2 in bf16 without a value).
+ *
+ * Backward (oracle_bwd, at the end of this file): the gradient of the forward
+ * by reverse mode of the same definition, row by row; see the comment there.
  */
 #include <math.h>
 #include <pthread.h>
@@ -371,5 +374,172 @@ int oracle_produce(const double *wraw, const double *cw, const double *z, double
             beta[(size_t)g * L + t] = b;
         }
     }
+    return 0;
+}
+
+/*
+ * Backward pass: the exact gradient of the forward above, by reverse mode of
+ * the definition, one query row at a time.  The pages present the blockwise
+ * algorithm as what makes PaTH trainable ([TS s.3]) but print no gradient
+ * formulas, so this is the chain rule applied to the definition of [TS s.2]
+ * and [IPX s.3-4], with nothing reordered beyond what the chain rule states.
+ *
+ * Loss whose gradient is taken: sum_i do_i . o_i + sum_i dlse_i lse_i, where
+ * o and lse are this file's forward outputs (dlse may be NULL, i.e. zero).
+ *
+ * For row i, with u_j = H_{j+1} ... H_i q_i (u_i = q_i, u_{j-1} = H_j u_j):
+ *   s_ij = scale k_j . u_j + (c_i - c_j),  P_ij = softmax_j,  o_i = sum_j P_ij v_j
+ *   dP_ij = do_i . v_j;  dS_ij = P_ij (dP_ij - do_i . o_i + dlse_i)
+ *   dv_j += P_ij do_i;   dk_j += scale dS_ij u_j
+ * The adjoint lam_j of u_j collects scale dS_ij k_j from the logit of key j
+ * and H_j lam_{j-1} from u_{j-1} = H_j u_j (H is symmetric); the same step
+ * gives dH_j = lam_{j-1} u_j^T, whose projections on H_j = I - beta_j w_j w_j^T are
+ *   dbeta_j -= (w_j . lam_{j-1}) (w_j . u_j)
+ *   dw_j    -= beta_j ((w_j . u_j) lam_{j-1} + (w_j . lam_{j-1}) u_j).
+ * Walking j = 0 .. i upward ends with dq_i = lam_i.  The gate bias c_i - c_j
+ * is the sum of log f_t over t = j+1 .. i, so dlogf_t += sum_{j<t} dS_ij for
+ * every t <= i.
+ */
+static void bwd_row(const double *q, const double *k, const double *v, const double *w, const double *beta,
+                    const double *logf, const double *dout, const double *dlse, int d, double scale, int i,
+                    double *U, double *s, double *lam, double *dq, double *dk, double *dv, double *dw,
+                    double *dbeta, double *dlogf, double *o, double *lse) {
+    /* states u_j for j = i .. 0 and the logits */
+    memcpy(U + (size_t)i * d, q + (size_t)i * d, sizeof(double) * (size_t)d);
+    for (int j = i - 1; j >= 0; --j) {
+        memcpy(U + (size_t)j * d, U + (size_t)(j + 1) * d, sizeof(double) * (size_t)d);
+        apply_h(U + (size_t)j * d, w + (size_t)(j + 1) * d, beta[j + 1], d);
+    }
+    double bias = 0.0, m = -INFINITY;
+    for (int j = i; j >= 0; --j) {
+        if (j < i && logf) bias += logf[j + 1];
+        double kt = 0.0;
+        for (int c = 0; c < d; ++c) kt += k[(size_t)j * d + c] * U[(size_t)j * d + c];
+        s[j] = scale * kt + bias;
+        if (s[j] > m) m = s[j];
+    }
+    double z = 0.0;
+    for (int j = 0; j <= i; ++j) z += exp(s[j] - m);
+    for (int c = 0; c < d; ++c) o[c] = 0.0;
+    for (int j = 0; j <= i; ++j) {
+        s[j] = exp(s[j] - m) / z; /* s now holds P_ij */
+        for (int c = 0; c < d; ++c) o[c] += s[j] * v[(size_t)j * d + c];
+    }
+    *lse = m + log(z);
+    const double *doi = dout + (size_t)i * d;
+    double D = 0.0;
+    for (int c = 0; c < d; ++c) D += doi[c] * o[c];
+    const double gl = dlse ? dlse[i] : 0.0;
+    for (int j = 0; j <= i; ++j) {
+        double dp = 0.0;
+        for (int c = 0; c < d; ++c) dp += doi[c] * v[(size_t)j * d + c];
+        const double P = s[j];
+        for (int c = 0; c < d; ++c) dv[(size_t)j * d + c] += P * doi[c];
+        s[j] = P * (dp - D + gl); /* s now holds dS_ij */
+        for (int c = 0; c < d; ++c) dk[(size_t)j * d + c] += scale * s[j] * U[(size_t)j * d + c];
+    }
+    /* adjoints, j upward */
+    for (int c = 0; c < d; ++c) lam[c] = scale * s[0] * k[c];
+    for (int j = 1; j <= i; ++j) {
+        const double *wj = w + (size_t)j * d, *uj = U + (size_t)j * d;
+        double a = 0.0, b = 0.0;
+        for (int c = 0; c < d; ++c) {
+            a += wj[c] * lam[c];
+            b += wj[c] * uj[c];
+        }
+        dbeta[j] -= a * b;
+        for (int c = 0; c < d; ++c) dw[(size_t)j * d + c] -= beta[j] * (b * lam[c] + a * uj[c]);
+        for (int c = 0; c < d; ++c) lam[c] += -beta[j] * a * wj[c] + scale * s[j] * k[(size_t)j * d + c];
+    }
+    memcpy(dq, lam, sizeof(double) * (size_t)d);
+    if (logf) {
+        double acc = 0.0;
+        for (int t = 1; t <= i; ++t) {
+            acc += s[t - 1];
+            dlogf[t] += acc;
+        }
+    }
+}
+
+typedef struct {
+    const double *q, *k, *v, *w, *beta, *logf, *dout, *dlse;
+    int L, d, nthreads, tid;
+    double scale;
+    double *dq, *acc; /* acc: this thread's [dk | dv | dw] (3 L d) then [dbeta | dlogf] (2 L) */
+    double *o, *lse;
+} bwd_job_t;
+
+static void *bwd_worker(void *arg) {
+    bwd_job_t *jb = (bwd_job_t *)arg;
+    const int L = jb->L, d = jb->d;
+    double *U = (double *)malloc(sizeof(double) * (size_t)L * d);
+    double *s = (double *)malloc(sizeof(double) * (size_t)L);
+    double *lam = (double *)malloc(sizeof(double) * (size_t)d);
+    const size_t Ld = (size_t)L * d;
+    for (int i = jb->tid; i < L; i += jb->nthreads)
+        bwd_row(jb->q, jb->k, jb->v, jb->w, jb->beta, jb->logf, jb->dout, jb->dlse, d, jb->scale, i, U, s, lam,
+                jb->dq + (size_t)i * d, jb->acc, jb->acc + Ld, jb->acc + 2 * Ld, jb->acc + 3 * Ld,
+                jb->acc + 3 * Ld + L, jb->o + (size_t)i * d, jb->lse + i);
+    free(U);
+    free(s);
+    free(lam);
+    return NULL;
+}
+
+/*
+ * Backward over G heads ([L, d] row-major each; beta, logf, dlse: [L]).
+ * Inputs q, k, v, w, beta, logf (NULL = no gate), dout = dLoss/do [G, L, d],
+ * dlse = dLoss/dlse [G, L] (NULL = 0).  Outputs dq, dk, dv, dw [G, L, d],
+ * dbeta [G, L], dlogf [G, L] (only with logf), and the forward's o [G, L, d]
+ * and lse [G, L].  Threads split the rows of a head; each keeps its own
+ * key-side sums, added in thread order at the end (deterministic).
+ * Returns 0 or -1.
+ */
+int oracle_bwd(const double *q, const double *k, const double *v, const double *w, const double *beta,
+               const double *logf, const double *dout, const double *dlse, int G, int L, int d, double scale,
+               double *dq, double *dk, double *dv, double *dw, double *dbeta, double *dlogf, double *o, double *lse,
+               int nthreads) {
+    if (G < 0 || L < 0 || d < 1 || nthreads < 1 || ((logf == NULL) != (dlogf == NULL))) return -1;
+    if (nthreads > L) nthreads = L > 0 ? L : 1;
+    const size_t Ld = (size_t)L * d, accn = 3 * Ld + 2 * (size_t)L;
+    double *acc = (double *)malloc(sizeof(double) * accn * (size_t)nthreads);
+    bwd_job_t *jobs = (bwd_job_t *)malloc(sizeof(bwd_job_t) * (size_t)nthreads);
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    for (int g = 0; g < G; ++g) {
+        const size_t hd = (size_t)g * Ld, hl = (size_t)g * L;
+        memset(acc, 0, sizeof(double) * accn * (size_t)nthreads);
+        for (int t = 0; t < nthreads; ++t) {
+            bwd_job_t *jb = &jobs[t];
+            jb->q = q + hd; jb->k = k + hd; jb->v = v + hd; jb->w = w + hd; jb->beta = beta + hl;
+            jb->logf = logf ? logf + hl : NULL; jb->dout = dout + hd; jb->dlse = dlse ? dlse + hl : NULL;
+            jb->L = L; jb->d = d; jb->nthreads = nthreads; jb->tid = t; jb->scale = scale;
+            jb->dq = dq + hd; jb->acc = acc + accn * (size_t)t; jb->o = o + hd; jb->lse = lse + hl;
+            pthread_create(&th[t], NULL, bwd_worker, jb);
+        }
+        for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+        for (size_t e = 0; e < Ld; ++e) {
+            double a = 0.0, b = 0.0, c = 0.0;
+            for (int t = 0; t < nthreads; ++t) {
+                a += acc[accn * (size_t)t + e];
+                b += acc[accn * (size_t)t + Ld + e];
+                c += acc[accn * (size_t)t + 2 * Ld + e];
+            }
+            dk[hd + e] = a;
+            dv[hd + e] = b;
+            dw[hd + e] = c;
+        }
+        for (int j = 0; j < L; ++j) {
+            double a = 0.0, b = 0.0;
+            for (int t = 0; t < nthreads; ++t) {
+                a += acc[accn * (size_t)t + 3 * Ld + j];
+                b += acc[accn * (size_t)t + 3 * Ld + L + j];
+            }
+            dbeta[hl + j] = a;
+            if (dlogf) dlogf[hl + j] = b;
+        }
+    }
+    free(acc);
+    free(jobs);
+    free(th);
     return 0;
 }

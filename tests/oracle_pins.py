@@ -16,7 +16,10 @@ AssertionError when that build disagrees with an independent fact:
   * all w equal with beta = 2 (H^2 = I: closed form by parity),
   * decode reproducing forward rows (the in-place key update of section 3),
   * the decode cache after a prefix equal to explicit products and to feeding
-    the prefix through decode steps one token at a time.
+    the prefix through decode steps one token at a time,
+  * the backward: finite differences of a dense forward, autograd of a dense
+    torch fp64 forward, the softmax-attention gradient at beta = 0, and exact
+    invariances of the loss.
 They are used by test_oracle_pins.py on the real oracle and by
 test_oracle_mutants.py on deliberately broken copies of it.
 """
@@ -351,6 +354,134 @@ def pin_produce(lib):
     _close(o1, o3, 0.0, "fused forward = forward on the produced (w, beta)")
 
 
+# ---------------------------------------------------------------------------
+# Backward pass.  The pages print no gradient formulas; what pins the oracle's
+# gradient is the calculus itself: central finite differences of a forward
+# written with explicit dense transition products (no shared code with the
+# oracle), autograd of a dense torch fp64 implementation, the textbook
+# softmax-attention gradient at beta = 0, and exact invariances of the loss.
+# ---------------------------------------------------------------------------
+
+def _bwd_case(L, d, seed, beta=None, fox=False):
+    q, k, v, w, b, lf = _rand_inputs(L, d, seed, beta=beta, fox=fox)
+    rng = np.random.default_rng(seed + 1000)
+    return dict(q=q, k=k, v=v, w=w, beta=b, logf=lf), rng.standard_normal((L, d)), rng.standard_normal(L)
+
+
+def _dense_loss(x, dout, dlse, scale):
+    S = _brute_scores(x["q"], x["k"], x["w"], x["beta"], x["logf"], scale)
+    o, lse = _softmax_out(S, x["v"])
+    return float((o * dout).sum() + (lse * dlse).sum())
+
+
+def pin_bwd_finite_diff(lib):
+    """Directional derivatives of the loss against central differences of a dense numpy forward."""
+    for (L, d, beta, fox, seed) in [(1, 3, None, False, 1), (2, 2, None, True, 2), (5, 3, None, True, 3),
+                                    (9, 4, None, True, 4), (7, 3, 2.0, False, 5), (6, 3, 1.0, True, 6)]:
+        x, dout, dlse = _bwd_case(L, d, seed, beta=beta, fox=fox)
+        scale = 0.7
+        g = oracle.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], dout, dlse, scale=scale, lib=lib)
+        S = _brute_scores(x["q"], x["k"], x["w"], x["beta"], x["logf"], scale)
+        o, lse = _softmax_out(S, x["v"])
+        _close(g["o"], o, 1e-12, "backward's forward output")
+        _close(g["lse"], lse, 1e-12, "backward's lse")
+        rng = np.random.default_rng(seed + 77)
+        for name in ("q", "k", "v", "w", "beta", "logf"):
+            if x[name] is None:
+                continue
+            for _ in range(3):
+                dirn = rng.standard_normal(x[name].shape)
+                eps = 1e-5
+                xp, xm = dict(x), dict(x)
+                xp[name] = x[name] + eps * dirn
+                xm[name] = x[name] - eps * dirn
+                fd = (_dense_loss(xp, dout, dlse, scale) - _dense_loss(xm, dout, dlse, scale)) / (2 * eps)
+                an = float((g["d" + name] * dirn).sum())
+                assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), \
+                    "d%s L%d: finite difference %.9g vs gradient %.9g" % (name, L, fd, an)
+
+
+def _torch_dense_forward(t, scale):
+    """Dense fp64 torch forward with explicit d x d products (for autograd)."""
+    L, d = t["q"].shape
+    I = torch.eye(d, dtype=torch.float64)
+    Hs = [I - t["beta"][s] * torch.outer(t["w"][s], t["w"][s]) for s in range(L)]
+    c = torch.cumsum(t["logf"], 0) if "logf" in t else None
+    rows_o, rows_l = [], []
+    for i in range(L):
+        logits = []
+        for j in range(i + 1):
+            M = I
+            for s in range(j + 1, i + 1):
+                M = M @ Hs[s]
+            sij = scale * (t["k"][j] @ (M @ t["q"][i]))
+            if c is not None:
+                sij = sij + (c[i] - c[j])
+            logits.append(sij)
+        sv = torch.stack(logits)
+        p = torch.softmax(sv, 0)
+        rows_o.append(p @ t["v"][: i + 1])
+        rows_l.append(torch.logsumexp(sv, 0))
+    return torch.stack(rows_o), torch.stack(rows_l)
+
+
+def pin_bwd_autograd(lib):
+    """Every gradient element against torch autograd of the dense fp64 forward."""
+    for (L, d, beta, fox, seed) in [(4, 3, None, True, 11), (8, 5, None, True, 12), (6, 4, None, False, 13)]:
+        x, dout, dlse = _bwd_case(L, d, seed, beta=beta, fox=fox)
+        scale = 0.45
+        t = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True) for n, a in x.items() if a is not None}
+        o, lse = _torch_dense_forward(t, scale)
+        ((o * torch.from_numpy(dout)).sum() + (lse * torch.from_numpy(dlse)).sum()).backward()
+        g = oracle.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], dout, dlse, scale=scale, lib=lib)
+        for n in t:
+            ref = t[n].grad.numpy()
+            _close(g["d" + n], ref, 1e-11 * max(1.0, float(np.abs(ref).max())), "autograd d%s L%d" % (n, L))
+
+
+def pin_bwd_beta_zero(lib):
+    """beta = 0: the textbook gradient of causal softmax attention (torch SDPA, fp64), and dw = 0."""
+    L, d = 24, 8
+    for fox in (False, True):
+        x, dout, dlse = _bwd_case(L, d, 21, beta=0.0, fox=fox)
+        tq, tk, tv = (torch.tensor(x[n], requires_grad=True) for n in ("q", "k", "v"))
+        if fox:
+            tl = torch.tensor(x["logf"], requires_grad=True)
+            c = torch.cumsum(tl, 0)
+            mask = (c[:, None] - c[None, :]).masked_fill(torch.ones(L, L, dtype=torch.bool).triu(1), float("-inf"))
+            o = torch.nn.functional.scaled_dot_product_attention(tq[None, None], tk[None, None], tv[None, None],
+                                                                 attn_mask=mask[None, None])[0, 0]
+        else:
+            o = torch.nn.functional.scaled_dot_product_attention(tq[None, None], tk[None, None], tv[None, None],
+                                                                 is_causal=True)[0, 0]
+        (o * torch.from_numpy(dout)).sum().backward()
+        g = oracle.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], dout, None, lib=lib)
+        for n, tt in (("q", tq), ("k", tk), ("v", tv)):
+            _close(g["d" + n], tt.grad.numpy(), 1e-11, "beta=0 d%s fox=%s" % (n, fox))
+        if fox:
+            _close(g["dlogf"], tl.grad.numpy(), 1e-11, "beta=0 dlogf")
+        _close(g["dw"], np.zeros_like(x["w"]), 0.0, "beta=0 dw")
+
+
+def pin_bwd_invariants(lib):
+    """Exact identities of the loss: each H_t is unchanged by (w_t, beta_t) -> (a w_t, beta_t / a^2), so
+    w_t . dw_t = 2 beta_t dbeta_t; the logits are unchanged by (q, k) -> (a q, k / a), so
+    sum q . dq = sum k . dk; the weights of a row sum to 1, so sum_j dv_j = sum_i do_i; no bias path
+    crosses token 0, so dlogf_0 = 0; and a zero upstream gradient gives zero gradients."""
+    L, d = 40, 6
+    x, dout, dlse = _bwd_case(L, d, 31, fox=True)
+    g = oracle.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], dout, dlse, lib=lib)
+    gs = max(1.0, float(np.abs(g["dw"]).max()), float(np.abs(g["dbeta"]).max()))
+    _close((g["dw"] * x["w"]).sum(-1), 2 * x["beta"] * g["dbeta"], 1e-10 * gs, "w.dw = 2 beta dbeta")
+    _close((g["dq"] * x["q"]).sum(), (g["dk"] * x["k"]).sum(), 1e-10 * max(1.0, float(np.abs(g["dq"]).max())),
+           "sum q.dq = sum k.dk")
+    _close(g["dv"].sum(0), dout.sum(0), 1e-10, "sum_j dv_j = sum_i do_i")
+    assert g["dlogf"][0] == 0.0, "dlogf_0 = %r" % g["dlogf"][0]
+    z = oracle.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], np.zeros_like(dout), None, lib=lib)
+    for n in ("dq", "dk", "dv", "dw", "dbeta", "dlogf"):
+        _close(z[n], np.zeros_like(z[n]), 0.0, "zero upstream gradient " + n)
+
+
 ALL_PINS = [pin_golden, pin_bruteforce, pin_ut_closed_form, pin_beta_zero, pin_beta_two, pin_beta_one,
             pin_equal_w, pin_small_L, pin_fox_zero, pin_rows_subset, pin_decode, pin_decode_fox, pin_decode_cache,
-            pin_produce]
+            pin_produce, pin_bwd_finite_diff, pin_bwd_autograd, pin_bwd_beta_zero, pin_bwd_invariants]

@@ -52,6 +52,18 @@ MUTANTS = [
     ("produce_beta_no_two", "double b = 2.0 / (1.0 + exp(-z", "double b = 1.0 / (1.0 + exp(-z", 1),
     ("produce_clip_ignored", "if (beta_clip > 0.0 && b > beta_clip) b = beta_clip;", "", 1),
     ("produce_head_index", "cwh = cw + (size_t)(g % H) * d * 3;", "cwh = cw + (size_t)(g / (G / H)) * d * 3;", 1),
+    ("bwd_states_off_by_one", "apply_h(U + (size_t)j * d, w + (size_t)(j + 1) * d, beta[j + 1], d);",
+     "apply_h(U + (size_t)j * d, w + (size_t)j * d, beta[j], d);", 1),
+    ("bwd_dbeta_sign", "dbeta[j] -= a * b;", "dbeta[j] += a * b;", 1),
+    ("bwd_dw_drop_term", "(b * lam[c] + a * uj[c])", "(b * lam[c])", 1),
+    ("bwd_dw_wrong_state", "*uj = U + (size_t)j * d;", "*uj = U + (size_t)(j - 1) * d;", 1),
+    ("bwd_adjoint_skips_H", "lam[c] += -beta[j] * a * wj[c] + scale", "lam[c] += scale", 1),
+    ("bwd_dk_no_scale", "dk[(size_t)j * d + c] += scale * s[j] * U", "dk[(size_t)j * d + c] += s[j] * U", 1),
+    ("bwd_dlse_dropped", "s[j] = P * (dp - D + gl);", "s[j] = P * (dp - D);", 1),
+    ("bwd_dv_unweighted", "dv[(size_t)j * d + c] += P * doi[c];", "dv[(size_t)j * d + c] += doi[c];", 1),
+    ("bwd_dlogf_index", "acc += s[t - 1];", "acc += s[t];", 1),
+    ("bwd_adjoint_init_no_scale", "lam[c] = scale * s[0] * k[c];", "lam[c] = s[0] * k[c];", 1),
+    ("bwd_dq_key_operand", "scale * s[j] * k[(size_t)j * d + c];", "scale * s[j] * v[(size_t)j * d + c];", 1),
 ]
 
 
