@@ -13,7 +13,7 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_fused", "fwd_prep", "fwd_scan", "decode_step", "decode_cache_from_fwd", "fwd_workspace_size",
-           "decode_workspace_size", "lib", "PathError", "PATH_OK", "PATH_EINVAL", "PATH_EUNSUPPORTED", "PATH_EHIP", "PATH_DTYPE_F32", "PATH_DTYPE_BF16",
+           "decode_workspace_size", "bwd", "bwd_workspace_size", "lib", "PathError", "PATH_OK", "PATH_EINVAL", "PATH_EUNSUPPORTED", "PATH_EHIP", "PATH_DTYPE_F32", "PATH_DTYPE_BF16",
            "PATH_FWD_SKIP_NEGLIGIBLE"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpath_attn.so")
@@ -66,6 +66,11 @@ def lib():
                                        ctypes.c_float, vp, sz, vp]
         L.path_decode_cache_from_fwd.restype = ctypes.c_int
         L.path_decode_cache_from_fwd.argtypes = [vp, sz, vp, fp, vp, vp, fp, i64, i, i, i, i, ctypes.c_int, vp]
+        L.path_attn_bwd_workspace_size.restype = sz
+        L.path_attn_bwd_workspace_size.argtypes = [i, i, i, i, ctypes.c_int]
+        L.path_attn_bwd.restype = ctypes.c_int
+        L.path_attn_bwd.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, vp, fp, vp, vp, vp, vp, fp, fp, i, i, i, i,
+                                    ctypes.c_int, ctypes.c_float, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -312,3 +317,53 @@ def decode_cache_from_fwd(workspace, v, kcache, vcache, stream=None, logf=None, 
     if st != PATH_OK:
         raise PathError(st, "path_decode_cache_from_fwd")
     return kcache, vcache
+
+
+def bwd_workspace_size(B, H, L, d, dtype=torch.bfloat16):
+    return int(lib().path_attn_bwd_workspace_size(B, H, L, d, _DTYPES[dtype]))
+
+
+def bwd(q, k, v, w, beta, logf, out, lse, dout, dlse=None, scale=None, workspace=None, stream=None, grads=None):
+    """Backward of fwd (path_attn_bwd): gradients of sum(dout * out) + sum(dlse * lse).
+
+    q, k, v, w, out, dout: [B, H, L, d] (bf16 or fp32, one dtype); beta, lse, logf,
+    dlse: [B, H, L] fp32 (logf, dlse optional); out and lse are fwd's outputs.
+    Returns (dq, dk, dv, dw, dbeta, dlogf) with dlogf None without logf; grads
+    may supply those output tensors.
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d]")
+    B, H, L, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError("dtype must be bfloat16 or float32")
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (w, "w"), (out, "out"), (dout, "dout")):
+        _check(t, n, dt, (B, H, L, d), dev)
+    for t, n in ((beta, "beta"), (lse, "lse"), (logf, "logf"), (dlse, "dlse")):
+        if t is not None:
+            _check(t, n, torch.float32, (B, H, L), dev)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), torch.empty_like(q),
+                 torch.empty((B, H, L), device=dev, dtype=torch.float32),
+                 torch.empty((B, H, L), device=dev, dtype=torch.float32) if logf is not None else None)
+    dq, dk, dv, dw, dbeta, dlogf = grads
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"), (dw, "dw")):
+        _check(t, n, dt, (B, H, L, d), dev)
+    _check(dbeta, "dbeta", torch.float32, (B, H, L), dev)
+    if dlogf is not None:
+        _check(dlogf, "dlogf", torch.float32, (B, H, L), dev)
+    if workspace is None:
+        need = bwd_workspace_size(B, H, L, d, dt)
+        if need == 0:
+            raise PathError(PATH_EUNSUPPORTED if d != 64 else PATH_EINVAL, "path_attn_bwd_workspace_size")
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    _check(workspace, "workspace", None, None, dev)
+    with torch.cuda.device(dev):
+        st = lib().path_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf), _ptr(out), _ptr(lse),
+                                 _ptr(dout), _ptr(dlse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(dbeta),
+                                 _ptr(dlogf), B, H, L, d, _DTYPES[dt], float(scale or 0.0), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != PATH_OK:
+        raise PathError(st, "path_attn_bwd")
+    return dq, dk, dv, dw, dbeta, dlogf

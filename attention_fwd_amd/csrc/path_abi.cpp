@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "path_bwd.h"
 #include "path_kernels.h"
 #include "path_layout.h"
 
@@ -299,6 +300,98 @@ path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace
     path::CacheArgs ca{workspace, v, logf, fcache, kcache, vcache, ncap, B, H, L, d};
     if ((int64_t)B * H > kMaxGrid) return PATH_EINVAL;
     return path::launch_cache(ca, dtype == PATH_DTYPE_BF16, (hipStream_t)stream) == hipSuccess ? PATH_OK : PATH_EHIP;
+}
+
+namespace {
+
+constexpr int64_t kBwdCap = int64_t(8) << 30;  // default workspace: all heads, or what fits in 8 GiB
+
+path_status_t bwd_sizes_ok(int B, int H, int L, int d, path_dtype_t dtype) {
+    if (B < 1 || H < 1 || L < 1 || d < 1 || elem_size(dtype) == 0) return PATH_EINVAL;
+    if (d != 64) return PATH_EUNSUPPORTED;  // the backward kernels are written for d = 64
+    const int64_t nb = ((int64_t)L + 63) / 64;
+    if (mul_chk({B, H, nb * 64, d, 8}) < 0 || mul_chk({nb, nb, 64 * 64 * 8}) < 0) return PATH_EINVAL;
+    if (nb > 65535 || mul_chk({B, H, nb}) > kMaxGrid) return PATH_EINVAL;
+    return PATH_OK;
+}
+
+}  // namespace
+
+size_t path_attn_bwd_workspace_size(int B, int H, int L, int d, path_dtype_t dtype) {
+    if (bwd_sizes_ok(B, H, L, d, dtype) != PATH_OK) return 0;
+    const int64_t share = path::bwd_layout(L).head, G = (int64_t)B * H;
+    int64_t hc = kBwdCap / share;
+    if (hc < 1) hc = 1;
+    if (hc > G) hc = G;
+    return (size_t)(hc * share);
+}
+
+path_status_t path_attn_bwd(const void *q, const void *k, const void *v, const void *w, const float *beta,
+                            const float *logf, const void *out, const float *lse, const void *dout,
+                            const float *dlse, void *dq, void *dk, void *dv, void *dw, float *dbeta, float *dlogf,
+                            int B, int H, int L, int d, path_dtype_t dtype, float scale, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    path_status_t st = bwd_sizes_ok(B, H, L, d, dtype);
+    if (st != PATH_OK) return st;
+    if (!q || !k || !v || !w || !beta || !out || !lse || !dout || !dq || !dk || !dv || !dw || !dbeta || !workspace)
+        return PATH_EINVAL;
+    if ((logf == nullptr) != (dlogf == nullptr)) return PATH_EINVAL;
+    const void *tens_in[] = {q, k, v, w, out, dout};
+    void *tens_out[] = {dq, dk, dv, dw};
+    const void *tok_in[] = {beta, logf, lse, dlse};
+    void *tok_out[] = {dbeta, dlogf};
+    for (const void *p : tens_in)
+        if (!aligned(p, 16)) return PATH_EINVAL;
+    for (const void *p : tens_out)
+        if (!aligned(p, 16)) return PATH_EINVAL;
+    if (!aligned(workspace, 16)) return PATH_EINVAL;
+    for (const void *p : tok_in)
+        if (p && !aligned(p, 4)) return PATH_EINVAL;
+    for (const void *p : tok_out)
+        if (p && !aligned(p, 4)) return PATH_EINVAL;
+    if (!std::isfinite(scale)) return PATH_EINVAL;
+    const int64_t share = path::bwd_layout(L).head, G = (int64_t)B * H;
+    if ((int64_t)workspace_bytes < share) return PATH_EINVAL;
+    int64_t hc = (int64_t)workspace_bytes / share;
+    if (hc > G) hc = G;
+    if (hc > 65535) hc = 65535;
+    const int64_t wsb = hc * share;
+    const int64_t tens = (int64_t)B * H * L * d * elem_size(dtype), tok = (int64_t)B * H * L * 4;
+    // every output against every other buffer
+    for (int i = 0; i < 4; ++i) {
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(tens_out[i], tens, tens_out[j], tens)) return PATH_EINVAL;
+        for (const void *p : tens_in)
+            if (overlap(tens_out[i], tens, p, tens)) return PATH_EINVAL;
+        for (const void *p : tok_in)
+            if (overlap(tens_out[i], tens, p, tok)) return PATH_EINVAL;
+        for (void *p : tok_out)
+            if (overlap(tens_out[i], tens, p, tok)) return PATH_EINVAL;
+        if (overlap(tens_out[i], tens, workspace, wsb)) return PATH_EINVAL;
+    }
+    for (int i = 0; i < 2; ++i) {
+        if (!tok_out[i]) continue;
+        if (i == 0 && overlap(dbeta, tok, dlogf, tok)) return PATH_EINVAL;
+        for (const void *p : tens_in)
+            if (overlap(tok_out[i], tok, p, tens)) return PATH_EINVAL;
+        for (const void *p : tok_in)
+            if (overlap(tok_out[i], tok, p, tok)) return PATH_EINVAL;
+        if (overlap(tok_out[i], tok, workspace, wsb)) return PATH_EINVAL;
+    }
+    for (const void *p : tens_in)
+        if (overlap(workspace, wsb, p, tens)) return PATH_EINVAL;
+    for (const void *p : tok_in)
+        if (overlap(workspace, wsb, p, tok)) return PATH_EINVAL;
+
+    path::BwdArgs ba{};
+    ba.q = q; ba.k = k; ba.v = v; ba.w = w; ba.beta = beta; ba.logf = logf; ba.out = out; ba.lse = lse;
+    ba.dout = dout; ba.dlse = dlse; ba.dq = dq; ba.dk = dk; ba.dv = dv; ba.dw = dw; ba.dbeta = dbeta;
+    ba.dlogf = dlogf; ba.ws = workspace;
+    ba.B = B; ba.H = H; ba.L = L; ba.d = d; ba.scale = eff_scale(scale, d);
+    ba.nb = (L + 63) / 64;
+    ba.hc_max = (int)hc;
+    ba.ly = path::bwd_layout(L);
+    return path::launch_bwd(ba, dtype == PATH_DTYPE_BF16, (hipStream_t)stream) == hipSuccess ? PATH_OK : PATH_EHIP;
 }
 
 }  // extern "C"

@@ -1,0 +1,720 @@
+// path_bwd.hip -- backward pass of PaTH attention (gradients of q, k, v, w,
+// beta and the log forget gate), gfx950.
+//
+// The pages present the blockwise algorithm (UT transform per block, scan over
+// key blocks) as what makes PaTH trainable ("技術要約: PaTH Attention", section 3,
+// and "거리에서 경로로, PaTH Attention", section 9) but print no gradient; what is
+// computed here is the chain rule applied to the forward's definition
+// (summary section 2: s_ij = scale k_j^T H_{j+1} ... H_i q_i, H = I - beta w w^T,
+// plus the forget-gate path sum; blog sections 3-4: causal softmax, weighted
+// sum of values), organised on the same 64-token blocks as the forward.
+//
+// Loss: sum do . o + sum dlse . lse, with o and lse the forward's outputs.
+//
+// Per block J (tokens s..e, local index 0..63), with W the block's w rows and
+// B = diag(beta):
+//   X = (I + B su(W W^T))^-1 (unit upper triangular), A = X B
+//   q^_i = H_s ... H_i q_i      = q_i - (Z W)_i,  Z = (Q W^T o [r <= i]) A^T
+//   k^_j = H_e ... H_{j+1} k_j  = k_j - (Y W)_j,  Y = N A,  N = K W^T o [r > j]
+//   T_J  = H_s ... H_e          = I - W^T A W                (d x d, dense)
+//   diagonal logits  s_ij = scale (Q K^T - Z N^T)_ij + gate,  j <= i
+// For query block I and key block J < I the logits are scale q~ . k^ with the
+// query carried down q~^(J-1) = T_J q~^(J), q~^(I-1) = q^.  The adjoint of
+// q~^(J) obeys G^(J) = G^(J-1) T_J + scale dS_IJ K^_J (rows), running upward
+// while q~ runs downward, so:
+//   prep (per block): the quantities above, the diagonal block's dS, its
+//     value gradient, and fp32 copies of v and do;
+//   query-major walk (per query block I): down J = I-1 .. 0 storing q~^(J)
+//     for every pair, then up J = 0 .. I-1 storing G^(J-1) for every pair and
+//     ending with dq^_I = G^(I-1);
+//   key-major walk (per key block J): over I > J, dV_J += P^T dO_I,
+//     dk^_J += scale dS^T q~, dT_J += G^(J-1)^T q~ -- sums owned by one
+//     workgroup, so no atomics;
+//   block backward (per block): the matrix-form chain rule through the
+//     formulas above (including the triangular inverse: dT' = -X^T dX X^T)
+//     gives dq, dk, dw, dbeta; dv adds the two value sums; the gate's
+//     per-token adjoint dc_t = rowsum_t(dS) - colsum_t(dS);
+//   gate: dlogf_t = sum_{t' >= t} dc_t' (one workgroup per head).
+// Every contraction is a 64x64x64 fp32 product on the matrix cores
+// (v_mfma_f32_32x32x2f32) with operands in LDS, so the gradients are fp32
+// for either input type.  Head dimension 64.
+#include <hip/hip_runtime.h>
+
+#include "path_bwd.h"
+#include "path_common.h"
+
+namespace path {
+namespace {
+
+constexpr int kC = 64;   // tokens per block
+constexpr int kD = 64;   // head dimension
+constexpr int kP = 65;   // LDS row stride of a 64x64 fp32 tile (odd: conflict-free rows and columns)
+constexpr int kT = 256;  // threads per workgroup (4 waves)
+constexpr int kTile = kC * kP;
+
+// A 64x64 fp32 matrix in LDS; element (r, c) at p[r * rs + c * cs].
+struct LMat {
+    const float *p;
+    int rs, cs;
+};
+__device__ __forceinline__ LMat nat(const float *p) { return {p, kP, 1}; }
+__device__ __forceinline__ LMat tr(const float *p) { return {p, 1, kP}; }
+
+// acc += A * B for 64x64 operands; wave w owns the 32x32 output tile at rows
+// 32 (w >> 1), columns 32 (w & 1).
+__device__ __forceinline__ void mm(f32x16 &acc, LMat A, LMat B, int lane, int wave) {
+    const int r = 32 * (wave >> 1) + (lane & 31), c = 32 * (wave & 1) + (lane & 31), h = lane >> 5;
+    const float *pa = A.p + r * A.rs + h * A.cs, *pb = B.p + c * B.cs + h * B.rs;
+#pragma unroll 16
+    for (int k = 0; k < 64; k += 2)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[k * A.cs], pb[k * B.rs], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) z[v] = 0.f;
+    return z;
+}
+
+// Row / column of accumulator register v of this lane.
+__device__ __forceinline__ int arow(int v, int lane, int wave) { return 32 * (wave >> 1) + acc_row(v, lane >> 5); }
+__device__ __forceinline__ int acol(int lane, int wave) { return 32 * (wave & 1) + (lane & 31); }
+
+template <typename F>
+__device__ __forceinline__ void store_lds(float *buf, const f32x16 &acc, int lane, int wave, F f) {
+    const int c = acol(lane, wave);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int r = arow(v, lane, wave);
+        buf[r * kP + c] = f(r, c, acc[v]);
+    }
+}
+
+// Global fp32 tile [64][64] (row stride 64) <-> LDS.
+__device__ __forceinline__ void g2l(float *buf, const float *g, int tid) {
+#pragma unroll
+    for (int e = tid; e < kC * kD / 4; e += kT) {
+        const int r = e >> 4, c = (e & 15) * 4;
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(g + r * kD + c);
+        float *d = buf + r * kP + c;
+        d[0] = x[0]; d[1] = x[1]; d[2] = x[2]; d[3] = x[3];
+    }
+}
+__device__ __forceinline__ void zero_lds(float *buf, int tid) {
+    for (int e = tid; e < kTile; e += kT) buf[e] = 0.f;
+}
+__device__ __forceinline__ void acc2g(float *g, const f32x16 &acc, int lane, int wave) {
+    const int c = acol(lane, wave);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) g[arow(v, lane, wave) * kD + c] = acc[v];
+}
+
+// Input tensor rows [row0, row0 + 64) of one head (rows >= L read as 0) -> LDS fp32.
+template <typename T>
+__device__ __forceinline__ void in2l(float *buf, const T *g, int row0, int L, int tid) {
+    for (int e = tid; e < kC * kD; e += kT) {
+        const int r = e >> 6, c = e & 63;
+        buf[r * kP + c] = (row0 + r < L) ? Elem<T>::to_f32(g[(int64_t)(row0 + r) * kD + c]) : 0.f;
+    }
+}
+
+__device__ __forceinline__ int64_t pair_index(int I, int J) { return (int64_t)I * (I - 1) / 2 + J; }
+
+// X = (I + diag(beta) su(G))^-1 by back substitution, one column per thread.
+__device__ __forceinline__ void unit_upper_inverse(float *X, const float *G, const float *beta, int tid) {
+    if (tid < kC) {
+        const int c = tid;
+        for (int r = c + 1; r < kC; ++r) X[r * kP + c] = 0.f;
+        X[c * kP + c] = 1.f;
+        for (int r = c - 1; r >= 0; --r) {
+            float s = 0.f;
+            for (int t = r + 1; t <= c; ++t) s += G[r * kP + t] * X[t * kP + c];
+            X[r * kP + c] = -beta[r] * s;
+        }
+    }
+}
+
+// Block-local gate prefix sums (inclusive) of one block: cl[i] for its 64 rows.
+__device__ __forceinline__ void gate_prefix(float *cl, const float *logf, int row0, int L, int tid) {
+    if (tid == 0) {
+        float c = 0.f;
+        for (int i = 0; i < kC; ++i) {
+            c += (logf && row0 + i < L) ? logf[row0 + i] : 0.f;
+            cl[i] = c;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prep: one workgroup per (block J, head).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
+    __shared__ float sm[9 * kTile + 4 * kC];
+    float *bW = sm, *bQ = bW + kTile, *bK = bQ + kTile, *bG = bK + kTile, *bA = bG + kTile, *bQW = bA + kTile,
+          *bN = bQW + kTile, *bZ = bN + kTile, *bY = bZ + kTile;
+    float *sB = bY + kTile, *sCl = sB + kC, *sL2 = sCl + kC, *sDD = sL2 + kC;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int J = blockIdx.x, gl = blockIdx.y, g = a.g0 + gl, L = a.L, row0 = J * kC;
+    const int64_t hoff = (int64_t)g * L;
+    const T *q = (const T *)a.q + hoff * kD, *k = (const T *)a.k + hoff * kD, *w = (const T *)a.w + hoff * kD;
+    const T *v = (const T *)a.v + hoff * kD, *o = (const T *)a.out + hoff * kD, *dout = (const T *)a.dout + hoff * kD;
+    const BwdLayout &ly = a.ly;
+    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
+    const float scale = a.scale;
+
+    in2l(bW, w, row0, L, tid);
+    in2l(bQ, q, row0, L, tid);
+    in2l(bK, k, row0, L, tid);
+    if (tid < kC) {
+        const int i = row0 + tid;
+        sB[tid] = i < L ? a.beta[hoff + i] : 0.f;
+        sL2[tid] = i < L ? a.lse[hoff + i] * kLog2e : 0.f;
+    }
+    gate_prefix(sCl, a.logf ? a.logf + hoff : nullptr, row0, L, tid);
+    {   // D_i = do_i . o_i - dlse_i: four lanes per row, 16 columns each
+        const int r = tid >> 2, c0 = (tid & 3) * 16, i = row0 + r;
+        float s = 0.f;
+        if (i < L)
+            for (int c = c0; c < c0 + 16; ++c)
+                s += Elem<T>::to_f32(dout[(int64_t)i * kD + c]) * Elem<T>::to_f32(o[(int64_t)i * kD + c]);
+        s = sum4(s);
+        if ((tid & 3) == 0) sDD[r] = i < L ? s - (a.dlse ? a.dlse[hoff + i] : 0.f) : 0.f;
+    }
+    __syncthreads();
+    f32x16 acc = zero16();
+    mm(acc, nat(bW), tr(bW), lane, wave);  // G = W W^T
+    store_lds(bG, acc, lane, wave, [](int, int, float x) { return x; });
+    __syncthreads();
+    unit_upper_inverse(bA, bG, sB, tid);
+    __syncthreads();
+    for (int e = tid; e < kC * kC; e += kT) bA[(e >> 6) * kP + (e & 63)] *= sB[e & 63];  // A = X diag(beta)
+    acc = zero16();
+    mm(acc, nat(bQ), tr(bW), lane, wave);  // Q W^T, keep r <= i
+    store_lds(bQW, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });
+    acc = zero16();
+    mm(acc, nat(bK), tr(bW), lane, wave);  // N = K W^T, keep r > j
+    store_lds(bN, acc, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });
+    __syncthreads();
+    acc = zero16();
+    mm(acc, nat(bQW), tr(bA), lane, wave);  // Z = QWm A^T
+    store_lds(bZ, acc, lane, wave, [](int, int, float x) { return x; });
+    acc = zero16();
+    mm(acc, nat(bN), nat(bA), lane, wave);  // Y = N A
+    store_lds(bY, acc, lane, wave, [](int, int, float x) { return x; });
+    __syncthreads();
+    float *QH = (float *)(ws + ly.qh) + row0 * kD, *KH = (float *)(ws + ly.kh) + row0 * kD;
+    {
+        const int c = acol(lane, wave);
+        acc = zero16();
+        mm(acc, nat(bZ), nat(bW), lane, wave);  // q^ = q - Z W
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            const int r = arow(vv, lane, wave);
+            QH[r * kD + c] = bQ[r * kP + c] - acc[vv];
+        }
+        acc = zero16();
+        mm(acc, nat(bY), nat(bW), lane, wave);  // k^ = k - Y W
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            const int r = arow(vv, lane, wave);
+            KH[r * kD + c] = bK[r * kP + c] - acc[vv];
+        }
+        acc = zero16();
+        mm(acc, nat(bA), nat(bW), lane, wave);  // A W (into bQW, free after Z)
+    }
+    __syncthreads();
+    store_lds(bQW, acc, lane, wave, [](int, int, float x) { return x; });
+    __syncthreads();
+    {
+        float *TT = (float *)(ws + ly.tt) + (int64_t)J * kD * kD;
+        acc = zero16();
+        mm(acc, tr(bW), nat(bQW), lane, wave);  // T = I - W^T (A W)
+        const int c = acol(lane, wave);
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            const int r = arow(vv, lane, wave);
+            TT[r * kD + c] = (r == c ? 1.f : 0.f) - acc[vv];
+        }
+    }
+    // diagonal block: P = exp(scale (Q K^T - Z N^T) + cl_i - cl_j - lse_i) for j <= i
+    f32x16 sQK = zero16(), sZN = zero16();
+    mm(sQK, nat(bQ), tr(bK), lane, wave);
+    mm(sZN, nat(bZ), tr(bN), lane, wave);
+    __syncthreads();  // bG, bY free: P -> bG, v -> bY, do -> bA
+    {
+        const int c = acol(lane, wave);
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            const int r = arow(vv, lane, wave);
+            const float s = (scale * (sQK[vv] - sZN[vv]) + (sCl[r] - sCl[c])) * kLog2e - sL2[r];
+            bG[r * kP + c] = c <= r ? fast_exp2(s) : 0.f;
+        }
+    }
+    in2l(bY, v, row0, L, tid);
+    in2l(bA, dout, row0, L, tid);
+    __syncthreads();
+    acc = zero16();
+    mm(acc, nat(bA), tr(bY), lane, wave);  // dP = dO V^T
+    store_lds(bZ, acc, lane, wave, [&](int r, int c, float x) { return bG[r * kP + c] * (x - sDD[r]); });
+    __syncthreads();
+    {
+        float *EE = (float *)(ws + ly.ee) + (int64_t)J * kC * kC;
+        for (int e = tid; e < kC * kC; e += kT) EE[e] = scale * bZ[(e >> 6) * kP + (e & 63)];
+        float *VF = (float *)(ws + ly.vf) + row0 * kD, *DOF = (float *)(ws + ly.dof) + row0 * kD;
+        for (int e = tid; e < kC * kD; e += kT) {
+            VF[e] = bY[(e >> 6) * kP + (e & 63)];
+            DOF[e] = bA[(e >> 6) * kP + (e & 63)];
+        }
+        acc = zero16();
+        mm(acc, tr(bG), nat(bA), lane, wave);  // diagonal value gradient P^T dO
+        acc2g((float *)(ws + ly.dvd) + row0 * kD, acc, lane, wave);
+        float *rs = (float *)(ws + ly.rsd) + row0, *cs = (float *)(ws + ly.csd) + row0;
+        if (tid < kC) {
+            float s = 0.f;
+            for (int c = 0; c < kC; ++c) s += bZ[tid * kP + c];
+            rs[tid] = s;
+        } else if (tid < 2 * kC) {
+            const int c = tid - kC;
+            float s = 0.f;
+            for (int r = 0; r < kC; ++r) s += bZ[r * kP + c];
+            cs[c] = s;
+        } else if (tid < 3 * kC) {
+            const int r = tid - 2 * kC;
+            ((float *)(ws + ly.l2))[row0 + r] = sL2[r];
+            ((float *)(ws + ly.dd))[row0 + r] = sDD[r];
+            ((float *)(ws + ly.clq))[row0 + r] = sCl[r];
+            ((float *)(ws + ly.ckk))[row0 + r] = sCl[kC - 1] - sCl[r];
+            if (r == 0) ((float *)(ws + ly.tot))[J] = sCl[kC - 1];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Query-major walk: one workgroup per (query block I >= 1, head); heaviest first.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
+    __shared__ float sm[7 * kTile + 4 * kC];
+    float *bQt = sm, *bT = bQt + kTile, *bK = bT + kTile, *bV = bK + kTile, *bDO = bV + kTile, *bG = bDO + kTile,
+          *bS = bG + kTile;
+    float *sL2 = bS + kTile, *sDD = sL2 + kC, *sCq = sDD + kC, *sCk = sCq + kC;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nb = a.nb, hc = a.hc;
+    const int gl = blockIdx.x % hc, I = nb - 1 - blockIdx.x / hc;
+    const BwdLayout &ly = a.ly;
+    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
+    const float *TT = (const float *)(ws + ly.tt), *KH = (const float *)(ws + ly.kh), *VF = (const float *)(ws + ly.vf);
+    const float *tot = (const float *)(ws + ly.tot);
+    float *QS = (float *)(ws + ly.qs), *GS = (float *)(ws + ly.gs), *MID = (float *)(ws + ly.mid);
+    const float scale = a.scale;
+    const int row0 = I * kC, c = acol(lane, wave);
+
+    // down: q~^(J) for J = I-1 .. 0
+    g2l(bQt, (const float *)(ws + ly.qh) + row0 * kD, tid);
+    float mid = 0.f;
+    {
+        float *dst = QS + pair_index(I, I - 1) * kC * kD;
+        const float *src = (const float *)(ws + ly.qh) + row0 * kD;
+        for (int e = tid; e < kC * kD / 4; e += kT)
+            reinterpret_cast<f32x4 *>(dst)[e] = reinterpret_cast<const f32x4 *>(src)[e];
+    }
+    if (tid == 0) MID[pair_index(I, I - 1)] = 0.f;
+    for (int J = I - 1; J >= 1; --J) {
+        g2l(bT, TT + (int64_t)J * kD * kD, tid);
+        __syncthreads();
+        f32x16 acc = zero16();
+        mm(acc, nat(bQt), tr(bT), lane, wave);  // q~^(J-1) = T_J q~^(J) (rows: Q~ T^T)
+        __syncthreads();
+        store_lds(bQt, acc, lane, wave, [](int, int, float x) { return x; });
+        acc2g(QS + pair_index(I, J - 1) * kC * kD, acc, lane, wave);
+        mid += tot[J];
+        if (tid == 0) MID[pair_index(I, J - 1)] = mid;
+    }
+    // up: adjoint G
+    g2l(bDO, (const float *)(ws + ly.dof) + row0 * kD, tid);
+    if (tid < kC) {
+        sL2[tid] = ((const float *)(ws + ly.l2))[row0 + tid];
+        sDD[tid] = ((const float *)(ws + ly.dd))[row0 + tid];
+        sCq[tid] = ((const float *)(ws + ly.clq))[row0 + tid];
+    }
+    f32x16 accG = zero16();
+    float rsum = 0.f;
+    __syncthreads();
+    for (int J = 0; J < I; ++J) {
+        const int64_t p = pair_index(I, J);
+        g2l(bQt, QS + p * kC * kD, tid);
+        g2l(bK, KH + (int64_t)J * kC * kD, tid);
+        g2l(bV, VF + (int64_t)J * kC * kD, tid);
+        if (J >= 1) g2l(bT, TT + (int64_t)J * kD * kD, tid);
+        if (tid < kC) sCk[tid] = ((const float *)(ws + ly.ckk))[J * kC + tid];
+        const float midJ = MID[p];
+        if (J >= 1) acc2g(GS + p * kC * kD, accG, lane, wave);  // G^(J-1) for the key-major walk
+        __syncthreads();
+        f32x16 s = zero16(), dp = zero16();
+        mm(s, nat(bQt), tr(bK), lane, wave);
+        mm(dp, nat(bDO), tr(bV), lane, wave);
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            const int r = arow(vv, lane, wave);
+            const float x = (scale * s[vv] + sCq[r] + sCk[c] + midJ) * kLog2e - sL2[r];
+            bS[r * kP + c] = fast_exp2(x) * (dp[vv] - sDD[r]);
+        }
+        __syncthreads();
+        f32x16 gt = zero16(), xs = zero16();
+        if (J >= 1) mm(gt, nat(bG), nat(bT), lane, wave);
+        mm(xs, nat(bS), nat(bK), lane, wave);
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) accG[vv] = gt[vv] + scale * xs[vv];
+        if (tid < kC) {
+            float t = 0.f;
+            for (int cc = 0; cc < kC; ++cc) t += bS[tid * kP + cc];
+            rsum += t;
+        }
+        __syncthreads();
+        store_lds(bG, accG, lane, wave, [](int, int, float x) { return x; });
+    }
+    acc2g((float *)(ws + ly.dqo) + row0 * kD, accG, lane, wave);
+    if (tid < kC) ((float *)(ws + ly.rso))[row0 + tid] = rsum;
+}
+
+// ---------------------------------------------------------------------------
+// Key-major walk: one workgroup per (key block J <= nb-2, head); heaviest first.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
+    __shared__ float sm[7 * kTile + 4 * kC];
+    float *bK = sm, *bV = bK + kTile, *bQt = bV + kTile, *bDO = bQt + kTile, *bG = bDO + kTile, *bP = bG + kTile,
+          *bS = bP + kTile;
+    float *sL2 = bS + kTile, *sDD = sL2 + kC, *sCq = sDD + kC, *sCk = sCq + kC;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nb = a.nb, hc = a.hc;
+    const int gl = blockIdx.x % hc, J = blockIdx.x / hc;
+    const BwdLayout &ly = a.ly;
+    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
+    const float *tot = (const float *)(ws + ly.tot), *QS = (const float *)(ws + ly.qs),
+                *GS = (const float *)(ws + ly.gs);
+    const float scale = a.scale;
+    const int c = acol(lane, wave);
+
+    g2l(bK, (const float *)(ws + ly.kh) + (int64_t)J * kC * kD, tid);
+    g2l(bV, (const float *)(ws + ly.vf) + (int64_t)J * kC * kD, tid);
+    if (tid < kC) sCk[tid] = ((const float *)(ws + ly.ckk))[J * kC + tid];
+    f32x16 dV = zero16(), dK = zero16(), dT = zero16();
+    float csum = 0.f, mid = 0.f;
+    for (int I = J + 1; I < nb; ++I) {
+        const int64_t p = pair_index(I, J);
+        const int row0 = I * kC;
+        g2l(bQt, QS + p * kC * kD, tid);
+        g2l(bDO, (const float *)(ws + ly.dof) + row0 * kD, tid);
+        if (J >= 1) g2l(bG, GS + p * kC * kD, tid);
+        if (tid < kC) {
+            sL2[tid] = ((const float *)(ws + ly.l2))[row0 + tid];
+            sDD[tid] = ((const float *)(ws + ly.dd))[row0 + tid];
+            sCq[tid] = ((const float *)(ws + ly.clq))[row0 + tid];
+        }
+        __syncthreads();
+        f32x16 s = zero16(), dp = zero16();
+        mm(s, nat(bQt), tr(bK), lane, wave);
+        mm(dp, nat(bDO), tr(bV), lane, wave);
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            const int r = arow(vv, lane, wave);
+            const float P = fast_exp2((scale * s[vv] + sCq[r] + sCk[c] + mid) * kLog2e - sL2[r]);
+            bP[r * kP + c] = P;
+            bS[r * kP + c] = P * (dp[vv] - sDD[r]);
+        }
+        __syncthreads();
+        mm(dV, tr(bP), nat(bDO), lane, wave);
+        mm(dK, tr(bS), nat(bQt), lane, wave);
+        if (J >= 1) mm(dT, tr(bG), nat(bQt), lane, wave);
+        if (tid < kC) {
+            float t = 0.f;
+            for (int r = 0; r < kC; ++r) t += bS[r * kP + tid];
+            csum += t;
+        }
+        mid += tot[I];
+        __syncthreads();
+    }
+    const int row0 = J * kC;
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) dK[vv] *= scale;
+    acc2g((float *)(ws + ly.dko) + row0 * kD, dK, lane, wave);
+    acc2g((float *)(ws + ly.dvo) + row0 * kD, dV, lane, wave);
+    acc2g((float *)(ws + ly.dt) + (int64_t)J * kD * kD, dT, lane, wave);
+    if (tid < kC) ((float *)(ws + ly.cso))[row0 + tid] = csum;
+}
+
+// ---------------------------------------------------------------------------
+// Block backward: one workgroup per (block J, head).
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void acc2out(T *g, const f32x16 &acc, int row0, int L, int lane, int wave) {
+    const int c = acol(lane, wave);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int r = arow(v, lane, wave);
+        if (row0 + r < L) g[(int64_t)(row0 + r) * kD + c] = Elem<T>::from_float(acc[v]);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
+    __shared__ float sm[9 * kTile + 2 * kC];
+    float *bW = sm, *bQ = bW + kTile, *bK = bQ + kTile, *bX = bK + kTile, *bA = bX + kTile, *bQW = bA + kTile,
+          *b6 = bQW + kTile, *bN = b6 + kTile, *b8 = bN + kTile;
+    float *sB = b8 + kTile, *sRed = sB + kC;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int J = blockIdx.x, gl = blockIdx.y, g = a.g0 + gl, L = a.L, nb = a.nb, row0 = J * kC;
+    const int64_t hoff = (int64_t)g * L;
+    const T *q = (const T *)a.q + hoff * kD, *k = (const T *)a.k + hoff * kD, *w = (const T *)a.w + hoff * kD;
+    const BwdLayout &ly = a.ly;
+    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
+    const bool hasQ = J >= 1, hasK = J <= nb - 2, hasT = J >= 1 && J <= nb - 2;
+    auto id = [](int, int, float x) { return x; };
+
+    in2l(bW, w, row0, L, tid);
+    in2l(bQ, q, row0, L, tid);
+    in2l(bK, k, row0, L, tid);
+    if (tid < kC) sB[tid] = row0 + tid < L ? a.beta[hoff + row0 + tid] : 0.f;
+    __syncthreads();
+    f32x16 acc = zero16();
+    mm(acc, nat(bW), tr(bW), lane, wave);  // G
+    store_lds(b8, acc, lane, wave, id);
+    __syncthreads();
+    unit_upper_inverse(bX, b8, sB, tid);
+    __syncthreads();
+    for (int e = tid; e < kC * kC; e += kT) {
+        const int r = e >> 6, cc = e & 63;
+        bA[r * kP + cc] = bX[r * kP + cc] * sB[cc];
+    }
+    acc = zero16();
+    mm(acc, nat(bQ), tr(bW), lane, wave);
+    store_lds(bQW, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });
+    acc = zero16();
+    mm(acc, nat(bK), tr(bW), lane, wave);
+    store_lds(bN, acc, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });
+    __syncthreads();
+    acc = zero16();
+    mm(acc, nat(bQW), tr(bA), lane, wave);  // Z
+    store_lds(b6, acc, lane, wave, id);
+    g2l(b8, (const float *)(ws + ly.ee) + (int64_t)J * kC * kC, tid);  // E = scale dS of the diagonal block
+    __syncthreads();
+    f32x16 dQ = zero16(), dK = zero16(), dZ = zero16(), dN = zero16(), dW = zero16(), dA = zero16();
+    mm(dQ, nat(b8), nat(bK), lane, wave);   // E K
+    mm(dK, tr(b8), nat(bQ), lane, wave);    // E^T Q
+    mm(dZ, nat(b8), nat(bN), lane, wave);   // (E N), negated below
+    mm(dN, tr(b8), nat(b6), lane, wave);    // (E^T Z), negated below
+    __syncthreads();
+    if (hasQ) g2l(b8, (const float *)(ws + ly.dqo) + row0 * kD, tid);  // dq^ from the query-major walk
+    else zero_lds(b8, tid);
+    __syncthreads();
+    mm(dZ, nat(b8), tr(bW), lane, wave);    // + dq^ W^T
+    mm(dW, tr(b6), nat(b8), lane, wave);    // Z^T dq^ (negated below)
+    {
+        const int c = acol(lane, wave);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = arow(v, lane, wave);
+            dQ[v] += b8[r * kP + c];
+            dZ[v] = -dZ[v];
+            dN[v] = -dN[v];
+            dW[v] = -dW[v];
+        }
+    }
+    __syncthreads();
+    if (hasK) g2l(b8, (const float *)(ws + ly.dko) + row0 * kD, tid);  // dk^ from the key-major walk
+    else zero_lds(b8, tid);
+    __syncthreads();
+    {
+        const int c = acol(lane, wave);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dK[v] += b8[arow(v, lane, wave) * kP + c];
+    }
+    acc = zero16();
+    mm(acc, nat(b8), tr(bW), lane, wave);  // dY = -dk^ W^T
+    store_lds(b6, acc, lane, wave, [](int, int, float x) { return -x; });
+    acc = zero16();
+    mm(acc, tr(bN), nat(b8), lane, wave);  // R = N^T dk^ (into bQ; q is read again later)
+    __syncthreads();
+    store_lds(bQ, acc, lane, wave, id);
+    __syncthreads();
+    mm(dN, nat(b6), tr(bA), lane, wave);   // += dY A^T
+    mm(dA, tr(bN), nat(b6), lane, wave);   // N^T dY
+    acc = zero16();
+    mm(acc, tr(bA), nat(bQ), lane, wave);  // A^T R = Y^T dk^
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dW[v] -= acc[v];
+    __syncthreads();
+    store_lds(b6, dN, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });  // dKW = dN o [r > j]
+    in2l(bQ, q, row0, L, tid);
+    __syncthreads();
+    mm(dK, nat(b6), nat(bW), lane, wave);  // += dKW W
+    mm(dW, tr(b6), nat(bK), lane, wave);   // += dKW^T K
+    __syncthreads();
+    store_lds(b6, dZ, lane, wave, id);
+    __syncthreads();
+    acc = zero16();
+    mm(acc, nat(b6), nat(bA), lane, wave);  // dQWm = (dZ A) o [r <= i]
+    mm(dA, tr(b6), nat(bQW), lane, wave);   // += dZ^T QWm
+    store_lds(bN, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });
+    __syncthreads();
+    mm(dQ, nat(bN), nat(bW), lane, wave);   // += dQWm W
+    mm(dW, tr(bN), nat(bQ), lane, wave);    // += dQWm^T Q
+    __syncthreads();
+    if (hasT) {  // T = I - W^T A W
+        g2l(b6, (const float *)(ws + ly.dt) + (int64_t)J * kD * kD, tid);
+        acc = zero16();
+        mm(acc, nat(bA), nat(bW), lane, wave);  // A W
+        __syncthreads();
+        store_lds(bN, acc, lane, wave, id);
+        acc = zero16();
+        mm(acc, nat(bW), nat(b6), lane, wave);  // W dT
+        store_lds(bQW, acc, lane, wave, id);
+        __syncthreads();
+        acc = zero16();
+        mm(acc, nat(bQW), tr(bW), lane, wave);  // W dT W^T
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dA[v] -= acc[v];
+        acc = zero16();
+        mm(acc, nat(bN), tr(b6), lane, wave);   // A W dT^T
+        mm(acc, tr(bA), nat(bQW), lane, wave);  // + A^T W dT
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dW[v] -= acc[v];
+        __syncthreads();
+    }
+    // A = X diag(beta): dX = dA diag(beta), dbeta_c += sum_r X_rc dA_rc (dA kept on the upper triangle)
+    {
+        const int c = acol(lane, wave);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = arow(v, lane, wave);
+            dA[v] = c >= r ? dA[v] : 0.f;
+            b6[r * kP + c] = dA[v] * sB[c];
+            bQW[r * kP + c] = bX[r * kP + c] * dA[v];
+        }
+    }
+    __syncthreads();
+    float dbeta = 0.f;
+    if (tid < kC)
+        for (int r = 0; r < kC; ++r) dbeta += bQW[r * kP + tid];
+    acc = zero16();
+    mm(acc, tr(bX), nat(b6), lane, wave);  // X^T dX
+    __syncthreads();
+    store_lds(bN, acc, lane, wave, id);
+    __syncthreads();
+    f32x16 dTp = zero16(), G = zero16();
+    mm(dTp, nat(bN), tr(bX), lane, wave);  // (X^T dX) X^T; dT' is its negative
+    mm(G, nat(bW), tr(bW), lane, wave);
+    {
+        const int c = acol(lane, wave);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = arow(v, lane, wave);
+            const float t = -dTp[v];
+            bQW[r * kP + c] = c > r ? t * G[v] : 0.f;    // dbeta_r += sum_c dT'_rc U_rc
+            b6[r * kP + c] = c > r ? sB[r] * t : 0.f;    // dG = diag(beta) dT' on the strict upper triangle
+        }
+    }
+    __syncthreads();
+    if (tid >= kC && tid < 2 * kC) {
+        float s = 0.f;
+        for (int c = 0; c < kC; ++c) s += bQW[(tid - kC) * kP + c];
+        sRed[tid - kC] = s;
+    }
+    mm(dW, nat(b6), nat(bW), lane, wave);  // += (dG + dG^T) W
+    mm(dW, tr(b6), nat(bW), lane, wave);
+    __syncthreads();
+    if (tid < kC && row0 + tid < L) a.dbeta[hoff + row0 + tid] = dbeta + sRed[tid];
+    acc2out((T *)a.dq + hoff * kD, dQ, row0, L, lane, wave);
+    acc2out((T *)a.dk + hoff * kD, dK, row0, L, lane, wave);
+    acc2out((T *)a.dw + hoff * kD, dW, row0, L, lane, wave);
+    {
+        const float *dvd = (const float *)(ws + ly.dvd) + row0 * kD, *dvo = (const float *)(ws + ly.dvo) + row0 * kD;
+        T *dv = (T *)a.dv + hoff * kD;
+        for (int e = tid; e < kC * kD; e += kT) {
+            const int r = e >> 6;
+            if (row0 + r < L)
+                dv[(int64_t)(row0 + r) * kD + (e & 63)] = Elem<T>::from_float(dvd[e] + (hasK ? dvo[e] : 0.f));
+        }
+    }
+    if (tid < kC) {
+        const int i = row0 + tid;
+        const float rs = ((const float *)(ws + ly.rsd))[i] + (hasQ ? ((const float *)(ws + ly.rso))[i] : 0.f);
+        const float cs = ((const float *)(ws + ly.csd))[i] + (hasK ? ((const float *)(ws + ly.cso))[i] : 0.f);
+        ((float *)(ws + ly.dc))[i] = rs - cs;
+    }
+}
+
+// dlogf_t = sum_{t' >= t} dc_t' for one head: 256 threads, contiguous chunks, fixed order.
+__global__ __launch_bounds__(kT) void bwd_gate_kernel(BwdArgs a) {
+    __shared__ float part[kT];
+    const int tid = threadIdx.x, gl = blockIdx.x, L = a.L;
+    const int64_t hoff = (int64_t)(a.g0 + gl) * L;
+    const float *dc = (const float *)((const char *)a.ws + (int64_t)gl * a.ly.head + a.ly.dc);
+    const int ch = (L + kT - 1) / kT, t0 = tid * ch, t1 = min(L, t0 + ch);
+    float s = 0.f;
+    for (int t = t1 - 1; t >= t0; --t) s += dc[t];
+    part[tid] = s;
+    __syncthreads();
+    if (tid == 0) {  // exclusive suffix sums of the chunk totals, in place
+        float run = 0.f;
+        for (int u = kT - 1; u >= 0; --u) {
+            const float x = part[u];
+            part[u] = run;
+            run += x;
+        }
+    }
+    __syncthreads();
+    float run = part[tid];
+    for (int t = t1 - 1; t >= t0; --t) {
+        run += dc[t];
+        a.dlogf[hoff + t] = run;
+    }
+}
+
+}  // namespace
+
+BwdLayout bwd_layout(int L) {
+    BwdLayout ly{};
+    const int64_t nb = (L + kC - 1) / kC, Lp = nb * kC, np = nb * (nb - 1) / 2;
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t o = off;
+        off += (bytes + 255) / 256 * 256;
+        return o;
+    };
+    const int64_t tile = Lp * kD * 4, rows = Lp * 4;
+    ly.qh = take(tile); ly.kh = take(tile); ly.vf = take(tile); ly.dof = take(tile); ly.tt = take(nb * kD * kD * 4);
+    ly.ee = take(nb * kC * kC * 4); ly.dvd = take(tile); ly.dqo = take(tile); ly.dko = take(tile); ly.dvo = take(tile);
+    ly.dt = take(nb * kD * kD * 4);
+    ly.l2 = take(rows); ly.dd = take(rows); ly.clq = take(rows); ly.ckk = take(rows); ly.rsd = take(rows);
+    ly.csd = take(rows); ly.rso = take(rows); ly.cso = take(rows); ly.dc = take(rows);
+    ly.tot = take(nb * 4); ly.mid = take(np * 4);
+    ly.qs = take(np * kC * kD * 4); ly.gs = take(np * kC * kD * 4);
+    ly.head = off;
+    return ly;
+}
+
+hipError_t launch_bwd(const BwdArgs &a0, bool bf16, hipStream_t st) {
+    BwdArgs a = a0;
+    const int G = a.B * a.H;
+    for (int g0 = 0; g0 < G; g0 += a.hc_max) {
+        a.g0 = g0;
+        a.hc = min(a.hc_max, G - g0);
+        const dim3 blk(kT);
+        if (bf16) hipLaunchKernelGGL(bwd_prep_kernel<uint16_t>, dim3(a.nb, a.hc), blk, 0, st, a);
+        else hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3(a.nb, a.hc), blk, 0, st, a);
+        if (a.nb > 1) {
+            hipLaunchKernelGGL(bwd_query_kernel, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
+            hipLaunchKernelGGL(bwd_key_kernel, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
+        }
+        if (bf16) hipLaunchKernelGGL(bwd_block_kernel<uint16_t>, dim3(a.nb, a.hc), blk, 0, st, a);
+        else hipLaunchKernelGGL(bwd_block_kernel<float>, dim3(a.nb, a.hc), blk, 0, st, a);
+        if (a.dlogf) hipLaunchKernelGGL(bwd_gate_kernel, dim3(a.hc), blk, 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace path

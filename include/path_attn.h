@@ -45,12 +45,12 @@
 extern "C" {
 #endif
 
-#define PATH_ABI_VERSION 3
+#define PATH_ABI_VERSION 4
 
 typedef enum {
     PATH_OK = 0,
     PATH_EINVAL = 1,        /* NULL pointer, bad size, misaligned, workspace too small, n > ncap */
-    PATH_EUNSUPPORTED = 2,  /* valid but not implemented (head dimension other than 64, 128) */
+    PATH_EUNSUPPORTED = 2,  /* valid but not implemented (head dimension other than 64, 128; 128 in the backward) */
     PATH_EHIP = 3           /* the HIP runtime rejected a launch */
 } path_status_t;
 
@@ -242,6 +242,51 @@ path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace
                                          const float *logf, void *kcache, void *vcache, float *fcache,
                                          int64_t ncap, int B, int H, int L, int d, path_dtype_t dtype,
                                          void *stream);
+
+/*
+ * Workspace bytes for path_attn_bwd (0 if the sizes are invalid or not
+ * supported): enough to process all B*H heads at once when that takes at most
+ * 8 GiB, else the largest whole number of heads that fits in 8 GiB (at least
+ * one).  path_attn_bwd_workspace_size(1, 1, L, d, dtype) is one head's share;
+ * path_attn_bwd accepts any workspace of at least one share and processes
+ * floor(workspace_bytes / share) heads at a time (results do not depend on it).
+ * One share is about (32 nb (nb - 1) / 2 + 13 nb) KiB + 40 bytes per token,
+ * nb = ceil(L / 64), for d = 64.
+ */
+size_t path_attn_bwd_workspace_size(int B, int H, int L, int d, path_dtype_t dtype);
+
+/*
+ * Backward pass of path_attn_fwd: gradients of
+ *     loss = sum_{b,h,i} dout_i . out_i  +  sum_{b,h,i} dlse_i lse_i
+ * with respect to q, k, v, w, beta and (with the forget gate) logf.  The pages
+ * give the blockwise algorithm ([TS] s.3) as what makes PaTH trainable and
+ * print no gradient; this is the chain rule applied to the forward's definition
+ * (path_attn_fwd above), evaluated on the same 64-token blocks: a walk over
+ * key blocks per query block for the query side, one per key block for the
+ * key side and the block transitions, and a per-block pass through the UT
+ * transform.  All arithmetic is fp32 (fp32 matrix cores) for either dtype.
+ *
+ * q, k, v, w, out, dout : [B, H, L, d] element type `dtype` (read only); out is the
+ *                         forward's output for these inputs
+ * beta, lse             : [B, H, L] fp32 (read only); lse is the forward's natural-log
+ *                         normaliser (path_attn_fwd's lse output)
+ * logf, dlogf           : [B, H, L] fp32 log forget gate and its gradient, or both NULL
+ * dlse                  : [B, H, L] fp32 gradient with respect to lse, or NULL (zero)
+ * dq, dk, dv, dw        : [B, H, L, d] element type `dtype` (written)
+ * dbeta                 : [B, H, L] fp32 (written)
+ * scale                 : as in path_attn_fwd (<= 0 selects 1/sqrt(d))
+ * workspace             : device scratch, see path_attn_bwd_workspace_size
+ *
+ * d must be 64 (128 returns PATH_EUNSUPPORTED).  Outputs must not overlap each
+ * other, the inputs or the workspace.  Returns PATH_OK, PATH_EINVAL (NULL,
+ * sizes, misaligned, workspace below one head's share, overlaps),
+ * PATH_EUNSUPPORTED or PATH_EHIP.
+ */
+path_status_t path_attn_bwd(const void *q, const void *k, const void *v, const void *w, const float *beta,
+                            const float *logf, const void *out, const float *lse, const void *dout,
+                            const float *dlse, void *dq, void *dk, void *dv, void *dw, float *dbeta, float *dlogf,
+                            int B, int H, int L, int d, path_dtype_t dtype, float scale, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

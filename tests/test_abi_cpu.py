@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = pa.lib()
-    assert lib.path_abi_version() == 3
+    assert lib.path_abi_version() == 4
     for s in range(4):
         assert lib.path_status_string(s)
     assert lib.path_status_string(99) == b"unknown status"
@@ -189,3 +189,53 @@ def test_fwd_ex_rejects_unknown_flags():
     args = [P(0), P(1), P(2), P(3), P(4), None, P(5), None, 1, 1, 64, 64, BF, 0.0, P(6), 1 << 40]
     assert lib.path_attn_fwd_ex(*args, 2, None) == pa.PATH_EINVAL
     assert lib.path_attn_fwd_ex(*args[:1], None, *args[2:], 1, None) == pa.PATH_EINVAL  # k NULL, valid flag
+
+
+def test_bwd_workspace_sizes():
+    lib = pa.lib()
+    one = lib.path_attn_bwd_workspace_size(1, 1, 200, 64, BF)
+    assert one > 0
+    assert lib.path_attn_bwd_workspace_size(2, 3, 200, 64, BF) == 6 * one   # all heads at once
+    assert lib.path_attn_bwd_workspace_size(1, 1, 200, 128, BF) == 0        # d = 128 not in the backward
+    assert lib.path_attn_bwd_workspace_size(1, 1, 0, 64, BF) == 0
+    assert lib.path_attn_bwd_workspace_size(1, 1, 64, 64, 9) == 0
+    share = lib.path_attn_bwd_workspace_size(1, 1, 4096, 64, BF)
+    big = lib.path_attn_bwd_workspace_size(32, 32, 4096, 64, BF)
+    assert big % share == 0 and share <= big <= 8 << 30                     # capped at whole heads in 8 GiB
+    assert lib.path_attn_bwd_workspace_size(1, 1, 65, 64, F32) > lib.path_attn_bwd_workspace_size(1, 1, 64, 64, F32)
+
+
+def bwd_call(**over):
+    share = pa.lib().path_attn_bwd_workspace_size(1, 1, 64, 64, BF)
+    args = dict(q=P(0), k=P(1), v=P(2), w=P(3), beta=P(4), logf=None, out=P(5), lse=P(6), dout=P(7), dlse=None,
+                dq=P(8), dk=P(9), dv=P(10), dw=P(11), dbeta=P(12), dlogf=None, B=1, H=1, L=64, d=64, dtype=BF,
+                scale=0.0, ws=ctypes.c_void_p(A * 64), wsb=share, stream=None)
+    args.update(over)
+    a = args
+    return pa.lib().path_attn_bwd(a["q"], a["k"], a["v"], a["w"], a["beta"], a["logf"], a["out"], a["lse"], a["dout"],
+                                  a["dlse"], a["dq"], a["dk"], a["dv"], a["dw"], a["dbeta"], a["dlogf"], a["B"],
+                                  a["H"], a["L"], a["d"], a["dtype"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(lse=None), pa.PATH_EINVAL),                          # the forward's lse is required
+    (dict(out=None), pa.PATH_EINVAL),
+    (dict(dout=None), pa.PATH_EINVAL),
+    (dict(dbeta=None), pa.PATH_EINVAL),
+    (dict(logf=P(13)), pa.PATH_EINVAL),                        # gate without its gradient
+    (dict(dlogf=P(13)), pa.PATH_EINVAL),                       # gradient without the gate
+    (dict(d=128), pa.PATH_EUNSUPPORTED),
+    (dict(d=96), pa.PATH_EUNSUPPORTED),
+    (dict(L=0), pa.PATH_EINVAL),
+    (dict(dtype=7), pa.PATH_EINVAL),
+    (dict(wsb=1024), pa.PATH_EINVAL),                          # below one head's share
+    (dict(dq=ctypes.c_void_p(A * 9 + 8)), pa.PATH_EINVAL),     # misaligned
+    (dict(dk=P(8)), pa.PATH_EINVAL),                           # two outputs alias
+    (dict(dq=P(0)), pa.PATH_EINVAL),                           # output over an input
+    (dict(dbeta=P(4)), pa.PATH_EINVAL),                        # dbeta over beta
+    (dict(dv=ctypes.c_void_p(A * 64)), pa.PATH_EINVAL),        # output inside the workspace
+    (dict(ws=P(1)), pa.PATH_EINVAL),                           # workspace over an input
+    (dict(scale=float("inf")), pa.PATH_EINVAL),
+])
+def test_bwd_rejects_bad_arguments(over, status):
+    assert bwd_call(**over) == status

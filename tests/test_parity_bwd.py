@@ -1,0 +1,123 @@
+"""GPU parity of path_attn_bwd (the backward pass) against the fp64 oracle's reverse mode.
+
+The GPU backward is fed the GPU forward's own out and lse (as a training step
+would); the oracle recomputes its forward exactly.  Bars, per gradient tensor,
+relative to the tensor's largest reference magnitude (gradients are not
+normalised the way attention outputs are): max|g - ref| <= tol * max(1, max|ref|)
+with tol 1e-4 for fp32 inputs (fp32 arithmetic throughout) and 2e-2 for bf16
+inputs (the backward computes in fp32, but its inputs out/lse carry the bf16
+forward's rounding and dq, dk, dv, dw are rounded to bf16 on output).
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_fwd_amd as pa
+import oracle
+import pathgen
+from parity_util import say, to_np
+
+gpu = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+NAMES = ("dq", "dk", "dv", "dw", "dbeta", "dlogf")
+
+
+def run_case(B, H, L, dtype, seed, fox, beta=None, with_dlse=True, scale=None, workspace=None):
+    x = pathgen.fwd_inputs(B, H, L, 64, dtype, seed=seed, fox=fox, clip=1.98 if dtype == "bf16" else None,
+                           device="cuda")
+    if beta is not None:
+        x["beta"] = torch.full((B, H, L), float(beta), device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 500)
+    dout = torch.randn((B, H, L, 64), generator=g, device="cuda").to(x["q"].dtype)
+    dlse = torch.randn((B, H, L), generator=g, device="cuda") if with_dlse else None
+    out, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], scale=scale, return_lse=True)
+    grads = pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out, lse, dout, dlse, scale=scale,
+                   workspace=workspace)
+    torch.cuda.synchronize()
+    return x, dout, dlse, out, lse, grads
+
+
+def compare(x, dout, dlse, grads, dtype, scale=None, what=""):
+    ref = oracle.bwd(*(x[n].cpu() for n in ("q", "k", "v", "w", "beta")), x["logf"].cpu() if x["logf"] is not None
+                     else None, dout.cpu(), dlse.cpu() if dlse is not None else None, scale=scale)
+    worst = {}
+    for n, t in zip(NAMES, grads):
+        if t is None:
+            assert ref[n] is None
+            continue
+        r = ref[n]
+        e = float(np.abs(to_np(t) - r).max())
+        bar = TOL[dtype] * max(1.0, float(np.abs(r).max()))
+        worst[n] = e / bar
+        assert e <= bar, "%s %s: max-abs %.3e > bar %.3e (max|ref| %.3e)" % (what, n, e, bar, np.abs(r).max())
+    say("  %s error / bar: %s" % (what, " ".join("%s %.3f" % kv for kv in worst.items())))
+
+
+@gpu
+@pytest.mark.parametrize("fox", [False, True])
+@pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 130, 200, 333])
+def test_bwd_fp32(L, fox):
+    say("case bwd fp32 L%d fox=%s" % (L, fox))
+    x, dout, dlse, _, _, grads = run_case(1, 2, L, "f32", seed=L, fox=fox)
+    compare(x, dout, dlse, grads, "f32", what="L%d" % L)
+
+
+@gpu
+@pytest.mark.parametrize("fox", [False, True])
+@pytest.mark.parametrize("L", [64, 300, 700])
+def test_bwd_bf16(L, fox):
+    say("case bwd bf16 L%d fox=%s" % (L, fox))
+    x, dout, dlse, _, _, grads = run_case(2, 2, L, "bf16", seed=10 + L, fox=fox)
+    compare(x, dout, dlse, grads, "bf16", what="L%d" % L)
+
+
+@gpu
+@pytest.mark.parametrize("beta", [0.0, 1.0, 2.0])
+def test_bwd_beta_regimes(beta):
+    """beta = 0 (plain softmax attention), 1 (projectors) and 2 (reflections), fp32, without dlse."""
+    say("case bwd beta=%g" % beta)
+    x, dout, dlse, _, _, grads = run_case(1, 2, 150, "f32", seed=77, fox=True, beta=beta, with_dlse=False)
+    compare(x, dout, dlse, grads, "f32", what="beta=%g" % beta)
+    if beta == 0.0:
+        assert float(grads[3].abs().max()) == 0.0, "dw must vanish at beta = 0"
+
+
+@gpu
+def test_bwd_scale():
+    say("case bwd scale 0.3")
+    x, dout, dlse, _, _, grads = run_case(2, 1, 257, "f32", seed=5, fox=True, scale=0.3)
+    compare(x, dout, dlse, grads, "f32", scale=0.3, what="scale 0.3")
+
+
+@gpu
+def test_bwd_chunked_workspace_and_determinism():
+    """A workspace of one head's share (heads one at a time) gives the same bits as all heads at once,
+    and repeated calls are bitwise identical."""
+    say("case bwd chunked workspace")
+    B, H, L = 1, 3, 200
+    share = pa.bwd_workspace_size(1, 1, L, 64, torch.float32)
+    ws1 = torch.empty(share, device="cuda", dtype=torch.uint8)
+    x, dout, dlse, out, lse, g_all = run_case(B, H, L, "f32", seed=9, fox=True)
+    g_one = pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out, lse, dout, dlse, workspace=ws1)
+    g_rep = pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out, lse, dout, dlse)
+    torch.cuda.synchronize()
+    for n, a, b, c in zip(NAMES, g_all, g_one, g_rep):
+        assert torch.equal(a, b), "chunked " + n
+        assert torch.equal(a, c), "repeat " + n
+
+
+@gpu
+def test_bwd_per_head_workload_shape():
+    """One head at the per-head shape of the B32 H32 L4096 d64 bf16 workload, every gradient element."""
+    say("case bwd bf16 L4096 one head")
+    x, dout, dlse, _, _, grads = run_case(1, 1, 4096, "bf16", seed=3, fox=False)
+    compare(x, dout, dlse, grads, "bf16", what="L4096")
+
+
+@gpu
+def test_bwd_rejects_d128():
+    x = pathgen.fwd_inputs(1, 1, 64, 128, "f32", seed=0, device="cuda")
+    o, l = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], return_lse=True)
+    with pytest.raises(pa.PathError):
+        pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], None, o, l, torch.ones_like(o))
