@@ -17,6 +17,13 @@ Work units (fixed, declared):
            counted.
   decode   bytes = 3 B H n d * 2: read every cached key, write it back
            updated, read every cached value.
+  backward Fb = 8 B H L^2 d flop: per causal pair of 64-token blocks eight
+           64 x 64 x d contractions (logits, dO V^T, dV, dk^, dS k^, the
+           adjoint's and the query's transition products, the transition
+           gradient) at 2 * 64^2 d each; the key-major walk's recomputation
+           of the logits and dO V^T and the in-block work are not counted.
+           The backward computes in fp32, so it is priced against the fp32
+           matrix-core peak.
 """
 from __future__ import annotations
 
@@ -33,6 +40,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 matrix peak (published)
 METRIC = "PaTH fwd TFLOP/s + % MFMA peak (B32 H32 d64 L4096); decode-step HBM GB/s"
 FWD_WORKLOAD = "sweep_L4096_d64_bf16"
 DEC_WORKLOAD = "decode_N32768_bf16"
@@ -295,6 +303,50 @@ def bench_cache(steps, f):
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": read_traffic("path_cache_kernel")}}
 
 
+def bench_backward(steps, warmup, name=FWD_WORKLOAD):
+    """Backward pass (path_attn_bwd) on the forward workload: gradients of q, k, v, w, beta
+    for a random upstream gradient, fed the forward's own out and lse."""
+    import torch
+
+    import attention_fwd_amd as pa
+    import pathgen
+
+    c = pathgen.WORKLOADS[name]
+    B, H, L, d = c["B"], c["H"], c["L"], c["d"]
+    x = pathgen.fwd_inputs(B, H, L, d, c["dtype"], seed=0, fox=c["fox"], clip=c["clip"], device="cuda")
+    out, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], return_lse=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    dout = torch.randn(x["q"].shape, generator=g, device="cuda").to(x["q"].dtype)
+    ws = torch.empty(pa.bwd_workspace_size(B, H, L, d, x["q"].dtype), device="cuda", dtype=torch.uint8)
+    grads = (torch.empty_like(x["q"]), torch.empty_like(x["q"]), torch.empty_like(x["q"]), torch.empty_like(x["q"]),
+             torch.empty_like(x["beta"]), torch.empty_like(x["beta"]) if x["logf"] is not None else None)
+    call = lambda: pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out, lse, dout, workspace=ws,
+                          grads=grads)
+    for _ in range(warmup):
+        call()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    heads_per_pass = ws.numel() // pa.bwd_workspace_size(1, 1, L, d, x["q"].dtype)
+    del x, out, lse, dout, ws, grads
+    torch.cuda.empty_cache()
+    flops = 8.0 * B * H * L * L * d
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": name + " backward", "ms_per_step": round(ms, 3), "flop_per_step": flops,
+            "TFLOP_per_s": round(tf, 2), "steps": steps,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_FP32_TFLOPS, 4), "traffic": None},
+            "heads_per_workspace_pass": int(heads_per_pass),
+            "tokens_per_s": round(B * L / (ms * 1e-3))}
+
+
 def counter_run(fwd_steps=2, dec_steps=2):
     """No timing: the kernels a hardware-counter pass reads.  First a plain
     device copy of COPY_BYTES (read and written once each, the calibration of
@@ -373,6 +425,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline budget; 0 skips it")
     ap.add_argument("--sweep-steps", type=int, default=5, help="timed steps per other forward workload; 0 skips them")
+    ap.add_argument("--backward-steps", type=int, default=3, help="timed backward passes; 0 skips them")
+    ap.add_argument("--backward-only", action="store_true", help="only the backward leg (for kernel traces)")
     ap.add_argument("--counter-run", action="store_true",
                     help="no timing: a calibration copy plus a few forward and decode steps, for rocprofv3 --pmc")
     args = ap.parse_args()
@@ -389,6 +443,9 @@ def main():
     torch.cuda.set_device(0)
     if args.counter_run:
         counter_run()
+        return
+    if args.backward_only:
+        print(json.dumps({"backward": bench_backward(max(1, args.backward_steps), 1)}), flush=True)
         return
     log("forward: %s, %d warm-up + %d timed steps" % (FWD_WORKLOAD, args.warmup, args.steps))
     f = bench_forward(args.steps, args.warmup)
@@ -409,6 +466,11 @@ def main():
             (fused["workload"], fused["ms_per_step"], fused["plain_forward_ms_per_step"]))
         log("fox workload, skipping negligible blocks: %.3f ms/step (full walk %.3f ms)" %
             (fox_skip["ms_per_step"], fox_skip["full_walk_ms_per_step"]))
+    bwd = None
+    if args.backward_steps > 0:
+        bwd = bench_backward(args.backward_steps, 1)
+        log("backward: %.2f ms/step, %.1f TFLOP/s (%.1f%% of the fp32 matrix peak)" %
+            (bwd["ms_per_step"], bwd["TFLOP_per_s"], 100 * bwd["roofline"]["frac"]))
     cpu = None
     if args.cpu_seconds > 0:
         log("cpu baseline: oracle, ~%.0f s" % args.cpu_seconds)
@@ -454,6 +516,7 @@ def main():
         "other_workloads": sweep,
         "fox_skip_negligible": fox_skip,
         "fused_producer": fused,
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
