@@ -101,6 +101,26 @@ __device__ __forceinline__ void g2l(float *buf, const float *g, int tid) {
         d[0] = x[0]; d[1] = x[1]; d[2] = x[2]; d[3] = x[3];
     }
 }
+// One thread's share of a 64x64 fp32 tile, so the next step's tiles can be
+// fetched from global memory while the current step computes.
+struct Stage {
+    f32x4 v[kC * kD / 4 / kT];
+};
+__device__ __forceinline__ void gload(Stage &t, const float *g, int tid) {
+#pragma unroll
+    for (int u = 0; u < kC * kD / 4 / kT; ++u) {
+        const int e = tid + u * kT, r = e >> 4, c = (e & 15) * 4;
+        t.v[u] = *reinterpret_cast<const f32x4 *>(g + r * kD + c);
+    }
+}
+__device__ __forceinline__ void lstore(float *buf, const Stage &t, int tid) {
+#pragma unroll
+    for (int u = 0; u < kC * kD / 4 / kT; ++u) {
+        const int e = tid + u * kT, r = e >> 4, c = (e & 15) * 4;
+        float *d = buf + r * kP + c;
+        d[0] = t.v[u][0]; d[1] = t.v[u][1]; d[2] = t.v[u][2]; d[3] = t.v[u][3];
+    }
+}
 __device__ __forceinline__ void zero_lds(float *buf, int tid) {
     for (int e = tid; e < kTile; e += kT) buf[e] = 0.f;
 }
@@ -320,9 +340,12 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
             reinterpret_cast<f32x4 *>(dst)[e] = reinterpret_cast<const f32x4 *>(src)[e];
     }
     if (tid == 0) MID[pair_index(I, I - 1)] = 0.f;
+    Stage rT, rQ, rK, rV;
+    if (I - 1 >= 1) gload(rT, TT + (int64_t)(I - 1) * kD * kD, tid);
     for (int J = I - 1; J >= 1; --J) {
-        g2l(bT, TT + (int64_t)J * kD * kD, tid);
+        lstore(bT, rT, tid);
         __syncthreads();
+        if (J - 1 >= 1) gload(rT, TT + (int64_t)(J - 1) * kD * kD, tid);  // next step's transition
         f32x16 acc = zero16();
         mm(acc, nat(bQt), tr(bT), lane, wave);  // q~^(J-1) = T_J q~^(J) (rows: Q~ T^T)
         __syncthreads();
@@ -340,17 +363,29 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
     }
     f32x16 accG = zero16();
     float rsum = 0.f;
-    __syncthreads();
+    __syncthreads();  // the down phase's stores of q~ and the gate sums are visible below
+    gload(rQ, QS + pair_index(I, 0) * kC * kD, tid);
+    gload(rK, KH, tid);
+    gload(rV, VF, tid);
+    float rck = tid < kC ? ((const float *)(ws + ly.ckk))[tid] : 0.f, rmid = MID[pair_index(I, 0)];
     for (int J = 0; J < I; ++J) {
         const int64_t p = pair_index(I, J);
-        g2l(bQt, QS + p * kC * kD, tid);
-        g2l(bK, KH + (int64_t)J * kC * kD, tid);
-        g2l(bV, VF + (int64_t)J * kC * kD, tid);
-        if (J >= 1) g2l(bT, TT + (int64_t)J * kD * kD, tid);
-        if (tid < kC) sCk[tid] = ((const float *)(ws + ly.ckk))[J * kC + tid];
-        const float midJ = MID[p];
+        lstore(bQt, rQ, tid);
+        lstore(bK, rK, tid);
+        lstore(bV, rV, tid);
+        if (J >= 1) lstore(bT, rT, tid);
+        if (tid < kC) sCk[tid] = rck;
+        const float midJ = rmid;
         if (J >= 1) acc2g(GS + p * kC * kD, accG, lane, wave);  // G^(J-1) for the key-major walk
         __syncthreads();
+        if (J + 1 < I) {  // next step's tiles, in flight while this step computes
+            gload(rQ, QS + (p + 1) * kC * kD, tid);
+            gload(rK, KH + (int64_t)(J + 1) * kC * kD, tid);
+            gload(rV, VF + (int64_t)(J + 1) * kC * kD, tid);
+            gload(rT, TT + (int64_t)(J + 1) * kD * kD, tid);
+            if (tid < kC) rck = ((const float *)(ws + ly.ckk))[(J + 1) * kC + tid];
+            rmid = MID[p + 1];
+        }
         f32x16 s = zero16(), dp = zero16();
         mm(s, nat(bQt), tr(bK), lane, wave);
         mm(dp, nat(bDO), tr(bV), lane, wave);
@@ -401,18 +436,31 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
     if (tid < kC) sCk[tid] = ((const float *)(ws + ly.ckk))[J * kC + tid];
     f32x16 dV = zero16(), dK = zero16(), dT = zero16();
     float csum = 0.f, mid = 0.f;
-    for (int I = J + 1; I < nb; ++I) {
+    Stage rQ, rO, rG;
+    float rl2 = 0.f, rdd = 0.f, rcq = 0.f;
+    auto fetch = [&](int I) {
         const int64_t p = pair_index(I, J);
-        const int row0 = I * kC;
-        g2l(bQt, QS + p * kC * kD, tid);
-        g2l(bDO, (const float *)(ws + ly.dof) + row0 * kD, tid);
-        if (J >= 1) g2l(bG, GS + p * kC * kD, tid);
+        gload(rQ, QS + p * kC * kD, tid);
+        gload(rO, (const float *)(ws + ly.dof) + (int64_t)I * kC * kD, tid);
+        if (J >= 1) gload(rG, GS + p * kC * kD, tid);
         if (tid < kC) {
-            sL2[tid] = ((const float *)(ws + ly.l2))[row0 + tid];
-            sDD[tid] = ((const float *)(ws + ly.dd))[row0 + tid];
-            sCq[tid] = ((const float *)(ws + ly.clq))[row0 + tid];
+            rl2 = ((const float *)(ws + ly.l2))[I * kC + tid];
+            rdd = ((const float *)(ws + ly.dd))[I * kC + tid];
+            rcq = ((const float *)(ws + ly.clq))[I * kC + tid];
+        }
+    };
+    fetch(J + 1);
+    for (int I = J + 1; I < nb; ++I) {
+        lstore(bQt, rQ, tid);
+        lstore(bDO, rO, tid);
+        if (J >= 1) lstore(bG, rG, tid);
+        if (tid < kC) {
+            sL2[tid] = rl2;
+            sDD[tid] = rdd;
+            sCq[tid] = rcq;
         }
         __syncthreads();
+        if (I + 1 < nb) fetch(I + 1);  // next step's tiles, in flight while this step computes
         f32x16 s = zero16(), dp = zero16();
         mm(s, nat(bQt), tr(bK), lane, wave);
         mm(dp, nat(bDO), tr(bV), lane, wave);
