@@ -11,7 +11,7 @@ namespace path {
 // a query block I and an earlier key block J, pair index I (I - 1) / 2 + J).
 struct BwdLayout {
     int64_t qh, kh, vf, dof;  // [Lp, 64]: block-adjusted q and k, v and do as fp32
-    int64_t tt, ee;           // [nb, 64, 64]: block transitions, scale * dS of the diagonal blocks
+    int64_t tt, ttt, ee;      // [nb, 64, 64]: block transitions and their transposes, scale * dS of the diagonal blocks
     int64_t dvd, dqo, dko, dvo;  // [Lp, 64]: diagonal value gradient; walk outputs dq^, dk^, dv
     int64_t dt;               // [nb, 64, 64]: gradient of each block transition
     int64_t l2, dd, clq, ckk;  // [Lp]: lse in log2 units, do.o - dlse, gate prefix terms of rows / keys

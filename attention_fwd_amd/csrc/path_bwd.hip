@@ -48,7 +48,7 @@ namespace {
 
 constexpr int kC = 64;   // tokens per block
 constexpr int kD = 64;   // head dimension
-constexpr int kP = 65;   // LDS row stride of a 64x64 fp32 tile (odd: conflict-free rows and columns)
+constexpr int kP = 68;   // LDS row stride of a 64x64 fp32 tile: rows 16-byte aligned, columns conflict-free
 constexpr int kT = 256;  // threads per workgroup (4 waves)
 constexpr int kTile = kC * kP;
 
@@ -61,13 +61,33 @@ __device__ __forceinline__ LMat nat(const float *p) { return {p, kP, 1}; }
 __device__ __forceinline__ LMat tr(const float *p) { return {p, 1, kP}; }
 
 // acc += A * B for 64x64 operands; wave w owns the 32x32 output tile at rows
-// 32 (w >> 1), columns 32 (w & 1).
+// 32 (w >> 1), columns 32 (w & 1).  The contraction runs in eight groups of
+// eight k; in group g, MFMA s (0..3) takes k = 8g + 4h + s from lane half h,
+// the same order for both operands.  An operand whose k index is contiguous
+// in LDS (A stored by rows, B stored by columns) is then read with one 16-byte
+// load per four MFMAs; otherwise with four single loads, whose 32 lanes walk
+// a row and so hit distinct banks.
 __device__ __forceinline__ void mm(f32x16 &acc, LMat A, LMat B, int lane, int wave) {
     const int r = 32 * (wave >> 1) + (lane & 31), c = 32 * (wave & 1) + (lane & 31), h = lane >> 5;
-    const float *pa = A.p + r * A.rs + h * A.cs, *pb = B.p + c * B.cs + h * B.rs;
-#pragma unroll 16
-    for (int k = 0; k < 64; k += 2)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[k * A.cs], pb[k * B.rs], acc, 0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        const int k0 = 8 * g + 4 * h;
+        f32x4 a, b;
+        if (A.cs == 1) {
+            a = *reinterpret_cast<const f32x4 *>(A.p + r * A.rs + k0);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) a[t] = A.p[r * A.rs + (k0 + t) * A.cs];
+        }
+        if (B.rs == 1) {
+            b = *reinterpret_cast<const f32x4 *>(B.p + c * B.cs + k0);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) b[t] = B.p[(k0 + t) * B.rs + c * B.cs];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], acc, 0, 0, 0);
+    }
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -96,9 +116,7 @@ __device__ __forceinline__ void g2l(float *buf, const float *g, int tid) {
 #pragma unroll
     for (int e = tid; e < kC * kD / 4; e += kT) {
         const int r = e >> 4, c = (e & 15) * 4;
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(g + r * kD + c);
-        float *d = buf + r * kP + c;
-        d[0] = x[0]; d[1] = x[1]; d[2] = x[2]; d[3] = x[3];
+        *reinterpret_cast<f32x4 *>(buf + r * kP + c) = *reinterpret_cast<const f32x4 *>(g + r * kD + c);
     }
 }
 // One thread's share of a 64x64 fp32 tile, so the next step's tiles can be
@@ -117,8 +135,7 @@ __device__ __forceinline__ void lstore(float *buf, const Stage &t, int tid) {
 #pragma unroll
     for (int u = 0; u < kC * kD / 4 / kT; ++u) {
         const int e = tid + u * kT, r = e >> 4, c = (e & 15) * 4;
-        float *d = buf + r * kP + c;
-        d[0] = t.v[u][0]; d[1] = t.v[u][1]; d[2] = t.v[u][2]; d[3] = t.v[u][3];
+        *reinterpret_cast<f32x4 *>(buf + r * kP + c) = t.v[u];
     }
 }
 __device__ __forceinline__ void zero_lds(float *buf, int tid) {
@@ -171,7 +188,7 @@ __device__ __forceinline__ void gate_prefix(float *cl, const float *logf, int ro
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
-    __shared__ float sm[9 * kTile + 4 * kC];
+    __shared__ __attribute__((aligned(16))) float sm[9 * kTile + 4 * kC];
     float *bW = sm, *bQ = bW + kTile, *bK = bQ + kTile, *bG = bK + kTile, *bA = bG + kTile, *bQW = bA + kTile,
           *bN = bQW + kTile, *bZ = bN + kTile, *bY = bZ + kTile;
     float *sB = bY + kTile, *sCl = sB + kC, *sL2 = sCl + kC, *sDD = sL2 + kC;
@@ -248,14 +265,17 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     store_lds(bQW, acc, lane, wave, [](int, int, float x) { return x; });
     __syncthreads();
     {
-        float *TT = (float *)(ws + ly.tt) + (int64_t)J * kD * kD;
+        float *TT = (float *)(ws + ly.tt) + (int64_t)J * kD * kD, *TTt = (float *)(ws + ly.ttt) + (int64_t)J * kD * kD;
         acc = zero16();
         mm(acc, tr(bW), nat(bQW), lane, wave);  // T = I - W^T (A W)
+        f32x16 acct = zero16();
+        mm(acct, tr(bQW), nat(bW), lane, wave);  // T^T = I - (A W)^T W
         const int c = acol(lane, wave);
 #pragma unroll
         for (int vv = 0; vv < 16; ++vv) {
             const int r = arow(vv, lane, wave);
             TT[r * kD + c] = (r == c ? 1.f : 0.f) - acc[vv];
+            TTt[r * kD + c] = (r == c ? 1.f : 0.f) - acct[vv];
         }
     }
     // diagonal block: P = exp(scale (Q K^T - Z N^T) + cl_i - cl_j - lse_i) for j <= i
@@ -315,7 +335,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
 // Query-major walk: one workgroup per (query block I >= 1, head); heaviest first.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
-    __shared__ float sm[7 * kTile + 4 * kC];
+    __shared__ __attribute__((aligned(16))) float sm[7 * kTile + 4 * kC];
     float *bQt = sm, *bT = bQt + kTile, *bK = bT + kTile, *bV = bK + kTile, *bDO = bV + kTile, *bG = bDO + kTile,
           *bS = bG + kTile;
     float *sL2 = bS + kTile, *sDD = sL2 + kC, *sCq = sDD + kC, *sCk = sCq + kC;
@@ -324,7 +344,8 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
     const int gl = blockIdx.x % hc, I = nb - 1 - blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
-    const float *TT = (const float *)(ws + ly.tt), *KH = (const float *)(ws + ly.kh), *VF = (const float *)(ws + ly.vf);
+    const float *TT = (const float *)(ws + ly.tt), *TTt = (const float *)(ws + ly.ttt), *KH = (const float *)(ws + ly.kh),
+                *VF = (const float *)(ws + ly.vf);
     const float *tot = (const float *)(ws + ly.tot);
     float *QS = (float *)(ws + ly.qs), *GS = (float *)(ws + ly.gs), *MID = (float *)(ws + ly.mid);
     const float scale = a.scale;
@@ -382,7 +403,7 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
             gload(rQ, QS + (p + 1) * kC * kD, tid);
             gload(rK, KH + (int64_t)(J + 1) * kC * kD, tid);
             gload(rV, VF + (int64_t)(J + 1) * kC * kD, tid);
-            gload(rT, TT + (int64_t)(J + 1) * kD * kD, tid);
+            gload(rT, TTt + (int64_t)(J + 1) * kD * kD, tid);
             if (tid < kC) rck = ((const float *)(ws + ly.ckk))[(J + 1) * kC + tid];
             rmid = MID[p + 1];
         }
@@ -397,27 +418,29 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
         }
         __syncthreads();
         f32x16 gt = zero16(), xs = zero16();
-        if (J >= 1) mm(gt, nat(bG), nat(bT), lane, wave);
+        if (J >= 1) mm(gt, nat(bG), tr(bT), lane, wave);  // bT holds T_J^T here
         mm(xs, nat(bS), nat(bK), lane, wave);
 #pragma unroll
         for (int vv = 0; vv < 16; ++vv) accG[vv] = gt[vv] + scale * xs[vv];
-        if (tid < kC) {
+        {   // row sums of dS: four lanes per row, sixteen columns each
+            const f32x4 *row = reinterpret_cast<const f32x4 *>(bS + (tid >> 2) * kP + (tid & 3) * 16);
             float t = 0.f;
-            for (int cc = 0; cc < kC; ++cc) t += bS[tid * kP + cc];
-            rsum += t;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) t += (row[u][0] + row[u][1]) + (row[u][2] + row[u][3]);
+            rsum += sum4(t);
         }
         __syncthreads();
         store_lds(bG, accG, lane, wave, [](int, int, float x) { return x; });
     }
     acc2g((float *)(ws + ly.dqo) + row0 * kD, accG, lane, wave);
-    if (tid < kC) ((float *)(ws + ly.rso))[row0 + tid] = rsum;
+    if ((tid & 3) == 0) ((float *)(ws + ly.rso))[row0 + (tid >> 2)] = rsum;
 }
 
 // ---------------------------------------------------------------------------
 // Key-major walk: one workgroup per (key block J <= nb-2, head); heaviest first.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
-    __shared__ float sm[7 * kTile + 4 * kC];
+    __shared__ __attribute__((aligned(16))) float sm[7 * kTile + 4 * kC];
     float *bK = sm, *bV = bK + kTile, *bQt = bV + kTile, *bDO = bQt + kTile, *bG = bDO + kTile, *bP = bG + kTile,
           *bS = bP + kTile;
     float *sL2 = bS + kTile, *sDD = sL2 + kC, *sCq = sDD + kC, *sCk = sCq + kC;
@@ -468,17 +491,19 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
         for (int vv = 0; vv < 16; ++vv) {
             const int r = arow(vv, lane, wave);
             const float P = fast_exp2((scale * s[vv] + sCq[r] + sCk[c] + mid) * kLog2e - sL2[r]);
-            bP[r * kP + c] = P;
-            bS[r * kP + c] = P * (dp[vv] - sDD[r]);
+            bP[c * kP + r] = P;                      // P^T
+            bS[c * kP + r] = P * (dp[vv] - sDD[r]);  // dS^T
         }
         __syncthreads();
-        mm(dV, tr(bP), nat(bDO), lane, wave);
-        mm(dK, tr(bS), nat(bQt), lane, wave);
+        mm(dV, nat(bP), nat(bDO), lane, wave);
+        mm(dK, nat(bS), nat(bQt), lane, wave);
         if (J >= 1) mm(dT, tr(bG), nat(bQt), lane, wave);
-        if (tid < kC) {
+        {   // column sums of dS (rows of dS^T): four lanes per row
+            const f32x4 *row = reinterpret_cast<const f32x4 *>(bS + (tid >> 2) * kP + (tid & 3) * 16);
             float t = 0.f;
-            for (int r = 0; r < kC; ++r) t += bS[r * kP + tid];
-            csum += t;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) t += (row[u][0] + row[u][1]) + (row[u][2] + row[u][3]);
+            csum += sum4(t);
         }
         mid += tot[I];
         __syncthreads();
@@ -489,7 +514,7 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
     acc2g((float *)(ws + ly.dko) + row0 * kD, dK, lane, wave);
     acc2g((float *)(ws + ly.dvo) + row0 * kD, dV, lane, wave);
     acc2g((float *)(ws + ly.dt) + (int64_t)J * kD * kD, dT, lane, wave);
-    if (tid < kC) ((float *)(ws + ly.cso))[row0 + tid] = csum;
+    if ((tid & 3) == 0) ((float *)(ws + ly.cso))[row0 + (tid >> 2)] = csum;
 }
 
 // ---------------------------------------------------------------------------
@@ -507,7 +532,7 @@ __device__ __forceinline__ void acc2out(T *g, const f32x16 &acc, int row0, int L
 
 template <typename T>
 __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
-    __shared__ float sm[9 * kTile + 2 * kC];
+    __shared__ __attribute__((aligned(16))) float sm[9 * kTile + 2 * kC];
     float *bW = sm, *bQ = bW + kTile, *bK = bQ + kTile, *bX = bK + kTile, *bA = bX + kTile, *bQW = bA + kTile,
           *b6 = bQW + kTile, *bN = b6 + kTile, *b8 = bN + kTile;
     float *sB = b8 + kTile, *sRed = sB + kC;
@@ -733,6 +758,7 @@ BwdLayout bwd_layout(int L) {
     };
     const int64_t tile = Lp * kD * 4, rows = Lp * 4;
     ly.qh = take(tile); ly.kh = take(tile); ly.vf = take(tile); ly.dof = take(tile); ly.tt = take(nb * kD * kD * 4);
+    ly.ttt = take(nb * kD * kD * 4);
     ly.ee = take(nb * kC * kC * 4); ly.dvd = take(tile); ly.dqo = take(tile); ly.dko = take(tile); ly.dvo = take(tile);
     ly.dt = take(nb * kD * kD * 4);
     ly.l2 = take(rows); ly.dd = take(rows); ly.clq = take(rows); ly.ckk = take(rows); ly.rsd = take(rows);
