@@ -36,8 +36,8 @@
 //     per-token adjoint dc_t = rowsum_t(dS) - colsum_t(dS);
 //   gate: dlogf_t = sum_{t' >= t} dc_t' (one workgroup per head).
 // Every contraction is a 64x64x64 fp32 product on the matrix cores
-// (v_mfma_f32_32x32x2f32) with operands in LDS, so the gradients are fp32
-// for either input type.  Head dimension 64.
+// (v_mfma_f32_16x16x4f32, eight waves sharing each product) with operands in
+// LDS, so the gradients are fp32 for either input type.  Head dimension 64.
 #include <hip/hip_runtime.h>
 
 #include "path_bwd.h"
@@ -49,7 +49,7 @@ namespace {
 constexpr int kC = 64;   // tokens per block
 constexpr int kD = 64;   // head dimension
 constexpr int kP = 68;   // LDS row stride of a 64x64 fp32 tile: rows 16-byte aligned, columns conflict-free
-constexpr int kT = 256;  // threads per workgroup (4 waves)
+constexpr int kT = 512;  // threads per workgroup (8 waves, two per SIMD)
 constexpr int kTile = kC * kP;
 
 // A 64x64 fp32 matrix in LDS; element (r, c) at p[r * rs + c * cs].
@@ -60,53 +60,65 @@ struct LMat {
 __device__ __forceinline__ LMat nat(const float *p) { return {p, kP, 1}; }
 __device__ __forceinline__ LMat tr(const float *p) { return {p, 1, kP}; }
 
-// acc += A * B for 64x64 operands; wave w owns the 32x32 output tile at rows
-// 32 (w >> 1), columns 32 (w & 1).  The contraction runs in eight groups of
-// eight k; in group g, MFMA s (0..3) takes k = 8g + 4h + s from lane half h,
-// the same order for both operands.  An operand whose k index is contiguous
-// in LDS (A stored by rows, B stored by columns) is then read with one 16-byte
-// load per four MFMAs; otherwise with four single loads, whose 32 lanes walk
-// a row and so hit distinct banks.
-__device__ __forceinline__ void mm(f32x16 &acc, LMat A, LMat B, int lane, int wave) {
-    const int r = 32 * (wave >> 1) + (lane & 31), c = 32 * (wave & 1) + (lane & 31), h = lane >> 5;
+// acc += A * B for 64x64 operands on v_mfma_f32_16x16x4f32.  Wave w owns rows
+// 16 (w >> 1) .. +16 and columns 32 (w & 1) .. +32 of the output as two 16x16
+// tiles (accumulator elements 0-3 and 4-7), so all eight waves share every
+// product and each SIMD holds two waves.  The contraction runs in four
+// blocks of sixteen k; in block g, MFMA t (0..3) takes k = 16g + 4q + t from
+// lane group q = lane / 16, the same order for both operands.  An operand
+// whose k index is contiguous in LDS (A stored by rows, B stored by columns)
+// is read with one 16-byte load per four MFMAs; otherwise with four single
+// loads, whose sixteen lanes walk a row and so hit distinct banks.
+__device__ __forceinline__ void mm(f32x8 &acc, LMat A, LMat B, int lane, int wave) {
+    const int r = 16 * (wave >> 1) + (lane & 15), c0 = 32 * (wave & 1) + (lane & 15), q = lane >> 4;
+    f32x4 lo = acc.lo, hi = acc.hi;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-        const int k0 = 8 * g + 4 * h;
-        f32x4 a, b;
+    for (int g = 0; g < 4; ++g) {
+        const int k0 = 16 * g + 4 * q;
+        f32x4 x, y0, y1;
         if (A.cs == 1) {
-            a = *reinterpret_cast<const f32x4 *>(A.p + r * A.rs + k0);
+            x = *reinterpret_cast<const f32x4 *>(A.p + r * A.rs + k0);
         } else {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) a[t] = A.p[r * A.rs + (k0 + t) * A.cs];
+            for (int t = 0; t < 4; ++t) x[t] = A.p[r * A.rs + (k0 + t) * A.cs];
         }
         if (B.rs == 1) {
-            b = *reinterpret_cast<const f32x4 *>(B.p + c * B.cs + k0);
+            y0 = *reinterpret_cast<const f32x4 *>(B.p + c0 * B.cs + k0);
+            y1 = *reinterpret_cast<const f32x4 *>(B.p + (c0 + 16) * B.cs + k0);
         } else {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) b[t] = B.p[(k0 + t) * B.rs + c * B.cs];
+            for (int t = 0; t < 4; ++t) {
+                y0[t] = B.p[(k0 + t) * B.rs + c0 * B.cs];
+                y1[t] = B.p[(k0 + t) * B.rs + (c0 + 16) * B.cs];
+            }
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], acc, 0, 0, 0);
+        for (int t = 0; t < 4; ++t) {
+            lo = __builtin_amdgcn_mfma_f32_16x16x4f32(x[t], y0[t], lo, 0, 0, 0);
+            hi = __builtin_amdgcn_mfma_f32_16x16x4f32(x[t], y1[t], hi, 0, 0, 0);
+        }
     }
+    acc.lo = lo;
+    acc.hi = hi;
 }
 
-__device__ __forceinline__ f32x16 zero16() {
-    f32x16 z;
+__device__ __forceinline__ f32x8 zero8() {
+    f32x8 z;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) z[v] = 0.f;
+    for (int v = 0; v < 8; ++v) z[v] = 0.f;
     return z;
 }
 
-// Row / column of accumulator register v of this lane.
-__device__ __forceinline__ int arow(int v, int lane, int wave) { return 32 * (wave >> 1) + acc_row(v, lane >> 5); }
-__device__ __forceinline__ int acol(int lane, int wave) { return 32 * (wave & 1) + (lane & 31); }
+// Row / column of accumulator element v (0..7) of this lane: a 16x16 MFMA
+// tile holds (row, col) = (4 (lane / 16) + i, lane % 16) in register i.
+__device__ __forceinline__ int arow(int v, int lane, int wave) { return 16 * (wave >> 1) + 4 * (lane >> 4) + (v & 3); }
+__device__ __forceinline__ int acol(int v, int lane, int wave) { return 32 * (wave & 1) + 16 * (v >> 2) + (lane & 15); }
 
 template <typename F>
-__device__ __forceinline__ void store_lds(float *buf, const f32x16 &acc, int lane, int wave, F f) {
-    const int c = acol(lane, wave);
+__device__ __forceinline__ void store_lds(float *buf, const f32x8 &acc, int lane, int wave, F f) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int r = arow(v, lane, wave);
+    for (int v = 0; v < 8; ++v) {
+        const int r = arow(v, lane, wave), c = acol(v, lane, wave);
         buf[r * kP + c] = f(r, c, acc[v]);
     }
 }
@@ -141,10 +153,9 @@ __device__ __forceinline__ void lstore(float *buf, const Stage &t, int tid) {
 __device__ __forceinline__ void zero_lds(float *buf, int tid) {
     for (int e = tid; e < kTile; e += kT) buf[e] = 0.f;
 }
-__device__ __forceinline__ void acc2g(float *g, const f32x16 &acc, int lane, int wave) {
-    const int c = acol(lane, wave);
+__device__ __forceinline__ void acc2g(float *g, const f32x8 &acc, int lane, int wave) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) g[arow(v, lane, wave) * kD + c] = acc[v];
+    for (int v = 0; v < 8; ++v) g[arow(v, lane, wave) * kD + acol(v, lane, wave)] = acc[v];
 }
 
 // Input tensor rows [row0, row0 + 64) of one head (rows >= L read as 0) -> LDS fp32.
@@ -210,55 +221,55 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
         sL2[tid] = i < L ? a.lse[hoff + i] * kLog2e : 0.f;
     }
     gate_prefix(sCl, a.logf ? a.logf + hoff : nullptr, row0, L, tid);
-    {   // D_i = do_i . o_i - dlse_i: four lanes per row, 16 columns each
-        const int r = tid >> 2, c0 = (tid & 3) * 16, i = row0 + r;
+    {   // D_i = do_i . o_i - dlse_i: eight lanes per row, 8 columns each
+        const int r = tid >> 3, c0 = (tid & 7) * 8, i = row0 + r;
         float s = 0.f;
         if (i < L)
-            for (int c = c0; c < c0 + 16; ++c)
+#pragma unroll
+            for (int c = c0; c < c0 + 8; ++c)
                 s += Elem<T>::to_f32(dout[(int64_t)i * kD + c]) * Elem<T>::to_f32(o[(int64_t)i * kD + c]);
-        s = sum4(s);
-        if ((tid & 3) == 0) sDD[r] = i < L ? s - (a.dlse ? a.dlse[hoff + i] : 0.f) : 0.f;
+        s = sum8(s);
+        if ((tid & 7) == 0) sDD[r] = i < L ? s - (a.dlse ? a.dlse[hoff + i] : 0.f) : 0.f;
     }
     __syncthreads();
-    f32x16 acc = zero16();
+    f32x8 acc = zero8();
     mm(acc, nat(bW), tr(bW), lane, wave);  // G = W W^T
     store_lds(bG, acc, lane, wave, [](int, int, float x) { return x; });
     __syncthreads();
     unit_upper_inverse(bA, bG, sB, tid);
     __syncthreads();
     for (int e = tid; e < kC * kC; e += kT) bA[(e >> 6) * kP + (e & 63)] *= sB[e & 63];  // A = X diag(beta)
-    acc = zero16();
+    acc = zero8();
     mm(acc, nat(bQ), tr(bW), lane, wave);  // Q W^T, keep r <= i
     store_lds(bQW, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });
-    acc = zero16();
+    acc = zero8();
     mm(acc, nat(bK), tr(bW), lane, wave);  // N = K W^T, keep r > j
     store_lds(bN, acc, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });
     __syncthreads();
-    acc = zero16();
+    acc = zero8();
     mm(acc, nat(bQW), tr(bA), lane, wave);  // Z = QWm A^T
     store_lds(bZ, acc, lane, wave, [](int, int, float x) { return x; });
-    acc = zero16();
+    acc = zero8();
     mm(acc, nat(bN), nat(bA), lane, wave);  // Y = N A
     store_lds(bY, acc, lane, wave, [](int, int, float x) { return x; });
     __syncthreads();
     float *QH = (float *)(ws + ly.qh) + row0 * kD, *KH = (float *)(ws + ly.kh) + row0 * kD;
     {
-        const int c = acol(lane, wave);
-        acc = zero16();
+        acc = zero8();
         mm(acc, nat(bZ), nat(bW), lane, wave);  // q^ = q - Z W
 #pragma unroll
-        for (int vv = 0; vv < 16; ++vv) {
-            const int r = arow(vv, lane, wave);
+        for (int vv = 0; vv < 8; ++vv) {
+            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
             QH[r * kD + c] = bQ[r * kP + c] - acc[vv];
         }
-        acc = zero16();
+        acc = zero8();
         mm(acc, nat(bY), nat(bW), lane, wave);  // k^ = k - Y W
 #pragma unroll
-        for (int vv = 0; vv < 16; ++vv) {
-            const int r = arow(vv, lane, wave);
+        for (int vv = 0; vv < 8; ++vv) {
+            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
             KH[r * kD + c] = bK[r * kP + c] - acc[vv];
         }
-        acc = zero16();
+        acc = zero8();
         mm(acc, nat(bA), nat(bW), lane, wave);  // A W (into bQW, free after Z)
     }
     __syncthreads();
@@ -266,28 +277,26 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     __syncthreads();
     {
         float *TT = (float *)(ws + ly.tt) + (int64_t)J * kD * kD, *TTt = (float *)(ws + ly.ttt) + (int64_t)J * kD * kD;
-        acc = zero16();
+        acc = zero8();
         mm(acc, tr(bW), nat(bQW), lane, wave);  // T = I - W^T (A W)
-        f32x16 acct = zero16();
+        f32x8 acct = zero8();
         mm(acct, tr(bQW), nat(bW), lane, wave);  // T^T = I - (A W)^T W
-        const int c = acol(lane, wave);
 #pragma unroll
-        for (int vv = 0; vv < 16; ++vv) {
-            const int r = arow(vv, lane, wave);
+        for (int vv = 0; vv < 8; ++vv) {
+            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
             TT[r * kD + c] = (r == c ? 1.f : 0.f) - acc[vv];
             TTt[r * kD + c] = (r == c ? 1.f : 0.f) - acct[vv];
         }
     }
     // diagonal block: P = exp(scale (Q K^T - Z N^T) + cl_i - cl_j - lse_i) for j <= i
-    f32x16 sQK = zero16(), sZN = zero16();
+    f32x8 sQK = zero8(), sZN = zero8();
     mm(sQK, nat(bQ), tr(bK), lane, wave);
     mm(sZN, nat(bZ), tr(bN), lane, wave);
     __syncthreads();  // bG, bY free: P -> bG, v -> bY, do -> bA
     {
-        const int c = acol(lane, wave);
 #pragma unroll
-        for (int vv = 0; vv < 16; ++vv) {
-            const int r = arow(vv, lane, wave);
+        for (int vv = 0; vv < 8; ++vv) {
+            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
             const float s = (scale * (sQK[vv] - sZN[vv]) + (sCl[r] - sCl[c])) * kLog2e - sL2[r];
             bG[r * kP + c] = c <= r ? fast_exp2(s) : 0.f;
         }
@@ -295,7 +304,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     in2l(bY, v, row0, L, tid);
     in2l(bA, dout, row0, L, tid);
     __syncthreads();
-    acc = zero16();
+    acc = zero8();
     mm(acc, nat(bA), tr(bY), lane, wave);  // dP = dO V^T
     store_lds(bZ, acc, lane, wave, [&](int r, int c, float x) { return bG[r * kP + c] * (x - sDD[r]); });
     __syncthreads();
@@ -307,7 +316,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
             VF[e] = bY[(e >> 6) * kP + (e & 63)];
             DOF[e] = bA[(e >> 6) * kP + (e & 63)];
         }
-        acc = zero16();
+        acc = zero8();
         mm(acc, tr(bG), nat(bA), lane, wave);  // diagonal value gradient P^T dO
         acc2g((float *)(ws + ly.dvd) + row0 * kD, acc, lane, wave);
         float *rs = (float *)(ws + ly.rsd) + row0, *cs = (float *)(ws + ly.csd) + row0;
@@ -349,7 +358,7 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
     const float *tot = (const float *)(ws + ly.tot);
     float *QS = (float *)(ws + ly.qs), *GS = (float *)(ws + ly.gs), *MID = (float *)(ws + ly.mid);
     const float scale = a.scale;
-    const int row0 = I * kC, c = acol(lane, wave);
+    const int row0 = I * kC;
 
     // down: q~^(J) for J = I-1 .. 0
     g2l(bQt, (const float *)(ws + ly.qh) + row0 * kD, tid);
@@ -367,7 +376,7 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
         lstore(bT, rT, tid);
         __syncthreads();
         if (J - 1 >= 1) gload(rT, TT + (int64_t)(J - 1) * kD * kD, tid);  // next step's transition
-        f32x16 acc = zero16();
+        f32x8 acc = zero8();
         mm(acc, nat(bQt), tr(bT), lane, wave);  // q~^(J-1) = T_J q~^(J) (rows: Q~ T^T)
         __syncthreads();
         store_lds(bQt, acc, lane, wave, [](int, int, float x) { return x; });
@@ -382,7 +391,7 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
         sDD[tid] = ((const float *)(ws + ly.dd))[row0 + tid];
         sCq[tid] = ((const float *)(ws + ly.clq))[row0 + tid];
     }
-    f32x16 accG = zero16();
+    f32x8 accG = zero8();
     float rsum = 0.f;
     __syncthreads();  // the down phase's stores of q~ and the gate sums are visible below
     gload(rQ, QS + pair_index(I, 0) * kC * kD, tid);
@@ -407,33 +416,32 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
             if (tid < kC) rck = ((const float *)(ws + ly.ckk))[(J + 1) * kC + tid];
             rmid = MID[p + 1];
         }
-        f32x16 s = zero16(), dp = zero16();
+        f32x8 s = zero8(), dp = zero8();
         mm(s, nat(bQt), tr(bK), lane, wave);
         mm(dp, nat(bDO), tr(bV), lane, wave);
 #pragma unroll
-        for (int vv = 0; vv < 16; ++vv) {
-            const int r = arow(vv, lane, wave);
+        for (int vv = 0; vv < 8; ++vv) {
+            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
             const float x = (scale * s[vv] + sCq[r] + sCk[c] + midJ) * kLog2e - sL2[r];
             bS[r * kP + c] = fast_exp2(x) * (dp[vv] - sDD[r]);
         }
         __syncthreads();
-        f32x16 gt = zero16(), xs = zero16();
+        f32x8 gt = zero8(), xs = zero8();
         if (J >= 1) mm(gt, nat(bG), tr(bT), lane, wave);  // bT holds T_J^T here
         mm(xs, nat(bS), nat(bK), lane, wave);
 #pragma unroll
-        for (int vv = 0; vv < 16; ++vv) accG[vv] = gt[vv] + scale * xs[vv];
-        {   // row sums of dS: four lanes per row, sixteen columns each
-            const f32x4 *row = reinterpret_cast<const f32x4 *>(bS + (tid >> 2) * kP + (tid & 3) * 16);
-            float t = 0.f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) t += (row[u][0] + row[u][1]) + (row[u][2] + row[u][3]);
-            rsum += sum4(t);
+        for (int vv = 0; vv < 8; ++vv) accG[vv] = gt[vv] + scale * xs[vv];
+        {   // row sums of dS: eight lanes per row, eight columns each
+            const f32x4 *row = reinterpret_cast<const f32x4 *>(bS + (tid >> 3) * kP + (tid & 7) * 8);
+            const float t = ((row[0][0] + row[0][1]) + (row[0][2] + row[0][3])) +
+                            ((row[1][0] + row[1][1]) + (row[1][2] + row[1][3]));
+            rsum += sum8(t);
         }
         __syncthreads();
         store_lds(bG, accG, lane, wave, [](int, int, float x) { return x; });
     }
     acc2g((float *)(ws + ly.dqo) + row0 * kD, accG, lane, wave);
-    if ((tid & 3) == 0) ((float *)(ws + ly.rso))[row0 + (tid >> 2)] = rsum;
+    if ((tid & 7) == 0) ((float *)(ws + ly.rso))[row0 + (tid >> 3)] = rsum;
 }
 
 // ---------------------------------------------------------------------------
@@ -452,12 +460,11 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
     const float *tot = (const float *)(ws + ly.tot), *QS = (const float *)(ws + ly.qs),
                 *GS = (const float *)(ws + ly.gs);
     const float scale = a.scale;
-    const int c = acol(lane, wave);
 
     g2l(bK, (const float *)(ws + ly.kh) + (int64_t)J * kC * kD, tid);
     g2l(bV, (const float *)(ws + ly.vf) + (int64_t)J * kC * kD, tid);
     if (tid < kC) sCk[tid] = ((const float *)(ws + ly.ckk))[J * kC + tid];
-    f32x16 dV = zero16(), dK = zero16(), dT = zero16();
+    f32x8 dV = zero8(), dK = zero8(), dT = zero8();
     float csum = 0.f, mid = 0.f;
     Stage rQ, rO, rG;
     float rl2 = 0.f, rdd = 0.f, rcq = 0.f;
@@ -484,12 +491,12 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
         }
         __syncthreads();
         if (I + 1 < nb) fetch(I + 1);  // next step's tiles, in flight while this step computes
-        f32x16 s = zero16(), dp = zero16();
+        f32x8 s = zero8(), dp = zero8();
         mm(s, nat(bQt), tr(bK), lane, wave);
         mm(dp, nat(bDO), tr(bV), lane, wave);
 #pragma unroll
-        for (int vv = 0; vv < 16; ++vv) {
-            const int r = arow(vv, lane, wave);
+        for (int vv = 0; vv < 8; ++vv) {
+            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
             const float P = fast_exp2((scale * s[vv] + sCq[r] + sCk[c] + mid) * kLog2e - sL2[r]);
             bP[c * kP + r] = P;                      // P^T
             bS[c * kP + r] = P * (dp[vv] - sDD[r]);  // dS^T
@@ -498,34 +505,32 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
         mm(dV, nat(bP), nat(bDO), lane, wave);
         mm(dK, nat(bS), nat(bQt), lane, wave);
         if (J >= 1) mm(dT, tr(bG), nat(bQt), lane, wave);
-        {   // column sums of dS (rows of dS^T): four lanes per row
-            const f32x4 *row = reinterpret_cast<const f32x4 *>(bS + (tid >> 2) * kP + (tid & 3) * 16);
-            float t = 0.f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) t += (row[u][0] + row[u][1]) + (row[u][2] + row[u][3]);
-            csum += sum4(t);
+        {   // column sums of dS (rows of dS^T): eight lanes per row
+            const f32x4 *row = reinterpret_cast<const f32x4 *>(bS + (tid >> 3) * kP + (tid & 7) * 8);
+            const float t = ((row[0][0] + row[0][1]) + (row[0][2] + row[0][3])) +
+                            ((row[1][0] + row[1][1]) + (row[1][2] + row[1][3]));
+            csum += sum8(t);
         }
         mid += tot[I];
         __syncthreads();
     }
     const int row0 = J * kC;
 #pragma unroll
-    for (int vv = 0; vv < 16; ++vv) dK[vv] *= scale;
+    for (int vv = 0; vv < 8; ++vv) dK[vv] *= scale;
     acc2g((float *)(ws + ly.dko) + row0 * kD, dK, lane, wave);
     acc2g((float *)(ws + ly.dvo) + row0 * kD, dV, lane, wave);
     acc2g((float *)(ws + ly.dt) + (int64_t)J * kD * kD, dT, lane, wave);
-    if ((tid & 3) == 0) ((float *)(ws + ly.cso))[row0 + (tid >> 2)] = csum;
+    if ((tid & 7) == 0) ((float *)(ws + ly.cso))[row0 + (tid >> 3)] = csum;
 }
 
 // ---------------------------------------------------------------------------
 // Block backward: one workgroup per (block J, head).
 // ---------------------------------------------------------------------------
 template <typename T>
-__device__ __forceinline__ void acc2out(T *g, const f32x16 &acc, int row0, int L, int lane, int wave) {
-    const int c = acol(lane, wave);
+__device__ __forceinline__ void acc2out(T *g, const f32x8 &acc, int row0, int L, int lane, int wave) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int r = arow(v, lane, wave);
+    for (int v = 0; v < 8; ++v) {
+        const int r = arow(v, lane, wave), c = acol(v, lane, wave);
         if (row0 + r < L) g[(int64_t)(row0 + r) * kD + c] = Elem<T>::from_float(acc[v]);
     }
 }
@@ -550,7 +555,7 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
     in2l(bK, k, row0, L, tid);
     if (tid < kC) sB[tid] = row0 + tid < L ? a.beta[hoff + row0 + tid] : 0.f;
     __syncthreads();
-    f32x16 acc = zero16();
+    f32x8 acc = zero8();
     mm(acc, nat(bW), tr(bW), lane, wave);  // G
     store_lds(b8, acc, lane, wave, id);
     __syncthreads();
@@ -560,19 +565,19 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
         const int r = e >> 6, cc = e & 63;
         bA[r * kP + cc] = bX[r * kP + cc] * sB[cc];
     }
-    acc = zero16();
+    acc = zero8();
     mm(acc, nat(bQ), tr(bW), lane, wave);
     store_lds(bQW, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });
-    acc = zero16();
+    acc = zero8();
     mm(acc, nat(bK), tr(bW), lane, wave);
     store_lds(bN, acc, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });
     __syncthreads();
-    acc = zero16();
+    acc = zero8();
     mm(acc, nat(bQW), tr(bA), lane, wave);  // Z
     store_lds(b6, acc, lane, wave, id);
     g2l(b8, (const float *)(ws + ly.ee) + (int64_t)J * kC * kC, tid);  // E = scale dS of the diagonal block
     __syncthreads();
-    f32x16 dQ = zero16(), dK = zero16(), dZ = zero16(), dN = zero16(), dW = zero16(), dA = zero16();
+    f32x8 dQ = zero8(), dK = zero8(), dZ = zero8(), dN = zero8(), dW = zero8(), dA = zero8();
     mm(dQ, nat(b8), nat(bK), lane, wave);   // E K
     mm(dK, tr(b8), nat(bQ), lane, wave);    // E^T Q
     mm(dZ, nat(b8), nat(bN), lane, wave);   // (E N), negated below
@@ -584,10 +589,9 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
     mm(dZ, nat(b8), tr(bW), lane, wave);    // + dq^ W^T
     mm(dW, tr(b6), nat(b8), lane, wave);    // Z^T dq^ (negated below)
     {
-        const int c = acol(lane, wave);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = arow(v, lane, wave);
+        for (int v = 0; v < 8; ++v) {
+            const int r = arow(v, lane, wave), c = acol(v, lane, wave);
             dQ[v] += b8[r * kP + c];
             dZ[v] = -dZ[v];
             dN[v] = -dN[v];
@@ -599,24 +603,23 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
     else zero_lds(b8, tid);
     __syncthreads();
     {
-        const int c = acol(lane, wave);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) dK[v] += b8[arow(v, lane, wave) * kP + c];
+        for (int v = 0; v < 8; ++v) dK[v] += b8[arow(v, lane, wave) * kP + acol(v, lane, wave)];
     }
-    acc = zero16();
+    acc = zero8();
     mm(acc, nat(b8), tr(bW), lane, wave);  // dY = -dk^ W^T
     store_lds(b6, acc, lane, wave, [](int, int, float x) { return -x; });
-    acc = zero16();
+    acc = zero8();
     mm(acc, tr(bN), nat(b8), lane, wave);  // R = N^T dk^ (into bQ; q is read again later)
     __syncthreads();
     store_lds(bQ, acc, lane, wave, id);
     __syncthreads();
     mm(dN, nat(b6), tr(bA), lane, wave);   // += dY A^T
     mm(dA, tr(bN), nat(b6), lane, wave);   // N^T dY
-    acc = zero16();
+    acc = zero8();
     mm(acc, tr(bA), nat(bQ), lane, wave);  // A^T R = Y^T dk^
 #pragma unroll
-    for (int v = 0; v < 16; ++v) dW[v] -= acc[v];
+    for (int v = 0; v < 8; ++v) dW[v] -= acc[v];
     __syncthreads();
     store_lds(b6, dN, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });  // dKW = dN o [r > j]
     in2l(bQ, q, row0, L, tid);
@@ -626,7 +629,7 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
     __syncthreads();
     store_lds(b6, dZ, lane, wave, id);
     __syncthreads();
-    acc = zero16();
+    acc = zero8();
     mm(acc, nat(b6), nat(bA), lane, wave);  // dQWm = (dZ A) o [r <= i]
     mm(dA, tr(b6), nat(bQW), lane, wave);   // += dZ^T QWm
     store_lds(bN, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });
@@ -636,31 +639,30 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
     __syncthreads();
     if (hasT) {  // T = I - W^T A W
         g2l(b6, (const float *)(ws + ly.dt) + (int64_t)J * kD * kD, tid);
-        acc = zero16();
+        acc = zero8();
         mm(acc, nat(bA), nat(bW), lane, wave);  // A W
         __syncthreads();
         store_lds(bN, acc, lane, wave, id);
-        acc = zero16();
+        acc = zero8();
         mm(acc, nat(bW), nat(b6), lane, wave);  // W dT
         store_lds(bQW, acc, lane, wave, id);
         __syncthreads();
-        acc = zero16();
+        acc = zero8();
         mm(acc, nat(bQW), tr(bW), lane, wave);  // W dT W^T
 #pragma unroll
-        for (int v = 0; v < 16; ++v) dA[v] -= acc[v];
-        acc = zero16();
+        for (int v = 0; v < 8; ++v) dA[v] -= acc[v];
+        acc = zero8();
         mm(acc, nat(bN), tr(b6), lane, wave);   // A W dT^T
         mm(acc, tr(bA), nat(bQW), lane, wave);  // + A^T W dT
 #pragma unroll
-        for (int v = 0; v < 16; ++v) dW[v] -= acc[v];
+        for (int v = 0; v < 8; ++v) dW[v] -= acc[v];
         __syncthreads();
     }
     // A = X diag(beta): dX = dA diag(beta), dbeta_c += sum_r X_rc dA_rc (dA kept on the upper triangle)
     {
-        const int c = acol(lane, wave);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = arow(v, lane, wave);
+        for (int v = 0; v < 8; ++v) {
+            const int r = arow(v, lane, wave), c = acol(v, lane, wave);
             dA[v] = c >= r ? dA[v] : 0.f;
             b6[r * kP + c] = dA[v] * sB[c];
             bQW[r * kP + c] = bX[r * kP + c] * dA[v];
@@ -670,19 +672,18 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
     float dbeta = 0.f;
     if (tid < kC)
         for (int r = 0; r < kC; ++r) dbeta += bQW[r * kP + tid];
-    acc = zero16();
+    acc = zero8();
     mm(acc, tr(bX), nat(b6), lane, wave);  // X^T dX
     __syncthreads();
     store_lds(bN, acc, lane, wave, id);
     __syncthreads();
-    f32x16 dTp = zero16(), G = zero16();
+    f32x8 dTp = zero8(), G = zero8();
     mm(dTp, nat(bN), tr(bX), lane, wave);  // (X^T dX) X^T; dT' is its negative
     mm(G, nat(bW), tr(bW), lane, wave);
     {
-        const int c = acol(lane, wave);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = arow(v, lane, wave);
+        for (int v = 0; v < 8; ++v) {
+            const int r = arow(v, lane, wave), c = acol(v, lane, wave);
             const float t = -dTp[v];
             bQW[r * kP + c] = c > r ? t * G[v] : 0.f;    // dbeta_r += sum_c dT'_rc U_rc
             b6[r * kP + c] = c > r ? sB[r] * t : 0.f;    // dG = diag(beta) dT' on the strict upper triangle
