@@ -14,6 +14,7 @@ struct BwdLayout {
     int64_t tt, ttt, ee;      // [nb, 64, 64]: block transitions and their transposes, scale * dS of the diagonal blocks
     int64_t dvd, dqo, dko, dvo;  // [Lp, 64]: diagonal value gradient; walk outputs dq^, dk^, dv
     int64_t dt;               // [nb, 64, 64]: gradient of each block transition
+    int64_t xx, aa, qwm, nn, zz;  // [nb, 64, 64]: X, A, Q W^T o [r <= i], N, Z of each block (prep -> block backward)
     int64_t l2, dd, clq, ckk;  // [Lp]: lse in log2 units, do.o - dlse, gate prefix terms of rows / keys
     int64_t rsd, csd, rso, cso, dc;  // [Lp]: row / column sums of dS (diagonal, off-diagonal), gate adjoint
     int64_t tot;              // [nb]: gate total of each block

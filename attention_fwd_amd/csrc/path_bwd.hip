@@ -169,17 +169,29 @@ __device__ __forceinline__ void in2l(float *buf, const T *g, int row0, int L, in
 
 __device__ __forceinline__ int64_t pair_index(int I, int J) { return (int64_t)I * (I - 1) / 2 + J; }
 
-// X = (I + diag(beta) su(G))^-1 by back substitution, one column per thread.
+// X = (I + diag(beta) su(G))^-1 by back substitution: eight lanes per column
+// (64 columns x 8 = 512 threads), each summing every eighth term of a row's
+// dot product.  The lanes of a column are one aligned group of eight in one
+// wave, so X[r][c], written by the group's first lane, is read back by the
+// others in program order.
 __device__ __forceinline__ void unit_upper_inverse(float *X, const float *G, const float *beta, int tid) {
-    if (tid < kC) {
-        const int c = tid;
-        for (int r = c + 1; r < kC; ++r) X[r * kP + c] = 0.f;
-        X[c * kP + c] = 1.f;
-        for (int r = c - 1; r >= 0; --r) {
-            float s = 0.f;
-            for (int t = r + 1; t <= c; ++t) s += G[r * kP + t] * X[t * kP + c];
-            X[r * kP + c] = -beta[r] * s;
-        }
+    const int c = tid >> 3, p = tid & 7;
+    for (int r = c + 1 + p; r < kC; r += 8) X[r * kP + c] = 0.f;
+    if (p == 0) X[c * kP + c] = 1.f;
+    for (int r = c - 1; r >= 0; --r) {
+        float s = 0.f;
+        for (int t = r + 1 + p; t <= c; t += 8) s += G[r * kP + t] * X[t * kP + c];
+        s = sum8(s);
+        if (p == 0) X[r * kP + c] = -beta[r] * s;
+    }
+}
+
+// LDS tile -> global fp32 tile [64][64].
+__device__ __forceinline__ void l2g(float *g, const float *buf, int tid) {
+#pragma unroll
+    for (int e = tid; e < kC * kD / 4; e += kT) {
+        const int r = e >> 4, c = (e & 15) * 4;
+        *reinterpret_cast<f32x4 *>(g + r * kD + c) = *reinterpret_cast<const f32x4 *>(buf + r * kP + c);
     }
 }
 
@@ -238,7 +250,16 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     __syncthreads();
     unit_upper_inverse(bA, bG, sB, tid);
     __syncthreads();
-    for (int e = tid; e < kC * kC; e += kT) bA[(e >> 6) * kP + (e & 63)] *= sB[e & 63];  // A = X diag(beta)
+    float *XX = (float *)(ws + ly.xx) + (int64_t)J * kC * kC, *AA = (float *)(ws + ly.aa) + (int64_t)J * kC * kC;
+#pragma unroll
+    for (int e = tid; e < kC * kC / 4; e += kT) {  // keep X, then A = X diag(beta) in place
+        const int r = e >> 4, c = (e & 15) * 4;
+        f32x4 x = *reinterpret_cast<const f32x4 *>(bA + r * kP + c);
+        *reinterpret_cast<f32x4 *>(XX + r * kC + c) = x;
+        x[0] *= sB[c]; x[1] *= sB[c + 1]; x[2] *= sB[c + 2]; x[3] *= sB[c + 3];
+        *reinterpret_cast<f32x4 *>(bA + r * kP + c) = x;
+        *reinterpret_cast<f32x4 *>(AA + r * kC + c) = x;
+    }
     acc = zero8();
     mm(acc, nat(bQ), tr(bW), lane, wave);  // Q W^T, keep r <= i
     store_lds(bQW, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });
@@ -246,6 +267,8 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     mm(acc, nat(bK), tr(bW), lane, wave);  // N = K W^T, keep r > j
     store_lds(bN, acc, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });
     __syncthreads();
+    l2g((float *)(ws + ly.qwm) + (int64_t)J * kC * kC, bQW, tid);
+    l2g((float *)(ws + ly.nn) + (int64_t)J * kC * kC, bN, tid);
     acc = zero8();
     mm(acc, nat(bQW), tr(bA), lane, wave);  // Z = QWm A^T
     store_lds(bZ, acc, lane, wave, [](int, int, float x) { return x; });
@@ -253,6 +276,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     mm(acc, nat(bN), nat(bA), lane, wave);  // Y = N A
     store_lds(bY, acc, lane, wave, [](int, int, float x) { return x; });
     __syncthreads();
+    l2g((float *)(ws + ly.zz) + (int64_t)J * kC * kC, bZ, tid);
     float *QH = (float *)(ws + ly.qh) + row0 * kD, *KH = (float *)(ws + ly.kh) + row0 * kD;
     {
         acc = zero8();
@@ -554,28 +578,16 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
     in2l(bQ, q, row0, L, tid);
     in2l(bK, k, row0, L, tid);
     if (tid < kC) sB[tid] = row0 + tid < L ? a.beta[hoff + row0 + tid] : 0.f;
-    __syncthreads();
-    f32x8 acc = zero8();
-    mm(acc, nat(bW), tr(bW), lane, wave);  // G
-    store_lds(b8, acc, lane, wave, id);
-    __syncthreads();
-    unit_upper_inverse(bX, b8, sB, tid);
-    __syncthreads();
-    for (int e = tid; e < kC * kC; e += kT) {
-        const int r = e >> 6, cc = e & 63;
-        bA[r * kP + cc] = bX[r * kP + cc] * sB[cc];
+    {   // the block's UT quantities, as prep computed them
+        const int64_t o = (int64_t)J * kC * kC;
+        g2l(bX, (const float *)(ws + ly.xx) + o, tid);
+        g2l(bA, (const float *)(ws + ly.aa) + o, tid);
+        g2l(bQW, (const float *)(ws + ly.qwm) + o, tid);
+        g2l(bN, (const float *)(ws + ly.nn) + o, tid);
+        g2l(b6, (const float *)(ws + ly.zz) + o, tid);
+        g2l(b8, (const float *)(ws + ly.ee) + o, tid);  // E = scale dS of the diagonal block
     }
-    acc = zero8();
-    mm(acc, nat(bQ), tr(bW), lane, wave);
-    store_lds(bQW, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });
-    acc = zero8();
-    mm(acc, nat(bK), tr(bW), lane, wave);
-    store_lds(bN, acc, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });
-    __syncthreads();
-    acc = zero8();
-    mm(acc, nat(bQW), tr(bA), lane, wave);  // Z
-    store_lds(b6, acc, lane, wave, id);
-    g2l(b8, (const float *)(ws + ly.ee) + (int64_t)J * kC * kC, tid);  // E = scale dS of the diagonal block
+    f32x8 acc;
     __syncthreads();
     f32x8 dQ = zero8(), dK = zero8(), dZ = zero8(), dN = zero8(), dW = zero8(), dA = zero8();
     mm(dQ, nat(b8), nat(bK), lane, wave);   // E K
@@ -760,6 +772,8 @@ BwdLayout bwd_layout(int L) {
     const int64_t tile = Lp * kD * 4, rows = Lp * 4;
     ly.qh = take(tile); ly.kh = take(tile); ly.vf = take(tile); ly.dof = take(tile); ly.tt = take(nb * kD * kD * 4);
     ly.ttt = take(nb * kD * kD * 4);
+    ly.xx = take(nb * kC * kC * 4); ly.aa = take(nb * kC * kC * 4); ly.qwm = take(nb * kC * kC * 4);
+    ly.nn = take(nb * kC * kC * 4); ly.zz = take(nb * kC * kC * 4);
     ly.ee = take(nb * kC * kC * 4); ly.dvd = take(tile); ly.dqo = take(tile); ly.dko = take(tile); ly.dvo = take(tile);
     ly.dt = take(nb * kD * kD * 4);
     ly.l2 = take(rows); ly.dd = take(rows); ly.clq = take(rows); ly.ckk = take(rows); ly.rsd = take(rows);
