@@ -20,6 +20,7 @@ struct BwdLayout {
     int64_t tot;              // [nb]: gate total of each block
     int64_t mid;              // [np]: gate sum over the blocks strictly between I and J
     int64_t qs, gs;           // [np, 64, 64]: carried queries q~_I^(J) and adjoints G_I^(J-1)
+    int64_t ps, ds;           // [np, 64, 64]: softmax weights P and dS of every pair
     int64_t head;             // bytes per head
 };
 

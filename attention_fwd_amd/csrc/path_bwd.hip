@@ -25,11 +25,11 @@
 //   prep (per block): the quantities above, the diagonal block's dS, its
 //     value gradient, and fp32 copies of v and do;
 //   query-major walk (per query block I): down J = I-1 .. 0 storing q~^(J)
-//     for every pair, then up J = 0 .. I-1 storing G^(J-1) for every pair and
+//     for every pair, then up J = 0 .. I-1 storing G^(J-1), P and dS for every pair and
 //     ending with dq^_I = G^(I-1);
 //   key-major walk (per key block J): over I > J, dV_J += P^T dO_I,
 //     dk^_J += scale dS^T q~, dT_J += G^(J-1)^T q~ -- sums owned by one
-//     workgroup, so no atomics;
+//     workgroup, so no atomics; P and dS come from the query-major walk;
 //   block backward (per block): the matrix-form chain rule through the
 //     formulas above (including the triangular inverse: dT' = -X^T dX X^T)
 //     gives dq, dk, dw, dbeta; dv adds the two value sums; the gate's
@@ -381,6 +381,7 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
                 *VF = (const float *)(ws + ly.vf);
     const float *tot = (const float *)(ws + ly.tot);
     float *QS = (float *)(ws + ly.qs), *GS = (float *)(ws + ly.gs), *MID = (float *)(ws + ly.mid);
+    float *PS = (float *)(ws + ly.ps), *DS = (float *)(ws + ly.ds);
     const float scale = a.scale;
     const int row0 = I * kC;
 
@@ -443,11 +444,17 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
         f32x8 s = zero8(), dp = zero8();
         mm(s, nat(bQt), tr(bK), lane, wave);
         mm(dp, nat(bDO), tr(bV), lane, wave);
+        {
+            float *PSp = PS + p * kC * kC, *DSp = DS + p * kC * kC;
 #pragma unroll
-        for (int vv = 0; vv < 8; ++vv) {
-            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
-            const float x = (scale * s[vv] + sCq[r] + sCk[c] + midJ) * kLog2e - sL2[r];
-            bS[r * kP + c] = fast_exp2(x) * (dp[vv] - sDD[r]);
+            for (int vv = 0; vv < 8; ++vv) {
+                const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
+                const float P = fast_exp2((scale * s[vv] + sCq[r] + sCk[c] + midJ) * kLog2e - sL2[r]);
+                const float dS = P * (dp[vv] - sDD[r]);
+                bS[r * kP + c] = dS;
+                PSp[r * kC + c] = P;  // for the key-major walk
+                DSp[r * kC + c] = dS;
+            }
         }
         __syncthreads();
         f32x8 gt = zero8(), xs = zero8();
@@ -470,72 +477,52 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Key-major walk: one workgroup per (key block J <= nb-2, head); heaviest first.
+// The query-major walk left P, dS, q~ and G of every pair, so this walk only
+// sums over the query blocks: dV_J += P^T dO_I, dk^_J += scale dS^T q~,
+// dT_J += G^(J-1)^T q~, and the column sums of dS for the gate.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) float sm[7 * kTile + 4 * kC];
-    float *bK = sm, *bV = bK + kTile, *bQt = bV + kTile, *bDO = bQt + kTile, *bG = bDO + kTile, *bP = bG + kTile,
-          *bS = bP + kTile;
-    float *sL2 = bS + kTile, *sDD = sL2 + kC, *sCq = sDD + kC, *sCk = sCq + kC;
+    __shared__ __attribute__((aligned(16))) float sm[5 * kTile];
+    float *bQt = sm, *bDO = bQt + kTile, *bG = bDO + kTile, *bP = bG + kTile, *bS = bP + kTile;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nb = a.nb, hc = a.hc;
     const int gl = blockIdx.x % hc, J = blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
-    const float *tot = (const float *)(ws + ly.tot), *QS = (const float *)(ws + ly.qs),
-                *GS = (const float *)(ws + ly.gs);
+    const float *QS = (const float *)(ws + ly.qs), *GS = (const float *)(ws + ly.gs), *PS = (const float *)(ws + ly.ps),
+                *DS = (const float *)(ws + ly.ds), *DOF = (const float *)(ws + ly.dof);
     const float scale = a.scale;
 
-    g2l(bK, (const float *)(ws + ly.kh) + (int64_t)J * kC * kD, tid);
-    g2l(bV, (const float *)(ws + ly.vf) + (int64_t)J * kC * kD, tid);
-    if (tid < kC) sCk[tid] = ((const float *)(ws + ly.ckk))[J * kC + tid];
     f32x8 dV = zero8(), dK = zero8(), dT = zero8();
-    float csum = 0.f, mid = 0.f;
-    Stage rQ, rO, rG;
-    float rl2 = 0.f, rdd = 0.f, rcq = 0.f;
+    float csum = 0.f;
+    Stage rQ, rO, rG, rP, rS;
     auto fetch = [&](int I) {
         const int64_t p = pair_index(I, J);
         gload(rQ, QS + p * kC * kD, tid);
-        gload(rO, (const float *)(ws + ly.dof) + (int64_t)I * kC * kD, tid);
+        gload(rO, DOF + (int64_t)I * kC * kD, tid);
         if (J >= 1) gload(rG, GS + p * kC * kD, tid);
-        if (tid < kC) {
-            rl2 = ((const float *)(ws + ly.l2))[I * kC + tid];
-            rdd = ((const float *)(ws + ly.dd))[I * kC + tid];
-            rcq = ((const float *)(ws + ly.clq))[I * kC + tid];
-        }
+        gload(rP, PS + p * kC * kC, tid);
+        gload(rS, DS + p * kC * kC, tid);
     };
     fetch(J + 1);
     for (int I = J + 1; I < nb; ++I) {
         lstore(bQt, rQ, tid);
         lstore(bDO, rO, tid);
         if (J >= 1) lstore(bG, rG, tid);
-        if (tid < kC) {
-            sL2[tid] = rl2;
-            sDD[tid] = rdd;
-            sCq[tid] = rcq;
-        }
+        lstore(bP, rP, tid);
+        lstore(bS, rS, tid);
         __syncthreads();
         if (I + 1 < nb) fetch(I + 1);  // next step's tiles, in flight while this step computes
-        f32x8 s = zero8(), dp = zero8();
-        mm(s, nat(bQt), tr(bK), lane, wave);
-        mm(dp, nat(bDO), tr(bV), lane, wave);
-#pragma unroll
-        for (int vv = 0; vv < 8; ++vv) {
-            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
-            const float P = fast_exp2((scale * s[vv] + sCq[r] + sCk[c] + mid) * kLog2e - sL2[r]);
-            bP[c * kP + r] = P;                      // P^T
-            bS[c * kP + r] = P * (dp[vv] - sDD[r]);  // dS^T
-        }
-        __syncthreads();
-        mm(dV, nat(bP), nat(bDO), lane, wave);
-        mm(dK, nat(bS), nat(bQt), lane, wave);
+        mm(dV, tr(bP), nat(bDO), lane, wave);
+        mm(dK, tr(bS), nat(bQt), lane, wave);
         if (J >= 1) mm(dT, tr(bG), nat(bQt), lane, wave);
-        {   // column sums of dS (rows of dS^T): eight lanes per row
-            const f32x4 *row = reinterpret_cast<const f32x4 *>(bS + (tid >> 3) * kP + (tid & 7) * 8);
-            const float t = ((row[0][0] + row[0][1]) + (row[0][2] + row[0][3])) +
-                            ((row[1][0] + row[1][1]) + (row[1][2] + row[1][3]));
+        {   // column sums of dS: eight lanes per column, every eighth row
+            const int cc = tid >> 3, p0 = tid & 7;
+            float t = 0.f;
+#pragma unroll
+            for (int r = p0; r < kC; r += 8) t += bS[r * kP + cc];
             csum += sum8(t);
         }
-        mid += tot[I];
         __syncthreads();
     }
     const int row0 = J * kC;
@@ -780,6 +767,7 @@ BwdLayout bwd_layout(int L) {
     ly.csd = take(rows); ly.rso = take(rows); ly.cso = take(rows); ly.dc = take(rows);
     ly.tot = take(nb * 4); ly.mid = take(np * 4);
     ly.qs = take(np * kC * kD * 4); ly.gs = take(np * kC * kD * 4);
+    ly.ps = take(np * kC * kC * 4); ly.ds = take(np * kC * kC * 4);
     ly.head = off;
     return ly;
 }
