@@ -47,6 +47,7 @@ DEC_WORKLOAD = "decode_N32768_bf16"
 SWEEP_WORKLOADS = ["sweep_L1024_d64_bf16", "sweep_L2048_d64_bf16", "sweep_L8192_d64_bf16", "sweep_L4096_d128_bf16",
                    "lm760m_L4096_bf16", "fox_L16384_bf16"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_B32H32L4096_decode_N32768.txt")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_B32H32L4096.txt")
 COPY_BYTES = 1 << 30        # calibration copy of the counter run
 KERNEL_SOURCES = {
     "path_fwd_kernel": ["attention_fwd_amd/csrc/path_fwd.hip", "attention_fwd_amd/csrc/path_common.h",
@@ -54,6 +55,8 @@ KERNEL_SOURCES = {
     "path_decode_kernel": ["attention_fwd_amd/csrc/path_decode.hip", "attention_fwd_amd/csrc/path_common.h"],
     "path_cache_kernel": ["attention_fwd_amd/csrc/path_cache.hip", "attention_fwd_amd/csrc/path_common.h",
                           "attention_fwd_amd/csrc/path_layout.h"],
+    "path_bwd": ["attention_fwd_amd/csrc/path_bwd.hip", "attention_fwd_amd/csrc/path_bwd.h",
+                 "attention_fwd_amd/csrc/path_common.h"],
 }
 
 
@@ -69,12 +72,12 @@ def kernel_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel):
+def read_traffic(kernel, path=TRAFFIC_FILE):
     """HBM bytes per launch of `kernel` from the committed counter summary, if
     the counters were taken on the current kernel source (else None)."""
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
@@ -340,9 +343,11 @@ def bench_backward(steps, warmup, name=FWD_WORKLOAD):
     flops = 8.0 * B * H * L * L * d
     tf = flops / (ms * 1e-3) / 1e12
     return {"workload": name + " backward", "ms_per_step": round(ms, 3), "flop_per_step": flops,
+            "traffic_note": "HBM bytes of one whole backward pass (all kernels, all passes over the workspace)",
             "TFLOP_per_s": round(tf, 2), "steps": steps,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_FP32_TFLOPS, 4), "traffic": None},
+                         "frac": round(tf / PEAK_FP32_TFLOPS, 4),
+                         "traffic": read_traffic("path_bwd", BWD_TRAFFIC_FILE)},
             "heads_per_workspace_pass": int(heads_per_pass),
             "tokens_per_s": round(B * L / (ms * 1e-3))}
 
@@ -392,6 +397,21 @@ def counter_run(fwd_steps=2, dec_steps=2):
         (COPY_BYTES, fwd_steps, dec_steps))
 
 
+def counter_run_backward():
+    """No timing: the calibration copy (as in counter_run), then one forward and one backward
+    pass of the forward workload, for rocprofv3 --pmc over the backward kernels."""
+    import torch
+
+    src = torch.ones(COPY_BYTES // 2, device="cuda", dtype=torch.bfloat16)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    bench_backward(1, 0)
+
+
 def cpu_baseline(x, target_s):
     """The fp64 oracle, as it stands, on whole heads of the forward workload."""
     import oracle
@@ -427,6 +447,8 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=5, help="timed steps per other forward workload; 0 skips them")
     ap.add_argument("--backward-steps", type=int, default=3, help="timed backward passes; 0 skips them")
     ap.add_argument("--backward-only", action="store_true", help="only the backward leg (for kernel traces)")
+    ap.add_argument("--counter-run-backward", action="store_true",
+                    help="no timing: a calibration copy plus one backward pass, for rocprofv3 --pmc")
     ap.add_argument("--counter-run", action="store_true",
                     help="no timing: a calibration copy plus a few forward and decode steps, for rocprofv3 --pmc")
     args = ap.parse_args()
@@ -443,6 +465,9 @@ def main():
     torch.cuda.set_device(0)
     if args.counter_run:
         counter_run()
+        return
+    if args.counter_run_backward:
+        counter_run_backward()
         return
     if args.backward_only:
         print(json.dumps({"backward": bench_backward(max(1, args.backward_steps), 1)}), flush=True)
