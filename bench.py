@@ -6,9 +6,10 @@ B32 H32 L4096 d64 bf16 workload; K steps are timed after W warm-up steps.
 Alongside it the decode step (B16 H32 d64, 32768 cached rows, bf16, 64 steps
 with fresh q, w, beta each), the prefill -> decode cache build on the
 forward's workspace, and the other forward workloads (L 1024 - 8192 at
-d64, L4096 at d128, B8 H16 L4096, PaTH-FoX B4 H16 L16384) are timed, and the
-fp64 CPU oracle is timed on a bounded sample of the forward workload.  Prints
-one JSON line.
+d64, L4096 at d128, B8 H16 L4096, PaTH-FoX B4 H16 L16384) and the backward
+pass on the forward workload are timed, and the fp64 CPU oracle is timed on
+bounded samples of the forward, decode and backward workloads.  Prints one
+JSON line.
 
 Work units (fixed, declared):
   forward  F = 4 B H L^2 d flop: per causal pair of 64-token blocks the query-
@@ -437,6 +438,60 @@ def cpu_baseline(x, target_s):
             "sample": "%d of %d heads of the B%d H%d L%d d%d workload, every row, %.1f s" % (nh, G, B, H, L, d, t)}
 
 
+def cpu_baseline_backward(target_s, name=FWD_WORKLOAD):
+    """The fp64 oracle's backward, as it stands, on whole heads of the backward workload (same seeds)."""
+    import torch
+
+    import oracle
+    import pathgen
+
+    c = pathgen.WORKLOADS[name]
+    L, d = c["L"], c["d"]
+    threads = oracle.default_threads()
+
+    def run(nh):
+        x = pathgen.fwd_inputs(1, nh, L, d, c["dtype"], seed=0, fox=c["fox"], clip=c["clip"], device="cpu")
+        dout = torch.randn((1, nh, L, d), generator=torch.Generator().manual_seed(1)).to(x["q"].dtype)
+        t0 = time.perf_counter()
+        oracle.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], dout, nthreads=threads)
+        return time.perf_counter() - t0
+
+    nh = 1
+    t = run(nh)
+    if t < target_s:
+        nh = int(max(1, round(nh * target_s / max(t, 1e-3))))
+        t = run(nh)
+    tflops = 8.0 * nh * L * L * d / t / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d heads of L%d d%d, every row, %.1f s (work unit 8 L^2 d per head)" % (nh, L, d, t)}
+
+
+def cpu_baseline_decode(target_s):
+    """The fp64 oracle's decode step, as it stands, on whole heads of the decode workload's cache."""
+    import oracle
+    import pathgen
+
+    c = pathgen.WORKLOADS[DEC_WORKLOAD]
+    n, d = c["n"], c["d"]
+    threads = oracle.default_threads()
+
+    def run(nh):
+        x = pathgen.decode_inputs(1, nh, n, d, steps=1, dtype=c["dtype"], seed=0, clip=c["clip"], device="cpu")
+        t0 = time.perf_counter()
+        oracle.decode(x["kcache"], x["vcache"], n, x["q"][0], x["w"][0], x["beta"][0], nthreads=threads)
+        return time.perf_counter() - t0
+
+    nh = 8
+    t = run(nh)
+    if t < target_s:
+        nh = int(min(c["B"] * c["H"], max(1, round(nh * target_s / max(t, 1e-3)))))
+        t = run(nh)
+    gbs = 3.0 * nh * n * d * 2 / t / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of the %d heads of the n%d d%d decode workload, one step, %.1f s (bytes counted as on the GPU, bf16)" % (
+                nh, c["B"] * c["H"], n, d, t)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -496,11 +551,16 @@ def main():
         bwd = bench_backward(args.backward_steps, 1)
         log("backward: %.2f ms/step, %.1f TFLOP/s (%.1f%% of the fp32 matrix peak)" %
             (bwd["ms_per_step"], bwd["TFLOP_per_s"], 100 * bwd["roofline"]["frac"]))
-    cpu = None
+    cpu = dec_cpu = None
     if args.cpu_seconds > 0:
         log("cpu baseline: oracle, ~%.0f s" % args.cpu_seconds)
         cpu = cpu_baseline(f["x"], args.cpu_seconds)
         log("cpu baseline: %s" % cpu["sample"])
+        dec_cpu = cpu_baseline_decode(args.cpu_seconds / 3)
+        log("cpu baseline, decode: %s" % dec_cpu["sample"])
+        if bwd is not None:
+            bwd["cpu_baseline"] = cpu_baseline_backward(args.cpu_seconds / 3)
+            log("cpu baseline, backward: %s" % bwd["cpu_baseline"]["sample"])
 
     value = f["flops"] / (f["ms_per_step"] * 1e-3) / 1e12
     scan_tflops = f["flops"] / (f["scan_ms"] * 1e-3) / 1e12
@@ -533,7 +593,7 @@ def main():
                                 "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                                 "traffic": read_traffic("path_decode_kernel")},
                    "tokens_per_s": round(dres["B"] / (dres["step_ms"] * 1e-3)), "bytes_per_step": dres["bytes"],
-                   "steps": dres["steps"]},
+                   "steps": dres["steps"], "cpu_baseline": dec_cpu},
         "decode_forget_gate": {"ms_per_step": round(gres["step_ms"], 4), "bytes_per_step": gres["bytes"],
                                "GB_per_s": round(gres["bytes"] / (gres["step_ms"] * 1e-3) / 1e9, 1),
                                "frac_of_hbm_peak": round(gres["bytes"] / (gres["step_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},

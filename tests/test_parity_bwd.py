@@ -121,3 +121,32 @@ def test_bwd_rejects_d128():
     o, l = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], return_lse=True)
     with pytest.raises(pa.PathError):
         pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], None, o, l, torch.ones_like(o))
+
+
+@gpu
+def test_bwd_full_workload_sampled_heads():
+    """The whole B32 H32 L4096 d64 bf16 workload through the default workspace (heads in passes over 8 GiB,
+    the launch configuration the benchmark times); heads are independent, so the first and the last head
+    are checked element by element against the oracle run on that head's inputs alone."""
+    c = pathgen.WORKLOADS["sweep_L4096_d64_bf16"]
+    B, H, L = c["B"], c["H"], c["L"]
+    say("case bwd full workload B%d H%d L%d bf16" % (B, H, L))
+    x = pathgen.fwd_inputs(B, H, L, 64, "bf16", seed=0, clip=1.98, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    dout = torch.randn((B, H, L, 64), generator=g, device="cuda").to(torch.bfloat16)
+    out, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], None, return_lse=True)
+    grads = pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], None, out, lse, dout)
+    torch.cuda.synchronize()
+    assert pa.bwd_workspace_size(B, H, L, 64, torch.bfloat16) < B * H * pa.bwd_workspace_size(1, 1, L, 64, torch.bfloat16)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        sl = lambda t: t[b:b + 1, h:h + 1].cpu()
+        ref = oracle.bwd(*(sl(x[n]) for n in ("q", "k", "v", "w", "beta")), None, sl(dout), None)
+        for n, t in zip(NAMES, grads):
+            if t is None:
+                continue
+            r = ref[n]
+            e = float(np.abs(to_np(t[b:b + 1, h:h + 1]) - r).max())
+            bar = TOL["bf16"] * max(1.0, float(np.abs(r).max()))
+            assert e <= bar, "head (%d, %d) %s: %.3e > %.3e" % (b, h, n, e, bar)
+        say("  head (%d, %d) ok" % (b, h))
