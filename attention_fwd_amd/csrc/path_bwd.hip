@@ -158,13 +158,40 @@ __device__ __forceinline__ void acc2g(float *g, const f32x8 &acc, int lane, int 
     for (int v = 0; v < 8; ++v) g[arow(v, lane, wave) * kD + acol(v, lane, wave)] = acc[v];
 }
 
-// Input tensor rows [row0, row0 + 64) of one head (rows >= L read as 0) -> LDS fp32.
+// Eight consecutive elements of an input tensor as fp32 (one 16-byte load for
+// bf16, two for fp32); the tensors are 16-byte aligned and rows are 64 elements.
+__device__ __forceinline__ void load8(float *x, const uint16_t *g) {
+    const u32x4 u = *reinterpret_cast<const u32x4 *>(g);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        x[2 * t] = __uint_as_float(u[t] << 16);
+        x[2 * t + 1] = __uint_as_float(u[t] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(float *x, const float *g) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(g), b = *reinterpret_cast<const f32x4 *>(g + 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        x[t] = a[t];
+        x[4 + t] = b[t];
+    }
+}
+
+// Input tensor rows [row0, row0 + 64) of one head (rows >= L read as 0) -> LDS fp32;
+// each thread converts eight consecutive elements of one row.
 template <typename T>
 __device__ __forceinline__ void in2l(float *buf, const T *g, int row0, int L, int tid) {
-    for (int e = tid; e < kC * kD; e += kT) {
-        const int r = e >> 6, c = e & 63;
-        buf[r * kP + c] = (row0 + r < L) ? Elem<T>::to_f32(g[(int64_t)(row0 + r) * kD + c]) : 0.f;
+    const int r = tid >> 3, c = (tid & 7) * 8;  // 512 threads = 64 rows x 8 groups
+    float x[8];
+    if (row0 + r < L) {
+        load8(x, g + (int64_t)(row0 + r) * kD + c);
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[t] = 0.f;
     }
+    f32x4 lo = {x[0], x[1], x[2], x[3]}, hi = {x[4], x[5], x[6], x[7]};
+    *reinterpret_cast<f32x4 *>(buf + r * kP + c) = lo;
+    *reinterpret_cast<f32x4 *>(buf + r * kP + c + 4) = hi;
 }
 
 __device__ __forceinline__ int64_t pair_index(int I, int J) { return (int64_t)I * (I - 1) / 2 + J; }
@@ -236,10 +263,13 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     {   // D_i = do_i . o_i - dlse_i: eight lanes per row, 8 columns each
         const int r = tid >> 3, c0 = (tid & 7) * 8, i = row0 + r;
         float s = 0.f;
-        if (i < L)
+        if (i < L) {
+            float xo[8], xd[8];
+            load8(xd, dout + (int64_t)i * kD + c0);
+            load8(xo, o + (int64_t)i * kD + c0);
 #pragma unroll
-            for (int c = c0; c < c0 + 8; ++c)
-                s += Elem<T>::to_f32(dout[(int64_t)i * kD + c]) * Elem<T>::to_f32(o[(int64_t)i * kD + c]);
+            for (int t = 0; t < 8; ++t) s += xd[t] * xo[t];
+        }
         s = sum8(s);
         if ((tid & 7) == 0) sDD[r] = i < L ? s - (a.dlse ? a.dlse[hoff + i] : 0.f) : 0.f;
     }
