@@ -319,7 +319,7 @@ path_status_t bwd_sizes_ok(int B, int H, int L, int d, path_dtype_t dtype) {
 
 size_t path_attn_bwd_workspace_size(int B, int H, int L, int d, path_dtype_t dtype) {
     if (bwd_sizes_ok(B, H, L, d, dtype) != PATH_OK) return 0;
-    const int64_t share = path::bwd_layout(L).head, G = (int64_t)B * H;
+    const int64_t share = path::bwd_layout(L, (int)elem_size(dtype)).head, G = (int64_t)B * H;
     int64_t hc = kBwdCap / share;
     if (hc < 1) hc = 1;
     if (hc > G) hc = G;
@@ -350,7 +350,7 @@ path_status_t path_attn_bwd(const void *q, const void *k, const void *v, const v
     for (const void *p : tok_out)
         if (p && !aligned(p, 4)) return PATH_EINVAL;
     if (!std::isfinite(scale)) return PATH_EINVAL;
-    const int64_t share = path::bwd_layout(L).head, G = (int64_t)B * H;
+    const int64_t share = path::bwd_layout(L, (int)elem_size(dtype)).head, G = (int64_t)B * H;
     if ((int64_t)workspace_bytes < share) return PATH_EINVAL;
     int64_t hc = (int64_t)workspace_bytes / share;
     if (hc > G) hc = G;
@@ -390,7 +390,7 @@ path_status_t path_attn_bwd(const void *q, const void *k, const void *v, const v
     ba.B = B; ba.H = H; ba.L = L; ba.d = d; ba.scale = eff_scale(scale, d);
     ba.nb = (L + 63) / 64;
     ba.hc_max = (int)hc;
-    ba.ly = path::bwd_layout(L);
+    ba.ly = path::bwd_layout(L, (int)elem_size(dtype));
     return path::launch_bwd(ba, dtype == PATH_DTYPE_BF16, (hipStream_t)stream) == hipSuccess ? PATH_OK : PATH_EHIP;
 }
 

@@ -150,6 +150,36 @@ __device__ __forceinline__ void lstore(float *buf, const Stage &t, int tid) {
         *reinterpret_cast<f32x4 *>(buf + r * kP + c) = t.v[u];
     }
 }
+// The same for a 64x64 tile stored as bf16 (the walks' scratch for bf16 inputs):
+// 8 KiB, one 16-byte load of eight elements per thread.
+struct Stage16 {
+    u32x4 v;
+};
+__device__ __forceinline__ void gload(Stage16 &t, const uint16_t *g, int tid) {
+    t.v = *reinterpret_cast<const u32x4 *>(g + tid * 8);
+}
+__device__ __forceinline__ void lstore(float *buf, const Stage16 &t, int tid) {
+    const int r = tid >> 3, c = (tid & 7) * 8;
+    f32x4 lo, hi;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        lo[2 * u] = __uint_as_float(t.v[u] << 16);
+        lo[2 * u + 1] = __uint_as_float(t.v[u] & 0xffff0000u);
+        hi[2 * u] = __uint_as_float(t.v[2 + u] << 16);
+        hi[2 * u + 1] = __uint_as_float(t.v[2 + u] & 0xffff0000u);
+    }
+    *reinterpret_cast<f32x4 *>(buf + r * kP + c) = lo;
+    *reinterpret_cast<f32x4 *>(buf + r * kP + c + 4) = hi;
+}
+template <typename SC>
+struct StageOf {
+    typedef Stage T;
+};
+template <>
+struct StageOf<uint16_t> {
+    typedef Stage16 T;
+};
+
 __device__ __forceinline__ void zero_lds(float *buf, int tid) {
     for (int e = tid; e < kTile; e += kT) buf[e] = 0.f;
 }
@@ -397,6 +427,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Query-major walk: one workgroup per (query block I >= 1, head); heaviest first.
 // ---------------------------------------------------------------------------
+template <typename SC>
 __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float sm[7 * kTile + 4 * kC];
     float *bQt = sm, *bT = bQt + kTile, *bK = bT + kTile, *bV = bK + kTile, *bDO = bV + kTile, *bG = bDO + kTile,
@@ -410,8 +441,8 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
     const float *TT = (const float *)(ws + ly.tt), *TTt = (const float *)(ws + ly.ttt), *KH = (const float *)(ws + ly.kh),
                 *VF = (const float *)(ws + ly.vf);
     const float *tot = (const float *)(ws + ly.tot);
-    float *QS = (float *)(ws + ly.qs), *GS = (float *)(ws + ly.gs), *MID = (float *)(ws + ly.mid);
-    float *PS = (float *)(ws + ly.ps), *DS = (float *)(ws + ly.ds);
+    float *QS = (float *)(ws + ly.qs), *MID = (float *)(ws + ly.mid), *CSP = (float *)(ws + ly.csp);
+    SC *GS = (SC *)(ws + ly.gs), *PS = (SC *)(ws + ly.ps), *DS = (SC *)(ws + ly.ds);
     const float scale = a.scale;
     const int row0 = I * kC;
 
@@ -461,7 +492,11 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
         if (J >= 1) lstore(bT, rT, tid);
         if (tid < kC) sCk[tid] = rck;
         const float midJ = rmid;
-        if (J >= 1) acc2g(GS + p * kC * kD, accG, lane, wave);  // G^(J-1) for the key-major walk
+        if (J >= 1) {  // G^(J-1) for the key-major walk
+            SC *g = GS + p * kC * kD;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) g[arow(v, lane, wave) * kD + acol(v, lane, wave)] = Elem<SC>::from_float(accG[v]);
+        }
         __syncthreads();
         if (J + 1 < I) {  // next step's tiles, in flight while this step computes
             gload(rQ, QS + (p + 1) * kC * kD, tid);
@@ -475,18 +510,26 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
         mm(s, nat(bQt), tr(bK), lane, wave);
         mm(dp, nat(bDO), tr(bV), lane, wave);
         {
-            float *PSp = PS + p * kC * kC, *DSp = DS + p * kC * kC;
+            SC *PSp = PS + p * kC * kC, *DSp = DS + p * kC * kC;
 #pragma unroll
             for (int vv = 0; vv < 8; ++vv) {
                 const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
                 const float P = fast_exp2((scale * s[vv] + sCq[r] + sCk[c] + midJ) * kLog2e - sL2[r]);
                 const float dS = P * (dp[vv] - sDD[r]);
                 bS[r * kP + c] = dS;
-                PSp[r * kC + c] = P;  // for the key-major walk
-                DSp[r * kC + c] = dS;
+                PSp[r * kC + c] = Elem<SC>::from_float(P);  // for the key-major walk
+                DSp[r * kC + c] = Elem<SC>::from_float(dS);
             }
         }
         __syncthreads();
+        {   // column sums of this pair's dS (fp32) for the gate, summed over I by the key-major walk
+            const int cc = tid >> 3, p0 = tid & 7;
+            float t = 0.f;
+#pragma unroll
+            for (int r = p0; r < kC; r += 8) t += bS[r * kP + cc];
+            t = sum8(t);
+            if (p0 == 0) CSP[p * kC + cc] = t;
+        }
         f32x8 gt = zero8(), xs = zero8();
         if (J >= 1) mm(gt, nat(bG), tr(bT), lane, wave);  // bT holds T_J^T here
         mm(xs, nat(bS), nat(bK), lane, wave);
@@ -511,6 +554,7 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
 // sums over the query blocks: dV_J += P^T dO_I, dk^_J += scale dS^T q~,
 // dT_J += G^(J-1)^T q~, and the column sums of dS for the gate.
 // ---------------------------------------------------------------------------
+template <typename SC>
 __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float sm[5 * kTile];
     float *bQt = sm, *bDO = bQt + kTile, *bG = bDO + kTile, *bP = bG + kTile, *bS = bP + kTile;
@@ -519,13 +563,15 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
     const int gl = blockIdx.x % hc, J = blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
-    const float *QS = (const float *)(ws + ly.qs), *GS = (const float *)(ws + ly.gs), *PS = (const float *)(ws + ly.ps),
-                *DS = (const float *)(ws + ly.ds), *DOF = (const float *)(ws + ly.dof);
+    const float *QS = (const float *)(ws + ly.qs), *DOF = (const float *)(ws + ly.dof), *CSP = (const float *)(ws + ly.csp);
+    const SC *GS = (const SC *)(ws + ly.gs), *PS = (const SC *)(ws + ly.ps), *DS = (const SC *)(ws + ly.ds);
     const float scale = a.scale;
 
     f32x8 dV = zero8(), dK = zero8(), dT = zero8();
     float csum = 0.f;
-    Stage rQ, rO, rG, rP, rS;
+    Stage rQ, rO;
+    typename StageOf<SC>::T rG, rP, rS;
+    float rcs = 0.f;
     auto fetch = [&](int I) {
         const int64_t p = pair_index(I, J);
         gload(rQ, QS + p * kC * kD, tid);
@@ -533,6 +579,7 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
         if (J >= 1) gload(rG, GS + p * kC * kD, tid);
         gload(rP, PS + p * kC * kC, tid);
         gload(rS, DS + p * kC * kC, tid);
+        if (tid < kC) rcs = CSP[p * kC + tid];
     };
     fetch(J + 1);
     for (int I = J + 1; I < nb; ++I) {
@@ -542,17 +589,11 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
         lstore(bP, rP, tid);
         lstore(bS, rS, tid);
         __syncthreads();
+        if (tid < kC) csum += rcs;
         if (I + 1 < nb) fetch(I + 1);  // next step's tiles, in flight while this step computes
         mm(dV, tr(bP), nat(bDO), lane, wave);
         mm(dK, tr(bS), nat(bQt), lane, wave);
         if (J >= 1) mm(dT, tr(bG), nat(bQt), lane, wave);
-        {   // column sums of dS: eight lanes per column, every eighth row
-            const int cc = tid >> 3, p0 = tid & 7;
-            float t = 0.f;
-#pragma unroll
-            for (int r = p0; r < kC; r += 8) t += bS[r * kP + cc];
-            csum += sum8(t);
-        }
         __syncthreads();
     }
     const int row0 = J * kC;
@@ -561,7 +602,7 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
     acc2g((float *)(ws + ly.dko) + row0 * kD, dK, lane, wave);
     acc2g((float *)(ws + ly.dvo) + row0 * kD, dV, lane, wave);
     acc2g((float *)(ws + ly.dt) + (int64_t)J * kD * kD, dT, lane, wave);
-    if ((tid & 7) == 0) ((float *)(ws + ly.cso))[row0 + (tid >> 3)] = csum;
+    if (tid < kC) ((float *)(ws + ly.cso))[row0 + tid] = csum;
 }
 
 // ---------------------------------------------------------------------------
@@ -777,7 +818,7 @@ __global__ __launch_bounds__(kT) void bwd_gate_kernel(BwdArgs a) {
 
 }  // namespace
 
-BwdLayout bwd_layout(int L) {
+BwdLayout bwd_layout(int L, int es) {
     BwdLayout ly{};
     const int64_t nb = (L + kC - 1) / kC, Lp = nb * kC, np = nb * (nb - 1) / 2;
     int64_t off = 0;
@@ -796,8 +837,8 @@ BwdLayout bwd_layout(int L) {
     ly.l2 = take(rows); ly.dd = take(rows); ly.clq = take(rows); ly.ckk = take(rows); ly.rsd = take(rows);
     ly.csd = take(rows); ly.rso = take(rows); ly.cso = take(rows); ly.dc = take(rows);
     ly.tot = take(nb * 4); ly.mid = take(np * 4);
-    ly.qs = take(np * kC * kD * 4); ly.gs = take(np * kC * kD * 4);
-    ly.ps = take(np * kC * kC * 4); ly.ds = take(np * kC * kC * 4);
+    ly.qs = take(np * kC * kD * 4); ly.gs = take(np * kC * kD * es);
+    ly.ps = take(np * kC * kC * es); ly.ds = take(np * kC * kC * es); ly.csp = take(np * kC * 4);
     ly.head = off;
     return ly;
 }
@@ -812,8 +853,13 @@ hipError_t launch_bwd(const BwdArgs &a0, bool bf16, hipStream_t st) {
         if (bf16) hipLaunchKernelGGL(bwd_prep_kernel<uint16_t>, dim3(a.nb, a.hc), blk, 0, st, a);
         else hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3(a.nb, a.hc), blk, 0, st, a);
         if (a.nb > 1) {
-            hipLaunchKernelGGL(bwd_query_kernel, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
-            hipLaunchKernelGGL(bwd_key_kernel, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
+            if (bf16) {
+                hipLaunchKernelGGL(bwd_query_kernel<uint16_t>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
+                hipLaunchKernelGGL(bwd_key_kernel<uint16_t>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
+            } else {
+                hipLaunchKernelGGL(bwd_query_kernel<float>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
+                hipLaunchKernelGGL(bwd_key_kernel<float>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
+            }
         }
         if (bf16) hipLaunchKernelGGL(bwd_block_kernel<uint16_t>, dim3(a.nb, a.hc), blk, 0, st, a);
         else hipLaunchKernelGGL(bwd_block_kernel<float>, dim3(a.nb, a.hc), blk, 0, st, a);
