@@ -19,10 +19,10 @@ struct BwdLayout {
     int64_t rsd, csd, rso, cso, dc;  // [Lp]: row / column sums of dS (diagonal, off-diagonal), gate adjoint
     int64_t tot;              // [nb]: gate total of each block
     int64_t mid;              // [np]: gate sum over the blocks strictly between I and J
-    int64_t qs, gs;           // [np, 64, 64]: carried queries q~_I^(J) (fp32) and adjoints G_I^(J-1)
+    int64_t qs, gs;           // [np, 64, 64]: carried queries q~_I^(J) and adjoints G_I^(J-1)
     int64_t ps, ds;           // [np, 64, 64]: softmax weights P and dS of every pair
     int64_t csp;              // [np, 64]: column sums of each pair's dS (fp32)
-    // gs, ps, ds hold the input element type (bf16 for bf16 inputs, else fp32)
+    // qs, gs, ps, ds hold the input element type (bf16 for bf16 inputs, else fp32)
     int64_t head;             // bytes per head
 };
 

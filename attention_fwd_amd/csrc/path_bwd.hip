@@ -441,8 +441,8 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
     const float *TT = (const float *)(ws + ly.tt), *TTt = (const float *)(ws + ly.ttt), *KH = (const float *)(ws + ly.kh),
                 *VF = (const float *)(ws + ly.vf);
     const float *tot = (const float *)(ws + ly.tot);
-    float *QS = (float *)(ws + ly.qs), *MID = (float *)(ws + ly.mid), *CSP = (float *)(ws + ly.csp);
-    SC *GS = (SC *)(ws + ly.gs), *PS = (SC *)(ws + ly.ps), *DS = (SC *)(ws + ly.ds);
+    float *MID = (float *)(ws + ly.mid), *CSP = (float *)(ws + ly.csp);
+    SC *QS = (SC *)(ws + ly.qs), *GS = (SC *)(ws + ly.gs), *PS = (SC *)(ws + ly.ps), *DS = (SC *)(ws + ly.ds);
     const float scale = a.scale;
     const int row0 = I * kC;
 
@@ -450,13 +450,13 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
     g2l(bQt, (const float *)(ws + ly.qh) + row0 * kD, tid);
     float mid = 0.f;
     {
-        float *dst = QS + pair_index(I, I - 1) * kC * kD;
+        SC *dst = QS + pair_index(I, I - 1) * kC * kD;
         const float *src = (const float *)(ws + ly.qh) + row0 * kD;
-        for (int e = tid; e < kC * kD / 4; e += kT)
-            reinterpret_cast<f32x4 *>(dst)[e] = reinterpret_cast<const f32x4 *>(src)[e];
+        for (int e = tid; e < kC * kD; e += kT) dst[e] = Elem<SC>::from_float(src[e]);
     }
     if (tid == 0) MID[pair_index(I, I - 1)] = 0.f;
-    Stage rT, rQ, rK, rV;
+    Stage rT, rK, rV;
+    typename StageOf<SC>::T rQ;
     if (I - 1 >= 1) gload(rT, TT + (int64_t)(I - 1) * kD * kD, tid);
     for (int J = I - 1; J >= 1; --J) {
         lstore(bT, rT, tid);
@@ -466,7 +466,11 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
         mm(acc, nat(bQt), tr(bT), lane, wave);  // q~^(J-1) = T_J q~^(J) (rows: Q~ T^T)
         __syncthreads();
         store_lds(bQt, acc, lane, wave, [](int, int, float x) { return x; });
-        acc2g(QS + pair_index(I, J - 1) * kC * kD, acc, lane, wave);
+        {
+            SC *g = QS + pair_index(I, J - 1) * kC * kD;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) g[arow(v, lane, wave) * kD + acol(v, lane, wave)] = Elem<SC>::from_float(acc[v]);
+        }
         mid += tot[J];
         if (tid == 0) MID[pair_index(I, J - 1)] = mid;
     }
@@ -563,14 +567,15 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
     const int gl = blockIdx.x % hc, J = blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
-    const float *QS = (const float *)(ws + ly.qs), *DOF = (const float *)(ws + ly.dof), *CSP = (const float *)(ws + ly.csp);
-    const SC *GS = (const SC *)(ws + ly.gs), *PS = (const SC *)(ws + ly.ps), *DS = (const SC *)(ws + ly.ds);
+    const float *DOF = (const float *)(ws + ly.dof), *CSP = (const float *)(ws + ly.csp);
+    const SC *QS = (const SC *)(ws + ly.qs), *GS = (const SC *)(ws + ly.gs), *PS = (const SC *)(ws + ly.ps),
+             *DS = (const SC *)(ws + ly.ds);
     const float scale = a.scale;
 
     f32x8 dV = zero8(), dK = zero8(), dT = zero8();
     float csum = 0.f;
-    Stage rQ, rO;
-    typename StageOf<SC>::T rG, rP, rS;
+    Stage rO;
+    typename StageOf<SC>::T rQ, rG, rP, rS;
     float rcs = 0.f;
     auto fetch = [&](int I) {
         const int64_t p = pair_index(I, J);
@@ -837,7 +842,7 @@ BwdLayout bwd_layout(int L, int es) {
     ly.l2 = take(rows); ly.dd = take(rows); ly.clq = take(rows); ly.ckk = take(rows); ly.rsd = take(rows);
     ly.csd = take(rows); ly.rso = take(rows); ly.cso = take(rows); ly.dc = take(rows);
     ly.tot = take(nb * 4); ly.mid = take(np * 4);
-    ly.qs = take(np * kC * kD * 4); ly.gs = take(np * kC * kD * es);
+    ly.qs = take(np * kC * kD * es); ly.gs = take(np * kC * kD * es);
     ly.ps = take(np * kC * kC * es); ly.ds = take(np * kC * kC * es); ly.csp = take(np * kC * 4);
     ly.head = off;
     return ly;
