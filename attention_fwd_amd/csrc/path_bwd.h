@@ -10,7 +10,7 @@ namespace path {
 // Lp = 64 * ceil(L / 64) padded rows, nb blocks, np = nb (nb - 1) / 2 pairs of
 // a query block I and an earlier key block J, pair index I (I - 1) / 2 + J).
 struct BwdLayout {
-    int64_t qh, kh, vf, dof;  // [Lp, 64]: block-adjusted q and k, v and do as fp32
+    int64_t qh, kh, vf, dof;  // [Lp, 64]: block-adjusted q and k (fp32), copies of v and do (input type)
     int64_t tt, ttt, ee;      // [nb, 64, 64]: block transitions and their transposes, scale * dS of the diagonal blocks
     int64_t dvd, dqo, dko, dvo;  // [Lp, 64]: diagonal value gradient; walk outputs dq^, dk^, dv
     int64_t dt;               // [nb, 64, 64]: gradient of each block transition

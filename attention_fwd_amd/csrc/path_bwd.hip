@@ -395,10 +395,10 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     {
         float *EE = (float *)(ws + ly.ee) + (int64_t)J * kC * kC;
         for (int e = tid; e < kC * kC; e += kT) EE[e] = scale * bZ[(e >> 6) * kP + (e & 63)];
-        float *VF = (float *)(ws + ly.vf) + row0 * kD, *DOF = (float *)(ws + ly.dof) + row0 * kD;
+        T *VF = (T *)(ws + ly.vf) + row0 * kD, *DOF = (T *)(ws + ly.dof) + row0 * kD;  // exact copies of v, do
         for (int e = tid; e < kC * kD; e += kT) {
-            VF[e] = bY[(e >> 6) * kP + (e & 63)];
-            DOF[e] = bA[(e >> 6) * kP + (e & 63)];
+            VF[e] = Elem<T>::from_float(bY[(e >> 6) * kP + (e & 63)]);
+            DOF[e] = Elem<T>::from_float(bA[(e >> 6) * kP + (e & 63)]);
         }
         acc = zero8();
         mm(acc, tr(bG), nat(bA), lane, wave);  // diagonal value gradient P^T dO
@@ -438,8 +438,8 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
     const int gl = blockIdx.x % hc, I = nb - 1 - blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
-    const float *TT = (const float *)(ws + ly.tt), *TTt = (const float *)(ws + ly.ttt), *KH = (const float *)(ws + ly.kh),
-                *VF = (const float *)(ws + ly.vf);
+    const float *TT = (const float *)(ws + ly.tt), *TTt = (const float *)(ws + ly.ttt), *KH = (const float *)(ws + ly.kh);
+    const SC *VF = (const SC *)(ws + ly.vf);
     const float *tot = (const float *)(ws + ly.tot);
     float *MID = (float *)(ws + ly.mid), *CSP = (float *)(ws + ly.csp);
     SC *QS = (SC *)(ws + ly.qs), *GS = (SC *)(ws + ly.gs), *PS = (SC *)(ws + ly.ps), *DS = (SC *)(ws + ly.ds);
@@ -455,8 +455,8 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
         for (int e = tid; e < kC * kD; e += kT) dst[e] = Elem<SC>::from_float(src[e]);
     }
     if (tid == 0) MID[pair_index(I, I - 1)] = 0.f;
-    Stage rT, rK, rV;
-    typename StageOf<SC>::T rQ;
+    Stage rT, rK;
+    typename StageOf<SC>::T rQ, rV;
     if (I - 1 >= 1) gload(rT, TT + (int64_t)(I - 1) * kD * kD, tid);
     for (int J = I - 1; J >= 1; --J) {
         lstore(bT, rT, tid);
@@ -475,7 +475,11 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
         if (tid == 0) MID[pair_index(I, J - 1)] = mid;
     }
     // up: adjoint G
-    g2l(bDO, (const float *)(ws + ly.dof) + row0 * kD, tid);
+    {
+        typename StageOf<SC>::T rD;
+        gload(rD, (const SC *)(ws + ly.dof) + row0 * kD, tid);
+        lstore(bDO, rD, tid);
+    }
     if (tid < kC) {
         sL2[tid] = ((const float *)(ws + ly.l2))[row0 + tid];
         sDD[tid] = ((const float *)(ws + ly.dd))[row0 + tid];
@@ -567,15 +571,15 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
     const int gl = blockIdx.x % hc, J = blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
-    const float *DOF = (const float *)(ws + ly.dof), *CSP = (const float *)(ws + ly.csp);
+    const float *CSP = (const float *)(ws + ly.csp);
+    const SC *DOF = (const SC *)(ws + ly.dof);
     const SC *QS = (const SC *)(ws + ly.qs), *GS = (const SC *)(ws + ly.gs), *PS = (const SC *)(ws + ly.ps),
              *DS = (const SC *)(ws + ly.ds);
     const float scale = a.scale;
 
     f32x8 dV = zero8(), dK = zero8(), dT = zero8();
     float csum = 0.f;
-    Stage rO;
-    typename StageOf<SC>::T rQ, rG, rP, rS;
+    typename StageOf<SC>::T rO, rQ, rG, rP, rS;
     float rcs = 0.f;
     auto fetch = [&](int I) {
         const int64_t p = pair_index(I, J);
@@ -833,7 +837,8 @@ BwdLayout bwd_layout(int L, int es) {
         return o;
     };
     const int64_t tile = Lp * kD * 4, rows = Lp * 4;
-    ly.qh = take(tile); ly.kh = take(tile); ly.vf = take(tile); ly.dof = take(tile); ly.tt = take(nb * kD * kD * 4);
+    ly.qh = take(tile); ly.kh = take(tile); ly.vf = take(Lp * kD * es); ly.dof = take(Lp * kD * es);
+    ly.tt = take(nb * kD * kD * 4);
     ly.ttt = take(nb * kD * kD * 4);
     ly.xx = take(nb * kC * kC * 4); ly.aa = take(nb * kC * kC * 4); ly.qwm = take(nb * kC * kC * 4);
     ly.nn = take(nb * kC * kC * 4); ly.zz = take(nb * kC * kC * 4);
