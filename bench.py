@@ -126,9 +126,33 @@ def bench_forward(steps, warmup, name=FWD_WORKLOAD):
     wall = time.perf_counter() - t0
     prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    per_step = sorted(e[0].elapsed_time(e[2]) for e in evs)
     flops = 4.0 * B * H * L * L * d
     return dict(B=B, H=H, L=L, d=d, flops=flops, wall_s=wall, ms_per_step=wall * 1e3 / steps,
-                prep_ms=prep_ms, scan_ms=scan_ms, x=x)
+                prep_ms=prep_ms, scan_ms=scan_ms, x=x, ms_median=per_step[len(per_step) // 2], ms_min=per_step[0])
+
+
+def bench_copy(reps=10, nbytes=1 << 31):
+    """A plain device copy (torch copy_ of nbytes of bf16) in the same run, for the HBM rate the
+    memory-bound kernels can be compared with; GB/s counts read + write."""
+    import torch
+
+    a = torch.ones(nbytes // 2, device="cuda", dtype=torch.bfloat16)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * nbytes, "ms": round(ms, 4), "GB_per_s": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def bench_sweep(steps, warmup):
@@ -532,6 +556,8 @@ def main():
     log("forward: %.3f ms/step (prep %.3f ms, scan %.3f ms)" % (f["ms_per_step"], f["prep_ms"], f["scan_ms"]))
     cache = bench_cache(10, f)
     log("prefill -> decode cache: %.3f ms, %.1f GB/s" % (cache["ms"], cache["GB_per_s"]))
+    copy = bench_copy()
+    log("device copy: %.1f GB/s (read + write)" % copy["GB_per_s"])
     log("decode: %s, %d steps" % (DEC_WORKLOAD, args.decode_steps))
     dres = bench_decode(args.decode_steps)
     log("decode: %.3f ms/step" % dres["step_ms"])
@@ -584,7 +610,11 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "path_fwd_kernel (scan stage: bounded walk + redo launch)", "achieved": round(scan_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(scan_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
-        "forward": {"ms_per_step": round(f["ms_per_step"], 4), "prep_ms": round(f["prep_ms"], 4),
+        "forward": {"ms_per_step": round(f["ms_per_step"], 4), "ms_median": round(f["ms_median"], 4),
+                    "ms_min": round(f["ms_min"], 4),
+                    "TFLOP_per_s_fa_convention": round(2.0 * f["B"] * f["H"] * f["L"] ** 2 * f["d"] /
+                                                       (f["ms_per_step"] * 1e-3) / 1e12, 1),
+                    "prep_ms": round(f["prep_ms"], 4),
                     "scan_ms": round(f["scan_ms"], 4), "frac_of_peak_whole_pass": round(value / PEAK_BF16_TFLOPS, 4),
                     "tokens_per_s": round(f["B"] * f["L"] / (f["ms_per_step"] * 1e-3)),
                     "flop_per_step": f["flops"]},
@@ -598,6 +628,7 @@ def main():
                                "GB_per_s": round(gres["bytes"] / (gres["step_ms"] * 1e-3) / 1e9, 1),
                                "frac_of_hbm_peak": round(gres["bytes"] / (gres["step_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "decode_cache_from_fwd": cache,
+        "device_copy": copy,
         "other_workloads": sweep,
         "fox_skip_negligible": fox_skip,
         "fused_producer": fused,
