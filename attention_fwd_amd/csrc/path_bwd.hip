@@ -22,8 +22,9 @@
 // query carried down q~^(J-1) = T_J q~^(J), q~^(I-1) = q^.  The adjoint of
 // q~^(J) obeys G^(J) = G^(J-1) T_J + scale dS_IJ K^_J (rows), running upward
 // while q~ runs downward, so:
-//   prep (per block): the quantities above, the diagonal block's dS, its
-//     value gradient, and fp32 copies of v and do;
+//   prep (per block): the quantities above (X, A, Q W^T o mask, N and Z kept
+//     for the block backward), the diagonal block's dS, its value gradient,
+//     and copies of v and do;
 //   query-major walk (per query block I): down J = I-1 .. 0 storing q~^(J)
 //     for every pair, then up J = 0 .. I-1 storing G^(J-1), P and dS for every pair and
 //     ending with dq^_I = G^(I-1);
@@ -37,7 +38,11 @@
 //   gate: dlogf_t = sum_{t' >= t} dc_t' (one workgroup per head).
 // Every contraction is a 64x64x64 fp32 product on the matrix cores
 // (v_mfma_f32_16x16x4f32, eight waves sharing each product) with operands in
-// LDS, so the gradients are fp32 for either input type.  Head dimension 64.
+// LDS; the arithmetic is fp32 for either input type.  The walks exchange q~,
+// G, P and dS of every pair through the workspace in the input type: fp32,
+// or bf16 for bf16 inputs (the forward's own scan feeds q~ to its logit
+// products in bf16 too); the column sums of dS the gate needs stay fp32.
+// Head dimension 64.
 #include <hip/hip_runtime.h>
 
 #include "path_bwd.h"
@@ -179,6 +184,24 @@ template <>
 struct StageOf<uint16_t> {
     typedef Stage16 T;
 };
+
+// LDS fp32 tile -> global 64x64 tile of the scratch type, eight consecutive
+// elements per thread (one 16-byte store for bf16, two for fp32).
+__device__ __forceinline__ void l2g_sc(float *g, const float *buf, int tid) {
+    const int r = tid >> 3, c = (tid & 7) * 8;
+    *reinterpret_cast<f32x4 *>(g + r * kD + c) = *reinterpret_cast<const f32x4 *>(buf + r * kP + c);
+    *reinterpret_cast<f32x4 *>(g + r * kD + c + 4) = *reinterpret_cast<const f32x4 *>(buf + r * kP + c + 4);
+}
+__device__ __forceinline__ void l2g_sc(uint16_t *g, const float *buf, int tid) {
+    const int r = tid >> 3, c = (tid & 7) * 8;
+    const f32x4 lo = *reinterpret_cast<const f32x4 *>(buf + r * kP + c), hi = *reinterpret_cast<const f32x4 *>(buf + r * kP + c + 4);
+    u32x4 u;
+    u[0] = pack_bf16(lo[0], lo[1]);
+    u[1] = pack_bf16(lo[2], lo[3]);
+    u[2] = pack_bf16(hi[0], hi[1]);
+    u[3] = pack_bf16(hi[2], hi[3]);
+    *reinterpret_cast<u32x4 *>(g + r * kD + c) = u;
+}
 
 __device__ __forceinline__ void zero_lds(float *buf, int tid) {
     for (int e = tid; e < kTile; e += kT) buf[e] = 0.f;
@@ -429,10 +452,10 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 template <typename SC>
 __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) float sm[7 * kTile + 4 * kC];
+    __shared__ __attribute__((aligned(16))) float sm[8 * kTile + 4 * kC];
     float *bQt = sm, *bT = bQt + kTile, *bK = bT + kTile, *bV = bK + kTile, *bDO = bV + kTile, *bG = bDO + kTile,
-          *bS = bG + kTile;
-    float *sL2 = bS + kTile, *sDD = sL2 + kC, *sCq = sDD + kC, *sCk = sCq + kC;
+          *bS = bG + kTile, *bP = bS + kTile;
+    float *sL2 = bP + kTile, *sDD = sL2 + kC, *sCq = sDD + kC, *sCk = sCq + kC;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nb = a.nb, hc = a.hc;
     const int gl = blockIdx.x % hc, I = nb - 1 - blockIdx.x / hc;
@@ -458,21 +481,21 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
     Stage rT, rK;
     typename StageOf<SC>::T rQ, rV;
     if (I - 1 >= 1) gload(rT, TT + (int64_t)(I - 1) * kD * kD, tid);
-    for (int J = I - 1; J >= 1; --J) {
+    for (int J = I - 1; J >= 1; --J) {  // bQt holds q~^(J)
         lstore(bT, rT, tid);
         __syncthreads();
+        if (J < I - 1) l2g_sc(QS + pair_index(I, J) * kC * kD, bQt, tid);  // q^ = q~^(I-1) is stored above
         if (J - 1 >= 1) gload(rT, TT + (int64_t)(J - 1) * kD * kD, tid);  // next step's transition
         f32x8 acc = zero8();
         mm(acc, nat(bQt), tr(bT), lane, wave);  // q~^(J-1) = T_J q~^(J) (rows: Q~ T^T)
         __syncthreads();
         store_lds(bQt, acc, lane, wave, [](int, int, float x) { return x; });
-        {
-            SC *g = QS + pair_index(I, J - 1) * kC * kD;
-#pragma unroll
-            for (int v = 0; v < 8; ++v) g[arow(v, lane, wave) * kD + acol(v, lane, wave)] = Elem<SC>::from_float(acc[v]);
-        }
         mid += tot[J];
         if (tid == 0) MID[pair_index(I, J - 1)] = mid;
+    }
+    if (I >= 2) {
+        __syncthreads();
+        l2g_sc(QS + pair_index(I, 0) * kC * kD, bQt, tid);
     }
     // up: adjoint G
     {
@@ -500,12 +523,8 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
         if (J >= 1) lstore(bT, rT, tid);
         if (tid < kC) sCk[tid] = rck;
         const float midJ = rmid;
-        if (J >= 1) {  // G^(J-1) for the key-major walk
-            SC *g = GS + p * kC * kD;
-#pragma unroll
-            for (int v = 0; v < 8; ++v) g[arow(v, lane, wave) * kD + acol(v, lane, wave)] = Elem<SC>::from_float(accG[v]);
-        }
         __syncthreads();
+        if (J >= 1) l2g_sc(GS + p * kC * kD, bG, tid);  // G^(J-1) (in bG since the last step) for the key-major walk
         if (J + 1 < I) {  // next step's tiles, in flight while this step computes
             gload(rQ, QS + (p + 1) * kC * kD, tid);
             gload(rK, KH + (int64_t)(J + 1) * kC * kD, tid);
@@ -517,19 +536,16 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
         f32x8 s = zero8(), dp = zero8();
         mm(s, nat(bQt), tr(bK), lane, wave);
         mm(dp, nat(bDO), tr(bV), lane, wave);
-        {
-            SC *PSp = PS + p * kC * kC, *DSp = DS + p * kC * kC;
 #pragma unroll
-            for (int vv = 0; vv < 8; ++vv) {
-                const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
-                const float P = fast_exp2((scale * s[vv] + sCq[r] + sCk[c] + midJ) * kLog2e - sL2[r]);
-                const float dS = P * (dp[vv] - sDD[r]);
-                bS[r * kP + c] = dS;
-                PSp[r * kC + c] = Elem<SC>::from_float(P);  // for the key-major walk
-                DSp[r * kC + c] = Elem<SC>::from_float(dS);
-            }
+        for (int vv = 0; vv < 8; ++vv) {
+            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
+            const float P = fast_exp2((scale * s[vv] + sCq[r] + sCk[c] + midJ) * kLog2e - sL2[r]);
+            bP[r * kP + c] = P;
+            bS[r * kP + c] = P * (dp[vv] - sDD[r]);
         }
         __syncthreads();
+        l2g_sc(PS + p * kC * kC, bP, tid);  // P and dS for the key-major walk
+        l2g_sc(DS + p * kC * kC, bS, tid);
         {   // column sums of this pair's dS (fp32) for the gate, summed over I by the key-major walk
             const int cc = tid >> 3, p0 = tid & 7;
             float t = 0.f;

@@ -250,8 +250,9 @@ path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace
  * one).  path_attn_bwd_workspace_size(1, 1, L, d, dtype) is one head's share;
  * path_attn_bwd accepts any workspace of at least one share and processes
  * floor(workspace_bytes / share) heads at a time (results do not depend on it).
- * One share is about (32 nb (nb - 1) / 2 + 13 nb) KiB + 40 bytes per token,
- * nb = ceil(L / 64), for d = 64.
+ * One share is about 64 KiB (fp32) or 32 KiB (bf16) per pair of 64-token
+ * blocks (nb (nb - 1) / 2 pairs, nb = ceil(L / 64)) plus about 270 KiB per
+ * block: 144 MiB (fp32) or 80 MiB (bf16) at L = 4096.
  */
 size_t path_attn_bwd_workspace_size(int B, int H, int L, int d, path_dtype_t dtype);
 
