@@ -630,6 +630,88 @@ __global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
     if (tid < kC) ((float *)(ws + ly.cso))[row0 + tid] = csum;
 }
 
+// The key-major walk for bf16 inputs: its five tiles arrive in bf16 and every
+// product reads both operands with single loads (A transposed, B by rows), so
+// the tiles stay bf16 in LDS (8 KiB each, row stride 64: the sixteen lanes of
+// a read walk a row) and are widened as they are read.  At 40 KiB of LDS two
+// workgroups share a compute unit.
+__device__ __forceinline__ float h2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// acc += X^T Y for 64x64 bf16 tiles in LDS (row stride 64), fp32 products.
+__device__ __forceinline__ void mm_tn_h(f32x8 &acc, const uint16_t *X, const uint16_t *Y, int lane, int wave) {
+    const int r = 16 * (wave >> 1) + (lane & 15), c0 = 32 * (wave & 1) + (lane & 15), q = lane >> 4;
+    f32x4 lo = acc.lo, hi = acc.hi;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int k0 = 16 * g + 4 * q;
+        float x[4], y0[4], y1[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            x[t] = h2f(X[(k0 + t) * 64 + r]);
+            y0[t] = h2f(Y[(k0 + t) * 64 + c0]);
+            y1[t] = h2f(Y[(k0 + t) * 64 + c0 + 16]);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            lo = __builtin_amdgcn_mfma_f32_16x16x4f32(x[t], y0[t], lo, 0, 0, 0);
+            hi = __builtin_amdgcn_mfma_f32_16x16x4f32(x[t], y1[t], hi, 0, 0, 0);
+        }
+    }
+    acc.lo = lo;
+    acc.hi = hi;
+}
+
+__global__ __launch_bounds__(kT, 2) void bwd_key_kernel_h(BwdArgs a) {
+    constexpr int kTh = kC * 64;  // elements of one bf16 tile
+    __shared__ __attribute__((aligned(16))) uint16_t sm[5 * kTh];
+    uint16_t *bQt = sm, *bDO = bQt + kTh, *bG = bDO + kTh, *bP = bG + kTh, *bS = bP + kTh;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nb = a.nb, hc = a.hc;
+    const int gl = blockIdx.x % hc, J = blockIdx.x / hc;
+    const BwdLayout &ly = a.ly;
+    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
+    const float *CSP = (const float *)(ws + ly.csp);
+    const uint16_t *DOF = (const uint16_t *)(ws + ly.dof), *QS = (const uint16_t *)(ws + ly.qs),
+                   *GS = (const uint16_t *)(ws + ly.gs), *PS = (const uint16_t *)(ws + ly.ps),
+                   *DS = (const uint16_t *)(ws + ly.ds);
+    const float scale = a.scale;
+
+    f32x8 dV = zero8(), dK = zero8(), dT = zero8();
+    float csum = 0.f, rcs = 0.f;
+    u32x4 rO, rQ, rG, rP, rS;  // eight bf16 per thread and tile: row tid / 8, columns 8 (tid % 8) ..
+    auto fetch = [&](int I) {
+        const int64_t p = pair_index(I, J);
+        rQ = *reinterpret_cast<const u32x4 *>(QS + p * kC * kD + tid * 8);
+        rO = *reinterpret_cast<const u32x4 *>(DOF + (int64_t)I * kC * kD + tid * 8);
+        if (J >= 1) rG = *reinterpret_cast<const u32x4 *>(GS + p * kC * kD + tid * 8);
+        rP = *reinterpret_cast<const u32x4 *>(PS + p * kC * kC + tid * 8);
+        rS = *reinterpret_cast<const u32x4 *>(DS + p * kC * kC + tid * 8);
+        if (tid < kC) rcs = CSP[p * kC + tid];
+    };
+    fetch(J + 1);
+    for (int I = J + 1; I < nb; ++I) {
+        *reinterpret_cast<u32x4 *>(bQt + tid * 8) = rQ;
+        *reinterpret_cast<u32x4 *>(bDO + tid * 8) = rO;
+        if (J >= 1) *reinterpret_cast<u32x4 *>(bG + tid * 8) = rG;
+        *reinterpret_cast<u32x4 *>(bP + tid * 8) = rP;
+        *reinterpret_cast<u32x4 *>(bS + tid * 8) = rS;
+        __syncthreads();
+        if (tid < kC) csum += rcs;
+        if (I + 1 < nb) fetch(I + 1);  // next step's tiles, in flight while this step computes
+        mm_tn_h(dV, bP, bDO, lane, wave);              // P^T dO
+        mm_tn_h(dK, bS, bQt, lane, wave);              // dS^T q~
+        if (J >= 1) mm_tn_h(dT, bG, bQt, lane, wave);  // G^T q~
+        __syncthreads();
+    }
+    const int row0 = J * kC;
+#pragma unroll
+    for (int vv = 0; vv < 8; ++vv) dK[vv] *= scale;
+    acc2g((float *)(ws + ly.dko) + row0 * kD, dK, lane, wave);
+    acc2g((float *)(ws + ly.dvo) + row0 * kD, dV, lane, wave);
+    acc2g((float *)(ws + ly.dt) + (int64_t)J * kD * kD, dT, lane, wave);
+    if (tid < kC) ((float *)(ws + ly.cso))[row0 + tid] = csum;
+}
+
 // ---------------------------------------------------------------------------
 // Block backward: one workgroup per (block J, head).
 // ---------------------------------------------------------------------------
@@ -881,7 +963,7 @@ hipError_t launch_bwd(const BwdArgs &a0, bool bf16, hipStream_t st) {
         if (a.nb > 1) {
             if (bf16) {
                 hipLaunchKernelGGL(bwd_query_kernel<uint16_t>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
-                hipLaunchKernelGGL(bwd_key_kernel<uint16_t>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
+                hipLaunchKernelGGL(bwd_key_kernel_h, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
             } else {
                 hipLaunchKernelGGL(bwd_query_kernel<float>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
                 hipLaunchKernelGGL(bwd_key_kernel<float>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
