@@ -25,9 +25,10 @@
 //   prep (per block): the quantities above (X, A, Q W^T o mask, N and Z kept
 //     for the block backward), the diagonal block's dS, its value gradient,
 //     and copies of v and do;
-//   query-major walk (per query block I): down J = I-1 .. 0 storing q~^(J)
-//     for every pair, then up J = 0 .. I-1 storing G^(J-1), P and dS for every pair and
-//     ending with dq^_I = G^(I-1);
+//   query-major walk (per query block I): a down walk J = I-1 .. 0 storing
+//     q~^(J) for every pair (its own kernel: one product per step, so several
+//     workgroups per compute unit), then the up walk J = 0 .. I-1 storing
+//     G^(J-1), P and dS for every pair and ending with dq^_I = G^(I-1);
 //   key-major walk (per key block J): over I > J, dV_J += P^T dO_I,
 //     dk^_J += scale dS^T q~, dT_J += G^(J-1)^T q~ -- sums owned by one
 //     workgroup, so no atomics; P and dS come from the query-major walk;
@@ -448,8 +449,48 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Query-major walk: one workgroup per (query block I >= 1, head); heaviest first.
+// Query-major up walk: one workgroup per (query block I >= 1, head); heaviest first.
 // ---------------------------------------------------------------------------
+// Down walk of the query blocks: one workgroup per (query block I >= 1, head),
+// q~^(J-1) = T_J q~^(J) from q~^(I-1) = q^ down to J = 0, each q~^(J) stored for
+// the pair (I, J), with the gate sum of the blocks strictly between I and J.
+// One product per step on two LDS tiles, so four workgroups share a compute
+// unit and hide each other's latency.
+template <typename SC>
+__global__ __launch_bounds__(kT, 4) void bwd_down_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) float sm[2 * kTile];
+    float *bQt = sm, *bT = bQt + kTile;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nb = a.nb, hc = a.hc;
+    const int gl = blockIdx.x % hc, I = nb - 1 - blockIdx.x / hc;
+    const BwdLayout &ly = a.ly;
+    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
+    const float *TT = (const float *)(ws + ly.tt), *tot = (const float *)(ws + ly.tot);
+    float *MID = (float *)(ws + ly.mid);
+    SC *QS = (SC *)(ws + ly.qs);
+    const int row0 = I * kC;
+
+    g2l(bQt, (const float *)(ws + ly.qh) + row0 * kD, tid);
+    float mid = 0.f;
+    if (tid == 0) MID[pair_index(I, I - 1)] = 0.f;
+    Stage rT;
+    if (I - 1 >= 1) gload(rT, TT + (int64_t)(I - 1) * kD * kD, tid);
+    for (int J = I - 1; J >= 1; --J) {  // bQt holds q~^(J)
+        lstore(bT, rT, tid);
+        __syncthreads();
+        l2g_sc(QS + pair_index(I, J) * kC * kD, bQt, tid);
+        if (J - 1 >= 1) gload(rT, TT + (int64_t)(J - 1) * kD * kD, tid);  // next step's transition
+        f32x8 acc = zero8();
+        mm(acc, nat(bQt), tr(bT), lane, wave);  // q~^(J-1) = T_J q~^(J) (rows: Q~ T^T)
+        __syncthreads();
+        store_lds(bQt, acc, lane, wave, [](int, int, float x) { return x; });
+        mid += tot[J];
+        if (tid == 0) MID[pair_index(I, J - 1)] = mid;
+    }
+    __syncthreads();
+    l2g_sc(QS + pair_index(I, 0) * kC * kD, bQt, tid);
+}
+
 template <typename SC>
 __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float sm[8 * kTile + 4 * kC];
@@ -461,42 +502,16 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
     const int gl = blockIdx.x % hc, I = nb - 1 - blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
-    const float *TT = (const float *)(ws + ly.tt), *TTt = (const float *)(ws + ly.ttt), *KH = (const float *)(ws + ly.kh);
+    const float *TTt = (const float *)(ws + ly.ttt), *KH = (const float *)(ws + ly.kh);
     const SC *VF = (const SC *)(ws + ly.vf);
-    const float *tot = (const float *)(ws + ly.tot);
-    float *MID = (float *)(ws + ly.mid), *CSP = (float *)(ws + ly.csp);
+    const float *MID = (const float *)(ws + ly.mid);
+    float *CSP = (float *)(ws + ly.csp);
     SC *QS = (SC *)(ws + ly.qs), *GS = (SC *)(ws + ly.gs), *PS = (SC *)(ws + ly.ps), *DS = (SC *)(ws + ly.ds);
     const float scale = a.scale;
     const int row0 = I * kC;
 
-    // down: q~^(J) for J = I-1 .. 0
-    g2l(bQt, (const float *)(ws + ly.qh) + row0 * kD, tid);
-    float mid = 0.f;
-    {
-        SC *dst = QS + pair_index(I, I - 1) * kC * kD;
-        const float *src = (const float *)(ws + ly.qh) + row0 * kD;
-        for (int e = tid; e < kC * kD; e += kT) dst[e] = Elem<SC>::from_float(src[e]);
-    }
-    if (tid == 0) MID[pair_index(I, I - 1)] = 0.f;
     Stage rT, rK;
     typename StageOf<SC>::T rQ, rV;
-    if (I - 1 >= 1) gload(rT, TT + (int64_t)(I - 1) * kD * kD, tid);
-    for (int J = I - 1; J >= 1; --J) {  // bQt holds q~^(J)
-        lstore(bT, rT, tid);
-        __syncthreads();
-        if (J < I - 1) l2g_sc(QS + pair_index(I, J) * kC * kD, bQt, tid);  // q^ = q~^(I-1) is stored above
-        if (J - 1 >= 1) gload(rT, TT + (int64_t)(J - 1) * kD * kD, tid);  // next step's transition
-        f32x8 acc = zero8();
-        mm(acc, nat(bQt), tr(bT), lane, wave);  // q~^(J-1) = T_J q~^(J) (rows: Q~ T^T)
-        __syncthreads();
-        store_lds(bQt, acc, lane, wave, [](int, int, float x) { return x; });
-        mid += tot[J];
-        if (tid == 0) MID[pair_index(I, J - 1)] = mid;
-    }
-    if (I >= 2) {
-        __syncthreads();
-        l2g_sc(QS + pair_index(I, 0) * kC * kD, bQt, tid);
-    }
     // up: adjoint G
     {
         typename StageOf<SC>::T rD;
@@ -510,7 +525,6 @@ __global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
     }
     f32x8 accG = zero8();
     float rsum = 0.f;
-    __syncthreads();  // the down phase's stores of q~ and the gate sums are visible below
     gload(rQ, QS + pair_index(I, 0) * kC * kD, tid);
     gload(rK, KH, tid);
     gload(rV, VF, tid);
@@ -962,9 +976,11 @@ hipError_t launch_bwd(const BwdArgs &a0, bool bf16, hipStream_t st) {
         else hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3(a.nb, a.hc), blk, 0, st, a);
         if (a.nb > 1) {
             if (bf16) {
+                hipLaunchKernelGGL(bwd_down_kernel<uint16_t>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
                 hipLaunchKernelGGL(bwd_query_kernel<uint16_t>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
                 hipLaunchKernelGGL(bwd_key_kernel_h, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
             } else {
+                hipLaunchKernelGGL(bwd_down_kernel<float>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
                 hipLaunchKernelGGL(bwd_query_kernel<float>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
                 hipLaunchKernelGGL(bwd_key_kernel<float>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
             }
