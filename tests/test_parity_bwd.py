@@ -150,3 +150,20 @@ def test_bwd_full_workload_sampled_heads():
             bar = TOL["bf16"] * max(1.0, float(np.abs(r).max()))
             assert e <= bar, "head (%d, %d) %s: %.3e > %.3e" % (b, h, n, e, bar)
         say("  head (%d, %d) ok" % (b, h))
+
+
+@gpu
+def test_bwd_long_sequence_fox():
+    """One head at the shape of the B4 H16 L16384 d64 bf16 forget-gate workload (256 blocks, 32640 block
+    pairs), every gradient element against the oracle."""
+    say("case bwd bf16 L16384 fox one head")
+    x, dout, dlse, _, _, grads = run_case(1, 1, 16384, "bf16", seed=21, fox=True)
+    compare(x, dout, dlse, grads, "bf16", what="L16384 fox")
+
+
+@gpu
+def test_bwd_fp32_many_levels():
+    """fp32 with the gate at L = 1500 (24 blocks): the carried queries and the adjoint run 23 levels."""
+    say("case bwd fp32 L1500 fox")
+    x, dout, dlse, _, _, grads = run_case(1, 1, 1500, "f32", seed=22, fox=True)
+    compare(x, dout, dlse, grads, "f32", what="L1500")
