@@ -36,21 +36,29 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 template <typename S, int D>
 struct PrepCfg {
     static constexpr bool kBf = sizeof(S) == 2;
-    static constexpr int PAD = 16 / (int)sizeof(S);
+    // Row padding.  fp32: 4 elements, rows stay 16-byte aligned.  bf16: 12 elements, a
+    // row pitch of 38 (d = 64) or 70 (d = 128) dwords: the 8-byte fragment reads of 32
+    // consecutive rows then cover all 64 banks once, and the 2-byte transposed reads,
+    // whose lane halves sit 4 rows apart, fall on disjoint banks (a 16-byte pad, 36
+    // dwords, paired the rows r and r + 16 on the same banks); rows are 8-byte aligned
+    // only, so 16-byte accesses to them are split (lds_store16 / lds_load16).
+    static constexpr int PAD = kBf ? 12 : 4;
     static constexpr int SP = 64 + PAD;    // padded row stride of [.][64] matrices (X, Y, A, W^T, V^T)
     static constexpr int SPD = D + PAD;    // padded row stride of [64][D] matrices (W, Q, K)
     static constexpr int MAT = 64 * SP;    // one 64 x 64 matrix
     static constexpr int MATD = 64 * SPD;  // one 64 x D matrix, token rows
     static constexpr int MATT = D * SP;    // one D x 64 matrix, head-dimension rows
     // G and E of the triangular solve: fp32, only the ten 16 x 16 tiles on or
-    // below the diagonal, tile (I, K) at TS * (I (I + 1) / 2 + K), row pitch TP.
-    static constexpr int TP = 20, TS = 16 * TP;
+    // below the diagonal, tile (I, K) at TS * (I (I + 1) / 2 + K), row pitch TP
+    // (unpadded: the solve runs while the other workgroups of the compute unit
+    // keep it busy, and the LDS it saves keeps three workgroups per compute unit).
+    static constexpr int TP = 16, TS = 16 * TP;
     // W, X, Y live for the whole kernel.  bf16 also keeps W^T (fp32 has no
     // room for transposed copies and reads them with a stride instead) in W's
     // slot once the products with W are done, written from registers.  A
     // second region is reused: Q, K while the products with them run, then G
     // and E for the triangular solve, then A (fp32) or A^T (bf16; A is read
-    // from it with a stride) and V^T.  At D = 64, bf16, this is 53.8 KB, so
+    // from it with a stride) and V^T.  At D = 64, bf16, this is 49 KiB, so
     // three workgroups share a CU.
     static constexpr bool kWtLate = kBf;
     static constexpr int WSLOT = kWtLate ? cmax(MATD, MATT) : MATD;
@@ -61,7 +69,7 @@ struct PrepCfg {
 };
 
 // Offset (floats) of tile (I, K), K <= I, in the packed lower-triangular tile store.
-__device__ __forceinline__ int tri_tile(int I, int K) { return (I * (I + 1) / 2 + K) * (16 * 20); }
+__device__ __forceinline__ int tri_tile(int I, int K) { return (I * (I + 1) / 2 + K) * (16 * 16); }
 
 // Fragment of the matrix view `m` (element (row, k) at row*SP + k when KC, at
 // k*SP + row otherwise; SP = row stride in elements) for rows `row`, k in [k0, k0+16).
@@ -132,6 +140,27 @@ __device__ __forceinline__ void store_tile_t(S *mat, const f32x16 &c, int m0, in
         } else {
             *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
         }
+    }
+}
+
+// 16 bytes to / from a padded LDS row: one access for fp32 (rows 16-byte
+// aligned), two 8-byte accesses for bf16 (rows 8-byte aligned).
+template <typename S>
+__device__ __forceinline__ void lds_store16(S *p, const u32x4 &v) {
+    if constexpr (sizeof(S) == 2) {
+        *(u32x2 *)p = u32x2{v.x, v.y};
+        *(u32x2 *)(p + 4) = u32x2{v.z, v.w};
+    } else {
+        *(u32x4 *)p = v;
+    }
+}
+template <typename S>
+__device__ __forceinline__ u32x4 lds_load16(const S *p) {
+    if constexpr (sizeof(S) == 2) {
+        const u32x2 a = *(const u32x2 *)p, b = *(const u32x2 *)(p + 4);
+        return u32x4{a.x, a.y, b.x, b.y};
+    } else {
+        return *(const u32x4 *)p;
     }
 }
 
@@ -226,7 +255,7 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
     static_assert(D == 64 || D == 128, "prep kernel: head dimension 64 or 128");
     typedef PrepCfg<S, D> C;
     constexpr int SP = C::SP, SPD = C::SPD, MAT = C::MAT, TP = C::TP;
-    static_assert(C::TS == 16 * 20, "tri_tile assumes 16 x 20 tiles");
+    static_assert(C::TS == 16 * 16, "tri_tile assumes 16 x 16 tiles");
     constexpr bool kBf = C::kBf, kWtLate = C::kWtLate;
     constexpr int CH = 16 / (int)sizeof(S);  // elements per 16-byte chunk
     constexpr int RCH = D / CH;              // chunks per row
@@ -300,8 +329,8 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
             const int idx = tid + 256 * s;
             const int r = idx / RCH, cc = idx % RCH;
             const bool qok = r < nvalid, wok = lane < nvalid;
-            *(u32x4 *)(sQ + r * SPD + cc * CH) = qok ? lq[s] : z4;
-            *(u32x4 *)(sK + r * SPD + cc * CH) = qok ? lk[s] : z4;
+            lds_store16<S>(sQ + r * SPD + cc * CH, qok ? lq[s] : z4);
+            lds_store16<S>(sK + r * SPD + cc * CH, qok ? lk[s] : z4);
             const int rw = lane, cw = idx / 64;
             u32x4 vw = wok ? lw[s] : z4;
             const u32x4 vv = wok ? lv[s] : z4;
@@ -338,7 +367,7 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
                 }
             }
             vreg[s] = vv;
-            *(u32x4 *)(sW + rw * SPD + cw * CH) = vw;
+            lds_store16<S>(sW + rw * SPD + cw * CH, vw);
             wreg[s] = vw;
         }
         if (tid < 64) {
@@ -382,7 +411,7 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
 #pragma unroll
         for (int c0 = 0; c0 < D; c0 += CH) {
             if (!fused) {
-                const u32x4 uw = *(const u32x4 *)(sW + lane * SPD + c0);
+                const u32x4 uw = lds_load16<S>(sW + lane * SPD + c0);
                 const S *ew = (const S *)&uw;
 #pragma unroll
                 for (int e = 0; e < CH; ++e) {
@@ -391,7 +420,7 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
                 }
             }
             if (FOX) {
-                const u32x4 uk = *(const u32x4 *)(sK + lane * SPD + c0);
+                const u32x4 uk = lds_load16<S>(sK + lane * SPD + c0);
                 const S *ek = (const S *)&uk;
 #pragma unroll
                 for (int e = 0; e < CH; ++e) {
@@ -542,7 +571,7 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
             for (int e = 0; e < 16; e += 8) {
                 const u32x4 u = {pack_bf16(av[e], av[e + 1]), pack_bf16(av[e + 2], av[e + 3]),
                                  pack_bf16(av[e + 4], av[e + 5]), pack_bf16(av[e + 6], av[e + 7])};
-                *(u32x4 *)(sAup + c * SP + rg + e) = u;
+                lds_store16<S>(sAup + c * SP + rg + e, u);
             }
         }
 #pragma unroll
