@@ -485,16 +485,20 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
     };
     auto rec_ptr = [&](int J) { return recs + (int64_t)J * REC; };
     auto tail_ptr = [&](int J) { return fk + (int64_t)J * kBlk; };
+    // The first NB - 1 records' copies, issued before the query state is loaded
+    // so that the two memory latencies overlap.
+    auto prologue = [&]() {
+#pragma unroll
+        for (int k = 0; k < (NB > 1 ? NB - 1 : 1); ++k)
+            if (Jtop - k >= 0)
+                issue_record<S, REC, NLD, NW, FOX>(rec_ptr(Jtop - k), tail_ptr(Jtop - k), srec[k], stail[k], wv, lane);
+    };
     // One walk over the key blocks J = Jtop .. 0.  All waves in step; NB - 1
     // records ahead (a single buffer is refilled after every wave is done with
     // it).  The last step waits for every copy, so no copy is in flight after
     // a full walk.
     auto walk = [&](auto bounded) {
         constexpr bool BND = decltype(bounded)::value;
-#pragma unroll
-        for (int k = 0; k < (NB > 1 ? NB - 1 : 1); ++k)
-            if (Jtop - k >= 0)
-                issue_record<S, REC, NLD, NW, FOX>(rec_ptr(Jtop - k), tail_ptr(Jtop - k), srec[k], stail[k], wv, lane);
         // one step; false when the walk stops early (skipping)
         auto body = [&](int J, auto xform) -> bool {
             constexpr bool XF = decltype(xform)::value;
@@ -589,6 +593,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
         // with the running max for the flagged waves.  The bounded walk needs no
         // more than the logits being within about +-100 (log2 units) of 0, which
         // holds for any inputs of moderate norm.
+        prologue();
         init_state(std::true_type{});
         if (skip) setup_skip();
         walk(std::true_type{});
@@ -615,6 +620,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
     }
     // ---- checked walk: the running max is tracked block by block (refreshed
     // when it grows by more than 2^kTau)
+    prologue();
     init_state(std::false_type{});
     if (skip) setup_skip();
     walk(std::false_type{});
