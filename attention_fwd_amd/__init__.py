@@ -62,8 +62,11 @@ def lib():
         L.path_decode_workspace_size.restype = sz
         L.path_decode_workspace_size.argtypes = [i, i, i64, i, ctypes.c_int]
         L.path_decode_step.restype = ctypes.c_int
-        L.path_decode_step.argtypes = [vp, vp, i64, i64, vp, vp, fp, fp, fp, vp, vp, vp, fp, i, i, i, ctypes.c_int,
+        L.path_decode_step.argtypes = [vp, vp, i64, i64, vp, vp, fp, vp, vp, vp, fp, i, i, i, ctypes.c_int,
                                        ctypes.c_float, vp, sz, vp]
+        L.path_decode_step_ex.restype = ctypes.c_int
+        L.path_decode_step_ex.argtypes = [vp, vp, i64, i64, vp, vp, fp, fp, fp, vp, vp, vp, fp, i, i, i,
+                                          ctypes.c_int, ctypes.c_float, vp, sz, vp]
         L.path_decode_cache_from_fwd.restype = ctypes.c_int
         L.path_decode_cache_from_fwd.argtypes = [vp, sz, vp, fp, vp, vp, fp, i64, i, i, i, i, ctypes.c_int, vp]
         L.path_attn_bwd_workspace_size.restype = sz
@@ -99,6 +102,17 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _record(stream, *tensors):
+    """Tensors this binding allocated (on the current stream) and a kernel on
+    `stream` uses: tell the caching allocator, so their memory is not handed
+    out again before that stream's work is done."""
+    if stream is None or stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def fwd_workspace_size(B, H, L, d, dtype=torch.bfloat16):
     return int(lib().path_attn_fwd_workspace_size(B, H, L, d, _DTYPES[dtype]))
 
@@ -132,11 +146,14 @@ def fwd(q, k, v, w, beta, logf=None, scale=None, out=None, lse=None, return_lse=
     _check(beta, "beta", torch.float32, (B, H, L), dev)
     if logf is not None:
         _check(logf, "logf", torch.float32, (B, H, L), dev)
+    mine = []
     if out is None:
         out = torch.empty_like(q)
+        mine.append(out)
     _check(out, "out", dt, (B, H, L, d), dev)
     if lse is None and return_lse:
         lse = torch.empty((B, H, L), device=dev, dtype=torch.float32)
+        mine.append(lse)
     if lse is not None:
         _check(lse, "lse", torch.float32, (B, H, L), dev)
     need = fwd_workspace_size(B, H, L, d, dt)
@@ -144,8 +161,10 @@ def fwd(q, k, v, w, beta, logf=None, scale=None, out=None, lse=None, return_lse=
         raise PathError(PATH_EUNSUPPORTED if d not in (64, 128) else PATH_EINVAL, "path_attn_fwd_workspace_size")
     if workspace is None:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+        mine.append(workspace)
     _check(workspace, "workspace", None, None, dev)
     with torch.cuda.device(dev):
+        _record(stream, *mine)
         st = lib().path_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf), _ptr(out),
                                     _ptr(lse), B, H, L, d, _DTYPES[dt], float(scale or 0.0), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(),
@@ -176,11 +195,14 @@ def fwd_fused(q, k, v, wraw, conv_w, zbeta, beta_clip=0.0, logf=None, scale=None
     _check(zbeta, "zbeta", torch.float32, (B, H, L), dev)
     if logf is not None:
         _check(logf, "logf", torch.float32, (B, H, L), dev)
+    mine = []
     if out is None:
         out = torch.empty_like(q)
+        mine.append(out)
     _check(out, "out", dt, (B, H, L, d), dev)
     if lse is None and return_lse:
         lse = torch.empty((B, H, L), device=dev, dtype=torch.float32)
+        mine.append(lse)
     if lse is not None:
         _check(lse, "lse", torch.float32, (B, H, L), dev)
     need = fwd_workspace_size(B, H, L, d, dt)
@@ -188,8 +210,10 @@ def fwd_fused(q, k, v, wraw, conv_w, zbeta, beta_clip=0.0, logf=None, scale=None
         raise PathError(PATH_EUNSUPPORTED if d not in (64, 128) else PATH_EINVAL, "path_attn_fwd_workspace_size")
     if workspace is None:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+        mine.append(workspace)
     _check(workspace, "workspace", None, None, dev)
     with torch.cuda.device(dev):
+        _record(stream, *mine)
         st = lib().path_attn_fwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(wraw), _ptr(conv_w), _ptr(zbeta),
                                        float(beta_clip), _ptr(logf), _ptr(out), _ptr(lse), B, H, L, d, _DTYPES[dt],
                                        float(scale or 0.0), _ptr(workspace),
@@ -233,7 +257,8 @@ def fwd_scan(out, lse, has_logf, workspace, scale=None, stream=None):
 
 def decode_step(kcache, vcache, n, q, w, beta, k_new=None, v_new=None, scale=None, out=None, lse=None,
                 return_lse=False, workspace=None, stream=None, logf=None, fcache=None):
-    """One PaTH decode step (path_decode_step): updates kcache rows [0, n) in place.
+    """One PaTH decode step (path_decode_step, or path_decode_step_ex with the
+    forget gate): updates kcache rows [0, n) in place.
 
     kcache, vcache: [B, H, ncap, d]; q, w, k_new, v_new: [B, H, d]; beta: [B, H] fp32.
     PaTH-FoX: logf [B, H] fp32 (log f of the current token) with fcache
@@ -262,26 +287,36 @@ def decode_step(kcache, vcache, n, q, w, beta, k_new=None, v_new=None, scale=Non
     if k_new is not None:
         _check(k_new, "k_new", dt, (B, H, d), dev)
         _check(v_new, "v_new", dt, (B, H, d), dev)
+    mine = []
     if out is None:
         out = torch.empty((B, H, d), device=dev, dtype=dt)
+        mine.append(out)
     _check(out, "out", dt, (B, H, d), dev)
     if lse is None and return_lse:
         lse = torch.empty((B, H), device=dev, dtype=torch.float32)
+        mine.append(lse)
     if lse is not None:
         _check(lse, "lse", torch.float32, (B, H), dev)
     rows = int(n) + (1 if k_new is not None else 0)
     need = decode_workspace_size(B, H, max(rows, 1), d, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=dev, dtype=torch.uint8)
+        mine.append(workspace)
     _check(workspace, "workspace", None, None, dev)
+    common = (_ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), B, H, d, _DTYPES[dt], float(scale or 0.0),
+              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     with torch.cuda.device(dev):
-        st = lib().path_decode_step(_ptr(kcache), _ptr(vcache), int(n), ncap, _ptr(q), _ptr(w), _ptr(beta),
-                                    _ptr(logf), _ptr(fcache), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), B, H,
-                                    d, _DTYPES[dt],
-                                    float(scale or 0.0), _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(), _stream(stream))
+        _record(stream, *mine)
+        if logf is None:
+            name = "path_decode_step"
+            st = lib().path_decode_step(_ptr(kcache), _ptr(vcache), int(n), ncap, _ptr(q), _ptr(w), _ptr(beta),
+                                        *common)
+        else:
+            name = "path_decode_step_ex"
+            st = lib().path_decode_step_ex(_ptr(kcache), _ptr(vcache), int(n), ncap, _ptr(q), _ptr(w), _ptr(beta),
+                                           _ptr(logf), _ptr(fcache), *common)
     if st != PATH_OK:
-        raise PathError(st, "path_decode_step")
+        raise PathError(st, name)
     return (out, lse) if (return_lse or lse is not None) else out
 
 
@@ -343,10 +378,12 @@ def bwd(q, k, v, w, beta, logf, out, lse, dout, dlse=None, scale=None, workspace
     for t, n in ((beta, "beta"), (lse, "lse"), (logf, "logf"), (dlse, "dlse")):
         if t is not None:
             _check(t, n, torch.float32, (B, H, L), dev)
+    mine = []
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), torch.empty_like(q),
                  torch.empty((B, H, L), device=dev, dtype=torch.float32),
                  torch.empty((B, H, L), device=dev, dtype=torch.float32) if logf is not None else None)
+        mine.extend(grads)
     dq, dk, dv, dw, dbeta, dlogf = grads
     for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"), (dw, "dw")):
         _check(t, n, dt, (B, H, L, d), dev)
@@ -358,8 +395,10 @@ def bwd(q, k, v, w, beta, logf, out, lse, dout, dlse=None, scale=None, workspace
         if need == 0:
             raise PathError(PATH_EUNSUPPORTED if d != 64 else PATH_EINVAL, "path_attn_bwd_workspace_size")
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+        mine.append(workspace)
     _check(workspace, "workspace", None, None, dev)
     with torch.cuda.device(dev):
+        _record(stream, *mine)
         st = lib().path_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf), _ptr(out), _ptr(lse),
                                  _ptr(dout), _ptr(dlse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(dbeta),
                                  _ptr(dlogf), B, H, L, d, _DTYPES[dt], float(scale or 0.0), _ptr(workspace),

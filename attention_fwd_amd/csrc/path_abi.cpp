@@ -147,7 +147,7 @@ float eff_scale(float scale, int d) { return scale <= 0.f ? 1.0f / std::sqrt((fl
 path_status_t path_attn_fwd_ex(const void *q, const void *k, const void *v, const void *w, const float *beta,
                                const float *logf, void *out, float *lse, int B, int H, int L, int d,
                                path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
-                               unsigned flags, void *stream) {
+                               unsigned flags, path_stream_t stream) {
     if (flags & ~PATH_FWD_SKIP_NEGLIGIBLE) return PATH_EINVAL;
     path_status_t st = fwd_check(q, k, v, w, beta, logf, out, lse, B, H, L, d, dtype, scale, workspace,
                                  workspace_bytes);
@@ -163,7 +163,7 @@ path_status_t path_attn_fwd_ex(const void *q, const void *k, const void *v, cons
 path_status_t path_attn_fwd_fused(const void *q, const void *k, const void *v, const void *wraw,
                                   const float *conv_w, const float *zbeta, float beta_clip, const float *logf,
                                   void *out, float *lse, int B, int H, int L, int d, path_dtype_t dtype, float scale,
-                                  void *workspace, size_t workspace_bytes, void *stream) {
+                                  void *workspace, size_t workspace_bytes, path_stream_t stream) {
     path_status_t st = fwd_check(q, k, v, wraw, zbeta, logf, out, lse, B, H, L, d, dtype, scale, workspace,
                                  workspace_bytes);
     if (st != PATH_OK) return st;
@@ -185,7 +185,7 @@ path_status_t path_attn_fwd_fused(const void *q, const void *k, const void *v, c
 path_status_t path_attn_fwd(const void *q, const void *k, const void *v, const void *w, const float *beta,
                             const float *logf, void *out, float *lse, int B, int H, int L, int d,
                             path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
-                            void *stream) {
+                            path_stream_t stream) {
     return path_attn_fwd_ex(q, k, v, w, beta, logf, out, lse, B, H, L, d, dtype, scale, workspace, workspace_bytes,
                             0u, stream);
 }
@@ -193,7 +193,7 @@ path_status_t path_attn_fwd(const void *q, const void *k, const void *v, const v
 path_status_t path_attn_fwd_prep(const void *q, const void *k, const void *v, const void *w, const float *beta,
                                  const float *logf, void *out, float *lse, int B, int H, int L, int d,
                                  path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
-                                 void *stream) {
+                                 path_stream_t stream) {
     path_status_t st = fwd_check(q, k, v, w, beta, logf, out, lse, B, H, L, d, dtype, scale, workspace,
                                  workspace_bytes);
     if (st != PATH_OK) return st;
@@ -203,7 +203,7 @@ path_status_t path_attn_fwd_prep(const void *q, const void *k, const void *v, co
 
 path_status_t path_attn_fwd_scan(void *out, float *lse, int has_logf, int B, int H, int L, int d,
                                  path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
-                                 void *stream) {
+                                 path_stream_t stream) {
     path_status_t st = scan_check(out, lse, B, H, L, d, dtype, scale, workspace, workspace_bytes);
     if (st != PATH_OK) return st;
     return launch_scan_stage(out, lse, has_logf != 0, B, H, L, d, dtype, eff_scale(scale, d), workspace,
@@ -215,10 +215,10 @@ size_t path_decode_workspace_size(int B, int H, int64_t n, int d, path_dtype_t d
     return dec_ws_bytes(B, H, n, d);
 }
 
-path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,
-                               const float *beta, const float *logf, float *fcache, const void *k_new,
-                               const void *v_new, void *out, float *lse, int B, int H, int d, path_dtype_t dtype,
-                               float scale, void *workspace, size_t workspace_bytes, void *stream) {
+path_status_t path_decode_step_ex(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,
+                                  const float *beta, const float *logf, float *fcache, const void *k_new,
+                                  const void *v_new, void *out, float *lse, int B, int H, int d, path_dtype_t dtype,
+                                  float scale, void *workspace, size_t workspace_bytes, path_stream_t stream) {
     if (n < 0 || ncap < 1 || n > ncap) return PATH_EINVAL;
     if ((k_new == nullptr) != (v_new == nullptr)) return PATH_EINVAL;
     if ((logf == nullptr) != (fcache == nullptr)) return PATH_EINVAL;
@@ -270,10 +270,18 @@ path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t nc
     return PATH_OK;
 }
 
+path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,
+                               const float *beta, const void *k_new, const void *v_new, void *out, float *lse, int B,
+                               int H, int d, path_dtype_t dtype, float scale, void *workspace,
+                               size_t workspace_bytes, path_stream_t stream) {
+    return path_decode_step_ex(kcache, vcache, n, ncap, q, w, beta, nullptr, nullptr, k_new, v_new, out, lse, B, H, d,
+                               dtype, scale, workspace, workspace_bytes, stream);
+}
+
 path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace_bytes, const void *v,
                                          const float *logf, void *kcache, void *vcache, float *fcache,
                                          int64_t ncap, int B, int H, int L, int d, path_dtype_t dtype,
-                                         void *stream) {
+                                         path_stream_t stream) {
     path_status_t st = fwd_sizes_ok(B, H, L, d, dtype);
     if (st != PATH_OK) return st;
     if (ncap < L || mul_chk({B, H, ncap, d, 8}) < 0) return PATH_EINVAL;
@@ -330,7 +338,7 @@ path_status_t path_attn_bwd(const void *q, const void *k, const void *v, const v
                             const float *logf, const void *out, const float *lse, const void *dout,
                             const float *dlse, void *dq, void *dk, void *dv, void *dw, float *dbeta, float *dlogf,
                             int B, int H, int L, int d, path_dtype_t dtype, float scale, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+                            size_t workspace_bytes, path_stream_t stream) {
     path_status_t st = bwd_sizes_ok(B, H, L, d, dtype);
     if (st != PATH_OK) return st;
     if (!q || !k || !v || !w || !beta || !out || !lse || !dout || !dq || !dk || !dv || !dw || !dbeta || !workspace)

@@ -338,7 +338,10 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
     static_assert(REC % (VEC * NT) == 0, "record must split evenly over the workgroup");
     __shared__ __attribute__((aligned(32))) S srec[NB][REC];
     __shared__ __attribute__((aligned(16))) float stail[NB][kBlk];
-    __shared__ int sdone[NW];  // skipping: this wave needs no more key blocks
+    // skipping: this wave needs no more key blocks.  Two slots: step it reads slot it & 1 after
+    // its barrier and every wave writes its verdict for step it + 1 into the other slot, so a
+    // wave that runs ahead never changes flags that a slower wave of the same step still reads.
+    __shared__ int sdone[2][NW];
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const FwdLayout lay = fwd_layout(a.B, a.H, a.L, D, sizeof(S));
@@ -462,7 +465,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
                 for (int r = 0; r < 16; ++r) ss += w.qt[dt][ct][r] * w.qt[dt][ct][r];
             qbound[ct] = sqrtf(other_half_sum(ss)) * (1.f + 0x1p-10f) * km;  // rounded up; inf if not contractive
         }
-        if (lane == 0) sdone[wv] = wdone;
+        if (lane == 0) sdone[0][wv] = wdone;
     };
     // reference: the running max (checked walk) or the diagonal block's max, a lower bound of the
     // final max (bounded walk, whose m stays 0)
@@ -517,8 +520,8 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
             if (skip) {
                 bool all = true;
 #pragma unroll
-                for (int v2 = 0; v2 < NW; ++v2) all = all && sdone[v2];
-                if (all) return false;  // uniform: every wave read the same flags after the barrier
+                for (int v2 = 0; v2 < NW; ++v2) all = all && sdone[it & 1][v2];
+                if (all) return false;  // uniform: slot it & 1 is not written again before the next barrier
             }
             if (NB > 1 && J - (NB - 1) >= 0) {
                 const int jn = J - (NB - 1);
@@ -537,7 +540,7 @@ __global__ __launch_bounds__(64 * (FwdCfg<S, D>::NW), (FwdCfg<S, D>::WG_PER_CU))
             }
             if (skip) {  // bound for blocks J - 1 and earlier (off now sits at the J-1 / J boundary)
                 wdone = wdone || negligible(std::integral_constant<bool, BND>{});
-                if (lane == 0) sdone[wv] = wdone;
+                if (lane == 0) sdone[(it + 1) & 1][wv] = wdone;
             }
             if (NB == 1 && J >= 1) {
                 __syncthreads();  // every wave is done with the buffer

@@ -48,6 +48,7 @@ DEC_WORKLOAD = "decode_N32768_bf16"
 SWEEP_WORKLOADS = ["sweep_L1024_d64_bf16", "sweep_L2048_d64_bf16", "sweep_L8192_d64_bf16", "sweep_L4096_d128_bf16",
                    "lm760m_L4096_bf16", "fox_L16384_bf16"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_B32H32L4096_decode_N32768.txt")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_fwd_B32H32L4096_decode_N32768.txt")
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_B32H32L4096.txt")
 COPY_BYTES = 1 << 30        # calibration copy of the counter run
 KERNEL_SOURCES = {
@@ -88,6 +89,35 @@ def read_traffic(kernel, path=TRAFFIC_FILE):
         return float(kv[kernel + ".hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def read_mfma_flop(kernel="path_fwd_kernel", path=MFMA_FILE):
+    """Matrix-core flop one launch of `kernel` executes, from the committed counter summary
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), if the counters were taken on the current kernel source."""
+    try:
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get(kernel + ".source_sha256_16") != kernel_hash(kernel):
+            return None
+        return float(kv[kernel + ".mfma_flop_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_model():
+    """Model name of the host CPU (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def bench_forward(steps, warmup, name=FWD_WORKLOAD):
@@ -286,11 +316,13 @@ def bench_decode(steps, gate=False):
         evs[t][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    step_ms = sum(per) / steps
     nbytes = 3.0 * B * H * n * d * kc.element_size() + (4.0 * B * H * n if gate else 0.0)
     del x, kc, vc, fc, lf, ws
     torch.cuda.empty_cache()
-    return dict(B=B, H=H, n=n, d=d, steps=steps, step_ms=step_ms, wall_s=wall, bytes=nbytes)
+    return dict(B=B, H=H, n=n, d=d, steps=steps, step_ms=step_ms, wall_s=wall, bytes=nbytes,
+                ms_median=per[len(per) // 2], ms_min=per[0])
 
 
 def bench_cache(steps, f):
@@ -458,7 +490,7 @@ def cpu_baseline(x, target_s):
         nh = int(min(G, max(1, round(nh * target_s / max(t, 1e-3)))))
         t = run(nh)
     tflops = 4.0 * nh * L * L * d / t / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d of %d heads of the B%d H%d L%d d%d workload, every row, %.1f s" % (nh, G, B, H, L, d, t)}
 
 
@@ -486,7 +518,7 @@ def cpu_baseline_backward(target_s, name=FWD_WORKLOAD):
         nh = int(max(1, round(nh * target_s / max(t, 1e-3))))
         t = run(nh)
     tflops = 8.0 * nh * L * L * d / t / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d heads of L%d d%d, every row, %.1f s (work unit 8 L^2 d per head)" % (nh, L, d, t)}
 
 
@@ -511,7 +543,7 @@ def cpu_baseline_decode(target_s):
         nh = int(min(c["B"] * c["H"], max(1, round(nh * target_s / max(t, 1e-3)))))
         t = run(nh)
     gbs = 3.0 * nh * n * d * 2 / t / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d of the %d heads of the n%d d%d decode workload, one step, %.1f s (bytes counted as on the GPU, bf16)" % (
                 nh, c["B"] * c["H"], n, d, t)}
 
@@ -591,6 +623,7 @@ def main():
     value = f["flops"] / (f["ms_per_step"] * 1e-3) / 1e12
     scan_tflops = f["flops"] / (f["scan_ms"] * 1e-3) / 1e12
     traffic = read_traffic("path_fwd_kernel")
+    mfma_flop = read_mfma_flop("path_fwd_kernel")
     dec_gbs = dres["bytes"] / (dres["step_ms"] * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
@@ -607,9 +640,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": FWD_WORKLOAD, "B": f["B"], "H": f["H"], "L": f["L"], "d": f["d"], "causal": True,
                    "decode_workload": DEC_WORKLOAD},
-        "roofline": {"bound": "mfma", "kernel": "path_fwd_kernel (scan stage: bounded walk + redo launch)", "achieved": round(scan_tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(scan_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic},
+        "roofline": {"bound": "mfma", "kernel": "path_fwd_kernel (scan stage: bounded walk + redo launch)",
+                     "achieved": round(scan_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(scan_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "whole_pass_frac": round(value / PEAK_BF16_TFLOPS, 4),
+                     "declared_flop_per_launch": f["flops"],
+                     "mfma_flop_executed_per_launch": mfma_flop,
+                     "executed_over_declared": round(mfma_flop / f["flops"], 4) if mfma_flop else None},
         "forward": {"ms_per_step": round(f["ms_per_step"], 4), "ms_median": round(f["ms_median"], 4),
                     "ms_min": round(f["ms_min"], 4),
                     "TFLOP_per_s_fa_convention": round(2.0 * f["B"] * f["H"] * f["L"] ** 2 * f["d"] /
@@ -618,7 +655,8 @@ def main():
                     "scan_ms": round(f["scan_ms"], 4), "frac_of_peak_whole_pass": round(value / PEAK_BF16_TFLOPS, 4),
                     "tokens_per_s": round(f["B"] * f["L"] / (f["ms_per_step"] * 1e-3)),
                     "flop_per_step": f["flops"]},
-        "decode": {"ms_per_step": round(dres["step_ms"], 4), "GB_per_s": round(dec_gbs, 1),
+        "decode": {"ms_per_step": round(dres["step_ms"], 4), "ms_median": round(dres["ms_median"], 4),
+                   "ms_min": round(dres["ms_min"], 4), "GB_per_s": round(dec_gbs, 1),
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                                 "traffic": read_traffic("path_decode_kernel")},

@@ -16,8 +16,9 @@
  *
  * All functions are synchronous on the host: argument errors are reported
  * before anything is enqueued.  Kernels run asynchronously on `stream`
- * (a hipStream_t; NULL = the default stream) and results are valid once
- * that stream's work has completed.  The library keeps no pointer after a
+ * (path_stream_t is hipStream_t, declared here without the HIP headers;
+ * NULL = the default stream) and results are valid once that stream's work
+ * has completed.  The library keeps no pointer after a
  * call returns, allocates no device memory and holds no mutable global
  * state; calls from several host threads are safe (calls that share output
  * or workspace memory must be ordered by the caller).
@@ -45,7 +46,16 @@
 extern "C" {
 #endif
 
-#define PATH_ABI_VERSION 4
+/*
+ * ABI version.  It changes only when an existing entry point changes its
+ * parameters or meaning; new capabilities come as new entry points (the
+ * _ex variants), which leave it unchanged.
+ */
+#define PATH_ABI_VERSION 1
+
+/* The HIP stream type: hipStream_t is `struct ihipStream_t *`, so a
+ * hipStream_t converts to this type without a cast. */
+typedef struct ihipStream_t *path_stream_t;
 
 typedef enum {
     PATH_OK = 0,
@@ -95,7 +105,7 @@ size_t path_attn_fwd_workspace_size(int B, int H, int L, int d, path_dtype_t dty
 path_status_t path_attn_fwd(const void *q, const void *k, const void *v, const void *w, const float *beta,
                             const float *logf, void *out, float *lse, int B, int H, int L, int d,
                             path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
-                            void *stream);
+                            path_stream_t stream);
 
 /*
  * path_attn_fwd with options.  flags is a bitwise OR of:
@@ -117,7 +127,7 @@ path_status_t path_attn_fwd(const void *q, const void *k, const void *v, const v
 path_status_t path_attn_fwd_ex(const void *q, const void *k, const void *v, const void *w, const float *beta,
                                const float *logf, void *out, float *lse, int B, int H, int L, int d,
                                path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
-                               unsigned flags, void *stream);
+                               unsigned flags, path_stream_t stream);
 
 /*
  * PaTH forward with the producer of w and beta fused into it.
@@ -149,7 +159,7 @@ path_status_t path_attn_fwd_ex(const void *q, const void *k, const void *v, cons
 path_status_t path_attn_fwd_fused(const void *q, const void *k, const void *v, const void *wraw,
                                   const float *conv_w, const float *zbeta, float beta_clip, const float *logf,
                                   void *out, float *lse, int B, int H, int L, int d, path_dtype_t dtype, float scale,
-                                  void *workspace, size_t workspace_bytes, void *stream);
+                                  void *workspace, size_t workspace_bytes, path_stream_t stream);
 
 /*
  * The two stages of path_attn_fwd, for callers that schedule or time them
@@ -169,10 +179,10 @@ path_status_t path_attn_fwd_fused(const void *q, const void *k, const void *v, c
 path_status_t path_attn_fwd_prep(const void *q, const void *k, const void *v, const void *w, const float *beta,
                                  const float *logf, void *out, float *lse, int B, int H, int L, int d,
                                  path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
-                                 void *stream);
+                                 path_stream_t stream);
 path_status_t path_attn_fwd_scan(void *out, float *lse, int has_logf, int B, int H, int L, int d,
                                  path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
-                                 void *stream);
+                                 path_stream_t stream);
 
 /* Workspace bytes that path_decode_step needs (0 if the sizes are invalid). */
 size_t path_decode_workspace_size(int B, int H, int64_t n, int d, path_dtype_t dtype);
@@ -188,16 +198,9 @@ size_t path_decode_workspace_size(int B, int H, int64_t n, int d, path_dtype_t d
  * non-NULL they are stored at row n AFTER the update (the newest key has the
  * empty product) and the query attends to n+1 rows; otherwise to n rows.
  *
- * PaTH-FoX ([IPX] s.4): with logf and fcache (both or neither) row j's logit
- * gets sum_{s=j+1..t} log f_s = c_t - c_j, where fcache holds
- * c_j = sum_{s<=j} log f_s for the cached rows and c_t = c_{n-1} + logf_t
- * (c_{-1} = 0); with k_new, c_t is stored at fcache row n.
- *
  * kcache, vcache : [B, H, ncap, d] element type `dtype`; rows >= n (+1) untouched
  * n              : rows in use, 0 <= n <= ncap (n + 1 <= ncap with k_new; at least one row must attend)
  * q, w           : [B, H, d] element type `dtype`; beta: [B, H] fp32
- * logf           : [B, H] fp32 log f_t of the current token, or NULL
- * fcache         : [B, H, ncap] fp32 gate cache (read rows [0, n), row n written with k_new), or NULL
  * k_new, v_new   : [B, H, d] or both NULL
  * out            : [B, H, d] element type `dtype`; lse: [B, H] fp32 or NULL
  * scale          : <= 0 selects 1/sqrt(d)
@@ -205,13 +208,29 @@ size_t path_decode_workspace_size(int B, int H, int64_t n, int d, path_dtype_t d
  *
  * A cache row that went through steps j+1..t holds H_t ... H_{j+1} k_j; as
  * every H is symmetric its dot product with q_t equals the forward logit
- * k_j^T (H_{j+1} ... H_t) q_t.
+ * k_j^T (H_{j+1} ... H_t) q_t.  Buffers must not overlap (PATH_EINVAL).
  */
 path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,
-                               const float *beta, const float *logf, float *fcache, const void *k_new,
-                               const void *v_new, void *out, float *lse,
+                               const float *beta, const void *k_new, const void *v_new, void *out, float *lse,
                                int B, int H, int d, path_dtype_t dtype, float scale, void *workspace,
-                               size_t workspace_bytes, void *stream);
+                               size_t workspace_bytes, path_stream_t stream);
+
+/*
+ * path_decode_step with the PaTH-FoX forget gate ([IPX] s.4): with logf and
+ * fcache (both or neither; both NULL is exactly path_decode_step) row j's
+ * logit gets sum_{s=j+1..t} log f_s = c_t - c_j, where fcache holds
+ * c_j = sum_{s<=j} log f_s for the cached rows and c_t = c_{n-1} + logf_t
+ * (c_{-1} = 0); with k_new, c_t is stored at fcache row n.
+ *
+ * logf           : [B, H] fp32 log f_t of the current token, or NULL
+ * fcache         : [B, H, ncap] fp32 gate cache (rows [0, n) read, row n written with k_new), or NULL
+ * Every other argument, the workspace and the errors are those of
+ * path_decode_step.
+ */
+path_status_t path_decode_step_ex(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,
+                                  const float *beta, const float *logf, float *fcache, const void *k_new,
+                                  const void *v_new, void *out, float *lse, int B, int H, int d, path_dtype_t dtype,
+                                  float scale, void *workspace, size_t workspace_bytes, path_stream_t stream);
 
 /*
  * Decode cache of a prefix from its forward pass ([TS] s.3: prefill, then
@@ -241,7 +260,7 @@ path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t nc
 path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace_bytes, const void *v,
                                          const float *logf, void *kcache, void *vcache, float *fcache,
                                          int64_t ncap, int B, int H, int L, int d, path_dtype_t dtype,
-                                         void *stream);
+                                         path_stream_t stream);
 
 /*
  * Workspace bytes for path_attn_bwd (0 if the sizes are invalid or not
@@ -287,7 +306,7 @@ path_status_t path_attn_bwd(const void *q, const void *k, const void *v, const v
                             const float *logf, const void *out, const float *lse, const void *dout,
                             const float *dlse, void *dq, void *dk, void *dv, void *dw, float *dbeta, float *dlogf,
                             int B, int H, int L, int d, path_dtype_t dtype, float scale, void *workspace,
-                            size_t workspace_bytes, void *stream);
+                            size_t workspace_bytes, path_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -27,9 +27,30 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), "missing export " + n
 
 
+def declared_params(name):
+    """Parameter names of a function declared in the header, in order."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b%s\s*\(([^)]*)\)\s*;" % name, src)
+    assert m, name
+    return [re.findall(r"(\w+)\s*$", p.strip())[0] for p in m.group(1).split(",")]
+
+
+def test_entry_points_keep_their_parameter_lists():
+    """The two calls of the problem statement keep the frozen parameter lists;
+    options come through the _ex variants, which only add parameters."""
+    assert declared_params("path_attn_fwd") == [
+        "q", "k", "v", "w", "beta", "logf", "out", "lse", "B", "H", "L", "d", "dtype", "scale", "workspace",
+        "workspace_bytes", "stream"]
+    plain = ["kcache", "vcache", "n", "ncap", "q", "w", "beta", "k_new", "v_new", "out", "lse", "B", "H", "d",
+             "dtype", "scale", "workspace", "workspace_bytes", "stream"]
+    assert declared_params("path_decode_step") == plain
+    assert declared_params("path_decode_step_ex") == plain[:7] + ["logf", "fcache"] + plain[7:]
+    assert declared_params("path_attn_fwd_ex") == declared_params("path_attn_fwd")[:-1] + ["flags", "stream"]
+
+
 def test_version_and_status_strings():
     lib = pa.lib()
-    assert lib.path_abi_version() == 4
+    assert lib.path_abi_version() == 1
     for s in range(4):
         assert lib.path_status_string(s)
     assert lib.path_status_string(99) == b"unknown status"
@@ -91,16 +112,19 @@ def test_fwd_rejects_bad_arguments(over, status):
     assert fwd_call(**over) == status
 
 
-def dec_call(**over):
+def dec_call(ex=True, **over):
     args = dict(kc=P(0), vc=ctypes.c_void_p(A * 40), n=100, ncap=100, q=P(80), w=P(81), beta=P(82), lf=None, fc=None,
                 kn=None, vn=None,
                 out=P(83), lse=None, B=1, H=1, d=64, dtype=BF, scale=0.0, ws=P(84), wsb=1 << 30, stream=None)
     args.update(over)
-    return pa.lib().path_decode_step(args["kc"], args["vc"], args["n"], args["ncap"], args["q"], args["w"],
-                                     args["beta"], args["lf"], args["fc"], args["kn"], args["vn"], args["out"],
-                                     args["lse"], args["B"],
-                                     args["H"], args["d"], args["dtype"], args["scale"], args["ws"], args["wsb"],
-                                     args["stream"])
+    a = args
+    rest = (a["kn"], a["vn"], a["out"], a["lse"], a["B"], a["H"], a["d"], a["dtype"], a["scale"], a["ws"], a["wsb"],
+            a["stream"])
+    if ex:
+        return pa.lib().path_decode_step_ex(a["kc"], a["vc"], a["n"], a["ncap"], a["q"], a["w"], a["beta"], a["lf"],
+                                            a["fc"], *rest)
+    assert a["lf"] is None and a["fc"] is None
+    return pa.lib().path_decode_step(a["kc"], a["vc"], a["n"], a["ncap"], a["q"], a["w"], a["beta"], *rest)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -123,6 +147,8 @@ def dec_call(**over):
 ])
 def test_decode_rejects_bad_arguments(over, status):
     assert dec_call(**over) == status
+    if "lf" not in over and "fc" not in over:
+        assert dec_call(ex=False, **over) == status  # the plain entry point validates the same way
 
 
 def cache_call(**over):

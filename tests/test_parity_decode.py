@@ -139,6 +139,50 @@ def test_decode_workload_full_size():
 
 
 @gpu
+def test_decode_workload_64_steps_against_carried_oracle():
+    """The whole decode workload as timed: B16 H32, 32768 cached bf16 rows, 64 steps with fresh (q, w, beta),
+    every key updated in place each step.  On four heads the oracle keeps its OWN fp64 cache, carried from
+    the original bf16 rows through the same 64 steps, so the drift the bf16 cache accumulates (each step
+    rounds every key) enters the comparison.  Every step: out within 2e-2 absolute and relative to max|o|,
+    lse within 1e-2.  After the last step every key row's 2-norm error against the fp64 row is within
+    ((1 + u')^64 - 1) times the original row's 2-norm, u' = 2^-8 (1 + 2^-7): a step rounds each element to
+    bf16 (relative error at most 2^-8) and evaluates k - beta (w.k) w in fp32 (well inside the extra 2^-7),
+    every transition is a contraction (beta ||w||^2 <= 1.98 (1 + 2^-8) < 2), so an error carried from earlier
+    steps does not grow, and the row being rounded is at most the exact row plus that error."""
+    c = pathgen.WORKLOADS["decode_N32768_bf16"]
+    B, H, n, d, T = c["B"], c["H"], c["n"], c["d"], c["steps"]
+    G = B * H
+    heads = [0, 5, 300, G - 1]
+    say("case decode workload, %d steps, oracle cache carried on heads %s" % (T, heads))
+    x = pathgen.decode_inputs(B, H, n, d, steps=T, dtype="bf16", seed=0, clip=1.98, device="cuda")
+    kc, vc = x["kcache"], x["vcache"]
+    k0 = kc.reshape(G, n, d)[heads].cpu()
+    rk = to_np(k0)
+    rv = to_np(vc.reshape(G, n, d)[heads])
+    worst = dict(out=0.0, rel=0.0, lse=0.0)
+    for t in range(T):
+        out, lse = pa.decode_step(kc, vc, n, x["q"][t], x["w"][t], x["beta"][t], return_lse=True)
+        qs = x["q"][t].reshape(G, d)[heads].cpu()
+        ws = x["w"][t].reshape(G, d)[heads].cpu()
+        bs = x["beta"][t].reshape(G)[heads].cpu()
+        rk, _, ro, rl = oracle.decode(rk, rv, n, qs, ws, bs)
+        torch.cuda.synchronize()
+        og, lg = to_np(out.reshape(G, d)[heads]), to_np(lse.reshape(G)[heads])
+        eo, el = max_abs(og, ro), max_abs(lg, rl)
+        rel = eo / max(float(np.abs(ro).max()), 1e-30)
+        worst = dict(out=max(worst["out"], eo), rel=max(worst["rel"], rel), lse=max(worst["lse"], el))
+        if t in (0, 31, T - 1):
+            say("  step %d: out %.2e (rel %.2e) lse %.2e" % (t + 1, eo, rel, el))
+        assert eo <= 2e-2 and rel <= 2e-2 and el <= 1e-2, "step %d: out %.3e rel %.3e lse %.3e" % (t + 1, eo, rel, el)
+    kg = to_np(kc.reshape(G, n, d)[heads])
+    row_err = np.linalg.norm(kg - rk, axis=-1)
+    bound = ((1 + 2.0 ** -8 * (1 + 2.0 ** -7)) ** T - 1) * np.linalg.norm(to_np(k0), axis=-1)
+    say("  worst over %d steps: out %.2e (rel %.2e) lse %.2e; key drift max-abs %.3e, row 2-norm / bound %.3f"
+        % (T, worst["out"], worst["rel"], worst["lse"], float(np.abs(kg - rk).max()), float((row_err / bound).max())))
+    assert (row_err <= bound).all()
+
+
+@gpu
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_reproduces_forward_fp32(d):
     """Decoding token by token from an empty cache gives the forward pass's rows."""

@@ -93,8 +93,9 @@ def test_fwd_bf16_d128_small(B, H, L, fox):
 
 
 @gpu
-def test_fwd_bf16_beta_extremes():
-    """beta at the ends of its range: near 0 (plain attention) and exactly 2 (reflections) in fp32."""
+def test_fwd_fp32_beta_extremes():
+    """fp32 inputs with beta at the ends of its range: 0 (plain attention), exactly 2 (reflections) and 1
+    (projections)."""
     B, H, L, d = 1, 2, 300, 64
     for bval in (0.0, 2.0, 1.0):
         x = pathgen.fwd_inputs(B, H, L, d, "f32", seed=7, device="cuda")
@@ -104,6 +105,27 @@ def test_fwd_bf16_beta_extremes():
         ro, rl = oracle.fwd(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["w"].cpu(), beta.cpu())
         assert max_abs(to_np(out), ro) <= 1e-4
         assert max_abs(to_np(lse), rl) <= 1e-4
+
+
+@gpu
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bval", [0.0, 1.98], ids=["beta0", "beta1.98"])
+@pytest.mark.parametrize("fox", [False, True], ids=["path", "fox"])
+def test_fwd_bf16_beta_edges_long(d, bval, fox):
+    """bf16 inputs over a long sequence (L = 2048, 32 key blocks) with beta held at an end of the range the
+    bf16 workloads use: 0 (every transition is the identity: plain causal attention) and the 1.98 clip
+    (near-reflections, where the pages warn that bf16 products of transitions lose accuracy).  Flat bars."""
+    B, H, L = 1, 2, 2048
+    say("case bf16 beta=%g d%d L%d fox=%s" % (bval, d, L, fox))
+    x = pathgen.fwd_inputs(B, H, L, d, "bf16", seed=8 + d, fox=fox, clip=1.98, device="cuda")
+    beta = torch.full((B, H, L), bval, device="cuda")
+    out, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], beta, x["logf"], return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.fwd(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["w"].cpu(), beta.cpu(),
+                        x["logf"].cpu() if fox else None)
+    eo, el = max_abs(to_np(out), ro), max_abs(to_np(lse), rl)
+    say("  max-abs out %.3e  lse %.3e" % (eo, el))
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
 
 
 @gpu
