@@ -13,12 +13,12 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_fused", "fwd_prep", "fwd_scan", "decode_step", "decode_cache_from_fwd", "fwd_workspace_size",
-           "decode_workspace_size", "bwd", "bwd_workspace_size", "lib", "PathError", "PATH_OK", "PATH_EINVAL", "PATH_EUNSUPPORTED", "PATH_EHIP", "PATH_DTYPE_F32", "PATH_DTYPE_BF16",
+           "decode_workspace_size", "bwd", "bwd_workspace_size", "lib", "PathError", "PATH_OK", "PATH_EINVAL", "PATH_EUNSUPPORTED", "PATH_EHIP", "PATH_ESCRATCH", "decode_step_noalloc", "PATH_DTYPE_F32", "PATH_DTYPE_BF16",
            "PATH_FWD_SKIP_NEGLIGIBLE"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpath_attn.so")
 
-PATH_OK, PATH_EINVAL, PATH_EUNSUPPORTED, PATH_EHIP = 0, 1, 2, 3
+PATH_OK, PATH_EINVAL, PATH_EUNSUPPORTED, PATH_EHIP, PATH_ESCRATCH = 0, 1, 2, 3, 4
 PATH_DTYPE_F32, PATH_DTYPE_BF16 = 0, 1
 _DTYPES = {torch.float32: PATH_DTYPE_F32, torch.bfloat16: PATH_DTYPE_BF16}
 
@@ -67,6 +67,11 @@ def lib():
         L.path_decode_step_ex.restype = ctypes.c_int
         L.path_decode_step_ex.argtypes = [vp, vp, i64, i64, vp, vp, fp, fp, fp, vp, vp, vp, fp, i, i, i,
                                           ctypes.c_int, ctypes.c_float, vp, sz, vp]
+        L.path_decode_noalloc_max_bytes.restype = sz
+        L.path_decode_noalloc_max_bytes.argtypes = []
+        L.path_decode_step_noalloc.restype = ctypes.c_int
+        L.path_decode_step_noalloc.argtypes = [vp, vp, i64, i64, vp, vp, fp, fp, fp, vp, vp, vp, fp, i, i, i,
+                                               ctypes.c_int, ctypes.c_float, vp]
         L.path_decode_cache_from_fwd.restype = ctypes.c_int
         L.path_decode_cache_from_fwd.argtypes = [vp, sz, vp, fp, vp, vp, fp, i64, i, i, i, i, ctypes.c_int, vp]
         L.path_attn_bwd_workspace_size.restype = sz
@@ -318,6 +323,44 @@ def decode_step(kcache, vcache, n, q, w, beta, k_new=None, v_new=None, scale=Non
     if st != PATH_OK:
         raise PathError(st, name)
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_step_noalloc(kcache, vcache, n, q, w, beta, out, k_new=None, v_new=None, scale=None, lse=None,
+                        stream=None, logf=None, fcache=None):
+    """decode_step through path_decode_step_noalloc: no workspace, the library's fixed
+    scratch instead (calls overlapping on one device race).  The caller passes out
+    (and lse, if wanted); nothing is allocated.  Returns out (and lse when given)."""
+    if kcache.dim() != 4:
+        raise ValueError("kcache must be [B, H, ncap, d]")
+    B, H, ncap, d = kcache.shape
+    dt = kcache.dtype
+    if dt not in _DTYPES:
+        raise ValueError("dtype must be bfloat16 or float32")
+    dev = kcache.device
+    _check(kcache, "kcache", dt, (B, H, ncap, d), dev)
+    _check(vcache, "vcache", dt, (B, H, ncap, d), dev)
+    for t, nm in ((q, "q"), (w, "w"), (out, "out")):
+        _check(t, nm, dt, (B, H, d), dev)
+    _check(beta, "beta", torch.float32, (B, H), dev)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if (logf is None) != (fcache is None):
+        raise ValueError("logf and fcache go together")
+    if logf is not None:
+        _check(logf, "logf", torch.float32, (B, H), dev)
+        _check(fcache, "fcache", torch.float32, (B, H, ncap), dev)
+    if k_new is not None:
+        _check(k_new, "k_new", dt, (B, H, d), dev)
+        _check(v_new, "v_new", dt, (B, H, d), dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H), dev)
+    with torch.cuda.device(dev):
+        st = lib().path_decode_step_noalloc(_ptr(kcache), _ptr(vcache), int(n), ncap, _ptr(q), _ptr(w), _ptr(beta),
+                                            _ptr(logf), _ptr(fcache), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse),
+                                            B, H, d, _DTYPES[dt], float(scale or 0.0), _stream(stream))
+    if st != PATH_OK:
+        raise PathError(st, "path_decode_step_noalloc")
+    return (out, lse) if lse is not None else out
 
 
 def decode_cache_from_fwd(workspace, v, kcache, vcache, stream=None, logf=None, fcache=None):

@@ -72,6 +72,7 @@ const char *path_status_string(path_status_t s) {
         case PATH_EINVAL: return "invalid argument";
         case PATH_EUNSUPPORTED: return "unsupported configuration";
         case PATH_EHIP: return "HIP launch error";
+        case PATH_ESCRATCH: return "problem larger than the fixed scratch of the no-allocation entry point";
     }
     return "unknown status";
 }
@@ -215,10 +216,17 @@ size_t path_decode_workspace_size(int B, int H, int64_t n, int d, path_dtype_t d
     return dec_ws_bytes(B, H, n, d);
 }
 
-path_status_t path_decode_step_ex(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,
-                                  const float *beta, const float *logf, float *fcache, const void *k_new,
-                                  const void *v_new, void *out, float *lse, int B, int H, int d, path_dtype_t dtype,
-                                  float scale, void *workspace, size_t workspace_bytes, path_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the decode entry points (nothing is enqueued).  With
+// own_scratch the kernels use the library's fixed scratch array instead of a
+// caller workspace: `workspace` is then NULL and the scratch must hold `need`.
+path_status_t dec_check(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,
+                        const float *beta, const float *logf, float *fcache, const void *k_new, const void *v_new,
+                        void *out, float *lse, int B, int H, int d, path_dtype_t dtype, float scale,
+                        const void *workspace, size_t workspace_bytes, bool own_scratch, int64_t *natt_out) {
     if (n < 0 || ncap < 1 || n > ncap) return PATH_EINVAL;
     if ((k_new == nullptr) != (v_new == nullptr)) return PATH_EINVAL;
     if ((logf == nullptr) != (fcache == nullptr)) return PATH_EINVAL;
@@ -227,23 +235,30 @@ path_status_t path_decode_step_ex(void *kcache, void *vcache, int64_t n, int64_t
     path_status_t st = dec_sizes_ok(B, H, natt, d, dtype);
     if (st != PATH_OK) return st;
     if (mul_chk({B, H, ncap, d, 8}) < 0) return PATH_EINVAL;
-    if (!kcache || !vcache || !q || !w || !beta || !out || !workspace) return PATH_EINVAL;
+    if (!kcache || !vcache || !q || !w || !beta || !out) return PATH_EINVAL;
+    if (!own_scratch && !workspace) return PATH_EINVAL;
     for (const void *p : {(const void *)kcache, (const void *)vcache, q, w, k_new, v_new, (const void *)out,
-                          (const void *)workspace})
+                          workspace})
         if (p && !aligned(p, 16)) return PATH_EINVAL;
     if (!aligned(beta, 4) || (lse && !aligned(lse, 4))) return PATH_EINVAL;
     if (logf && (!aligned(logf, 4) || !aligned(fcache, 4))) return PATH_EINVAL;
     const size_t need = dec_ws_bytes(B, H, natt, d);
-    if (workspace_bytes < need) return PATH_EINVAL;
+    if (!own_scratch && workspace_bytes < need) return PATH_EINVAL;
     if (!(std::isfinite(scale))) return PATH_EINVAL;
+    {
+        int nsplit;
+        int64_t chunk;
+        path::decode_plan((int64_t)B * H, natt, &nsplit, &chunk);
+        if ((int64_t)nsplit * B * H > kMaxGrid) return PATH_EINVAL;
+    }
     const int64_t es = elem_size(dtype);
     const int64_t cache = (int64_t)B * H * ncap * d * es, vec = (int64_t)B * H * d * es, sc = (int64_t)B * H * 4;
     if (overlap(kcache, cache, vcache, cache)) return PATH_EINVAL;
-    for (const void *p : {q, w, k_new, v_new, (const void *)out, (const void *)workspace}) {
+    for (const void *p : {q, w, k_new, v_new, (const void *)out, workspace}) {
         const int64_t sz = p == workspace ? (int64_t)need : vec;
         if (overlap(kcache, cache, p, sz) || overlap(vcache, cache, p, sz)) return PATH_EINVAL;
     }
-    for (const void *p : {q, w, k_new, v_new, (const void *)workspace})
+    for (const void *p : {q, w, k_new, v_new, workspace})
         if (overlap(out, vec, p, p == workspace ? (int64_t)need : vec)) return PATH_EINVAL;
     if (lse && (overlap(lse, sc, beta, sc) || overlap(lse, sc, out, vec) || overlap(lse, sc, workspace, (int64_t)need) ||
                 overlap(lse, sc, kcache, cache) || overlap(lse, sc, vcache, cache)))
@@ -252,22 +267,60 @@ path_status_t path_decode_step_ex(void *kcache, void *vcache, int64_t n, int64_t
         const int64_t fcs = (int64_t)B * H * ncap * 4;
         for (const void *p : {(const void *)kcache, (const void *)vcache})
             if (overlap(fcache, fcs, p, cache)) return PATH_EINVAL;
-        for (const void *p : {q, w, k_new, v_new, (const void *)out, (const void *)workspace})
+        for (const void *p : {q, w, k_new, v_new, (const void *)out, workspace})
             if (overlap(fcache, fcs, p, p == workspace ? (int64_t)need : vec)) return PATH_EINVAL;
         for (const void *p : {(const void *)beta, (const void *)logf, (const void *)lse})
             if (overlap(fcache, fcs, p, sc)) return PATH_EINVAL;
     }
-    if (scale <= 0.f) scale = 1.0f / std::sqrt((float)d);
+    if (own_scratch && need > path::decode_scratch_bytes()) return PATH_ESCRATCH;
+    *natt_out = natt;
+    return PATH_OK;
+}
 
+path_status_t dec_launch(void *kcache, void *vcache, int64_t n, int64_t ncap, int64_t natt, const void *q,
+                         const void *w, const float *beta, const float *logf, float *fcache, const void *k_new,
+                         const void *v_new, void *out, float *lse, int B, int H, int d, path_dtype_t dtype, float scale,
+                         void *workspace, path_stream_t stream) {
     path::DecodeArgs da{};
     da.kc = kcache; da.vc = vcache; da.n = n; da.ncap = ncap;
     da.q = q; da.w = w; da.beta = beta; da.logf = logf; da.fcache = fcache; da.knew = k_new; da.vnew = v_new;
     da.out = out; da.lse = lse; da.ws = workspace;
-    da.B = B; da.H = H; da.d = d; da.scale = scale;
+    da.B = B; da.H = H; da.d = d; da.scale = eff_scale(scale, d);
     path::decode_plan((int64_t)B * H, natt, &da.nsplit, &da.chunk);
-    if ((int64_t)da.nsplit * B * H > kMaxGrid) return PATH_EINVAL;
     if (path::launch_decode(da, dtype == PATH_DTYPE_BF16, (hipStream_t)stream) != hipSuccess) return PATH_EHIP;
     return PATH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+path_status_t path_decode_step_ex(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,
+                                  const float *beta, const float *logf, float *fcache, const void *k_new,
+                                  const void *v_new, void *out, float *lse, int B, int H, int d, path_dtype_t dtype,
+                                  float scale, void *workspace, size_t workspace_bytes, path_stream_t stream) {
+    int64_t natt = 0;
+    path_status_t st = dec_check(kcache, vcache, n, ncap, q, w, beta, logf, fcache, k_new, v_new, out, lse, B, H, d,
+                                 dtype, scale, workspace, workspace_bytes, false, &natt);
+    if (st != PATH_OK) return st;
+    return dec_launch(kcache, vcache, n, ncap, natt, q, w, beta, logf, fcache, k_new, v_new, out, lse, B, H, d, dtype,
+                      scale, workspace, stream);
+}
+
+size_t path_decode_noalloc_max_bytes(void) { return path::decode_scratch_bytes(); }
+
+path_status_t path_decode_step_noalloc(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q,
+                                       const void *w, const float *beta, const float *logf, float *fcache,
+                                       const void *k_new, const void *v_new, void *out, float *lse, int B, int H,
+                                       int d, path_dtype_t dtype, float scale, path_stream_t stream) {
+    int64_t natt = 0;
+    path_status_t st = dec_check(kcache, vcache, n, ncap, q, w, beta, logf, fcache, k_new, v_new, out, lse, B, H, d,
+                                 dtype, scale, nullptr, 0, true, &natt);
+    if (st != PATH_OK) return st;
+    void *scratch = nullptr;  // this device's copy of the library's scratch array
+    if (path::decode_scratch(&scratch) != hipSuccess) return PATH_EHIP;
+    return dec_launch(kcache, vcache, n, ncap, natt, q, w, beta, logf, fcache, k_new, v_new, out, lse, B, H, d, dtype,
+                      scale, scratch, stream);
 }
 
 path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q, const void *w,

@@ -20,10 +20,44 @@
 // so its loads and stores carry the non-temporal hint (5% faster here).  Splits of the cache write partial
 // (max, sum, accumulator) records that a second small kernel merges in a fixed
 // order, so results are bitwise reproducible.
+#include <mutex>
+
 #include "path_common.h"
 #include "path_kernels.h"
 
 namespace path {
+
+// Scratch of the no-allocation decode entry point: the split partials (max, sum,
+// d accumulators per head and split) live in this fixed array instead of a
+// caller workspace.  Each device holds its own copy from module load to the end
+// of the process.  Host code must not use the name itself (on the host it is
+// only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, looked up once per device in decode_scratch().
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with device `dev` current: its copy
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
 namespace {
 
 constexpr int kDecThreads = 256;

@@ -66,4 +66,10 @@ hipError_t launch_cache(const CacheArgs &a, bool bf16, hipStream_t st);
 // Decode split plan: rows per split and number of splits for n attending rows.
 void decode_plan(int64_t BH, int64_t rows, int *nsplit, int64_t *chunk);
 
+// The decode kernels' fixed scratch array (for callers that cannot allocate):
+// its size in bytes, and its address on the current device (looked up once per
+// device, then cached).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void **ptr);
+
 }  // namespace path

@@ -61,7 +61,8 @@ typedef enum {
     PATH_OK = 0,
     PATH_EINVAL = 1,        /* NULL pointer, bad size, misaligned, workspace too small, n > ncap */
     PATH_EUNSUPPORTED = 2,  /* valid but not implemented (head dimension other than 64, 128; 128 in the backward) */
-    PATH_EHIP = 3           /* the HIP runtime rejected a launch */
+    PATH_EHIP = 3,          /* the HIP runtime rejected a launch */
+    PATH_ESCRATCH = 4       /* path_decode_step_noalloc: the problem needs more than its fixed scratch */
 } path_status_t;
 
 typedef enum {
@@ -231,6 +232,28 @@ path_status_t path_decode_step_ex(void *kcache, void *vcache, int64_t n, int64_t
                                   const float *beta, const float *logf, float *fcache, const void *k_new,
                                   const void *v_new, void *out, float *lse, int B, int H, int d, path_dtype_t dtype,
                                   float scale, void *workspace, size_t workspace_bytes, path_stream_t stream);
+
+/*
+ * path_decode_step_ex for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace: the split partials go to a fixed scratch
+ * array of path_decode_noalloc_max_bytes() bytes (16 MiB) that the library
+ * holds on every device it runs on until the process ends, and the call itself
+ * allocates nothing.  Every call on one device shares that device's array, so
+ * calls that overlap in time on one device (other streams, other host threads)
+ * race; calls ordered on one stream are safe.  Nothing in the array needs to
+ * start at zero (every split writes its whole record before the merge reads
+ * it).  The scratch a call needs is path_decode_workspace_size(B, H, n (+1),
+ * d, dtype); larger problems return PATH_ESCRATCH (before anything is
+ * enqueued: B * H above 63 550 at d = 64 or 32 263 at d = 128).  The first call on
+ * a device looks the array's address up on that device (the current device).
+ * Arguments, results and the other errors are those of path_decode_step_ex.
+ */
+size_t path_decode_noalloc_max_bytes(void);
+path_status_t path_decode_step_noalloc(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q,
+                                       const void *w, const float *beta, const float *logf, float *fcache,
+                                       const void *k_new, const void *v_new, void *out, float *lse, int B, int H,
+                                       int d, path_dtype_t dtype, float scale, path_stream_t stream);
 
 /*
  * Decode cache of a prefix from its forward pass ([TS] s.3: prefill, then

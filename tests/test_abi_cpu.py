@@ -51,8 +51,8 @@ def test_entry_points_keep_their_parameter_lists():
 def test_version_and_status_strings():
     lib = pa.lib()
     assert lib.path_abi_version() == 1
-    for s in range(4):
-        assert lib.path_status_string(s)
+    for s in range(5):
+        assert lib.path_status_string(s) and lib.path_status_string(s) != b"unknown status"
     assert lib.path_status_string(99) == b"unknown status"
 
 
@@ -149,6 +149,47 @@ def test_decode_rejects_bad_arguments(over, status):
     assert dec_call(**over) == status
     if "lf" not in over and "fc" not in over:
         assert dec_call(ex=False, **over) == status  # the plain entry point validates the same way
+
+
+def noalloc_call(**over):
+    G = 1 << 40  # fake device addresses far apart, so large sizes do not overlap
+    args = dict(kc=ctypes.c_void_p(G), vc=ctypes.c_void_p(2 * G), n=100, ncap=100, q=ctypes.c_void_p(3 * G),
+                w=ctypes.c_void_p(4 * G), beta=ctypes.c_void_p(5 * G), lf=None, fc=None, kn=None, vn=None,
+                out=ctypes.c_void_p(6 * G), lse=None, B=1, H=1, d=64, dtype=BF, scale=0.0, stream=None)
+    args.update(over)
+    a = args
+    return pa.lib().path_decode_step_noalloc(a["kc"], a["vc"], a["n"], a["ncap"], a["q"], a["w"], a["beta"], a["lf"],
+                                             a["fc"], a["kn"], a["vn"], a["out"], a["lse"], a["B"], a["H"], a["d"],
+                                             a["dtype"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(n=101), pa.PATH_EINVAL),                             # n > ncap
+    (dict(n=0), pa.PATH_EINVAL),                               # nothing to attend to
+    (dict(kc=None), pa.PATH_EINVAL),
+    (dict(out=None), pa.PATH_EINVAL),
+    (dict(d=96), pa.PATH_EUNSUPPORTED),
+    (dict(vc=ctypes.c_void_p(1 << 40)), pa.PATH_EINVAL),       # caches alias
+    (dict(lf=ctypes.c_void_p(7 << 40)), pa.PATH_EINVAL),       # gate without its cache
+    (dict(B=1000, H=100, d=128), pa.PATH_ESCRATCH),            # 100 000 heads: partials beyond the scratch
+    (dict(B=640, H=100, d=64), pa.PATH_ESCRATCH),              # 64 000 heads at d = 64
+])
+def test_decode_noalloc_rejects_before_launch(over, status):
+    """The no-allocation decode entry validates like path_decode_step_ex, and a problem whose split
+    partials exceed its fixed scratch is refused with PATH_ESCRATCH before any device call."""
+    assert noalloc_call(**over) == status
+
+
+def test_decode_noalloc_scratch_size():
+    lib = pa.lib()
+    cap = lib.path_decode_noalloc_max_bytes()
+    assert cap == 16 << 20
+    # the decode workload (B16 H32, 32768 rows, d 64) and the largest head counts named in the header fit
+    assert lib.path_decode_workspace_size(16, 32, 32768, 64, BF) <= cap
+    assert lib.path_decode_workspace_size(1, 63550, 32768, 64, BF) <= cap
+    assert lib.path_decode_workspace_size(1, 63551, 32768, 64, BF) > cap
+    assert lib.path_decode_workspace_size(1, 32263, 32768, 128, BF) <= cap
+    assert lib.path_decode_workspace_size(1, 32264, 32768, 128, BF) > cap
 
 
 def cache_call(**over):
