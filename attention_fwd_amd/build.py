@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpath_attn.so")
-SOURCES = ["path_abi.cpp", "path_prep.hip", "path_fwd.hip", "path_decode.hip", "path_cache.hip", "path_bwd.hip"]
+SOURCES = ["path_abi.cpp", "path_plan.cpp", "path_prep.hip", "path_fwd.hip", "path_decode.hip", "path_cache.hip", "path_bwd.hip"]
 
 COMPILE_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

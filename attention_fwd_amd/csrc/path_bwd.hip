@@ -939,32 +939,6 @@ __global__ __launch_bounds__(kT) void bwd_gate_kernel(BwdArgs a) {
 
 }  // namespace
 
-BwdLayout bwd_layout(int L, int es) {
-    BwdLayout ly{};
-    const int64_t nb = (L + kC - 1) / kC, Lp = nb * kC, np = nb * (nb - 1) / 2;
-    int64_t off = 0;
-    auto take = [&](int64_t bytes) {
-        const int64_t o = off;
-        off += (bytes + 255) / 256 * 256;
-        return o;
-    };
-    const int64_t tile = Lp * kD * 4, rows = Lp * 4;
-    ly.qh = take(tile); ly.kh = take(tile); ly.vf = take(Lp * kD * es); ly.dof = take(Lp * kD * es);
-    ly.tt = take(nb * kD * kD * 4);
-    ly.ttt = take(nb * kD * kD * 4);
-    ly.xx = take(nb * kC * kC * 4); ly.aa = take(nb * kC * kC * 4); ly.qwm = take(nb * kC * kC * 4);
-    ly.nn = take(nb * kC * kC * 4); ly.zz = take(nb * kC * kC * 4);
-    ly.ee = take(nb * kC * kC * 4); ly.dvd = take(tile); ly.dqo = take(tile); ly.dko = take(tile); ly.dvo = take(tile);
-    ly.dt = take(nb * kD * kD * 4);
-    ly.l2 = take(rows); ly.dd = take(rows); ly.clq = take(rows); ly.ckk = take(rows); ly.rsd = take(rows);
-    ly.csd = take(rows); ly.rso = take(rows); ly.cso = take(rows); ly.dc = take(rows);
-    ly.tot = take(nb * 4); ly.mid = take(np * 4);
-    ly.qs = take(np * kC * kD * es); ly.gs = take(np * kC * kD * es);
-    ly.ps = take(np * kC * kC * es); ly.ds = take(np * kC * kC * es); ly.csp = take(np * kC * 4);
-    ly.head = off;
-    return ly;
-}
-
 hipError_t launch_bwd(const BwdArgs &a0, bool bf16, hipStream_t st) {
     BwdArgs a = a0;
     const int G = a.B * a.H;

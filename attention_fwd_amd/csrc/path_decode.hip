@@ -289,20 +289,12 @@ __global__ __launch_bounds__(D) void path_decode_combine_kernel(DecodeArgs a) {
 
 }  // namespace
 
-void decode_plan(int64_t BH, int64_t rows, int *nsplit, int64_t *chunk) {
-    const int64_t target_wg = 8192;
-    const int64_t step = (int64_t)(kDecThreads / 8) * rows_per_iter<uint16_t, 64>();  // the largest rows per workgroup iteration (a multiple of the others)
-    int64_t per_head = (target_wg + BH - 1) / BH;
-    const int64_t max_split = (rows + step - 1) / step;
-    if (per_head > max_split) per_head = max_split;
-    if (per_head < 1) per_head = 1;
-    int64_t c = (rows + per_head - 1) / per_head;
-    c = (c + step - 1) / step * step;
-    if (c < step) c = step;
-    *chunk = c;
-    *nsplit = (int)((rows + c - 1) / c);
-    if (*nsplit < 1) *nsplit = 1;
-}
+// the split plan (decode_plan, host code) sizes splits in multiples of the rows one
+// workgroup iteration covers; it assumes this value
+static_assert(kDecodeRowStep == (kDecThreads / 8) * rows_per_iter<uint16_t, 64>(), "decode row step");
+static_assert(kDecodeRowStep % ((kDecThreads / 8) * rows_per_iter<uint16_t, 128>()) == 0, "decode row step");
+static_assert(kDecodeRowStep % ((kDecThreads / 8) * rows_per_iter<float, 64>()) == 0, "decode row step");
+static_assert(kDecodeRowStep % ((kDecThreads / 8) * rows_per_iter<float, 128>()) == 0, "decode row step");
 
 template <typename S, int D>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {

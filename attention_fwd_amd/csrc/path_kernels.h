@@ -63,6 +63,10 @@ hipError_t launch_fwd(const FwdArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_cache(const CacheArgs &a, bool bf16, hipStream_t st);
 
+// Rows one decode workgroup covers per iteration (bf16, d = 64: 32 lane groups x
+// 8 rows; the other element types and head sizes cover a divisor of it).
+constexpr int kDecodeRowStep = 256;
+
 // Decode split plan: rows per split and number of splits for n attending rows.
 void decode_plan(int64_t BH, int64_t rows, int *nsplit, int64_t *chunk);
 
