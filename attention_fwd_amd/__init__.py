@@ -436,7 +436,7 @@ def bwd(q, k, v, w, beta, logf, out, lse, dout, dlse=None, scale=None, workspace
     if workspace is None:
         need = bwd_workspace_size(B, H, L, d, dt)
         if need == 0:
-            raise PathError(PATH_EUNSUPPORTED if d != 64 else PATH_EINVAL, "path_attn_bwd_workspace_size")
+            raise PathError(PATH_EUNSUPPORTED if d not in (64, 128) else PATH_EINVAL, "path_attn_bwd_workspace_size")
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
         mine.append(workspace)
     _check(workspace, "workspace", None, None, dev)

@@ -369,9 +369,9 @@ constexpr int64_t kBwdCap = int64_t(8) << 30;  // default workspace: all heads, 
 
 path_status_t bwd_sizes_ok(int B, int H, int L, int d, path_dtype_t dtype) {
     if (B < 1 || H < 1 || L < 1 || d < 1 || elem_size(dtype) == 0) return PATH_EINVAL;
-    if (d != 64) return PATH_EUNSUPPORTED;  // the backward kernels are written for d = 64
+    if (d != 64 && d != 128) return PATH_EUNSUPPORTED;
     const int64_t nb = ((int64_t)L + 63) / 64;
-    if (mul_chk({B, H, nb * 64, d, 8}) < 0 || mul_chk({nb, nb, 64 * 64 * 8}) < 0) return PATH_EINVAL;
+    if (mul_chk({B, H, nb * 64, d, 8}) < 0 || mul_chk({nb, nb, 64, d, 8}) < 0) return PATH_EINVAL;
     if (nb > 65535 || mul_chk({B, H, nb}) > kMaxGrid) return PATH_EINVAL;
     return PATH_OK;
 }
@@ -380,7 +380,7 @@ path_status_t bwd_sizes_ok(int B, int H, int L, int d, path_dtype_t dtype) {
 
 size_t path_attn_bwd_workspace_size(int B, int H, int L, int d, path_dtype_t dtype) {
     if (bwd_sizes_ok(B, H, L, d, dtype) != PATH_OK) return 0;
-    const int64_t share = path::bwd_layout(L, (int)elem_size(dtype)).head, G = (int64_t)B * H;
+    const int64_t share = path::bwd_layout(L, d, (int)elem_size(dtype)).head, G = (int64_t)B * H;
     int64_t hc = kBwdCap / share;
     if (hc < 1) hc = 1;
     if (hc > G) hc = G;
@@ -411,7 +411,7 @@ path_status_t path_attn_bwd(const void *q, const void *k, const void *v, const v
     for (const void *p : tok_out)
         if (p && !aligned(p, 4)) return PATH_EINVAL;
     if (!std::isfinite(scale)) return PATH_EINVAL;
-    const int64_t share = path::bwd_layout(L, (int)elem_size(dtype)).head, G = (int64_t)B * H;
+    const int64_t share = path::bwd_layout(L, d, (int)elem_size(dtype)).head, G = (int64_t)B * H;
     if ((int64_t)workspace_bytes < share) return PATH_EINVAL;
     int64_t hc = (int64_t)workspace_bytes / share;
     if (hc > G) hc = G;
@@ -451,7 +451,7 @@ path_status_t path_attn_bwd(const void *q, const void *k, const void *v, const v
     ba.B = B; ba.H = H; ba.L = L; ba.d = d; ba.scale = eff_scale(scale, d);
     ba.nb = (L + 63) / 64;
     ba.hc_max = (int)hc;
-    ba.ly = path::bwd_layout(L, (int)elem_size(dtype));
+    ba.ly = path::bwd_layout(L, d, (int)elem_size(dtype));
     return path::launch_bwd(ba, dtype == PATH_DTYPE_BF16, (hipStream_t)stream) == hipSuccess ? PATH_OK : PATH_EHIP;
 }
 

@@ -6,27 +6,35 @@
 
 namespace path {
 
-// Byte offsets inside one head's share of the backward workspace (fp32 arrays;
-// Lp = 64 * ceil(L / 64) padded rows, nb blocks, np = nb (nb - 1) / 2 pairs of
-// a query block I and an earlier key block J, pair index I (I - 1) / 2 + J).
+// Byte offsets inside one head's share of the backward workspace.  Lp = 64 nb
+// padded rows, nb blocks, np = nb (nb - 1) / 2 pairs of a query block I and an
+// earlier key block J (pair index I (I - 1) / 2 + J).  "Fragments" are stored
+// in matrix-core fragment order in the element type S of the inputs (bf16 or
+// fp32): a matrix X of R rows and K contraction columns is kept as (R / 32) x
+// (K / 16) fragments of 64 lanes x 8 elements (see path_common.h), so a walk
+// reads each operand with one 16- or 32-byte load per lane.
 struct BwdLayout {
-    int64_t qh, kh, vf, dof;  // [Lp, 64]: block-adjusted q and k (fp32), copies of v and do (input type)
-    int64_t tt, ttt, ee;      // [nb, 64, 64]: block transitions and their transposes, scale * dS of the diagonal blocks
-    int64_t dvd, dqo, dko, dvo;  // [Lp, 64]: diagonal value gradient; walk outputs dq^, dk^, dv
-    int64_t dt;               // [nb, 64, 64]: gradient of each block transition
-    int64_t xx, aa, qwm, nn, zz;  // [nb, 64, 64]: X, A, Q W^T o [r <= i], N, Z of each block (prep -> block backward)
-    int64_t l2, dd, clq, ckk;  // [Lp]: lse in log2 units, do.o - dlse, gate prefix terms of rows / keys
-    int64_t rsd, csd, rso, cso, dc;  // [Lp]: row / column sums of dS (diagonal, off-diagonal), gate adjoint
-    int64_t tot;              // [nb]: gate total of each block
-    int64_t mid;              // [np]: gate sum over the blocks strictly between I and J
-    int64_t qs, gs;           // [np, 64, 64]: carried queries q~_I^(J) and adjoints G_I^(J-1)
-    int64_t ps, ds;           // [np, 64, 64]: softmax weights P and dS of every pair
-    int64_t csp;              // [np, 64]: column sums of each pair's dS (fp32)
-    // qs, gs, ps, ds hold the input element type (bf16 for bf16 inputs, else fp32)
-    int64_t head;             // bytes per head
+    int D, es;
+    // per block, fp32 64 x 64: X, A, Q W^T o [r <= i], N = K W^T o [r > j], Z, and scale * dS of the diagonal block
+    int64_t xx, aa, qwm, nn, zz, ee;
+    // per block, fragments (S): k^ (rows keys, k over d), k^^T (rows d, k over keys), V (rows keys),
+    // dO (rows queries), dO^T (rows d), and T - I, (T - I)^T of the block transition T (rows d, k over d)
+    int64_t kh1, kh2, v1, do1, do2, nt, ntt;
+    // fp32 [Lp, D]: q^; the diagonal value gradient; walk outputs dq^, dk^, dv; W dT and W dT^T of the
+    // block backward
+    int64_t qh, dvd, dqo, dko, dvo, uu, vv;
+    int64_t dtt;  // per block, fp32 [D, D]: dT^T (the transpose of the transition gradient)
+    // fp32 [Lp]: lse (log2 units), do.o - dlse, gate prefix terms of rows / keys, row / column sums of dS
+    // (diagonal, off-diagonal), gate adjoint
+    int64_t l2, dd, clq, ckk, rsd, csd, rso, cso, dc;
+    int64_t tot;  // [nb]: gate total of each block
+    int64_t mid;  // [np]: gate sum over the blocks strictly between I and J
+    // per pair, fragments (S): q~ (rows queries, k over d), q~^T (rows d, k over queries), G^(J-1)^T (rows d)
+    int64_t qs1, qs2, gs2;
+    int64_t head;  // bytes per head
 };
 
-BwdLayout bwd_layout(int L, int elem_bytes);
+BwdLayout bwd_layout(int L, int D, int elem_bytes);
 
 struct BwdArgs {
     const void *q, *k, *v, *w;

@@ -1,5 +1,5 @@
 // path_bwd.hip -- backward pass of PaTH attention (gradients of q, k, v, w,
-// beta and the log forget gate), gfx950.
+// beta and the log forget gate), gfx950, head dimension 64 or 128.
 //
 // The pages present the blockwise algorithm (UT transform per block, scan over
 // key blocks) as what makes PaTH trainable ("技術要約: PaTH Attention", section 3,
@@ -16,34 +16,37 @@
 //   X = (I + B su(W W^T))^-1 (unit upper triangular), A = X B
 //   q^_i = H_s ... H_i q_i      = q_i - (Z W)_i,  Z = (Q W^T o [r <= i]) A^T
 //   k^_j = H_e ... H_{j+1} k_j  = k_j - (Y W)_j,  Y = N A,  N = K W^T o [r > j]
-//   T_J  = H_s ... H_e          = I - W^T A W                (d x d, dense)
+//   T_J  = H_s ... H_e          = I - W^T A W                (d x d)
 //   diagonal logits  s_ij = scale (Q K^T - Z N^T)_ij + gate,  j <= i
 // For query block I and key block J < I the logits are scale q~ . k^ with the
 // query carried down q~^(J-1) = T_J q~^(J), q~^(I-1) = q^.  The adjoint of
 // q~^(J) obeys G^(J) = G^(J-1) T_J + scale dS_IJ K^_J (rows), running upward
-// while q~ runs downward, so:
-//   prep (per block): the quantities above (X, A, Q W^T o mask, N and Z kept
-//     for the block backward), the diagonal block's dS, its value gradient,
-//     and copies of v and do;
-//   query-major walk (per query block I): a down walk J = I-1 .. 0 storing
-//     q~^(J) for every pair (its own kernel: one product per step, so several
-//     workgroups per compute unit), then the up walk J = 0 .. I-1 storing
-//     G^(J-1), P and dS for every pair and ending with dq^_I = G^(I-1);
-//   key-major walk (per key block J): over I > J, dV_J += P^T dO_I,
-//     dk^_J += scale dS^T q~, dT_J += G^(J-1)^T q~ -- sums owned by one
-//     workgroup, so no atomics; P and dS come from the query-major walk;
+// while q~ runs downward, so the carried queries and adjoints of every pair
+// go through the workspace:
+//   prep (per block): the quantities above, kept as fp32 64 x 64 matrices for
+//     the block backward and as matrix-core fragments for the walks; the
+//     diagonal block's dS and value gradient;
+//   down walk (per query block I): q~^(J) for J = I-1 .. 0, stored per pair in
+//     two orientations (rows queries / rows d: the sums over queries below
+//     need the query index inside a lane's fragment);
+//   up walk (per query block I): J = 0 .. I-1, the logits, P and dS from the
+//     stored q~, the adjoint G, stored per pair (rows d), and dq^_I = G^(I-1);
+//   key walk (per key block J): over I > J the logits, P and dS again (from
+//     q~, dO, k^, V: recomputing them costs less than moving them), and the
+//     sums dV_J += P^T dO_I, dk^_J += scale dS^T q~, dT_J += G^(J-1)^T q~ --
+//     owned by one workgroup, so no atomics (bitwise reproducible);
 //   block backward (per block): the matrix-form chain rule through the
 //     formulas above (including the triangular inverse: dT' = -X^T dX X^T)
 //     gives dq, dk, dw, dbeta; dv adds the two value sums; the gate's
 //     per-token adjoint dc_t = rowsum_t(dS) - colsum_t(dS);
 //   gate: dlogf_t = sum_{t' >= t} dc_t' (one workgroup per head).
-// Every contraction is a 64x64x64 fp32 product on the matrix cores
-// (v_mfma_f32_16x16x4f32, eight waves sharing each product) with operands in
-// LDS; the arithmetic is fp32 for either input type.  The walks exchange q~,
-// G, P and dS of every pair through the workspace in the input type: fp32,
-// or bf16 for bf16 inputs (the forward's own scan feeds q~ to its logit
-// products in bf16 too); the column sums of dS the gate needs stay fp32.
-// Head dimension 64.
+// The walks run on the matrix cores in the input's element type (bf16
+// products with fp32 accumulation for bf16 inputs, fp32 products for fp32),
+// with operands stored in fragment order and the carried q~ and G held as
+// fp32 accumulators, rounded to the element type only as product operands,
+// as in the forward scan.  The per-block kernels use fp32 64 x 64 tiles in
+// LDS (v_mfma_f32_16x16x4f32), looping over 64-wide chunks of the head
+// dimension.
 #include <hip/hip_runtime.h>
 
 #include "path_bwd.h"
@@ -53,10 +56,13 @@ namespace path {
 namespace {
 
 constexpr int kC = 64;   // tokens per block
-constexpr int kD = 64;   // head dimension
 constexpr int kP = 68;   // LDS row stride of a 64x64 fp32 tile: rows 16-byte aligned, columns conflict-free
-constexpr int kT = 512;  // threads per workgroup (8 waves, two per SIMD)
+constexpr int kT = 512;  // threads per workgroup of the per-block kernels (8 waves, two per SIMD)
 constexpr int kTile = kC * kP;
+
+// ---------------------------------------------------------------------------
+// 64x64 fp32 tiles in LDS (per-block kernels)
+// ---------------------------------------------------------------------------
 
 // A 64x64 fp32 matrix in LDS; element (r, c) at p[r * rs + c * cs].
 struct LMat {
@@ -69,12 +75,10 @@ __device__ __forceinline__ LMat tr(const float *p) { return {p, 1, kP}; }
 // acc += A * B for 64x64 operands on v_mfma_f32_16x16x4f32.  Wave w owns rows
 // 16 (w >> 1) .. +16 and columns 32 (w & 1) .. +32 of the output as two 16x16
 // tiles (accumulator elements 0-3 and 4-7), so all eight waves share every
-// product and each SIMD holds two waves.  The contraction runs in four
-// blocks of sixteen k; in block g, MFMA t (0..3) takes k = 16g + 4q + t from
-// lane group q = lane / 16, the same order for both operands.  An operand
-// whose k index is contiguous in LDS (A stored by rows, B stored by columns)
-// is read with one 16-byte load per four MFMAs; otherwise with four single
-// loads, whose sixteen lanes walk a row and so hit distinct banks.
+// product.  The contraction runs in four blocks of sixteen k; in block g, MFMA
+// t (0..3) takes k = 16g + 4q + t from lane group q = lane / 16, the same
+// order for both operands.  An operand whose k index is contiguous in LDS is
+// read with one 16-byte load per four MFMAs; otherwise with four single loads.
 __device__ __forceinline__ void mm(f32x8 &acc, LMat A, LMat B, int lane, int wave) {
     const int r = 16 * (wave >> 1) + (lane & 15), c0 = 32 * (wave & 1) + (lane & 15), q = lane >> 4;
     f32x4 lo = acc.lo, hi = acc.hi;
@@ -128,92 +132,35 @@ __device__ __forceinline__ void store_lds(float *buf, const f32x8 &acc, int lane
         buf[r * kP + c] = f(r, c, acc[v]);
     }
 }
+struct Id {
+    __device__ float operator()(int, int, float x) const { return x; }
+};
 
-// Global fp32 tile [64][64] (row stride 64) <-> LDS.
-__device__ __forceinline__ void g2l(float *buf, const float *g, int tid) {
+// Global fp32 matrix [64 rows][row stride gs] <-> LDS tile.
+__device__ __forceinline__ void g2l(float *buf, const float *g, int gs, int tid) {
 #pragma unroll
-    for (int e = tid; e < kC * kD / 4; e += kT) {
+    for (int e = tid; e < kC * kC / 4; e += kT) {
         const int r = e >> 4, c = (e & 15) * 4;
-        *reinterpret_cast<f32x4 *>(buf + r * kP + c) = *reinterpret_cast<const f32x4 *>(g + r * kD + c);
+        *reinterpret_cast<f32x4 *>(buf + r * kP + c) = *reinterpret_cast<const f32x4 *>(g + (int64_t)r * gs + c);
     }
 }
-// One thread's share of a 64x64 fp32 tile, so the next step's tiles can be
-// fetched from global memory while the current step computes.
-struct Stage {
-    f32x4 v[kC * kD / 4 / kT];
-};
-__device__ __forceinline__ void gload(Stage &t, const float *g, int tid) {
+__device__ __forceinline__ void l2g(float *g, int gs, const float *buf, int tid) {
 #pragma unroll
-    for (int u = 0; u < kC * kD / 4 / kT; ++u) {
-        const int e = tid + u * kT, r = e >> 4, c = (e & 15) * 4;
-        t.v[u] = *reinterpret_cast<const f32x4 *>(g + r * kD + c);
+    for (int e = tid; e < kC * kC / 4; e += kT) {
+        const int r = e >> 4, c = (e & 15) * 4;
+        *reinterpret_cast<f32x4 *>(g + (int64_t)r * gs + c) = *reinterpret_cast<const f32x4 *>(buf + r * kP + c);
     }
 }
-__device__ __forceinline__ void lstore(float *buf, const Stage &t, int tid) {
-#pragma unroll
-    for (int u = 0; u < kC * kD / 4 / kT; ++u) {
-        const int e = tid + u * kT, r = e >> 4, c = (e & 15) * 4;
-        *reinterpret_cast<f32x4 *>(buf + r * kP + c) = t.v[u];
-    }
-}
-// The same for a 64x64 tile stored as bf16 (the walks' scratch for bf16 inputs):
-// 8 KiB, one 16-byte load of eight elements per thread.
-struct Stage16 {
-    u32x4 v;
-};
-__device__ __forceinline__ void gload(Stage16 &t, const uint16_t *g, int tid) {
-    t.v = *reinterpret_cast<const u32x4 *>(g + tid * 8);
-}
-__device__ __forceinline__ void lstore(float *buf, const Stage16 &t, int tid) {
-    const int r = tid >> 3, c = (tid & 7) * 8;
-    f32x4 lo, hi;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        lo[2 * u] = __uint_as_float(t.v[u] << 16);
-        lo[2 * u + 1] = __uint_as_float(t.v[u] & 0xffff0000u);
-        hi[2 * u] = __uint_as_float(t.v[2 + u] << 16);
-        hi[2 * u + 1] = __uint_as_float(t.v[2 + u] & 0xffff0000u);
-    }
-    *reinterpret_cast<f32x4 *>(buf + r * kP + c) = lo;
-    *reinterpret_cast<f32x4 *>(buf + r * kP + c + 4) = hi;
-}
-template <typename SC>
-struct StageOf {
-    typedef Stage T;
-};
-template <>
-struct StageOf<uint16_t> {
-    typedef Stage16 T;
-};
-
-// LDS fp32 tile -> global 64x64 tile of the scratch type, eight consecutive
-// elements per thread (one 16-byte store for bf16, two for fp32).
-__device__ __forceinline__ void l2g_sc(float *g, const float *buf, int tid) {
-    const int r = tid >> 3, c = (tid & 7) * 8;
-    *reinterpret_cast<f32x4 *>(g + r * kD + c) = *reinterpret_cast<const f32x4 *>(buf + r * kP + c);
-    *reinterpret_cast<f32x4 *>(g + r * kD + c + 4) = *reinterpret_cast<const f32x4 *>(buf + r * kP + c + 4);
-}
-__device__ __forceinline__ void l2g_sc(uint16_t *g, const float *buf, int tid) {
-    const int r = tid >> 3, c = (tid & 7) * 8;
-    const f32x4 lo = *reinterpret_cast<const f32x4 *>(buf + r * kP + c), hi = *reinterpret_cast<const f32x4 *>(buf + r * kP + c + 4);
-    u32x4 u;
-    u[0] = pack_bf16(lo[0], lo[1]);
-    u[1] = pack_bf16(lo[2], lo[3]);
-    u[2] = pack_bf16(hi[0], hi[1]);
-    u[3] = pack_bf16(hi[2], hi[3]);
-    *reinterpret_cast<u32x4 *>(g + r * kD + c) = u;
-}
-
 __device__ __forceinline__ void zero_lds(float *buf, int tid) {
     for (int e = tid; e < kTile; e += kT) buf[e] = 0.f;
 }
-__device__ __forceinline__ void acc2g(float *g, const f32x8 &acc, int lane, int wave) {
+__device__ __forceinline__ void acc2g(float *g, int gs, const f32x8 &acc, int lane, int wave) {
 #pragma unroll
-    for (int v = 0; v < 8; ++v) g[arow(v, lane, wave) * kD + acol(v, lane, wave)] = acc[v];
+    for (int v = 0; v < 8; ++v) g[(int64_t)arow(v, lane, wave) * gs + acol(v, lane, wave)] = acc[v];
 }
 
 // Eight consecutive elements of an input tensor as fp32 (one 16-byte load for
-// bf16, two for fp32); the tensors are 16-byte aligned and rows are 64 elements.
+// bf16, two for fp32); the tensors are 16-byte aligned, rows are D elements.
 __device__ __forceinline__ void load8(float *x, const uint16_t *g) {
     const u32x4 u = *reinterpret_cast<const u32x4 *>(g);
 #pragma unroll
@@ -231,14 +178,15 @@ __device__ __forceinline__ void load8(float *x, const float *g) {
     }
 }
 
-// Input tensor rows [row0, row0 + 64) of one head (rows >= L read as 0) -> LDS fp32;
-// each thread converts eight consecutive elements of one row.
+// Columns c0 .. c0+63 of input rows [row0, row0 + 64) of one head (rows of D
+// elements; rows >= L read as 0) -> LDS fp32; each thread converts eight
+// consecutive elements of one row.
 template <typename T>
-__device__ __forceinline__ void in2l(float *buf, const T *g, int row0, int L, int tid) {
+__device__ __forceinline__ void in2l(float *buf, const T *g, int D, int c0, int row0, int L, int tid) {
     const int r = tid >> 3, c = (tid & 7) * 8;  // 512 threads = 64 rows x 8 groups
     float x[8];
     if (row0 + r < L) {
-        load8(x, g + (int64_t)(row0 + r) * kD + c);
+        load8(x, g + (int64_t)(row0 + r) * D + c0 + c);
     } else {
 #pragma unroll
         for (int t = 0; t < 8; ++t) x[t] = 0.f;
@@ -249,6 +197,41 @@ __device__ __forceinline__ void in2l(float *buf, const T *g, int row0, int L, in
 }
 
 __device__ __forceinline__ int64_t pair_index(int I, int J) { return (int64_t)I * (I - 1) / 2 + J; }
+
+// Fragment (row tile rt, k chunk kc) of a fragment set with KC k chunks: 64
+// lanes x 8 elements; lane l holds row 32 rt + l % 32, k = 16 kc + frag_k(e, l / 32).
+template <typename S>
+__device__ __forceinline__ typename Elem<S>::Frag ldfrag(const S *base, int rt, int kc, int KC, int lane) {
+    return *reinterpret_cast<const typename Elem<S>::Frag *>(base + ((int64_t)(rt * KC + kc) * 64 + lane) * 8);
+}
+template <typename S>
+__device__ __forceinline__ void stfrag(S *base, int rt, int kc, int KC, int lane, const typename Elem<S>::Frag &f) {
+    *reinterpret_cast<typename Elem<S>::Frag *>(base + ((int64_t)(rt * KC + kc) * 64 + lane) * 8) = f;
+}
+
+// A 64x64 block of a matrix X (fp32 LDS tile) -> the 2 x 4 fragments of X it
+// covers, one (fragment, lane) per thread.  TRANS false: X rows are the tile's
+// rows and X's k the tile's columns; TRANS true: the transpose.  (rt0, kc0) is
+// the block's first fragment in X's fragment set of KC k chunks.
+template <typename S, bool TRANS>
+__device__ __forceinline__ void tile2frag(S *dst, int KC, int rt0, int kc0, const float *buf, int tid) {
+    const int f = tid >> 6, lane = tid & 63, rtl = f >> 2, kcl = f & 3, h = lane >> 5;
+    const int row = 32 * rtl + (lane & 31);
+    float x[8];
+    if constexpr (!TRANS) {
+        const float *p = buf + row * kP + 16 * kcl + 4 * h;
+        const f32x4 lo = *reinterpret_cast<const f32x4 *>(p), hi = *reinterpret_cast<const f32x4 *>(p + 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = lo[e];
+            x[4 + e] = hi[e];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = buf[(16 * kcl + frag_k(e, h)) * kP + row];
+    }
+    stfrag<S>(dst, rt0 + rtl, kc0 + kcl, KC, lane, Elem<S>::from_f32(x));
+}
 
 // X = (I + diag(beta) su(G))^-1 by back substitution: eight lanes per column
 // (64 columns x 8 = 512 threads), each summing every eighth term of a row's
@@ -267,15 +250,6 @@ __device__ __forceinline__ void unit_upper_inverse(float *X, const float *G, con
     }
 }
 
-// LDS tile -> global fp32 tile [64][64].
-__device__ __forceinline__ void l2g(float *g, const float *buf, int tid) {
-#pragma unroll
-    for (int e = tid; e < kC * kD / 4; e += kT) {
-        const int r = e >> 4, c = (e & 15) * 4;
-        *reinterpret_cast<f32x4 *>(g + r * kD + c) = *reinterpret_cast<const f32x4 *>(buf + r * kP + c);
-    }
-}
-
 // Block-local gate prefix sums (inclusive) of one block: cl[i] for its 64 rows.
 __device__ __forceinline__ void gate_prefix(float *cl, const float *logf, int row0, int L, int tid) {
     if (tid == 0) {
@@ -290,8 +264,10 @@ __device__ __forceinline__ void gate_prefix(float *cl, const float *logf, int ro
 // ---------------------------------------------------------------------------
 // Prep: one workgroup per (block J, head).
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
+    constexpr int NCH = D / 64, KCD = D / 16;
+    typedef T S;  // fragments are kept in the input's element type
     __shared__ __attribute__((aligned(16))) float sm[9 * kTile + 4 * kC];
     float *bW = sm, *bQ = bW + kTile, *bK = bQ + kTile, *bG = bK + kTile, *bA = bG + kTile, *bQW = bA + kTile,
           *bN = bQW + kTile, *bZ = bN + kTile, *bY = bZ + kTile;
@@ -299,143 +275,111 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int J = blockIdx.x, gl = blockIdx.y, g = a.g0 + gl, L = a.L, row0 = J * kC;
     const int64_t hoff = (int64_t)g * L;
-    const T *q = (const T *)a.q + hoff * kD, *k = (const T *)a.k + hoff * kD, *w = (const T *)a.w + hoff * kD;
-    const T *v = (const T *)a.v + hoff * kD, *o = (const T *)a.out + hoff * kD, *dout = (const T *)a.dout + hoff * kD;
+    const T *q = (const T *)a.q + hoff * D, *k = (const T *)a.k + hoff * D, *w = (const T *)a.w + hoff * D;
+    const T *v = (const T *)a.v + hoff * D, *o = (const T *)a.out + hoff * D, *dout = (const T *)a.dout + hoff * D;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
     const float scale = a.scale;
+    const int64_t tok = (int64_t)J * kC * kC;
 
-    in2l(bW, w, row0, L, tid);
-    in2l(bQ, q, row0, L, tid);
-    in2l(bK, k, row0, L, tid);
     if (tid < kC) {
         const int i = row0 + tid;
         sB[tid] = i < L ? a.beta[hoff + i] : 0.f;
         sL2[tid] = i < L ? a.lse[hoff + i] * kLog2e : 0.f;
     }
     gate_prefix(sCl, a.logf ? a.logf + hoff : nullptr, row0, L, tid);
-    {   // D_i = do_i . o_i - dlse_i: eight lanes per row, 8 columns each
-        const int r = tid >> 3, c0 = (tid & 7) * 8, i = row0 + r;
+    {   // D_i = do_i . o_i - dlse_i: eight lanes per row, D / 8 columns each
+        const int r = tid >> 3, c0 = (tid & 7) * (D / 8), i = row0 + r;
         float s = 0.f;
         if (i < L) {
-            float xo[8], xd[8];
-            load8(xd, dout + (int64_t)i * kD + c0);
-            load8(xo, o + (int64_t)i * kD + c0);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) s += xd[t] * xo[t];
+            for (int c = 0; c < D / 8; c += 8) {
+                float xo[8], xd[8];
+                load8(xd, dout + (int64_t)i * D + c0 + c);
+                load8(xo, o + (int64_t)i * D + c0 + c);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) s += xd[t] * xo[t];
+            }
         }
         s = sum8(s);
         if ((tid & 7) == 0) sDD[r] = i < L ? s - (a.dlse ? a.dlse[hoff + i] : 0.f) : 0.f;
     }
-    __syncthreads();
-    f32x8 acc = zero8();
-    mm(acc, nat(bW), tr(bW), lane, wave);  // G = W W^T
-    store_lds(bG, acc, lane, wave, [](int, int, float x) { return x; });
+    // G = W W^T, Q W^T, N = K W^T and Q K^T, summed over the chunks of the head dimension
+    f32x8 aG = zero8(), aQW = zero8(), aN = zero8(), aQK = zero8();
+    for (int c = 0; c < NCH; ++c) {
+        __syncthreads();
+        in2l(bW, w, D, 64 * c, row0, L, tid);
+        in2l(bQ, q, D, 64 * c, row0, L, tid);
+        in2l(bK, k, D, 64 * c, row0, L, tid);
+        __syncthreads();
+        mm(aG, nat(bW), tr(bW), lane, wave);
+        mm(aQW, nat(bQ), tr(bW), lane, wave);
+        mm(aN, nat(bK), tr(bW), lane, wave);
+        mm(aQK, nat(bQ), tr(bK), lane, wave);
+    }
+    store_lds(bG, aG, lane, wave, Id());
+    store_lds(bQW, aQW, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });  // Q W^T, r <= i
+    store_lds(bN, aN, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });     // N, r > j
     __syncthreads();
     unit_upper_inverse(bA, bG, sB, tid);
+    l2g((float *)(ws + ly.qwm) + tok, kC, bQW, tid);
+    l2g((float *)(ws + ly.nn) + tok, kC, bN, tid);
     __syncthreads();
-    float *XX = (float *)(ws + ly.xx) + (int64_t)J * kC * kC, *AA = (float *)(ws + ly.aa) + (int64_t)J * kC * kC;
+    {
+        float *XX = (float *)(ws + ly.xx) + tok, *AA = (float *)(ws + ly.aa) + tok;
 #pragma unroll
-    for (int e = tid; e < kC * kC / 4; e += kT) {  // keep X, then A = X diag(beta) in place
-        const int r = e >> 4, c = (e & 15) * 4;
-        f32x4 x = *reinterpret_cast<const f32x4 *>(bA + r * kP + c);
-        *reinterpret_cast<f32x4 *>(XX + r * kC + c) = x;
-        x[0] *= sB[c]; x[1] *= sB[c + 1]; x[2] *= sB[c + 2]; x[3] *= sB[c + 3];
-        *reinterpret_cast<f32x4 *>(bA + r * kP + c) = x;
-        *reinterpret_cast<f32x4 *>(AA + r * kC + c) = x;
+        for (int e = tid; e < kC * kC / 4; e += kT) {  // keep X, then A = X diag(beta) in place
+            const int r = e >> 4, c = (e & 15) * 4;
+            f32x4 x = *reinterpret_cast<const f32x4 *>(bA + r * kP + c);
+            *reinterpret_cast<f32x4 *>(XX + r * kC + c) = x;
+            x[0] *= sB[c]; x[1] *= sB[c + 1]; x[2] *= sB[c + 2]; x[3] *= sB[c + 3];
+            *reinterpret_cast<f32x4 *>(bA + r * kP + c) = x;
+            *reinterpret_cast<f32x4 *>(AA + r * kC + c) = x;
+        }
     }
-    acc = zero8();
-    mm(acc, nat(bQ), tr(bW), lane, wave);  // Q W^T, keep r <= i
-    store_lds(bQW, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });
-    acc = zero8();
-    mm(acc, nat(bK), tr(bW), lane, wave);  // N = K W^T, keep r > j
-    store_lds(bN, acc, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });
     __syncthreads();
-    l2g((float *)(ws + ly.qwm) + (int64_t)J * kC * kC, bQW, tid);
-    l2g((float *)(ws + ly.nn) + (int64_t)J * kC * kC, bN, tid);
-    acc = zero8();
+    f32x8 acc = zero8();
     mm(acc, nat(bQW), tr(bA), lane, wave);  // Z = QWm A^T
-    store_lds(bZ, acc, lane, wave, [](int, int, float x) { return x; });
+    store_lds(bZ, acc, lane, wave, Id());
     acc = zero8();
     mm(acc, nat(bN), nat(bA), lane, wave);  // Y = N A
-    store_lds(bY, acc, lane, wave, [](int, int, float x) { return x; });
+    store_lds(bY, acc, lane, wave, Id());
     __syncthreads();
-    l2g((float *)(ws + ly.zz) + (int64_t)J * kC * kC, bZ, tid);
-    float *QH = (float *)(ws + ly.qh) + row0 * kD, *KH = (float *)(ws + ly.kh) + row0 * kD;
+    l2g((float *)(ws + ly.zz) + tok, kC, bZ, tid);
+    // diagonal block: P = exp(scale (Q K^T - Z N^T) + cl_i - cl_j - lse_i) for j <= i  (G is dead: P -> bG)
     {
-        acc = zero8();
-        mm(acc, nat(bZ), nat(bW), lane, wave);  // q^ = q - Z W
+        f32x8 sZN = zero8();
+        mm(sZN, nat(bZ), tr(bN), lane, wave);
 #pragma unroll
         for (int vv = 0; vv < 8; ++vv) {
             const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
-            QH[r * kD + c] = bQ[r * kP + c] - acc[vv];
-        }
-        acc = zero8();
-        mm(acc, nat(bY), nat(bW), lane, wave);  // k^ = k - Y W
-#pragma unroll
-        for (int vv = 0; vv < 8; ++vv) {
-            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
-            KH[r * kD + c] = bK[r * kP + c] - acc[vv];
-        }
-        acc = zero8();
-        mm(acc, nat(bA), nat(bW), lane, wave);  // A W (into bQW, free after Z)
-    }
-    __syncthreads();
-    store_lds(bQW, acc, lane, wave, [](int, int, float x) { return x; });
-    __syncthreads();
-    {
-        float *TT = (float *)(ws + ly.tt) + (int64_t)J * kD * kD, *TTt = (float *)(ws + ly.ttt) + (int64_t)J * kD * kD;
-        acc = zero8();
-        mm(acc, tr(bW), nat(bQW), lane, wave);  // T = I - W^T (A W)
-        f32x8 acct = zero8();
-        mm(acct, tr(bQW), nat(bW), lane, wave);  // T^T = I - (A W)^T W
-#pragma unroll
-        for (int vv = 0; vv < 8; ++vv) {
-            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
-            TT[r * kD + c] = (r == c ? 1.f : 0.f) - acc[vv];
-            TTt[r * kD + c] = (r == c ? 1.f : 0.f) - acct[vv];
-        }
-    }
-    // diagonal block: P = exp(scale (Q K^T - Z N^T) + cl_i - cl_j - lse_i) for j <= i
-    f32x8 sQK = zero8(), sZN = zero8();
-    mm(sQK, nat(bQ), tr(bK), lane, wave);
-    mm(sZN, nat(bZ), tr(bN), lane, wave);
-    __syncthreads();  // bG, bY free: P -> bG, v -> bY, do -> bA
-    {
-#pragma unroll
-        for (int vv = 0; vv < 8; ++vv) {
-            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
-            const float s = (scale * (sQK[vv] - sZN[vv]) + (sCl[r] - sCl[c])) * kLog2e - sL2[r];
+            const float s = (scale * (aQK[vv] - sZN[vv]) + (sCl[r] - sCl[c])) * kLog2e - sL2[r];
             bG[r * kP + c] = c <= r ? fast_exp2(s) : 0.f;
         }
     }
-    in2l(bY, v, row0, L, tid);
-    in2l(bA, dout, row0, L, tid);
-    __syncthreads();
-    acc = zero8();
-    mm(acc, nat(bA), tr(bY), lane, wave);  // dP = dO V^T
-    store_lds(bZ, acc, lane, wave, [&](int r, int c, float x) { return bG[r * kP + c] * (x - sDD[r]); });
+    // dP = dO V^T over the chunks; dS = P (dP - D_i) -> bQW (Q W^T is stored)
+    f32x8 aDP = zero8();
+    for (int c = 0; c < NCH; ++c) {
+        __syncthreads();
+        in2l(bQ, dout, D, 64 * c, row0, L, tid);
+        in2l(bK, v, D, 64 * c, row0, L, tid);
+        __syncthreads();
+        mm(aDP, nat(bQ), tr(bK), lane, wave);
+    }
+    store_lds(bQW, aDP, lane, wave, [&](int r, int c, float x) { return bG[r * kP + c] * (x - sDD[r]); });
     __syncthreads();
     {
-        float *EE = (float *)(ws + ly.ee) + (int64_t)J * kC * kC;
-        for (int e = tid; e < kC * kC; e += kT) EE[e] = scale * bZ[(e >> 6) * kP + (e & 63)];
-        T *VF = (T *)(ws + ly.vf) + row0 * kD, *DOF = (T *)(ws + ly.dof) + row0 * kD;  // exact copies of v, do
-        for (int e = tid; e < kC * kD; e += kT) {
-            VF[e] = Elem<T>::from_float(bY[(e >> 6) * kP + (e & 63)]);
-            DOF[e] = Elem<T>::from_float(bA[(e >> 6) * kP + (e & 63)]);
-        }
-        acc = zero8();
-        mm(acc, tr(bG), nat(bA), lane, wave);  // diagonal value gradient P^T dO
-        acc2g((float *)(ws + ly.dvd) + row0 * kD, acc, lane, wave);
+        float *EE = (float *)(ws + ly.ee) + tok;
+        for (int e = tid; e < kC * kC; e += kT) EE[e] = scale * bQW[(e >> 6) * kP + (e & 63)];
         float *rs = (float *)(ws + ly.rsd) + row0, *cs = (float *)(ws + ly.csd) + row0;
         if (tid < kC) {
             float s = 0.f;
-            for (int c = 0; c < kC; ++c) s += bZ[tid * kP + c];
+            for (int c = 0; c < kC; ++c) s += bQW[tid * kP + c];
             rs[tid] = s;
         } else if (tid < 2 * kC) {
             const int c = tid - kC;
             float s = 0.f;
-            for (int r = 0; r < kC; ++r) s += bZ[r * kP + c];
+            for (int r = 0; r < kC; ++r) s += bQW[r * kP + c];
             cs[c] = s;
         } else if (tid < 3 * kC) {
             const int r = tid - 2 * kC;
@@ -446,439 +390,530 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
             if (r == 0) ((float *)(ws + ly.tot))[J] = sCl[kC - 1];
         }
     }
+    // chunks of the head dimension: q^, k^ (fragments), A W (kept for T), V and dO fragments,
+    // the diagonal value gradient
+    const int64_t fo = (int64_t)J * kC * D;  // this block's 64 x D fragment set
+    S *KH1 = (S *)(ws + ly.kh1) + fo, *KH2 = (S *)(ws + ly.kh2) + fo, *V1 = (S *)(ws + ly.v1) + fo;
+    S *DO1 = (S *)(ws + ly.do1) + fo, *DO2 = (S *)(ws + ly.do2) + fo;
+    float *bAW[2] = {bN, bQW};  // A W of chunk 0 / 1 (N and dS are done with)
+    for (int c = 0; c < NCH; ++c) {
+        __syncthreads();
+        in2l(bW, w, D, 64 * c, row0, L, tid);
+        in2l(bQ, q, D, 64 * c, row0, L, tid);
+        in2l(bK, k, D, 64 * c, row0, L, tid);
+        __syncthreads();
+        {
+            f32x8 zw = zero8(), yw = zero8(), aw = zero8();
+            mm(zw, nat(bZ), nat(bW), lane, wave);
+            mm(yw, nat(bY), nat(bW), lane, wave);
+            mm(aw, nat(bA), nat(bW), lane, wave);
+            float *QH = (float *)(ws + ly.qh) + (int64_t)row0 * D + 64 * c;
+#pragma unroll
+            for (int vv = 0; vv < 8; ++vv) {  // each element read and rewritten by the same thread
+                const int r = arow(vv, lane, wave), cc = acol(vv, lane, wave);
+                QH[(int64_t)r * D + cc] = bQ[r * kP + cc] - zw[vv];  // q^ = q - Z W
+                bK[r * kP + cc] -= yw[vv];                            // k^ = k - Y W
+            }
+            store_lds(bAW[c], aw, lane, wave, Id());
+        }
+        __syncthreads();
+        tile2frag<S, false>(KH1, KCD, 0, 4 * c, bK, tid);  // k^: rows keys, k over d
+        tile2frag<S, true>(KH2, 4, 2 * c, 0, bK, tid);     // k^^T: rows d, k over keys
+        __syncthreads();
+        in2l(bQ, v, D, 64 * c, row0, L, tid);
+        in2l(bK, dout, D, 64 * c, row0, L, tid);
+        __syncthreads();
+        tile2frag<S, false>(V1, KCD, 0, 4 * c, bQ, tid);   // V: rows keys
+        tile2frag<S, false>(DO1, KCD, 0, 4 * c, bK, tid);  // dO: rows queries
+        tile2frag<S, true>(DO2, 4, 2 * c, 0, bK, tid);     // dO^T: rows d
+        acc = zero8();
+        mm(acc, tr(bG), nat(bK), lane, wave);  // diagonal value gradient P^T dO
+        acc2g((float *)(ws + ly.dvd) + (int64_t)row0 * D + 64 * c, D, acc, lane, wave);
+    }
+    // T - I = -W^T (A W) and its transpose, block (c1, c2) = rows of chunk c1, columns of chunk c2
+    const int64_t fd = (int64_t)J * D * D;
+    S *NT = (S *)(ws + ly.nt) + fd, *NTT = (S *)(ws + ly.ntt) + fd;
+    for (int c1 = 0; c1 < NCH; ++c1) {
+        __syncthreads();
+        in2l(bW, w, D, 64 * c1, row0, L, tid);
+        __syncthreads();
+        for (int c2 = 0; c2 < NCH; ++c2) {
+            acc = zero8();
+            mm(acc, tr(bW), nat(bAW[c2]), lane, wave);
+            store_lds(bQ, acc, lane, wave, [](int, int, float x) { return -x; });
+            __syncthreads();
+            tile2frag<S, false>(NT, KCD, 2 * c1, 4 * c2, bQ, tid);  // (T - I): rows d_out, k over d_in
+            tile2frag<S, true>(NTT, KCD, 2 * c2, 4 * c1, bQ, tid);  // (T - I)^T
+            __syncthreads();
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Query-major up walk: one workgroup per (query block I >= 1, head); heaviest first.
+// The walks: two waves per query block (down and up walks), each owning 32 of
+// its queries; matrix-core operands are fragments loaded from the workspace.
 // ---------------------------------------------------------------------------
-// Down walk of the query blocks: one workgroup per (query block I >= 1, head),
-// q~^(J-1) = T_J q~^(J) from q~^(I-1) = q^ down to J = 0, each q~^(J) stored for
-// the pair (I, J), with the gate sum of the blocks strictly between I and J.
-// One product per step on two LDS tiles, so four workgroups share a compute
-// unit and hide each other's latency.
-template <typename SC>
-__global__ __launch_bounds__(kT, 4) void bwd_down_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) float sm[2 * kTile];
-    float *bQt = sm, *bT = bQt + kTile;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+// Per-wave LDS scratch for writing an accumulator tile set (rows d, columns the
+// wave's 32 queries) back as fragments with the query index inside the lane.
+constexpr int kXs = 36;  // row stride (floats): rows 16-byte aligned
+
+// acc tiles t[dt] (rows d = 32 dt + acc_row(r, h), columns this wave's 32 queries) ->
+// fragments (rt = dt, kc = 2 w + 0/1) of a set with rows d and k over the block's 64 queries.
+// Only this wave touches x, and a wave's LDS accesses are performed in order.
+template <typename S, int D>
+__device__ __forceinline__ void store_transposed(S *dst, const f32x16 *t, float *x, int w, int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[(32 * dt + acc_row(r, h)) * kXs + l32] = t[dt][r];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int kcl = 0; kcl < 2; ++kcl) {
+            const float *src = x + (32 * dt + l32) * kXs + 16 * kcl + 4 * h;
+            const f32x4 lo = *reinterpret_cast<const f32x4 *>(src), hi = *reinterpret_cast<const f32x4 *>(src + 8);
+            const float y[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            stfrag<S>(dst, dt, 2 * w + kcl, 4, lane, Elem<S>::from_f32(y));
+        }
+}
+
+// Down walk: one workgroup (two waves) per (query block I >= 1, head), heaviest
+// first.  q~^T (rows d, the wave's 32 queries) stays in fp32 accumulators:
+// q~^T <- q~^T + (T_J - I) q~^T; q~^(J) is stored for the pair (I, J) with rows
+// queries (for the logits) and with rows d (for the key walk's sums over
+// queries), with the gate sum of the blocks strictly between I and J.
+template <typename S, int D>
+__global__ __launch_bounds__(128) void bwd_down_kernel(BwdArgs a) {
+    typedef typename Elem<S>::Frag Frag;
+    constexpr int KCD = D / 16, RTD = D / 32;
+    __shared__ __attribute__((aligned(16))) float sx[2][D * kXs];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int nb = a.nb, hc = a.hc;
     const int gl = blockIdx.x % hc, I = nb - 1 - blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
-    const float *TT = (const float *)(ws + ly.tt), *tot = (const float *)(ws + ly.tot);
+    const S *NT = (const S *)(ws + ly.nt);
+    const float *tot = (const float *)(ws + ly.tot);
     float *MID = (float *)(ws + ly.mid);
-    SC *QS = (SC *)(ws + ly.qs);
+    S *QS1 = (S *)(ws + ly.qs1), *QS2 = (S *)(ws + ly.qs2);
     const int row0 = I * kC;
 
-    g2l(bQt, (const float *)(ws + ly.qh) + row0 * kD, tid);
+    f32x16 qt[RTD];
+    {
+        const float *qh = (const float *)(ws + ly.qh) + (int64_t)(row0 + 32 * w + l32) * D;
+#pragma unroll
+        for (int dt = 0; dt < RTD; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(qh + 32 * dt + 8 * g4 + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qt[dt][4 * g4 + e] = x[e];
+            }
+    }
     float mid = 0.f;
     if (tid == 0) MID[pair_index(I, I - 1)] = 0.f;
-    Stage rT;
-    if (I - 1 >= 1) gload(rT, TT + (int64_t)(I - 1) * kD * kD, tid);
-    for (int J = I - 1; J >= 1; --J) {  // bQt holds q~^(J)
-        lstore(bT, rT, tid);
-        __syncthreads();
-        l2g_sc(QS + pair_index(I, J) * kC * kD, bQt, tid);
-        if (J - 1 >= 1) gload(rT, TT + (int64_t)(J - 1) * kD * kD, tid);  // next step's transition
-        f32x8 acc = zero8();
-        mm(acc, nat(bQt), tr(bT), lane, wave);  // q~^(J-1) = T_J q~^(J) (rows: Q~ T^T)
-        __syncthreads();
-        store_lds(bQt, acc, lane, wave, [](int, int, float x) { return x; });
-        mid += tot[J];
-        if (tid == 0) MID[pair_index(I, J - 1)] = mid;
+    for (int J = I - 1; J >= 0; --J) {
+        const int64_t p = pair_index(I, J);
+        Frag qf[KCD];
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) qf[kc] = acc_frag<S>(qt[kc >> 1], kc & 1);
+        S *q1 = QS1 + p * kC * D;
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) stfrag<S>(q1, w, kc, KCD, lane, qf[kc]);
+        store_transposed<S, D>(QS2 + p * kC * D, qt, sx[w], w, lane);
+        if (J >= 1) {
+            const S *nt = NT + (int64_t)J * D * D;
+#pragma unroll
+            for (int dt = 0; dt < RTD; ++dt)
+#pragma unroll
+                for (int kc = 0; kc < KCD; ++kc) Elem<S>::mma(qt[dt], ldfrag<S>(nt, dt, kc, KCD, lane), qf[kc]);
+            mid += tot[J];
+            if (tid == 0) MID[pair_index(I, J - 1)] = mid;
+        }
     }
-    __syncthreads();
-    l2g_sc(QS + pair_index(I, 0) * kC * kD, bQt, tid);
 }
 
-template <typename SC>
-__global__ __launch_bounds__(kT) void bwd_query_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) float sm[8 * kTile + 4 * kC];
-    float *bQt = sm, *bT = bQt + kTile, *bK = bT + kTile, *bV = bK + kTile, *bDO = bV + kTile, *bG = bDO + kTile,
-          *bS = bG + kTile, *bP = bS + kTile;
-    float *sL2 = bP + kTile, *sDD = sL2 + kC, *sCq = sDD + kC, *sCk = sCq + kC;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Up walk: one workgroup (two waves) per (query block I >= 1, head), heaviest
+// first.  For J = 0 .. I-1: S^T = K^_J q~^T and dP^T = V_J dO^T (rows keys,
+// columns the wave's queries), P and dS, then the adjoint (rows d, fp32
+// accumulators) G^T <- G^T + (T_J - I)^T G^T + K^_J^T (scale dS^T).  G^(J) is
+// stored with rows d for the pair (I, J + 1); G^(I-1) = dq^_I.
+template <typename S, int D>
+__global__ __launch_bounds__(128) void bwd_up_kernel(BwdArgs a) {
+    typedef typename Elem<S>::Frag Frag;
+    constexpr int KCD = D / 16, RTD = D / 32;
+    __shared__ __attribute__((aligned(16))) float sx[2][D * kXs];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int nb = a.nb, hc = a.hc;
     const int gl = blockIdx.x % hc, I = nb - 1 - blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
-    const float *TTt = (const float *)(ws + ly.ttt), *KH = (const float *)(ws + ly.kh);
-    const SC *VF = (const SC *)(ws + ly.vf);
-    const float *MID = (const float *)(ws + ly.mid);
-    float *CSP = (float *)(ws + ly.csp);
-    SC *QS = (SC *)(ws + ly.qs), *GS = (SC *)(ws + ly.gs), *PS = (SC *)(ws + ly.ps), *DS = (SC *)(ws + ly.ds);
+    const S *KH1 = (const S *)(ws + ly.kh1), *KH2 = (const S *)(ws + ly.kh2), *V1 = (const S *)(ws + ly.v1);
+    const S *NTT = (const S *)(ws + ly.ntt), *QS1 = (const S *)(ws + ly.qs1);
+    S *GS2 = (S *)(ws + ly.gs2);
+    const float *MID = (const float *)(ws + ly.mid), *CKK = (const float *)(ws + ly.ckk);
     const float scale = a.scale;
-    const int row0 = I * kC;
+    const int row0 = I * kC, qi = row0 + 32 * w + l32;  // this lane's query (column of the accumulators)
+    const float l2 = ((const float *)(ws + ly.l2))[qi], dd = ((const float *)(ws + ly.dd))[qi];
+    const float cq = ((const float *)(ws + ly.clq))[qi];
 
-    Stage rT, rK;
-    typename StageOf<SC>::T rQ, rV;
-    // up: adjoint G
-    {
-        typename StageOf<SC>::T rD;
-        gload(rD, (const SC *)(ws + ly.dof) + row0 * kD, tid);
-        lstore(bDO, rD, tid);
-    }
-    if (tid < kC) {
-        sL2[tid] = ((const float *)(ws + ly.l2))[row0 + tid];
-        sDD[tid] = ((const float *)(ws + ly.dd))[row0 + tid];
-        sCq[tid] = ((const float *)(ws + ly.clq))[row0 + tid];
-    }
-    f32x8 accG = zero8();
+    Frag dof[KCD];  // dO with k over d, lane <-> query: the B operand of dP^T
+#pragma unroll
+    for (int kc = 0; kc < KCD; ++kc)
+        dof[kc] = ldfrag<S>((const S *)(ws + ly.do1) + (int64_t)I * kC * D, w, kc, KCD, lane);
+    f32x16 gt[RTD];
+#pragma unroll
+    for (int dt = 0; dt < RTD; ++dt) gt[dt] = f32x16{};
     float rsum = 0.f;
-    gload(rQ, QS + pair_index(I, 0) * kC * kD, tid);
-    gload(rK, KH, tid);
-    gload(rV, VF, tid);
-    float rck = tid < kC ? ((const float *)(ws + ly.ckk))[tid] : 0.f, rmid = MID[pair_index(I, 0)];
     for (int J = 0; J < I; ++J) {
-        const int64_t p = pair_index(I, J);
-        lstore(bQt, rQ, tid);
-        lstore(bK, rK, tid);
-        lstore(bV, rV, tid);
-        if (J >= 1) lstore(bT, rT, tid);
-        if (tid < kC) sCk[tid] = rck;
-        const float midJ = rmid;
-        __syncthreads();
-        if (J >= 1) l2g_sc(GS + p * kC * kD, bG, tid);  // G^(J-1) (in bG since the last step) for the key-major walk
-        if (J + 1 < I) {  // next step's tiles, in flight while this step computes
-            gload(rQ, QS + (p + 1) * kC * kD, tid);
-            gload(rK, KH + (int64_t)(J + 1) * kC * kD, tid);
-            gload(rV, VF + (int64_t)(J + 1) * kC * kD, tid);
-            gload(rT, TTt + (int64_t)(J + 1) * kD * kD, tid);
-            if (tid < kC) rck = ((const float *)(ws + ly.ckk))[(J + 1) * kC + tid];
-            rmid = MID[p + 1];
-        }
-        f32x8 s = zero8(), dp = zero8();
-        mm(s, nat(bQt), tr(bK), lane, wave);
-        mm(dp, nat(bDO), tr(bV), lane, wave);
+        const int64_t p = pair_index(I, J), fo = (int64_t)J * kC * D;
+        const float mid = MID[p];
+        Frag qf[KCD];
 #pragma unroll
-        for (int vv = 0; vv < 8; ++vv) {
-            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
-            const float P = fast_exp2((scale * s[vv] + sCq[r] + sCk[c] + midJ) * kLog2e - sL2[r]);
-            bP[r * kP + c] = P;
-            bS[r * kP + c] = P * (dp[vv] - sDD[r]);
-        }
-        __syncthreads();
-        l2g_sc(PS + p * kC * kC, bP, tid);  // P and dS for the key-major walk
-        l2g_sc(DS + p * kC * kC, bS, tid);
-        {   // column sums of this pair's dS (fp32) for the gate, summed over I by the key-major walk
-            const int cc = tid >> 3, p0 = tid & 7;
-            float t = 0.f;
+        for (int kc = 0; kc < KCD; ++kc) qf[kc] = ldfrag<S>(QS1 + p * kC * D, w, kc, KCD, lane);
+        f32x16 s[2], dp[2];
 #pragma unroll
-            for (int r = p0; r < kC; r += 8) t += bS[r * kP + cc];
-            t = sum8(t);
-            if (p0 == 0) CSP[p * kC + cc] = t;
-        }
-        f32x8 gt = zero8(), xs = zero8();
-        if (J >= 1) mm(gt, nat(bG), tr(bT), lane, wave);  // bT holds T_J^T here
-        mm(xs, nat(bS), nat(bK), lane, wave);
+        for (int kt = 0; kt < 2; ++kt) {
+            s[kt] = f32x16{};
+            dp[kt] = f32x16{};
 #pragma unroll
-        for (int vv = 0; vv < 8; ++vv) accG[vv] = gt[vv] + scale * xs[vv];
-        {   // row sums of dS: eight lanes per row, eight columns each
-            const f32x4 *row = reinterpret_cast<const f32x4 *>(bS + (tid >> 3) * kP + (tid & 7) * 8);
-            const float t = ((row[0][0] + row[0][1]) + (row[0][2] + row[0][3])) +
-                            ((row[1][0] + row[1][1]) + (row[1][2] + row[1][3]));
-            rsum += sum8(t);
+            for (int kc = 0; kc < KCD; ++kc) {
+                Elem<S>::mma(s[kt], ldfrag<S>(KH1 + fo, kt, kc, KCD, lane), qf[kc]);
+                Elem<S>::mma(dp[kt], ldfrag<S>(V1 + fo, kt, kc, KCD, lane), dof[kc]);
+            }
         }
-        __syncthreads();
-        store_lds(bG, accG, lane, wave, [](int, int, float x) { return x; });
+        // P^T and scale dS^T (rows: keys 32 kt + acc_row(r, h); column: this lane's query)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 ck = *reinterpret_cast<const f32x4 *>(CKK + J * kC + 32 * kt + 8 * g4 + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g4 + e;
+                    const float P = fast_exp2((scale * s[kt][r] + cq + ck[e] + mid) * kLog2e - l2);
+                    const float ds = P * (dp[kt][r] - dd);
+                    rsum += ds;
+                    s[kt][r] = scale * ds;
+                }
+            }
+        Frag gf[KCD], sf[4];
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) gf[kc] = acc_frag<S>(gt[kc >> 1], kc & 1);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) sf[kc] = acc_frag<S>(s[kc >> 1], kc & 1);
+        const S *ntt = NTT + (int64_t)J * D * D;
+#pragma unroll
+        for (int dt = 0; dt < RTD; ++dt) {
+            if (J >= 1) {
+#pragma unroll
+                for (int kc = 0; kc < KCD; ++kc) Elem<S>::mma(gt[dt], ldfrag<S>(ntt, dt, kc, KCD, lane), gf[kc]);
+            }
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) Elem<S>::mma(gt[dt], ldfrag<S>(KH2 + fo, dt, kc, 4, lane), sf[kc]);
+        }
+        if (J + 1 < I) store_transposed<S, D>(GS2 + pair_index(I, J + 1) * kC * D, gt, sx[w], w, lane);
     }
-    acc2g((float *)(ws + ly.dqo) + row0 * kD, accG, lane, wave);
-    if ((tid & 7) == 0) ((float *)(ws + ly.rso))[row0 + (tid >> 3)] = rsum;
+    rsum = other_half_sum(rsum);  // lanes l and l ^ 32 hold the other keys of the same query
+    float *dqo = (float *)(ws + ly.dqo) + (int64_t)qi * D;
+#pragma unroll
+    for (int dt = 0; dt < RTD; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 x = {gt[dt][4 * g4], gt[dt][4 * g4 + 1], gt[dt][4 * g4 + 2], gt[dt][4 * g4 + 3]};
+            *reinterpret_cast<f32x4 *>(dqo + 32 * dt + 8 * g4 + 4 * h) = x;
+        }
+    if (h == 0) ((float *)(ws + ly.rso))[qi] = rsum;
 }
 
-// ---------------------------------------------------------------------------
-// Key-major walk: one workgroup per (key block J <= nb-2, head); heaviest first.
-// The query-major walk left P, dS, q~ and G of every pair, so this walk only
-// sums over the query blocks: dV_J += P^T dO_I, dk^_J += scale dS^T q~,
-// dT_J += G^(J-1)^T q~, and the column sums of dS for the gate.
-// ---------------------------------------------------------------------------
-template <typename SC>
-__global__ __launch_bounds__(kT) void bwd_key_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) float sm[5 * kTile];
-    float *bQt = sm, *bDO = bQt + kTile, *bG = bDO + kTile, *bP = bG + kTile, *bS = bP + kTile;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Key walk: one workgroup per (key block J <= nb-2, head).  Wave w takes the
+// logit tile of queries 32 qt .. (qt = w & 1) and keys 32 kt .. (kt = (w >> 1)
+// & 1) of every later query block I, recomputes P and dS, and accumulates over
+// its 32 queries dV^T = dO^T P and dk^^T = q~^T dS (rows: its group dh = w >> 2
+// of head-dimension tiles) and dT = G^T q~ (its rows of dT); the two query
+// halves are added at the end.
+template <int D>
+struct KeyCfg {
+    static constexpr int NW = D == 64 ? 4 : 8;  // waves
+    static constexpr int NDH = NW / 4;           // groups of head-dimension tiles
+    static constexpr int RTW = (D / 32) / NDH;   // dV^T, dk^T row tiles per wave
+    static constexpr int NG = 2 * NDH;           // wave groups (kt, dh) splitting the rows of dT
+    static constexpr int TRW = (D / 32) / NG;    // dT row tiles per wave
+};
+
+template <typename S, int D>
+__global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel(BwdArgs a) {
+    typedef typename Elem<S>::Frag Frag;
+    typedef KeyCfg<D> K;
+    constexpr int KCD = D / 16, RTD = D / 32, RTW = K::RTW, TRW = K::TRW;
+    constexpr int NACC = 2 * RTW + TRW * RTD;  // accumulator tiles per wave
+    __shared__ __attribute__((aligned(16))) float sred[K::NW / 2][16 * 65];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int qt = w & 1, kt = (w >> 1) & 1, dh = w >> 2, grp = kt + 2 * dh;
     const int nb = a.nb, hc = a.hc;
     const int gl = blockIdx.x % hc, J = blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
-    const float *CSP = (const float *)(ws + ly.csp);
-    const SC *DOF = (const SC *)(ws + ly.dof);
-    const SC *QS = (const SC *)(ws + ly.qs), *GS = (const SC *)(ws + ly.gs), *PS = (const SC *)(ws + ly.ps),
-             *DS = (const SC *)(ws + ly.ds);
+    const S *QS1 = (const S *)(ws + ly.qs1), *QS2 = (const S *)(ws + ly.qs2), *GS2 = (const S *)(ws + ly.gs2);
+    const S *DO1 = (const S *)(ws + ly.do1), *DO2 = (const S *)(ws + ly.do2);
+    const float *MID = (const float *)(ws + ly.mid), *L2 = (const float *)(ws + ly.l2);
+    const float *DD = (const float *)(ws + ly.dd), *CLQ = (const float *)(ws + ly.clq);
     const float scale = a.scale;
+    const int key = J * kC + 32 * kt + l32;  // this lane's key (column of the logit tile)
+    const float ck = ((const float *)(ws + ly.ckk))[key];
 
-    f32x8 dV = zero8(), dK = zero8(), dT = zero8();
+    Frag kf[KCD], vf[KCD];  // k^ and V of key tile kt, k over d: the B operands of S and dP
+    {
+        const int64_t fo = (int64_t)J * kC * D;
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) {
+            kf[kc] = ldfrag<S>((const S *)(ws + ly.kh1) + fo, kt, kc, KCD, lane);
+            vf[kc] = ldfrag<S>((const S *)(ws + ly.v1) + fo, kt, kc, KCD, lane);
+        }
+    }
+    f32x16 acc[NACC];  // dV^T (RTW), dk^^T (RTW), dT rows grp * TRW .. (TRW x RTD)
+#pragma unroll
+    for (int t = 0; t < NACC; ++t) acc[t] = f32x16{};
     float csum = 0.f;
-    typename StageOf<SC>::T rO, rQ, rG, rP, rS;
-    float rcs = 0.f;
-    auto fetch = [&](int I) {
-        const int64_t p = pair_index(I, J);
-        gload(rQ, QS + p * kC * kD, tid);
-        gload(rO, DOF + (int64_t)I * kC * kD, tid);
-        if (J >= 1) gload(rG, GS + p * kC * kD, tid);
-        gload(rP, PS + p * kC * kC, tid);
-        gload(rS, DS + p * kC * kC, tid);
-        if (tid < kC) rcs = CSP[p * kC + tid];
-    };
-    fetch(J + 1);
     for (int I = J + 1; I < nb; ++I) {
-        lstore(bQt, rQ, tid);
-        lstore(bDO, rO, tid);
-        if (J >= 1) lstore(bG, rG, tid);
-        lstore(bP, rP, tid);
-        lstore(bS, rS, tid);
-        __syncthreads();
-        if (tid < kC) csum += rcs;
-        if (I + 1 < nb) fetch(I + 1);  // next step's tiles, in flight while this step computes
-        mm(dV, tr(bP), nat(bDO), lane, wave);
-        mm(dK, tr(bS), nat(bQt), lane, wave);
-        if (J >= 1) mm(dT, tr(bG), nat(bQt), lane, wave);
-        __syncthreads();
-    }
-    const int row0 = J * kC;
+        const int64_t p = pair_index(I, J), po = p * kC * D, bo = (int64_t)I * kC * D;
+        const float mid = MID[p];
+        f32x16 s = {}, dp = {};
 #pragma unroll
-    for (int vv = 0; vv < 8; ++vv) dK[vv] *= scale;
-    acc2g((float *)(ws + ly.dko) + row0 * kD, dK, lane, wave);
-    acc2g((float *)(ws + ly.dvo) + row0 * kD, dV, lane, wave);
-    acc2g((float *)(ws + ly.dt) + (int64_t)J * kD * kD, dT, lane, wave);
-    if (tid < kC) ((float *)(ws + ly.cso))[row0 + tid] = csum;
-}
-
-// The key-major walk for bf16 inputs: its five tiles arrive in bf16 and every
-// product reads both operands with single loads (A transposed, B by rows), so
-// the tiles stay bf16 in LDS (8 KiB each, row stride 64: the sixteen lanes of
-// a read walk a row) and are widened as they are read.  At 40 KiB of LDS two
-// workgroups share a compute unit.
-__device__ __forceinline__ float h2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
-
-// acc += X^T Y for 64x64 bf16 tiles in LDS (row stride 64), fp32 products.
-__device__ __forceinline__ void mm_tn_h(f32x8 &acc, const uint16_t *X, const uint16_t *Y, int lane, int wave) {
-    const int r = 16 * (wave >> 1) + (lane & 15), c0 = 32 * (wave & 1) + (lane & 15), q = lane >> 4;
-    f32x4 lo = acc.lo, hi = acc.hi;
+        for (int kc = 0; kc < KCD; ++kc) {
+            Elem<S>::mma(s, ldfrag<S>(QS1 + po, qt, kc, KCD, lane), kf[kc]);
+            Elem<S>::mma(dp, ldfrag<S>(DO1 + bo, qt, kc, KCD, lane), vf[kc]);
+        }
+        // P and dS (rows: queries 32 qt + acc_row(r, h) of block I; column: this lane's key)
+        const int q0 = I * kC + 32 * qt + 4 * h;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int k0 = 16 * g + 4 * q;
-        float x[4], y0[4], y1[4];
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 l2 = *reinterpret_cast<const f32x4 *>(L2 + q0 + 8 * g4);
+            const f32x4 dd = *reinterpret_cast<const f32x4 *>(DD + q0 + 8 * g4);
+            const f32x4 cq = *reinterpret_cast<const f32x4 *>(CLQ + q0 + 8 * g4);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            x[t] = h2f(X[(k0 + t) * 64 + r]);
-            y0[t] = h2f(Y[(k0 + t) * 64 + c0]);
-            y1[t] = h2f(Y[(k0 + t) * 64 + c0 + 16]);
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g4 + e;
+                const float P = fast_exp2((scale * s[r] + cq[e] + ck + mid) * kLog2e - l2[e]);
+                const float ds = P * (dp[r] - dd[e]);
+                csum += ds;
+                s[r] = ds;
+                dp[r] = P;
+            }
+        }
+        Frag pf[2], sf[2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            pf[cc] = acc_frag<S>(dp, cc);
+            sf[cc] = acc_frag<S>(s, cc);
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            lo = __builtin_amdgcn_mfma_f32_16x16x4f32(x[t], y0[t], lo, 0, 0, 0);
-            hi = __builtin_amdgcn_mfma_f32_16x16x4f32(x[t], y1[t], hi, 0, 0, 0);
+        for (int i = 0; i < RTW; ++i) {
+            const int dt = dh * RTW + i;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                Elem<S>::mma(acc[i], ldfrag<S>(DO2 + bo, dt, 2 * qt + cc, 4, lane), pf[cc]);
+                Elem<S>::mma(acc[RTW + i], ldfrag<S>(QS2 + po, dt, 2 * qt + cc, 4, lane), sf[cc]);
+            }
+        }
+        if (J >= 1) {
+#pragma unroll
+            for (int i = 0; i < TRW; ++i) {
+                const int rt = grp * TRW + i;
+                Frag ga[2];
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) ga[cc] = ldfrag<S>(GS2 + po, rt, 2 * qt + cc, 4, lane);
+#pragma unroll
+                for (int ct = 0; ct < RTD; ++ct)
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc)
+                        Elem<S>::mma(acc[2 * RTW + i * RTD + ct], ga[cc],
+                                     ldfrag<S>(QS2 + po, ct, 2 * qt + cc, 4, lane));
+            }
         }
     }
-    acc.lo = lo;
-    acc.hi = hi;
-}
-
-__global__ __launch_bounds__(kT, 2) void bwd_key_kernel_h(BwdArgs a) {
-    constexpr int kTh = kC * 64;  // elements of one bf16 tile
-    __shared__ __attribute__((aligned(16))) uint16_t sm[5 * kTh];
-    uint16_t *bQt = sm, *bDO = bQt + kTh, *bG = bDO + kTh, *bP = bG + kTh, *bS = bP + kTh;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nb = a.nb, hc = a.hc;
-    const int gl = blockIdx.x % hc, J = blockIdx.x / hc;
-    const BwdLayout &ly = a.ly;
-    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
-    const float *CSP = (const float *)(ws + ly.csp);
-    const uint16_t *DOF = (const uint16_t *)(ws + ly.dof), *QS = (const uint16_t *)(ws + ly.qs),
-                   *GS = (const uint16_t *)(ws + ly.gs), *PS = (const uint16_t *)(ws + ly.ps),
-                   *DS = (const uint16_t *)(ws + ly.ds);
-    const float scale = a.scale;
-
-    f32x8 dV = zero8(), dK = zero8(), dT = zero8();
-    float csum = 0.f, rcs = 0.f;
-    u32x4 rO, rQ, rG, rP, rS;  // eight bf16 per thread and tile: row tid / 8, columns 8 (tid % 8) ..
-    auto fetch = [&](int I) {
-        const int64_t p = pair_index(I, J);
-        rQ = *reinterpret_cast<const u32x4 *>(QS + p * kC * kD + tid * 8);
-        rO = *reinterpret_cast<const u32x4 *>(DOF + (int64_t)I * kC * kD + tid * 8);
-        if (J >= 1) rG = *reinterpret_cast<const u32x4 *>(GS + p * kC * kD + tid * 8);
-        rP = *reinterpret_cast<const u32x4 *>(PS + p * kC * kC + tid * 8);
-        rS = *reinterpret_cast<const u32x4 *>(DS + p * kC * kC + tid * 8);
-        if (tid < kC) rcs = CSP[p * kC + tid];
-    };
-    fetch(J + 1);
-    for (int I = J + 1; I < nb; ++I) {
-        *reinterpret_cast<u32x4 *>(bQt + tid * 8) = rQ;
-        *reinterpret_cast<u32x4 *>(bDO + tid * 8) = rO;
-        if (J >= 1) *reinterpret_cast<u32x4 *>(bG + tid * 8) = rG;
-        *reinterpret_cast<u32x4 *>(bP + tid * 8) = rP;
-        *reinterpret_cast<u32x4 *>(bS + tid * 8) = rS;
+    csum = other_half_sum(csum);  // lanes l and l ^ 32 hold the other queries of the same key
+    // add the query half qt = 1 into qt = 0 (the partner wave w + 1), one tile at a time
+    float *red = sred[w >> 1];
+    for (int t = 0; t <= NACC; ++t) {
         __syncthreads();
-        if (tid < kC) csum += rcs;
-        if (I + 1 < nb) fetch(I + 1);  // next step's tiles, in flight while this step computes
-        mm_tn_h(dV, bP, bDO, lane, wave);              // P^T dO
-        mm_tn_h(dK, bS, bQt, lane, wave);              // dS^T q~
-        if (J >= 1) mm_tn_h(dT, bG, bQt, lane, wave);  // G^T q~
-        __syncthreads();
-    }
-    const int row0 = J * kC;
+        if (qt == 1) {
+            if (t < NACC) {
 #pragma unroll
-    for (int vv = 0; vv < 8; ++vv) dK[vv] *= scale;
-    acc2g((float *)(ws + ly.dko) + row0 * kD, dK, lane, wave);
-    acc2g((float *)(ws + ly.dvo) + row0 * kD, dV, lane, wave);
-    acc2g((float *)(ws + ly.dt) + (int64_t)J * kD * kD, dT, lane, wave);
-    if (tid < kC) ((float *)(ws + ly.cso))[row0 + tid] = csum;
+                for (int r = 0; r < 16; ++r) red[r * 65 + lane] = acc[t][r];
+            } else {
+                red[lane] = csum;
+            }
+        }
+        __syncthreads();
+        if (qt == 0) {
+            if (t < NACC) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[t][r] += red[r * 65 + lane];
+            } else {
+                csum += red[lane];
+            }
+        }
+    }
+    if (qt != 0) return;
+    float *dvo = (float *)(ws + ly.dvo) + (int64_t)key * D, *dko = (float *)(ws + ly.dko) + (int64_t)key * D;
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+        const int dt = dh * RTW + i;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * dt + 8 * g4 + 4 * h;
+            const f32x4 xv = {acc[i][4 * g4], acc[i][4 * g4 + 1], acc[i][4 * g4 + 2], acc[i][4 * g4 + 3]};
+            const f32x4 xk = {scale * acc[RTW + i][4 * g4], scale * acc[RTW + i][4 * g4 + 1],
+                              scale * acc[RTW + i][4 * g4 + 2], scale * acc[RTW + i][4 * g4 + 3]};
+            *reinterpret_cast<f32x4 *>(dvo + d0) = xv;
+            *reinterpret_cast<f32x4 *>(dko + d0) = xk;
+        }
+    }
+    if (J >= 1) {  // dT^T: element (c, r) = dT[r][c]; lane c writes 4 consecutive r
+        float *dtt = (float *)(ws + ly.dtt) + (int64_t)J * D * D;
+#pragma unroll
+        for (int i = 0; i < TRW; ++i) {
+            const int rt = grp * TRW + i;
+#pragma unroll
+            for (int ct = 0; ct < RTD; ++ct)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const f32x16 &x = acc[2 * RTW + i * RTD + ct];
+                    const f32x4 y = {x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]};
+                    *reinterpret_cast<f32x4 *>(dtt + (int64_t)(32 * ct + l32) * D + 32 * rt + 8 * g4 + 4 * h) = y;
+                }
+        }
+    }
+    if (dh == 0 && h == 0) ((float *)(ws + ly.cso))[J * kC + 32 * kt + l32] = csum;
 }
 
 // ---------------------------------------------------------------------------
 // Block backward: one workgroup per (block J, head).
 // ---------------------------------------------------------------------------
 template <typename T>
-__device__ __forceinline__ void acc2out(T *g, const f32x8 &acc, int row0, int L, int lane, int wave) {
+__device__ __forceinline__ void acc2out(T *g, int D, const f32x8 &acc, int row0, int L, int lane, int wave) {
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
         const int r = arow(v, lane, wave), c = acol(v, lane, wave);
-        if (row0 + r < L) g[(int64_t)(row0 + r) * kD + c] = Elem<T>::from_float(acc[v]);
+        if (row0 + r < L) g[(int64_t)(row0 + r) * D + c] = Elem<T>::from_float(acc[v]);
     }
 }
 
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
+    constexpr int NCH = D / 64;
     __shared__ __attribute__((aligned(16))) float sm[9 * kTile + 2 * kC];
-    float *bW = sm, *bQ = bW + kTile, *bK = bQ + kTile, *bX = bK + kTile, *bA = bX + kTile, *bQW = bA + kTile,
-          *b6 = bQW + kTile, *bN = b6 + kTile, *b8 = bN + kTile;
+    float *bE = sm, *bN = bE + kTile, *bZ = bN + kTile, *bX = bZ + kTile, *bA = bX + kTile, *bQW = bA + kTile,
+          *b6 = bQW + kTile, *b7 = b6 + kTile, *b8 = b7 + kTile;
     float *sB = b8 + kTile, *sRed = sB + kC;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int J = blockIdx.x, gl = blockIdx.y, g = a.g0 + gl, L = a.L, nb = a.nb, row0 = J * kC;
     const int64_t hoff = (int64_t)g * L;
-    const T *q = (const T *)a.q + hoff * kD, *k = (const T *)a.k + hoff * kD, *w = (const T *)a.w + hoff * kD;
+    const T *q = (const T *)a.q + hoff * D, *k = (const T *)a.k + hoff * D, *w = (const T *)a.w + hoff * D;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
     const bool hasQ = J >= 1, hasK = J <= nb - 2, hasT = J >= 1 && J <= nb - 2;
-    auto id = [](int, int, float x) { return x; };
+    const int64_t tok = (int64_t)J * kC * kC, nat0 = (int64_t)row0 * D;
+    const float *dqo = (const float *)(ws + ly.dqo) + nat0, *dko = (const float *)(ws + ly.dko) + nat0;
 
-    in2l(bW, w, row0, L, tid);
-    in2l(bQ, q, row0, L, tid);
-    in2l(bK, k, row0, L, tid);
     if (tid < kC) sB[tid] = row0 + tid < L ? a.beta[hoff + row0 + tid] : 0.f;
-    {   // the block's UT quantities, as prep computed them
-        const int64_t o = (int64_t)J * kC * kC;
-        g2l(bX, (const float *)(ws + ly.xx) + o, tid);
-        g2l(bA, (const float *)(ws + ly.aa) + o, tid);
-        g2l(bQW, (const float *)(ws + ly.qwm) + o, tid);
-        g2l(bN, (const float *)(ws + ly.nn) + o, tid);
-        g2l(b6, (const float *)(ws + ly.zz) + o, tid);
-        g2l(b8, (const float *)(ws + ly.ee) + o, tid);  // E = scale dS of the diagonal block
+    g2l(bE, (const float *)(ws + ly.ee) + tok, kC, tid);  // scale dS of the diagonal block
+    g2l(bN, (const float *)(ws + ly.nn) + tok, kC, tid);
+    g2l(bZ, (const float *)(ws + ly.zz) + tok, kC, tid);
+    g2l(bX, (const float *)(ws + ly.xx) + tok, kC, tid);
+    g2l(bA, (const float *)(ws + ly.aa) + tok, kC, tid);
+    g2l(bQW, (const float *)(ws + ly.qwm) + tok, kC, tid);
+    __syncthreads();
+    // ---- token-level quantities
+    f32x8 aZ = zero8(), aNn = zero8(), aY = zero8(), aG = zero8(), aA = zero8(), acc;
+    mm(aZ, nat(bE), nat(bN), lane, wave);    // E N         (dZ = -(E N + dq^ W^T))
+    mm(aNn, tr(bE), nat(bZ), lane, wave);    // E^T Z       (dN = -E^T Z + dY A^T)
+    for (int c = 0; c < NCH; ++c) {
+        __syncthreads();
+        in2l(b6, w, D, 64 * c, row0, L, tid);
+        if (hasQ) g2l(b7, dqo + 64 * c, D, tid);
+        else zero_lds(b7, tid);
+        if (hasK) g2l(b8, dko + 64 * c, D, tid);
+        else zero_lds(b8, tid);
+        __syncthreads();
+        mm(aZ, nat(b7), tr(b6), lane, wave);  // + dq^ W^T
+        mm(aY, nat(b8), tr(b6), lane, wave);  // dk^ W^T   (dY = -dk^ W^T)
+        mm(aG, nat(b6), tr(b6), lane, wave);  // G = W W^T
     }
-    f32x8 acc;
-    __syncthreads();
-    f32x8 dQ = zero8(), dK = zero8(), dZ = zero8(), dN = zero8(), dW = zero8(), dA = zero8();
-    mm(dQ, nat(b8), nat(bK), lane, wave);   // E K
-    mm(dK, tr(b8), nat(bQ), lane, wave);    // E^T Q
-    mm(dZ, nat(b8), nat(bN), lane, wave);   // (E N), negated below
-    mm(dN, tr(b8), nat(b6), lane, wave);    // (E^T Z), negated below
-    __syncthreads();
-    if (hasQ) g2l(b8, (const float *)(ws + ly.dqo) + row0 * kD, tid);  // dq^ from the query-major walk
-    else zero_lds(b8, tid);
-    __syncthreads();
-    mm(dZ, nat(b8), tr(bW), lane, wave);    // + dq^ W^T
-    mm(dW, tr(b6), nat(b8), lane, wave);    // Z^T dq^ (negated below)
-    {
+    if (hasT) {
+        // U = W dT and V' = W dT^T (64 x D, for the backward through T = I - W^T A W) and
+        // U W^T = W dT W^T; the key walk left dT^T, so dT[c2, c] = (dT^T[c, c2])^T
+        const float *dtt = (const float *)(ws + ly.dtt) + (int64_t)J * D * D;
+        float *uu = (float *)(ws + ly.uu) + nat0, *vv = (float *)(ws + ly.vv) + nat0;
+        for (int c = 0; c < NCH; ++c) {
+            f32x8 aU = zero8(), aV = zero8();
+            for (int c2 = 0; c2 < NCH; ++c2) {
+                __syncthreads();
+                in2l(b6, w, D, 64 * c2, row0, L, tid);
+                g2l(b7, dtt + (int64_t)(64 * c) * D + 64 * c2, D, tid);   // dT^T block (c, c2)
+                g2l(b8, dtt + (int64_t)(64 * c2) * D + 64 * c, D, tid);   // dT^T block (c2, c)
+                __syncthreads();
+                mm(aU, nat(b6), tr(b7), lane, wave);  // W_c2 dT[c2, c]
+                mm(aV, nat(b6), nat(b8), lane, wave);  // W_c2 dT^T[c2, c]
+            }
+            acc2g(uu + 64 * c, D, aU, lane, wave);
+            acc2g(vv + 64 * c, D, aV, lane, wave);
+            __syncthreads();
+            store_lds(b7, aU, lane, wave, Id());
+            in2l(b6, w, D, 64 * c, row0, L, tid);
+            __syncthreads();
+            acc = zero8();
+            mm(acc, nat(b7), tr(b6), lane, wave);  // U_c W_c^T
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int r = arow(v, lane, wave), c = acol(v, lane, wave);
-            dQ[v] += b8[r * kP + c];
-            dZ[v] = -dZ[v];
-            dN[v] = -dN[v];
-            dW[v] = -dW[v];
+            for (int v = 0; v < 8; ++v) aA[v] -= acc[v];  // dA = -W dT W^T + ...
         }
     }
     __syncthreads();
-    if (hasK) g2l(b8, (const float *)(ws + ly.dko) + row0 * kD, tid);  // dk^ from the key-major walk
-    else zero_lds(b8, tid);
+    store_lds(b6, aY, lane, wave, [](int, int, float x) { return -x; });  // dY
+    store_lds(b7, aZ, lane, wave, [](int, int, float x) { return -x; });  // dZ
     __syncthreads();
-    {
 #pragma unroll
-        for (int v = 0; v < 8; ++v) dK[v] += b8[arow(v, lane, wave) * kP + acol(v, lane, wave)];
-    }
+    for (int v = 0; v < 8; ++v) aNn[v] = -aNn[v];
+    mm(aNn, nat(b6), tr(bA), lane, wave);   // dN = -E^T Z + dY A^T
+    mm(aA, tr(bN), nat(b6), lane, wave);    // dA += N^T dY
+    mm(aA, tr(b7), nat(bQW), lane, wave);   // dA += dZ^T QWm
     acc = zero8();
-    mm(acc, nat(b8), tr(bW), lane, wave);  // dY = -dk^ W^T
-    store_lds(b6, acc, lane, wave, [](int, int, float x) { return -x; });
-    acc = zero8();
-    mm(acc, tr(bN), nat(b8), lane, wave);  // R = N^T dk^ (into bQ; q is read again later)
+    mm(acc, nat(b7), nat(bA), lane, wave);  // dQWm = (dZ A) o [r <= i]
+    f32x8 aYv = zero8();
+    mm(aYv, nat(bN), nat(bA), lane, wave);  // Y = N A
     __syncthreads();
-    store_lds(bQ, acc, lane, wave, id);
-    __syncthreads();
-    mm(dN, nat(b6), tr(bA), lane, wave);   // += dY A^T
-    mm(dA, tr(bN), nat(b6), lane, wave);   // N^T dY
-    acc = zero8();
-    mm(acc, tr(bA), nat(bQ), lane, wave);  // A^T R = Y^T dk^
-#pragma unroll
-    for (int v = 0; v < 8; ++v) dW[v] -= acc[v];
-    __syncthreads();
-    store_lds(b6, dN, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });  // dKW = dN o [r > j]
-    in2l(bQ, q, row0, L, tid);
-    __syncthreads();
-    mm(dK, nat(b6), nat(bW), lane, wave);  // += dKW W
-    mm(dW, tr(b6), nat(bK), lane, wave);   // += dKW^T K
-    __syncthreads();
-    store_lds(b6, dZ, lane, wave, id);
-    __syncthreads();
-    acc = zero8();
-    mm(acc, nat(b6), nat(bA), lane, wave);  // dQWm = (dZ A) o [r <= i]
-    mm(dA, tr(b6), nat(bQW), lane, wave);   // += dZ^T QWm
-    store_lds(bN, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });
-    __syncthreads();
-    mm(dQ, nat(bN), nat(bW), lane, wave);   // += dQWm W
-    mm(dW, tr(bN), nat(bQ), lane, wave);    // += dQWm^T Q
-    __syncthreads();
-    if (hasT) {  // T = I - W^T A W
-        g2l(b6, (const float *)(ws + ly.dt) + (int64_t)J * kD * kD, tid);
-        acc = zero8();
-        mm(acc, nat(bA), nat(bW), lane, wave);  // A W
-        __syncthreads();
-        store_lds(bN, acc, lane, wave, id);
-        acc = zero8();
-        mm(acc, nat(bW), nat(b6), lane, wave);  // W dT
-        store_lds(bQW, acc, lane, wave, id);
-        __syncthreads();
-        acc = zero8();
-        mm(acc, nat(bQW), tr(bW), lane, wave);  // W dT W^T
-#pragma unroll
-        for (int v = 0; v < 8; ++v) dA[v] -= acc[v];
-        acc = zero8();
-        mm(acc, nat(bN), tr(b6), lane, wave);   // A W dT^T
-        mm(acc, tr(bA), nat(bQW), lane, wave);  // + A^T W dT
-#pragma unroll
-        for (int v = 0; v < 8; ++v) dW[v] -= acc[v];
-        __syncthreads();
-    }
+    store_lds(b8, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });  // dQWm
+    store_lds(b6, aNn, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });   // dKW = dN o [r > j]
+    store_lds(bN, aYv, lane, wave, Id());                                                    // Y (N is done with)
     // A = X diag(beta): dX = dA diag(beta), dbeta_c += sum_r X_rc dA_rc (dA kept on the upper triangle)
-    {
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int r = arow(v, lane, wave), c = acol(v, lane, wave);
-            dA[v] = c >= r ? dA[v] : 0.f;
-            b6[r * kP + c] = dA[v] * sB[c];
-            bQW[r * kP + c] = bX[r * kP + c] * dA[v];
-        }
+    for (int v = 0; v < 8; ++v) {
+        const int r = arow(v, lane, wave), c = acol(v, lane, wave);
+        aA[v] = c >= r ? aA[v] : 0.f;
+        b7[r * kP + c] = aA[v] * sB[c];
+        bQW[r * kP + c] = bX[r * kP + c] * aA[v];
     }
     __syncthreads();
     float dbeta = 0.f;
     if (tid < kC)
         for (int r = 0; r < kC; ++r) dbeta += bQW[r * kP + tid];
     acc = zero8();
-    mm(acc, tr(bX), nat(b6), lane, wave);  // X^T dX
+    mm(acc, tr(bX), nat(b7), lane, wave);  // X^T dX
     __syncthreads();
-    store_lds(bN, acc, lane, wave, id);
+    store_lds(bQW, acc, lane, wave, Id());
     __syncthreads();
-    f32x8 dTp = zero8(), G = zero8();
-    mm(dTp, nat(bN), tr(bX), lane, wave);  // (X^T dX) X^T; dT' is its negative
-    mm(G, nat(bW), tr(bW), lane, wave);
-    {
+    f32x8 dTp = zero8();
+    mm(dTp, nat(bQW), tr(bX), lane, wave);  // (X^T dX) X^T; dT' is its negative
+    __syncthreads();
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int r = arow(v, lane, wave), c = acol(v, lane, wave);
-            const float t = -dTp[v];
-            bQW[r * kP + c] = c > r ? t * G[v] : 0.f;    // dbeta_r += sum_c dT'_rc U_rc
-            b6[r * kP + c] = c > r ? sB[r] * t : 0.f;    // dG = diag(beta) dT' on the strict upper triangle
-        }
+    for (int v = 0; v < 8; ++v) {
+        const int r = arow(v, lane, wave), c = acol(v, lane, wave);
+        const float t = -dTp[v];
+        bQW[r * kP + c] = c > r ? t * aG[v] : 0.f;  // dbeta_r += sum_c dT'_rc G_rc
+        b7[r * kP + c] = c > r ? sB[r] * t : 0.f;   // dG = diag(beta) dT' on the strict upper triangle
     }
     __syncthreads();
     if (tid >= kC && tid < 2 * kC) {
@@ -886,20 +921,65 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
         for (int c = 0; c < kC; ++c) s += bQW[(tid - kC) * kP + c];
         sRed[tid - kC] = s;
     }
-    mm(dW, nat(b6), nat(bW), lane, wave);  // += (dG + dG^T) W
-    mm(dW, tr(b6), nat(bW), lane, wave);
     __syncthreads();
     if (tid < kC && row0 + tid < L) a.dbeta[hoff + row0 + tid] = dbeta + sRed[tid];
-    acc2out((T *)a.dq + hoff * kD, dQ, row0, L, lane, wave);
-    acc2out((T *)a.dk + hoff * kD, dK, row0, L, lane, wave);
-    acc2out((T *)a.dw + hoff * kD, dW, row0, L, lane, wave);
+    // ---- chunks of the head dimension.  LDS: E, Y (bN), Z, A, dKW (b6), dG (b7), dQWm (b8);
+    //      bX and bQW hold the chunk operands.
+    const float *uu = (const float *)(ws + ly.uu) + nat0, *vvp = (const float *)(ws + ly.vv) + nat0;
+    for (int c = 0; c < NCH; ++c) {
+        f32x8 dQ = zero8(), dK = zero8(), dW = zero8();
+        __syncthreads();
+        in2l(bX, k, D, 64 * c, row0, L, tid);
+        in2l(bQW, q, D, 64 * c, row0, L, tid);
+        __syncthreads();
+        mm(dQ, nat(bE), nat(bX), lane, wave);   // E K
+        mm(dK, tr(bE), nat(bQW), lane, wave);   // E^T Q
+        mm(dW, tr(b6), nat(bX), lane, wave);    // dKW^T K
+        mm(dW, tr(b8), nat(bQW), lane, wave);   // dQWm^T Q
+        __syncthreads();
+        in2l(bX, w, D, 64 * c, row0, L, tid);
+        __syncthreads();
+        mm(dQ, nat(b8), nat(bX), lane, wave);   // dQWm W
+        mm(dK, nat(b6), nat(bX), lane, wave);   // dKW W
+        mm(dW, nat(b7), nat(bX), lane, wave);   // (dG + dG^T) W
+        mm(dW, tr(b7), nat(bX), lane, wave);
+        __syncthreads();
+        if (hasQ) g2l(bX, dqo + 64 * c, D, tid);
+        else zero_lds(bX, tid);
+        if (hasK) g2l(bQW, dko + 64 * c, D, tid);
+        else zero_lds(bQW, tid);
+        __syncthreads();
+        acc = zero8();
+        mm(acc, tr(bZ), nat(bX), lane, wave);   // Z^T dq^
+        mm(acc, tr(bN), nat(bQW), lane, wave);  // + Y^T dk^ (= A^T N^T dk^)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const int r = arow(v, lane, wave), cc = acol(v, lane, wave);
+            dQ[v] += bX[r * kP + cc];
+            dK[v] += bQW[r * kP + cc];
+            dW[v] -= acc[v];
+        }
+        if (hasT) {
+            __syncthreads();
+            g2l(bX, uu + 64 * c, D, tid);
+            g2l(bQW, vvp + 64 * c, D, tid);
+            __syncthreads();
+            acc = zero8();
+            mm(acc, nat(bA), nat(bQW), lane, wave);  // A W dT^T
+            mm(acc, tr(bA), nat(bX), lane, wave);    // + A^T W dT
+#pragma unroll
+            for (int v = 0; v < 8; ++v) dW[v] -= acc[v];
+        }
+        acc2out((T *)a.dq + hoff * D + 64 * c, D, dQ, row0, L, lane, wave);
+        acc2out((T *)a.dk + hoff * D + 64 * c, D, dK, row0, L, lane, wave);
+        acc2out((T *)a.dw + hoff * D + 64 * c, D, dW, row0, L, lane, wave);
+    }
     {
-        const float *dvd = (const float *)(ws + ly.dvd) + row0 * kD, *dvo = (const float *)(ws + ly.dvo) + row0 * kD;
-        T *dv = (T *)a.dv + hoff * kD;
-        for (int e = tid; e < kC * kD; e += kT) {
-            const int r = e >> 6;
-            if (row0 + r < L)
-                dv[(int64_t)(row0 + r) * kD + (e & 63)] = Elem<T>::from_float(dvd[e] + (hasK ? dvo[e] : 0.f));
+        const float *dvd = (const float *)(ws + ly.dvd) + nat0, *dvo = (const float *)(ws + ly.dvo) + nat0;
+        T *dv = (T *)a.dv + hoff * D;
+        for (int e = tid; e < kC * D; e += kT) {
+            const int r = e / D;
+            if (row0 + r < L) dv[(int64_t)row0 * D + e] = Elem<T>::from_float(dvd[e] + (hasK ? dvo[e] : 0.f));
         }
     }
     if (tid < kC) {
@@ -910,7 +990,7 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
     }
 }
 
-// dlogf_t = sum_{t' >= t} dc_t' for one head: 256 threads, contiguous chunks, fixed order.
+// dlogf_t = sum_{t' >= t} dc_t' for one head: 512 threads, contiguous chunks, fixed order.
 __global__ __launch_bounds__(kT) void bwd_gate_kernel(BwdArgs a) {
     __shared__ float part[kT];
     const int tid = threadIdx.x, gl = blockIdx.x, L = a.L;
@@ -937,35 +1017,34 @@ __global__ __launch_bounds__(kT) void bwd_gate_kernel(BwdArgs a) {
     }
 }
 
-}  // namespace
-
-hipError_t launch_bwd(const BwdArgs &a0, bool bf16, hipStream_t st) {
+template <typename T, int D>
+hipError_t launch_bwd_t(const BwdArgs &a0, hipStream_t st) {
     BwdArgs a = a0;
     const int G = a.B * a.H;
     for (int g0 = 0; g0 < G; g0 += a.hc_max) {
         a.g0 = g0;
         a.hc = min(a.hc_max, G - g0);
-        const dim3 blk(kT);
-        if (bf16) hipLaunchKernelGGL(bwd_prep_kernel<uint16_t>, dim3(a.nb, a.hc), blk, 0, st, a);
-        else hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3(a.nb, a.hc), blk, 0, st, a);
+        hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(a.nb, a.hc), dim3(kT), 0, st, a);
         if (a.nb > 1) {
-            if (bf16) {
-                hipLaunchKernelGGL(bwd_down_kernel<uint16_t>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
-                hipLaunchKernelGGL(bwd_query_kernel<uint16_t>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
-                hipLaunchKernelGGL(bwd_key_kernel_h, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
-            } else {
-                hipLaunchKernelGGL(bwd_down_kernel<float>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
-                hipLaunchKernelGGL(bwd_query_kernel<float>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
-                hipLaunchKernelGGL(bwd_key_kernel<float>, dim3((a.nb - 1) * a.hc), blk, 0, st, a);
-            }
+            const dim3 walks((unsigned)((a.nb - 1) * a.hc));
+            hipLaunchKernelGGL((bwd_down_kernel<T, D>), walks, dim3(128), 0, st, a);
+            hipLaunchKernelGGL((bwd_up_kernel<T, D>), walks, dim3(128), 0, st, a);
+            hipLaunchKernelGGL((bwd_key_kernel<T, D>), walks, dim3(64 * KeyCfg<D>::NW), 0, st, a);
         }
-        if (bf16) hipLaunchKernelGGL(bwd_block_kernel<uint16_t>, dim3(a.nb, a.hc), blk, 0, st, a);
-        else hipLaunchKernelGGL(bwd_block_kernel<float>, dim3(a.nb, a.hc), blk, 0, st, a);
-        if (a.dlogf) hipLaunchKernelGGL(bwd_gate_kernel, dim3(a.hc), blk, 0, st, a);
+        hipLaunchKernelGGL((bwd_block_kernel<T, D>), dim3(a.nb, a.hc), dim3(kT), 0, st, a);
+        if (a.dlogf) hipLaunchKernelGGL(bwd_gate_kernel, dim3(a.hc), dim3(kT), 0, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs &a, bool bf16, hipStream_t st) {
+    if (a.d == 64) return bf16 ? launch_bwd_t<uint16_t, 64>(a, st) : launch_bwd_t<float, 64>(a, st);
+    if (a.d == 128) return bf16 ? launch_bwd_t<uint16_t, 128>(a, st) : launch_bwd_t<float, 128>(a, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace path

@@ -25,28 +25,32 @@ void decode_plan(int64_t BH, int64_t rows, int *nsplit, int64_t *chunk) {
     if (*nsplit < 1) *nsplit = 1;
 }
 
-BwdLayout bwd_layout(int L, int es) {
+BwdLayout bwd_layout(int L, int D, int es) {
     BwdLayout ly{};
-    const int64_t nb = (L + 64 - 1) / 64, Lp = nb * 64, np = nb * (nb - 1) / 2;
+    ly.D = D;
+    ly.es = es;
+    const int64_t nb = (L + 63) / 64, Lp = nb * 64, np = nb * (nb - 1) / 2;
     int64_t off = 0;
     auto take = [&](int64_t bytes) {
         const int64_t o = off;
         off += (bytes + 255) / 256 * 256;
         return o;
     };
-    const int64_t tile = Lp * 64 * 4, rows = Lp * 4;
-    ly.qh = take(tile); ly.kh = take(tile); ly.vf = take(Lp * 64 * es); ly.dof = take(Lp * 64 * es);
-    ly.tt = take(nb * 64 * 64 * 4);
-    ly.ttt = take(nb * 64 * 64 * 4);
-    ly.xx = take(nb * 64 * 64 * 4); ly.aa = take(nb * 64 * 64 * 4); ly.qwm = take(nb * 64 * 64 * 4);
-    ly.nn = take(nb * 64 * 64 * 4); ly.zz = take(nb * 64 * 64 * 4);
-    ly.ee = take(nb * 64 * 64 * 4); ly.dvd = take(tile); ly.dqo = take(tile); ly.dko = take(tile); ly.dvo = take(tile);
-    ly.dt = take(nb * 64 * 64 * 4);
+    const int64_t tok = nb * 64 * 64 * 4;          // a 64 x 64 fp32 matrix per block
+    const int64_t fr = nb * 64 * D * es;           // a 64 x D fragment set per block
+    const int64_t frd = nb * (int64_t)D * D * es;  // a D x D fragment set per block
+    const int64_t nat = Lp * D * 4, rows = Lp * 4;
+    ly.xx = take(tok); ly.aa = take(tok); ly.qwm = take(tok); ly.nn = take(tok); ly.zz = take(tok); ly.ee = take(tok);
+    ly.kh1 = take(fr); ly.kh2 = take(fr); ly.v1 = take(fr); ly.do1 = take(fr); ly.do2 = take(fr);
+    ly.nt = take(frd); ly.ntt = take(frd);
+    ly.qh = take(nat); ly.dvd = take(nat); ly.dqo = take(nat); ly.dko = take(nat); ly.dvo = take(nat);
+    ly.uu = take(nat); ly.vv = take(nat);
+    ly.dtt = take(nb * (int64_t)D * D * 4);
     ly.l2 = take(rows); ly.dd = take(rows); ly.clq = take(rows); ly.ckk = take(rows); ly.rsd = take(rows);
     ly.csd = take(rows); ly.rso = take(rows); ly.cso = take(rows); ly.dc = take(rows);
     ly.tot = take(nb * 4); ly.mid = take(np * 4);
-    ly.qs = take(np * 64 * 64 * es); ly.gs = take(np * 64 * 64 * es);
-    ly.ps = take(np * 64 * 64 * es); ly.ds = take(np * 64 * 64 * es); ly.csp = take(np * 64 * 4);
+    const int64_t pr = np * 64 * D * es;  // a 64 x D fragment set per pair
+    ly.qs1 = take(pr); ly.qs2 = take(pr); ly.gs2 = take(pr);
     ly.head = off;
     return ly;
 }

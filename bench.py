@@ -23,8 +23,8 @@ Work units (fixed, declared):
            adjoint's and the query's transition products, the transition
            gradient) at 2 * 64^2 d each; the key-major walk's recomputation
            of the logits and dO V^T and the in-block work are not counted.
-           The backward computes in fp32, so it is priced against the fp32
-           matrix-core peak.
+           Its walks run on bf16 matrix cores for bf16 inputs, so it is
+           priced against the bf16 matrix-core peak.
 """
 from __future__ import annotations
 
@@ -364,7 +364,7 @@ def bench_cache(steps, f):
 
 
 def bench_backward(steps, warmup, name=FWD_WORKLOAD):
-    """Backward pass (path_attn_bwd) on the forward workload: gradients of q, k, v, w, beta
+    """Backward pass (path_attn_bwd) on a forward workload: gradients of q, k, v, w, beta
     for a random upstream gradient, fed the forward's own out and lse."""
     import torch
 
@@ -402,9 +402,9 @@ def bench_backward(steps, warmup, name=FWD_WORKLOAD):
     return {"workload": name + " backward", "ms_per_step": round(ms, 3), "flop_per_step": flops,
             "traffic_note": "HBM bytes of one whole backward pass (all kernels, all passes over the workspace)",
             "TFLOP_per_s": round(tf, 2), "steps": steps,
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_FP32_TFLOPS, 4),
-                         "traffic": read_traffic("path_bwd", BWD_TRAFFIC_FILE)},
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": read_traffic("path_bwd", BWD_TRAFFIC_FILE) if name == FWD_WORKLOAD else None},
             "heads_per_workspace_pass": int(heads_per_pass),
             "tokens_per_s": round(B * L / (ms * 1e-3))}
 
@@ -581,7 +581,9 @@ def main():
         counter_run_backward()
         return
     if args.backward_only:
-        print(json.dumps({"backward": bench_backward(max(1, args.backward_steps), 1)}), flush=True)
+        print(json.dumps({"backward": bench_backward(max(1, args.backward_steps), 1),
+                          "backward_d128": bench_backward(max(1, args.backward_steps), 1, "sweep_L4096_d128_bf16")}),
+              flush=True)
         return
     log("forward: %s, %d warm-up + %d timed steps" % (FWD_WORKLOAD, args.warmup, args.steps))
     f = bench_forward(args.steps, args.warmup)
@@ -604,11 +606,13 @@ def main():
             (fused["workload"], fused["ms_per_step"], fused["plain_forward_ms_per_step"]))
         log("fox workload, skipping negligible blocks: %.3f ms/step (full walk %.3f ms)" %
             (fox_skip["ms_per_step"], fox_skip["full_walk_ms_per_step"]))
-    bwd = None
+    bwd = bwd128 = None
     if args.backward_steps > 0:
         bwd = bench_backward(args.backward_steps, 1)
-        log("backward: %.2f ms/step, %.1f TFLOP/s (%.1f%% of the fp32 matrix peak)" %
+        log("backward: %.2f ms/step, %.1f TFLOP/s (%.1f%% of the bf16 matrix peak)" %
             (bwd["ms_per_step"], bwd["TFLOP_per_s"], 100 * bwd["roofline"]["frac"]))
+        bwd128 = bench_backward(args.backward_steps, 1, "sweep_L4096_d128_bf16")
+        log("backward d128: %.2f ms/step, %.1f TFLOP/s" % (bwd128["ms_per_step"], bwd128["TFLOP_per_s"]))
     cpu = dec_cpu = None
     if args.cpu_seconds > 0:
         log("cpu baseline: oracle, ~%.0f s" % args.cpu_seconds)
@@ -671,6 +675,7 @@ def main():
         "fox_skip_negligible": fox_skip,
         "fused_producer": fused,
         "backward": bwd,
+        "backward_d128": bwd128,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -60,7 +60,7 @@ typedef struct ihipStream_t *path_stream_t;
 typedef enum {
     PATH_OK = 0,
     PATH_EINVAL = 1,        /* NULL pointer, bad size, misaligned, workspace too small, n > ncap */
-    PATH_EUNSUPPORTED = 2,  /* valid but not implemented (head dimension other than 64, 128; 128 in the backward) */
+    PATH_EUNSUPPORTED = 2,  /* valid but not implemented (head dimension other than 64, 128) */
     PATH_EHIP = 3,          /* the HIP runtime rejected a launch */
     PATH_ESCRATCH = 4       /* path_decode_step_noalloc: the problem needs more than its fixed scratch */
 } path_status_t;
@@ -292,9 +292,10 @@ path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace
  * one).  path_attn_bwd_workspace_size(1, 1, L, d, dtype) is one head's share;
  * path_attn_bwd accepts any workspace of at least one share and processes
  * floor(workspace_bytes / share) heads at a time (results do not depend on it).
- * One share is about 64 KiB (fp32) or 32 KiB (bf16) per pair of 64-token
- * blocks (nb (nb - 1) / 2 pairs, nb = ceil(L / 64)) plus about 270 KiB per
- * block: 144 MiB (fp32) or 80 MiB (bf16) at L = 4096.
+ * One share is 3 * 64 * d element-type values per pair of 64-token blocks
+ * (nb (nb - 1) / 2 pairs, nb = ceil(L / 64)) plus 4.4 KiB (d = 64, bf16) to
+ * 10.5 KiB (d = 128, fp32) per token: 65 MiB per head at L = 4096, d = 64,
+ * bf16; 128 MiB at d = 128.
  */
 size_t path_attn_bwd_workspace_size(int B, int H, int L, int d, path_dtype_t dtype);
 
@@ -307,7 +308,9 @@ size_t path_attn_bwd_workspace_size(int B, int H, int L, int d, path_dtype_t dty
  * (path_attn_fwd above), evaluated on the same 64-token blocks: a walk over
  * key blocks per query block for the query side, one per key block for the
  * key side and the block transitions, and a per-block pass through the UT
- * transform.  All arithmetic is fp32 (fp32 matrix cores) for either dtype.
+ * transform.  The walks run on the matrix cores in `dtype` (bf16 operands
+ * with fp32 accumulation for bf16, fp32 for fp32); the per-block passes in
+ * fp32.
  *
  * q, k, v, w, out, dout : [B, H, L, d] element type `dtype` (read only); out is the
  *                         forward's output for these inputs
@@ -320,7 +323,7 @@ size_t path_attn_bwd_workspace_size(int B, int H, int L, int d, path_dtype_t dty
  * scale                 : as in path_attn_fwd (<= 0 selects 1/sqrt(d))
  * workspace             : device scratch, see path_attn_bwd_workspace_size
  *
- * d must be 64 (128 returns PATH_EUNSUPPORTED).  Outputs must not overlap each
+ * d must be 64 or 128.  Outputs must not overlap each
  * other, the inputs or the workspace.  Returns PATH_OK, PATH_EINVAL (NULL,
  * sizes, misaligned, workspace below one head's share, overlaps),
  * PATH_EUNSUPPORTED or PATH_EHIP.

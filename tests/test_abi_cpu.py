@@ -263,7 +263,8 @@ def test_bwd_workspace_sizes():
     one = lib.path_attn_bwd_workspace_size(1, 1, 200, 64, BF)
     assert one > 0
     assert lib.path_attn_bwd_workspace_size(2, 3, 200, 64, BF) == 6 * one   # all heads at once
-    assert lib.path_attn_bwd_workspace_size(1, 1, 200, 128, BF) == 0        # d = 128 not in the backward
+    assert lib.path_attn_bwd_workspace_size(1, 1, 200, 128, BF) > one      # head dimension 128
+    assert lib.path_attn_bwd_workspace_size(1, 1, 200, 96, BF) == 0
     assert lib.path_attn_bwd_workspace_size(1, 1, 0, 64, BF) == 0
     assert lib.path_attn_bwd_workspace_size(1, 1, 64, 64, 9) == 0
     share = lib.path_attn_bwd_workspace_size(1, 1, 4096, 64, BF)
@@ -291,7 +292,6 @@ def bwd_call(**over):
     (dict(dbeta=None), pa.PATH_EINVAL),
     (dict(logf=P(13)), pa.PATH_EINVAL),                        # gate without its gradient
     (dict(dlogf=P(13)), pa.PATH_EINVAL),                       # gradient without the gate
-    (dict(d=128), pa.PATH_EUNSUPPORTED),
     (dict(d=96), pa.PATH_EUNSUPPORTED),
     (dict(L=0), pa.PATH_EINVAL),
     (dict(dtype=7), pa.PATH_EINVAL),

@@ -22,14 +22,14 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 NAMES = ("dq", "dk", "dv", "dw", "dbeta", "dlogf")
 
 
-def run_case(B, H, L, dtype, seed, fox, beta=None, with_dlse=True, scale=None, workspace=None):
-    x = pathgen.fwd_inputs(B, H, L, 64, dtype, seed=seed, fox=fox, clip=1.98 if dtype == "bf16" else None,
+def run_case(B, H, L, dtype, seed, fox, beta=None, with_dlse=True, scale=None, workspace=None, d=64):
+    x = pathgen.fwd_inputs(B, H, L, d, dtype, seed=seed, fox=fox, clip=1.98 if dtype == "bf16" else None,
                            device="cuda")
     if beta is not None:
         x["beta"] = torch.full((B, H, L), float(beta), device="cuda")
     g = torch.Generator(device="cuda")
     g.manual_seed(seed + 500)
-    dout = torch.randn((B, H, L, 64), generator=g, device="cuda").to(x["q"].dtype)
+    dout = torch.randn((B, H, L, d), generator=g, device="cuda").to(x["q"].dtype)
     dlse = torch.randn((B, H, L), generator=g, device="cuda") if with_dlse else None
     out, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], scale=scale, return_lse=True)
     grads = pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out, lse, dout, dlse, scale=scale,
@@ -116,11 +116,54 @@ def test_bwd_per_head_workload_shape():
 
 
 @gpu
-def test_bwd_rejects_d128():
-    x = pathgen.fwd_inputs(1, 1, 64, 128, "f32", seed=0, device="cuda")
-    o, l = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], return_lse=True)
-    with pytest.raises(pa.PathError):
-        pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], None, o, l, torch.ones_like(o))
+@pytest.mark.parametrize("fox", [False, True])
+@pytest.mark.parametrize("L", [1, 64, 65, 200, 333])
+def test_bwd_fp32_d128(L, fox):
+    say("case bwd fp32 d128 L%d fox=%s" % (L, fox))
+    x, dout, dlse, _, _, grads = run_case(1, 2, L, "f32", seed=400 + L, fox=fox, d=128)
+    compare(x, dout, dlse, grads, "f32", what="d128 L%d" % L)
+
+
+@gpu
+@pytest.mark.parametrize("fox", [False, True])
+@pytest.mark.parametrize("L", [64, 300, 700])
+def test_bwd_bf16_d128(L, fox):
+    say("case bwd bf16 d128 L%d fox=%s" % (L, fox))
+    x, dout, dlse, _, _, grads = run_case(2, 2, L, "bf16", seed=500 + L, fox=fox, d=128)
+    compare(x, dout, dlse, grads, "bf16", what="d128 L%d" % L)
+
+
+@gpu
+@pytest.mark.parametrize("beta", [0.0, 1.0, 2.0])
+def test_bwd_beta_regimes_d128(beta):
+    """beta = 0, 1 and 2 at head dimension 128, fp32, with the gate."""
+    say("case bwd d128 beta=%g" % beta)
+    x, dout, dlse, _, _, grads = run_case(1, 1, 150, "f32", seed=78, fox=True, beta=beta, d=128)
+    compare(x, dout, dlse, grads, "f32", what="d128 beta=%g" % beta)
+    if beta == 0.0:
+        assert float(grads[3].abs().max()) == 0.0, "dw must vanish at beta = 0"
+
+
+@gpu
+def test_bwd_per_head_workload_shape_d128():
+    """One head at the per-head shape of the B32 H32 L4096 d128 bf16 workload, every gradient element."""
+    say("case bwd bf16 d128 L4096 one head")
+    x, dout, dlse, _, _, grads = run_case(1, 1, 4096, "bf16", seed=4, fox=False, d=128)
+    compare(x, dout, dlse, grads, "bf16", what="d128 L4096")
+
+
+@gpu
+def test_bwd_chunked_workspace_d128():
+    """d = 128: a workspace of one head's share gives the same bits as all heads at once."""
+    say("case bwd chunked workspace d128")
+    B, H, L = 1, 3, 130
+    share = pa.bwd_workspace_size(1, 1, L, 128, torch.bfloat16)
+    ws1 = torch.empty(share, device="cuda", dtype=torch.uint8)
+    x, dout, dlse, out, lse, g_all = run_case(B, H, L, "bf16", seed=19, fox=True, d=128)
+    g_one = pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out, lse, dout, dlse, workspace=ws1)
+    torch.cuda.synchronize()
+    for n, a, b in zip(NAMES, g_all, g_one):
+        assert torch.equal(a, b), "chunked " + n
 
 
 @gpu

@@ -146,24 +146,25 @@ def test_random_cache(seed):
 
 
 @gpu
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(14))
 def test_random_backward(seed):
-    """path_attn_bwd on random shapes and regimes (head dimension 64): every gradient element against the
-    oracle's reverse mode, bars as in test_parity_bwd (relative to the tensor's largest magnitude)."""
+    """path_attn_bwd on random shapes and regimes (head dimension 64 or 128): every gradient element against
+    the oracle's reverse mode, bars as in test_parity_bwd (relative to the tensor's largest magnitude)."""
     r = np.random.default_rng(5000 + seed)
     B, H, L = int(r.integers(1, 3)), int(r.integers(1, 3)), int(r.integers(1, 600))
     dt, fox, with_dlse = str(r.choice(["f32", "bf16"])), bool(r.integers(0, 2)), bool(r.integers(0, 2))
     scale = float(r.choice([0.0, r.uniform(0.05, 0.2)]))
     breg = str(r.choice(["sigmoid", "uniform", "zero"]))
-    say("case random bwd %d: B%d H%d L%d %s fox=%s dlse=%s scale=%g beta=%s" % (seed, B, H, L, dt, fox, with_dlse,
-                                                                              scale, breg))
-    x = pathgen.fwd_inputs(B, H, L, 64, dt, seed=seed, fox=fox, clip=1.98 if dt == "bf16" else None, device="cuda")
+    d = int(r.choice([64, 128]))
+    say("case random bwd %d: B%d H%d L%d d%d %s fox=%s dlse=%s scale=%g beta=%s" % (seed, B, H, L, d, dt, fox,
+                                                                                  with_dlse, scale, breg))
+    x = pathgen.fwd_inputs(B, H, L, d, dt, seed=seed, fox=fox, clip=1.98 if dt == "bf16" else None, device="cuda")
     g = torch.Generator(device="cuda")
     g.manual_seed(seed + 900)
     if breg != "sigmoid":
         x["beta"] = (torch.rand((B, H, L), generator=g, device="cuda") * (1.98 if dt == "bf16" else 2.0)
                      if breg == "uniform" else torch.zeros((B, H, L), device="cuda"))
-    dout = torch.randn((B, H, L, 64), generator=g, device="cuda").to(x["q"].dtype)
+    dout = torch.randn((B, H, L, d), generator=g, device="cuda").to(x["q"].dtype)
     dlse = torch.randn((B, H, L), generator=g, device="cuda") if with_dlse else None
     sc = scale if scale > 0 else None
     out, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], scale=sc, return_lse=True)
@@ -171,7 +172,7 @@ def test_random_backward(seed):
     torch.cuda.synchronize()
     ref = oracle.bwd(*(x[n].cpu() for n in ("q", "k", "v", "w", "beta")),
                      x["logf"].cpu() if fox else None, dout.cpu(), dlse.cpu() if with_dlse else None, scale=sc)
-    tol = TOL[dt] * (max(1.0, scale * 8.0) if dt == "bf16" else 1.0)
+    tol = TOL[dt] * (max(1.0, scale * math.sqrt(d)) if dt == "bf16" else 1.0)
     worst = []
     for n, t in zip(("dq", "dk", "dv", "dw", "dbeta", "dlogf"), grads):
         if t is None:
