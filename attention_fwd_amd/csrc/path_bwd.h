@@ -17,18 +17,21 @@ struct BwdLayout {
     int D, es;
     // per block, fp32 64 x 64: X, A, Q W^T o [r <= i], N = K W^T o [r > j], Z, and scale * dS of the diagonal block
     int64_t xx, aa, qwm, nn, zz, ee;
-    // per block, fragments (S): k^ (rows keys, k over d), k^^T (rows d, k over keys), V (rows keys),
-    // dO (rows queries), dO^T (rows d), and T - I, (T - I)^T of the block transition T (rows d, k over d)
-    int64_t kh1, kh2, v1, do1, do2, nt, ntt;
+    // per block, fragments (S): the up walk's record -- k^ (rows keys, k over d), V (rows keys), k^^T
+    // (rows d, k over keys) and (T - I)^T of the block transition T (rows d, k over d), contiguous, of
+    // rec_elems elements (parts at 0, 64 D, 128 D, 192 D) -- and dO (rows queries), dO^T (rows d),
+    // T - I (rows d, k over d)
+    int64_t urec, rec_elems, do1, do2, nt;
     // fp32 [Lp, D]: q^; the diagonal value gradient; walk outputs dq^, dk^, dv; W dT and W dT^T of the
     // block backward
     int64_t qh, dvd, dqo, dko, dvo, uu, vv;
     int64_t dtt;  // per block, fp32 [D, D]: dT^T (the transpose of the transition gradient)
-    // fp32 [Lp]: lse (log2 units), do.o - dlse, gate prefix terms of rows / keys, row / column sums of dS
-    // (diagonal, off-diagonal), gate adjoint
-    int64_t l2, dd, clq, ckk, rsd, csd, rso, cso, dc;
-    int64_t tot;  // [nb]: gate total of each block
-    int64_t mid;  // [np]: gate sum over the blocks strictly between I and J
+    // fp32 [Lp]: do.o - dlse; the query and key terms of the exponent of P in log2 units (a query's
+    // block-local gate prefix less its lse, a key's gate sum to the end of its block); row / column
+    // sums of dS (diagonal, off-diagonal); gate adjoint
+    int64_t dd, cql, ckl, rsd, csd, rso, cso, dc;
+    int64_t tot;  // [nb]: gate total of each block (log2 units)
+    int64_t mid;  // [np]: gate sum over the blocks strictly between I and J (log2 units)
     // per pair, fragments (S): q~ (rows queries, k over d), q~^T (rows d, k over queries), G^(J-1)^T (rows d)
     int64_t qs1, qs2, gs2;
     int64_t head;  // bytes per head

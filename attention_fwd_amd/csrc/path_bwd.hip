@@ -383,17 +383,17 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
             cs[c] = s;
         } else if (tid < 3 * kC) {
             const int r = tid - 2 * kC;
-            ((float *)(ws + ly.l2))[row0 + r] = sL2[r];
             ((float *)(ws + ly.dd))[row0 + r] = sDD[r];
-            ((float *)(ws + ly.clq))[row0 + r] = sCl[r];
-            ((float *)(ws + ly.ckk))[row0 + r] = sCl[kC - 1] - sCl[r];
-            if (r == 0) ((float *)(ws + ly.tot))[J] = sCl[kC - 1];
+            ((float *)(ws + ly.cql))[row0 + r] = sCl[r] * kLog2e - sL2[r];
+            ((float *)(ws + ly.ckl))[row0 + r] = (sCl[kC - 1] - sCl[r]) * kLog2e;
+            if (r == 0) ((float *)(ws + ly.tot))[J] = sCl[kC - 1] * kLog2e;
         }
     }
     // chunks of the head dimension: q^, k^ (fragments), A W (kept for T), V and dO fragments,
     // the diagonal value gradient
     const int64_t fo = (int64_t)J * kC * D;  // this block's 64 x D fragment set
-    S *KH1 = (S *)(ws + ly.kh1) + fo, *KH2 = (S *)(ws + ly.kh2) + fo, *V1 = (S *)(ws + ly.v1) + fo;
+    S *REC = (S *)(ws + ly.urec) + J * ly.rec_elems;
+    S *KH1 = REC, *V1 = REC + kC * D, *KH2 = REC + 2 * kC * D;
     S *DO1 = (S *)(ws + ly.do1) + fo, *DO2 = (S *)(ws + ly.do2) + fo;
     float *bAW[2] = {bN, bQW};  // A W of chunk 0 / 1 (N and dS are done with)
     for (int c = 0; c < NCH; ++c) {
@@ -431,8 +431,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
         acc2g((float *)(ws + ly.dvd) + (int64_t)row0 * D + 64 * c, D, acc, lane, wave);
     }
     // T - I = -W^T (A W) and its transpose, block (c1, c2) = rows of chunk c1, columns of chunk c2
-    const int64_t fd = (int64_t)J * D * D;
-    S *NT = (S *)(ws + ly.nt) + fd, *NTT = (S *)(ws + ly.ntt) + fd;
+    S *NT = (S *)(ws + ly.nt) + (int64_t)J * D * D, *NTT = REC + 3 * kC * D;
     for (int c1 = 0; c1 < NCH; ++c1) {
         __syncthreads();
         in2l(bW, w, D, 64 * c1, row0, L, tid);
@@ -550,14 +549,13 @@ __global__ __launch_bounds__(128) void bwd_up_kernel(BwdArgs a) {
     const int gl = blockIdx.x % hc, I = nb - 1 - blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
-    const S *KH1 = (const S *)(ws + ly.kh1), *KH2 = (const S *)(ws + ly.kh2), *V1 = (const S *)(ws + ly.v1);
-    const S *NTT = (const S *)(ws + ly.ntt), *QS1 = (const S *)(ws + ly.qs1);
+    const S *RECS = (const S *)(ws + ly.urec), *QS1 = (const S *)(ws + ly.qs1);
+    const int64_t RE = ly.rec_elems;
     S *GS2 = (S *)(ws + ly.gs2);
-    const float *MID = (const float *)(ws + ly.mid), *CKK = (const float *)(ws + ly.ckk);
-    const float scale = a.scale;
+    const float *MID = (const float *)(ws + ly.mid), *CKK = (const float *)(ws + ly.ckl);
+    const float scale = a.scale, c2 = scale * kLog2e;
     const int row0 = I * kC, qi = row0 + 32 * w + l32;  // this lane's query (column of the accumulators)
-    const float l2 = ((const float *)(ws + ly.l2))[qi], dd = ((const float *)(ws + ly.dd))[qi];
-    const float cq = ((const float *)(ws + ly.clq))[qi];
+    const float dd = ((const float *)(ws + ly.dd))[qi], cq = ((const float *)(ws + ly.cql))[qi];
 
     Frag dof[KCD];  // dO with k over d, lane <-> query: the B operand of dP^T
 #pragma unroll
@@ -567,8 +565,93 @@ __global__ __launch_bounds__(128) void bwd_up_kernel(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < RTD; ++dt) gt[dt] = f32x16{};
     float rsum = 0.f;
+    if constexpr (D == 64) {
+    // A step loads k^ and V of block J with the stored q~ at its top (q~ one step ahead),
+    // and the operands of the adjoint update while the logits are computed.
+    Frag qf[KCD];
+#pragma unroll
+    for (int kc = 0; kc < KCD; ++kc) qf[kc] = ldfrag<S>(QS1 + pair_index(I, 0) * kC * D, w, kc, KCD, lane);
     for (int J = 0; J < I; ++J) {
-        const int64_t p = pair_index(I, J), fo = (int64_t)J * kC * D;
+        const int64_t p = pair_index(I, J);
+        const S *rec = RECS + J * RE;  // k^, V, k^^T, (T - I)^T of block J
+        Frag kf[2][KCD], vf[2][KCD];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int kc = 0; kc < KCD; ++kc) {
+                kf[kt][kc] = ldfrag<S>(rec, kt, kc, KCD, lane);
+                vf[kt][kc] = ldfrag<S>(rec + kC * D, kt, kc, KCD, lane);
+            }
+        const float mid = MID[p];
+        f32x4 ck[2][4];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+                ck[kt][g4] = *reinterpret_cast<const f32x4 *>(CKK + J * kC + 32 * kt + 8 * g4 + 4 * h);
+        Frag qn[KCD];
+        if (J + 1 < I) {
+#pragma unroll
+            for (int kc = 0; kc < KCD; ++kc) qn[kc] = ldfrag<S>(QS1 + (p + 1) * kC * D, w, kc, KCD, lane);
+        }
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            s[kt] = f32x16{};
+            dp[kt] = f32x16{};
+#pragma unroll
+            for (int kc = 0; kc < KCD; ++kc) {
+                Elem<S>::mma(s[kt], kf[kt][kc], qf[kc]);
+                Elem<S>::mma(dp[kt], vf[kt][kc], dof[kc]);
+            }
+        }
+        const S *ntt = rec + 3 * kC * D;
+        Frag tf[RTD][KCD], k2[RTD][4];
+#pragma unroll
+        for (int dt = 0; dt < RTD; ++dt) {
+#pragma unroll
+            for (int kc = 0; kc < KCD; ++kc) tf[dt][kc] = J >= 1 ? ldfrag<S>(ntt, dt, kc, KCD, lane) : Frag{};
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) k2[dt][kc] = ldfrag<S>(rec + 2 * kC * D, dt, kc, 4, lane);
+        }
+        // P^T and scale dS^T (rows: keys 32 kt + acc_row(r, h); column: this lane's query)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g4 + e;
+                    const float P = fast_exp2(c2 * s[kt][r] + cq + ck[kt][g4][e] + mid);
+                    const float ds = P * (dp[kt][r] - dd);
+                    rsum += ds;
+                    s[kt][r] = scale * ds;
+                }
+        Frag gf[KCD], sf[4];
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) gf[kc] = acc_frag<S>(gt[kc >> 1], kc & 1);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) sf[kc] = acc_frag<S>(s[kc >> 1], kc & 1);
+#pragma unroll
+        for (int dt = 0; dt < RTD; ++dt) {
+            if (J >= 1) {
+#pragma unroll
+                for (int kc = 0; kc < KCD; ++kc) Elem<S>::mma(gt[dt], tf[dt][kc], gf[kc]);
+            }
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) Elem<S>::mma(gt[dt], k2[dt][kc], sf[kc]);
+        }
+        if (J + 1 < I) {
+            store_transposed<S, D>(GS2 + pair_index(I, J + 1) * kC * D, gt, sx[w], w, lane);
+#pragma unroll
+            for (int kc = 0; kc < KCD; ++kc) qf[kc] = qn[kc];
+        }
+    }
+    } else {
+    // (d = 128: a step's operands do not fit the registers at once; each is loaded where it is used)
+    for (int J = 0; J < I; ++J) {
+        const int64_t p = pair_index(I, J);
+        const S *rec = RECS + J * RE;  // k^, V, k^^T, (T - I)^T of block J
         const float mid = MID[p];
         Frag qf[KCD];
 #pragma unroll
@@ -580,11 +663,10 @@ __global__ __launch_bounds__(128) void bwd_up_kernel(BwdArgs a) {
             dp[kt] = f32x16{};
 #pragma unroll
             for (int kc = 0; kc < KCD; ++kc) {
-                Elem<S>::mma(s[kt], ldfrag<S>(KH1 + fo, kt, kc, KCD, lane), qf[kc]);
-                Elem<S>::mma(dp[kt], ldfrag<S>(V1 + fo, kt, kc, KCD, lane), dof[kc]);
+                Elem<S>::mma(s[kt], ldfrag<S>(rec, kt, kc, KCD, lane), qf[kc]);
+                Elem<S>::mma(dp[kt], ldfrag<S>(rec + kC * D, kt, kc, KCD, lane), dof[kc]);
             }
         }
-        // P^T and scale dS^T (rows: keys 32 kt + acc_row(r, h); column: this lane's query)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -593,7 +675,7 @@ __global__ __launch_bounds__(128) void bwd_up_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g4 + e;
-                    const float P = fast_exp2((scale * s[kt][r] + cq + ck[e] + mid) * kLog2e - l2);
+                    const float P = fast_exp2(c2 * s[kt][r] + cq + ck[e] + mid);
                     const float ds = P * (dp[kt][r] - dd);
                     rsum += ds;
                     s[kt][r] = scale * ds;
@@ -604,7 +686,7 @@ __global__ __launch_bounds__(128) void bwd_up_kernel(BwdArgs a) {
         for (int kc = 0; kc < KCD; ++kc) gf[kc] = acc_frag<S>(gt[kc >> 1], kc & 1);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) sf[kc] = acc_frag<S>(s[kc >> 1], kc & 1);
-        const S *ntt = NTT + (int64_t)J * D * D;
+        const S *ntt = rec + 3 * kC * D;
 #pragma unroll
         for (int dt = 0; dt < RTD; ++dt) {
             if (J >= 1) {
@@ -612,11 +694,202 @@ __global__ __launch_bounds__(128) void bwd_up_kernel(BwdArgs a) {
                 for (int kc = 0; kc < KCD; ++kc) Elem<S>::mma(gt[dt], ldfrag<S>(ntt, dt, kc, KCD, lane), gf[kc]);
             }
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc) Elem<S>::mma(gt[dt], ldfrag<S>(KH2 + fo, dt, kc, 4, lane), sf[kc]);
+            for (int kc = 0; kc < 4; ++kc) Elem<S>::mma(gt[dt], ldfrag<S>(rec + 2 * kC * D, dt, kc, 4, lane), sf[kc]);
         }
         if (J + 1 < I) store_transposed<S, D>(GS2 + pair_index(I, J + 1) * kC * D, gt, sx[w], w, lane);
     }
+    }
     rsum = other_half_sum(rsum);  // lanes l and l ^ 32 hold the other keys of the same query
+    float *dqo = (float *)(ws + ly.dqo) + (int64_t)qi * D;
+#pragma unroll
+    for (int dt = 0; dt < RTD; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 x = {gt[dt][4 * g4], gt[dt][4 * g4 + 1], gt[dt][4 * g4 + 2], gt[dt][4 * g4 + 3]};
+            *reinterpret_cast<f32x4 *>(dqo + 32 * dt + 8 * g4 + 4 * h) = x;
+        }
+    if (h == 0) ((float *)(ws + ly.rso))[qi] = rsum;
+}
+
+// Up walk for bf16 inputs at head dimension 64: as bwd_up_kernel, but four query
+// blocks (eight waves, two per block) share each key block's record (k^, V, k^^T,
+// (T - I)^T: 32 KiB), which is copied global -> LDS one step ahead by the DMA path
+// (global_load_lds, double-buffered), as in the forward scan; each wave prefetches its
+// next stored q~ into registers.  The transposition scratch holds bf16 (rounding each
+// element before transposing gives the same fragments).
+//
+// Every step issues the same memory operations on every wave, whether or not the wave
+// has work in it (a copy for the next record, a q~ prefetch from a clamped valid pair,
+// and the stores of a transposed G, to a spare fragment set of the workspace when there
+// is nothing to store), so that one wait for all but the last stores at the top of each
+// step covers every path and the compiler adds no wait of its own inside the step.
+constexpr int kUpQB = 4;  // query blocks per workgroup
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy NLD 16-byte chunks per thread of a contiguous record into LDS (lane l of a wave
+// lands at the wave's LDS base + 16 l); completion is tracked by vmcnt.
+template <int NTH, int NLD>
+__device__ __forceinline__ void dma_record(const void *src, void *dst, int tid) {
+    const int wv = tid >> 6;
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+        const char *g = (const char *)src + (size_t)t * NTH * 16 + 16 * tid;
+        char *l = (char *)dst + (size_t)t * NTH * 16 + 1024 * wv;
+        __builtin_amdgcn_global_load_lds((const void *)g, (lds_void *)l, 16, 0, 0);
+    }
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14,
+// expcnt left at its maximum): at most n vector-memory operations outstanding and every
+// LDS access of the wave returned.
+constexpr int vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
+
+__global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_lds(BwdArgs a) {
+    typedef uint16_t S;
+    typedef Elem<S>::Frag Frag;
+    constexpr int D = 64, KCD = D / 16, RTD = D / 32, NTH = 64 * 2 * kUpQB;
+    constexpr int REC = 3 * kC * D + D * D;  // elements of a record
+    constexpr int NLD = REC * 2 / 16 / NTH;   // DMA chunks per thread and record
+    static_assert(REC * 2 % (16 * NTH) == 0, "record must split evenly over the workgroup");
+    constexpr int XB = 40;        // bf16 row stride of the transposition scratch
+    constexpr int NST = 2 * RTD;  // global stores of one transposed G
+    // One LDS array: two buffers, each a record followed by 64 key terms of the exponent and 64
+    // gate sums (between each of the tile's query blocks and the record's key block, repeated
+    // over the lanes), then the transposition scratch.  The copies into LDS are ordered by the
+    // explicit waits and barriers of the walk alone.
+    constexpr int BUF = REC * 2 + 2 * 4 * kC;  // bytes per buffer
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF + 2 * kUpQB * D * XB * 2];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int nb = a.nb, hc = a.hc;
+    const int ntile = (nb - 1 + kUpQB - 1) / kUpQB;  // query blocks 1 .. nb-1, four per tile
+    const int gl = blockIdx.x % hc, tile = ntile - 1 - blockIdx.x / hc;
+    const int I0 = 1 + kUpQB * tile;                 // the tile's first query block
+    const int Imax = min(nb - 1, I0 + kUpQB - 1);    // and its last
+    // this wave's query block and query half (wave-uniform, so the per-pair scalars are scalar loads)
+    const int I = __builtin_amdgcn_readfirstlane(I0 + (w >> 1)), wq = __builtin_amdgcn_readfirstlane(w & 1);
+    const bool active = I <= nb - 1;
+    const int Ic = active ? I : Imax;  // idle waves read a valid block and discard it
+    const BwdLayout &ly = a.ly;
+    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
+    const S *RECS = (const S *)(ws + ly.urec), *QS1 = (const S *)(ws + ly.qs1);
+    S *GS2 = (S *)(ws + ly.gs2);
+    S *const spare = GS2 + (int64_t)nb * (nb - 1) / 2 * kC * D;  // the fragment set after the last pair's
+    const float *MID = (const float *)(ws + ly.mid), *CKK = (const float *)(ws + ly.ckl);
+    const float scale = a.scale, c2 = scale * kLog2e;
+    const int qi = Ic * kC + 32 * wq + l32;
+    const float dd = ((const float *)(ws + ly.dd))[qi], cq = ((const float *)(ws + ly.cql))[qi];
+    S *const myx = (S *)(smem + 2 * BUF) + w * D * XB;
+    // the gate-sum lane of wave 1: query block I0 + (lane % 4), clamped to the last block
+    const int Il = min(I0 + (lane & (kUpQB - 1)), nb - 1);
+
+    // copies of key block J's record (all threads) and its side values (one 4-byte element per
+    // lane: key terms from wave 0 and waves 2.. (the same values), gate sums from wave 1) into
+    // buffer B.  J <= nb - 1, so every source lies inside the workspace.
+    auto issue = [&](int J, int B) {
+        unsigned char *buf = smem + B * BUF;
+        dma_record<NTH, NLD>(RECS + (int64_t)J * REC, buf, tid);
+        const float *src = w == 1 ? MID + pair_index(Il, min(J, Il - 1)) : CKK + J * kC + lane;
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(buf + REC * 2 + (w == 1 ? 4 * kC : 0)), 4, 0, 0);
+    };
+    issue(0, 0);
+    // q~ of the pair (I, J) is in qa for even J and in qb for odd J; each step loads the next one
+    Frag dof[KCD], qa[KCD], qb[KCD];
+#pragma unroll
+    for (int kc = 0; kc < KCD; ++kc) {
+        dof[kc] = ldfrag<S>((const S *)(ws + ly.do1) + (int64_t)Ic * kC * D, wq, kc, KCD, lane);
+        qa[kc] = ldfrag<S>(QS1 + pair_index(Ic, 0) * kC * D, wq, kc, KCD, lane);
+    }
+    f32x16 gt[RTD];
+#pragma unroll
+    for (int dt = 0; dt < RTD; ++dt) gt[dt] = f32x16{};
+    float rsum = 0.f;
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
+    // one step over key block J, whose copies are in buffer B (J % 2); it refills the other one
+    auto step = [&](int J, auto bsel) {
+        constexpr int B = decltype(bsel)::value;
+        const S *rec = (const S *)(smem + B * BUF);
+        const float *sck = (const float *)(smem + B * BUF + REC * 2), *smid = sck + kC;
+        // this wave's copies of record J and its q~ prefetch have landed (only the previous
+        // step's stores may still be in flight) and its LDS accesses of the previous step have
+        // returned; after the barrier every wave's copies have landed and the other buffer is free
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0(NST));
+        asm volatile("s_barrier" ::: "memory");
+        issue(min(J + 1, nb - 1), 1 - B);
+        asm volatile("" ::: "memory");  // the copies stay ahead of this step's stores
+        const bool act = active && J < I, store = act && J + 1 < I;
+        Frag(&qf)[KCD] = B ? qb : qa;
+        Frag(&qn)[KCD] = B ? qa : qb;
+        {
+            const int64_t pn = pair_index(Ic, min(J + 1, Ic - 1));
+#pragma unroll
+            for (int kc = 0; kc < KCD; ++kc) qn[kc] = ldfrag<S>(QS1 + pn * kC * D, wq, kc, KCD, lane);
+        }
+        if (act) {
+            const float mid = smid[w >> 1];
+            f32x16 sv[2], dp[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                sv[kt] = f32x16{};
+                dp[kt] = f32x16{};
+#pragma unroll
+                for (int kc = 0; kc < KCD; ++kc) {
+                    Elem<S>::mma(sv[kt], ldfrag<S>(rec, kt, kc, KCD, lane), qf[kc]);
+                    Elem<S>::mma(dp[kt], ldfrag<S>(rec + kC * D, kt, kc, KCD, lane), dof[kc]);
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const f32x4 ck = *reinterpret_cast<const f32x4 *>(sck + 32 * kt + 8 * g4 + 4 * h);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * g4 + e;
+                        const float P = fast_exp2(c2 * sv[kt][r] + cq + ck[e] + mid);
+                        const float ds = P * (dp[kt][r] - dd);
+                        rsum += ds;
+                        sv[kt][r] = scale * ds;
+                    }
+                }
+            Frag gf[KCD], sf[4];
+#pragma unroll
+            for (int kc = 0; kc < KCD; ++kc) gf[kc] = acc_frag<S>(gt[kc >> 1], kc & 1);
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) sf[kc] = acc_frag<S>(sv[kc >> 1], kc & 1);
+#pragma unroll
+            for (int dt = 0; dt < RTD; ++dt) {
+                if (J >= 1) {
+#pragma unroll
+                    for (int kc = 0; kc < KCD; ++kc)
+                        Elem<S>::mma(gt[dt], ldfrag<S>(rec + 3 * kC * D, dt, kc, KCD, lane), gf[kc]);
+                }
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) Elem<S>::mma(gt[dt], ldfrag<S>(rec + 2 * kC * D, dt, kc, 4, lane), sf[kc]);
+            }
+            // G^(J) with rows d for the pair (I, J + 1), into the bf16 scratch
+#pragma unroll
+            for (int dt = 0; dt < RTD; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) myx[(32 * dt + acc_row(r, h)) * XB + l32] = Elem<S>::from_float(gt[dt][r]);
+        }
+        // the stores (the scratch's stale contents to the spare set when there is nothing to store)
+        S *dst = store ? GS2 + pair_index(I, J + 1) * kC * D : spare;
+#pragma unroll
+        for (int dt = 0; dt < RTD; ++dt)
+#pragma unroll
+            for (int kcl = 0; kcl < 2; ++kcl) {
+                const S *src = myx + (32 * dt + l32) * XB + 16 * kcl + 4 * h;
+                const u32x2 lo = *reinterpret_cast<const u32x2 *>(src), hi = *reinterpret_cast<const u32x2 *>(src + 8);
+                stfrag<S>(dst, dt, 2 * wq + kcl, 4, lane, __builtin_bit_cast(Frag, u32x4{lo.x, lo.y, hi.x, hi.y}));
+            }
+    };
+    for (int J = 0; J < Imax; J += 2) {
+        step(J, std::integral_constant<int, 0>{});
+        if (J + 1 < Imax) step(J + 1, std::integral_constant<int, 1>{});
+    }
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));  // no copy may still be landing in LDS when the workgroup leaves
+    if (!active) return;
+    rsum = other_half_sum(rsum);
     float *dqo = (float *)(ws + ly.dqo) + (int64_t)qi * D;
 #pragma unroll
     for (int dt = 0; dt < RTD; ++dt)
@@ -651,32 +924,122 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel(BwdArgs a) 
     constexpr int NACC = 2 * RTW + TRW * RTD;  // accumulator tiles per wave
     __shared__ __attribute__((aligned(16))) float sred[K::NW / 2][16 * 65];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-    const int qt = w & 1, kt = (w >> 1) & 1, dh = w >> 2, grp = kt + 2 * dh;
+    const int qt = w & 1, kt = (w >> 1) & 1, dh = K::NDH == 1 ? 0 : w >> 2, grp = kt + 2 * dh;
     const int nb = a.nb, hc = a.hc;
     const int gl = blockIdx.x % hc, J = blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
     const S *QS1 = (const S *)(ws + ly.qs1), *QS2 = (const S *)(ws + ly.qs2), *GS2 = (const S *)(ws + ly.gs2);
     const S *DO1 = (const S *)(ws + ly.do1), *DO2 = (const S *)(ws + ly.do2);
-    const float *MID = (const float *)(ws + ly.mid), *L2 = (const float *)(ws + ly.l2);
-    const float *DD = (const float *)(ws + ly.dd), *CLQ = (const float *)(ws + ly.clq);
-    const float scale = a.scale;
+    const float *MID = (const float *)(ws + ly.mid);
+    const float *DD = (const float *)(ws + ly.dd), *CQL = (const float *)(ws + ly.cql);
+    const float scale = a.scale, c2 = scale * kLog2e;
     const int key = J * kC + 32 * kt + l32;  // this lane's key (column of the logit tile)
-    const float ck = ((const float *)(ws + ly.ckk))[key];
+    const float ck = ((const float *)(ws + ly.ckl))[key];
 
     Frag kf[KCD], vf[KCD];  // k^ and V of key tile kt, k over d: the B operands of S and dP
     {
-        const int64_t fo = (int64_t)J * kC * D;
+        const S *rec = (const S *)(ws + ly.urec) + J * ly.rec_elems;
 #pragma unroll
         for (int kc = 0; kc < KCD; ++kc) {
-            kf[kc] = ldfrag<S>((const S *)(ws + ly.kh1) + fo, kt, kc, KCD, lane);
-            vf[kc] = ldfrag<S>((const S *)(ws + ly.v1) + fo, kt, kc, KCD, lane);
+            kf[kc] = ldfrag<S>(rec, kt, kc, KCD, lane);
+            vf[kc] = ldfrag<S>(rec + kC * D, kt, kc, KCD, lane);
         }
     }
     f32x16 acc[NACC];  // dV^T (RTW), dk^^T (RTW), dT rows grp * TRW .. (TRW x RTD)
 #pragma unroll
     for (int t = 0; t < NACC; ++t) acc[t] = f32x16{};
     float csum = 0.f;
+    if constexpr (D == 64) {
+    // Every fragment a step needs is loaded at its top, and the next pair's q~ and dO
+    // (the first operands of a step) one step ahead, so a step waits for memory once.
+    Frag q1[KCD], o1[KCD];
+    auto load_first = [&](int I, Frag *q, Frag *o) {
+        const int64_t po = pair_index(I, J) * kC * D, bo = (int64_t)I * kC * D;
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) {
+            q[kc] = ldfrag<S>(QS1 + po, qt, kc, KCD, lane);
+            o[kc] = ldfrag<S>(DO1 + bo, qt, kc, KCD, lane);
+        }
+    };
+    load_first(J + 1, q1, o1);
+    for (int I = J + 1; I < nb; ++I) {
+        const int64_t p = pair_index(I, J), po = p * kC * D, bo = (int64_t)I * kC * D;
+        // (the dk^ operands are loaded apart from the dT ones: indexing a register array with the
+        // wave's tile group would compile into selects over the whole array)
+        Frag q2[RTD][2], q2k[RTW][2], o2[RTW][2], g2[TRW][2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+            for (int ct = 0; ct < RTD; ++ct) q2[ct][cc] = ldfrag<S>(QS2 + po, ct, 2 * qt + cc, 4, lane);
+#pragma unroll
+            for (int i = 0; i < RTW; ++i) {
+                q2k[i][cc] = ldfrag<S>(QS2 + po, dh * RTW + i, 2 * qt + cc, 4, lane);
+                o2[i][cc] = ldfrag<S>(DO2 + bo, dh * RTW + i, 2 * qt + cc, 4, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < TRW; ++i)
+                g2[i][cc] = J >= 1 ? ldfrag<S>(GS2 + po, grp * TRW + i, 2 * qt + cc, 4, lane) : Frag{};
+        }
+        const float mid = MID[p];
+        const int q0 = I * kC + 32 * qt + 4 * h;
+        f32x4 ddv[4], cqv[4];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            ddv[g4] = *reinterpret_cast<const f32x4 *>(DD + q0 + 8 * g4);
+            cqv[g4] = *reinterpret_cast<const f32x4 *>(CQL + q0 + 8 * g4);
+        }
+        Frag q1n[KCD], o1n[KCD];
+        if (I + 1 < nb) load_first(I + 1, q1n, o1n);
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) {
+            Elem<S>::mma(s, q1[kc], kf[kc]);
+            Elem<S>::mma(dp, o1[kc], vf[kc]);
+        }
+        // P and dS (rows: queries 32 qt + acc_row(r, h) of block I; column: this lane's key)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g4 + e;
+                const float P = fast_exp2(c2 * s[r] + cqv[g4][e] + ck + mid);
+                const float ds = P * (dp[r] - ddv[g4][e]);
+                csum += ds;
+                s[r] = ds;
+                dp[r] = P;
+            }
+        Frag pf[2], sf[2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            pf[cc] = acc_frag<S>(dp, cc);
+            sf[cc] = acc_frag<S>(s, cc);
+        }
+#pragma unroll
+        for (int i = 0; i < RTW; ++i)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                Elem<S>::mma(acc[i], o2[i][cc], pf[cc]);
+                Elem<S>::mma(acc[RTW + i], q2k[i][cc], sf[cc]);
+            }
+        if (J >= 1) {
+#pragma unroll
+            for (int i = 0; i < TRW; ++i)
+#pragma unroll
+                for (int ct = 0; ct < RTD; ++ct)
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) Elem<S>::mma(acc[2 * RTW + i * RTD + ct], g2[i][cc], q2[ct][cc]);
+        }
+        if (I + 1 < nb) {
+#pragma unroll
+            for (int kc = 0; kc < KCD; ++kc) {
+                q1[kc] = q1n[kc];
+                o1[kc] = o1n[kc];
+            }
+        }
+    }
+    } else {
+    // (d = 128: a step's operands do not fit the registers at once; each is loaded where it is used)
     for (int I = J + 1; I < nb; ++I) {
         const int64_t p = pair_index(I, J), po = p * kC * D, bo = (int64_t)I * kC * D;
         const float mid = MID[p];
@@ -686,17 +1049,15 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel(BwdArgs a) 
             Elem<S>::mma(s, ldfrag<S>(QS1 + po, qt, kc, KCD, lane), kf[kc]);
             Elem<S>::mma(dp, ldfrag<S>(DO1 + bo, qt, kc, KCD, lane), vf[kc]);
         }
-        // P and dS (rows: queries 32 qt + acc_row(r, h) of block I; column: this lane's key)
         const int q0 = I * kC + 32 * qt + 4 * h;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 l2 = *reinterpret_cast<const f32x4 *>(L2 + q0 + 8 * g4);
             const f32x4 dd = *reinterpret_cast<const f32x4 *>(DD + q0 + 8 * g4);
-            const f32x4 cq = *reinterpret_cast<const f32x4 *>(CLQ + q0 + 8 * g4);
+            const f32x4 cq = *reinterpret_cast<const f32x4 *>(CQL + q0 + 8 * g4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g4 + e;
-                const float P = fast_exp2((scale * s[r] + cq[e] + ck + mid) * kLog2e - l2[e]);
+                const float P = fast_exp2(c2 * s[r] + cq[e] + ck + mid);
                 const float ds = P * (dp[r] - dd[e]);
                 csum += ds;
                 s[r] = ds;
@@ -733,6 +1094,7 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel(BwdArgs a) 
                                      ldfrag<S>(QS2 + po, ct, 2 * qt + cc, 4, lane));
             }
         }
+    }
     }
     csum = other_half_sum(csum);  // lanes l and l ^ 32 hold the other queries of the same key
     // add the query half qt = 1 into qt = 0 (the partner wave w + 1), one tile at a time
@@ -1028,7 +1390,12 @@ hipError_t launch_bwd_t(const BwdArgs &a0, hipStream_t st) {
         if (a.nb > 1) {
             const dim3 walks((unsigned)((a.nb - 1) * a.hc));
             hipLaunchKernelGGL((bwd_down_kernel<T, D>), walks, dim3(128), 0, st, a);
-            hipLaunchKernelGGL((bwd_up_kernel<T, D>), walks, dim3(128), 0, st, a);
+            if constexpr (sizeof(T) == 2 && D == 64) {
+                const dim3 tiles((unsigned)((a.nb - 1 + kUpQB - 1) / kUpQB * a.hc));
+                hipLaunchKernelGGL(bwd_up_kernel_lds, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
+            } else {
+                hipLaunchKernelGGL((bwd_up_kernel<T, D>), walks, dim3(128), 0, st, a);
+            }
             hipLaunchKernelGGL((bwd_key_kernel<T, D>), walks, dim3(64 * KeyCfg<D>::NW), 0, st, a);
         }
         hipLaunchKernelGGL((bwd_block_kernel<T, D>), dim3(a.nb, a.hc), dim3(kT), 0, st, a);

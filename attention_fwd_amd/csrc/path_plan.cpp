@@ -41,16 +41,19 @@ BwdLayout bwd_layout(int L, int D, int es) {
     const int64_t frd = nb * (int64_t)D * D * es;  // a D x D fragment set per block
     const int64_t nat = Lp * D * 4, rows = Lp * 4;
     ly.xx = take(tok); ly.aa = take(tok); ly.qwm = take(tok); ly.nn = take(tok); ly.zz = take(tok); ly.ee = take(tok);
-    ly.kh1 = take(fr); ly.kh2 = take(fr); ly.v1 = take(fr); ly.do1 = take(fr); ly.do2 = take(fr);
-    ly.nt = take(frd); ly.ntt = take(frd);
+    ly.rec_elems = 3 * 64 * (int64_t)D + (int64_t)D * D;
+    ly.urec = take(nb * ly.rec_elems * es);
+    ly.do1 = take(fr); ly.do2 = take(fr);
+    ly.nt = take(frd);
     ly.qh = take(nat); ly.dvd = take(nat); ly.dqo = take(nat); ly.dko = take(nat); ly.dvo = take(nat);
     ly.uu = take(nat); ly.vv = take(nat);
     ly.dtt = take(nb * (int64_t)D * D * 4);
-    ly.l2 = take(rows); ly.dd = take(rows); ly.clq = take(rows); ly.ckk = take(rows); ly.rsd = take(rows);
+    ly.dd = take(rows); ly.cql = take(rows); ly.ckl = take(rows); ly.rsd = take(rows);
     ly.csd = take(rows); ly.rso = take(rows); ly.cso = take(rows); ly.dc = take(rows);
     ly.tot = take(nb * 4); ly.mid = take(np * 4);
     const int64_t pr = np * 64 * D * es;  // a 64 x D fragment set per pair
-    ly.qs1 = take(pr); ly.qs2 = take(pr); ly.gs2 = take(pr);
+    ly.qs1 = take(pr); ly.qs2 = take(pr);
+    ly.gs2 = take(pr + 64 * D * es);  // one spare set after the last pair's: target of discarded stores
     ly.head = off;
     return ly;
 }
