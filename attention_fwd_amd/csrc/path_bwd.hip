@@ -26,9 +26,10 @@
 //   prep (per block): the quantities above, kept as fp32 64 x 64 matrices for
 //     the block backward and as matrix-core fragments for the walks; the
 //     diagonal block's dS and value gradient;
-//   down walk (per query block I): q~^(J) for J = I-1 .. 0, stored per pair in
-//     two orientations (rows queries / rows d: the sums over queries below
-//     need the query index inside a lane's fragment);
+//   down walk (per query block I): q~^(J) for J = I-1 .. 0, stored per pair
+//     with rows queries and, except for bf16 at d = 64, with rows d (the sums
+//     over queries below need the query index inside a lane's fragment; the
+//     bf16 d = 64 key walk gathers that orientation from an LDS copy);
 //   up walk (per query block I): J = 0 .. I-1, the logits, P and dS from the
 //     stored q~, the adjoint G, stored per pair (rows d), and dq^_I = G^(I-1);
 //   key walk (per key block J): over I > J the logits, P and dS again (from
@@ -481,9 +482,9 @@ __device__ __forceinline__ void store_transposed(S *dst, const f32x16 *t, float 
 // Down walk: one workgroup (two waves) per (query block I >= 1, head), heaviest
 // first.  q~^T (rows d, the wave's 32 queries) stays in fp32 accumulators:
 // q~^T <- q~^T + (T_J - I) q~^T; q~^(J) is stored for the pair (I, J) with rows
-// queries (for the logits) and with rows d (for the key walk's sums over
-// queries), with the gate sum of the blocks strictly between I and J.
-template <typename S, int D>
+// queries (for the logits) and, with Q2, with rows d (for the key walk's sums
+// over queries), with the gate sum of the blocks strictly between I and J.
+template <typename S, int D, bool Q2>
 __global__ __launch_bounds__(128) void bwd_down_kernel(BwdArgs a) {
     typedef typename Elem<S>::Frag Frag;
     constexpr int KCD = D / 16, RTD = D / 32;
@@ -521,7 +522,7 @@ __global__ __launch_bounds__(128) void bwd_down_kernel(BwdArgs a) {
         S *q1 = QS1 + p * kC * D;
 #pragma unroll
         for (int kc = 0; kc < KCD; ++kc) stfrag<S>(q1, w, kc, KCD, lane, qf[kc]);
-        store_transposed<S, D>(QS2 + p * kC * D, qt, sx[w], w, lane);
+        if constexpr (Q2) store_transposed<S, D>(QS2 + p * kC * D, qt, sx[w], w, lane);
         if (J >= 1) {
             const S *nt = NT + (int64_t)J * D * D;
 #pragma unroll
@@ -1379,6 +1380,192 @@ __global__ __launch_bounds__(kT) void bwd_gate_kernel(BwdArgs a) {
     }
 }
 
+// Key walk for bf16 inputs at head dimension 64: as bwd_key_kernel (four waves:
+// query half qt = w & 1, key half kt = w >> 1), but each step's operands -- the
+// pair's q~ (rows queries) and G^T, the query block's dO in both orientations, its
+// exponent terms and the pair's gate sum: 32.8 KiB -- are copied global -> LDS one
+// step ahead (global_load_lds, double-buffered) and read by every wave from there.
+// The q~^T fragments (rows d, k over queries) are gathered from the q~ copy with
+// 2-byte LDS reads, so the down walk stores q~ in one orientation only.
+__global__ __launch_bounds__(256) void bwd_key_kernel_lds(BwdArgs a) {
+    typedef uint16_t S;
+    typedef Elem<S>::Frag Frag;
+    constexpr int D = 64, KCD = D / 16, RTD = D / 32, NTH = 256;
+    constexpr int FR = kC * D;               // elements of a 64 x D fragment set
+    constexpr int NLD = FR * 2 / 16 / NTH;   // 16-byte copies per thread and fragment set
+    static_assert(FR * 2 % (16 * NTH) == 0, "a fragment set must split evenly over the workgroup");
+    // a buffer: q~, G^T, dO (rows queries), dO^T (rows d), then 64 floats each of the query
+    // terms dd and cq and of the gate sum (the same value 64 times)
+    constexpr int BUF = 4 * FR * 2 + 3 * 4 * kC;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int qt = w & 1, kt = w >> 1;
+    const int nb = a.nb, hc = a.hc;
+    const int gl = blockIdx.x % hc, J = blockIdx.x / hc;
+    const BwdLayout &ly = a.ly;
+    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
+    const S *QS1 = (const S *)(ws + ly.qs1), *GS2 = (const S *)(ws + ly.gs2);
+    const S *DO1 = (const S *)(ws + ly.do1), *DO2 = (const S *)(ws + ly.do2);
+    const float *MID = (const float *)(ws + ly.mid);
+    const float *DD = (const float *)(ws + ly.dd), *CQL = (const float *)(ws + ly.cql);
+    const float scale = a.scale, c2 = scale * kLog2e;
+    const int key = J * kC + 32 * kt + l32;  // this lane's key (column of the logit tile)
+    const float ck = ((const float *)(ws + ly.ckl))[key];
+
+    // copies of query block I's step into buffer B (I <= nb - 1, so every source is in the
+    // workspace; for J = 0 the G^T slot holds no adjoint and is not used)
+    auto issue = [&](int I, int B) {
+        unsigned char *buf = smem + B * BUF;
+        const int64_t po = pair_index(I, J) * FR, bo = (int64_t)I * FR;
+        dma_record<NTH, NLD>(QS1 + po, buf, tid);
+        dma_record<NTH, NLD>(GS2 + po, buf + FR * 2, tid);
+        dma_record<NTH, NLD>(DO1 + bo, buf + 2 * FR * 2, tid);
+        dma_record<NTH, NLD>(DO2 + bo, buf + 3 * FR * 2, tid);
+        const float *src = w == 0 ? DD + I * kC + lane : w == 1 ? CQL + I * kC + lane : MID + pair_index(I, J);
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(buf + 4 * FR * 2 + 4 * kC * min(w, 2)), 4, 0, 0);
+    };
+    issue(J + 1, 0);
+    Frag kf[KCD], vf[KCD];  // k^ and V of key tile kt, k over d: the B operands of S and dP
+    {
+        const S *rec = (const S *)(ws + ly.urec) + J * ly.rec_elems;
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) {
+            kf[kc] = ldfrag<S>(rec, kt, kc, KCD, lane);
+            vf[kc] = ldfrag<S>(rec + kC * D, kt, kc, KCD, lane);
+        }
+    }
+    f32x16 acc[6];  // dV^T (2 row tiles of d), dk^^T (2), dT rows 32 kt .. (2 column tiles)
+#pragma unroll
+    for (int t = 0; t < 6; ++t) acc[t] = f32x16{};
+    float csum = 0.f;
+    // q~^T fragment (rows d = 32 ct + lane % 32, k over queries 16 kq ..) gathered from the q~ copy:
+    // element e of a lane is q~[16 kq + 8 (e >> 2) + 4 h + (e & 3)][d], which sits in the q~
+    // fragment of rows 32 (kq >> 1) .. and d chunk d >> 4 at lane (query % 32) + 32 ((d >> 2) & 1),
+    // element 4 ((d >> 3) & 1) + (d & 3)
+    const int dl = l32, qlane = 32 * ((dl >> 2) & 1), qel = 4 * ((dl >> 3) & 1) + (dl & 3);
+    auto gather_qt = [&](const S *sq, int ct, int kq) {
+        const int d = 32 * ct + dl;
+        const S *base = sq + ((((kq >> 1) * KCD + (d >> 4)) * 64 + 16 * (kq & 1) + 4 * h + qlane) * 8 + qel);
+        Frag f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = base[(8 * (e >> 2) + (e & 3)) * 8];
+        return f;
+    };
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
+    // one step over query block I, whose copies are in buffer B ((I - J - 1) % 2); it refills the other
+    auto step = [&](int I, auto bsel) {
+        constexpr int B = decltype(bsel)::value;
+        const unsigned char *buf = smem + B * BUF;
+        const S *sq = (const S *)buf, *sg = sq + FR, *so1 = sq + 2 * FR, *so2 = sq + 3 * FR;
+        const float *sdd = (const float *)(buf + 4 * FR * 2), *scq = sdd + kC, *smid = scq + kC;
+        // this wave's copies of step I have landed and its LDS reads of the previous step have
+        // returned; after the barrier every wave's copies have landed and the other buffer is free
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
+        asm volatile("s_barrier" ::: "memory");
+        issue(min(I + 1, nb - 1), 1 - B);
+        asm volatile("" ::: "memory");
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) {
+            Elem<S>::mma(s, ldfrag<S>(sq, qt, kc, KCD, lane), kf[kc]);
+            Elem<S>::mma(dp, ldfrag<S>(so1, qt, kc, KCD, lane), vf[kc]);
+        }
+        const float mid = smid[0];
+        // P and dS (rows: queries 32 qt + acc_row(r, h) of block I; column: this lane's key)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 ddv = *reinterpret_cast<const f32x4 *>(sdd + 32 * qt + 8 * g4 + 4 * h);
+            const f32x4 cqv = *reinterpret_cast<const f32x4 *>(scq + 32 * qt + 8 * g4 + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g4 + e;
+                const float P = fast_exp2(c2 * s[r] + cqv[e] + ck + mid);
+                const float ds = P * (dp[r] - ddv[e]);
+                csum += ds;
+                s[r] = ds;
+                dp[r] = P;
+            }
+        }
+        Frag pf[2], sf[2], q2[RTD][2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            pf[cc] = acc_frag<S>(dp, cc);
+            sf[cc] = acc_frag<S>(s, cc);
+#pragma unroll
+            for (int ct = 0; ct < RTD; ++ct) q2[ct][cc] = gather_qt(sq, ct, 2 * qt + cc);
+        }
+#pragma unroll
+        for (int i = 0; i < RTD; ++i)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                Elem<S>::mma(acc[i], ldfrag<S>(so2, i, 2 * qt + cc, 4, lane), pf[cc]);
+                Elem<S>::mma(acc[RTD + i], q2[i][cc], sf[cc]);
+            }
+        if (J >= 1) {
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const Frag ga = ldfrag<S>(sg, kt, 2 * qt + cc, 4, lane);
+#pragma unroll
+                for (int ct = 0; ct < RTD; ++ct) Elem<S>::mma(acc[2 * RTD + ct], ga, q2[ct][cc]);
+            }
+        }
+    };
+    for (int I = J + 1; I < nb; I += 2) {
+        step(I, std::integral_constant<int, 0>{});
+        if (I + 1 < nb) step(I + 1, std::integral_constant<int, 1>{});
+    }
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));  // the last (unused) copy has landed
+    csum = other_half_sum(csum);  // lanes l and l ^ 32 hold the other queries of the same key
+    // add the query half qt = 1 (wave w + 1) into qt = 0 (wave w), one tile at a time, through
+    // the buffers (free now)
+    float *red = (float *)smem + (w >> 1) * 16 * 65;
+    for (int t = 0; t <= 6; ++t) {
+        __syncthreads();
+        if (qt == 1) {
+            if (t < 6) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) red[r * 65 + lane] = acc[t][r];
+            } else {
+                red[lane] = csum;
+            }
+        }
+        __syncthreads();
+        if (qt == 0) {
+            if (t < 6) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[t][r] += red[r * 65 + lane];
+            } else {
+                csum += red[lane];
+            }
+        }
+    }
+    if (qt != 0) return;
+    float *dvo = (float *)(ws + ly.dvo) + (int64_t)key * D, *dko = (float *)(ws + ly.dko) + (int64_t)key * D;
+#pragma unroll
+    for (int i = 0; i < RTD; ++i)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * i + 8 * g4 + 4 * h;
+            const f32x4 xv = {acc[i][4 * g4], acc[i][4 * g4 + 1], acc[i][4 * g4 + 2], acc[i][4 * g4 + 3]};
+            const f32x4 xk = {scale * acc[RTD + i][4 * g4], scale * acc[RTD + i][4 * g4 + 1],
+                              scale * acc[RTD + i][4 * g4 + 2], scale * acc[RTD + i][4 * g4 + 3]};
+            *reinterpret_cast<f32x4 *>(dvo + d0) = xv;
+            *reinterpret_cast<f32x4 *>(dko + d0) = xk;
+        }
+    if (J >= 1) {  // dT^T: element (c, r) = dT[r][c]; lane c writes 4 consecutive r
+        float *dtt = (float *)(ws + ly.dtt) + (int64_t)J * D * D;
+#pragma unroll
+        for (int ct = 0; ct < RTD; ++ct)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x16 &x = acc[2 * RTD + ct];
+                const f32x4 y = {x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]};
+                *reinterpret_cast<f32x4 *>(dtt + (int64_t)(32 * ct + l32) * D + 32 * kt + 8 * g4 + 4 * h) = y;
+            }
+    }
+    if (h == 0) ((float *)(ws + ly.cso))[J * kC + 32 * kt + l32] = csum;
+}
+
 template <typename T, int D>
 hipError_t launch_bwd_t(const BwdArgs &a0, hipStream_t st) {
     BwdArgs a = a0;
@@ -1389,14 +1576,16 @@ hipError_t launch_bwd_t(const BwdArgs &a0, hipStream_t st) {
         hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(a.nb, a.hc), dim3(kT), 0, st, a);
         if (a.nb > 1) {
             const dim3 walks((unsigned)((a.nb - 1) * a.hc));
-            hipLaunchKernelGGL((bwd_down_kernel<T, D>), walks, dim3(128), 0, st, a);
             if constexpr (sizeof(T) == 2 && D == 64) {
+                hipLaunchKernelGGL((bwd_down_kernel<T, D, false>), walks, dim3(128), 0, st, a);
                 const dim3 tiles((unsigned)((a.nb - 1 + kUpQB - 1) / kUpQB * a.hc));
                 hipLaunchKernelGGL(bwd_up_kernel_lds, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
+                hipLaunchKernelGGL(bwd_key_kernel_lds, walks, dim3(256), 0, st, a);
             } else {
+                hipLaunchKernelGGL((bwd_down_kernel<T, D, true>), walks, dim3(128), 0, st, a);
                 hipLaunchKernelGGL((bwd_up_kernel<T, D>), walks, dim3(128), 0, st, a);
+                hipLaunchKernelGGL((bwd_key_kernel<T, D>), walks, dim3(64 * KeyCfg<D>::NW), 0, st, a);
             }
-            hipLaunchKernelGGL((bwd_key_kernel<T, D>), walks, dim3(64 * KeyCfg<D>::NW), 0, st, a);
         }
         hipLaunchKernelGGL((bwd_block_kernel<T, D>), dim3(a.nb, a.hc), dim3(kT), 0, st, a);
         if (a.dlogf) hipLaunchKernelGGL(bwd_gate_kernel, dim3(a.hc), dim3(kT), 0, st, a);
