@@ -43,7 +43,7 @@ struct PrepCfg {
     // dwords, paired the rows r and r + 16 on the same banks); rows are 8-byte aligned
     // only, so 16-byte accesses to them are split (lds_store16 / lds_load16).
     static constexpr int PAD = kBf ? 12 : 4;
-    static constexpr int SP = 64 + PAD;    // padded row stride of [.][64] matrices (X, Y, A, W^T, V^T)
+    static constexpr int SP = 64 + PAD;    // padded row stride of [.][64] matrices (W^T)
     static constexpr int SPD = D + PAD;    // padded row stride of [64][D] matrices (W, Q, K)
     static constexpr int MAT = 64 * SP;    // one 64 x 64 matrix
     static constexpr int MATD = 64 * SPD;  // one 64 x D matrix, token rows
@@ -57,19 +57,39 @@ struct PrepCfg {
     // room for transposed copies and reads them with a stride instead) in W's
     // slot once the products with W are done, written from registers.  A
     // second region is reused: Q, K while the products with them run, then G
-    // and E for the triangular solve, then A (fp32) or A^T (bf16; A is read
-    // from it with a stride) and V^T.  At D = 64, bf16, this is 49 KiB, so
+    // and E for the triangular solve, then A, A^T and V^T.  X, Y, A, A^T and
+    // V^T are kept in matrix-core fragment order (FRAG: 64 rows x 64 k, each
+    // lane's 8 elements contiguous), so a wave reads each operand with
+    // 16-byte accesses of consecutive lanes (conflict-free) and writes X and
+    // Y straight from its accumulators.  At D = 64, bf16, this is 50 KiB, so
     // three workgroups share a CU.
+    static constexpr int FRAG = 64 * 64;
     static constexpr bool kWtLate = kBf;
     static constexpr int WSLOT = kWtLate ? cmax(MATD, MATT) : MATD;
-    static constexpr int FIX = WSLOT + 2 * MAT;  // elements
+    static constexpr int FIX = WSLOT + 2 * FRAG;  // elements
     // (+ 1 KiB after Q, K in phases 1-2: per-thread partial norms of the fused producer)
-    static constexpr int RB = cmax(cmax(2 * MATD * (int)sizeof(S) + 1024, 2 * 10 * TS * 4), (MAT + MATT) * (int)sizeof(S));
+    static constexpr int RB = cmax(cmax(2 * MATD * (int)sizeof(S) + 1024, 2 * 10 * TS * 4), (2 * FRAG + D * 64) * (int)sizeof(S));
     static constexpr int WG_PER_CU = kBf ? (D == 64 ? 3 : 2) : 1;  // = waves per SIMD (4-wave workgroups)
 };
 
 // Offset (floats) of tile (I, K), K <= I, in the packed lower-triangular tile store.
 __device__ __forceinline__ int tri_tile(int I, int K) { return (I * (I + 1) / 2 + K) * (16 * 16); }
+
+// Matrices of 64 k (tokens) in fragment order: fragment (row tile rt, k chunk kc) of
+// lane l is 8 contiguous elements at ((4 rt + kc) 64 + l) 8; element e of lane l
+// is (row 32 rt + l % 32, k 16 kc + frag_k(e, l / 32)).
+template <typename S>
+__device__ __forceinline__ typename Elem<S>::Frag frag_ld(const S *m, int rt, int kc, int lane) {
+    return *(const typename Elem<S>::Frag *)(m + ((4 * rt + kc) * 64 + lane) * 8);
+}
+template <typename S>
+__device__ __forceinline__ void frag_st(S *m, int rt, int kc, int lane, const typename Elem<S>::Frag &f) {
+    *(typename Elem<S>::Frag *)(m + ((4 * rt + kc) * 64 + lane) * 8) = f;
+}
+// index of element (row, k)
+__device__ __forceinline__ int frag_at(int row, int k) {
+    return ((4 * (row >> 5) + (k >> 4)) * 64 + (row & 31) + 32 * ((k >> 2) & 1)) * 8 + 4 * ((k >> 3) & 1) + (k & 3);
+}
 
 // Fragment of the matrix view `m` (element (row, k) at row*SP + k when KC, at
 // k*SP + row otherwise; SP = row stride in elements) for rows `row`, k in [k0, k0+16).
@@ -123,26 +143,6 @@ __device__ __forceinline__ void tile_mma(f32x16 &c, const S *A, const S *B, int 
     }
 }
 
-// Store the transpose of a 32x32 accumulator tile: element (row, col) goes to
-// mat[col][row] (zero where keep(row, col) is false); 4 contiguous rows per store.
-template <typename S, int SP, typename F>
-__device__ __forceinline__ void store_tile_t(S *mat, const f32x16 &c, int m0, int n0, int lane, F keep) {
-    const int h = lane >> 5, col = n0 + (lane & 31);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int row = m0 + 8 * g + 4 * h;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = keep(row + e, col) ? c[4 * g + e] : 0.f;
-        S *p = mat + col * SP + row;
-        if constexpr (sizeof(S) == 2) {
-            *(u32x2 *)p = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-        } else {
-            *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
-        }
-    }
-}
-
 // 16 bytes to / from a padded LDS row: one access for fp32 (rows 16-byte
 // aligned), two 8-byte accesses for bf16 (rows 8-byte aligned).
 template <typename S>
@@ -161,27 +161,6 @@ __device__ __forceinline__ u32x4 lds_load16(const S *p) {
         return u32x4{a.x, a.y, b.x, b.y};
     } else {
         return *(const u32x4 *)p;
-    }
-}
-
-// Accumulator tile initialised from the transpose of an LDS matrix:
-// c(row, col) = mat[col][row] (rows = k index of mat, 4 contiguous per group).
-template <typename S, int SP>
-__device__ __forceinline__ void load_tile_t(f32x16 &c, const S *mat, int m0, int n0, int lane) {
-    const int h = lane >> 5, col = n0 + (lane & 31);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const S *p = mat + col * SP + m0 + 8 * g + 4 * h;
-        if constexpr (sizeof(S) == 2) {
-            const u32x2 u = *(const u32x2 *)p;
-            c[4 * g + 0] = bf16_to_f32(u.x & 0xffff);
-            c[4 * g + 1] = bf16_to_f32(u.x >> 16);
-            c[4 * g + 2] = bf16_to_f32(u.y & 0xffff);
-            c[4 * g + 3] = bf16_to_f32(u.y >> 16);
-        } else {
-            const f32x4 v = *(const f32x4 *)p;
-            c[4 * g + 0] = v.x; c[4 * g + 1] = v.y; c[4 * g + 2] = v.z; c[4 * g + 3] = v.w;
-        }
     }
 }
 
@@ -238,16 +217,19 @@ __device__ __forceinline__ void tile_mma_breg(f32x16 &c, const S *A, int m0, con
         Elem<S>::mma(c, a, acc_frag<S>(bt[kc >> 1], kc & 1));
     }
 }
-
-// c += A * B(n0.., k) where A's fragments come from two accumulator tiles.
-template <typename S, bool BKC, int SB>
-__device__ __forceinline__ void tile_mma_areg(f32x16 &c, const f32x16 *at, const S *B, int n0, int lane) {
-    const int h = lane >> 5, l = lane & 31;
+// the same with A in fragment order (row tile rt)
+template <typename S>
+__device__ __forceinline__ void tile_mma_fbreg(f32x16 &c, const S *A, int rt, const f32x16 *bt, int lane) {
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-        auto b = lds_frag<S, BKC, SB>(B, n0 + l, 16 * kc, h);
-        Elem<S>::mma(c, acc_frag<S>(at[kc >> 1], kc & 1), b);
-    }
+    for (int kc = 0; kc < 4; ++kc) Elem<S>::mma(c, frag_ld<S>(A, rt, kc, lane), acc_frag<S>(bt[kc >> 1], kc & 1));
+}
+
+// c += A * B where A's fragments come from two accumulator tiles and B is in fragment
+// order (row tile rt).
+template <typename S>
+__device__ __forceinline__ void tile_mma_areg_f(f32x16 &c, const f32x16 *at, const S *B, int rt, int lane) {
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) Elem<S>::mma(c, acc_frag<S>(at[kc >> 1], kc & 1), frag_ld<S>(B, rt, kc, lane));
 }
 
 template <typename S, int D, bool FOX>
@@ -265,13 +247,15 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
     __shared__ __attribute__((aligned(16))) char region[C::RB];
     __shared__ float sBeta[64], sCl[64];
 
-    S *sW = fixed, *sX = fixed + C::WSLOT, *sY = fixed + C::WSLOT + MAT;
+    // X = tril(Q W^T) (rows queries i, k over tokens c) and -Y, Y = strictly_upper(K W^T)
+    // (rows keys j, k over tokens r), in fragment order
+    S *sW = fixed, *sX = fixed + C::WSLOT, *sY = sX + C::FRAG;
     S *sWt = kBf ? fixed : nullptr;
     S *sQ = (S *)region, *sK = (S *)region + C::MATD;               // phases 1-2
     float *sPart = (float *)((char *)region + 2 * C::MATD * sizeof(S));  // phases 1-2, fused producer: [4][64]
     float *sG = (float *)region, *sE = (float *)region + 10 * C::TS;  // phase 3
-    S *sA = kBf ? nullptr : (S *)region, *sAup = kBf ? (S *)region : nullptr;  // phase 4
-    S *sVt = (S *)region + MAT;
+    // phase 4, fragment order: A (rows t, k over c), A^T (rows r, k over c: A[c][r]), V^T (rows d, k over tokens)
+    S *sA = (S *)region, *sAt = sA + C::FRAG, *sVt = sAt + C::FRAG;
 
     const int L = a.L;
     const FwdLayout lay = fwd_layout(a.B, a.H, L, D, sizeof(S));
@@ -445,34 +429,76 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
     }
 
     const int mt = (wv >> 1) * 32, nt = (wv & 1) * 32;  // this wave's tile of a 64x64 product
+    typedef typename Elem<S>::Frag Frag;
 
-    // ---- 2. G = W W^T, X = tril(Q W^T), Y = strictly_upper(K W^T); products with Q and K
+    // ---- 2. G = W W^T, X = tril(Q W^T), -Y = -strictly_upper(K W^T); products with Q and K
     f32x16 g = {};
-    f32x16 s[2];                     // waves 0,1: diagonal logits K Q^T
-    f32x16 qi[2], ki[2];             // Q^T, K^T tiles of the head-dimension tile this wave takes in phase 4b
+    // Accumulators carried into phase 4: waves 0,1 the diagonal logits K Q^T (s), the waves of
+    // phase 4b the Q^T and K^T tiles of their head-dimension tile (qi, ki).  At D = 64 no wave
+    // has both, and s shares qi's registers.
+    f32x16 carry[D == 64 ? 4 : 6];
+    f32x16 *const s = carry, *const qi = D == 64 ? carry : carry + 2, *const ki = qi + 2;
     tile_mma<S, true, true, SPD, SPD>(g, sW, sW, mt, nt, D, lane);
     {
-        // X^T = W Q^T and Y^T = W K^T, stored back transposed (4 contiguous elements per store)
-        f32x16 c = {};
-        tile_mma<S, true, true, SPD, SPD>(c, sW, sQ, mt, nt, D, lane);
-        store_tile_t<S, SP>(sX, c, mt, nt, lane, [](int cc, int i) { return cc <= i; });
-        c = f32x16{};
-        tile_mma<S, true, true, SPD, SPD>(c, sW, sK, mt, nt, D, lane);
-        store_tile_t<S, SP>(sY, c, mt, nt, lane, [](int r, int j) { return r > j; });
+        // The accumulator tile W Q^T (rows c, columns i), read as fragments whose k is the
+        // accumulator row, is X's fragments of row tile nt / 32, k chunks mt / 16 .. (likewise
+        // W K^T and Y).  Tiles wholly outside a triangle are zero: for mt < nt every c <= i and
+        // no r > j, for mt > nt the reverse.
+        const Frag zf = {};
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {  // 0: X, 1: -Y
+            const bool full = which == 0 ? mt < nt : mt > nt, none = which == 0 ? mt > nt : mt < nt;
+            S *dst = which == 0 ? sX : sY;
+            if (none) {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) frag_st<S>(dst, nt >> 5, (mt >> 4) + hf, lane, zf);
+            } else {
+                f32x16 cx = {};
+                tile_mma<S, true, true, SPD, SPD>(cx, sW, which == 0 ? sQ : sK, mt, nt, D, lane);
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int row = mt + 16 * hf + frag_k(e, h), col = nt + l32;
+                        const bool keep = full || (which == 0 ? row <= col : row > col);
+                        const float v = which == 0 ? cx[8 * hf + e] : -cx[8 * hf + e];
+                        x[e] = keep ? v : 0.f;
+                    }
+                    frag_st<S>(dst, nt >> 5, (mt >> 4) + hf, lane, Elem<S>::from_f32(x));
+                }
+            }
+        }
     }
     if (wv < 2) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             s[rt] = f32x16{};
-            tile_mma<S, true, true, SPD, SPD>(s[rt], sK, sQ, 32 * rt, 32 * wv, D, lane);
+            // key tiles after the query tile are wholly masked
+            if (rt <= wv) tile_mma<S, true, true, SPD, SPD>(s[rt], sK, sQ, 32 * rt, 32 * wv, D, lane);
         }
     }
     if (wv >= 2 || D > 64) {
+        // Q^T and K^T tiles (rows d, columns tokens) as products with identity fragments
+        // (exact: one nonzero term per sum)
+        Frag idp[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 16 * hf + frag_k(e, h) == l32 ? 1.f : 0.f;
+            idp[hf] = Elem<S>::from_f32(x);
+        }
         const int dt = D == 64 ? (wv & 1) : (wv ^ 2);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            load_tile_t<S, SPD>(qi[t], sQ, 32 * dt, 32 * t, lane);
-            load_tile_t<S, SPD>(ki[t], sK, 32 * dt, 32 * t, lane);
+            qi[t] = f32x16{};
+            ki[t] = f32x16{};
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                Elem<S>::mma(qi[t], idp[hf], lds_frag<S, true, SPD>(sQ, 32 * t + l32, 32 * dt + 16 * hf, h));
+                Elem<S>::mma(ki[t], idp[hf], lds_frag<S, true, SPD>(sK, 32 * t + l32, 32 * dt + 16 * hf, h));
+            }
         }
     }
     __syncthreads();  // Q, K dead: their space becomes G and E (tiles on or below the diagonal)
@@ -484,7 +510,6 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
         }
     }
     __syncthreads();
-
     // ---- 3. E = (I + strictly_lower(D_b G))^-1 in 16 x 16 tiles, A = E D_b.
     // (a) diagonal tiles, one per wave: column t, rows c = p (mod 4) per lane;
     //     x_r = [r == t] - beta_r sum_{c<r} G_rc x_c (entries not yet known are 0)
@@ -550,7 +575,7 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
         __syncthreads();
     }
     {
-        // A = E D_b (lower triangle only: tiles above the diagonal are not stored).
+        // A = E D_b (lower triangle only: tiles above the diagonal are zero).
         // Thread (column c, 16 rows of row tile wv).
         const int c = tid & 63, rg = 16 * wv;
         const float bc = sBeta[c];
@@ -562,24 +587,24 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
             const float ev = et[e * TP];  // always in bounds; read unconditionally, then selected
             av[e] = (tile_ok && c <= rg + e) ? ev * bc : 0.f;
         }
-        __syncthreads();  // E and G are dead: their space becomes A (fp32) or A^T (bf16) and V^T
-        if constexpr (!kBf) {
+        __syncthreads();  // E and G are dead: their space becomes A, A^T and V^T
+        // -A: rows rg + e, k = c (one element each); A^T: row c, k = rg .. rg + 15 (k chunk wv),
+        // the two lane halves of the row
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sA[(rg + e) * SP + c] = Elem<S>::from_float(av[e]);
-        } else {
+        for (int e = 0; e < 16; ++e) sA[frag_at(rg + e, c)] = Elem<S>::from_float(-av[e]);
 #pragma unroll
-            for (int e = 0; e < 16; e += 8) {
-                const u32x4 u = {pack_bf16(av[e], av[e + 1]), pack_bf16(av[e + 2], av[e + 3]),
-                                 pack_bf16(av[e + 4], av[e + 5]), pack_bf16(av[e + 6], av[e + 7])};
-                lds_store16<S>(sAup + c * SP + rg + e, u);
-            }
+        for (int h2 = 0; h2 < 2; ++h2) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = av[frag_k(e, h2)];
+            frag_st<S>(sAt, c >> 5, wv, (c & 31) + 32 * h2, Elem<S>::from_f32(x));
         }
 #pragma unroll
         for (int s2 = 0; s2 < VPT; ++s2) {
             const int idx = tid + 256 * s2, vr = idx % 64, cw = idx / 64;
             const S *ve = (const S *)&vreg[s2];
 #pragma unroll
-            for (int e = 0; e < CH; ++e) sVt[(cw * CH + e) * SP + vr] = ve[e];
+            for (int e = 0; e < CH; ++e) sVt[frag_at(cw * CH + e, vr)] = ve[e];
             if constexpr (kWtLate) {  // W is dead since phase 2: its slot becomes W^T
                 const S *we = (const S *)&wreg[s2];
 #pragma unroll
@@ -602,53 +627,57 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             zt[rt] = f32x16{};
-            if constexpr (kBf)
-                tile_mma<S, true, true, SP, SP>(zt[rt], sAup, sX, 32 * rt, 32 * ct, 64, lane);
-            else
-                tile_mma<S, false, true, SP, SP>(zt[rt], sA, sX, 32 * rt, 32 * ct, 64, lane);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) zt[rt][r] = -zt[rt][r];
+            for (int kc = 0; kc < 4; ++kc) Elem<S>::mma(zt[rt], frag_ld<S>(sAt, rt, kc, lane), frag_ld<S>(sX, ct, kc, lane));
         }
+        // key tiles rt <= ct only: the later one is wholly masked (P = 0); the mask is needed in
+        // the tile rt = ct alone
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) tile_mma_breg<S, true, SP>(s[rt], sY, 32 * rt, zt, lane);
+        for (int rt = 0; rt < 2; ++rt)
+            if (rt <= ct) tile_mma_fbreg<S>(s[rt], sY, rt, zt, lane);  // sY holds -Y
         const float c2 = a.scale * kLog2e;
         const float cli = FOX ? sCl[i] : 0.f;
         float mx = -INFINITY;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < 2; ++rt) {
+            if (rt > ct) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int j = 32 * rt + acc_row(r, h);
                 float x = s[rt][r] * c2;
                 if (FOX) x += (cli - sCl[j]) * kLog2e;
-                x = j <= i ? x : -INFINITY;
+                if (rt == ct) x = j <= i ? x : -INFINITY;
                 s[rt][r] = x;
                 mx = fmaxf(mx, x);
             }
+        }
         mx = other_half_max(mx);
         float sum = 0.f;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < 2; ++rt) {
+            if (rt > ct) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float p = fast_exp2(s[rt][r] - mx);
                 s[rt][r] = p;
                 sum += p;
             }
+        }
         sum = other_half_sum(sum);
         f32x16 o[DT];
 #pragma unroll
         for (int d2 = 0; d2 < DT; ++d2) o[d2] = f32x16{};
         // each of the two waves stores half of the V^T record: fragments d2 = wv, wv + 2, ...,
         // kept by selects during the products and stored after them (no branch among the products)
-        typename Elem<S>::Frag vkeep[DT / 2][4];
+        Frag vkeep[DT / 2][4];
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
+            const bool live = (kc >> 1) <= ct;
             auto pf = acc_frag<S>(s[kc >> 1], kc & 1);
 #pragma unroll
             for (int d2 = 0; d2 < DT; ++d2) {
-                auto vf = lds_frag<S, true, SP>(sVt, 32 * d2 + l32, 16 * kc, h);
-                Elem<S>::mma(o[d2], vf, pf);
+                const Frag vf = frag_ld<S>(sVt, d2, kc, lane);
+                if (live) Elem<S>::mma(o[d2], vf, pf);
                 if ((d2 & 1) == 0) vkeep[d2 >> 1][kc] = vf;
                 else vkeep[d2 >> 1][kc] = wv == 1 ? vf : vkeep[d2 >> 1][kc];
             }
@@ -658,7 +687,7 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
                 S *dst = recV + ((int64_t)((2 * k2 + wv) * 4 + kc) * 64 + lane) * 8;
-                *(typename Elem<S>::Frag *)dst = vkeep[k2][kc];
+                *(Frag *)dst = vkeep[k2][kc];
             }
         if (h == 0) {
             float *md = (float *)((char *)a.ws + lay.off_mdiag), *ld = (float *)((char *)a.ws + lay.off_ldiag);
@@ -674,45 +703,39 @@ __global__ __launch_bounds__(256, (PrepCfg<S, D>::WG_PER_CU)) void path_prep_ker
         }
     }
     if (wv >= 2 || D > 64) {
-        // ---- 4b. head-dimension tile dt: -U = -A W and -R = -A^T W (rows = block
-        //      token, cols = d), then qhat^T = Q^T - U^T X^T, khat^T = K^T - R^T Y^T
-        //      and (-M)^T = -W^T U, each using those accumulators as operands.
-        //      D = 64: waves 2, 3 take one tile each; D = 128: every wave takes
-        //      one (waves 0, 1 after the diagonal block).
+        // ---- 4b. head-dimension tile dt: -U = (-A) W and R = A^T W (rows = block token,
+        //      cols = d), then qhat^T = Q^T - U^T X^T, khat^T = K^T + R^T (-Y)^T and
+        //      (-M)^T = W^T (-U), each using those accumulators as operands (bf16 reads W^T,
+        //      fp32 reads W with a stride).  D = 64: waves 2, 3 take one tile each; D = 128:
+        //      every wave takes one (waves 0, 1 after the diagonal block).
         const int dt = D == 64 ? (wv & 1) : (wv ^ 2);
         f32x16 nu[2], nr[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             nu[rt] = f32x16{};
             nr[rt] = f32x16{};
-            if constexpr (kBf) {
-                tile_mma<S, false, true, SP, SP>(nu[rt], sAup, sWt, 32 * rt, 32 * dt, 64, lane);
-                tile_mma<S, true, true, SP, SP>(nr[rt], sAup, sWt, 32 * rt, 32 * dt, 64, lane);
-            } else {
-                tile_mma<S, true, false, SP, SPD>(nu[rt], sA, sW, 32 * rt, 32 * dt, 64, lane);
-                tile_mma<S, false, false, SP, SPD>(nr[rt], sA, sW, 32 * rt, 32 * dt, 64, lane);
-            }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                nu[rt][r] = -nu[rt][r];
-                nr[rt][r] = -nr[rt][r];
+            for (int kc = 0; kc < 4; ++kc) {
+                Frag wb;
+                if constexpr (kBf) wb = lds_frag<S, true, SP>(sWt, 32 * dt + l32, 16 * kc, h);
+                else wb = lds_frag<S, false, SPD>(sW, 32 * dt + l32, 16 * kc, h);
+                Elem<S>::mma(nu[rt], frag_ld<S>(sA, rt, kc, lane), wb);
+                Elem<S>::mma(nr[rt], frag_ld<S>(sAt, rt, kc, lane), wb);
             }
         }
         S *gqh = (S *)((char *)a.ws + lay.off_qhat) + (bh * lay.lp + row0) * D;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            tile_mma_areg<S, true, SP>(qi[t], nu, sX, 32 * t, lane);
+            tile_mma_areg_f<S>(qi[t], nu, sX, t, lane);
             store_rows_t<S, D>(gqh, qi[t], 32 * dt, 32 * t + l32, a.scale * kLog2e, lane);  // log2 units
-            tile_mma_areg<S, true, SP>(ki[t], nr, sY, 32 * t, lane);
+            tile_mma_areg_f<S>(ki[t], nr, sY, t, lane);  // sY holds -Y
             store_frags<S>(recK, ki[t], t * KCH + 2 * dt, lane);
         }
 #pragma unroll
         for (int rt2 = 0; rt2 < DT; ++rt2) {
             f32x16 c = {};
-            if constexpr (kBf)
-                tile_mma_breg<S, true, SP>(c, sWt, 32 * rt2, nu, lane);
-            else
-                tile_mma_breg<S, false, SPD>(c, sW, 32 * rt2, nu, lane);
+            if constexpr (kBf) tile_mma_breg<S, true, SP>(c, sWt, 32 * rt2, nu, lane);
+            else tile_mma_breg<S, false, SPD>(c, sW, 32 * rt2, nu, lane);
             store_frags<S>(recM, c, dt * KCH + 2 * rt2, lane);
         }
     }
