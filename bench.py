@@ -454,6 +454,43 @@ def counter_run(fwd_steps=2, dec_steps=2):
         (COPY_BYTES, fwd_steps, dec_steps))
 
 
+def counter_run_sweep():
+    """No timing: the calibration copy (as in counter_run), then one forward (prep + scan) of
+    each other forward workload in SWEEP_WORKLOADS order, then one fused-producer forward of the
+    headline shape, for rocprofv3 --pmc beyond the headline shape (three dispatches per forward:
+    prep, bounded walk, redo)."""
+    import torch
+
+    import attention_fwd_amd as pa
+    import pathgen
+
+    src = torch.ones(COPY_BYTES // 2, device="cuda", dtype=torch.bfloat16)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for name in SWEEP_WORKLOADS:
+        c = pathgen.WORKLOADS[name]
+        x = pathgen.fwd_inputs(c["B"], c["H"], c["L"], c["d"], c["dtype"], seed=0, fox=c["fox"], clip=c["clip"],
+                               device="cuda")
+        out = torch.empty_like(x["q"])
+        lse = torch.empty(x["beta"].shape, device="cuda", dtype=torch.float32)
+        ws = torch.empty(pa.fwd_workspace_size(c["B"], c["H"], c["L"], c["d"], x["q"].dtype), device="cuda",
+                         dtype=torch.uint8)
+        pa.fwd_prep(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out, lse, ws)
+        pa.fwd_scan(out, lse, x["logf"] is not None, ws)
+        torch.cuda.synchronize()
+        del x, out, lse, ws
+        torch.cuda.empty_cache()
+        log("counter run: forward %s" % name)
+    c = pathgen.WORKLOADS[FWD_WORKLOAD]
+    x = pathgen.fused_inputs(c["B"], c["H"], c["L"], c["d"], c["dtype"], seed=0, device="cuda")
+    pa.fwd_fused(x["q"], x["k"], x["v"], x["wraw"], x["conv_w"], x["zbeta"], c["clip"])
+    torch.cuda.synchronize()
+    log("counter run: fused-producer forward %s" % FWD_WORKLOAD)
+
+
 def counter_run_backward():
     """No timing: the calibration copy (as in counter_run), then one forward and one backward
     pass of the forward workload, for rocprofv3 --pmc over the backward kernels."""
@@ -560,6 +597,8 @@ def main():
     ap.add_argument("--backward-only", action="store_true", help="only the backward leg (for kernel traces)")
     ap.add_argument("--counter-run-backward", action="store_true",
                     help="no timing: a calibration copy plus one backward pass, for rocprofv3 --pmc")
+    ap.add_argument("--counter-run-sweep", action="store_true",
+                    help="no timing: one forward of each other workload, for rocprofv3 --pmc")
     ap.add_argument("--counter-run", action="store_true",
                     help="no timing: a calibration copy plus a few forward and decode steps, for rocprofv3 --pmc")
     args = ap.parse_args()
@@ -579,6 +618,9 @@ def main():
         return
     if args.counter_run_backward:
         counter_run_backward()
+        return
+    if args.counter_run_sweep:
+        counter_run_sweep()
         return
     if args.backward_only:
         print(json.dumps({"backward": bench_backward(max(1, args.backward_steps), 1),
