@@ -399,14 +399,20 @@ def bench_backward(steps, warmup, name=FWD_WORKLOAD):
     torch.cuda.empty_cache()
     flops = 8.0 * B * H * L * L * d
     tf = flops / (ms * 1e-3) / 1e12
-    return {"workload": name + " backward", "ms_per_step": round(ms, 3), "flop_per_step": flops,
-            "traffic_note": "HBM bytes of one whole backward pass (all kernels, all passes over the workspace)",
-            "TFLOP_per_s": round(tf, 2), "steps": steps,
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": read_traffic("path_bwd", BWD_TRAFFIC_FILE) if name == FWD_WORKLOAD else None},
-            "heads_per_workspace_pass": int(heads_per_pass),
-            "tokens_per_s": round(B * L / (ms * 1e-3))}
+    traffic = read_traffic("path_bwd", BWD_TRAFFIC_FILE) if name == FWD_WORKLOAD else None
+    res = {"workload": name + " backward", "ms_per_step": round(ms, 3), "flop_per_step": flops,
+           "traffic_note": "HBM bytes of one whole backward pass (all kernels, all passes over the workspace)",
+           "TFLOP_per_s": round(tf, 2), "steps": steps,
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+           "heads_per_workspace_pass": int(heads_per_pass),
+           "tokens_per_s": round(B * L / (ms * 1e-3))}
+    if traffic:
+        # the measured HBM bytes of the pass (counters, while their source hash matches) over its time:
+        # the walks materialise per-pair state, so this rate is the other bound to read the time against
+        gbs = traffic / (ms * 1e-3) / 1e9
+        res["hbm_measured"] = {"GB_per_s": round(gbs, 1), "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return res
 
 
 def counter_run(fwd_steps=2, dec_steps=2):
