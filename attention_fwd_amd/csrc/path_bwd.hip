@@ -745,6 +745,97 @@ __device__ __forceinline__ void dma_record(const void *src, void *dst, int tid) 
 // LDS access of the wave returned.
 constexpr int vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
 
+// Down walk for bf16 inputs at head dimension 64: as bwd_down_kernel (without the q~^T
+// copy), but four query blocks (eight waves, two per block) share each key block's
+// transition T - I (8 KiB), copied global -> LDS one step ahead (global_load_lds,
+// double-buffered), as in the up walk below.  The tile walks J = Imax - 1 .. 0; a wave
+// joins at J = I - 1.  Every step issues the same memory operations on every wave (the
+// next copy, the next gate total, the stores of q~ and of the gate sum, to a spare target
+// when the wave has nothing to store), so that one wait at the top of a step covers every
+// path.
+__global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_down_kernel_lds(BwdArgs a) {
+    typedef uint16_t S;
+    typedef Elem<S>::Frag Frag;
+    constexpr int D = 64, KCD = D / 16, RTD = D / 32, NTH = 64 * 2 * kUpQB;
+    constexpr int REC = D * D;               // elements of a transition
+    constexpr int NLD = REC * 2 / 16 / NTH;  // DMA chunks per thread and transition
+    static_assert(REC * 2 % (16 * NTH) == 0, "transition must split evenly over the workgroup");
+    constexpr int NST = KCD + 1;  // global stores of one step: the q~ fragments and the gate sum
+    constexpr int BUF = REC * 2;  // bytes per buffer
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int nb = a.nb, hc = a.hc;
+    const int ntile = (nb - 1 + kUpQB - 1) / kUpQB;  // query blocks 1 .. nb-1, four per tile
+    const int gl = blockIdx.x % hc, tile = ntile - 1 - blockIdx.x / hc;
+    const int I0 = 1 + kUpQB * tile, Imax = min(nb - 1, I0 + kUpQB - 1);
+    const int I = __builtin_amdgcn_readfirstlane(I0 + (w >> 1)), wq = __builtin_amdgcn_readfirstlane(w & 1);
+    const bool active = I <= nb - 1;
+    const int Ic = active ? I : Imax;  // idle waves carry a valid block and discard it
+    const BwdLayout &ly = a.ly;
+    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
+    const S *NT = (const S *)(ws + ly.nt);
+    const float *tot = (const float *)(ws + ly.tot);
+    float *MID = (float *)(ws + ly.mid);
+    S *QS1 = (S *)(ws + ly.qs1);
+    // the spare fragment set after the last pair's G (written before the up walk fills it)
+    S *const spare = (S *)(ws + ly.gs2) + (int64_t)nb * (nb - 1) / 2 * kC * D;
+    float *const mspare = (float *)spare;
+
+    auto issue = [&](int J, int B) { dma_record<NTH, NLD>(NT + (int64_t)J * REC, smem + B * BUF, tid); };
+    const int Jtop = Imax - 1;
+    issue(Jtop, 0);
+    f32x16 qt[RTD];
+    {
+        const float *qh = (const float *)(ws + ly.qh) + (int64_t)(Ic * kC + 32 * wq + l32) * D;
+#pragma unroll
+        for (int dt = 0; dt < RTD; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(qh + 32 * dt + 8 * g4 + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qt[dt][4 * g4 + e] = x[e];
+            }
+    }
+    float tcur = tot[Jtop];  // gate total of the step's key block, loaded one step ahead
+    float mid = 0.f;         // gate sum over the blocks strictly between I and the step's J
+    asm volatile("" ::: "memory");  // the wait below stays after these loads
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
+    auto step = [&](int J, auto bsel) {
+        constexpr int B = decltype(bsel)::value;
+        const S *nt = (const S *)(smem + B * BUF);
+        // this wave's copy of T_J - I and its gate-total load have landed (only the previous
+        // step's stores may still be in flight); after the barrier every wave's copies have
+        // landed and every wave is done with the other buffer
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0(NST));
+        asm volatile("s_barrier" ::: "memory");
+        issue(max(J - 1, 0), 1 - B);
+        const float tnext = tot[max(J - 1, 0)];
+        asm volatile("" ::: "memory");  // the loads stay ahead of this step's stores
+        const bool act = active && J <= I - 1;
+        Frag qf[KCD];
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) qf[kc] = acc_frag<S>(qt[kc >> 1], kc & 1);
+        S *dst = act ? QS1 + pair_index(I, J) * kC * D : spare;
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) stfrag<S>(dst, wq, kc, KCD, lane, qf[kc]);
+        // every lane stores the same value (one store instruction, no branch)
+        *((act && wq == 0) ? MID + pair_index(I, J) : mspare) = mid;
+        if (act && J >= 1) {
+#pragma unroll
+            for (int dt = 0; dt < RTD; ++dt)
+#pragma unroll
+                for (int kc = 0; kc < KCD; ++kc) Elem<S>::mma(qt[dt], ldfrag<S>(nt, dt, kc, KCD, lane), qf[kc]);
+        }
+        if (act) mid += tcur;
+        tcur = tnext;
+    };
+    for (int J = Jtop; J >= 0; J -= 2) {
+        step(J, std::integral_constant<int, 0>{});
+        if (J >= 1) step(J - 1, std::integral_constant<int, 1>{});
+    }
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));  // no copy may still be landing in LDS when the workgroup leaves
+}
+
 __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_lds(BwdArgs a) {
     typedef uint16_t S;
     typedef Elem<S>::Frag Frag;
@@ -1577,8 +1668,8 @@ hipError_t launch_bwd_t(const BwdArgs &a0, hipStream_t st) {
         if (a.nb > 1) {
             const dim3 walks((unsigned)((a.nb - 1) * a.hc));
             if constexpr (sizeof(T) == 2 && D == 64) {
-                hipLaunchKernelGGL((bwd_down_kernel<T, D, false>), walks, dim3(128), 0, st, a);
                 const dim3 tiles((unsigned)((a.nb - 1 + kUpQB - 1) / kUpQB * a.hc));
+                hipLaunchKernelGGL(bwd_down_kernel_lds, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
                 hipLaunchKernelGGL(bwd_up_kernel_lds, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
                 hipLaunchKernelGGL(bwd_key_kernel_lds, walks, dim3(256), 0, st, a);
             } else {
