@@ -455,27 +455,39 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 
 // Per-wave LDS scratch for writing an accumulator tile set (rows d, columns the
-// wave's 32 queries) back as fragments with the query index inside the lane.
-constexpr int kXs = 36;  // row stride (floats): rows 16-byte aligned
+// wave's 32 queries) back as fragments with the query index inside the lane.  It
+// holds the element type: each value is rounded before it is transposed, which
+// gives the same fragments.
+template <typename S>
+struct XScr {
+    static constexpr int kStride = sizeof(S) == 2 ? 40 : 36;  // row stride (elements): rows 16- (fp32) or 8-byte aligned
+};
 
 // acc tiles t[dt] (rows d = 32 dt + acc_row(r, h), columns this wave's 32 queries) ->
 // fragments (rt = dt, kc = 2 w + 0/1) of a set with rows d and k over the block's 64 queries.
 // Only this wave touches x, and a wave's LDS accesses are performed in order.
 template <typename S, int D>
-__device__ __forceinline__ void store_transposed(S *dst, const f32x16 *t, float *x, int w, int lane) {
+__device__ __forceinline__ void store_transposed(S *dst, const f32x16 *t, S *x, int w, int lane) {
+    typedef typename Elem<S>::Frag Frag;
+    constexpr int XS = XScr<S>::kStride;
     const int h = lane >> 5, l32 = lane & 31;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[(32 * dt + acc_row(r, h)) * kXs + l32] = t[dt][r];
+        for (int r = 0; r < 16; ++r) x[(32 * dt + acc_row(r, h)) * XS + l32] = Elem<S>::from_float(t[dt][r]);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int kcl = 0; kcl < 2; ++kcl) {
-            const float *src = x + (32 * dt + l32) * kXs + 16 * kcl + 4 * h;
-            const f32x4 lo = *reinterpret_cast<const f32x4 *>(src), hi = *reinterpret_cast<const f32x4 *>(src + 8);
-            const float y[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            stfrag<S>(dst, dt, 2 * w + kcl, 4, lane, Elem<S>::from_f32(y));
+            const S *src = x + (32 * dt + l32) * XS + 16 * kcl + 4 * h;
+            if constexpr (sizeof(S) == 2) {
+                const u32x2 lo = *reinterpret_cast<const u32x2 *>(src), hi = *reinterpret_cast<const u32x2 *>(src + 8);
+                stfrag<S>(dst, dt, 2 * w + kcl, 4, lane, __builtin_bit_cast(Frag, u32x4{lo.x, lo.y, hi.x, hi.y}));
+            } else {
+                const f32x4 lo = *reinterpret_cast<const f32x4 *>(src), hi = *reinterpret_cast<const f32x4 *>(src + 8);
+                const float y[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                stfrag<S>(dst, dt, 2 * w + kcl, 4, lane, Elem<S>::from_f32(y));
+            }
         }
 }
 
@@ -485,10 +497,10 @@ __device__ __forceinline__ void store_transposed(S *dst, const f32x16 *t, float 
 // queries (for the logits) and, with Q2, with rows d (for the key walk's sums
 // over queries), with the gate sum of the blocks strictly between I and J.
 template <typename S, int D, bool Q2>
-__global__ __launch_bounds__(128) void bwd_down_kernel(BwdArgs a) {
+__global__ __launch_bounds__(128, (D == 128 && sizeof(S) == 2) ? 3 : 1) void bwd_down_kernel(BwdArgs a) {
     typedef typename Elem<S>::Frag Frag;
     constexpr int KCD = D / 16, RTD = D / 32;
-    __shared__ __attribute__((aligned(16))) float sx[2][D * kXs];
+    __shared__ __attribute__((aligned(16))) S sx[2][D * XScr<S>::kStride];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int nb = a.nb, hc = a.hc;
     const int gl = blockIdx.x % hc, I = nb - 1 - blockIdx.x / hc;
@@ -541,10 +553,10 @@ __global__ __launch_bounds__(128) void bwd_down_kernel(BwdArgs a) {
 // accumulators) G^T <- G^T + (T_J - I)^T G^T + K^_J^T (scale dS^T).  G^(J) is
 // stored with rows d for the pair (I, J + 1); G^(I-1) = dq^_I.
 template <typename S, int D>
-__global__ __launch_bounds__(128) void bwd_up_kernel(BwdArgs a) {
+__global__ __launch_bounds__(128, (D == 128 && sizeof(S) == 2) ? 2 : 1) void bwd_up_kernel(BwdArgs a) {
     typedef typename Elem<S>::Frag Frag;
     constexpr int KCD = D / 16, RTD = D / 32;
-    __shared__ __attribute__((aligned(16))) float sx[2][D * kXs];
+    __shared__ __attribute__((aligned(16))) S sx[2][D * XScr<S>::kStride];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int nb = a.nb, hc = a.hc;
     const int gl = blockIdx.x % hc, I = nb - 1 - blockIdx.x / hc;
