@@ -113,6 +113,74 @@ __device__ __forceinline__ void mm(f32x8 &acc, LMat A, LMat B, int lane, int wav
     acc.hi = hi;
 }
 
+// The same product for bf16 inputs on v_mfma_f32_16x16x32_bf16 (16 times the rate of the
+// fp32 shape).  An operand marked exact (EA, EB) holds bf16 numbers (a tile loaded from the
+// bf16 inputs) and is converted without loss; any other operand x is split as hi + lo, two
+// bf16 numbers (hi = x rounded, lo = the rest rounded), and the product takes hi*hi + hi*lo +
+// lo*hi: about 16 significant bits per operand, fp32 accumulation.  Lane l supplies k =
+// 32 s + 8 (l / 16) + t, t = 0..7, at step s, the same order for both operands; the
+// accumulator layout is that of mm.
+__device__ __forceinline__ void ld8(float *x, LMat M, int row, int k0, bool kc) {
+    // element (row, k0 + t); kc: k is contiguous in LDS (two 16-byte loads)
+    if (kc) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(M.p + row * M.rs + k0);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(M.p + row * M.rs + k0 + 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            x[t] = a[t];
+            x[4 + t] = b[t];
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[t] = M.p[row * M.rs + (k0 + t) * M.cs];
+    }
+}
+template <bool EXACT>
+__device__ __forceinline__ void split8(const float *x, i16x8 &hi, i16x8 &lo) {
+    u32x4 uh, ul;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        uh[t] = pack_bf16(x[2 * t], x[2 * t + 1]);
+        if constexpr (!EXACT) {
+            const float h0 = __uint_as_float(uh[t] << 16), h1 = __uint_as_float(uh[t] & 0xffff0000u);
+            ul[t] = pack_bf16(x[2 * t] - h0, x[2 * t + 1] - h1);
+        }
+    }
+    hi = __builtin_bit_cast(i16x8, uh);
+    if constexpr (!EXACT) lo = __builtin_bit_cast(i16x8, ul);
+}
+template <bool EA, bool EB>
+__device__ __forceinline__ void mmb(f32x8 &acc, LMat A, LMat B, int lane, int wave) {
+    const int r = 16 * (wave >> 1) + (lane & 15), c0 = 32 * (wave & 1) + (lane & 15), q = lane >> 4;
+    f32x4 lo = acc.lo, hi = acc.hi;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const int k0 = 32 * st + 8 * q;
+        float x[8], y[8];
+        i16x8 ah, al, bh, bl;
+        ld8(x, A, r, k0, A.cs == 1);
+        split8<EA>(x, ah, al);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            // B element (k, c) at k * rs + c * cs: the transposed view of ld8
+            ld8(y, LMat{B.p, B.cs, B.rs}, c0 + 16 * ct, k0, B.rs == 1);
+            split8<EB>(y, bh, bl);
+            f32x4 &c = ct == 0 ? lo : hi;
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+            if constexpr (!EB) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+            if constexpr (!EA) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+        }
+    }
+    acc.lo = lo;
+    acc.hi = hi;
+}
+// mm for fp32 inputs, mmb for bf16 inputs (EA, EB: the operand is a tile of bf16 input values)
+template <typename T, bool EA, bool EB>
+__device__ __forceinline__ void mmx(f32x8 &acc, LMat A, LMat B, int lane, int wave) {
+    if constexpr (sizeof(T) == 2) mmb<EA, EB>(acc, A, B, lane, wave);
+    else mm(acc, A, B, lane, wave);
+}
+
 __device__ __forceinline__ f32x8 zero8() {
     f32x8 z;
 #pragma unroll
@@ -313,10 +381,10 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
         in2l(bQ, q, D, 64 * c, row0, L, tid);
         in2l(bK, k, D, 64 * c, row0, L, tid);
         __syncthreads();
-        mm(aG, nat(bW), tr(bW), lane, wave);
-        mm(aQW, nat(bQ), tr(bW), lane, wave);
-        mm(aN, nat(bK), tr(bW), lane, wave);
-        mm(aQK, nat(bQ), tr(bK), lane, wave);
+        mmx<T, true, true>(aG, nat(bW), tr(bW), lane, wave);
+        mmx<T, true, true>(aQW, nat(bQ), tr(bW), lane, wave);
+        mmx<T, true, true>(aN, nat(bK), tr(bW), lane, wave);
+        mmx<T, true, true>(aQK, nat(bQ), tr(bK), lane, wave);
     }
     store_lds(bG, aG, lane, wave, Id());
     store_lds(bQW, aQW, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });  // Q W^T, r <= i
@@ -340,17 +408,17 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     }
     __syncthreads();
     f32x8 acc = zero8();
-    mm(acc, nat(bQW), tr(bA), lane, wave);  // Z = QWm A^T
+    mmx<T, false, false>(acc, nat(bQW), tr(bA), lane, wave);  // Z = QWm A^T
     store_lds(bZ, acc, lane, wave, Id());
     acc = zero8();
-    mm(acc, nat(bN), nat(bA), lane, wave);  // Y = N A
+    mmx<T, false, false>(acc, nat(bN), nat(bA), lane, wave);  // Y = N A
     store_lds(bY, acc, lane, wave, Id());
     __syncthreads();
     l2g((float *)(ws + ly.zz) + tok, kC, bZ, tid);
     // diagonal block: P = exp(scale (Q K^T - Z N^T) + cl_i - cl_j - lse_i) for j <= i  (G is dead: P -> bG)
     {
         f32x8 sZN = zero8();
-        mm(sZN, nat(bZ), tr(bN), lane, wave);
+        mmx<T, false, false>(sZN, nat(bZ), tr(bN), lane, wave);
 #pragma unroll
         for (int vv = 0; vv < 8; ++vv) {
             const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
@@ -365,7 +433,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
         in2l(bQ, dout, D, 64 * c, row0, L, tid);
         in2l(bK, v, D, 64 * c, row0, L, tid);
         __syncthreads();
-        mm(aDP, nat(bQ), tr(bK), lane, wave);
+        mmx<T, true, true>(aDP, nat(bQ), tr(bK), lane, wave);
     }
     store_lds(bQW, aDP, lane, wave, [&](int r, int c, float x) { return bG[r * kP + c] * (x - sDD[r]); });
     __syncthreads();
@@ -405,9 +473,9 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
         __syncthreads();
         {
             f32x8 zw = zero8(), yw = zero8(), aw = zero8();
-            mm(zw, nat(bZ), nat(bW), lane, wave);
-            mm(yw, nat(bY), nat(bW), lane, wave);
-            mm(aw, nat(bA), nat(bW), lane, wave);
+            mmx<T, false, true>(zw, nat(bZ), nat(bW), lane, wave);
+            mmx<T, false, true>(yw, nat(bY), nat(bW), lane, wave);
+            mmx<T, false, true>(aw, nat(bA), nat(bW), lane, wave);
             float *QH = (float *)(ws + ly.qh) + (int64_t)row0 * D + 64 * c;
 #pragma unroll
             for (int vv = 0; vv < 8; ++vv) {  // each element read and rewritten by the same thread
@@ -428,7 +496,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
         tile2frag<S, false>(DO1, KCD, 0, 4 * c, bK, tid);  // dO: rows queries
         tile2frag<S, true>(DO2, 4, 2 * c, 0, bK, tid);     // dO^T: rows d
         acc = zero8();
-        mm(acc, tr(bG), nat(bK), lane, wave);  // diagonal value gradient P^T dO
+        mmx<T, false, true>(acc, tr(bG), nat(bK), lane, wave);  // diagonal value gradient P^T dO
         acc2g((float *)(ws + ly.dvd) + (int64_t)row0 * D + 64 * c, D, acc, lane, wave);
     }
     // T - I = -W^T (A W) and its transpose, block (c1, c2) = rows of chunk c1, columns of chunk c2
@@ -439,7 +507,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
         __syncthreads();
         for (int c2 = 0; c2 < NCH; ++c2) {
             acc = zero8();
-            mm(acc, tr(bW), nat(bAW[c2]), lane, wave);
+            mmx<T, true, false>(acc, tr(bW), nat(bAW[c2]), lane, wave);
             store_lds(bQ, acc, lane, wave, [](int, int, float x) { return -x; });
             __syncthreads();
             tile2frag<S, false>(NT, KCD, 2 * c1, 4 * c2, bQ, tid);  // (T - I): rows d_out, k over d_in
@@ -1295,8 +1363,8 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
     __syncthreads();
     // ---- token-level quantities
     f32x8 aZ = zero8(), aNn = zero8(), aY = zero8(), aG = zero8(), aA = zero8(), acc;
-    mm(aZ, nat(bE), nat(bN), lane, wave);    // E N         (dZ = -(E N + dq^ W^T))
-    mm(aNn, tr(bE), nat(bZ), lane, wave);    // E^T Z       (dN = -E^T Z + dY A^T)
+    mmx<T, false, false>(aZ, nat(bE), nat(bN), lane, wave);    // E N         (dZ = -(E N + dq^ W^T))
+    mmx<T, false, false>(aNn, tr(bE), nat(bZ), lane, wave);    // E^T Z       (dN = -E^T Z + dY A^T)
     for (int c = 0; c < NCH; ++c) {
         __syncthreads();
         in2l(b6, w, D, 64 * c, row0, L, tid);
@@ -1305,9 +1373,9 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
         if (hasK) g2l(b8, dko + 64 * c, D, tid);
         else zero_lds(b8, tid);
         __syncthreads();
-        mm(aZ, nat(b7), tr(b6), lane, wave);  // + dq^ W^T
-        mm(aY, nat(b8), tr(b6), lane, wave);  // dk^ W^T   (dY = -dk^ W^T)
-        mm(aG, nat(b6), tr(b6), lane, wave);  // G = W W^T
+        mmx<T, false, true>(aZ, nat(b7), tr(b6), lane, wave);  // + dq^ W^T
+        mmx<T, false, true>(aY, nat(b8), tr(b6), lane, wave);  // dk^ W^T   (dY = -dk^ W^T)
+        mmx<T, true, true>(aG, nat(b6), tr(b6), lane, wave);  // G = W W^T
     }
     if (hasT) {
         // U = W dT and V' = W dT^T (64 x D, for the backward through T = I - W^T A W) and
@@ -1322,8 +1390,8 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
                 g2l(b7, dtt + (int64_t)(64 * c) * D + 64 * c2, D, tid);   // dT^T block (c, c2)
                 g2l(b8, dtt + (int64_t)(64 * c2) * D + 64 * c, D, tid);   // dT^T block (c2, c)
                 __syncthreads();
-                mm(aU, nat(b6), tr(b7), lane, wave);  // W_c2 dT[c2, c]
-                mm(aV, nat(b6), nat(b8), lane, wave);  // W_c2 dT^T[c2, c]
+                mmx<T, true, false>(aU, nat(b6), tr(b7), lane, wave);  // W_c2 dT[c2, c]
+                mmx<T, true, false>(aV, nat(b6), nat(b8), lane, wave);  // W_c2 dT^T[c2, c]
             }
             acc2g(uu + 64 * c, D, aU, lane, wave);
             acc2g(vv + 64 * c, D, aV, lane, wave);
@@ -1332,7 +1400,7 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
             in2l(b6, w, D, 64 * c, row0, L, tid);
             __syncthreads();
             acc = zero8();
-            mm(acc, nat(b7), tr(b6), lane, wave);  // U_c W_c^T
+            mmx<T, false, true>(acc, nat(b7), tr(b6), lane, wave);  // U_c W_c^T
 #pragma unroll
             for (int v = 0; v < 8; ++v) aA[v] -= acc[v];  // dA = -W dT W^T + ...
         }
@@ -1343,13 +1411,13 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
     __syncthreads();
 #pragma unroll
     for (int v = 0; v < 8; ++v) aNn[v] = -aNn[v];
-    mm(aNn, nat(b6), tr(bA), lane, wave);   // dN = -E^T Z + dY A^T
-    mm(aA, tr(bN), nat(b6), lane, wave);    // dA += N^T dY
-    mm(aA, tr(b7), nat(bQW), lane, wave);   // dA += dZ^T QWm
+    mmx<T, false, false>(aNn, nat(b6), tr(bA), lane, wave);   // dN = -E^T Z + dY A^T
+    mmx<T, false, false>(aA, tr(bN), nat(b6), lane, wave);    // dA += N^T dY
+    mmx<T, false, false>(aA, tr(b7), nat(bQW), lane, wave);   // dA += dZ^T QWm
     acc = zero8();
-    mm(acc, nat(b7), nat(bA), lane, wave);  // dQWm = (dZ A) o [r <= i]
+    mmx<T, false, false>(acc, nat(b7), nat(bA), lane, wave);  // dQWm = (dZ A) o [r <= i]
     f32x8 aYv = zero8();
-    mm(aYv, nat(bN), nat(bA), lane, wave);  // Y = N A
+    mmx<T, false, false>(aYv, nat(bN), nat(bA), lane, wave);  // Y = N A
     __syncthreads();
     store_lds(b8, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });  // dQWm
     store_lds(b6, aNn, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });   // dKW = dN o [r > j]
@@ -1367,12 +1435,12 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
     if (tid < kC)
         for (int r = 0; r < kC; ++r) dbeta += bQW[r * kP + tid];
     acc = zero8();
-    mm(acc, tr(bX), nat(b7), lane, wave);  // X^T dX
+    mmx<T, false, false>(acc, tr(bX), nat(b7), lane, wave);  // X^T dX
     __syncthreads();
     store_lds(bQW, acc, lane, wave, Id());
     __syncthreads();
     f32x8 dTp = zero8();
-    mm(dTp, nat(bQW), tr(bX), lane, wave);  // (X^T dX) X^T; dT' is its negative
+    mmx<T, false, false>(dTp, nat(bQW), tr(bX), lane, wave);  // (X^T dX) X^T; dT' is its negative
     __syncthreads();
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
@@ -1398,17 +1466,17 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
         in2l(bX, k, D, 64 * c, row0, L, tid);
         in2l(bQW, q, D, 64 * c, row0, L, tid);
         __syncthreads();
-        mm(dQ, nat(bE), nat(bX), lane, wave);   // E K
-        mm(dK, tr(bE), nat(bQW), lane, wave);   // E^T Q
-        mm(dW, tr(b6), nat(bX), lane, wave);    // dKW^T K
-        mm(dW, tr(b8), nat(bQW), lane, wave);   // dQWm^T Q
+        mmx<T, false, true>(dQ, nat(bE), nat(bX), lane, wave);   // E K
+        mmx<T, false, true>(dK, tr(bE), nat(bQW), lane, wave);   // E^T Q
+        mmx<T, false, true>(dW, tr(b6), nat(bX), lane, wave);    // dKW^T K
+        mmx<T, false, true>(dW, tr(b8), nat(bQW), lane, wave);   // dQWm^T Q
         __syncthreads();
         in2l(bX, w, D, 64 * c, row0, L, tid);
         __syncthreads();
-        mm(dQ, nat(b8), nat(bX), lane, wave);   // dQWm W
-        mm(dK, nat(b6), nat(bX), lane, wave);   // dKW W
-        mm(dW, nat(b7), nat(bX), lane, wave);   // (dG + dG^T) W
-        mm(dW, tr(b7), nat(bX), lane, wave);
+        mmx<T, false, true>(dQ, nat(b8), nat(bX), lane, wave);   // dQWm W
+        mmx<T, false, true>(dK, nat(b6), nat(bX), lane, wave);   // dKW W
+        mmx<T, false, true>(dW, nat(b7), nat(bX), lane, wave);   // (dG + dG^T) W
+        mmx<T, false, true>(dW, tr(b7), nat(bX), lane, wave);
         __syncthreads();
         if (hasQ) g2l(bX, dqo + 64 * c, D, tid);
         else zero_lds(bX, tid);
@@ -1416,8 +1484,8 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
         else zero_lds(bQW, tid);
         __syncthreads();
         acc = zero8();
-        mm(acc, tr(bZ), nat(bX), lane, wave);   // Z^T dq^
-        mm(acc, tr(bN), nat(bQW), lane, wave);  // + Y^T dk^ (= A^T N^T dk^)
+        mmx<T, false, false>(acc, tr(bZ), nat(bX), lane, wave);   // Z^T dq^
+        mmx<T, false, false>(acc, tr(bN), nat(bQW), lane, wave);  // + Y^T dk^ (= A^T N^T dk^)
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
             const int r = arow(v, lane, wave), cc = acol(v, lane, wave);
@@ -1431,8 +1499,8 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
             g2l(bQW, vvp + 64 * c, D, tid);
             __syncthreads();
             acc = zero8();
-            mm(acc, nat(bA), nat(bQW), lane, wave);  // A W dT^T
-            mm(acc, tr(bA), nat(bX), lane, wave);    // + A^T W dT
+            mmx<T, false, false>(acc, nat(bA), nat(bQW), lane, wave);  // A W dT^T
+            mmx<T, false, false>(acc, tr(bA), nat(bX), lane, wave);    // + A^T W dT
 #pragma unroll
             for (int v = 0; v < 8; ++v) dW[v] -= acc[v];
         }
