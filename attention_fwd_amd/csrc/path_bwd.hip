@@ -1551,26 +1551,38 @@ __global__ __launch_bounds__(kT) void bwd_gate_kernel(BwdArgs a) {
     }
 }
 
-// Key walk for bf16 inputs at head dimension 64: as bwd_key_kernel (four waves:
-// query half qt = w & 1, key half kt = w >> 1), but each step's operands -- the
-// pair's q~ (rows queries) and G^T, the query block's dO in both orientations, its
-// exponent terms and the pair's gate sum: 32.8 KiB -- are copied global -> LDS one
-// step ahead (global_load_lds, double-buffered) and read by every wave from there.
-// The q~^T fragments (rows d, k over queries) are gathered from the q~ copy with
-// 2-byte LDS reads, so the down walk stores q~ in one orientation only.
-__global__ __launch_bounds__(256) void bwd_key_kernel_lds(BwdArgs a) {
+// Key walk for bf16 inputs: as bwd_key_kernel (the same waves: query half qt = w & 1,
+// key half kt = (w >> 1) & 1, head-dimension group dh = w >> 2), but each step's
+// operands -- the pair's q~ (rows queries) and G^T, the query block's dO in both
+// orientations, its exponent terms and the pair's gate sum: 32.8 KiB at d = 64, 64.8
+// KiB at d = 128 -- are copied global -> LDS one step ahead (global_load_lds,
+// double-buffered) and read by every wave from there.  The q~^T fragments (rows d, k
+// over queries) are gathered from the q~ copy with 2-byte LDS reads, so the down walk
+// stores q~ in one orientation only.  At d = 128 the registers do not hold k^ and V of
+// the key tile besides the accumulators: they are read from an LDS copy, and dO^T is
+// gathered from the dO copy like q~^T (the buffers then hold q~, G^T and dO: 48.8 KiB).
+template <int D>
+__global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs a) {
     typedef uint16_t S;
     typedef Elem<S>::Frag Frag;
-    constexpr int D = 64, KCD = D / 16, RTD = D / 32, NTH = 256;
+    typedef KeyCfg<D> K;
+    constexpr int KCD = D / 16, RTD = D / 32, RTW = K::RTW, NTH = 64 * K::NW;
+    static_assert(K::TRW == 1, "one row tile of dT per wave");
+    constexpr int NACC = 2 * RTW + RTD;      // dV^T, dk^^T (RTW each), dT row tile grp (RTD column tiles)
+    constexpr bool KVL = D == 128;           // k^, V from LDS; dO^T gathered from dO
+    constexpr int NSET = KVL ? 3 : 4;        // fragment sets per buffer
     constexpr int FR = kC * D;               // elements of a 64 x D fragment set
     constexpr int NLD = FR * 2 / 16 / NTH;   // 16-byte copies per thread and fragment set
     static_assert(FR * 2 % (16 * NTH) == 0, "a fragment set must split evenly over the workgroup");
-    // a buffer: q~, G^T, dO (rows queries), dO^T (rows d), then 64 floats each of the query
-    // terms dd and cq and of the gate sum (the same value 64 times)
-    constexpr int BUF = 4 * FR * 2 + 3 * 4 * kC;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+    // a buffer: q~, G^T, dO (rows queries), [dO^T (rows d)], then 64 floats each of the query
+    // terms dd and cq and of the gate sum (the same value 64 times); with KVL, k^ and V of the
+    // key block after the two buffers
+    constexpr int BUF = NSET * FR * 2 + 3 * 4 * kC;
+    constexpr int KVB = KVL ? 2 * FR * 2 : 0;
+    static_assert(K::NW / 2 * 16 * 65 * 4 <= 2 * BUF, "the final reduction reuses the buffers");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF + KVB];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-    const int qt = w & 1, kt = w >> 1;
+    const int qt = w & 1, kt = (w >> 1) & 1, dh = w >> 2, grp = kt + 2 * dh;
     const int nb = a.nb, hc = a.hc;
     const int gl = blockIdx.x % hc, J = blockIdx.x / hc;
     const BwdLayout &ly = a.ly;
@@ -1591,23 +1603,27 @@ __global__ __launch_bounds__(256) void bwd_key_kernel_lds(BwdArgs a) {
         dma_record<NTH, NLD>(QS1 + po, buf, tid);
         dma_record<NTH, NLD>(GS2 + po, buf + FR * 2, tid);
         dma_record<NTH, NLD>(DO1 + bo, buf + 2 * FR * 2, tid);
-        dma_record<NTH, NLD>(DO2 + bo, buf + 3 * FR * 2, tid);
+        if constexpr (!KVL) dma_record<NTH, NLD>(DO2 + bo, buf + 3 * FR * 2, tid);
         const float *src = w == 0 ? DD + I * kC + lane : w == 1 ? CQL + I * kC + lane : MID + pair_index(I, J);
-        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(buf + 4 * FR * 2 + 4 * kC * min(w, 2)), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(buf + NSET * FR * 2 + 4 * kC * min(w, 2)), 4, 0,
+                                         0);
     };
+    const S *rec = (const S *)(ws + ly.urec) + J * ly.rec_elems;  // k^ (rows keys, k over d), then V
+    const S *skv = (const S *)(smem + 2 * BUF);
+    if constexpr (KVL) dma_record<NTH, 2 * NLD>(rec, smem + 2 * BUF, tid);
     issue(J + 1, 0);
-    Frag kf[KCD], vf[KCD];  // k^ and V of key tile kt, k over d: the B operands of S and dP
-    {
-        const S *rec = (const S *)(ws + ly.urec) + J * ly.rec_elems;
+    // k^ and V of key tile kt, k over d: the B operands of S and dP (registers, or the LDS copy)
+    Frag kf[KVL ? 1 : KCD], vf[KVL ? 1 : KCD];
+    if constexpr (!KVL) {
 #pragma unroll
         for (int kc = 0; kc < KCD; ++kc) {
             kf[kc] = ldfrag<S>(rec, kt, kc, KCD, lane);
             vf[kc] = ldfrag<S>(rec + kC * D, kt, kc, KCD, lane);
         }
     }
-    f32x16 acc[6];  // dV^T (2 row tiles of d), dk^^T (2), dT rows 32 kt .. (2 column tiles)
+    f32x16 acc[NACC];
 #pragma unroll
-    for (int t = 0; t < 6; ++t) acc[t] = f32x16{};
+    for (int t = 0; t < NACC; ++t) acc[t] = f32x16{};
     float csum = 0.f;
     // q~^T fragment (rows d = 32 ct + lane % 32, k over queries 16 kq ..) gathered from the q~ copy:
     // element e of a lane is q~[16 kq + 8 (e >> 2) + 4 h + (e & 3)][d], which sits in the q~
@@ -1628,7 +1644,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel_lds(BwdArgs a) {
         constexpr int B = decltype(bsel)::value;
         const unsigned char *buf = smem + B * BUF;
         const S *sq = (const S *)buf, *sg = sq + FR, *so1 = sq + 2 * FR, *so2 = sq + 3 * FR;
-        const float *sdd = (const float *)(buf + 4 * FR * 2), *scq = sdd + kC, *smid = scq + kC;
+        const float *sdd = (const float *)(buf + NSET * FR * 2), *scq = sdd + kC, *smid = scq + kC;
         // this wave's copies of step I have landed and its LDS reads of the previous step have
         // returned; after the barrier every wave's copies have landed and the other buffer is free
         __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
@@ -1638,8 +1654,10 @@ __global__ __launch_bounds__(256) void bwd_key_kernel_lds(BwdArgs a) {
         f32x16 s = {}, dp = {};
 #pragma unroll
         for (int kc = 0; kc < KCD; ++kc) {
-            Elem<S>::mma(s, ldfrag<S>(sq, qt, kc, KCD, lane), kf[kc]);
-            Elem<S>::mma(dp, ldfrag<S>(so1, qt, kc, KCD, lane), vf[kc]);
+            const Frag kb = KVL ? ldfrag<S>(skv, kt, kc, KCD, lane) : kf[KVL ? 0 : kc];
+            const Frag vb = KVL ? ldfrag<S>(skv + FR, kt, kc, KCD, lane) : vf[KVL ? 0 : kc];
+            Elem<S>::mma(s, ldfrag<S>(sq, qt, kc, KCD, lane), kb);
+            Elem<S>::mma(dp, ldfrag<S>(so1, qt, kc, KCD, lane), vb);
         }
         const float mid = smid[0];
         // P and dS (rows: queries 32 qt + acc_row(r, h) of block I; column: this lane's key)
@@ -1657,27 +1675,35 @@ __global__ __launch_bounds__(256) void bwd_key_kernel_lds(BwdArgs a) {
                 dp[r] = P;
             }
         }
-        Frag pf[2], sf[2], q2[RTD][2];
+        Frag pf[2], sf[2];
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             pf[cc] = acc_frag<S>(dp, cc);
             sf[cc] = acc_frag<S>(s, cc);
-#pragma unroll
-            for (int ct = 0; ct < RTD; ++ct) q2[ct][cc] = gather_qt(sq, ct, 2 * qt + cc);
         }
 #pragma unroll
-        for (int i = 0; i < RTD; ++i)
+        for (int i = 0; i < RTW; ++i)
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
-                Elem<S>::mma(acc[i], ldfrag<S>(so2, i, 2 * qt + cc, 4, lane), pf[cc]);
-                Elem<S>::mma(acc[RTD + i], q2[i][cc], sf[cc]);
+                const Frag ob = KVL ? gather_qt(so1, dh * RTW + i, 2 * qt + cc) : ldfrag<S>(so2, dh * RTW + i, 2 * qt + cc, 4, lane);
+                Elem<S>::mma(acc[i], ob, pf[cc]);
             }
-        if (J >= 1) {
+        Frag ga[2];
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const Frag ga = ldfrag<S>(sg, kt, 2 * qt + cc, 4, lane);
+        for (int cc = 0; cc < 2; ++cc) ga[cc] = ldfrag<S>(sg, grp, 2 * qt + cc, 4, lane);
+        // per column tile of q~^T: dT (row tile grp) and, for the wave's own tiles, dk^
 #pragma unroll
-                for (int ct = 0; ct < RTD; ++ct) Elem<S>::mma(acc[2 * RTD + ct], ga, q2[ct][cc]);
+        for (int ct = 0; ct < RTD; ++ct) {
+            Frag q2[2];
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) q2[cc] = gather_qt(sq, ct, 2 * qt + cc);
+            if (ct / RTW == dh) {  // wave-uniform
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) Elem<S>::mma(acc[RTW + ct % RTW], q2[cc], sf[cc]);
+            }
+            if (J >= 1) {
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) Elem<S>::mma(acc[2 * RTW + ct], ga[cc], q2[cc]);
             }
         }
     };
@@ -1690,10 +1716,10 @@ __global__ __launch_bounds__(256) void bwd_key_kernel_lds(BwdArgs a) {
     // add the query half qt = 1 (wave w + 1) into qt = 0 (wave w), one tile at a time, through
     // the buffers (free now)
     float *red = (float *)smem + (w >> 1) * 16 * 65;
-    for (int t = 0; t <= 6; ++t) {
+    for (int t = 0; t <= NACC; ++t) {
         __syncthreads();
         if (qt == 1) {
-            if (t < 6) {
+            if (t < NACC) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) red[r * 65 + lane] = acc[t][r];
             } else {
@@ -1702,7 +1728,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel_lds(BwdArgs a) {
         }
         __syncthreads();
         if (qt == 0) {
-            if (t < 6) {
+            if (t < NACC) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[t][r] += red[r * 65 + lane];
             } else {
@@ -1713,13 +1739,13 @@ __global__ __launch_bounds__(256) void bwd_key_kernel_lds(BwdArgs a) {
     if (qt != 0) return;
     float *dvo = (float *)(ws + ly.dvo) + (int64_t)key * D, *dko = (float *)(ws + ly.dko) + (int64_t)key * D;
 #pragma unroll
-    for (int i = 0; i < RTD; ++i)
+    for (int i = 0; i < RTW; ++i)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-            const int d0 = 32 * i + 8 * g4 + 4 * h;
+            const int d0 = 32 * (dh * RTW + i) + 8 * g4 + 4 * h;
             const f32x4 xv = {acc[i][4 * g4], acc[i][4 * g4 + 1], acc[i][4 * g4 + 2], acc[i][4 * g4 + 3]};
-            const f32x4 xk = {scale * acc[RTD + i][4 * g4], scale * acc[RTD + i][4 * g4 + 1],
-                              scale * acc[RTD + i][4 * g4 + 2], scale * acc[RTD + i][4 * g4 + 3]};
+            const f32x4 xk = {scale * acc[RTW + i][4 * g4], scale * acc[RTW + i][4 * g4 + 1],
+                              scale * acc[RTW + i][4 * g4 + 2], scale * acc[RTW + i][4 * g4 + 3]};
             *reinterpret_cast<f32x4 *>(dvo + d0) = xv;
             *reinterpret_cast<f32x4 *>(dko + d0) = xk;
         }
@@ -1729,12 +1755,12 @@ __global__ __launch_bounds__(256) void bwd_key_kernel_lds(BwdArgs a) {
         for (int ct = 0; ct < RTD; ++ct)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x16 &x = acc[2 * RTD + ct];
+                const f32x16 &x = acc[2 * RTW + ct];
                 const f32x4 y = {x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]};
-                *reinterpret_cast<f32x4 *>(dtt + (int64_t)(32 * ct + l32) * D + 32 * kt + 8 * g4 + 4 * h) = y;
+                *reinterpret_cast<f32x4 *>(dtt + (int64_t)(32 * ct + l32) * D + 32 * grp + 8 * g4 + 4 * h) = y;
             }
     }
-    if (h == 0) ((float *)(ws + ly.cso))[J * kC + 32 * kt + l32] = csum;
+    if (dh == 0 && h == 0) ((float *)(ws + ly.cso))[J * kC + 32 * kt + l32] = csum;
 }
 
 template <typename T, int D>
@@ -1751,7 +1777,11 @@ hipError_t launch_bwd_t(const BwdArgs &a0, hipStream_t st) {
                 const dim3 tiles((unsigned)((a.nb - 1 + kUpQB - 1) / kUpQB * a.hc));
                 hipLaunchKernelGGL(bwd_down_kernel_lds, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
                 hipLaunchKernelGGL(bwd_up_kernel_lds, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
-                hipLaunchKernelGGL(bwd_key_kernel_lds, walks, dim3(256), 0, st, a);
+                hipLaunchKernelGGL(bwd_key_kernel_lds<D>, walks, dim3(64 * KeyCfg<D>::NW), 0, st, a);
+            } else if constexpr (sizeof(T) == 2) {
+                hipLaunchKernelGGL((bwd_down_kernel<T, D, false>), walks, dim3(128), 0, st, a);
+                hipLaunchKernelGGL((bwd_up_kernel<T, D>), walks, dim3(128), 0, st, a);
+                hipLaunchKernelGGL(bwd_key_kernel_lds<D>, walks, dim3(64 * KeyCfg<D>::NW), 0, st, a);
             } else {
                 hipLaunchKernelGGL((bwd_down_kernel<T, D, true>), walks, dim3(128), 0, st, a);
                 hipLaunchKernelGGL((bwd_up_kernel<T, D>), walks, dim3(128), 0, st, a);

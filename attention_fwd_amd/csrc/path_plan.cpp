@@ -53,8 +53,8 @@ BwdLayout bwd_layout(int L, int D, int es) {
     ly.tot = take(nb * 4); ly.mid = take(np * 4);
     const int64_t pr = np * 64 * D * es;  // a 64 x D fragment set per pair
     ly.qs1 = take(pr);
-    // q~ with rows d: not stored for bf16 at d = 64, whose key walk gathers it from the other orientation
-    ly.qs2 = take(D == 64 && es == 2 ? 0 : pr);
+    // q~ with rows d: not stored for bf16, whose key walk gathers it from the other orientation
+    ly.qs2 = take(es == 2 ? 0 : pr);
     ly.gs2 = take(pr + 64 * D * es);  // one spare set after the last pair's: target of discarded stores
     ly.head = off;
     return ly;

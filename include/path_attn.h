@@ -292,10 +292,10 @@ path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace
  * one).  path_attn_bwd_workspace_size(1, 1, L, d, dtype) is one head's share;
  * path_attn_bwd accepts any workspace of at least one share and processes
  * floor(workspace_bytes / share) heads at a time (results do not depend on it).
- * One share is 3 * 64 * d element-type values (2 * 64 * d for bf16 at d = 64)
- * per pair of 64-token blocks (nb (nb - 1) / 2 pairs, nb = ceil(L / 64)) plus
- * 4.4 KiB (d = 64, bf16) to 10.5 KiB (d = 128, fp32) per token: 49 MiB per
- * head at L = 4096, d = 64, bf16; 128 MiB at d = 128.
+ * One share is 3 * 64 * d element-type values (2 * 64 * d for bf16) per pair
+ * of 64-token blocks (nb (nb - 1) / 2 pairs, nb = ceil(L / 64)) plus 4.4 KiB
+ * (d = 64, bf16) to 10.5 KiB (d = 128, fp32) per token: 49 MiB per head at
+ * L = 4096, d = 64, bf16; 96 MiB at d = 128, bf16.
  */
 size_t path_attn_bwd_workspace_size(int B, int H, int L, int d, path_dtype_t dtype);
 
