@@ -825,18 +825,19 @@ __device__ __forceinline__ void dma_record(const void *src, void *dst, int tid) 
 // LDS access of the wave returned.
 constexpr int vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
 
-// Down walk for bf16 inputs at head dimension 64: as bwd_down_kernel (without the q~^T
-// copy), but four query blocks (eight waves, two per block) share each key block's
-// transition T - I (8 KiB), copied global -> LDS one step ahead (global_load_lds,
+// Down walk for bf16 inputs: as bwd_down_kernel (without the q~^T copy), but four query
+// blocks (eight waves, two per block) share each key block's transition T - I (8 KiB at
+// d = 64, 32 KiB at d = 128), copied global -> LDS one step ahead (global_load_lds,
 // double-buffered), as in the up walk below.  The tile walks J = Imax - 1 .. 0; a wave
 // joins at J = I - 1.  Every step issues the same memory operations on every wave (the
 // next copy, the next gate total, the stores of q~ and of the gate sum, to a spare target
 // when the wave has nothing to store), so that one wait at the top of a step covers every
 // path.
+template <int D>
 __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_down_kernel_lds(BwdArgs a) {
     typedef uint16_t S;
     typedef Elem<S>::Frag Frag;
-    constexpr int D = 64, KCD = D / 16, RTD = D / 32, NTH = 64 * 2 * kUpQB;
+    constexpr int KCD = D / 16, RTD = D / 32, NTH = 64 * 2 * kUpQB;
     constexpr int REC = D * D;               // elements of a transition
     constexpr int NLD = REC * 2 / 16 / NTH;  // DMA chunks per thread and transition
     static_assert(REC * 2 % (16 * NTH) == 0, "transition must split evenly over the workgroup");
@@ -1775,11 +1776,12 @@ hipError_t launch_bwd_t(const BwdArgs &a0, hipStream_t st) {
             const dim3 walks((unsigned)((a.nb - 1) * a.hc));
             if constexpr (sizeof(T) == 2 && D == 64) {
                 const dim3 tiles((unsigned)((a.nb - 1 + kUpQB - 1) / kUpQB * a.hc));
-                hipLaunchKernelGGL(bwd_down_kernel_lds, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
+                hipLaunchKernelGGL(bwd_down_kernel_lds<D>, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
                 hipLaunchKernelGGL(bwd_up_kernel_lds, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
                 hipLaunchKernelGGL(bwd_key_kernel_lds<D>, walks, dim3(64 * KeyCfg<D>::NW), 0, st, a);
             } else if constexpr (sizeof(T) == 2) {
-                hipLaunchKernelGGL((bwd_down_kernel<T, D, false>), walks, dim3(128), 0, st, a);
+                const dim3 tiles((unsigned)((a.nb - 1 + kUpQB - 1) / kUpQB * a.hc));
+                hipLaunchKernelGGL(bwd_down_kernel_lds<D>, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
                 hipLaunchKernelGGL((bwd_up_kernel<T, D>), walks, dim3(128), 0, st, a);
                 hipLaunchKernelGGL(bwd_key_kernel_lds<D>, walks, dim3(64 * KeyCfg<D>::NW), 0, st, a);
             } else {
