@@ -1074,6 +1074,161 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_lds(BwdArgs a) {
     if (h == 0) ((float *)(ws + ly.rso))[qi] = rsum;
 }
 
+// Up walk for bf16 inputs at head dimension 128: as bwd_up_kernel_lds, but a record (80
+// KiB) is copied in two parts: k^ and V (the operands of the logits, 32 KiB) one step
+// ahead into two buffers, and k^^T and (T - I)^T (the operands of the adjoint update, 48
+// KiB) into one buffer at the top of the step, landing while the logits and dS are
+// computed.  G^(J-1) is stored for the pair (I, J) with rows queries, k over d -- the
+// fragments of the update's B operand, so no transposition -- and the key walk gathers
+// G^T from it.  Every step issues the same memory operations on every wave, as in the
+// d = 64 walks.
+__global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_split(BwdArgs a) {
+    typedef uint16_t S;
+    typedef Elem<S>::Frag Frag;
+    constexpr int D = 128, KCD = D / 16, RTD = D / 32, NTH = 64 * 2 * kUpQB;
+    constexpr int RA = 2 * kC * D;            // elements of the first part: k^, V
+    constexpr int RB = kC * D + D * D;        // of the second: k^^T, (T - I)^T
+    constexpr int NLA = RA * 2 / 16 / NTH, NLB = RB * 2 / 16 / NTH;
+    static_assert(RA * 2 % (16 * NTH) == 0 && RB * 2 % (16 * NTH) == 0, "parts must split evenly over the workgroup");
+    constexpr int NST = KCD;                  // global stores of one step: G^(J-1)
+    constexpr int NAFTER = NLA + 1 + KCD;     // memory operations issued after the second part's copy
+    // one LDS array: two buffers of the first part, each followed by 64 key terms and 64 gate
+    // sums, then the second part's buffer
+    constexpr int ABUF = RA * 2 + 2 * 4 * kC;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * ABUF + RB * 2];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int nb = a.nb, hc = a.hc;
+    const int ntile = (nb - 1 + kUpQB - 1) / kUpQB;
+    const int gl = blockIdx.x % hc, tile = ntile - 1 - blockIdx.x / hc;
+    const int I0 = 1 + kUpQB * tile, Imax = min(nb - 1, I0 + kUpQB - 1);
+    const int I = __builtin_amdgcn_readfirstlane(I0 + (w >> 1)), wq = __builtin_amdgcn_readfirstlane(w & 1);
+    const bool active = I <= nb - 1;
+    const int Ic = active ? I : Imax;
+    const BwdLayout &ly = a.ly;
+    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
+    const S *RECS = (const S *)(ws + ly.urec), *QS1 = (const S *)(ws + ly.qs1);
+    const int64_t RE = ly.rec_elems;
+    S *GS2 = (S *)(ws + ly.gs2);
+    S *const spare = GS2 + (int64_t)nb * (nb - 1) / 2 * kC * D;
+    const float *MID = (const float *)(ws + ly.mid), *CKK = (const float *)(ws + ly.ckl);
+    const float scale = a.scale, c2 = scale * kLog2e;
+    const int qi = Ic * kC + 32 * wq + l32;
+    const float dd = ((const float *)(ws + ly.dd))[qi], cq = ((const float *)(ws + ly.cql))[qi];
+    const int Il = min(I0 + (lane & (kUpQB - 1)), nb - 1);
+    const S *sb = (const S *)(smem + 2 * ABUF);  // k^^T (rows d, k over keys), then (T - I)^T
+
+    // first part of record J and its side values (key terms from waves other than 1, gate sums
+    // from wave 1) into buffer B; J <= nb - 1
+    auto issue_a = [&](int J, int B) {
+        unsigned char *buf = smem + B * ABUF;
+        dma_record<NTH, NLA>(RECS + (int64_t)J * RE, buf, tid);
+        const float *src = w == 1 ? MID + pair_index(Il, min(J, Il - 1)) : CKK + J * kC + lane;
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(buf + RA * 2 + (w == 1 ? 4 * kC : 0)), 4, 0, 0);
+    };
+    issue_a(0, 0);
+    Frag dof[KCD], qa[KCD], qb[KCD];
+#pragma unroll
+    for (int kc = 0; kc < KCD; ++kc) {
+        dof[kc] = ldfrag<S>((const S *)(ws + ly.do1) + (int64_t)Ic * kC * D, wq, kc, KCD, lane);
+        qa[kc] = ldfrag<S>(QS1 + pair_index(Ic, 0) * kC * D, wq, kc, KCD, lane);
+    }
+    f32x16 gt[RTD];
+#pragma unroll
+    for (int dt = 0; dt < RTD; ++dt) gt[dt] = f32x16{};
+    float rsum = 0.f;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
+    auto step = [&](int J, auto bsel) {
+        constexpr int B = decltype(bsel)::value;
+        const S *rec = (const S *)(smem + B * ABUF);
+        const float *sck = (const float *)(smem + B * ABUF + RA * 2), *smid = sck + kC;
+        // this wave's copies of the first part of record J and its q~ prefetch have landed (only
+        // the previous step's stores may be in flight); after the barrier every wave's have, and
+        // every wave is done with the second-part buffer and the other first-part buffer
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0(NST));
+        asm volatile("s_barrier" ::: "memory");
+        dma_record<NTH, NLB>(RECS + (int64_t)J * RE + RA, smem + 2 * ABUF, tid);
+        issue_a(min(J + 1, nb - 1), 1 - B);
+        asm volatile("" ::: "memory");
+        const bool act = active && J < I;
+        Frag(&qf)[KCD] = B ? qb : qa;
+        Frag(&qn)[KCD] = B ? qa : qb;
+        {
+            const int64_t pn = pair_index(Ic, min(J + 1, Ic - 1));
+#pragma unroll
+            for (int kc = 0; kc < KCD; ++kc) qn[kc] = ldfrag<S>(QS1 + pn * kC * D, wq, kc, KCD, lane);
+        }
+        f32x16 sv[2];
+        if (act) {
+            const float mid = smid[w >> 1];
+            // one key tile at a time (its dP dies before the next tile's products)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                f32x16 dp = {};
+                sv[kt] = f32x16{};
+#pragma unroll
+                for (int kc = 0; kc < KCD; ++kc) {
+                    Elem<S>::mma(sv[kt], ldfrag<S>(rec, kt, kc, KCD, lane), qf[kc]);
+                    Elem<S>::mma(dp, ldfrag<S>(rec + kC * D, kt, kc, KCD, lane), dof[kc]);
+                }
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const f32x4 ck = *reinterpret_cast<const f32x4 *>(sck + 32 * kt + 8 * g4 + 4 * h);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * g4 + e;
+                        const float P = fast_exp2(c2 * sv[kt][r] + cq + ck[e] + mid);
+                        const float ds = P * (dp[r] - dd);
+                        rsum += ds;
+                        sv[kt][r] = scale * ds;
+                    }
+                }
+            }
+        }
+        // this wave's copies of the second part have landed (the first part's next copy and the
+        // q~ prefetch, issued after them, may stay in flight); after the barrier every wave's have
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0(NAFTER));
+        asm volatile("s_barrier" ::: "memory");
+        Frag gf[KCD];  // G^(J-1) (rows: the wave's queries, k over d), rounded: the B operand below
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) gf[kc] = acc_frag<S>(gt[kc >> 1], kc & 1);
+        if (act) {
+            Frag sf[4];
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) sf[kc] = acc_frag<S>(sv[kc >> 1], kc & 1);
+#pragma unroll
+            for (int dt = 0; dt < RTD; ++dt) {
+                if (J >= 1) {
+#pragma unroll
+                    for (int kc = 0; kc < KCD; ++kc) Elem<S>::mma(gt[dt], ldfrag<S>(sb + kC * D, dt, kc, KCD, lane), gf[kc]);
+                }
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) Elem<S>::mma(gt[dt], ldfrag<S>(sb, dt, kc, 4, lane), sf[kc]);
+            }
+        }
+        // G^(J-1) for the pair (I, J) (J >= 1; to the spare set otherwise)
+        S *dst = (act && J >= 1) ? GS2 + pair_index(I, J) * kC * D : spare;
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) stfrag<S>(dst, wq, kc, KCD, lane, gf[kc]);
+    };
+    for (int J = 0; J < Imax; J += 2) {
+        step(J, std::integral_constant<int, 0>{});
+        if (J + 1 < Imax) step(J + 1, std::integral_constant<int, 1>{});
+    }
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));  // no copy may still be landing in LDS when the workgroup leaves
+    if (!active) return;
+    rsum = other_half_sum(rsum);
+    float *dqo = (float *)(ws + ly.dqo) + (int64_t)qi * D;
+#pragma unroll
+    for (int dt = 0; dt < RTD; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 x = {gt[dt][4 * g4], gt[dt][4 * g4 + 1], gt[dt][4 * g4 + 2], gt[dt][4 * g4 + 3]};
+            *reinterpret_cast<f32x4 *>(dqo + 32 * dt + 8 * g4 + 4 * h) = x;
+        }
+    if (h == 0) ((float *)(ws + ly.rso))[qi] = rsum;
+}
+
 // Key walk: one workgroup per (key block J <= nb-2, head).  Wave w takes the
 // logit tile of queries 32 qt .. (qt = w & 1) and keys 32 kt .. (kt = (w >> 1)
 // & 1) of every later query block I, recomputes P and dS, and accumulates over
@@ -1561,7 +1716,8 @@ __global__ __launch_bounds__(kT) void bwd_gate_kernel(BwdArgs a) {
 // over queries) are gathered from the q~ copy with 2-byte LDS reads, so the down walk
 // stores q~ in one orientation only.  At d = 128 the registers do not hold k^ and V of
 // the key tile besides the accumulators: they are read from an LDS copy, and dO^T is
-// gathered from the dO copy like q~^T (the buffers then hold q~, G^T and dO: 48.8 KiB).
+// gathered from the dO copy like q~^T (the buffers then hold q~, G and dO: 48.8 KiB);
+// the up walk stores G with rows queries there, so G^T is gathered the same way.
 template <int D>
 __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs a) {
     typedef uint16_t S;
@@ -1691,7 +1847,8 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
             }
         Frag ga[2];
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) ga[cc] = ldfrag<S>(sg, grp, 2 * qt + cc, 4, lane);
+        for (int cc = 0; cc < 2; ++cc)
+            ga[cc] = KVL ? gather_qt(sg, grp, 2 * qt + cc) : ldfrag<S>(sg, grp, 2 * qt + cc, 4, lane);
         // per column tile of q~^T: dT (row tile grp) and, for the wave's own tiles, dk^
 #pragma unroll
         for (int ct = 0; ct < RTD; ++ct) {
@@ -1782,7 +1939,7 @@ hipError_t launch_bwd_t(const BwdArgs &a0, hipStream_t st) {
             } else if constexpr (sizeof(T) == 2) {
                 const dim3 tiles((unsigned)((a.nb - 1 + kUpQB - 1) / kUpQB * a.hc));
                 hipLaunchKernelGGL(bwd_down_kernel_lds<D>, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
-                hipLaunchKernelGGL((bwd_up_kernel<T, D>), walks, dim3(128), 0, st, a);
+                hipLaunchKernelGGL(bwd_up_kernel_split, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
                 hipLaunchKernelGGL(bwd_key_kernel_lds<D>, walks, dim3(64 * KeyCfg<D>::NW), 0, st, a);
             } else {
                 hipLaunchKernelGGL((bwd_down_kernel<T, D, true>), walks, dim3(128), 0, st, a);
