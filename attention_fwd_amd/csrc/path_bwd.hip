@@ -1713,8 +1713,8 @@ __global__ __launch_bounds__(kT) void bwd_gate_kernel(BwdArgs a) {
 // orientations, its exponent terms and the pair's gate sum: 32.8 KiB at d = 64, 64.8
 // KiB at d = 128 -- are copied global -> LDS one step ahead (global_load_lds,
 // double-buffered) and read by every wave from there.  The q~^T fragments (rows d, k
-// over queries) are gathered from the q~ copy with 2-byte LDS reads, so the down walk
-// stores q~ in one orientation only.  At d = 128 the registers do not hold k^ and V of
+// over queries) are gathered from the q~ copy with transposing LDS reads, so the down
+// walk stores q~ in one orientation only.  At d = 128 the registers do not hold k^ and V of
 // the key tile besides the accumulators: they are read from an LDS copy, and dO^T is
 // gathered from the dO copy like q~^T (the buffers then hold q~, G and dO: 48.8 KiB);
 // the up walk stores G with rows queries there, so G^T is gathered the same way.
@@ -1782,19 +1782,35 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
 #pragma unroll
     for (int t = 0; t < NACC; ++t) acc[t] = f32x16{};
     float csum = 0.f;
-    // q~^T fragment (rows d = 32 ct + lane % 32, k over queries 16 kq ..) gathered from the q~ copy:
-    // element e of a lane is q~[16 kq + 8 (e >> 2) + 4 h + (e & 3)][d], which sits in the q~
-    // fragment of rows 32 (kq >> 1) .. and d chunk d >> 4 at lane (query % 32) + 32 ((d >> 2) & 1),
-    // element 4 ((d >> 3) & 1) + (d & 3)
-    const int dl = l32, qlane = 32 * ((dl >> 2) & 1), qel = 4 * ((dl >> 3) & 1) + (dl & 3);
-    auto gather_qt = [&](const S *sq, int ct, int kq) {
-        const int d = 32 * ct + dl;
-        const S *base = sq + ((((kq >> 1) * KCD + (d >> 4)) * 64 + 16 * (kq & 1) + 4 * h + qlane) * 8 + qel);
-        Frag f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = base[(8 * (e >> 2) + (e & 3)) * 8];
-        return f;
+    // q~^T fragment (rows d = 32 ct + lane % 32, k over queries 16 kq ..) gathered from the q~ copy
+    // (fragments of rows queries, k over d) with two transposing LDS reads.  ds_read_b64_tr_b16
+    // works on groups of 16 lanes: lane 16 g + i receives element i % 4 of the 8-byte chunks that
+    // lanes 16 g + 4 t + i / 4 (t = 0..3) address, as its elements t.  Element t of the first read
+    // must be q~[16 kq + 4 (lane / 32) + t][d] (the second: 8 queries on), so lane s = 16 g + 4 t + m
+    // addresses the four consecutive d = 32 ct + 16 (g & 1) + 4 m .. of query 16 kq + 4 (g >> 1) + t,
+    // which sit together in the q~ fragment of d chunk 2 ct + (g & 1) at lane (query % 32) +
+    // 32 (m & 1), elements 4 (m >> 1) ..
+    // The reads are issued by inline assembly and waited for by an explicit lgkmcnt(0) tied to
+    // their results (the compiler would otherwise wait for every copy in flight before each
+    // one); LDS operations complete in order, so the compiler's own counts stay safe.
+    const int tg = lane >> 4, tt = (lane >> 2) & 3, tm = lane & 3;
+    const int troff = ((tg & 1) * 64 + 4 * (tg >> 1) + tt + 32 * (tm & 1)) * 8 + 4 * (tm >> 1);
+    struct TrF {
+        u32x2 lo, hi;
     };
+    auto tr_issue = [&](const S *sq, int ct, int kq) {
+        const S *p = sq + (((kq >> 1) * KCD + 2 * ct) * 64 + 16 * (kq & 1)) * 8 + troff;
+        const unsigned la = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) S *)p;
+        TrF t;
+        asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:128"  // queries + 8
+                     : "=&v"(t.lo), "=&v"(t.hi)
+                     : "v"(la));
+        return t;
+    };
+    auto tr_wait2 = [](TrF &a, TrF &b) {
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a.lo), "+v"(a.hi), "+v"(b.lo), "+v"(b.hi));
+    };
+    auto tr_frag = [](const TrF &t) { return __builtin_bit_cast(Frag, u32x4{t.lo.x, t.lo.y, t.hi.x, t.hi.y}); };
     __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
     // one step over query block I, whose copies are in buffer B ((I - J - 1) % 2); it refills the other
     auto step = [&](int I, auto bsel) {
@@ -1838,23 +1854,44 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
             pf[cc] = acc_frag<S>(dp, cc);
             sf[cc] = acc_frag<S>(s, cc);
         }
+        // dV^T += dO^T P^T (dO^T: the LDS copy, or gathered from dO)
 #pragma unroll
-        for (int i = 0; i < RTW; ++i)
+        for (int i = 0; i < RTW; ++i) {
+            Frag ob[2];
+            if constexpr (KVL) {
+                TrF t0 = tr_issue(so1, dh * RTW + i, 2 * qt), t1 = tr_issue(so1, dh * RTW + i, 2 * qt + 1);
+                tr_wait2(t0, t1);
+                ob[0] = tr_frag(t0);
+                ob[1] = tr_frag(t1);
+            } else {
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const Frag ob = KVL ? gather_qt(so1, dh * RTW + i, 2 * qt + cc) : ldfrag<S>(so2, dh * RTW + i, 2 * qt + cc, 4, lane);
-                Elem<S>::mma(acc[i], ob, pf[cc]);
+                for (int cc = 0; cc < 2; ++cc) ob[cc] = ldfrag<S>(so2, dh * RTW + i, 2 * qt + cc, 4, lane);
             }
-        Frag ga[2];
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-            ga[cc] = KVL ? gather_qt(sg, grp, 2 * qt + cc) : ldfrag<S>(sg, grp, 2 * qt + cc, 4, lane);
-        // per column tile of q~^T: dT (row tile grp) and, for the wave's own tiles, dk^
+            for (int cc = 0; cc < 2; ++cc) Elem<S>::mma(acc[i], ob[cc], pf[cc]);
+        }
+        // G^T (rows d of tile grp, k over queries) and the first column tile of q~^T
+        Frag ga[2];
+        TrF qn0 = tr_issue(sq, 0, 2 * qt), qn1 = tr_issue(sq, 0, 2 * qt + 1);
+        if constexpr (KVL) {
+            TrF g0 = tr_issue(sg, grp, 2 * qt), g1 = tr_issue(sg, grp, 2 * qt + 1);
+            tr_wait2(g0, g1);
+            ga[0] = tr_frag(g0);
+            ga[1] = tr_frag(g1);
+        } else {
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) ga[cc] = ldfrag<S>(sg, grp, 2 * qt + cc, 4, lane);
+        }
+        tr_wait2(qn0, qn1);
+        // per column tile of q~^T: dT (row tile grp) and, for the wave's own tiles, dk^; the next
+        // tile's reads are in flight during this tile's products
 #pragma unroll
         for (int ct = 0; ct < RTD; ++ct) {
-            Frag q2[2];
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) q2[cc] = gather_qt(sq, ct, 2 * qt + cc);
+            const Frag q2[2] = {tr_frag(qn0), tr_frag(qn1)};
+            if (ct + 1 < RTD) {
+                qn0 = tr_issue(sq, ct + 1, 2 * qt);
+                qn1 = tr_issue(sq, ct + 1, 2 * qt + 1);
+            }
             if (ct / RTW == dh) {  // wave-uniform
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) Elem<S>::mma(acc[RTW + ct % RTW], q2[cc], sf[cc]);
@@ -1863,6 +1900,7 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) Elem<S>::mma(acc[2 * RTW + ct], ga[cc], q2[cc]);
             }
+            if (ct + 1 < RTD) tr_wait2(qn0, qn1);
         }
     };
     for (int I = J + 1; I < nb; I += 2) {
