@@ -33,7 +33,7 @@ struct BwdLayout {
     int64_t tot;  // [nb]: gate total of each block (log2 units)
     int64_t mid;  // [np]: gate sum over the blocks strictly between I and J (log2 units)
     // per pair, fragments (S): q~ (rows queries, k over d), q~^T (rows d, k over queries; none for bf16
-    // inputs), G^(J-1)^T (rows d; for bf16 at D = 128 G^(J-1) with rows queries, k over d; plus one
+    // inputs), G^(J-1)^T (rows d; for bf16 inputs G^(J-1) with rows queries, k over d; plus one
     // spare set at the end)
     int64_t qs1, qs2, gs2;
     int64_t head;  // bytes per head

@@ -796,14 +796,15 @@ __global__ __launch_bounds__(128, (D == 128 && sizeof(S) == 2) ? 2 : 1) void bwd
 // blocks (eight waves, two per block) share each key block's record (k^, V, k^^T,
 // (T - I)^T: 32 KiB), which is copied global -> LDS one step ahead by the DMA path
 // (global_load_lds, double-buffered), as in the forward scan; each wave prefetches its
-// next stored q~ into registers.  The transposition scratch holds bf16 (rounding each
-// element before transposing gives the same fragments).
+// next stored q~ into registers.  G^(J-1) is stored for the pair (I, J) with rows
+// queries, k over d: the rounded fragments that are the update's B operand, so it needs
+// no transposition; the key walk gathers G^T from it.
 //
 // Every step issues the same memory operations on every wave, whether or not the wave
 // has work in it (a copy for the next record, a q~ prefetch from a clamped valid pair,
-// and the stores of a transposed G, to a spare fragment set of the workspace when there
-// is nothing to store), so that one wait for all but the last stores at the top of each
-// step covers every path and the compiler adds no wait of its own inside the step.
+// and the stores of G, to a spare fragment set of the workspace when there is nothing to
+// store), so that one wait for all but the last stores at the top of each step covers
+// every path and the compiler adds no wait of its own inside the step.
 constexpr int kUpQB = 4;  // query blocks per workgroup
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -924,14 +925,13 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_lds(BwdArgs a) {
     constexpr int REC = 3 * kC * D + D * D;  // elements of a record
     constexpr int NLD = REC * 2 / 16 / NTH;   // DMA chunks per thread and record
     static_assert(REC * 2 % (16 * NTH) == 0, "record must split evenly over the workgroup");
-    constexpr int XB = 40;        // bf16 row stride of the transposition scratch
-    constexpr int NST = 2 * RTD;  // global stores of one transposed G
+    constexpr int NST = KCD;  // global stores of one step: G^(J-1)
     // One LDS array: two buffers, each a record followed by 64 key terms of the exponent and 64
     // gate sums (between each of the tile's query blocks and the record's key block, repeated
-    // over the lanes), then the transposition scratch.  The copies into LDS are ordered by the
-    // explicit waits and barriers of the walk alone.
+    // over the lanes).  The copies into LDS are ordered by the explicit waits and barriers of the
+    // walk alone.
     constexpr int BUF = REC * 2 + 2 * 4 * kC;  // bytes per buffer
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF + 2 * kUpQB * D * XB * 2];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int nb = a.nb, hc = a.hc;
     const int ntile = (nb - 1 + kUpQB - 1) / kUpQB;  // query blocks 1 .. nb-1, four per tile
@@ -951,7 +951,6 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_lds(BwdArgs a) {
     const float scale = a.scale, c2 = scale * kLog2e;
     const int qi = Ic * kC + 32 * wq + l32;
     const float dd = ((const float *)(ws + ly.dd))[qi], cq = ((const float *)(ws + ly.cql))[qi];
-    S *const myx = (S *)(smem + 2 * BUF) + w * D * XB;
     // the gate-sum lane of wave 1: query block I0 + (lane % 4), clamped to the last block
     const int Il = min(I0 + (lane & (kUpQB - 1)), nb - 1);
 
@@ -989,7 +988,7 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_lds(BwdArgs a) {
         asm volatile("s_barrier" ::: "memory");
         issue(min(J + 1, nb - 1), 1 - B);
         asm volatile("" ::: "memory");  // the copies stay ahead of this step's stores
-        const bool act = active && J < I, store = act && J + 1 < I;
+        const bool act = active && J < I;
         Frag(&qf)[KCD] = B ? qb : qa;
         Frag(&qn)[KCD] = B ? qa : qb;
         {
@@ -997,6 +996,9 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_lds(BwdArgs a) {
 #pragma unroll
             for (int kc = 0; kc < KCD; ++kc) qn[kc] = ldfrag<S>(QS1 + pn * kC * D, wq, kc, KCD, lane);
         }
+        Frag gf[KCD];  // G^(J-1) (rows: the wave's queries, k over d), rounded: the B operand below
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) gf[kc] = acc_frag<S>(gt[kc >> 1], kc & 1);
         if (act) {
             const float mid = smid[w >> 1];
             f32x16 sv[2], dp[2];
@@ -1024,9 +1026,7 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_lds(BwdArgs a) {
                         sv[kt][r] = scale * ds;
                     }
                 }
-            Frag gf[KCD], sf[4];
-#pragma unroll
-            for (int kc = 0; kc < KCD; ++kc) gf[kc] = acc_frag<S>(gt[kc >> 1], kc & 1);
+            Frag sf[4];
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) sf[kc] = acc_frag<S>(sv[kc >> 1], kc & 1);
 #pragma unroll
@@ -1039,22 +1039,11 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_lds(BwdArgs a) {
 #pragma unroll
                 for (int kc = 0; kc < 4; ++kc) Elem<S>::mma(gt[dt], ldfrag<S>(rec + 2 * kC * D, dt, kc, 4, lane), sf[kc]);
             }
-            // G^(J) with rows d for the pair (I, J + 1), into the bf16 scratch
-#pragma unroll
-            for (int dt = 0; dt < RTD; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) myx[(32 * dt + acc_row(r, h)) * XB + l32] = Elem<S>::from_float(gt[dt][r]);
         }
-        // the stores (the scratch's stale contents to the spare set when there is nothing to store)
-        S *dst = store ? GS2 + pair_index(I, J + 1) * kC * D : spare;
+        // G^(J-1) for the pair (I, J) (J >= 1; to the spare set otherwise)
+        S *dst = (act && J >= 1) ? GS2 + pair_index(I, J) * kC * D : spare;
 #pragma unroll
-        for (int dt = 0; dt < RTD; ++dt)
-#pragma unroll
-            for (int kcl = 0; kcl < 2; ++kcl) {
-                const S *src = myx + (32 * dt + l32) * XB + 16 * kcl + 4 * h;
-                const u32x2 lo = *reinterpret_cast<const u32x2 *>(src), hi = *reinterpret_cast<const u32x2 *>(src + 8);
-                stfrag<S>(dst, dt, 2 * wq + kcl, 4, lane, __builtin_bit_cast(Frag, u32x4{lo.x, lo.y, hi.x, hi.y}));
-            }
+        for (int kc = 0; kc < KCD; ++kc) stfrag<S>(dst, wq, kc, KCD, lane, gf[kc]);
     };
     for (int J = 0; J < Imax; J += 2) {
         step(J, std::integral_constant<int, 0>{});
@@ -1078,10 +1067,8 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_lds(BwdArgs a) {
 // KiB) is copied in two parts: k^ and V (the operands of the logits, 32 KiB) one step
 // ahead into two buffers, and k^^T and (T - I)^T (the operands of the adjoint update, 48
 // KiB) into one buffer at the top of the step, landing while the logits and dS are
-// computed.  G^(J-1) is stored for the pair (I, J) with rows queries, k over d -- the
-// fragments of the update's B operand, so no transposition -- and the key walk gathers
-// G^T from it.  Every step issues the same memory operations on every wave, as in the
-// d = 64 walks.
+// computed.  G^(J-1) is stored as at d = 64.  Every step issues the same memory
+// operations on every wave, as in the d = 64 walks.
 __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_split(BwdArgs a) {
     typedef uint16_t S;
     typedef Elem<S>::Frag Frag;
@@ -1716,8 +1703,8 @@ __global__ __launch_bounds__(kT) void bwd_gate_kernel(BwdArgs a) {
 // over queries) are gathered from the q~ copy with transposing LDS reads, so the down
 // walk stores q~ in one orientation only.  At d = 128 the registers do not hold k^ and V of
 // the key tile besides the accumulators: they are read from an LDS copy, and dO^T is
-// gathered from the dO copy like q~^T (the buffers then hold q~, G and dO: 48.8 KiB);
-// the up walk stores G with rows queries there, so G^T is gathered the same way.
+// gathered from the dO copy like q~^T (the buffers then hold q~, G and dO: 48.8 KiB).
+// G^T is gathered the same way: the up walk stores G with rows queries.
 template <int D>
 __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs a) {
     typedef uint16_t S;
@@ -1873,14 +1860,11 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
         // G^T (rows d of tile grp, k over queries) and the first column tile of q~^T
         Frag ga[2];
         TrF qn0 = tr_issue(sq, 0, 2 * qt), qn1 = tr_issue(sq, 0, 2 * qt + 1);
-        if constexpr (KVL) {
+        {
             TrF g0 = tr_issue(sg, grp, 2 * qt), g1 = tr_issue(sg, grp, 2 * qt + 1);
             tr_wait2(g0, g1);
             ga[0] = tr_frag(g0);
             ga[1] = tr_frag(g1);
-        } else {
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) ga[cc] = ldfrag<S>(sg, grp, 2 * qt + cc, 4, lane);
         }
         tr_wait2(qn0, qn1);
         // per column tile of q~^T: dT (row tile grp) and, for the wave's own tiles, dk^; the next
