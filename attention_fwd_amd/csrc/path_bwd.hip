@@ -302,20 +302,74 @@ __device__ __forceinline__ void tile2frag(S *dst, int KC, int rt0, int kc0, cons
     stfrag<S>(dst, rt0 + rtl, kc0 + kcl, KC, lane, Elem<S>::from_f32(x));
 }
 
-// X = (I + diag(beta) su(G))^-1 by back substitution: eight lanes per column
-// (64 columns x 8 = 512 threads), each summing every eighth term of a row's
-// dot product.  The lanes of a column are one aligned group of eight in one
-// wave, so X[r][c], written by the group's first lane, is read back by the
-// others in program order.
+// X = (I + diag(beta) su(G))^-1, unit upper triangular, in 16 x 16 blocks (512 threads).
+// With N = diag(beta) su(G) and U = I + N: the diagonal blocks X_II = (I + N_II)^-1 by back
+// substitution, one wave per block, then the blocks above the diagonal by distance from it,
+// one block per wave and level: U X = I gives X_IJ = -X_II T, T = sum_{K=I+1}^{J} N_IK X_KJ,
+// N_IK = diag(beta_I) G_IK (every entry of a block right of the diagonal is above it).
+// Blocks below the diagonal are zero.  The caller synchronises before X is read.
 __device__ __forceinline__ void unit_upper_inverse(float *X, const float *G, const float *beta, int tid) {
-    const int c = tid >> 3, p = tid & 7;
-    for (int r = c + 1 + p; r < kC; r += 8) X[r * kP + c] = 0.f;
-    if (p == 0) X[c * kP + c] = 1.f;
-    for (int r = c - 1; r >= 0; --r) {
-        float s = 0.f;
-        for (int t = r + 1 + p; t <= c; t += 8) s += G[r * kP + t] * X[t * kP + c];
-        s = sum8(s);
-        if (p == 0) X[r * kP + c] = -beta[r] * s;
+    const int wv = tid >> 6, lane = tid & 63;
+    // zero the six blocks below the diagonal: 1536 entries, three per thread
+#pragma unroll
+    for (int e = tid; e < 6 * 256; e += kT) {
+        const int blk = e >> 8, I = blk < 1 ? 1 : (blk < 3 ? 2 : 3), Jb = blk < 1 ? 0 : (blk < 3 ? blk - 1 : blk - 3);
+        X[(16 * I + ((e >> 4) & 15)) * kP + 16 * Jb + (e & 15)] = 0.f;
+    }
+    // (a) diagonal blocks, one per wave: column t of the block, rows r = 4 q + p held by lane
+    //     (t, p); x_r = [r == t] - beta_r sum_{t' > r} G_rt' x_t' (entries not yet known are 0)
+    if (wv < 4) {
+        const int I16 = 16 * wv, t = lane >> 2, p = lane & 3;
+        float xs[4] = {0.f, 0.f, 0.f, 0.f};
+        // the G entries and betas a step uses do not depend on the chain: read PF steps ahead
+        constexpr int PF = 3;
+        float gv[PF][4], bv[PF];
+        auto fetch = [&](int r, int slot) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) gv[slot][q] = G[(I16 + r) * kP + I16 + 4 * q + p];
+            bv[slot] = beta[I16 + r];
+        };
+#pragma unroll
+        for (int k = 0; k < PF; ++k) fetch(15 - k, k);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int r = 15 - k, sl = k % PF;
+            float part = (gv[sl][0] * xs[0] + gv[sl][1] * xs[1]) + (gv[sl][2] * xs[2] + gv[sl][3] * xs[3]);
+            const float br = bv[sl];
+            if (k + PF < 16) fetch(15 - k - PF, sl);
+            part = sum4(part);
+            const float x = (r == t) ? 1.f : (r < t ? -br * part : 0.f);
+            xs[r >> 2] = (p == (r & 3)) ? x : xs[r >> 2];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) X[(I16 + 4 * q + p) * kP + I16 + t] = xs[q];
+    }
+    // (b) blocks above the diagonal as 16x16x4 fp32 matrix-core products.  With the k order
+    //     k(s, g) = 4 g + s (lane group g = lane / 16 supplies k = 4 g + s at step s), register s
+    //     of a 16 x 16 accumulator (rows 4 g .. 4 g + 3, column lane % 16) is the B operand of step
+    //     s, so T feeds the second product from registers.
+    const int i16 = lane & 15, g4 = 4 * (lane >> 4);
+#pragma unroll
+    for (int lev = 1; lev < 4; ++lev) {
+        __syncthreads();
+        if (wv < 4 - lev) {
+            const int Ib = wv, Jb = wv + lev;
+            f32x4 tacc = {0.f, 0.f, 0.f, 0.f};
+            for (int K = Ib + 1; K <= Jb; ++K) {
+                const f32x4 ga = *reinterpret_cast<const f32x4 *>(G + (16 * Ib + i16) * kP + 16 * K + g4);
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    tacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[st], X[(16 * K + g4 + st) * kP + 16 * Jb + i16], tacc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tacc[r] *= beta[16 * Ib + g4 + r];
+            const f32x4 xa = *reinterpret_cast<const f32x4 *>(X + (16 * Ib + i16) * kP + 16 * Ib + g4);
+            f32x4 e = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) e = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[st], tacc[st], e, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) X[(16 * Ib + g4 + r) * kP + 16 * Jb + i16] = -e[r];
+        }
     }
 }
 
