@@ -134,6 +134,17 @@ def test_bwd_bf16_d128(L, fox):
 
 
 @gpu
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L", [65, 130, 200, 333])
+def test_bwd_bf16_partial_tiles(L, d):
+    """bf16 with the gate where the walks' groups of four query blocks are partly idle: 1, 2, 3 and 5
+    query blocks past the first (the idle waves store to the spare set and must not disturb the rest)."""
+    say("case bwd bf16 partial tiles d%d L%d" % (d, L))
+    x, dout, dlse, _, _, grads = run_case(1, 2, L, "bf16", seed=600 + L + d, fox=True, d=d)
+    compare(x, dout, dlse, grads, "bf16", what="partial d%d L%d" % (d, L))
+
+
+@gpu
 @pytest.mark.parametrize("beta", [0.0, 1.0, 2.0])
 def test_bwd_beta_regimes_d128(beta):
     """beta = 0, 1 and 2 at head dimension 128, fp32, with the gate."""
@@ -183,6 +194,38 @@ def test_bwd_full_workload_sampled_heads():
     torch.cuda.synchronize()
     assert pa.bwd_workspace_size(B, H, L, 64, torch.bfloat16) < B * H * pa.bwd_workspace_size(1, 1, L, 64, torch.bfloat16)
     for b, h in ((0, 0), (B - 1, H - 1)):
+        sl = lambda t: t[b:b + 1, h:h + 1].cpu()
+        ref = oracle.bwd(*(sl(x[n]) for n in ("q", "k", "v", "w", "beta")), None, sl(dout), None)
+        for n, t in zip(NAMES, grads):
+            if t is None:
+                continue
+            r = ref[n]
+            e = float(np.abs(to_np(t[b:b + 1, h:h + 1]) - r).max())
+            bar = TOL["bf16"] * max(1.0, float(np.abs(r).max()))
+            assert e <= bar, "head (%d, %d) %s: %.3e > %.3e" % (b, h, n, e, bar)
+        say("  head (%d, %d) ok" % (b, h))
+
+
+@gpu
+def test_bwd_full_workload_sampled_heads_d128():
+    """The whole B32 H32 L4096 d128 bf16 workload through the default workspace (85 heads per pass over
+    8 GiB, as the benchmark times it); the first head, one at a pass boundary and the last head are
+    checked element by element against the oracle run on that head's inputs alone."""
+    c = pathgen.WORKLOADS["sweep_L4096_d128_bf16"]
+    B, H, L, d = c["B"], c["H"], c["L"], c["d"]
+    say("case bwd full workload B%d H%d L%d d%d bf16" % (B, H, L, d))
+    x = pathgen.fwd_inputs(B, H, L, d, "bf16", seed=0, clip=1.98, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    dout = torch.randn((B, H, L, d), generator=g, device="cuda").to(torch.bfloat16)
+    out, lse = pa.fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], None, return_lse=True)
+    grads = pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], None, out, lse, dout)
+    torch.cuda.synchronize()
+    share = pa.bwd_workspace_size(1, 1, L, d, torch.bfloat16)
+    per_pass = pa.bwd_workspace_size(B, H, L, d, torch.bfloat16) // share
+    assert 1 <= per_pass < B * H
+    for flat in (0, per_pass, B * H - 1):
+        b, h = divmod(flat, H)
         sl = lambda t: t[b:b + 1, h:h + 1].cpu()
         ref = oracle.bwd(*(sl(x[n]) for n in ("q", "k", "v", "w", "beta")), None, sl(dout), None)
         for n, t in zip(NAMES, grads):
