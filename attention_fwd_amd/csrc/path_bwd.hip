@@ -27,11 +27,13 @@
 //     the block backward and as matrix-core fragments for the walks; the
 //     diagonal block's dS and value gradient;
 //   down walk (per query block I): q~^(J) for J = I-1 .. 0, stored per pair
-//     with rows queries and, except for bf16 at d = 64, with rows d (the sums
-//     over queries below need the query index inside a lane's fragment; the
-//     bf16 d = 64 key walk gathers that orientation from an LDS copy);
+//     with rows queries and, for fp32 inputs, with rows d (the sums over
+//     queries below need the query index inside a lane's fragment; the bf16
+//     key walks gather that orientation from an LDS copy with transposing
+//     reads);
 //   up walk (per query block I): J = 0 .. I-1, the logits, P and dS from the
-//     stored q~, the adjoint G, stored per pair (rows d), and dq^_I = G^(I-1);
+//     stored q~, the adjoint G, stored per pair (rows d for fp32 inputs, rows
+//     queries for bf16, gathered like q~), and dq^_I = G^(I-1);
 //   key walk (per key block J): over I > J the logits, P and dS again (from
 //     q~, dO, k^, V: recomputing them costs less than moving them), and the
 //     sums dV_J += P^T dO_I, dk^_J += scale dS^T q~, dT_J += G^(J-1)^T q~ --
@@ -45,9 +47,10 @@
 // products with fp32 accumulation for bf16 inputs, fp32 products for fp32),
 // with operands stored in fragment order and the carried q~ and G held as
 // fp32 accumulators, rounded to the element type only as product operands,
-// as in the forward scan.  The per-block kernels use fp32 64 x 64 tiles in
-// LDS (v_mfma_f32_16x16x4f32), looping over 64-wide chunks of the head
-// dimension.
+// as in the forward scan.  The per-block kernels keep fp32 64 x 64 tiles in
+// LDS, looping over 64-wide chunks of the head dimension; their products run
+// on v_mfma_f32_16x16x4f32 for fp32 inputs and on v_mfma_f32_16x16x32_bf16 for
+// bf16 inputs (tiles of input values exact, other operands split hi + lo).
 #include <hip/hip_runtime.h>
 
 #include "path_bwd.h"
@@ -619,7 +622,7 @@ __device__ __forceinline__ void store_transposed(S *dst, const f32x16 *t, S *x, 
 // queries (for the logits) and, with Q2, with rows d (for the key walk's sums
 // over queries), with the gate sum of the blocks strictly between I and J.
 template <typename S, int D, bool Q2>
-__global__ __launch_bounds__(128, (D == 128 && sizeof(S) == 2) ? 3 : 1) void bwd_down_kernel(BwdArgs a) {
+__global__ __launch_bounds__(128) void bwd_down_kernel(BwdArgs a) {
     typedef typename Elem<S>::Frag Frag;
     constexpr int KCD = D / 16, RTD = D / 32;
     __shared__ __attribute__((aligned(16))) S sx[2][D * XScr<S>::kStride];
@@ -675,7 +678,7 @@ __global__ __launch_bounds__(128, (D == 128 && sizeof(S) == 2) ? 3 : 1) void bwd
 // accumulators) G^T <- G^T + (T_J - I)^T G^T + K^_J^T (scale dS^T).  G^(J) is
 // stored with rows d for the pair (I, J + 1); G^(I-1) = dq^_I.
 template <typename S, int D>
-__global__ __launch_bounds__(128, (D == 128 && sizeof(S) == 2) ? 2 : 1) void bwd_up_kernel(BwdArgs a) {
+__global__ __launch_bounds__(128) void bwd_up_kernel(BwdArgs a) {
     typedef typename Elem<S>::Frag Frag;
     constexpr int KCD = D / 16, RTD = D / 32;
     __shared__ __attribute__((aligned(16))) S sx[2][D * XScr<S>::kStride];
@@ -846,19 +849,7 @@ __global__ __launch_bounds__(128, (D == 128 && sizeof(S) == 2) ? 2 : 1) void bwd
     if (h == 0) ((float *)(ws + ly.rso))[qi] = rsum;
 }
 
-// Up walk for bf16 inputs at head dimension 64: as bwd_up_kernel, but four query
-// blocks (eight waves, two per block) share each key block's record (k^, V, k^^T,
-// (T - I)^T: 32 KiB), which is copied global -> LDS one step ahead by the DMA path
-// (global_load_lds, double-buffered), as in the forward scan; each wave prefetches its
-// next stored q~ into registers.  G^(J-1) is stored for the pair (I, J) with rows
-// queries, k over d: the rounded fragments that are the update's B operand, so it needs
-// no transposition; the key walk gathers G^T from it.
-//
-// Every step issues the same memory operations on every wave, whether or not the wave
-// has work in it (a copy for the next record, a q~ prefetch from a clamped valid pair,
-// and the stores of G, to a spare fragment set of the workspace when there is nothing to
-// store), so that one wait for all but the last stores at the top of each step covers
-// every path and the compiler adds no wait of its own inside the step.
+// Shared by the LDS-staged walks below.
 constexpr int kUpQB = 4;  // query blocks per workgroup
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -972,6 +963,19 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_down_kernel_lds(BwdArgs a)
     __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));  // no copy may still be landing in LDS when the workgroup leaves
 }
 
+// Up walk for bf16 inputs at head dimension 64: as bwd_up_kernel, but four query
+// blocks (eight waves, two per block) share each key block's record (k^, V, k^^T,
+// (T - I)^T: 32 KiB), which is copied global -> LDS one step ahead by the DMA path
+// (global_load_lds, double-buffered), as in the forward scan; each wave prefetches its
+// next stored q~ into registers.  G^(J-1) is stored for the pair (I, J) with rows
+// queries, k over d: the rounded fragments that are the update's B operand, so it needs
+// no transposition; the key walk gathers G^T from it.
+//
+// Every step issues the same memory operations on every wave, whether or not the wave
+// has work in it (a copy for the next record, a q~ prefetch from a clamped valid pair,
+// and the stores of G, to a spare fragment set of the workspace when there is nothing to
+// store), so that one wait for all but the last stores at the top of each step covers
+// every path and the compiler adds no wait of its own inside the step.
 __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_lds(BwdArgs a) {
     typedef uint16_t S;
     typedef Elem<S>::Frag Frag;
@@ -2007,15 +2011,12 @@ hipError_t launch_bwd_t(const BwdArgs &a0, hipStream_t st) {
         hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(a.nb, a.hc), dim3(kT), 0, st, a);
         if (a.nb > 1) {
             const dim3 walks((unsigned)((a.nb - 1) * a.hc));
-            if constexpr (sizeof(T) == 2 && D == 64) {
+            if constexpr (sizeof(T) == 2) {
+                // bf16: the LDS-staged walks (four query blocks per workgroup for the down and up walks)
                 const dim3 tiles((unsigned)((a.nb - 1 + kUpQB - 1) / kUpQB * a.hc));
                 hipLaunchKernelGGL(bwd_down_kernel_lds<D>, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
-                hipLaunchKernelGGL(bwd_up_kernel_lds, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
-                hipLaunchKernelGGL(bwd_key_kernel_lds<D>, walks, dim3(64 * KeyCfg<D>::NW), 0, st, a);
-            } else if constexpr (sizeof(T) == 2) {
-                const dim3 tiles((unsigned)((a.nb - 1 + kUpQB - 1) / kUpQB * a.hc));
-                hipLaunchKernelGGL(bwd_down_kernel_lds<D>, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
-                hipLaunchKernelGGL(bwd_up_kernel_split, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
+                if constexpr (D == 64) hipLaunchKernelGGL(bwd_up_kernel_lds, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
+                else hipLaunchKernelGGL(bwd_up_kernel_split, tiles, dim3(64 * 2 * kUpQB), 0, st, a);
                 hipLaunchKernelGGL(bwd_key_kernel_lds<D>, walks, dim3(64 * KeyCfg<D>::NW), 0, st, a);
             } else {
                 hipLaunchKernelGGL((bwd_down_kernel<T, D, true>), walks, dim3(128), 0, st, a);
