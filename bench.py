@@ -165,7 +165,8 @@ def bench_forward(steps, warmup, name=FWD_WORKLOAD):
 def bench_copy(reps=10, nbytes=1 << 31):
     """Plain device streams in the same run, for the HBM rates the memory-bound kernels can be
     compared with: a copy (torch copy_ of nbytes of bf16; GB/s counts read + write), a write-only
-    fill of the same buffer and a read-only sum over three times as many bytes."""
+    fill of the same buffer, a read-only sum over three times as many bytes, and an in-place add
+    b += a (two reads and one write per element: the decode step's mix)."""
     import torch
 
     a = torch.ones(nbytes // 2, device="cuda", dtype=torch.bfloat16)
@@ -187,12 +188,14 @@ def bench_copy(reps=10, nbytes=1 << 31):
     ms = timed(lambda: b.copy_(a))
     ms_fill = timed(lambda: b.fill_(1.0))
     ms_sum = timed(lambda: torch.sum(big, dtype=torch.float32))
+    ms_add = timed(lambda: b.add_(a))
     del a, b, big
     torch.cuda.empty_cache()
     gbs = lambda nb, t: round(nb / (t * 1e-3) / 1e9, 1)
     return {"bytes_moved": 2 * nbytes, "ms": round(ms, 4), "GB_per_s": gbs(2 * nbytes, ms),
             "frac_of_hbm_peak": round(2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "fill_GB_per_s": gbs(nbytes, ms_fill), "read_sum_GB_per_s": gbs(3 * nbytes, ms_sum)}
+            "fill_GB_per_s": gbs(nbytes, ms_fill), "read_sum_GB_per_s": gbs(3 * nbytes, ms_sum),
+            "add_2r1w_GB_per_s": gbs(3 * nbytes, ms_add)}
 
 
 def bench_sweep(steps, warmup):
@@ -649,8 +652,8 @@ def main():
     cache = bench_cache(10, f)
     log("prefill -> decode cache: %.3f ms, %.1f GB/s" % (cache["ms"], cache["GB_per_s"]))
     copy = bench_copy()
-    log("device copy: %.1f GB/s (read + write); fill %.1f GB/s (write); sum %.1f GB/s (read)"
-        % (copy["GB_per_s"], copy["fill_GB_per_s"], copy["read_sum_GB_per_s"]))
+    log("device copy: %.1f GB/s (read + write); fill %.1f GB/s (write); sum %.1f GB/s (read); add %.1f GB/s (2 reads + 1 write)"
+        % (copy["GB_per_s"], copy["fill_GB_per_s"], copy["read_sum_GB_per_s"], copy["add_2r1w_GB_per_s"]))
     log("decode: %s, %d steps" % (DEC_WORKLOAD, args.decode_steps))
     dres = bench_decode(args.decode_steps)
     log("decode: %.3f ms/step" % dres["step_ms"])
