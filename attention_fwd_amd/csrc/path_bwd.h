@@ -19,8 +19,8 @@ struct BwdLayout {
     int64_t xx, aa, qwm, nn, zz, ee;
     // per block, fragments (S): the up walk's record -- k^ (rows keys, k over d), V (rows keys), k^^T
     // (rows d, k over keys) and (T - I)^T of the block transition T (rows d, k over d), contiguous, of
-    // rec_elems elements (parts at 0, 64 D, 128 D, 192 D) -- and dO (rows queries), dO^T (rows d),
-    // T - I (rows d, k over d)
+    // rec_elems elements (parts at 0, 64 D, 128 D, 192 D) -- and dO (rows queries), dO^T (rows d; none
+    // for bf16 inputs), T - I (rows d, k over d)
     int64_t urec, rec_elems, do1, do2, nt;
     // fp32 [Lp, D]: q^; the diagonal value gradient; walk outputs dq^, dk^, dv; W dT and W dT^T of the
     // block backward

@@ -551,7 +551,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
         __syncthreads();
         tile2frag<S, false>(V1, KCD, 0, 4 * c, bQ, tid);   // V: rows keys
         tile2frag<S, false>(DO1, KCD, 0, 4 * c, bK, tid);  // dO: rows queries
-        tile2frag<S, true>(DO2, 4, 2 * c, 0, bK, tid);     // dO^T: rows d
+        if constexpr (sizeof(S) == 4) tile2frag<S, true>(DO2, 4, 2 * c, 0, bK, tid);  // dO^T: rows d (fp32 only)
         acc = zero8();
         mmx<T, false, true>(acc, tr(bG), nat(bK), lane, wave);  // diagonal value gradient P^T dO
         acc2g((float *)(ws + ly.dvd) + (int64_t)row0 * D + 64 * c, D, acc, lane, wave);
@@ -1754,15 +1754,14 @@ __global__ __launch_bounds__(kT) void bwd_gate_kernel(BwdArgs a) {
 
 // Key walk for bf16 inputs: as bwd_key_kernel (the same waves: query half qt = w & 1,
 // key half kt = (w >> 1) & 1, head-dimension group dh = w >> 2), but each step's
-// operands -- the pair's q~ (rows queries) and G^T, the query block's dO in both
-// orientations, its exponent terms and the pair's gate sum: 32.8 KiB at d = 64, 64.8
-// KiB at d = 128 -- are copied global -> LDS one step ahead (global_load_lds,
-// double-buffered) and read by every wave from there.  The q~^T fragments (rows d, k
-// over queries) are gathered from the q~ copy with transposing LDS reads, so the down
-// walk stores q~ in one orientation only.  At d = 128 the registers do not hold k^ and V of
-// the key tile besides the accumulators: they are read from an LDS copy, and dO^T is
-// gathered from the dO copy like q~^T (the buffers then hold q~, G and dO: 48.8 KiB).
-// G^T is gathered the same way: the up walk stores G with rows queries.
+// operands -- the pair's q~ (rows queries) and G, the query block's dO (rows queries),
+// its exponent terms and the pair's gate sum: 24.8 KiB at d = 64, 48.8 KiB at d = 128 --
+// are copied global -> LDS one step ahead (global_load_lds, double-buffered) and read by
+// every wave from there.  The fragments with k over queries -- q~^T, G^T and dO^T (rows
+// d) -- are gathered from those copies with transposing LDS reads, so the down and up
+// walks store q~ and G in one orientation only and dO^T is not stored at all.  At d = 128
+// the registers do not hold k^ and V of the key tile besides the accumulators: they are
+// read from an LDS copy.
 template <int D>
 __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs a) {
     typedef uint16_t S;
@@ -1771,12 +1770,12 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
     constexpr int KCD = D / 16, RTD = D / 32, RTW = K::RTW, NTH = 64 * K::NW;
     static_assert(K::TRW == 1, "one row tile of dT per wave");
     constexpr int NACC = 2 * RTW + RTD;      // dV^T, dk^^T (RTW each), dT row tile grp (RTD column tiles)
-    constexpr bool KVL = D == 128;           // k^, V from LDS; dO^T gathered from dO
-    constexpr int NSET = KVL ? 3 : 4;        // fragment sets per buffer
+    constexpr bool KVL = D == 128;           // k^, V from LDS
+    constexpr int NSET = 3;                  // fragment sets per buffer: q~, G, dO
     constexpr int FR = kC * D;               // elements of a 64 x D fragment set
     constexpr int NLD = FR * 2 / 16 / NTH;   // 16-byte copies per thread and fragment set
     static_assert(FR * 2 % (16 * NTH) == 0, "a fragment set must split evenly over the workgroup");
-    // a buffer: q~, G^T, dO (rows queries), [dO^T (rows d)], then 64 floats each of the query
+    // a buffer: q~, G, dO (rows queries), then 64 floats each of the query
     // terms dd and cq and of the gate sum (the same value 64 times); with KVL, k^ and V of the
     // key block after the two buffers
     constexpr int BUF = NSET * FR * 2 + 3 * 4 * kC;
@@ -1790,7 +1789,7 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
     const S *QS1 = (const S *)(ws + ly.qs1), *GS2 = (const S *)(ws + ly.gs2);
-    const S *DO1 = (const S *)(ws + ly.do1), *DO2 = (const S *)(ws + ly.do2);
+    const S *DO1 = (const S *)(ws + ly.do1);
     const float *MID = (const float *)(ws + ly.mid);
     const float *DD = (const float *)(ws + ly.dd), *CQL = (const float *)(ws + ly.cql);
     const float scale = a.scale, c2 = scale * kLog2e;
@@ -1805,7 +1804,6 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
         dma_record<NTH, NLD>(QS1 + po, buf, tid);
         dma_record<NTH, NLD>(GS2 + po, buf + FR * 2, tid);
         dma_record<NTH, NLD>(DO1 + bo, buf + 2 * FR * 2, tid);
-        if constexpr (!KVL) dma_record<NTH, NLD>(DO2 + bo, buf + 3 * FR * 2, tid);
         const float *src = w == 0 ? DD + I * kC + lane : w == 1 ? CQL + I * kC + lane : MID + pair_index(I, J);
         __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(buf + NSET * FR * 2 + 4 * kC * min(w, 2)), 4, 0,
                                          0);
@@ -1861,7 +1859,7 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
     auto step = [&](int I, auto bsel) {
         constexpr int B = decltype(bsel)::value;
         const unsigned char *buf = smem + B * BUF;
-        const S *sq = (const S *)buf, *sg = sq + FR, *so1 = sq + 2 * FR, *so2 = sq + 3 * FR;
+        const S *sq = (const S *)buf, *sg = sq + FR, *so1 = sq + 2 * FR;
         const float *sdd = (const float *)(buf + NSET * FR * 2), *scq = sdd + kC, *smid = scq + kC;
         // this wave's copies of step I have landed and its LDS reads of the previous step have
         // returned; after the barrier every wave's copies have landed and the other buffer is free
@@ -1899,19 +1897,12 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
             pf[cc] = acc_frag<S>(dp, cc);
             sf[cc] = acc_frag<S>(s, cc);
         }
-        // dV^T += dO^T P^T (dO^T: the LDS copy, or gathered from dO)
+        // dV^T += dO^T P^T (dO^T gathered from the dO copy)
 #pragma unroll
         for (int i = 0; i < RTW; ++i) {
-            Frag ob[2];
-            if constexpr (KVL) {
-                TrF t0 = tr_issue(so1, dh * RTW + i, 2 * qt), t1 = tr_issue(so1, dh * RTW + i, 2 * qt + 1);
-                tr_wait2(t0, t1);
-                ob[0] = tr_frag(t0);
-                ob[1] = tr_frag(t1);
-            } else {
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) ob[cc] = ldfrag<S>(so2, dh * RTW + i, 2 * qt + cc, 4, lane);
-            }
+            TrF t0 = tr_issue(so1, dh * RTW + i, 2 * qt), t1 = tr_issue(so1, dh * RTW + i, 2 * qt + 1);
+            tr_wait2(t0, t1);
+            const Frag ob[2] = {tr_frag(t0), tr_frag(t1)};
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) Elem<S>::mma(acc[i], ob[cc], pf[cc]);
         }

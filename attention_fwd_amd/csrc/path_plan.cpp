@@ -43,7 +43,8 @@ BwdLayout bwd_layout(int L, int D, int es) {
     ly.xx = take(tok); ly.aa = take(tok); ly.qwm = take(tok); ly.nn = take(tok); ly.zz = take(tok); ly.ee = take(tok);
     ly.rec_elems = 3 * 64 * (int64_t)D + (int64_t)D * D;
     ly.urec = take(nb * ly.rec_elems * es);
-    ly.do1 = take(fr); ly.do2 = take(fr);
+    // dO^T: not stored for bf16, whose key walk gathers it from dO
+    ly.do1 = take(fr); ly.do2 = take(es == 2 ? 0 : fr);
     ly.nt = take(frd);
     ly.qh = take(nat); ly.dvd = take(nat); ly.dqo = take(nat); ly.dko = take(nat); ly.dvo = take(nat);
     ly.uu = take(nat); ly.vv = take(nat);
