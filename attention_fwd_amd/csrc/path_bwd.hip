@@ -853,6 +853,28 @@ __global__ __launch_bounds__(128) void bwd_up_kernel(BwdArgs a) {
 constexpr int kUpQB = 4;  // query blocks per workgroup
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Work item of a walk launch with nu units (query tiles or key blocks) per head over hc
+// heads, for a kernel that keeps wpc workgroups on a compute unit.  Workgroups are dealt
+// round-robin over gfx950's 8 XCDs, each with its own L2 and 32 compute units: the items
+// are numbered XCD by XCD, so that every XCD takes a contiguous range of heads, in groups
+// of about two rounds of its workgroup slots.  Inside a group, rank r (0: the longest walk)
+// runs on every head of the group before rank r + 1, so the group's walks read the same
+// key or query blocks at about the same time and share them through the XCD's L2.
+// Returns the head (gl) and the rank (r).
+constexpr int kXcds = 8, kCusPerXcd = 32;
+__device__ __forceinline__ void walk_item(int nu, int hc, int wpc, int &gl, int &r) {
+    // the grid (nu hc workgroups) is below 2^31, so 32-bit arithmetic suffices
+    const unsigned total = (unsigned)nu * (unsigned)hc, x = blockIdx.x;
+    const unsigned q = total / kXcds, rem = total % kXcds, k = x % kXcds;
+    const unsigned item = k * q + min(k, rem) + x / kXcds;  // XCD k holds items [k q + min(k, rem), ...)
+    const unsigned G = (unsigned)max(1, 2 * kCusPerXcd * wpc / nu);
+    const unsigned gbase = item / (G * (unsigned)nu) * G;  // first head of the item's group
+    const unsigned gn = min(G, (unsigned)hc - gbase);
+    const unsigned rank = item - gbase * (unsigned)nu;
+    gl = (int)(gbase + rank % gn);
+    r = (int)(rank / gn);
+}
+
 // Copy NLD 16-byte chunks per thread of a contiguous record into LDS (lane l of a wave
 // lands at the wave's LDS base + 16 l); completion is tracked by vmcnt.
 template <int NTH, int NLD>
@@ -893,7 +915,9 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_down_kernel_lds(BwdArgs a)
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int nb = a.nb, hc = a.hc;
     const int ntile = (nb - 1 + kUpQB - 1) / kUpQB;  // query blocks 1 .. nb-1, four per tile
-    const int gl = blockIdx.x % hc, tile = ntile - 1 - blockIdx.x / hc;
+    int gl, tile;
+    walk_item(ntile, hc, 2, gl, tile);
+    tile = ntile - 1 - tile;
     const int I0 = 1 + kUpQB * tile, Imax = min(nb - 1, I0 + kUpQB - 1);
     const int I = __builtin_amdgcn_readfirstlane(I0 + (w >> 1)), wq = __builtin_amdgcn_readfirstlane(w & 1);
     const bool active = I <= nb - 1;
@@ -993,7 +1017,9 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_lds(BwdArgs a) {
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int nb = a.nb, hc = a.hc;
     const int ntile = (nb - 1 + kUpQB - 1) / kUpQB;  // query blocks 1 .. nb-1, four per tile
-    const int gl = blockIdx.x % hc, tile = ntile - 1 - blockIdx.x / hc;
+    int gl, tile;
+    walk_item(ntile, hc, 1, gl, tile);
+    tile = ntile - 1 - tile;
     const int I0 = 1 + kUpQB * tile;                 // the tile's first query block
     const int Imax = min(nb - 1, I0 + kUpQB - 1);    // and its last
     // this wave's query block and query half (wave-uniform, so the per-pair scalars are scalar loads)
@@ -1144,7 +1170,9 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_split(BwdArgs a)
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int nb = a.nb, hc = a.hc;
     const int ntile = (nb - 1 + kUpQB - 1) / kUpQB;
-    const int gl = blockIdx.x % hc, tile = ntile - 1 - blockIdx.x / hc;
+    int gl, tile;
+    walk_item(ntile, hc, 1, gl, tile);
+    tile = ntile - 1 - tile;
     const int I0 = 1 + kUpQB * tile, Imax = min(nb - 1, I0 + kUpQB - 1);
     const int I = __builtin_amdgcn_readfirstlane(I0 + (w >> 1)), wq = __builtin_amdgcn_readfirstlane(w & 1);
     const bool active = I <= nb - 1;
@@ -1785,7 +1813,8 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
     const int qt = w & 1, kt = (w >> 1) & 1, dh = w >> 2, grp = kt + 2 * dh;
     const int nb = a.nb, hc = a.hc;
-    const int gl = blockIdx.x % hc, J = blockIdx.x / hc;
+    int gl, J;  // head and key block; J = 0 (the longest walk) first
+    walk_item(nb - 1, hc, K::NW == 4 ? 2 : 1, gl, J);
     const BwdLayout &ly = a.ly;
     char *ws = (char *)a.ws + (int64_t)gl * ly.head;
     const S *QS1 = (const S *)(ws + ly.qs1), *GS2 = (const S *)(ws + ly.gs2);
@@ -1811,7 +1840,7 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
     const S *rec = (const S *)(ws + ly.urec) + J * ly.rec_elems;  // k^ (rows keys, k over d), then V
     const S *skv = (const S *)(smem + 2 * BUF);
     if constexpr (KVL) dma_record<NTH, 2 * NLD>(rec, smem + 2 * BUF, tid);
-    issue(J + 1, 0);
+    issue(nb - 1, 0);
     // k^ and V of key tile kt, k over d: the B operands of S and dP (registers, or the LDS copy)
     Frag kf[KVL ? 1 : KCD], vf[KVL ? 1 : KCD];
     if constexpr (!KVL) {
@@ -1855,7 +1884,9 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
     };
     auto tr_frag = [](const TrF &t) { return __builtin_bit_cast(Frag, u32x4{t.lo.x, t.lo.y, t.hi.x, t.hi.y}); };
     __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
-    // one step over query block I, whose copies are in buffer B ((I - J - 1) % 2); it refills the other
+    // one step over query block I, whose copies are in buffer B ((nb - 1 - I) % 2); it refills the
+    // other.  The walk runs I = nb - 1 .. J + 1, so that the key walks of a head start on the same
+    // query block and read its dO and query terms at about the same time.
     auto step = [&](int I, auto bsel) {
         constexpr int B = decltype(bsel)::value;
         const unsigned char *buf = smem + B * BUF;
@@ -1865,7 +1896,7 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
         // returned; after the barrier every wave's copies have landed and the other buffer is free
         __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));
         asm volatile("s_barrier" ::: "memory");
-        issue(min(I + 1, nb - 1), 1 - B);
+        issue(max(I - 1, J + 1), 1 - B);
         asm volatile("" ::: "memory");
         f32x16 s = {}, dp = {};
 #pragma unroll
@@ -1936,9 +1967,9 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel_lds(BwdArgs
             if (ct + 1 < RTD) tr_wait2(qn0, qn1);
         }
     };
-    for (int I = J + 1; I < nb; I += 2) {
+    for (int I = nb - 1; I > J; I -= 2) {
         step(I, std::integral_constant<int, 0>{});
-        if (I + 1 < nb) step(I + 1, std::integral_constant<int, 1>{});
+        if (I - 1 > J) step(I - 1, std::integral_constant<int, 1>{});
     }
     __builtin_amdgcn_s_waitcnt(vm_lgkm0(0));  // the last (unused) copy has landed
     csum = other_half_sum(csum);  // lanes l and l ^ 32 hold the other queries of the same key
