@@ -1753,6 +1753,333 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(BwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Block backward for bf16 inputs: the same steps as bwd_block_kernel, with every
+// 64x64 tile held in LDS already split for the bf16 products.
+// ---------------------------------------------------------------------------
+// A split tile is two planes of bf16 numbers, hi and lo, with x ~ hi + lo (hi = x rounded,
+// lo = the rest rounded: about 16 significant bits; lo = 0 for a tile of bf16 input values).
+// Each element is split once, when the tile is written, instead of by every wave that reads it
+// in a product.  Rows of 64 elements; the 16-byte chunks of row r are swizzled (chunk c / 8 at
+// position (c / 8) ^ (r % 8)), which spreads both the row-wise 16-byte reads of 16 consecutive
+// rows and the transposing reads below over the LDS banks.
+constexpr int kSP = kC * kC;  // elements per plane; a tile is 2 kSP bf16 (hi plane, then lo)
+__device__ __forceinline__ int sidx(int r, int c) { return r * kC + ((((c >> 3) ^ r) & 7) << 3) + (c & 7); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// A split tile as a product operand: t false, element (r, c) = tile[r][c]; t true, tile[c][r].
+struct SMat {
+    const uint16_t *p;
+    bool t;
+};
+__device__ __forceinline__ SMat snat(const uint16_t *p) { return {p, false}; }
+__device__ __forceinline__ SMat str(const uint16_t *p) { return {p, true}; }
+
+// Operand fragment of v_mfma_f32_16x16x32_bf16 for k = k0 .. k0 + 31 from one plane: lane
+// l = 16 q + i holds index rho0 + i (a row of A, a column of B) and k = k0 + 8 q + e, e = 0..7.
+// KC (k runs along the plane's rows, element (rho, k) at [rho][k]): one 16-byte read.
+// Otherwise (element at [k][rho]) two transposing reads: ds_read_b64_tr_b16 gives lane 16 g + i
+// (in each group of 16 lanes) element i % 4 of the 8-byte chunks addressed by lanes 16 g + 4 t +
+// i / 4, t = 0..3, as its elements t; lane 16 g + 4 t + j addresses elements rho0 + 4 j .. + 3 of
+// row k0 + 8 g + t (second read: row k0 + 8 g + 4 + t).
+template <bool KC>
+__device__ __forceinline__ i16x8 sfrag(const uint16_t *pl, int rho0, int k0, int lane) {
+    if constexpr (KC) {
+        const int q = lane >> 4, i = lane & 15;
+        return *reinterpret_cast<const i16x8 *>(pl + sidx(rho0 + i, k0 + 8 * q));
+    } else {
+        const int g = lane >> 4, t = (lane >> 2) & 3, j = lane & 3;
+        const uint16_t *p1 = pl + sidx(k0 + 8 * g + t, rho0 + 4 * j);
+        const uint16_t *p2 = pl + sidx(k0 + 8 * g + 4 + t, rho0 + 4 * j);
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+        const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p2);
+        return i16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    }
+}
+// A's fragment: rho is A's row, k contiguous unless A is the transposed view.
+__device__ __forceinline__ i16x8 afrag(SMat A, int plane, int rho0, int k0, int lane) {
+    const uint16_t *pl = A.p + plane * kSP;
+    return A.t ? sfrag<false>(pl, rho0, k0, lane) : sfrag<true>(pl, rho0, k0, lane);
+}
+// B's fragment: rho is B's column; B(k, c) = tile[c][k] (k contiguous) for the transposed view.
+__device__ __forceinline__ i16x8 bfrag(SMat B, int plane, int rho0, int k0, int lane) {
+    const uint16_t *pl = B.p + plane * kSP;
+    return B.t ? sfrag<true>(pl, rho0, k0, lane) : sfrag<false>(pl, rho0, k0, lane);
+}
+
+// acc += A * B on split tiles, the output layout of mm; EA, EB: the operand is a tile of bf16
+// input values (lo = 0), so its lo products are skipped.  hi*hi + hi*lo + lo*hi otherwise.
+template <bool EA, bool EB>
+__device__ __forceinline__ void smm(f32x8 &acc, SMat A, SMat B, int lane, int wave) {
+    const int r0 = 16 * (wave >> 1), c0 = 32 * (wave & 1);
+    f32x4 lo = acc.lo, hi = acc.hi;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const int k0 = 32 * st;
+        const i16x8 ah = afrag(A, 0, r0, k0, lane);
+        i16x8 al;
+        if constexpr (!EA) al = afrag(A, 1, r0, k0, lane);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const i16x8 bh = bfrag(B, 0, c0 + 16 * ct, k0, lane);
+            i16x8 bl;
+            if constexpr (!EB) bl = bfrag(B, 1, c0 + 16 * ct, k0, lane);
+            f32x4 &c = ct == 0 ? lo : hi;
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+            if constexpr (!EB) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+            if constexpr (!EA) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+        }
+    }
+    acc.lo = lo;
+    acc.hi = hi;
+}
+
+// Element access and writes of split tiles.
+__device__ __forceinline__ float sld(const uint16_t *p, int r, int c) {
+    const int e = sidx(r, c);
+    return bf16_to_f32(p[e]) + bf16_to_f32(p[kSP + e]);
+}
+__device__ __forceinline__ void sst(uint16_t *p, int r, int c, float x) {
+    const int e = sidx(r, c);
+    const uint16_t h = to_bf16(x);
+    p[e] = h;
+    p[kSP + e] = to_bf16(x - bf16_to_f32(h));
+}
+template <typename F>
+__device__ __forceinline__ void sstore(uint16_t *p, const f32x8 &acc, int lane, int wave, F f) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const int r = arow(v, lane, wave), c = acol(v, lane, wave);
+        sst(p, r, c, f(r, c, acc[v]));
+    }
+}
+// Eight consecutive elements (one 16-byte chunk) of row r, split, into both planes.
+__device__ __forceinline__ void sput8(uint16_t *p, int r, int c8, const float *x) {
+    u32x4 h, l;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        h[t] = pack_bf16(x[2 * t], x[2 * t + 1]);
+        l[t] = pack_bf16(x[2 * t] - __uint_as_float(h[t] << 16), x[2 * t + 1] - __uint_as_float(h[t] & 0xffff0000u));
+    }
+    const int e = sidx(r, c8);
+    *reinterpret_cast<u32x4 *>(p + e) = h;
+    *reinterpret_cast<u32x4 *>(p + kSP + e) = l;
+}
+// Global fp32 matrix [64 rows][row stride gs] -> split tile (one chunk per thread).
+__device__ __forceinline__ void sg2l(uint16_t *p, const float *g, int gs, int tid) {
+    const int r = tid >> 3, c8 = (tid & 7) * 8;
+    float x[8];
+    load8(x, g + (int64_t)r * gs + c8);
+    sput8(p, r, c8, x);
+}
+// Columns c0 .. c0+63 of bf16 input rows [row0, row0 + 64) (rows >= L read as 0) -> split tile.
+__device__ __forceinline__ void sin2l(uint16_t *p, const uint16_t *g, int D, int c0, int row0, int L, int tid) {
+    const int r = tid >> 3, c8 = (tid & 7) * 8;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 h = row0 + r < L ? *reinterpret_cast<const u32x4 *>(g + (int64_t)(row0 + r) * D + c0 + c8) : z;
+    const int e = sidx(r, c8);
+    *reinterpret_cast<u32x4 *>(p + e) = h;
+    *reinterpret_cast<u32x4 *>(p + kSP + e) = z;
+}
+__device__ __forceinline__ void szero(uint16_t *p, int tid) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int r = tid >> 3, c8 = (tid & 7) * 8, e = sidx(r, c8);
+    *reinterpret_cast<u32x4 *>(p + e) = z;
+    *reinterpret_cast<u32x4 *>(p + kSP + e) = z;
+}
+
+template <int D>
+__global__ __launch_bounds__(kT) void bwd_block_kernel_bf16(BwdArgs a) {
+    typedef uint16_t T;
+    constexpr int NCH = D / 64;
+    constexpr int TS = 2 * kSP;  // elements of a split tile
+    __shared__ __attribute__((aligned(16))) uint16_t sm[9 * TS];
+    __shared__ float sB[kC], sRed[kC];
+    uint16_t *bE = sm, *bN = bE + TS, *bZ = bN + TS, *bX = bZ + TS, *bA = bX + TS, *bQW = bA + TS, *b6 = bQW + TS,
+             *b7 = b6 + TS, *b8 = b7 + TS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int J = blockIdx.x, gl = blockIdx.y, g = a.g0 + gl, L = a.L, nb = a.nb, row0 = J * kC;
+    const int64_t hoff = (int64_t)g * L;
+    const T *q = (const T *)a.q + hoff * D, *k = (const T *)a.k + hoff * D, *w = (const T *)a.w + hoff * D;
+    const BwdLayout &ly = a.ly;
+    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
+    const bool hasQ = J >= 1, hasK = J <= nb - 2, hasT = J >= 1 && J <= nb - 2;
+    const int64_t tok = (int64_t)J * kC * kC, nat0 = (int64_t)row0 * D;
+    const float *dqo = (const float *)(ws + ly.dqo) + nat0, *dko = (const float *)(ws + ly.dko) + nat0;
+
+    if (tid < kC) sB[tid] = row0 + tid < L ? a.beta[hoff + row0 + tid] : 0.f;
+    sg2l(bE, (const float *)(ws + ly.ee) + tok, kC, tid);  // scale dS of the diagonal block
+    sg2l(bN, (const float *)(ws + ly.nn) + tok, kC, tid);
+    sg2l(bZ, (const float *)(ws + ly.zz) + tok, kC, tid);
+    sg2l(bX, (const float *)(ws + ly.xx) + tok, kC, tid);
+    sg2l(bA, (const float *)(ws + ly.aa) + tok, kC, tid);
+    sg2l(bQW, (const float *)(ws + ly.qwm) + tok, kC, tid);
+    __syncthreads();
+    // ---- token-level quantities
+    f32x8 aZ = zero8(), aNn = zero8(), aY = zero8(), aG = zero8(), aA = zero8(), acc;
+    smm<false, false>(aZ, snat(bE), snat(bN), lane, wave);  // E N         (dZ = -(E N + dq^ W^T))
+    smm<false, false>(aNn, str(bE), snat(bZ), lane, wave);  // E^T Z       (dN = -E^T Z + dY A^T)
+    for (int c = 0; c < NCH; ++c) {
+        __syncthreads();
+        sin2l(b6, w, D, 64 * c, row0, L, tid);
+        if (hasQ) sg2l(b7, dqo + 64 * c, D, tid);
+        else szero(b7, tid);
+        if (hasK) sg2l(b8, dko + 64 * c, D, tid);
+        else szero(b8, tid);
+        __syncthreads();
+        smm<false, true>(aZ, snat(b7), str(b6), lane, wave);  // + dq^ W^T
+        smm<false, true>(aY, snat(b8), str(b6), lane, wave);  // dk^ W^T   (dY = -dk^ W^T)
+        smm<true, true>(aG, snat(b6), str(b6), lane, wave);   // G = W W^T
+    }
+    if (hasT) {
+        // U = W dT and V' = W dT^T (64 x D, for the backward through T = I - W^T A W) and
+        // U W^T = W dT W^T; the key walk left dT^T, so dT[c2, c] = (dT^T[c, c2])^T
+        const float *dtt = (const float *)(ws + ly.dtt) + (int64_t)J * D * D;
+        float *uu = (float *)(ws + ly.uu) + nat0, *vv = (float *)(ws + ly.vv) + nat0;
+        for (int c = 0; c < NCH; ++c) {
+            f32x8 aU = zero8(), aV = zero8();
+            for (int c2 = 0; c2 < NCH; ++c2) {
+                __syncthreads();
+                sin2l(b6, w, D, 64 * c2, row0, L, tid);
+                sg2l(b7, dtt + (int64_t)(64 * c) * D + 64 * c2, D, tid);  // dT^T block (c, c2)
+                sg2l(b8, dtt + (int64_t)(64 * c2) * D + 64 * c, D, tid);  // dT^T block (c2, c)
+                __syncthreads();
+                smm<true, false>(aU, snat(b6), str(b7), lane, wave);   // W_c2 dT[c2, c]
+                smm<true, false>(aV, snat(b6), snat(b8), lane, wave);  // W_c2 dT^T[c2, c]
+            }
+            acc2g(uu + 64 * c, D, aU, lane, wave);
+            acc2g(vv + 64 * c, D, aV, lane, wave);
+            __syncthreads();
+            sstore(b7, aU, lane, wave, Id());
+            sin2l(b6, w, D, 64 * c, row0, L, tid);
+            __syncthreads();
+            acc = zero8();
+            smm<false, true>(acc, snat(b7), str(b6), lane, wave);  // U_c W_c^T
+#pragma unroll
+            for (int v = 0; v < 8; ++v) aA[v] -= acc[v];  // dA = -W dT W^T + ...
+        }
+    }
+    __syncthreads();
+    sstore(b6, aY, lane, wave, [](int, int, float x) { return -x; });  // dY
+    sstore(b7, aZ, lane, wave, [](int, int, float x) { return -x; });  // dZ
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 8; ++v) aNn[v] = -aNn[v];
+    smm<false, false>(aNn, snat(b6), str(bA), lane, wave);   // dN = -E^T Z + dY A^T
+    smm<false, false>(aA, str(bN), snat(b6), lane, wave);    // dA += N^T dY
+    smm<false, false>(aA, str(b7), snat(bQW), lane, wave);   // dA += dZ^T QWm
+    acc = zero8();
+    smm<false, false>(acc, snat(b7), snat(bA), lane, wave);  // dQWm = (dZ A) o [r <= i]
+    f32x8 aYv = zero8();
+    smm<false, false>(aYv, snat(bN), snat(bA), lane, wave);  // Y = N A
+    __syncthreads();
+    sstore(b8, acc, lane, wave, [](int r, int c, float x) { return c <= r ? x : 0.f; });  // dQWm
+    sstore(b6, aNn, lane, wave, [](int r, int c, float x) { return c > r ? x : 0.f; });   // dKW = dN o [r > j]
+    sstore(bN, aYv, lane, wave, Id());                                                    // Y (N is done with)
+    // A = X diag(beta): dX = dA diag(beta), dbeta_c += sum_r X_rc dA_rc (dA kept on the upper triangle)
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const int r = arow(v, lane, wave), c = acol(v, lane, wave);
+        aA[v] = c >= r ? aA[v] : 0.f;
+        sst(b7, r, c, aA[v] * sB[c]);
+        sst(bQW, r, c, sld(bX, r, c) * aA[v]);
+    }
+    __syncthreads();
+    float dbeta = 0.f;
+    if (tid < kC)
+        for (int r = 0; r < kC; ++r) dbeta += sld(bQW, r, tid);
+    acc = zero8();
+    smm<false, false>(acc, str(bX), snat(b7), lane, wave);  // X^T dX
+    __syncthreads();
+    sstore(bQW, acc, lane, wave, Id());
+    __syncthreads();
+    f32x8 dTp = zero8();
+    smm<false, false>(dTp, snat(bQW), str(bX), lane, wave);  // (X^T dX) X^T; dT' is its negative
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const int r = arow(v, lane, wave), c = acol(v, lane, wave);
+        const float t = -dTp[v];
+        sst(bQW, r, c, c > r ? t * aG[v] : 0.f);  // dbeta_r += sum_c dT'_rc G_rc
+        sst(b7, r, c, c > r ? sB[r] * t : 0.f);   // dG = diag(beta) dT' on the strict upper triangle
+    }
+    __syncthreads();
+    if (tid >= kC && tid < 2 * kC) {
+        float s = 0.f;
+        for (int c = 0; c < kC; ++c) s += sld(bQW, tid - kC, c);
+        sRed[tid - kC] = s;
+    }
+    __syncthreads();
+    if (tid < kC && row0 + tid < L) a.dbeta[hoff + row0 + tid] = dbeta + sRed[tid];
+    // ---- chunks of the head dimension.  LDS: E, Y (bN), Z, A, dKW (b6), dG (b7), dQWm (b8);
+    //      bX and bQW hold the chunk operands.
+    const float *uu = (const float *)(ws + ly.uu) + nat0, *vvp = (const float *)(ws + ly.vv) + nat0;
+    for (int c = 0; c < NCH; ++c) {
+        f32x8 dQ = zero8(), dK = zero8(), dW = zero8();
+        __syncthreads();
+        sin2l(bX, k, D, 64 * c, row0, L, tid);
+        sin2l(bQW, q, D, 64 * c, row0, L, tid);
+        __syncthreads();
+        smm<false, true>(dQ, snat(bE), snat(bX), lane, wave);  // E K
+        smm<false, true>(dK, str(bE), snat(bQW), lane, wave);  // E^T Q
+        smm<false, true>(dW, str(b6), snat(bX), lane, wave);   // dKW^T K
+        smm<false, true>(dW, str(b8), snat(bQW), lane, wave);  // dQWm^T Q
+        __syncthreads();
+        sin2l(bX, w, D, 64 * c, row0, L, tid);
+        __syncthreads();
+        smm<false, true>(dQ, snat(b8), snat(bX), lane, wave);  // dQWm W
+        smm<false, true>(dK, snat(b6), snat(bX), lane, wave);  // dKW W
+        smm<false, true>(dW, snat(b7), snat(bX), lane, wave);  // (dG + dG^T) W
+        smm<false, true>(dW, str(b7), snat(bX), lane, wave);
+        __syncthreads();
+        if (hasQ) sg2l(bX, dqo + 64 * c, D, tid);
+        else szero(bX, tid);
+        if (hasK) sg2l(bQW, dko + 64 * c, D, tid);
+        else szero(bQW, tid);
+        __syncthreads();
+        acc = zero8();
+        smm<false, false>(acc, str(bZ), snat(bX), lane, wave);   // Z^T dq^
+        smm<false, false>(acc, str(bN), snat(bQW), lane, wave);  // + Y^T dk^ (= A^T N^T dk^)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const int r = arow(v, lane, wave), cc = acol(v, lane, wave);
+            dQ[v] += sld(bX, r, cc);
+            dK[v] += sld(bQW, r, cc);
+            dW[v] -= acc[v];
+        }
+        if (hasT) {
+            __syncthreads();
+            sg2l(bX, uu + 64 * c, D, tid);
+            sg2l(bQW, vvp + 64 * c, D, tid);
+            __syncthreads();
+            acc = zero8();
+            smm<false, false>(acc, snat(bA), snat(bQW), lane, wave);  // A W dT^T
+            smm<false, false>(acc, str(bA), snat(bX), lane, wave);    // + A^T W dT
+#pragma unroll
+            for (int v = 0; v < 8; ++v) dW[v] -= acc[v];
+        }
+        acc2out((T *)a.dq + hoff * D + 64 * c, D, dQ, row0, L, lane, wave);
+        acc2out((T *)a.dk + hoff * D + 64 * c, D, dK, row0, L, lane, wave);
+        acc2out((T *)a.dw + hoff * D + 64 * c, D, dW, row0, L, lane, wave);
+    }
+    {
+        const float *dvd = (const float *)(ws + ly.dvd) + nat0, *dvo = (const float *)(ws + ly.dvo) + nat0;
+        T *dv = (T *)a.dv + hoff * D;
+        for (int e = tid; e < kC * D; e += kT) {
+            const int r = e / D;
+            if (row0 + r < L) dv[(int64_t)row0 * D + e] = Elem<T>::from_float(dvd[e] + (hasK ? dvo[e] : 0.f));
+        }
+    }
+    if (tid < kC) {
+        const int i = row0 + tid;
+        const float rs = ((const float *)(ws + ly.rsd))[i] + (hasQ ? ((const float *)(ws + ly.rso))[i] : 0.f);
+        const float cs = ((const float *)(ws + ly.csd))[i] + (hasK ? ((const float *)(ws + ly.cso))[i] : 0.f);
+        ((float *)(ws + ly.dc))[i] = rs - cs;
+    }
+}
+
 // dlogf_t = sum_{t' >= t} dc_t' for one head: 512 threads, contiguous chunks, fixed order.
 __global__ __launch_bounds__(kT) void bwd_gate_kernel(BwdArgs a) {
     __shared__ float part[kT];
@@ -2046,7 +2373,8 @@ hipError_t launch_bwd_t(const BwdArgs &a0, hipStream_t st) {
                 hipLaunchKernelGGL((bwd_key_kernel<T, D>), walks, dim3(64 * KeyCfg<D>::NW), 0, st, a);
             }
         }
-        hipLaunchKernelGGL((bwd_block_kernel<T, D>), dim3(a.nb, a.hc), dim3(kT), 0, st, a);
+        if constexpr (sizeof(T) == 2) hipLaunchKernelGGL(bwd_block_kernel_bf16<D>, dim3(a.nb, a.hc), dim3(kT), 0, st, a);
+        else hipLaunchKernelGGL((bwd_block_kernel<T, D>), dim3(a.nb, a.hc), dim3(kT), 0, st, a);
         if (a.dlogf) hipLaunchKernelGGL(bwd_gate_kernel, dim3(a.hc), dim3(kT), 0, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
