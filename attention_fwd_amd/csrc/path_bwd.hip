@@ -1890,6 +1890,240 @@ __device__ __forceinline__ void szero(uint16_t *p, int tid) {
     *reinterpret_cast<u32x4 *>(p + kSP + e) = z;
 }
 
+// A 64x64 block of a matrix X held as a split tile -> the 2 x 4 fragments of X it covers (bf16:
+// the hi plane, i.e. each value rounded to nearest), one (fragment, lane) per thread; as tile2frag.
+template <bool TRANS>
+__device__ __forceinline__ void stile2frag(uint16_t *dst, int KC, int rt0, int kc0, const uint16_t *p, int tid) {
+    const int f = tid >> 6, lane = tid & 63, rtl = f >> 2, kcl = f & 3, h = lane >> 5;
+    const int row = 32 * rtl + (lane & 31);
+    u32x4 u;
+    if constexpr (!TRANS) {
+        // k = 16 kcl + frag_k(e, h): elements 0..3 at 16 kcl + 4 h .., 4..7 at 16 kcl + 8 + 4 h ..
+        const u32x2 x = *reinterpret_cast<const u32x2 *>(p + sidx(row, 16 * kcl + 4 * h));
+        const u32x2 y = *reinterpret_cast<const u32x2 *>(p + sidx(row, 16 * kcl + 8 + 4 * h));
+        u = u32x4{x.x, x.y, y.x, y.y};
+    } else {
+        uint16_t x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = p[sidx(16 * kcl + frag_k(e, h), row)];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) u[t] = (uint32_t)x[2 * t] | ((uint32_t)x[2 * t + 1] << 16);
+    }
+    stfrag<uint16_t>(dst, rt0 + rtl, kc0 + kcl, KC, lane, __builtin_bit_cast(i16x8, u));
+}
+// An fp32 64x64 tile without padding, columns swizzled by the row, so that one thread per row
+// or one per column walking the tile hits 64 different banks.
+__device__ __forceinline__ int fidx(int r, int c) { return r * kC + ((c ^ r) & 63); }
+
+// Prep for bf16 inputs: the steps of bwd_prep_kernel with split tiles.  G and X stay fp32 for
+// the triangular inverse (their space then holds P and A as split tiles); the diagonal dS is an
+// fp32 tile, for the exact row and column sums; the matrices kept for the block backward go to
+// the workspace straight from the accumulators.
+template <int D>
+__global__ __launch_bounds__(kT) void bwd_prep_kernel_bf16(BwdArgs a) {
+    typedef uint16_t T;
+    constexpr int NCH = D / 64, KCD = D / 16, TS = 2 * kSP;
+    __shared__ __attribute__((aligned(16))) float sf[2 * kTile];  // G, then P (split); X, then A (split)
+    __shared__ __attribute__((aligned(16))) uint16_t sm[7 * TS];
+    __shared__ float sB[kC], sCl[kC], sL2[kC], sDD[kC];
+    float *fG = sf, *fX = sf + kTile;
+    uint16_t *bP = (uint16_t *)fG, *bA = (uint16_t *)fX;
+    uint16_t *bW = sm, *bQ = bW + TS, *bK = bQ + TS, *bQW = bK + TS, *bN = bQW + TS, *bZ = bN + TS, *bY = bZ + TS;
+    float *fS = (float *)bQW;  // the diagonal dS (fp32, fidx order), once Q W^T is done with
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int J = blockIdx.x, gl = blockIdx.y, g = a.g0 + gl, L = a.L, row0 = J * kC;
+    const int64_t hoff = (int64_t)g * L;
+    const T *q = (const T *)a.q + hoff * D, *k = (const T *)a.k + hoff * D, *w = (const T *)a.w + hoff * D;
+    const T *v = (const T *)a.v + hoff * D, *o = (const T *)a.out + hoff * D, *dout = (const T *)a.dout + hoff * D;
+    const BwdLayout &ly = a.ly;
+    char *ws = (char *)a.ws + (int64_t)gl * ly.head;
+    const float scale = a.scale;
+    const int64_t tok = (int64_t)J * kC * kC;
+
+    if (tid < kC) {
+        const int i = row0 + tid;
+        sB[tid] = i < L ? a.beta[hoff + i] : 0.f;
+        sL2[tid] = i < L ? a.lse[hoff + i] * kLog2e : 0.f;
+    }
+    gate_prefix(sCl, a.logf ? a.logf + hoff : nullptr, row0, L, tid);
+    {   // D_i = do_i . o_i - dlse_i: eight lanes per row, D / 8 columns each
+        const int r = tid >> 3, c0 = (tid & 7) * (D / 8), i = row0 + r;
+        float s = 0.f;
+        if (i < L) {
+#pragma unroll
+            for (int c = 0; c < D / 8; c += 8) {
+                float xo[8], xd[8];
+                load8(xd, dout + (int64_t)i * D + c0 + c);
+                load8(xo, o + (int64_t)i * D + c0 + c);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) s += xd[t] * xo[t];
+            }
+        }
+        s = sum8(s);
+        if ((tid & 7) == 0) sDD[r] = i < L ? s - (a.dlse ? a.dlse[hoff + i] : 0.f) : 0.f;
+    }
+    // G = W W^T, Q W^T, N = K W^T and Q K^T, summed over the chunks of the head dimension
+    f32x8 aG = zero8(), aQW = zero8(), aN = zero8(), aQK = zero8();
+    for (int c = 0; c < NCH; ++c) {
+        __syncthreads();
+        sin2l(bW, w, D, 64 * c, row0, L, tid);
+        sin2l(bQ, q, D, 64 * c, row0, L, tid);
+        sin2l(bK, k, D, 64 * c, row0, L, tid);
+        __syncthreads();
+        smm<true, true>(aG, snat(bW), str(bW), lane, wave);
+        smm<true, true>(aQW, snat(bQ), str(bW), lane, wave);
+        smm<true, true>(aN, snat(bK), str(bW), lane, wave);
+        smm<true, true>(aQK, snat(bQ), str(bK), lane, wave);
+    }
+#pragma unroll
+    for (int vv = 0; vv < 8; ++vv) {
+        const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
+        aQW[vv] = c <= r ? aQW[vv] : 0.f;  // Q W^T, r <= i
+        aN[vv] = c > r ? aN[vv] : 0.f;     // N, r > j
+    }
+    store_lds(fG, aG, lane, wave, Id());
+    sstore(bQW, aQW, lane, wave, Id());
+    sstore(bN, aN, lane, wave, Id());
+    acc2g((float *)(ws + ly.qwm) + tok, kC, aQW, lane, wave);
+    acc2g((float *)(ws + ly.nn) + tok, kC, aN, lane, wave);
+    __syncthreads();
+    unit_upper_inverse(fX, fG, sB, tid);
+    __syncthreads();
+    {   // X and A = X diag(beta) to the workspace; A, split, into X's space
+        const int r = tid >> 3, c8 = (tid & 7) * 8;
+        float *XX = (float *)(ws + ly.xx) + tok + r * kC + c8, *AA = (float *)(ws + ly.aa) + tok + r * kC + c8;
+        f32x4 x0 = *reinterpret_cast<const f32x4 *>(fX + r * kP + c8);
+        f32x4 x1 = *reinterpret_cast<const f32x4 *>(fX + r * kP + c8 + 4);
+        *reinterpret_cast<f32x4 *>(XX) = x0;
+        *reinterpret_cast<f32x4 *>(XX + 4) = x1;
+        float x[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            x[t] = x0[t] * sB[c8 + t];
+            x[4 + t] = x1[t] * sB[c8 + 4 + t];
+        }
+        *reinterpret_cast<f32x4 *>(AA) = f32x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f32x4 *>(AA + 4) = f32x4{x[4], x[5], x[6], x[7]};
+        __syncthreads();  // every thread has read its part of X
+        sput8(bA, r, c8, x);
+    }
+    __syncthreads();
+    f32x8 acc = zero8();
+    smm<false, false>(acc, snat(bQW), str(bA), lane, wave);  // Z = QWm A^T
+    sstore(bZ, acc, lane, wave, Id());
+    acc2g((float *)(ws + ly.zz) + tok, kC, acc, lane, wave);
+    acc = zero8();
+    smm<false, false>(acc, snat(bN), snat(bA), lane, wave);  // Y = N A
+    sstore(bY, acc, lane, wave, Id());
+    __syncthreads();
+    // diagonal block: P = exp(scale (Q K^T - Z N^T) + cl_i - cl_j - lse_i) for j <= i (G is dead: P -> bP)
+    f32x8 pv;
+    {
+        f32x8 sZN = zero8();
+        smm<false, false>(sZN, snat(bZ), str(bN), lane, wave);
+#pragma unroll
+        for (int vv = 0; vv < 8; ++vv) {
+            const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
+            const float s = (scale * (aQK[vv] - sZN[vv]) + (sCl[r] - sCl[c])) * kLog2e - sL2[r];
+            pv[vv] = c <= r ? fast_exp2(s) : 0.f;
+        }
+        sstore(bP, pv, lane, wave, Id());
+    }
+    // dP = dO V^T over the chunks; dS = P (dP - D_i) -> fS (Q W^T is stored)
+    f32x8 aDP = zero8();
+    for (int c = 0; c < NCH; ++c) {
+        __syncthreads();
+        sin2l(bQ, dout, D, 64 * c, row0, L, tid);
+        sin2l(bK, v, D, 64 * c, row0, L, tid);
+        __syncthreads();
+        smm<true, true>(aDP, snat(bQ), str(bK), lane, wave);
+    }
+#pragma unroll
+    for (int vv = 0; vv < 8; ++vv) {
+        const int r = arow(vv, lane, wave), c = acol(vv, lane, wave);
+        const float ds = pv[vv] * (aDP[vv] - sDD[r]);
+        fS[fidx(r, c)] = ds;
+        aDP[vv] = scale * ds;
+    }
+    acc2g((float *)(ws + ly.ee) + tok, kC, aDP, lane, wave);
+    __syncthreads();
+    {
+        float *rs = (float *)(ws + ly.rsd) + row0, *cs = (float *)(ws + ly.csd) + row0;
+        if (tid < kC) {
+            float s = 0.f;
+            for (int c = 0; c < kC; ++c) s += fS[fidx(tid, c)];
+            rs[tid] = s;
+        } else if (tid < 2 * kC) {
+            const int c = tid - kC;
+            float s = 0.f;
+            for (int r = 0; r < kC; ++r) s += fS[fidx(r, c)];
+            cs[c] = s;
+        } else if (tid < 3 * kC) {
+            const int r = tid - 2 * kC;
+            ((float *)(ws + ly.dd))[row0 + r] = sDD[r];
+            ((float *)(ws + ly.cql))[row0 + r] = sCl[r] * kLog2e - sL2[r];
+            ((float *)(ws + ly.ckl))[row0 + r] = (sCl[kC - 1] - sCl[r]) * kLog2e;
+            if (r == 0) ((float *)(ws + ly.tot))[J] = sCl[kC - 1] * kLog2e;
+        }
+    }
+    // chunks of the head dimension: q^, k^ (fragments), A W (kept for T), V and dO fragments,
+    // the diagonal value gradient
+    const int64_t fo = (int64_t)J * kC * D;  // this block's 64 x D fragment set
+    T *REC = (T *)(ws + ly.urec) + J * ly.rec_elems;
+    T *KH1 = REC, *V1 = REC + kC * D, *KH2 = REC + 2 * kC * D;
+    T *DO1 = (T *)(ws + ly.do1) + fo;
+    uint16_t *bAW[2] = {bN, bQW};  // A W of chunk 0 / 1 (N and dS are done with)
+    for (int c = 0; c < NCH; ++c) {
+        __syncthreads();
+        sin2l(bW, w, D, 64 * c, row0, L, tid);
+        sin2l(bQ, q, D, 64 * c, row0, L, tid);
+        sin2l(bK, k, D, 64 * c, row0, L, tid);
+        __syncthreads();
+        {
+            f32x8 zw = zero8(), yw = zero8(), aw = zero8();
+            smm<false, true>(zw, snat(bZ), snat(bW), lane, wave);
+            smm<false, true>(yw, snat(bY), snat(bW), lane, wave);
+            smm<false, true>(aw, snat(bA), snat(bW), lane, wave);
+            float *QH = (float *)(ws + ly.qh) + (int64_t)row0 * D + 64 * c;
+#pragma unroll
+            for (int vv = 0; vv < 8; ++vv) {  // each element read and rewritten by the same thread
+                const int r = arow(vv, lane, wave), cc = acol(vv, lane, wave);
+                QH[(int64_t)r * D + cc] = sld(bQ, r, cc) - zw[vv];  // q^ = q - Z W
+                sst(bK, r, cc, sld(bK, r, cc) - yw[vv]);            // k^ = k - Y W
+            }
+            sstore(bAW[c], aw, lane, wave, Id());
+        }
+        __syncthreads();
+        stile2frag<false>(KH1, KCD, 0, 4 * c, bK, tid);  // k^: rows keys, k over d
+        stile2frag<true>(KH2, 4, 2 * c, 0, bK, tid);     // k^^T: rows d, k over keys
+        __syncthreads();
+        sin2l(bQ, v, D, 64 * c, row0, L, tid);
+        sin2l(bK, dout, D, 64 * c, row0, L, tid);
+        __syncthreads();
+        stile2frag<false>(V1, KCD, 0, 4 * c, bQ, tid);   // V: rows keys
+        stile2frag<false>(DO1, KCD, 0, 4 * c, bK, tid);  // dO: rows queries
+        acc = zero8();
+        smm<false, true>(acc, str(bP), snat(bK), lane, wave);  // diagonal value gradient P^T dO
+        acc2g((float *)(ws + ly.dvd) + (int64_t)row0 * D + 64 * c, D, acc, lane, wave);
+    }
+    // T - I = -W^T (A W) and its transpose, block (c1, c2) = rows of chunk c1, columns of chunk c2
+    T *NT = (T *)(ws + ly.nt) + (int64_t)J * D * D, *NTT = REC + 3 * kC * D;
+    for (int c1 = 0; c1 < NCH; ++c1) {
+        __syncthreads();
+        sin2l(bW, w, D, 64 * c1, row0, L, tid);
+        __syncthreads();
+        for (int c2 = 0; c2 < NCH; ++c2) {
+            acc = zero8();
+            smm<true, false>(acc, str(bW), snat(bAW[c2]), lane, wave);
+            sstore(bQ, acc, lane, wave, [](int, int, float x) { return -x; });
+            __syncthreads();
+            stile2frag<false>(NT, KCD, 2 * c1, 4 * c2, bQ, tid);  // (T - I): rows d_out, k over d_in
+            stile2frag<true>(NTT, KCD, 2 * c2, 4 * c1, bQ, tid);  // (T - I)^T
+            __syncthreads();
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(kT) void bwd_block_kernel_bf16(BwdArgs a) {
     typedef uint16_t T;
@@ -2357,7 +2591,8 @@ hipError_t launch_bwd_t(const BwdArgs &a0, hipStream_t st) {
     for (int g0 = 0; g0 < G; g0 += a.hc_max) {
         a.g0 = g0;
         a.hc = min(a.hc_max, G - g0);
-        hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(a.nb, a.hc), dim3(kT), 0, st, a);
+        if constexpr (sizeof(T) == 2) hipLaunchKernelGGL(bwd_prep_kernel_bf16<D>, dim3(a.nb, a.hc), dim3(kT), 0, st, a);
+        else hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(a.nb, a.hc), dim3(kT), 0, st, a);
         if (a.nb > 1) {
             const dim3 walks((unsigned)((a.nb - 1) * a.hc));
             if constexpr (sizeof(T) == 2) {
