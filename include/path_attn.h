@@ -293,9 +293,9 @@ path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace
  * path_attn_bwd accepts any workspace of at least one share and processes
  * floor(workspace_bytes / share) heads at a time (results do not depend on it).
  * One share is 3 * 64 * d element-type values (2 * 64 * d for bf16) per pair
- * of 64-token blocks (nb (nb - 1) / 2 pairs, nb = ceil(L / 64)) plus 4.4 KiB
- * (d = 64, bf16) to 10.5 KiB (d = 128, fp32) per token: 49 MiB per head at
- * L = 4096, d = 64, bf16; 96 MiB at d = 128, bf16.
+ * of 64-token blocks (nb (nb - 1) / 2 pairs, nb = ceil(L / 64)) plus 4.3 KiB
+ * (d = 64, bf16) to 10.5 KiB (d = 128, fp32) per token: 48.6 MiB per head at
+ * L = 4096, d = 64, bf16; 95.2 MiB at d = 128, bf16.
  */
 size_t path_attn_bwd_workspace_size(int B, int H, int L, int d, path_dtype_t dtype);
 
@@ -309,8 +309,10 @@ size_t path_attn_bwd_workspace_size(int B, int H, int L, int d, path_dtype_t dty
  * key blocks per query block for the query side, one per key block for the
  * key side and the block transitions, and a per-block pass through the UT
  * transform.  The walks run on the matrix cores in `dtype` (bf16 operands
- * with fp32 accumulation for bf16, fp32 for fp32); the per-block passes in
- * fp32.
+ * with fp32 accumulation for bf16, fp32 for fp32); the per-block passes on
+ * the matrix cores too, with fp32 operands for fp32 and, for bf16, bf16
+ * operands where they are input values and hi + lo bf16 pairs (about 16
+ * significant bits) for the derived fp32 matrices.
  *
  * q, k, v, w, out, dout : [B, H, L, d] element type `dtype` (read only); out is the
  *                         forward's output for these inputs

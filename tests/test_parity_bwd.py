@@ -108,6 +108,22 @@ def test_bwd_chunked_workspace_and_determinism():
 
 
 @gpu
+def test_bwd_uneven_passes_bf16():
+    """bf16, five heads through workspaces of two and four heads' shares (passes of 2, 2, 1 and of 4, 1
+    heads): the same bits as all heads at once."""
+    say("case bwd uneven passes bf16")
+    B, H, L = 1, 5, 200
+    share = pa.bwd_workspace_size(1, 1, L, 64, torch.bfloat16)
+    x, dout, dlse, out, lse, g_all = run_case(B, H, L, "bf16", seed=29, fox=True)
+    for n_sh in (2, 4):
+        ws = torch.empty(n_sh * share, device="cuda", dtype=torch.uint8)
+        g_n = pa.bwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], out, lse, dout, dlse, workspace=ws)
+        torch.cuda.synchronize()
+        for n, a, b in zip(NAMES, g_all, g_n):
+            assert torch.equal(a, b), "%d shares: %s" % (n_sh, n)
+
+
+@gpu
 def test_bwd_per_head_workload_shape():
     """One head at the per-head shape of the B32 H32 L4096 d64 bf16 workload, every gradient element."""
     say("case bwd bf16 L4096 one head")
@@ -208,7 +224,7 @@ def test_bwd_full_workload_sampled_heads():
 
 @gpu
 def test_bwd_full_workload_sampled_heads_d128():
-    """The whole B32 H32 L4096 d128 bf16 workload through the default workspace (85 heads per pass over
+    """The whole B32 H32 L4096 d128 bf16 workload through the default workspace (86 heads per pass over
     8 GiB, as the benchmark times it); the first head, one at a pass boundary and the last head are
     checked element by element against the oracle run on that head's inputs alone."""
     c = pathgen.WORKLOADS["sweep_L4096_d128_bf16"]
