@@ -193,24 +193,55 @@ __device__ __forceinline__ void step_mma(WaveState<D, CT, NS> &w, const S *rec, 
                 w.s[SB][hf][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, w.mb[ct], w.s[SB][hf][ct], 0, 0, 0);
         }
     }
+    if constexpr (sizeof(S) == 2 && CT == 1) {
+        // Every A fragment of the step -- the logits' khat, then the transform's -M (qt <- P_J qt;
+        // XF false: block 0, whose transform no later block uses) -- in one sequence, each read
+        // PF fragments ahead of its product so that the LDS read has returned when the product
+        // issues.  The logit fragments alternate between the two key halves, so consecutive
+        // products accumulate into different tiles (each tile still sums its k-chunks in order).
+        constexpr int NL = 2 * KCH, NF = NL + (XF ? KCH * DT : 0), PF = 4;
+        auto src = [&](int i) -> const Frag * {
+            if (i < NL) return (const Frag *)(sk + (((i & 1) * KCH + (i >> 1)) * 64 + lane) * 8);
+            const int j = i - NL;
+            return (const Frag *)(sm + (((j % DT) * KCH + j / DT) * 64 + lane) * 8);
+        };
+        Frag ring[PF];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+        for (int i = 0; i < PF && i < NF; ++i) ring[i] = *src(i);
 #pragma unroll
-        for (int kc = 0; kc < KCH; ++kc) {
-            const Frag af = *(const Frag *)(sk + ((hf * KCH + kc) * 64 + lane) * 8);
+        for (int i = 0; i < NF; ++i) {
+            const Frag af = ring[i % PF];
+            if (i + PF < NF) ring[i % PF] = *src(i + PF);
+            if (i < NL) {
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) E::mma(w.s[SB][hf][ct], af, qb[ct][kc]);
+                for (int ct = 0; ct < CT; ++ct) E::mma(w.s[SB][i & 1][ct], af, qb[ct][i >> 1]);
+            } else {
+                const int j = i - NL;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) E::mma(w.qt[j % DT][ct], af, qb[ct][j / DT]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the read PF products ahead
         }
-    // qt <- P_J qt (XF false: block 0, whose transform no later block uses)
-    if constexpr (XF)
+    } else {
 #pragma unroll
-    for (int kc = 0; kc < KCH; ++kc)
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const Frag af = *(const Frag *)(sm + ((dt * KCH + kc) * 64 + lane) * 8);
+            for (int kc = 0; kc < KCH; ++kc) {
+                const Frag af = *(const Frag *)(sk + ((hf * KCH + kc) * 64 + lane) * 8);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) E::mma(w.qt[dt][ct], af, qb[ct][kc]);
-        }
+                for (int ct = 0; ct < CT; ++ct) E::mma(w.s[SB][hf][ct], af, qb[ct][kc]);
+            }
+        // qt <- P_J qt (XF false: block 0, whose transform no later block uses)
+        if constexpr (XF)
+#pragma unroll
+        for (int kc = 0; kc < KCH; ++kc)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const Frag af = *(const Frag *)(sm + ((dt * KCH + kc) * 64 + lane) * 8);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) E::mma(w.qt[dt][ct], af, qb[ct][kc]);
+            }
+    }
 }
 
 // Column maxima of logit buffer SB (with the forget-gate tail bias added) and,
