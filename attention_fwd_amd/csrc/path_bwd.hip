@@ -47,10 +47,11 @@
 // products with fp32 accumulation for bf16 inputs, fp32 products for fp32),
 // with operands stored in fragment order and the carried q~ and G held as
 // fp32 accumulators, rounded to the element type only as product operands,
-// as in the forward scan.  The per-block kernels keep fp32 64 x 64 tiles in
-// LDS, looping over 64-wide chunks of the head dimension; their products run
-// on v_mfma_f32_16x16x4f32 for fp32 inputs and on v_mfma_f32_16x16x32_bf16 for
-// bf16 inputs (tiles of input values exact, other operands split hi + lo).
+// as in the forward scan.  The per-block kernels keep 64 x 64 tiles in LDS,
+// looping over 64-wide chunks of the head dimension: fp32 tiles and products
+// on v_mfma_f32_16x16x4f32 for fp32 inputs; for bf16 inputs tiles held as bf16
+// hi + lo pairs (lo = 0 for tiles of input values) and products on
+// v_mfma_f32_16x16x32_bf16 (hi*hi + hi*lo + lo*hi).
 #include <hip/hip_runtime.h>
 
 #include "path_bwd.h"
