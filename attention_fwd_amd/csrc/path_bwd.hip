@@ -858,7 +858,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // heads, for a kernel that keeps wpc workgroups on a compute unit.  Workgroups are dealt
 // round-robin over gfx950's 8 XCDs, each with its own L2 and 32 compute units: the items
 // are numbered XCD by XCD, so that every XCD takes a contiguous range of heads, in groups
-// of about two rounds of its workgroup slots.  Inside a group, rank r (0: the longest walk)
+// of about one round of its workgroup slots.  Inside a group, rank r (0: the longest walk)
 // runs on every head of the group before rank r + 1, so the group's walks read the same
 // key or query blocks at about the same time and share them through the XCD's L2.
 // Returns the head (gl) and the rank (r).
@@ -868,7 +868,7 @@ __device__ __forceinline__ void walk_item(int nu, int hc, int wpc, int &gl, int 
     const unsigned total = (unsigned)nu * (unsigned)hc, x = blockIdx.x;
     const unsigned q = total / kXcds, rem = total % kXcds, k = x % kXcds;
     const unsigned item = k * q + min(k, rem) + x / kXcds;  // XCD k holds items [k q + min(k, rem), ...)
-    const unsigned G = (unsigned)max(1, 2 * kCusPerXcd * wpc / nu);
+    const unsigned G = (unsigned)max(1, kCusPerXcd * wpc / nu);
     const unsigned gbase = item / (G * (unsigned)nu) * G;  // first head of the item's group
     const unsigned gn = min(G, (unsigned)hc - gbase);
     const unsigned rank = item - gbase * (unsigned)nu;
