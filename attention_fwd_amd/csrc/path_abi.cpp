@@ -365,7 +365,9 @@ path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace
 
 namespace {
 
-constexpr int64_t kBwdCap = int64_t(8) << 30;  // default workspace: all heads, or what fits in 8 GiB
+// default workspace: all heads, or what fits in 32 GiB (an eighth of the device's 288 GB; fewer,
+// larger passes over the heads leave fewer kernel tails)
+constexpr int64_t kBwdCap = int64_t(32) << 30;
 
 path_status_t bwd_sizes_ok(int B, int H, int L, int d, path_dtype_t dtype) {
     if (B < 1 || H < 1 || L < 1 || d < 1 || elem_size(dtype) == 0) return PATH_EINVAL;

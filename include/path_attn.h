@@ -288,7 +288,7 @@ path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace
 /*
  * Workspace bytes for path_attn_bwd (0 if the sizes are invalid or not
  * supported): enough to process all B*H heads at once when that takes at most
- * 8 GiB, else the largest whole number of heads that fits in 8 GiB (at least
+ * 32 GiB, else the largest whole number of heads that fits in 32 GiB (at least
  * one).  path_attn_bwd_workspace_size(1, 1, L, d, dtype) is one head's share;
  * path_attn_bwd accepts any workspace of at least one share and processes
  * floor(workspace_bytes / share) heads at a time (results do not depend on it).

@@ -195,7 +195,7 @@ def test_bwd_chunked_workspace_d128():
 
 @gpu
 def test_bwd_full_workload_sampled_heads():
-    """The whole B32 H32 L4096 d64 bf16 workload through the default workspace (heads in passes over 8 GiB,
+    """The whole B32 H32 L4096 d64 bf16 workload through the default workspace (heads in passes over 32 GiB,
     the launch configuration the benchmark times); heads are independent, so the first and the last head
     are checked element by element against the oracle run on that head's inputs alone."""
     c = pathgen.WORKLOADS["sweep_L4096_d64_bf16"]
@@ -224,8 +224,8 @@ def test_bwd_full_workload_sampled_heads():
 
 @gpu
 def test_bwd_full_workload_sampled_heads_d128():
-    """The whole B32 H32 L4096 d128 bf16 workload through the default workspace (86 heads per pass over
-    8 GiB, as the benchmark times it); the first head, one at a pass boundary and the last head are
+    """The whole B32 H32 L4096 d128 bf16 workload through the default workspace (344 heads per pass over
+    32 GiB, as the benchmark times it); the first head, one at a pass boundary and the last head are
     checked element by element against the oracle run on that head's inputs alone."""
     c = pathgen.WORKLOADS["sweep_L4096_d128_bf16"]
     B, H, L, d = c["B"], c["H"], c["L"], c["d"]
