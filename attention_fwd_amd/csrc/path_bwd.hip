@@ -117,72 +117,12 @@ __device__ __forceinline__ void mm(f32x8 &acc, LMat A, LMat B, int lane, int wav
     acc.hi = hi;
 }
 
-// The same product for bf16 inputs on v_mfma_f32_16x16x32_bf16 (16 times the rate of the
-// fp32 shape).  An operand marked exact (EA, EB) holds bf16 numbers (a tile loaded from the
-// bf16 inputs) and is converted without loss; any other operand x is split as hi + lo, two
-// bf16 numbers (hi = x rounded, lo = the rest rounded), and the product takes hi*hi + hi*lo +
-// lo*hi: about 16 significant bits per operand, fp32 accumulation.  Lane l supplies k =
-// 32 s + 8 (l / 16) + t, t = 0..7, at step s, the same order for both operands; the
-// accumulator layout is that of mm.
-__device__ __forceinline__ void ld8(float *x, LMat M, int row, int k0, bool kc) {
-    // element (row, k0 + t); kc: k is contiguous in LDS (two 16-byte loads)
-    if (kc) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(M.p + row * M.rs + k0);
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(M.p + row * M.rs + k0 + 4);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            x[t] = a[t];
-            x[4 + t] = b[t];
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) x[t] = M.p[row * M.rs + (k0 + t) * M.cs];
-    }
-}
-template <bool EXACT>
-__device__ __forceinline__ void split8(const float *x, i16x8 &hi, i16x8 &lo) {
-    u32x4 uh, ul;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        uh[t] = pack_bf16(x[2 * t], x[2 * t + 1]);
-        if constexpr (!EXACT) {
-            const float h0 = __uint_as_float(uh[t] << 16), h1 = __uint_as_float(uh[t] & 0xffff0000u);
-            ul[t] = pack_bf16(x[2 * t] - h0, x[2 * t + 1] - h1);
-        }
-    }
-    hi = __builtin_bit_cast(i16x8, uh);
-    if constexpr (!EXACT) lo = __builtin_bit_cast(i16x8, ul);
-}
-template <bool EA, bool EB>
-__device__ __forceinline__ void mmb(f32x8 &acc, LMat A, LMat B, int lane, int wave) {
-    const int r = 16 * (wave >> 1) + (lane & 15), c0 = 32 * (wave & 1) + (lane & 15), q = lane >> 4;
-    f32x4 lo = acc.lo, hi = acc.hi;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        const int k0 = 32 * st + 8 * q;
-        float x[8], y[8];
-        i16x8 ah, al, bh, bl;
-        ld8(x, A, r, k0, A.cs == 1);
-        split8<EA>(x, ah, al);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            // B element (k, c) at k * rs + c * cs: the transposed view of ld8
-            ld8(y, LMat{B.p, B.cs, B.rs}, c0 + 16 * ct, k0, B.rs == 1);
-            split8<EB>(y, bh, bl);
-            f32x4 &c = ct == 0 ? lo : hi;
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
-            if constexpr (!EB) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
-            if constexpr (!EA) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
-        }
-    }
-    acc.lo = lo;
-    acc.hi = hi;
-}
-// mm for fp32 inputs, mmb for bf16 inputs (EA, EB: the operand is a tile of bf16 input values)
+// The product of the generic per-block kernels, which serve fp32 inputs (bf16 inputs have the
+// split-tile kernels below); EA, EB mark operands that are tiles of input values.
 template <typename T, bool EA, bool EB>
 __device__ __forceinline__ void mmx(f32x8 &acc, LMat A, LMat B, int lane, int wave) {
-    if constexpr (sizeof(T) == 2) mmb<EA, EB>(acc, A, B, lane, wave);
-    else mm(acc, A, B, lane, wave);
+    static_assert(sizeof(T) == 4, "bf16 inputs use the split-tile kernels");
+    mm(acc, A, B, lane, wave);
 }
 
 __device__ __forceinline__ f32x8 zero8() {
@@ -389,7 +329,7 @@ __device__ __forceinline__ void gate_prefix(float *cl, const float *logf, int ro
 }
 
 // ---------------------------------------------------------------------------
-// Prep: one workgroup per (block J, head).
+// Prep: one workgroup per (block J, head); fp32 inputs (bf16: bwd_prep_kernel_bf16).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
@@ -580,13 +520,13 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
 // its queries; matrix-core operands are fragments loaded from the workspace.
 // ---------------------------------------------------------------------------
 
-// Per-wave LDS scratch for writing an accumulator tile set (rows d, columns the
-// wave's 32 queries) back as fragments with the query index inside the lane.  It
-// holds the element type: each value is rounded before it is transposed, which
-// gives the same fragments.
+// Per-wave LDS scratch of the generic (fp32) walks for writing an accumulator tile set
+// (rows d, columns the wave's 32 queries) back as fragments with the query index inside
+// the lane.
 template <typename S>
 struct XScr {
-    static constexpr int kStride = sizeof(S) == 2 ? 40 : 36;  // row stride (elements): rows 16- (fp32) or 8-byte aligned
+    static_assert(sizeof(S) == 4, "the generic walks serve fp32 inputs");
+    static constexpr int kStride = 36;  // row stride (elements): rows 16-byte aligned
 };
 
 // acc tiles t[dt] (rows d = 32 dt + acc_row(r, h), columns this wave's 32 queries) ->
@@ -594,7 +534,6 @@ struct XScr {
 // Only this wave touches x, and a wave's LDS accesses are performed in order.
 template <typename S, int D>
 __device__ __forceinline__ void store_transposed(S *dst, const f32x16 *t, S *x, int w, int lane) {
-    typedef typename Elem<S>::Frag Frag;
     constexpr int XS = XScr<S>::kStride;
     const int h = lane >> 5, l32 = lane & 31;
 #pragma unroll
@@ -606,19 +545,14 @@ __device__ __forceinline__ void store_transposed(S *dst, const f32x16 *t, S *x, 
 #pragma unroll
         for (int kcl = 0; kcl < 2; ++kcl) {
             const S *src = x + (32 * dt + l32) * XS + 16 * kcl + 4 * h;
-            if constexpr (sizeof(S) == 2) {
-                const u32x2 lo = *reinterpret_cast<const u32x2 *>(src), hi = *reinterpret_cast<const u32x2 *>(src + 8);
-                stfrag<S>(dst, dt, 2 * w + kcl, 4, lane, __builtin_bit_cast(Frag, u32x4{lo.x, lo.y, hi.x, hi.y}));
-            } else {
-                const f32x4 lo = *reinterpret_cast<const f32x4 *>(src), hi = *reinterpret_cast<const f32x4 *>(src + 8);
-                const float y[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                stfrag<S>(dst, dt, 2 * w + kcl, 4, lane, Elem<S>::from_f32(y));
-            }
+            const f32x4 lo = *reinterpret_cast<const f32x4 *>(src), hi = *reinterpret_cast<const f32x4 *>(src + 8);
+            const float y[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            stfrag<S>(dst, dt, 2 * w + kcl, 4, lane, Elem<S>::from_f32(y));
         }
 }
 
-// Down walk: one workgroup (two waves) per (query block I >= 1, head), heaviest
-// first.  q~^T (rows d, the wave's 32 queries) stays in fp32 accumulators:
+// Down walk (fp32 inputs; bf16: bwd_down_kernel_lds): one workgroup (two waves) per
+// (query block I >= 1, head), heaviest first.  q~^T (rows d, the wave's 32 queries) stays in fp32 accumulators:
 // q~^T <- q~^T + (T_J - I) q~^T; q~^(J) is stored for the pair (I, J) with rows
 // queries (for the logits) and, with Q2, with rows d (for the key walk's sums
 // over queries), with the gate sum of the blocks strictly between I and J.
@@ -673,7 +607,8 @@ __global__ __launch_bounds__(128) void bwd_down_kernel(BwdArgs a) {
     }
 }
 
-// Up walk: one workgroup (two waves) per (query block I >= 1, head), heaviest
+// Up walk (fp32 inputs; bf16: bwd_up_kernel_lds, bwd_up_kernel_split): one workgroup
+// (two waves) per (query block I >= 1, head), heaviest
 // first.  For J = 0 .. I-1: S^T = K^_J q~^T and dP^T = V_J dO^T (rows keys,
 // columns the wave's queries), P and dS, then the adjoint (rows d, fp32
 // accumulators) G^T <- G^T + (T_J - I)^T G^T + K^_J^T (scale dS^T).  G^(J) is
@@ -1303,7 +1238,7 @@ __global__ __launch_bounds__(64 * 2 * kUpQB) void bwd_up_kernel_split(BwdArgs a)
     if (h == 0) ((float *)(ws + ly.rso))[qi] = rsum;
 }
 
-// Key walk: one workgroup per (key block J <= nb-2, head).  Wave w takes the
+// Key walk (fp32 inputs; bf16: bwd_key_kernel_lds): one workgroup per (key block J <= nb-2, head).  Wave w takes the
 // logit tile of queries 32 qt .. (qt = w & 1) and keys 32 kt .. (kt = (w >> 1)
 // & 1) of every later query block I, recomputes P and dS, and accumulates over
 // its 32 queries dV^T = dO^T P and dk^^T = q~^T dS (rows: its group dh = w >> 2
@@ -1555,7 +1490,7 @@ __global__ __launch_bounds__(64 * KeyCfg<D>::NW) void bwd_key_kernel(BwdArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// Block backward: one workgroup per (block J, head).
+// Block backward: one workgroup per (block J, head); fp32 inputs (bf16: bwd_block_kernel_bf16).
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void acc2out(T *g, int D, const f32x8 &acc, int row0, int L, int lane, int wave) {
