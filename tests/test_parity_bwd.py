@@ -108,6 +108,17 @@ def test_bwd_chunked_workspace_and_determinism():
 
 
 @gpu
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_many_heads_short_bf16(d):
+    """bf16 with the gate, 255 heads of L = 130 (B5 H51): the walks' work order deals heads to the XCDs in
+    groups, here with a head count that is no multiple of the 8 XCDs and walks of one or two steps;
+    every element of every head against the oracle."""
+    say("case bwd many heads short d%d" % d)
+    x, dout, dlse, _, _, grads = run_case(5, 51, 130, "bf16", seed=31 + d, fox=True, d=d)
+    compare(x, dout, dlse, grads, "bf16", what="B5 H51 L130 d%d" % d)
+
+
+@gpu
 def test_bwd_uneven_passes_bf16():
     """bf16, five heads through workspaces of two and four heads' shares (passes of 2, 2, 1 and of 4, 1
     heads): the same bits as all heads at once."""
