@@ -14,7 +14,7 @@ import torch
 
 __all__ = ["fwd", "fwd_fused", "fwd_prep", "fwd_scan", "decode_step", "decode_cache_from_fwd", "fwd_workspace_size",
            "decode_workspace_size", "bwd", "bwd_workspace_size", "lib", "PathError", "PATH_OK", "PATH_EINVAL", "PATH_EUNSUPPORTED", "PATH_EHIP", "PATH_ESCRATCH", "decode_step_noalloc", "PATH_DTYPE_F32", "PATH_DTYPE_BF16",
-           "PATH_FWD_SKIP_NEGLIGIBLE"]
+           "PATH_FWD_SKIP_NEGLIGIBLE", "decode_step_fused", "decode_fused_workspace_size"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpath_attn.so")
 
@@ -67,6 +67,11 @@ def lib():
         L.path_decode_step_ex.restype = ctypes.c_int
         L.path_decode_step_ex.argtypes = [vp, vp, i64, i64, vp, vp, fp, fp, fp, vp, vp, vp, fp, i, i, i,
                                           ctypes.c_int, ctypes.c_float, vp, sz, vp]
+        L.path_decode_fused_workspace_size.restype = sz
+        L.path_decode_fused_workspace_size.argtypes = [i, i, i64, i, ctypes.c_int]
+        L.path_decode_step_fused.restype = ctypes.c_int
+        L.path_decode_step_fused.argtypes = [vp, vp, i64, i64, vp, vp, fp, fp, ctypes.c_float, vp, fp, fp, vp, vp, vp,
+                                             fp, i, i, i, ctypes.c_int, ctypes.c_float, vp, sz, vp]
         L.path_decode_noalloc_max_bytes.restype = sz
         L.path_decode_noalloc_max_bytes.argtypes = []
         L.path_decode_step_noalloc.restype = ctypes.c_int
@@ -124,6 +129,10 @@ def fwd_workspace_size(B, H, L, d, dtype=torch.bfloat16):
 
 def decode_workspace_size(B, H, rows, d, dtype=torch.bfloat16):
     return int(lib().path_decode_workspace_size(B, H, rows, d, _DTYPES[dtype]))
+
+
+def decode_fused_workspace_size(B, H, rows, d, dtype=torch.bfloat16):
+    return int(lib().path_decode_fused_workspace_size(B, H, rows, d, _DTYPES[dtype]))
 
 
 PATH_FWD_SKIP_NEGLIGIBLE = 1
@@ -322,6 +331,69 @@ def decode_step(kcache, vcache, n, q, w, beta, k_new=None, v_new=None, scale=Non
                                            _ptr(logf), _ptr(fcache), *common)
     if st != PATH_OK:
         raise PathError(st, name)
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_step_fused(kcache, vcache, n, q, wraw, conv_w, zbeta, conv_state, beta_clip=0.0, k_new=None,
+                      v_new=None, scale=None, out=None, lse=None, return_lse=False, workspace=None, stream=None,
+                      logf=None, fcache=None):
+    """One decode step with the producer of w and beta fused in (path_decode_step_fused):
+    y_t = the width-3 causal convolution of (conv_state rows x_{t-2}, x_{t-1}, wraw = x_t)
+    with conv_w, w_t = y_t / ||y_t||, beta_t = 2 sigmoid(zbeta) (capped at beta_clip > 0),
+    then decode_step with (w_t, beta_t).  conv_state moves on to (x_{t-1}, x_t) in place.
+
+    wraw: [B, H, d] and conv_state: [B, H, 2, d] in the cache's dtype; conv_w: [H, d, 3] fp32;
+    zbeta: [B, H] fp32.  Every other argument as in decode_step.
+    """
+    if kcache.dim() != 4:
+        raise ValueError("kcache must be [B, H, ncap, d]")
+    B, H, ncap, d = kcache.shape
+    dt = kcache.dtype
+    if dt not in _DTYPES:
+        raise ValueError("dtype must be bfloat16 or float32")
+    dev = kcache.device
+    _check(kcache, "kcache", dt, (B, H, ncap, d), dev)
+    _check(vcache, "vcache", dt, (B, H, ncap, d), dev)
+    for t, nm in ((q, "q"), (wraw, "wraw")):
+        _check(t, nm, dt, (B, H, d), dev)
+    _check(conv_state, "conv_state", dt, (B, H, 2, d), dev)
+    _check(conv_w, "conv_w", torch.float32, (H, d, 3), dev)
+    _check(zbeta, "zbeta", torch.float32, (B, H), dev)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if (logf is None) != (fcache is None):
+        raise ValueError("logf and fcache go together")
+    if logf is not None:
+        _check(logf, "logf", torch.float32, (B, H), dev)
+        _check(fcache, "fcache", torch.float32, (B, H, ncap), dev)
+    if k_new is not None:
+        _check(k_new, "k_new", dt, (B, H, d), dev)
+        _check(v_new, "v_new", dt, (B, H, d), dev)
+    mine = []
+    if out is None:
+        out = torch.empty((B, H, d), device=dev, dtype=dt)
+        mine.append(out)
+    _check(out, "out", dt, (B, H, d), dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H), device=dev, dtype=torch.float32)
+        mine.append(lse)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H), dev)
+    rows = int(n) + (1 if k_new is not None else 0)
+    need = decode_fused_workspace_size(B, H, max(rows, 1), d, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=dev, dtype=torch.uint8)
+        mine.append(workspace)
+    _check(workspace, "workspace", None, None, dev)
+    with torch.cuda.device(dev):
+        _record(stream, *mine)
+        st = lib().path_decode_step_fused(_ptr(kcache), _ptr(vcache), int(n), ncap, _ptr(q), _ptr(wraw), _ptr(conv_w),
+                                          _ptr(zbeta), float(beta_clip), _ptr(conv_state), _ptr(logf), _ptr(fcache),
+                                          _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), B, H, d, _DTYPES[dt],
+                                          float(scale or 0.0), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != PATH_OK:
+        raise PathError(st, "path_decode_step_fused")
     return (out, lse) if (return_lse or lse is not None) else out
 
 

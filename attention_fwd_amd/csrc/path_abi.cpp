@@ -220,6 +220,30 @@ size_t path_decode_workspace_size(int B, int H, int64_t n, int d, path_dtype_t d
 
 namespace {
 
+// Workspace of the fused decode step: the decode partials, then the step's w (element
+// type, [B, H, d]) and beta (fp32, [B, H]) made by the producer.
+struct FusedDecWs {
+    int64_t w_off, b_off, total;
+};
+FusedDecWs fused_dec_ws(int B, int H, int64_t rows, int d, int64_t es) {
+    const int64_t a = ((int64_t)dec_ws_bytes(B, H, rows, d) + 255) / 256 * 256;
+    const int64_t b = (a + (int64_t)B * H * d * es + 255) / 256 * 256;
+    return {a, b, b + (int64_t)B * H * 4};
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t path_decode_fused_workspace_size(int B, int H, int64_t n, int d, path_dtype_t dtype) {
+    if (dec_sizes_ok(B, H, n, d, dtype) != PATH_OK) return 0;
+    return (size_t)fused_dec_ws(B, H, n, d, elem_size(dtype)).total;
+}
+
+}  // extern "C"
+
+namespace {
+
 // Argument checks shared by the decode entry points (nothing is enqueued).  With
 // own_scratch the kernels use the library's fixed scratch array instead of a
 // caller workspace: `workspace` is then NULL and the scratch must hold `need`.
@@ -329,6 +353,57 @@ path_status_t path_decode_step(void *kcache, void *vcache, int64_t n, int64_t nc
                                size_t workspace_bytes, path_stream_t stream) {
     return path_decode_step_ex(kcache, vcache, n, ncap, q, w, beta, nullptr, nullptr, k_new, v_new, out, lse, B, H, d,
                                dtype, scale, workspace, workspace_bytes, stream);
+}
+
+path_status_t path_decode_step_fused(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q,
+                                     const void *wraw, const float *conv_w, const float *zbeta, float beta_clip,
+                                     void *conv_state, const float *logf, float *fcache, const void *k_new,
+                                     const void *v_new, void *out, float *lse, int B, int H, int d,
+                                     path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
+                                     path_stream_t stream) {
+    if (!workspace || !wraw || !conv_w || !zbeta || !conv_state) return PATH_EINVAL;
+    if (!std::isfinite(beta_clip) || beta_clip < 0.f) return PATH_EINVAL;
+    if (n < 0 || n > ncap) return PATH_EINVAL;
+    const int64_t rows = n + (k_new ? 1 : 0);
+    path_status_t st = dec_sizes_ok(B, H, rows, d, dtype);
+    if (st != PATH_OK) return st;
+    const int64_t es = elem_size(dtype);
+    const FusedDecWs fw = fused_dec_ws(B, H, rows, d, es);
+    if ((int64_t)workspace_bytes < fw.total || !aligned(workspace, 16)) return PATH_EINVAL;
+    void *wp = (char *)workspace + fw.w_off;
+    float *bp = (float *)((char *)workspace + fw.b_off);
+    // the decode step's own checks, with the produced w and beta in the workspace after its partials
+    int64_t natt = 0;
+    st = dec_check(kcache, vcache, n, ncap, q, wp, bp, logf, fcache, k_new, v_new, out, lse, B, H, d, dtype, scale,
+                   workspace, (size_t)fw.w_off, false, &natt);
+    if (st != PATH_OK) return st;
+    // the producer's inputs and its state
+    if (!aligned(wraw, 16) || !aligned(conv_state, 16) || !aligned(conv_w, 16) || !aligned(zbeta, 4))
+        return PATH_EINVAL;
+    const int64_t vec = (int64_t)B * H * d * es, sc = (int64_t)B * H * 4, stb = 2 * vec, cwb = (int64_t)H * d * 3 * 4;
+    const int64_t cache = (int64_t)B * H * ncap * d * es, fcs = (int64_t)B * H * ncap * 4;
+    const struct {
+        const void *p;
+        int64_t n;
+    } others[] = {{kcache, cache}, {vcache, cache}, {q, vec},      {wraw, vec},    {conv_w, cwb},
+                  {zbeta, sc},     {logf, sc},      {fcache, fcs}, {k_new, vec},   {v_new, vec},
+                  {out, vec},      {lse, sc},       {workspace, fw.total}};
+    for (const auto &o : others)  // the state is read and written: it shares memory with nothing
+        if (overlap(conv_state, stb, o.p, o.n)) return PATH_EINVAL;
+    const struct {
+        const void *p;
+        int64_t n;
+    } written[] = {{kcache, cache}, {vcache, cache}, {out, vec}, {lse, sc}, {fcache, fcs}, {workspace, fw.total}};
+    for (const auto &o : written)
+        if (overlap(o.p, o.n, wraw, vec) || overlap(o.p, o.n, conv_w, cwb) || overlap(o.p, o.n, zbeta, sc))
+            return PATH_EINVAL;
+    path::ProduceArgs pa{};
+    pa.wraw = wraw; pa.conv_w = conv_w; pa.zbeta = zbeta; pa.beta_clip = beta_clip; pa.state = conv_state;
+    pa.w_out = wp; pa.beta_out = bp; pa.B = B; pa.H = H; pa.d = d;
+    if (path::launch_decode_produce(pa, dtype == PATH_DTYPE_BF16, (hipStream_t)stream) != hipSuccess)
+        return PATH_EHIP;
+    return dec_launch(kcache, vcache, n, ncap, natt, q, wp, bp, logf, fcache, k_new, v_new, out, lse, B, H, d, dtype,
+                      scale, workspace, stream);
 }
 
 path_status_t path_decode_cache_from_fwd(const void *workspace, size_t workspace_bytes, const void *v,

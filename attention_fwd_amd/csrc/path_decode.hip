@@ -312,4 +312,59 @@ hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+// The producer of w and beta for one decode step ("거리에서 경로로, PaTH Attention",
+// section 3: a short convolution of width 3 and an L2 normalisation; "技術要約: PaTH
+// Attention", section 2: beta = 2 sigmoid(.)), computed as the fused forward's prep does
+// for a whole sequence: y_t[c] = sum_tau conv_w[h][c][tau] x_{t-2+tau}[c] over the raw
+// rows (x_{t-2}, x_{t-1} from the convolution state), rounded to the element type, and
+// beta_t = 2 sigmoid(z_t) (capped) divided by max(||y_t||^2, 1e-24), the squared norm of
+// the rounded row: I - beta' y y^T is then H_t with w_t = y_t / max(||y_t||, 1e-12).  One
+// wave per (batch, head), lane c holding channels c, c + 64, ...; the state moves on to
+// (x_{t-1}, x_t), each lane rewriting only the channels it has read.
+template <typename S, int D>
+__global__ __launch_bounds__(64) void path_decode_produce_kernel(ProduceArgs a) {
+    typedef Elem<S> E;
+    constexpr int CPL = D / 64;  // channels per lane
+    const int64_t g = blockIdx.x;
+    const int hd = (int)(g % a.H), lane = threadIdx.x;
+    const S *xr = (const S *)a.wraw + g * D;
+    S *st = (S *)a.state + g * 2 * D;
+    const float *cw = a.conv_w + (int64_t)hd * D * 3;
+    S *wo = (S *)a.w_out + g * D;
+    float yy = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        const int c = lane + 64 * k;
+        const S s0 = st[c], s1 = st[D + c], s2 = xr[c];
+        const float y = cw[3 * c] * E::to_f32(s0) + cw[3 * c + 1] * E::to_f32(s1) + cw[3 * c + 2] * E::to_f32(s2);
+        const S yr = E::from_float(y);
+        wo[c] = yr;
+        const float yf = E::to_f32(yr);
+        yy += yf * yf;
+        st[c] = s1;
+        st[D + c] = s2;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) yy += __shfl_xor(yy, o);
+    if (lane == 0) {
+        float bt = 2.f / (1.f + expf(-a.zbeta[g]));
+        if (a.beta_clip > 0.f) bt = fminf(bt, a.beta_clip);
+        a.beta_out[g] = bt / fmaxf(yy, 1e-24f);
+    }
+}
+
+hipError_t launch_decode_produce(const ProduceArgs &a, bool bf16, hipStream_t st) {
+    const dim3 grid((unsigned)((int64_t)a.B * a.H));
+    if (a.d == 64) {
+        if (bf16) hipLaunchKernelGGL((path_decode_produce_kernel<uint16_t, 64>), grid, dim3(64), 0, st, a);
+        else hipLaunchKernelGGL((path_decode_produce_kernel<float, 64>), grid, dim3(64), 0, st, a);
+    } else if (a.d == 128) {
+        if (bf16) hipLaunchKernelGGL((path_decode_produce_kernel<uint16_t, 128>), grid, dim3(64), 0, st, a);
+        else hipLaunchKernelGGL((path_decode_produce_kernel<float, 128>), grid, dim3(64), 0, st, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace path

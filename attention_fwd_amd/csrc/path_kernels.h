@@ -49,6 +49,18 @@ struct DecodeArgs {
     int64_t chunk;
 };
 
+// The producer of w and beta for one decode step (path_decode_produce_kernel).
+struct ProduceArgs {
+    const void *wraw;      // [B, H, d] element type: the current token's raw row x_t
+    const float *conv_w;   // [H, d, 3]
+    const float *zbeta;    // [B, H]
+    float beta_clip;       // 0: no cap
+    void *state;           // [B, H, 2, d] element type: x_{t-2}, x_{t-1}; moved on to x_{t-1}, x_t
+    void *w_out;           // [B, H, d] element type: y_t rounded
+    float *beta_out;       // [B, H]: beta_t / max(||y_t||^2, 1e-24)
+    int B, H, d;
+};
+
 struct CacheArgs {
     const void *ws, *v;
     const float *logf;  // prefix log-forget gate [B, H, L] or NULL
@@ -61,6 +73,7 @@ struct CacheArgs {
 hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t st);
+hipError_t launch_decode_produce(const ProduceArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_cache(const CacheArgs &a, bool bf16, hipStream_t st);
 
 // Rows one decode workgroup covers per iteration (bf16, d = 64: 32 lane groups x

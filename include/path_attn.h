@@ -234,6 +234,51 @@ path_status_t path_decode_step_ex(void *kcache, void *vcache, int64_t n, int64_t
                                   float scale, void *workspace, size_t workspace_bytes, path_stream_t stream);
 
 /*
+ * Workspace bytes that path_decode_step_fused needs (0 if the sizes are
+ * invalid): those of path_decode_workspace_size plus room for the step's w and
+ * beta.  n as for path_decode_workspace_size (the attending rows).
+ */
+size_t path_decode_fused_workspace_size(int B, int H, int64_t n, int d, path_dtype_t dtype);
+
+/*
+ * path_decode_step_ex with the producer of w and beta fused into it: the
+ * decode counterpart of path_attn_fwd_fused ("거리에서 경로로, PaTH
+ * Attention", section 3: w from a projection, a short convolution of width 3
+ * and an L2 normalisation; "技術要約: PaTH Attention", section 2: beta =
+ * 2 sigmoid(.)).  For the current token t, with x the rows of raw projection
+ * outputs (the role of wraw in path_attn_fwd_fused):
+ *   y_t[c]  = sum_{tau=0..2} conv_w[h][c][tau] * x_{t-2+tau}[c]
+ *             (x_t = wraw; x_{t-2}, x_{t-1} from conv_state)
+ *   w_t     = y_t / max(||y_t||, 1e-12)
+ *   beta_t  = 2 sigmoid(zbeta), capped at beta_clip when beta_clip > 0
+ * and then exactly path_decode_step_ex with (w_t, beta_t).  As in the forward,
+ * the kernels use y_t rounded to the element type with beta_t / max(||y_t||^2,
+ * 1e-24), which gives the same transition.  conv_state then moves on by one
+ * token: it holds (x_{t-1}, x_t) for the next step.
+ *
+ *   wraw        [B, H, d] element type, 16-byte aligned: the current token's raw row
+ *   conv_w      [H, d, 3] fp32, 16-byte aligned (as in path_attn_fwd_fused)
+ *   zbeta       [B, H] fp32
+ *   beta_clip   0 for no cap, else a cap in (0, 2]; negative or non-finite
+ *               values are rejected
+ *   conv_state  [B, H, 2, d] element type, 16-byte aligned, read and written:
+ *               the raw rows of the two previous tokens, oldest first (zero rows
+ *               before the first token; after a prefix of L tokens, its rows L-2
+ *               and L-1)
+ *   workspace   at least path_decode_fused_workspace_size(B, H, n (+1), d, dtype) bytes
+ * Every other argument, the results and the errors are those of
+ * path_decode_step_ex.  conv_state must not overlap any other buffer, and
+ * wraw, conv_w and zbeta no buffer the step writes (PATH_EINVAL).  Device
+ * pointers, owned by the caller.
+ */
+path_status_t path_decode_step_fused(void *kcache, void *vcache, int64_t n, int64_t ncap, const void *q,
+                                     const void *wraw, const float *conv_w, const float *zbeta, float beta_clip,
+                                     void *conv_state, const float *logf, float *fcache, const void *k_new,
+                                     const void *v_new, void *out, float *lse, int B, int H, int d,
+                                     path_dtype_t dtype, float scale, void *workspace, size_t workspace_bytes,
+                                     path_stream_t stream);
+
+/*
  * path_decode_step_ex for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  It takes no workspace: the split partials go to a fixed scratch

@@ -48,6 +48,14 @@ int main() {
                 expect("decode_ex", path_decode_step_ex(P(10), P(11), L, L + 1, P(0), P(3), F(4), F(8), F(12), P(1),
                                                         P(2), P(5), F(6), 2, 3, d, t, 0.f, P(7), dws, nullptr),
                        PATH_OK);
+                const size_t fws = path_decode_fused_workspace_size(2, 3, L + 1, d, t);
+                expect("decode fused", path_decode_step_fused(P(10), P(11), L, L + 1, P(0), P(21), F(9), F(4), 1.98f,
+                                                              P(22), F(8), F(12), P(1), P(2), P(5), F(6), 2, 3, d, t,
+                                                              0.f, P(7), fws, nullptr), PATH_OK);
+                expect("decode fused small ws",
+                       path_decode_step_fused(P(10), P(11), L, L + 1, P(0), P(21), F(9), F(4), 0.f, P(22), nullptr,
+                                              nullptr, P(1), P(2), P(5), F(6), 2, 3, d, t, 0.f, P(7), fws - 1, nullptr),
+                       PATH_EINVAL);
                 expect("decode noalloc (no device here)",
                        path_decode_step_noalloc(P(10), P(11), L, L + 1, P(0), P(3), F(4), nullptr, nullptr, nullptr,
                                                 nullptr, P(5), F(6), 2, 3, d, t, 0.f, nullptr),
@@ -72,6 +80,12 @@ int main() {
     expect("noalloc too big", path_decode_step_noalloc(P(10), P(11), 100, 100, P(0), P(3), F(4), nullptr, nullptr,
                                                        nullptr, nullptr, P(5), nullptr, 1000, 100, 128, BF, 0.f,
                                                        nullptr), PATH_ESCRATCH);
+    expect("decode fused state over the cache",
+           path_decode_step_fused(P(10), P(11), 10, 11, P(0), P(21), F(9), F(4), 0.f, P(10), nullptr, nullptr, nullptr,
+                                  nullptr, P(5), nullptr, 1, 1, 64, BF, 0.f, P(7), 1u << 20, nullptr), PATH_EINVAL);
+    expect("decode fused negative cap",
+           path_decode_step_fused(P(10), P(11), 10, 11, P(0), P(21), F(9), F(4), -1.f, P(22), nullptr, nullptr, nullptr,
+                                  nullptr, P(5), nullptr, 1, 1, 64, BF, 0.f, P(7), 1u << 20, nullptr), PATH_EINVAL);
     expect("fwd_ex bad flag", path_attn_fwd_ex(P(0), P(1), P(2), P(3), F(4), nullptr, P(5), nullptr, 1, 1, 64, 64, BF,
                                                0.f, P(7), 1u << 30, 4u, nullptr), PATH_EINVAL);
     std::printf("%s: %d failures\n", failures ? "FAILED" : "abi ok", failures);

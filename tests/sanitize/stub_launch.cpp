@@ -10,6 +10,7 @@ namespace path {
 hipError_t launch_prep(const PrepArgs &, bool, hipStream_t) { return hipSuccess; }
 hipError_t launch_fwd(const FwdArgs &, bool, hipStream_t) { return hipSuccess; }
 hipError_t launch_decode(const DecodeArgs &, bool, hipStream_t) { return hipSuccess; }
+hipError_t launch_decode_produce(const ProduceArgs &, bool, hipStream_t) { return hipSuccess; }
 hipError_t launch_cache(const CacheArgs &, bool, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd(const BwdArgs &, bool, hipStream_t) { return hipSuccess; }
 size_t decode_scratch_bytes() { return size_t(16) << 20; }

@@ -151,6 +151,51 @@ def test_decode_rejects_bad_arguments(over, status):
         assert dec_call(ex=False, **over) == status  # the plain entry point validates the same way
 
 
+def dec_fused_call(**over):
+    args = dict(kc=P(0), vc=P(40), n=100, ncap=101, q=P(80), wraw=P(81), cw=P(82), zb=P(83), clip=0.0, st=P(84),
+                lf=None, fc=None, kn=None, vn=None, out=P(85), lse=None, B=1, H=1, d=64, dtype=BF, scale=0.0,
+                ws=P(86), wsb=1 << 30, stream=None)
+    args.update(over)
+    a = args
+    return pa.lib().path_decode_step_fused(a["kc"], a["vc"], a["n"], a["ncap"], a["q"], a["wraw"], a["cw"], a["zb"],
+                                           a["clip"], a["st"], a["lf"], a["fc"], a["kn"], a["vn"], a["out"], a["lse"],
+                                           a["B"], a["H"], a["d"], a["dtype"], a["scale"], a["ws"], a["wsb"],
+                                           a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(clip=-0.5), pa.PATH_EINVAL),
+    (dict(clip=float("inf")), pa.PATH_EINVAL),
+    (dict(clip=float("nan")), pa.PATH_EINVAL),
+    (dict(st=None), pa.PATH_EINVAL),
+    (dict(wraw=None), pa.PATH_EINVAL),
+    (dict(cw=None), pa.PATH_EINVAL),
+    (dict(zb=None), pa.PATH_EINVAL),
+    (dict(ws=None), pa.PATH_EINVAL),
+    (dict(n=102), pa.PATH_EINVAL),                             # n > ncap
+    (dict(d=96), pa.PATH_EUNSUPPORTED),
+    (dict(wsb=64), pa.PATH_EINVAL),                            # workspace below the fused size
+    (dict(st=P(0)), pa.PATH_EINVAL),                           # state inside the key cache
+    (dict(st=P(81)), pa.PATH_EINVAL),                          # state over the raw row
+    (dict(st=P(86)), pa.PATH_EINVAL),                          # state inside the workspace
+    (dict(wraw=P(85)), pa.PATH_EINVAL),                        # raw row is the output
+    (dict(zb=P(0)), pa.PATH_EINVAL),                           # zbeta inside the key cache
+    (dict(cw=P(86)), pa.PATH_EINVAL),                          # taps inside the workspace
+    (dict(wraw=ctypes.c_void_p(A * 81 + 8)), pa.PATH_EINVAL),  # misaligned raw row
+    (dict(st=ctypes.c_void_p(A * 84 + 8)), pa.PATH_EINVAL),    # misaligned state
+    (dict(lf=P(87)), pa.PATH_EINVAL),                          # gate without its cache
+])
+def test_decode_fused_rejects_bad_arguments(over, status):
+    assert dec_fused_call(**over) == status
+
+
+def test_decode_fused_workspace_size():
+    plain = pa.decode_workspace_size(2, 3, 100, 64, pa.torch.bfloat16)
+    fused = pa.decode_fused_workspace_size(2, 3, 100, 64, pa.torch.bfloat16)
+    assert fused >= plain + 2 * 3 * 64 * 2 + 2 * 3 * 4  # room for the step's w and beta
+    assert pa.decode_fused_workspace_size(2, 3, 100, 96, pa.torch.bfloat16) == 0
+
+
 def noalloc_call(**over):
     G = 1 << 40  # fake device addresses far apart, so large sizes do not overlap
     args = dict(kc=ctypes.c_void_p(G), vc=ctypes.c_void_p(2 * G), n=100, ncap=100, q=ctypes.c_void_p(3 * G),
