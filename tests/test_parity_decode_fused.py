@@ -42,7 +42,7 @@ def test_decode_fused_steps(dtype, d, gate):
     vn = torch.randn((T, B, H, d), generator=g, device="cuda").to(tdt)
     clip = 1.98 if dtype == "bf16" else 0.0
     w_ref, b_ref = oracle.produce(raw.cpu(), conv_w.cpu(), zb.cpu(), clip)  # positions 2.. are the steps'
-    state = raw[:, :, :2].contiguous()
+    state = raw[:, :, :2].clone()  # a copy: the step moves it on in place
     logf = fcache = fc_ref = None
     if gate:
         logf = torch.nn.functional.logsigmoid(torch.randn((T, B, H), generator=g, device="cuda") + 3.0)

@@ -120,6 +120,58 @@ def test_random_decode(seed):
 
 
 @gpu
+@pytest.mark.parametrize("seed", range(8))
+def test_random_decode_fused(seed):
+    """path_decode_step_fused on random shapes: the oracle's producer on the raw rows (the state drawn at
+    random or zero, as before a sequence's first token) followed by oracle.decode, at the decode bars."""
+    r = np.random.default_rng(3500 + seed)
+    B, H, n, d = int(r.integers(1, 3)), int(r.integers(1, 4)), int(r.integers(0, 3000)), int(r.choice([64, 128]))
+    dt, append, gate = str(r.choice(["f32", "bf16"])), bool(r.integers(0, 2)), bool(r.integers(0, 2))
+    zero_state, clip = bool(r.integers(0, 2)), float(r.choice([0.0, r.uniform(1.0, 2.0)]))
+    if n == 0:
+        append = True
+    ncap = n + 1 + int(r.integers(0, 5))
+    say("case random fused decode %d: B%d H%d n%d d%d %s append=%s gate=%s zero_state=%s clip=%g" % (
+        seed, B, H, n, d, dt, append, gate, zero_state, clip))
+    tdt = pathgen.TORCH_DTYPES[dt]
+    x = pathgen.decode_inputs(B, H, n, d, steps=2, dtype=dt, seed=seed + 40, device="cuda", rowcap=ncap)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 41)
+    raw = torch.randn((B, H, 3, d), generator=g, device="cuda").to(tdt)
+    if zero_state:
+        raw[:, :, :2] = 0
+    conv_w = (torch.randn((H, d, 3), generator=g, device="cuda") / 3.0 ** 0.5).contiguous()
+    zb = torch.randn((B, H, 3), generator=g, device="cuda")
+    state = raw[:, :, :2].clone()  # a copy: the step moves it on in place
+    fc = lf = None
+    if gate:
+        lfs = torch.nn.functional.logsigmoid(3.0 + torch.randn((B, H, ncap + 1), generator=g, device="cuda"))
+        fc = torch.zeros((B, H, ncap), device="cuda")
+        fc[:, :, :n] = torch.cumsum(lfs[:, :, :n].double(), dim=-1).float()
+        lf = lfs[:, :, n].contiguous()
+    kn = x["q"][1].clone() if append else None
+    vn = x["w"][1].clone() if append else None
+    kc0, vc0 = x["kcache"].cpu(), x["vcache"].cpu()
+    fc0 = fc.cpu() if gate else None
+    out, lse = pa.decode_step_fused(x["kcache"], x["vcache"], n, x["q"][0], raw[:, :, 2].contiguous(), conv_w,
+                                    zb[:, :, 2].contiguous(), state, beta_clip=clip, k_new=kn, v_new=vn,
+                                    return_lse=True, logf=lf, fcache=fc)
+    torch.cuda.synchronize()
+    w_ref, b_ref = oracle.produce(raw.cpu(), conv_w.cpu(), zb.cpu(), clip)
+    res = oracle.decode(kc0, vc0, n, x["q"][0].cpu(), w_ref[:, :, 2], b_ref[:, :, 2],
+                        k_new=kn.cpu() if append else None, v_new=vn.cpu() if append else None,
+                        logf=lf.cpu() if gate else None, fcache=fc0)
+    ro, rl = res[2], res[3]
+    eo, el = max_abs(to_np(out), ro), max_abs(to_np(lse), rl)
+    say("  max-abs out %.3e  lse %.3e" % (eo, el))
+    if dt == "f32":
+        assert eo <= 1e-4 and el <= 1e-4
+    else:
+        assert eo <= 2e-2 and eo <= 2e-2 * max(1.0, float(np.abs(ro).max())) and el <= 1e-2
+    assert torch.equal(state, raw[:, :, 1:3])
+
+
+@gpu
 @pytest.mark.parametrize("seed", range(6))
 def test_random_cache(seed):
     r = np.random.default_rng(4000 + seed)

@@ -83,3 +83,33 @@ def test_decode_on_side_stream():
     rel = eo / float(np.abs(ro).max())
     say("  out %.2e (rel %.2e) lse %.2e" % (eo, rel, el))
     assert eo <= 2e-2 and rel <= 2e-2 and el <= 1e-2
+
+
+@gpu
+def test_decode_fused_on_side_stream():
+    B, H, n, d = 2, 2, 3000, 64
+    say("case fused decode on a side stream")
+    x = pathgen.decode_inputs(B, H, n, d, steps=1, dtype="bf16", seed=33, clip=1.98, device="cuda")
+    kc0, vc0 = x["kcache"].cpu(), x["vcache"].cpu()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(34)
+    raw = torch.randn((B, H, 3, d), generator=g, device="cuda").to(torch.bfloat16)
+    conv_w = (torch.randn((H, d, 3), generator=g, device="cuda") / 3.0 ** 0.5).contiguous()
+    zb = torch.randn((B, H, 3), generator=g, device="cuda")
+    state = raw[:, :, :2].clone()  # a copy: the step moves it on in place
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    busy(s)
+    with Spy("path_decode_step_fused", 21) as spy:
+        out, lse = pa.decode_step_fused(x["kcache"], x["vcache"], n, x["q"][0], raw[:, :, 2].contiguous(), conv_w,
+                                        zb[:, :, 2].contiguous(), state, beta_clip=1.98, return_lse=True, stream=s)
+    nbytes = max(pa.decode_fused_workspace_size(B, H, n, d, torch.bfloat16), 16)
+    junk = torch.full((nbytes,), 0xFF, device="cuda", dtype=torch.uint8)
+    assert junk.data_ptr() != spy.ws, "workspace handed out again while the side stream still uses it"
+    s.synchronize()
+    w_ref, b_ref = oracle.produce(raw.cpu(), conv_w.cpu(), zb.cpu(), 1.98)
+    _, _, ro, rl = oracle.decode(kc0, vc0, n, x["q"][0].cpu(), w_ref[:, :, 2], b_ref[:, :, 2])
+    eo, el = max_abs(to_np(out), ro), max_abs(to_np(lse), rl)
+    say("  out %.2e lse %.2e" % (eo, el))
+    assert eo <= 2e-2 and el <= 1e-2
+    assert torch.equal(state, raw[:, :, 1:3])
