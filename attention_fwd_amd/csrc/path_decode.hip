@@ -33,7 +33,7 @@ namespace path {
 // of the process.  Host code must not use the name itself (on the host it is
 // only a stand-in for the symbol): the device address comes from
 // hipGetSymbolAddress, looked up once per device in decode_scratch().
-constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr size_t kScratchBytes = size_t(32) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 size_t decode_scratch_bytes() { return kScratchBytes; }
@@ -61,6 +61,7 @@ hipError_t decode_scratch(void **ptr) {
 namespace {
 
 constexpr int kDecThreads = 256;
+constexpr int kCombThreads = 256;  // threads of the merge kernel (a multiple of D)
 // rows each lane group keeps in flight per iteration (fewer for the wider head
 // and for fp32 rows, so that the raw rows of two iterations, 128 VGPRs, fit):
 // for bf16, half as many rows were 5% (d = 64) and 12% (d = 128) slower on
@@ -269,22 +270,51 @@ __global__ __launch_bounds__(kDecThreads) void path_decode_kernel(DecodeArgs a) 
     }
 }
 
+// Merge of the split partials of one (batch, head): the maximum over the
+// splits, then the weighted sums, both spread over the workgroup (thread group
+// g of D threads sums splits g, g + NG, ...; the NG group sums are then added
+// in order), so the merge stays short when a head has many splits and its
+// result does not depend on timing.
 template <typename S, int D>
-__global__ __launch_bounds__(D) void path_decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kCombThreads) void path_decode_combine_kernel(DecodeArgs a) {
+    constexpr int NG = kCombThreads / D;
+    __shared__ float smax[kCombThreads];
+    __shared__ float ssum[NG][D + 1];
     const int64_t bh = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, g = tid / D, c = tid % D;
     const float *part = (const float *)a.ws + (int64_t)bh * a.nsplit * (D + 2);
     float mm = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) mm = fmaxf(mm, part[(int64_t)s * (D + 2) + D]);
-    float ls = 0.f, as = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
-        const float *p = part + (int64_t)s * (D + 2);
-        const float wgt = p[D] == -INFINITY ? 0.f : fast_exp2(p[D] - mm);
-        ls += wgt * p[D + 1];
-        as += wgt * p[tid];
+    for (int s = tid; s < a.nsplit; s += kCombThreads) mm = fmaxf(mm, part[(int64_t)s * (D + 2) + D]);
+    smax[tid] = mm;
+    __syncthreads();
+#pragma unroll
+    for (int o = kCombThreads / 2; o > 0; o >>= 1) {
+        if (tid < o) smax[tid] = fmaxf(smax[tid], smax[tid + o]);
+        __syncthreads();
     }
-    if (tid < D) ((S *)a.out)[bh * D + tid] = Elem<S>::from_float(as / ls);
-    if (tid == 0 && a.lse) a.lse[bh] = (mm + __log2f(ls)) * kLn2;
+    mm = smax[0];
+    float ls = 0.f, as = 0.f;
+#pragma unroll 4
+    for (int s = g; s < a.nsplit; s += NG) {
+        const float *p = part + (int64_t)s * (D + 2);
+        const float pm = p[D];
+        const float wgt = pm == -INFINITY ? 0.f : fast_exp2(pm - mm);
+        ls += wgt * p[D + 1];
+        as += wgt * p[c];
+    }
+    ssum[g][c] = as;
+    if (c == 0) ssum[g][D] = ls;
+    __syncthreads();
+    if (tid < D) {
+        float at = 0.f, lt = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < NG; ++g2) {
+            at += ssum[g2][tid];
+            lt += ssum[g2][D];
+        }
+        ((S *)a.out)[bh * D + tid] = Elem<S>::from_float(at / lt);
+        if (tid == 0 && a.lse) a.lse[bh] = (mm + __log2f(lt)) * kLn2;
+    }
 }
 
 }  // namespace
@@ -302,7 +332,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((path_decode_kernel<S, D>), grid, dim3(kDecThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((path_decode_combine_kernel<S, D>), dim3((unsigned)(a.B * a.H)), dim3(D), 0, st, a);
+    hipLaunchKernelGGL((path_decode_combine_kernel<S, D>), dim3((unsigned)(a.B * a.H)), dim3(kCombThreads), 0, st, a);
     return hipGetLastError();
 }
 

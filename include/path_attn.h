@@ -282,7 +282,7 @@ path_status_t path_decode_step_fused(void *kcache, void *vcache, int64_t n, int6
  * path_decode_step_ex for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  It takes no workspace: the split partials go to a fixed scratch
- * array of path_decode_noalloc_max_bytes() bytes (16 MiB) that the library
+ * array of path_decode_noalloc_max_bytes() bytes (32 MiB) that the library
  * holds on every device it runs on until the process ends, and the call itself
  * allocates nothing.  Every call on one device shares that device's array, so
  * calls that overlap in time on one device (other streams, other host threads)
@@ -290,7 +290,7 @@ path_status_t path_decode_step_fused(void *kcache, void *vcache, int64_t n, int6
  * start at zero (every split writes its whole record before the merge reads
  * it).  The scratch a call needs is path_decode_workspace_size(B, H, n (+1),
  * d, dtype); larger problems return PATH_ESCRATCH (before anything is
- * enqueued: B * H above 63 550 at d = 64 or 32 263 at d = 128).  The first call on
+ * enqueued: B * H above 127 100 at d = 64 or 64 527 at d = 128).  The first call on
  * a device looks the array's address up on that device (the current device).
  * Arguments, results and the other errors are those of path_decode_step_ex.
  */

@@ -217,7 +217,7 @@ def noalloc_call(**over):
     (dict(vc=ctypes.c_void_p(1 << 40)), pa.PATH_EINVAL),       # caches alias
     (dict(lf=ctypes.c_void_p(7 << 40)), pa.PATH_EINVAL),       # gate without its cache
     (dict(B=1000, H=100, d=128), pa.PATH_ESCRATCH),            # 100 000 heads: partials beyond the scratch
-    (dict(B=640, H=100, d=64), pa.PATH_ESCRATCH),              # 64 000 heads at d = 64
+    (dict(B=1280, H=100, d=64), pa.PATH_ESCRATCH),             # 128 000 heads at d = 64
 ])
 def test_decode_noalloc_rejects_before_launch(over, status):
     """The no-allocation decode entry validates like path_decode_step_ex, and a problem whose split
@@ -228,13 +228,13 @@ def test_decode_noalloc_rejects_before_launch(over, status):
 def test_decode_noalloc_scratch_size():
     lib = pa.lib()
     cap = lib.path_decode_noalloc_max_bytes()
-    assert cap == 16 << 20
+    assert cap == 32 << 20
     # the decode workload (B16 H32, 32768 rows, d 64) and the largest head counts named in the header fit
     assert lib.path_decode_workspace_size(16, 32, 32768, 64, BF) <= cap
-    assert lib.path_decode_workspace_size(1, 63550, 32768, 64, BF) <= cap
-    assert lib.path_decode_workspace_size(1, 63551, 32768, 64, BF) > cap
-    assert lib.path_decode_workspace_size(1, 32263, 32768, 128, BF) <= cap
-    assert lib.path_decode_workspace_size(1, 32264, 32768, 128, BF) > cap
+    assert lib.path_decode_workspace_size(1, 127100, 32768, 64, BF) <= cap
+    assert lib.path_decode_workspace_size(1, 127101, 32768, 64, BF) > cap
+    assert lib.path_decode_workspace_size(1, 64527, 32768, 128, BF) <= cap
+    assert lib.path_decode_workspace_size(1, 64528, 32768, 128, BF) > cap
 
 
 def cache_call(**over):
