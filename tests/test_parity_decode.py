@@ -128,6 +128,22 @@ def test_decode_bf16_peaky():
 
 
 @gpu
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "f32")])
+def test_decode_many_splits(d, dtype):
+    """One head with 100 000 cached rows and one appended token: the split plan gives it hundreds of
+    splits (more than the merge kernel's 256 threads take in one pass, so the maximum is folded over
+    several passes and each of the summing groups adds about a hundred partials)."""
+    B, H, n = 1, 1, 100000
+    say("case decode many splits d%d %s" % (d, dtype))
+    x = pathgen.decode_inputs(B, H, n, d, steps=1, dtype=dtype, seed=23, clip=1.98 if dtype == "bf16" else None,
+                              device="cuda", rowcap=n + 1)
+    tdt = x["kcache"].dtype
+    kn = torch.randn(B, H, d, device="cuda").to(tdt)
+    vn = torch.randn(B, H, d, device="cuda").to(tdt)
+    step_and_check(x["kcache"], x["vcache"], n, x["q"][0], x["w"][0], x["beta"][0], kn, vn, dtype=dtype)
+
+
+@gpu
 def test_decode_workload_full_size():
     """Full decode workload (B16 H32 n=32768 bf16), two steps, four heads checked."""
     c = pathgen.WORKLOADS["decode_N32768_bf16"]
